@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Throughput of C = ReLU(A.B) (fp16 in, fp32 accumulation, fp16 out) on one
+MI355X, through the tlg C ABI.
+
+One step is one full call of the path on one batch of synthetic input that is
+already resident in HBM. The default workload is M = N = K = 8192 with
+U[-1,1] inputs from seed 4. The other workloads are accepted with
+--workload for measurement runs; the parity tests cover them all.
+
+Prints one JSON line: the contract fields, plus
+  roofline     - the dominant kernel's achieved rate (algorithmic FLOP or bytes
+                 per launch / its average launch duration from HIP events on
+                 the stream it runs on) against the MI355X peak;
+  cpu_baseline - the CPU oracle timed on a bounded sample of the same workload
+                 (sampled output rows), in the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM+ReLU TFLOPS (fp16 in, fp32 acc) at 8192³ and % of fp16 MFMA peak"
+# MI355X dense fp16 MFMA: 256 CUs x 4096 FLOP/clock/CU x 2.4 GHz = 2516.6 TFLOP/s (AMD's "2.5 PF")
+PEAK_MFMA_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20  # MI355X Infinity Cache; rotated buffers exceed twice this
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_06_amd", "csrc", f)
+                  for f in ("gemm_relu_gfx950.hip", "tile_layout.h", "api.cpp")]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters,
+    scaled by the copy-kernel calibration, if they were taken on the current
+    kernel sources; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    w = t.get("workloads", {}).get(workload)
+    if not w:
+        return None
+    return w.get("bytes_per_launch")
+
+
+def cpu_baseline(w, A, B, target_s: float):
+    """The oracle as it stands, on whole sampled output rows of the workload."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    rows = np.arange(min(2, w.M))
+    t0 = time.perf_counter()
+    oracle.gemm_relu_rows(A, B, rows)
+    per_row = (time.perf_counter() - t0) / len(rows)
+    n = int(max(1, min(w.M, math.ceil(target_s / max(per_row, 1e-6)))))
+    rows = np.linspace(0, w.M - 1, n).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.gemm_relu_rows(A, B, rows)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * n * w.N * w.K
+    return {
+        "value": flop / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+        "sample": f"{n} of {w.M} output rows ({n}x{w.N}x{w.K} multiply-adds), {dt:.2f} s wall",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="square8192")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample size, in seconds of CPU work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this path runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "multi-GPU runs are not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import tiled_dense_gemm_06_amd as tlg
+    from tiled_dense_gemm_06_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    A, B = wl.make_inputs(w)
+    plan = tlg.plan(w.M, w.N, w.K)
+
+    # Rotate among R copies of the inputs and outputs so the working set is
+    # more than twice the Infinity Cache: every step reads from HBM.
+    per_copy = w.alg_bytes
+    R = max(2, math.ceil(2 * MALL_BYTES / per_copy) + 1)
+    Ad0 = torch.from_numpy(A).to(dev)
+    Bd0 = torch.from_numpy(B).to(dev)
+    As = [Ad0] + [Ad0.clone() for _ in range(R - 1)]
+    Bs = [Bd0] + [Bd0.clone() for _ in range(R - 1)]
+    Cs = [torch.empty((w.M, w.N), dtype=torch.float16, device=dev) for _ in range(R)]
+    h = tlg.handle_for(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        j = i % R
+        tlg.gemm_relu(As[j], Bs[j], out=Cs[j], handle=h, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    span_ms = starts[0].elapsed_time(ends[-1])
+    ms_per_step = span_ms / K
+    avg_launch_s = float(np.mean(per_launch_ms)) / 1e3
+
+    tflops = w.flop / (ms_per_step / 1e3) / 1e12
+    if plan["variant_name"] == "splitk" or w.flop / w.alg_bytes < 314.6:
+        achieved = w.alg_bytes / avg_launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = w.flop / avg_launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_MFMA_TFLOPS}
+    roof["traffic"] = measured_traffic(w.name)
+    roof["kernel"] = plan["config_name"]
+    roof["launch_ms_avg"] = avg_launch_s * 1e3
+    roof["launch_ms_min"] = float(np.min(per_launch_ms))
+
+    props = torch.cuda.get_device_properties(dev)
+    out = {
+        "metric": METRIC, "value": tflops, "unit": "TFLOPS", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "seed": w.seed, "inputs": w.description,
+                   "lda": w.K, "ldb": w.N, "ldc": w.N, "kernel": plan["config_name"],
+                   "variant": plan["variant_name"], "splits": plan["splits"], "rotated_buffers": R,
+                   "accumulate": "f32", "epilogue": "relu, round-to-nearest-even to f16"},
+        "roofline": roof,
+        "pct_of_fp16_peak": 100.0 * tflops / PEAK_MFMA_TFLOPS,
+        "wall_s_timed": wall,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

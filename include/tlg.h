@@ -1,0 +1,152 @@
+/*
+ * tlg: C = ReLU(A . B) on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is TileLang's quick-start kernel `matmul_relu` (TileLang
+ * article, aiwiki.ai/wiki/tilelang, section "Programming model", the listing):
+ * A is an (M, K) float16 matrix and B a (K, N) float16 matrix; the products
+ * are accumulated in float32 over the whole K range; ReLU is applied to the
+ * float32 accumulator; the result is written to the float16 (M, N) matrix C.
+ * Tile sizes, pipeline depth and thread counts are schedule choices of the
+ * library and never change what is computed.
+ *
+ * Conventions for every entry point below:
+ *   - Matrices are row-major with leading dimensions in ELEMENTS:
+ *       A[i][k] is at A + i*lda + k,  B[k][j] at B + k*ldb + j,
+ *       C[i][j] at C + i*ldc + j.
+ *   - A, B and C are DEVICE pointers on the handle's GPU, IEEE binary16,
+ *     at least 2-byte aligned. The caller owns them. Any alignment and any
+ *     leading dimension is accepted; 16-byte-aligned pointers with leading
+ *     dimensions, K and N all multiples of 8 select the fastest kernels.
+ *   - C is overwritten inside its M x N window only; elements of a padded
+ *     row beyond column N are never written. C must not overlap A or B.
+ *   - Calls are asynchronous: work is enqueued on `stream` (0 = the null
+ *     stream) and the call returns at once; results are visible once the
+ *     caller synchronises that stream. No entry point allocates device
+ *     memory except tlg_create, and none synchronises the device.
+ *   - Rounding: float32 sums in an order chosen by the kernel; ReLU maps
+ *     every value that is not > 0 to +0; the float32 -> float16 conversion
+ *     rounds to nearest, ties to even, keeps subnormals and overflows to
+ *     +infinity.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef TLG_H
+#define TLG_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tlg_context *tlg_handle; /* opaque */
+
+typedef enum {
+    TLG_SUCCESS = 0,
+    TLG_ERROR_INVALID_VALUE = 1, /* a bad argument; nothing was enqueued */
+    TLG_ERROR_NOT_SUPPORTED = 2, /* the device is not gfx950, or a request the library cannot serve */
+    TLG_ERROR_OUT_OF_MEMORY = 3, /* tlg_create could not allocate its workspace */
+    TLG_ERROR_HIP = 4            /* the HIP runtime reported an error (e.g. a launch failure) */
+} tlg_status;
+
+/* Kernel families the dispatcher can choose. */
+typedef enum {
+    TLG_VARIANT_AUTO = 0,          /* let tlg_gemm_relu choose (the default) */
+    TLG_VARIANT_NOOP = 1,          /* M == 0 or N == 0: nothing to do */
+    TLG_VARIANT_FILL_ZERO = 2,     /* K == 0: C = +0 (the empty sum after ReLU) */
+    TLG_VARIANT_TILED_DMA = 3,     /* MFMA tiles fed by direct global->LDS loads; needs the aligned fast-path conditions */
+    TLG_VARIANT_TILED_GENERAL = 4, /* MFMA tiles fed through registers; any alignment and leading dimension */
+    TLG_VARIANT_SPLITK = 5,        /* skinny M: K split across work-groups, fp32 partials, then an ordered reduce + ReLU + cast */
+    TLG_VARIANT_NAIVE = 6          /* one thread per output, sequential k; for cross-checks only, never chosen automatically */
+} tlg_variant;
+
+/* What tlg_gemm_relu will launch for a given problem (pure host logic). */
+typedef struct {
+    int32_t variant;          /* a tlg_variant */
+    int32_t config;           /* tile configuration index inside the variant (see tlg_plan_config_name) */
+    int32_t block_m, block_n, block_k; /* output tile and K step of one work-group (0 if none) */
+    int32_t threads;          /* threads per work-group */
+    int32_t splits;           /* K splits (1 unless variant == TLG_VARIANT_SPLITK) */
+    int32_t kernels;          /* kernel launches per call */
+    int64_t grid;             /* work-groups of the main kernel */
+    int64_t workspace_bytes;  /* bytes of the handle's fp32 workspace the call uses */
+} tlg_plan_info;
+
+/* Creates a handle bound to the CURRENT HIP device. Checks that the device
+ * is gfx950 (TLG_ERROR_NOT_SUPPORTED otherwise) and allocates the handle's
+ * fp32 split-K workspace (TLG_ERROR_OUT_OF_MEMORY on failure). *out is set
+ * only on success. One handle may be used by one stream at a time, because
+ * calls on it share its workspace. */
+tlg_status tlg_create(tlg_handle *out);
+
+/* Releases the handle and its workspace. NULL is a no-op. The caller must
+ * make sure no call enqueued with the handle is still running. */
+tlg_status tlg_destroy(tlg_handle h);
+
+/* C = ReLU(A . B) (the quick-start `matmul_relu` of the TileLang article,
+ * "Programming model"). M, N, K >= 0. lda >= max(1, K), ldb >= max(1, N),
+ * ldc >= max(1, N). M == 0 or N == 0: success, nothing enqueued. K == 0:
+ * every C element in the window becomes +0. A, B and C may be NULL only when
+ * nothing would be read or written through them. Returns
+ * TLG_ERROR_INVALID_VALUE (nothing enqueued) for a NULL handle, negative
+ * sizes, a leading dimension below the row width, a needed NULL pointer or a
+ * pointer that is not 2-byte aligned; TLG_ERROR_HIP if a launch fails.
+ * Device faults surface when the caller synchronises. */
+tlg_status tlg_gemm_relu(tlg_handle h, int64_t M, int64_t N, int64_t K,
+                         const void *A, int64_t lda,
+                         const void *B, int64_t ldb,
+                         void *C, int64_t ldc,
+                         hipStream_t stream);
+
+/* Same operation as tlg_gemm_relu with a forced kernel family and split
+ * count, for tests and measurements: variant is a tlg_variant (AUTO picks as
+ * tlg_gemm_relu does); splits <= 0 lets the library choose. Returns
+ * TLG_ERROR_NOT_SUPPORTED if the forced variant cannot serve the problem
+ * (e.g. DMA tiles on unaligned data) and nothing is enqueued. */
+tlg_status tlg_gemm_relu_variant(tlg_handle h, int32_t variant, int32_t splits,
+                                 int64_t M, int64_t N, int64_t K,
+                                 const void *A, int64_t lda,
+                                 const void *B, int64_t ldb,
+                                 void *C, int64_t ldc,
+                                 hipStream_t stream);
+
+/* Argument check used by tlg_gemm_relu, without a handle or a GPU (pure host
+ * logic): TLG_SUCCESS or TLG_ERROR_INVALID_VALUE. */
+tlg_status tlg_check_args(int64_t M, int64_t N, int64_t K,
+                          const void *A, int64_t lda,
+                          const void *B, int64_t ldb,
+                          const void *C, int64_t ldc);
+
+/* The launch plan for a problem (pure host logic, no GPU needed). variant and
+ * splits have the meaning of tlg_gemm_relu_variant; workspace_cap_bytes is
+ * the workspace available (tlg_workspace_bytes() for a handle). Returns
+ * TLG_ERROR_INVALID_VALUE for bad arguments, TLG_ERROR_NOT_SUPPORTED when the
+ * forced variant cannot serve the problem. */
+tlg_status tlg_plan(int64_t M, int64_t N, int64_t K,
+                    const void *A, int64_t lda,
+                    const void *B, int64_t ldb,
+                    const void *C, int64_t ldc,
+                    int32_t variant, int32_t splits, int64_t workspace_cap_bytes,
+                    tlg_plan_info *out);
+
+/* Name of a tile configuration reported by tlg_plan ("" if unknown). */
+const char *tlg_plan_config_name(int32_t variant, int32_t config);
+
+/* Bytes of fp32 workspace a handle allocates at creation. */
+int64_t tlg_workspace_bytes(void);
+
+/* 1 if a device architecture name (as in hipDeviceProp_t::gcnArchName, e.g.
+ * "gfx950:sramecc+:xnack-") is one this library runs on, else 0. */
+int32_t tlg_arch_supported(const char *gcn_arch_name);
+
+/* A static description of a status code; never NULL. */
+const char *tlg_status_string(tlg_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t tlg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TLG_H */

@@ -1,0 +1,303 @@
+// CPU emulation of the data movement of the gfx950 GEMM+ReLU kernels
+// (test-only). It uses the kernels' own index arithmetic (tile_layout.h) and
+// models, lane by lane:
+//   * the direct-to-LDS loads (16 bytes per lane, zeros for out-of-range
+//     lanes), checking that every real global access lies inside its matrix
+//     and that each LDS stage is written exactly once;
+//   * the operand fragment reads (ds_read_b128 and ds_read_b64_tr_b16 with
+//     their measured lane semantics), checking LDS bounds and that each read
+//     is free of bank conflicts on a 64-bank LDS;
+//   * v_mfma_f32_32x32x16_f16 with its measured operand and result layouts
+//     (fp32 products, fp32 sums);
+//   * the epilogue (ReLU and round-to-nearest-even fp16, or fp32 partials),
+//     checking that every element of the M x N window is written exactly once
+//     and nothing outside it.
+// Its output is compared against the CPU oracle by the tests. It shares no
+// code with the oracle.
+#include <stdint.h>
+#include <string.h>
+
+#include <cmath>
+#include <cstdio>
+#include <vector>
+
+#include "tile_layout.h"
+
+using namespace tlg;
+
+namespace {
+
+float h2f(uint16_t h) {
+    // binary16 -> binary32 via the hardware-independent definition
+    uint32_t s = (uint32_t)(h >> 15) << 31, e = (h >> 10) & 31, f = h & 1023, u;
+    if (e == 31) u = s | 0x7f800000u | (f << 13);
+    else if (e == 0) {
+        if (!f) u = s;
+        else {
+            int ex = -14;
+            while (!(f & 1024)) { f <<= 1; ex--; }
+            u = s | ((uint32_t)(ex + 127) << 23) | ((f & 1023) << 13);
+        }
+    } else u = s | ((e + 112) << 23) | (f << 13);
+    float x;
+    memcpy(&x, &u, 4);
+    return x;
+}
+
+uint16_t f2h(float x) {  // round to nearest even via the C library's rounding of a scaled value
+    if (std::isnan(x)) return 0x7e00;
+    uint16_t sign = std::signbit(x) ? 0x8000 : 0;
+    double a = std::fabs((double)x);
+    if (a >= 65520.0) return sign | 0x7c00;
+    if (a < std::ldexp(1.0, -14)) {
+        double q = std::nearbyint(a * std::ldexp(1.0, 24));  // FE_TONEAREST by default
+        return sign | (uint16_t)q;
+    }
+    int e;
+    std::frexp(a, &e);  // a = m * 2^e, m in [0.5, 1)
+    double q = std::nearbyint(std::ldexp(a, 11 - e));  // 11 significant bits
+    if (q >= 2048.0) { q /= 2; e += 1; }
+    return sign | (uint16_t)(((e - 1 + 15) << 10) + ((int)q - 1024));
+}
+
+struct Errs {
+    long oob_global = 0, lds_multi = 0, lds_oob = 0, bank_conflict = 0, c_multi = 0, c_missing = 0, c_outside = 0,
+         tile_dup = 0;
+};
+
+struct Problem {
+    int M, N, K;
+    const uint16_t *A;
+    long lda;
+    const uint16_t *B;
+    long ldb;
+    uint16_t *C;
+    long ldc;
+    float *W;  // split mode: partials (splits x M x N)
+    int k_split;
+    int splits;
+};
+
+// slot of a 16-byte access in a 256-byte bank window (64 banks x 4 bytes)
+int slot16(int byte) { return (byte % 256) / 16; }
+
+template <class S>
+void run_dma(const Problem &p, bool split, Errs &er, std::vector<int> &cover) {
+    const int tiles_m = (p.M + S::BM - 1) / S::BM, tiles_n = (p.N + S::BN - 1) / S::BN;
+    const int nwg = tiles_m * tiles_n;
+    std::vector<int> seen(nwg, 0);
+    std::vector<uint8_t> lds(S::STAGE_BYTES);
+    std::vector<int> lds_w(S::STAGE_BYTES);
+    for (int y = 0; y < (split ? p.splits : 1); ++y)
+        for (int pid = 0; pid < nwg; ++pid) {
+            int tmi, tni;
+            grouped_tile(xcd_remap(pid, nwg), tiles_m, tiles_n, 4, &tmi, &tni);
+            if (tmi < 0 || tmi >= tiles_m || tni < 0 || tni >= tiles_n) { er.tile_dup++; continue; }
+            if (y == 0) {
+                if (seen[tmi * tiles_n + tni]++) er.tile_dup++;
+            }
+            const int m0 = tmi * S::BM, n0 = tni * S::BN;
+            const int kbeg = split ? y * p.k_split : 0;
+            const int kend = split ? std::min(p.K, kbeg + p.k_split) : p.K;
+            const int nk = kend > kbeg ? (kend - kbeg + S::BK - 1) / S::BK : 0;
+            // accumulators: [wave][tn][tm][lane][16]
+            std::vector<float> acc((size_t)S::WAVES * S::TN * S::TM * 64 * 16, 0.0f);
+            for (int kt = 0; kt < nk; ++kt) {
+                const int k0 = kbeg + kt * S::BK;
+                std::fill(lds.begin(), lds.end(), 0xAB);
+                std::fill(lds_w.begin(), lds_w.end(), 0);
+                for (int w = 0; w < S::WAVES; ++w)
+                    for (int lane = 0; lane < 64; ++lane) {
+                        for (int i = 0; i < S::DMA_A; ++i) {
+                            ChunkRef c = dma_a_chunk<S>(w, i, lane);
+                            int dst = (w * S::DMA_A + i) * 1024 + lane * 16;
+                            bool ok = m0 + c.row < p.M && k0 + 8 * c.chunk < kend;
+                            for (int b = 0; b < 16; ++b) {
+                                if (dst + b >= S::A_BYTES) { er.lds_oob++; continue; }
+                                if (lds_w[dst + b]++) er.lds_multi++;
+                            }
+                            for (int e = 0; e < 8; ++e) {
+                                uint16_t v = 0;
+                                if (ok) {
+                                    long row = m0 + c.row, col = k0 + 8 * c.chunk + e;
+                                    if (row >= p.M || col >= p.K || col >= p.lda) er.oob_global++;
+                                    else v = p.A[row * p.lda + col];
+                                }
+                                memcpy(&lds[dst + 2 * e], &v, 2);
+                            }
+                        }
+                        for (int i = 0; i < S::DMA_B; ++i) {
+                            ChunkRef c = dma_b_chunk<S>(w, i, lane);
+                            int dst = S::A_BYTES + (w * S::DMA_B + i) * 1024 + lane * 16;
+                            bool ok = n0 + 8 * c.chunk < p.N && k0 + c.row < kend;
+                            for (int b = 0; b < 16; ++b) {
+                                if (dst + b >= S::STAGE_BYTES) { er.lds_oob++; continue; }
+                                if (lds_w[dst + b]++) er.lds_multi++;
+                            }
+                            for (int e = 0; e < 8; ++e) {
+                                uint16_t v = 0;
+                                if (ok) {
+                                    long row = k0 + c.row, col = n0 + 8 * c.chunk + e;
+                                    if (row >= p.K || col >= p.N || col >= p.ldb) er.oob_global++;
+                                    else v = p.B[row * p.ldb + col];
+                                }
+                                memcpy(&lds[dst + 2 * e], &v, 2);
+                            }
+                        }
+                    }
+                for (int b = 0; b < S::STAGE_BYTES; ++b)
+                    if (lds_w[b] != 1) er.lds_multi++;
+                // fragments and MFMAs
+                for (int w = 0; w < S::WAVES; ++w) {
+                    const int wm0 = (w / S::WN) * S::WTM, wn0 = (w % S::WN) * S::WTN;
+                    for (int s = 0; s < S::KSTEPS; ++s) {
+                        // bf[tn][lane][8], af[tm][lane][8]
+                        std::vector<float> bf((size_t)S::TN * 64 * 8), af((size_t)S::TM * 64 * 8);
+                        for (int tn = 0; tn < S::TN; ++tn)
+                            for (int h = 0; h < 2; ++h) {
+                                int addr[64];
+                                for (int l = 0; l < 64; ++l) {
+                                    addr[l] = frag_b_offset<S>(wn0, tn, s, h, l);
+                                    if (addr[l] < 0 || addr[l] + 8 > S::B_BYTES || addr[l] % 8) er.lds_oob++;
+                                }
+                                // 32 lanes per LDS cycle: 32 x 8 bytes must hit 64 distinct banks
+                                for (int half = 0; half < 2; ++half) {
+                                    int used[64] = {0};
+                                    for (int l = 32 * half; l < 32 * half + 32; ++l)
+                                        for (int d = 0; d < 2; ++d) {
+                                            int bank = ((addr[l] + 4 * d) / 4) % 64;
+                                            if (used[bank]++) er.bank_conflict++;
+                                        }
+                                }
+                                for (int l = 0; l < 64; ++l) {
+                                    int g = l / 16, i = l % 16;
+                                    for (int j = 0; j < 4; ++j) {
+                                        int src = 16 * g + i / 4 + 4 * j;
+                                        int a = addr[src];
+                                        uint16_t v = 0;
+                                        if (a >= 0 && a + 8 <= S::B_BYTES) memcpy(&v, &lds[S::A_BYTES + a + 2 * (i % 4)], 2);
+                                        bf[((size_t)tn * 64 + l) * 8 + 4 * h + j] = h2f(v);
+                                    }
+                                }
+                            }
+                        for (int tm = 0; tm < S::TM; ++tm) {
+                            int addr[64];
+                            for (int l = 0; l < 64; ++l) {
+                                addr[l] = frag_a_offset<S>(wm0, tm, s, l);
+                                if (addr[l] < 0 || addr[l] + 16 > S::A_BYTES || addr[l] % 16) er.lds_oob++;
+                            }
+                            // 16 lanes per LDS cycle: 16 x 16 bytes must hit 16 distinct slots
+                            for (int q = 0; q < 4; ++q) {
+                                int used[16] = {0};
+                                for (int l = 16 * q; l < 16 * q + 16; ++l)
+                                    if (used[slot16(addr[l])]++) er.bank_conflict++;
+                            }
+                            for (int l = 0; l < 64; ++l)
+                                for (int e = 0; e < 8; ++e) {
+                                    uint16_t v = 0;
+                                    if (addr[l] >= 0 && addr[l] + 16 <= S::A_BYTES) memcpy(&v, &lds[addr[l] + 2 * e], 2);
+                                    af[((size_t)tm * 64 + l) * 8 + e] = h2f(v);
+                                }
+                        }
+                        // D = X * Y: X from bf (rows i = lane%32, k = 8*(lane/32)+e), Y from af (cols j)
+                        for (int tn = 0; tn < S::TN; ++tn)
+                            for (int tm = 0; tm < S::TM; ++tm)
+                                for (int l = 0; l < 64; ++l)
+                                    for (int r = 0; r < 16; ++r) {
+                                        int i = 8 * (r / 4) + 4 * (l / 32) + r % 4, j = l % 32;
+                                        float sum = 0.0f;
+                                        for (int kk = 0; kk < 16; ++kk) {
+                                            int lx = i + 32 * (kk / 8), ly = j + 32 * (kk / 8), e = kk % 8;
+                                            sum += bf[((size_t)tn * 64 + lx) * 8 + e] * af[((size_t)tm * 64 + ly) * 8 + e];
+                                        }
+                                        float &d = acc[((((size_t)w * S::TN + tn) * S::TM + tm) * 64 + l) * 16 + r];
+                                        d = d + sum;
+                                    }
+                    }
+                }
+            }
+            // epilogue
+            for (int w = 0; w < S::WAVES; ++w) {
+                const int wm0 = (w / S::WN) * S::WTM, wn0 = (w % S::WN) * S::WTN;
+                for (int tn = 0; tn < S::TN; ++tn)
+                    for (int tm = 0; tm < S::TM; ++tm)
+                        for (int l = 0; l < 64; ++l)
+                            for (int r = 0; r < 16; ++r) {
+                                int m = m0 + acc_m(wm0, tm, l), n = n0 + acc_n(wn0, tn, r, l);
+                                float v = acc[((((size_t)w * S::TN + tn) * S::TM + tm) * 64 + l) * 16 + r];
+                                if (m >= p.M || n >= p.N) continue;  // the kernel masks these
+                                if (split) {
+                                    p.W[((size_t)y * p.M + m) * p.N + n] = v;
+                                    cover[((size_t)y * p.M + m) * p.N + n]++;
+                                } else {
+                                    p.C[(size_t)m * p.ldc + n] = f2h(v > 0.0f ? v : 0.0f);
+                                    cover[(size_t)m * p.N + n]++;
+                                }
+                            }
+            }
+        }
+    for (int t = 0; t < nwg; ++t)
+        if (seen[t] != 1) er.tile_dup++;
+}
+
+template <class S>
+int emulate(const Problem &p, bool split, long *errs) {
+    Errs er;
+    std::vector<int> cover((size_t)(split ? p.splits : 1) * p.M * p.N, 0);
+    run_dma<S>(p, split, er, cover);
+    for (int c : cover) {
+        if (c == 0) er.c_missing++;
+        if (c > 1) er.c_multi++;
+    }
+    if (split) {  // stage 2: ordered sum over splits, ReLU, cast
+        for (long mn = 0; mn < (long)p.M * p.N; ++mn) {
+            float a = p.W[mn];
+            for (int s = 1; s < p.splits; ++s) a = a + p.W[(size_t)s * p.M * p.N + mn];
+            p.C[(mn / p.N) * p.ldc + mn % p.N] = f2h(a > 0.0f ? a : 0.0f);
+        }
+    }
+    errs[0] = er.oob_global;
+    errs[1] = er.lds_multi;
+    errs[2] = er.lds_oob;
+    errs[3] = er.bank_conflict;
+    errs[4] = er.c_multi;
+    errs[5] = er.c_missing;
+    errs[6] = er.c_outside;
+    errs[7] = er.tile_dup;
+    return 0;
+}
+
+}  // namespace
+
+// Shapes mirrored from the kernels' configuration table.
+using E256 = TileShape<256, 256, 32, 2, 2, 4>;
+using E128 = TileShape<128, 128, 32, 2, 2, 4>;
+using E64 = TileShape<64, 64, 64, 2, 2, 3>;
+using ES128 = TileShape<32, 128, 64, 1, 4, 4>;
+using ES256 = TileShape<32, 256, 64, 1, 4, 3>;
+
+extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A, long lda, const uint16_t *B,
+                             long ldb, uint16_t *C, long ldc, int splits, int k_split, float *W, long *errs) {
+    Problem p{M, N, K, A, lda, B, ldb, C, ldc, W, k_split, splits};
+    switch (config) {
+        case 0: return emulate<E256>(p, false, errs);
+        case 1: return emulate<E128>(p, false, errs);
+        case 2: return emulate<E64>(p, false, errs);
+        case 10: return emulate<ES128>(p, true, errs);
+        case 11: return emulate<ES256>(p, true, errs);
+        default: return -1;
+    }
+}
+
+// xcd_remap must be a bijection on [0, nwg) for every nwg.
+extern "C" long emu_check_remap(int max_nwg) {
+    long bad = 0;
+    for (int n = 1; n <= max_nwg; ++n) {
+        std::vector<int> hit(n, 0);
+        for (int p = 0; p < n; ++p) {
+            int q = xcd_remap(p, n);
+            if (q < 0 || q >= n || hit[q]++) bad++;
+        }
+    }
+    return bad;
+}

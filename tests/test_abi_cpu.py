@@ -1,0 +1,129 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/tlg.h declares, and its pure host logic (argument checks, kernel
+choice, architecture check, status strings) behaves as documented."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_dense_gemm_06_amd as tlg
+from tiled_dense_gemm_06_amd import _native as nat
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tlg.h")
+
+A16 = 1 << 20  # stand-in device addresses (never dereferenced on the host)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tlg_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert "tlg_gemm_relu" in names and "tlg_create" in names and "tlg_destroy" in names
+    L = ctypes.CDLL(nat.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings():
+    assert tlg.tlg_version() >= 100
+    for st in range(5):
+        assert tlg.tlg_status_string(st).startswith("TLG_")
+    assert "unknown" in tlg.tlg_status_string(99)
+
+
+def test_arch_check():
+    assert tlg.tlg_arch_supported("gfx950")
+    assert tlg.tlg_arch_supported("gfx950:sramecc+:xnack-")
+    for bad in ["gfx942", "gfx9500", "gfx90a", "", "sm_90", "gfx95"]:
+        assert not tlg.tlg_arch_supported(bad), bad
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((4, 4, 4, A16, 4, A16, 4, A16, 4), 0),
+    ((-1, 4, 4, A16, 4, A16, 4, A16, 4), 1),
+    ((4, -1, 4, A16, 4, A16, 4, A16, 4), 1),
+    ((4, 4, -1, A16, 4, A16, 4, A16, 4), 1),
+    ((4, 4, 4, A16, 3, A16, 4, A16, 4), 1),   # lda < K
+    ((4, 4, 4, A16, 4, A16, 3, A16, 4), 1),   # ldb < N
+    ((4, 4, 4, A16, 4, A16, 4, A16, 3), 1),   # ldc < N
+    ((4, 4, 4, 0, 4, A16, 4, A16, 4), 1),     # A NULL
+    ((4, 4, 4, A16, 4, 0, 4, A16, 4), 1),     # B NULL
+    ((4, 4, 4, A16, 4, A16, 4, 0, 4), 1),     # C NULL
+    ((4, 4, 4, A16 + 1, 4, A16, 4, A16, 4), 1),  # odd address
+    ((0, 4, 4, 0, 4, 0, 4, 0, 4), 0),         # M == 0: nothing touched, NULLs allowed
+    ((4, 0, 4, 0, 4, 0, 1, 0, 1), 0),         # N == 0
+    ((4, 4, 0, 0, 1, 0, 4, A16, 4), 0),       # K == 0: A and B unused, C needed
+    ((4, 4, 0, 0, 1, 0, 4, 0, 4), 1),         # K == 0 but C NULL
+])
+def test_check_args(args, expect):
+    assert tlg.tlg_check_args(*args) == expect
+
+
+def test_plan_shapes_of_the_workloads():
+    assert tlg.plan(8192, 8192, 8192)["config_name"].startswith("dma_256x256")
+    assert tlg.plan(4096, 4096, 4096)["variant_name"] == "tiled_dma"
+    p = tlg.plan(3001, 2049, 1537)
+    assert p["variant_name"] == "tiled_general"  # odd leading dimensions
+    p = tlg.plan(16, 14336, 4096)
+    assert p["variant_name"] == "splitk" and p["splits"] >= 2 and p["kernels"] == 2
+    assert p["workspace_bytes"] == p["splits"] * 16 * 14336 * 4 <= tlg.tlg_workspace_bytes()
+    assert tlg.plan(256, 256, 256)["variant_name"] == "tiled_dma"
+    assert tlg.plan(5, 7, 0)["variant_name"] == "fill_zero"
+    assert tlg.plan(0, 7, 9)["variant_name"] == "noop"
+    assert tlg.plan(7, 0, 9)["variant_name"] == "noop"
+
+
+def test_plan_alignment_decides_dma():
+    assert tlg.plan(512, 512, 512, aligned=False)["variant_name"] == "tiled_general"
+    assert tlg.plan(512, 512, 512, lda=520)["variant_name"] == "tiled_dma"
+    assert tlg.plan(512, 512, 512, lda=513)["variant_name"] == "tiled_general"
+    assert tlg.plan(512, 516, 512)["variant_name"] == "tiled_general"  # N % 8 != 0
+    assert tlg.plan(512, 512, 500)["variant_name"] == "tiled_general"  # K % 8 != 0
+
+
+def test_forced_variants():
+    with pytest.raises(tlg.TlgError):
+        tlg.plan(512, 512, 512, aligned=False, variant=tlg.TLG_VARIANT_TILED_DMA)
+    with pytest.raises(tlg.TlgError):
+        tlg.plan(16, 14336, 4095, variant=tlg.TLG_VARIANT_SPLITK)
+    p = tlg.plan(16, 14336, 4096, variant=tlg.TLG_VARIANT_SPLITK, splits=8)
+    assert p["splits"] == 8 and p["grid"] == 112 * 8
+    p = tlg.plan(300, 300, 300, variant=tlg.TLG_VARIANT_NAIVE)
+    assert p["variant_name"] == "naive"
+    p = tlg.plan(300, 304, 304, variant=tlg.TLG_VARIANT_TILED_GENERAL)
+    assert p["variant_name"] == "tiled_general"
+    with pytest.raises(tlg.TlgError):
+        tlg.plan(4, 4, 4, variant=99)
+
+
+def test_split_counts_cover_k_without_empty_splits():
+    for K in [512, 520, 1000, 4096, 4104, 8192, 65536]:
+        for forced in [0, 2, 3, 7, 16, 64]:
+            try:
+                p = tlg.plan(16, 1024, K - K % 8, variant=tlg.TLG_VARIANT_SPLITK, splits=forced)
+            except tlg.TlgError:
+                continue
+            s, bk = p["splits"], p["block_k"]
+            k = K - K % 8
+            ksteps = -(-k // bk)
+            k_split = -(-ksteps // s) * bk
+            assert (s - 1) * k_split < k <= s * k_split, (K, forced, s)
+
+
+def test_workspace_cap_lowers_splits():
+    st, info = nat.tlg_plan(64, 14336, 4096, A16, 4096, A16, 14336, A16, 14336, tlg.TLG_VARIANT_SPLITK, 16,
+                            2 * 64 * 14336 * 4)
+    assert st == 0 and info.splits <= 2 and info.workspace_bytes <= 2 * 64 * 14336 * 4
+
+
+def test_gemm_relu_rejects_null_handle():
+    # no GPU needed: the handle check comes first
+    st = nat.tlg_gemm_relu(None, 4, 4, 4, A16, 4, A16, 4, A16, 4, None)
+    assert st == nat.TLG_ERROR_INVALID_VALUE
+    assert nat.tlg_destroy(None) == 0

@@ -1,0 +1,292 @@
+"""GPU parity: the gfx950 kernels, called through the C ABI, against the CPU
+oracle on the same seeded inputs.
+
+Bar: bit-exact on integer-valued inputs (every partial sum is an exact
+integer in fp32, so the order of the kernel's sums cannot matter), and
+|got - ref| <= 1e-2 + 4e-3 |ref| elementwise otherwise. Full outputs are
+compared where the oracle finishes in seconds; at 4096^3 and 8192^3 the
+oracle computes sampled rows and sampled elements, and the whole output is
+compared against the GPU's sequential cross-check kernel, which is itself
+checked bit-exact against the oracle on samples.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import tiled_dense_gemm_06_amd as tlg
+from tiled_dense_gemm_06_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+V_AUTO = tlg.TLG_VARIANT_AUTO
+V_DMA = tlg.TLG_VARIANT_TILED_DMA
+V_GEN = tlg.TLG_VARIANT_TILED_GENERAL
+V_SPLIT = tlg.TLG_VARIANT_SPLITK
+V_NAIVE = tlg.TLG_VARIANT_NAIVE
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def to_dev(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def bits(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def run(A, B, dev, variant=V_AUTO, splits=0, out=None):
+    Ad, Bd = (to_dev(A, dev), to_dev(B, dev)) if isinstance(A, np.ndarray) else (A, B)
+    C = tlg.gemm_relu(Ad, Bd, out=out, variant=variant, splits=splits)
+    torch.cuda.synchronize()
+    return C
+
+
+def assert_close(got_bits, ref_bits, what=""):
+    got = got_bits.view(np.float16).astype(np.float64)
+    ref = ref_bits.view(np.float16).astype(np.float64)
+    assert not np.isnan(got).any(), f"{what}: NaN in output"
+    err = np.abs(got - ref)
+    bad = err > 1e-2 + 4e-3 * np.abs(ref)
+    assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, max err {err.max()}"
+    assert np.all((got_bits & 0x8000) == 0), f"{what}: negative or -0 output"
+
+
+def variants_for(M, N, K, aligned=True, lda=None, ldb=None, ldc=None):
+    """Every kernel family that can serve this problem (AUTO first)."""
+    out = [V_AUTO, V_GEN, V_NAIVE]
+    kw = dict(lda=lda, ldb=ldb, ldc=ldc, aligned=aligned)
+    p = tlg.plan(M, N, K, **kw)
+    for v in (V_DMA, V_SPLIT):
+        try:
+            tlg.plan(M, N, K, variant=v, **kw)
+            out.append(v)
+        except tlg.TlgError:
+            pass
+    assert p["variant"] in out or p["variant_name"] in ("fill_zero", "noop")
+    return out
+
+
+# ---------------------------------------------------------------- the five workloads
+
+def test_square256_all_variants(dev):
+    w = wl.WORKLOADS["square256"]
+    for integer in (False, True):
+        A, B = wl.make_inputs(w, integer=integer)
+        ref = oracle.gemm_relu(A, B)
+        for v in variants_for(w.M, w.N, w.K):
+            got = bits(run(A, B, dev, variant=v))
+            if integer or v == V_NAIVE:
+                assert np.array_equal(got, ref), (integer, v)
+            else:
+                assert_close(got, ref, f"variant {v}")
+
+
+@pytest.mark.parametrize("kind", ["normal", "integer", "integer_pos"])
+def test_ragged_full_output(dev, kind):
+    w = wl.WORKLOADS["ragged3001x2049x1537"]
+    if kind == "normal":
+        A, B = wl.make_inputs(w)
+    elif kind == "integer":
+        A, B = wl.make_inputs(w, integer=True)
+    else:
+        A, B = wl.make_random(w.M, w.N, w.K, seed=w.seed, kind="integer_pos")
+    ref = oracle.gemm_relu(A, B)
+    got = bits(run(A, B, dev))
+    assert tlg.plan(w.M, w.N, w.K)["variant_name"] == "tiled_general"
+    if kind == "normal":
+        assert_close(got, ref, "ragged")
+        # the cross-check kernel is the sequential definition: bit-exact on any input
+        assert np.array_equal(bits(run(A, B, dev, variant=V_NAIVE)), ref)
+    else:
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 4, 8, 16])
+def test_skinny_full_output(dev, splits):
+    w = wl.WORKLOADS["skinny16x14336x4096"]
+    A, B = wl.make_inputs(w)
+    ref = oracle.gemm_relu(A, B)
+    v = V_AUTO if splits == 0 else V_SPLIT
+    got = bits(run(A, B, dev, variant=v, splits=splits))
+    assert_close(got, ref, f"skinny splits={splits}")
+    Ai, Bi = wl.make_inputs(w, integer=True)
+    got = bits(run(Ai, Bi, dev, variant=v, splits=splits))
+    assert np.array_equal(got, oracle.gemm_relu(Ai, Bi))
+
+
+def test_skinny_without_split(dev):
+    w = wl.WORKLOADS["skinny16x14336x4096"]
+    A, B = wl.make_random(w.M, w.N, w.K, seed=3, kind="integer_pos")
+    ref = oracle.gemm_relu(A, B)
+    for v in (V_DMA, V_GEN):
+        assert np.array_equal(bits(run(A, B, dev, variant=v)), ref), v
+
+
+def _sample_rows(M, bm=256):
+    rows = {0, 1, M - 1, M - 2, bm - 1, bm, M // 2, M // 2 + 1}
+    rows |= set(np.random.default_rng(M).choice(M, 12, replace=False).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < M))
+
+
+@pytest.mark.parametrize("name", ["square4096", "square8192"])
+def test_large_square_sampled(dev, name):
+    w = wl.WORKLOADS[name]
+    A, B = wl.make_inputs(w)
+    Ad, Bd = to_dev(A, dev), to_dev(B, dev)
+    C = tlg.gemm_relu(Ad, Bd)  # the launch configuration the benchmark times
+    Cn = tlg.gemm_relu(Ad, Bd, variant=V_NAIVE)
+    torch.cuda.synchronize()
+    got, naive = bits(C), bits(Cn)
+    rows = _sample_rows(w.M)
+    ref_rows = oracle.gemm_relu_rows(A, B, rows)
+    assert_close(got[rows], ref_rows, f"{name} sampled rows")
+    assert np.array_equal(naive[rows], ref_rows), "cross-check kernel differs from the oracle"
+    rng = np.random.default_rng(9)
+    ii, jj = rng.integers(0, w.M, 4096), rng.integers(0, w.N, 4096)
+    ref_el = oracle.gemm_relu_elems(A, B, ii, jj)
+    assert_close(got[ii, jj], ref_el, f"{name} sampled elements")
+    assert np.array_equal(naive[ii, jj], ref_el)
+    # the whole output against the sequential cross-check kernel
+    assert_close(got, naive, f"{name} full output vs cross-check kernel")
+    del Ad, Bd, C, Cn
+    # integer inputs: bit-exact on sampled rows
+    Ai, Bi = wl.make_inputs(w, integer=True)
+    got = bits(run(Ai, Bi, dev))
+    assert np.array_equal(got[rows], oracle.gemm_relu_rows(Ai, Bi, rows))
+
+
+# ---------------------------------------------------------------- writes, padding, edges
+
+@pytest.mark.parametrize("shape,aligned_ld", [((300, 264, 200), True), ((301, 259, 203), False),
+                                              ((16, 2048, 2048), True), ((513, 520, 64), True)])
+def test_sentinel_and_guard_bands(dev, shape, aligned_ld):
+    """C is prefilled with NaN (0xFFFF): every window element must be written;
+    the padding columns (ldc > N) and the rows after M must stay untouched."""
+    M, N, K = shape
+    A, B = wl.make_random(M, N, K, seed=11, kind="integer")
+    ref = oracle.gemm_relu(A, B)
+    ldc = N + (24 if aligned_ld else 5)
+    for v in variants_for(M, N, K, ldc=ldc):
+        big = torch.full((M + 3, ldc), float("nan"), dtype=torch.float16, device=dev)
+        out = big[:M, :N]
+        tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), out=out, variant=v)
+        torch.cuda.synchronize()
+        allb = bits(big)
+        assert np.array_equal(allb[:M, :N], ref), v
+        assert np.all(np.isnan(allb[:M, N:].view(np.float16))), v
+        assert np.all(np.isnan(allb[M:].view(np.float16))), v
+
+
+@pytest.mark.parametrize("pad_a,pad_b", [(8, 16), (3, 5), (0, 24), (64, 0)])
+def test_padded_inputs_never_read(dev, pad_a, pad_b):
+    """Padding of A and B rows holds NaN; it must never reach a product."""
+    M, N, K = 200, 136, 88
+    A, B = wl.make_random(M, N, K, seed=13, kind="integer_pos")
+    ref = oracle.gemm_relu(A, B)
+    Ap = torch.full((M, K + pad_a), float("nan"), dtype=torch.float16, device=dev)
+    Bp = torch.full((K, N + pad_b), float("nan"), dtype=torch.float16, device=dev)
+    Ap[:, :K] = to_dev(A, dev)
+    Bp[:, :N] = to_dev(B, dev)
+    for v in variants_for(M, N, K, lda=K + pad_a, ldb=N + pad_b):
+        got = bits(run(Ap[:, :K], Bp[:, :N], dev, variant=v))
+        assert np.array_equal(got, ref), (pad_a, pad_b, v)
+
+
+def test_random_ragged_sweep(dev):
+    rng = np.random.default_rng(2024)
+    for case in range(40):
+        M, N, K = (int(x) for x in rng.integers(1, 301, size=3))
+        if case % 3 == 0:  # make some cases eligible for the direct-to-LDS kernels
+            N, K = max(8, N - N % 8), max(8, K - K % 8)
+        kind = "integer_pos" if case % 2 else "integer"
+        A, B = wl.make_random(M, N, K, seed=case, kind=kind)
+        ref = oracle.gemm_relu(A, B)
+        for v in variants_for(M, N, K):
+            got = bits(run(A, B, dev, variant=v))
+            assert np.array_equal(got, ref), (case, M, N, K, v)
+
+
+def test_degenerate_sizes(dev):
+    # K == 0: C = +0 in the window
+    C = torch.full((5, 7), float("nan"), dtype=torch.float16, device=dev)
+    A = torch.empty((5, 0), dtype=torch.float16, device=dev)
+    B = torch.empty((0, 7), dtype=torch.float16, device=dev)
+    tlg.gemm_relu(A, B, out=C)
+    torch.cuda.synchronize()
+    assert np.all(bits(C) == 0)
+    # M == 0 and N == 0: nothing happens
+    tlg.gemm_relu(torch.empty((0, 4), dtype=torch.float16, device=dev),
+                  torch.ones((4, 3), dtype=torch.float16, device=dev))
+    tlg.gemm_relu(torch.ones((3, 4), dtype=torch.float16, device=dev),
+                  torch.empty((4, 0), dtype=torch.float16, device=dev))
+    # K == 1, M == 1, N == 1
+    for (M, N, K) in [(1, 1, 1), (1, 300, 1), (300, 1, 7), (1, 8, 4096), (4096, 8, 8)]:
+        A, B = wl.make_random(M, N, K, seed=M * 7 + N, kind="integer")
+        for v in variants_for(M, N, K):
+            assert np.array_equal(bits(run(A, B, dev, variant=v)), oracle.gemm_relu(A, B)), (M, N, K, v)
+
+
+def test_worked_examples_on_gpu(dev):
+    """The hand-worked fixtures (overflow to inf, subnormal outputs, ties) through the naive and tiled paths."""
+    from test_oracle_pins import _parse_worked
+    for case in _parse_worked():
+        M, N, K = case["M"], case["N"], case["K"]
+        if K == 0:
+            continue
+        A = case["A"].reshape(M, K).view(np.float16)
+        B = case["B"].reshape(K, N).view(np.float16)
+        want = case["C"].reshape(M, N)
+        assert np.array_equal(bits(run(A, B, dev, variant=V_NAIVE)), want), case["name"]
+        got = bits(run(A, B, dev, variant=V_GEN))
+        if case["name"] != "ascending_order_tie":  # the only case whose bits depend on the summation order
+            assert np.array_equal(got, want), case["name"]
+
+
+# ---------------------------------------------------------------- determinism, streams, errors
+
+def test_run_twice_identical(dev):
+    for name in ["square4096", "skinny16x14336x4096"]:
+        A, B = wl.make_inputs(name)
+        Ad, Bd = to_dev(A, dev), to_dev(B, dev)
+        c1 = tlg.gemm_relu(Ad, Bd)
+        c2 = tlg.gemm_relu(Ad, Bd)
+        torch.cuda.synchronize()
+        assert torch.equal(c1.view(torch.int16), c2.view(torch.int16)), name
+
+
+def test_nondefault_stream_ordering(dev):
+    """Work is enqueued on the caller's stream, after what precedes it there."""
+    M, N, K = 512, 512, 512
+    A, B = wl.make_random(M, N, K, seed=3, kind="integer")
+    A2, _ = wl.make_random(M, N, K, seed=4, kind="integer")
+    s = torch.cuda.Stream(device=dev)
+    Ad, Bd = to_dev(A, dev), to_dev(B, dev)
+    A2d = to_dev(A2, dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        Ad.copy_(A2d)  # on stream s, before the GEMM
+        C = tlg.gemm_relu(Ad, Bd)
+    s.synchronize()
+    assert np.array_equal(bits(C), oracle.gemm_relu(A2, B))
+
+
+def test_invalid_arguments_enqueue_nothing(dev):
+    from tiled_dense_gemm_06_amd import _native as nat
+    h = tlg.handle_for(dev)
+    C = torch.full((4, 4), 7.0, dtype=torch.float16, device=dev)
+    A = torch.ones((4, 4), dtype=torch.float16, device=dev)
+    st = nat.tlg_gemm_relu(h.ptr, 4, 4, 4, A.data_ptr(), 3, A.data_ptr(), 4, C.data_ptr(), 4, None)
+    assert st == nat.TLG_ERROR_INVALID_VALUE
+    st = nat.tlg_gemm_relu_variant(h.ptr, V_DMA, 0, 4, 4, 4, A.data_ptr() + 2, 4, A.data_ptr(), 4,
+                                   C.data_ptr(), 4, None)
+    assert st == nat.TLG_ERROR_NOT_SUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0)

@@ -1,0 +1,132 @@
+"""tlg: C = ReLU(A . B) on MI355X (gfx950), fp16 in, fp32 accumulation, fp16 out.
+
+The operation is the quick-start ``matmul_relu`` of the TileLang article
+(aiwiki.ai/wiki/tilelang, "Programming model"). All computation happens in
+the hand-written gfx950 kernels of ``libtlg.so`` behind the C ABI in
+``include/tlg.h``; this module only passes PyTorch device pointers, leading
+dimensions and the current stream to it. There is no CPU fallback: without
+the built library every call raises.
+"""
+from __future__ import annotations
+
+from . import _native
+from ._native import (  # noqa: F401  (re-exported C-ABI names)
+    TLG_VARIANT_AUTO, TLG_VARIANT_FILL_ZERO, TLG_VARIANT_NAIVE, TLG_VARIANT_NOOP,
+    TLG_VARIANT_SPLITK, TLG_VARIANT_TILED_DMA, TLG_VARIANT_TILED_GENERAL, TlgError,
+    tlg_arch_supported, tlg_check_args, tlg_plan, tlg_plan_config_name, tlg_status_string,
+    tlg_version, tlg_workspace_bytes,
+)
+
+__all__ = ["gemm_relu", "Handle", "handle_for", "plan"]
+
+
+class Handle:
+    """A tlg handle bound to one GPU (tlg_create / tlg_destroy)."""
+
+    def __init__(self, device=None):
+        import torch
+
+        self.device = torch.device("cuda", torch.cuda.current_device() if device is None else
+                                   torch.device(device).index or 0)
+        with torch.cuda.device(self.device):
+            self.ptr = _native.tlg_create()
+
+    def close(self):
+        if getattr(self, "ptr", None):
+            _native.tlg_destroy(self.ptr)
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_handles: dict[int, Handle] = {}
+
+
+def handle_for(device) -> Handle:
+    """The module's cached handle for a CUDA/HIP device (created on first use)."""
+    idx = device.index if device.index is not None else 0
+    h = _handles.get(idx)
+    if h is None:
+        h = Handle(device)
+        _handles[idx] = h
+    return h
+
+
+def _ld(t) -> int:
+    """Leading dimension (elements) of a row-major 2-D tensor."""
+    rows, cols = t.shape
+    if rows <= 1:
+        return max(1, cols)
+    return t.stride(0)
+
+
+def _check(t, name):
+    import torch
+
+    if t.dtype != torch.float16:
+        raise TypeError(f"{name} must be float16, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its rows (row-major)")
+    if t.shape[0] > 1 and t.stride(0) < max(1, t.shape[1]):
+        raise ValueError(f"{name} rows overlap")
+
+
+def gemm_relu(A, B, out=None, *, variant: int = TLG_VARIANT_AUTO, splits: int = 0, stream=None, handle=None):
+    """C = ReLU(A @ B) for fp16 row-major A (M, K) and B (K, N); returns C (M, N).
+
+    ``out`` may be a preallocated fp16 (M, N) tensor (a padded row view is
+    fine: only its M x N window is written). The work is enqueued on
+    ``stream`` (default: the current stream of A's device) and is
+    asynchronous. ``variant``/``splits`` force a kernel family (tests).
+    """
+    import torch
+
+    _check(A, "A")
+    _check(B, "B")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if A.device != B.device:
+        raise ValueError("A and B are on different devices")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    else:
+        _check(out, "out")
+        if tuple(out.shape) != (M, N) or out.device != A.device:
+            raise ValueError("out has the wrong shape or device")
+    h = handle if handle is not None else handle_for(A.device)
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    with torch.cuda.device(A.device):
+        st = _native.tlg_gemm_relu_variant(h.ptr, variant, splits, M, N, K, A.data_ptr(), _ld(A),
+                                           B.data_ptr(), _ld(B), out.data_ptr(), _ld(out), s.cuda_stream)
+    if st != _native.TLG_SUCCESS:
+        raise TlgError(st, "tlg_gemm_relu")
+    return out
+
+
+def plan(M, N, K, lda=None, ldb=None, ldc=None, *, aligned: bool = True, variant: int = TLG_VARIANT_AUTO,
+         splits: int = 0) -> dict:
+    """What gemm_relu would launch for a problem (host logic only, no GPU).
+
+    Pointers are stand-ins: 16-byte aligned when ``aligned`` else 2-byte aligned.
+    """
+    lda = max(1, K) if lda is None else lda
+    ldb = max(1, N) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    base = 1 << 20 if aligned else (1 << 20) + 2
+    st, info = _native.tlg_plan(M, N, K, base, lda, base, ldb, base, ldc, variant, splits)
+    if st != _native.TLG_SUCCESS:
+        raise TlgError(st, "tlg_plan")
+    d = info.as_dict()
+    d["variant_name"] = _native.VARIANT_NAMES.get(info.variant, "?")
+    d["config_name"] = _native.tlg_plan_config_name(info.variant, info.config)
+    return d

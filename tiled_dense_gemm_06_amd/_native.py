@@ -1,0 +1,141 @@
+"""ctypes binding of include/tlg.h: the same entry points under the same
+names, argument marshalling only. Every step of the computation runs in the
+library's gfx950 kernels; if the library is missing this module raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtlg.so")
+
+# tlg_status
+TLG_SUCCESS = 0
+TLG_ERROR_INVALID_VALUE = 1
+TLG_ERROR_NOT_SUPPORTED = 2
+TLG_ERROR_OUT_OF_MEMORY = 3
+TLG_ERROR_HIP = 4
+
+# tlg_variant
+TLG_VARIANT_AUTO = 0
+TLG_VARIANT_NOOP = 1
+TLG_VARIANT_FILL_ZERO = 2
+TLG_VARIANT_TILED_DMA = 3
+TLG_VARIANT_TILED_GENERAL = 4
+TLG_VARIANT_SPLITK = 5
+TLG_VARIANT_NAIVE = 6
+
+VARIANT_NAMES = {
+    TLG_VARIANT_AUTO: "auto", TLG_VARIANT_NOOP: "noop", TLG_VARIANT_FILL_ZERO: "fill_zero",
+    TLG_VARIANT_TILED_DMA: "tiled_dma", TLG_VARIANT_TILED_GENERAL: "tiled_general",
+    TLG_VARIANT_SPLITK: "splitk", TLG_VARIANT_NAIVE: "naive",
+}
+
+
+class tlg_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("variant", ctypes.c_int32), ("config", ctypes.c_int32),
+        ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
+        ("threads", ctypes.c_int32), ("splits", ctypes.c_int32), ("kernels", ctypes.c_int32),
+        ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class TlgError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {tlg_status_string(status)}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libtlg.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"tlg native library not found at {LIB_PATH}; build it first "
+                               "(python -m tiled_dense_gemm_06_amd.build or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        L.tlg_create.argtypes = [ctypes.POINTER(p)]
+        L.tlg_create.restype = i32
+        L.tlg_destroy.argtypes = [p]
+        L.tlg_destroy.restype = i32
+        L.tlg_gemm_relu.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p]
+        L.tlg_gemm_relu.restype = i32
+        L.tlg_gemm_relu_variant.argtypes = [p, i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, p]
+        L.tlg_gemm_relu_variant.restype = i32
+        L.tlg_check_args.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
+        L.tlg_check_args.restype = i32
+        L.tlg_plan.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i32, i32, i64,
+                               ctypes.POINTER(tlg_plan_info)]
+        L.tlg_plan.restype = i32
+        L.tlg_plan_config_name.argtypes = [i32, i32]
+        L.tlg_plan_config_name.restype = ctypes.c_char_p
+        L.tlg_workspace_bytes.argtypes = []
+        L.tlg_workspace_bytes.restype = i64
+        L.tlg_arch_supported.argtypes = [ctypes.c_char_p]
+        L.tlg_arch_supported.restype = i32
+        L.tlg_status_string.argtypes = [i32]
+        L.tlg_status_string.restype = ctypes.c_char_p
+        L.tlg_version.argtypes = []
+        L.tlg_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def tlg_create() -> int:
+    h = ctypes.c_void_p()
+    st = lib().tlg_create(ctypes.byref(h))
+    if st != TLG_SUCCESS:
+        raise TlgError(st, "tlg_create")
+    return h.value
+
+
+def tlg_destroy(h: int) -> int:
+    return lib().tlg_destroy(h)
+
+
+def tlg_gemm_relu(h, M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
+    return lib().tlg_gemm_relu(h, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def tlg_gemm_relu_variant(h, variant, splits, M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
+    return lib().tlg_gemm_relu_variant(h, variant, splits, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def tlg_check_args(M, N, K, A, lda, B, ldb, C, ldc) -> int:
+    return lib().tlg_check_args(M, N, K, A, lda, B, ldb, C, ldc)
+
+
+def tlg_plan(M, N, K, A, lda, B, ldb, C, ldc, variant=TLG_VARIANT_AUTO, splits=0, workspace_cap=None):
+    """Returns (status, tlg_plan_info)."""
+    info = tlg_plan_info()
+    cap = tlg_workspace_bytes() if workspace_cap is None else workspace_cap
+    st = lib().tlg_plan(M, N, K, A, lda, B, ldb, C, ldc, variant, splits, cap, ctypes.byref(info))
+    return st, info
+
+
+def tlg_plan_config_name(variant: int, config: int) -> str:
+    return lib().tlg_plan_config_name(variant, config).decode()
+
+
+def tlg_workspace_bytes() -> int:
+    return int(lib().tlg_workspace_bytes())
+
+
+def tlg_arch_supported(name: str) -> bool:
+    return bool(lib().tlg_arch_supported(name.encode()))
+
+
+def tlg_status_string(status: int) -> str:
+    return lib().tlg_status_string(status).decode()
+
+
+def tlg_version() -> int:
+    return int(lib().tlg_version())

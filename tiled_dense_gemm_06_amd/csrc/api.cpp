@@ -1,0 +1,304 @@
+// C ABI of the tlg library: handle, argument checks, kernel choice, launch.
+// The operation is the quick-start `matmul_relu` of the TileLang article
+// (aiwiki.ai/wiki/tilelang, "Programming model"); see include/tlg.h for the
+// contract of every entry point.
+#include "tlg.h"
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "kernels.h"
+
+struct tlg_context {
+    int device;
+    float *workspace;
+    int64_t workspace_bytes;
+};
+
+namespace {
+
+constexpr int32_t kVersion = 100;  // 0.1.0
+// fp32 split-K partials: 32 MiB covers S x M x N x 4 bytes for the skinny
+// shapes the split path serves (S is lowered when a shape needs more).
+constexpr int64_t kWorkspaceBytes = 32ll << 20;
+// Largest in-tile byte offset a buffer load may use (see the kernels).
+constexpr int64_t kMaxOffset = 0x7ffffff0ll - 16;
+constexpr int64_t kMaxDim = (1ll << 31) - 1024;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Conditions for the direct-to-LDS kernels: 16-byte aligned pointers,
+// leading dimensions, K and N multiples of 8 (so every 16-byte chunk lies
+// wholly inside or wholly outside the matrix), and in-tile offsets that fit
+// a buffer descriptor.
+bool dma_ok(const tlg::Problem &p, int bm, int bn, int bk) {
+    if (!aligned(p.A, 16) || !aligned(p.B, 16) || !aligned(p.C, 16)) return false;
+    if (p.lda % 8 || p.ldb % 8 || p.ldc % 8 || p.K % 8 || p.N % 8) return false;
+    if ((int64_t)bm * p.lda * 2 > kMaxOffset) return false;  // A tile loads
+    if ((int64_t)bk * p.ldb * 2 > kMaxOffset) return false;  // B tile loads
+    if ((int64_t)bm * p.ldc * 2 + (int64_t)bn * 2 > kMaxOffset) return false;  // C tile stores
+    if ((int64_t)bm * p.N * 4 + (int64_t)bn * 4 > kMaxOffset) return false;    // split-K partial stores
+    return true;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+void fill_info(tlg_plan_info *o, int variant, int config, const tlg::TileConfig *tc, int splits, int kernels,
+               int64_t grid, int64_t ws) {
+    memset(o, 0, sizeof *o);
+    o->variant = variant;
+    o->config = config;
+    if (tc) {
+        o->block_m = tc->bm;
+        o->block_n = tc->bn;
+        o->block_k = tc->bk;
+        o->threads = tc->threads;
+    }
+    o->splits = splits;
+    o->kernels = kernels;
+    o->grid = grid;
+    o->workspace_bytes = ws;
+}
+
+// Split count for the skinny path: enough work-groups to give every CU about
+// two, each split at least two K steps long, partials within the workspace.
+bool choose_splits(const tlg::Problem &p, const tlg::TileConfig &tc, int32_t forced, int64_t cap, int *splits_out,
+                   int64_t *k_split_out) {
+    const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
+    const int64_t ksteps = ceil_div(p.K, tc.bk);
+    int64_t s;
+    if (forced > 0) {
+        s = forced;
+    } else {
+        s = ceil_div(512, tiles);
+        if (s > 16) s = 16;
+        if (s > ksteps / 2) s = ksteps / 2;
+        if (s < 1) s = 1;
+    }
+    if (s > ksteps) s = ksteps > 0 ? ksteps : 1;
+    const int64_t per_split = p.M * p.N * 4;
+    if (per_split > 0 && s * per_split > cap) s = cap / per_split;
+    if (s < 1) return false;
+    // splits cover K in whole K steps; recompute the count so none is empty
+    int64_t k_split = ceil_div(ksteps, s) * tc.bk;
+    if (k_split <= 0) k_split = tc.bk;
+    s = p.K > 0 ? ceil_div(p.K, k_split) : 1;
+    *splits_out = (int)s;
+    *k_split_out = k_split;
+    return true;
+}
+
+tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t splits, int64_t cap, tlg_plan_info *o,
+                     int64_t *k_split_out) {
+    *k_split_out = 0;
+    if (variant < TLG_VARIANT_AUTO || variant > TLG_VARIANT_NAIVE) return TLG_ERROR_INVALID_VALUE;
+    if (p.M == 0 || p.N == 0) {
+        fill_info(o, TLG_VARIANT_NOOP, 0, nullptr, 1, 0, 0, 0);
+        return TLG_SUCCESS;
+    }
+    if (variant == TLG_VARIANT_NOOP) return TLG_ERROR_NOT_SUPPORTED;
+    if (p.M > kMaxDim || p.N > kMaxDim || p.K > kMaxDim) return TLG_ERROR_NOT_SUPPORTED;
+    if (variant == TLG_VARIANT_AUTO && p.K == 0) variant = TLG_VARIANT_FILL_ZERO;
+    if (variant == TLG_VARIANT_FILL_ZERO) {
+        if (p.K != 0) return TLG_ERROR_NOT_SUPPORTED;
+        int64_t blocks = ceil_div(p.M * p.N, 256);
+        if (blocks > 65536) blocks = 65536;
+        fill_info(o, TLG_VARIANT_FILL_ZERO, 0, nullptr, 1, 1, blocks, 0);
+        return TLG_SUCCESS;
+    }
+    if (variant == TLG_VARIANT_NAIVE) {
+        if (ceil_div(p.M, 16) > 65535) return TLG_ERROR_NOT_SUPPORTED;
+        fill_info(o, TLG_VARIANT_NAIVE, 0, nullptr, 1, 1, ceil_div(p.M, 16) * ceil_div(p.N, 16), 0);
+        o->threads = 256;
+        return TLG_SUCCESS;
+    }
+
+    // split-K for skinny M
+    if (variant == TLG_VARIANT_SPLITK || (variant == TLG_VARIANT_AUTO && p.M <= 64 && p.K >= 512)) {
+        const int cfg = tlg::SPLIT_32x128x64;
+        const tlg::TileConfig &tc = tlg::kSplitConfigs[cfg];
+        int s = 1;
+        int64_t k_split = 0;
+        bool ok = dma_ok(p, tc.bm, tc.bn, tc.bk) && choose_splits(p, tc, splits, cap, &s, &k_split);
+        if (ok && (s > 1 || variant == TLG_VARIANT_SPLITK)) {
+            const int64_t grid = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn) * s;
+            fill_info(o, TLG_VARIANT_SPLITK, cfg, &tc, s, 2, grid, (int64_t)s * p.M * p.N * 4);
+            *k_split_out = k_split;
+            return TLG_SUCCESS;
+        }
+        if (variant == TLG_VARIANT_SPLITK) return TLG_ERROR_NOT_SUPPORTED;
+    }
+
+    if (variant == TLG_VARIANT_TILED_DMA || variant == TLG_VARIANT_AUTO) {
+        int cfg;
+        const int64_t t256 = ceil_div(p.M, 256) * ceil_div(p.N, 256);
+        const int64_t t128 = ceil_div(p.M, 128) * ceil_div(p.N, 128);
+        if (t256 >= 224)
+            cfg = tlg::DMA_256x256x32;
+        else if (t128 >= 192)
+            cfg = tlg::DMA_128x128x32;
+        else
+            cfg = tlg::DMA_64x64x64;
+        const tlg::TileConfig &tc = tlg::kDmaConfigs[cfg];
+        if (dma_ok(p, tc.bm, tc.bn, tc.bk)) {
+            fill_info(o, TLG_VARIANT_TILED_DMA, cfg, &tc, 1, 1, ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn), 0);
+            return TLG_SUCCESS;
+        }
+        if (variant == TLG_VARIANT_TILED_DMA) return TLG_ERROR_NOT_SUPPORTED;
+    }
+
+    // TLG_VARIANT_TILED_GENERAL, or AUTO on data the DMA kernels cannot take
+    const int cfg = ceil_div(p.M, 128) * ceil_div(p.N, 128) >= 192 ? tlg::GEN_128x128x32 : tlg::GEN_64x64x32;
+    const tlg::TileConfig &tc = tlg::kGenConfigs[cfg];
+    fill_info(o, TLG_VARIANT_TILED_GENERAL, cfg, &tc, 1, 1, ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn), 0);
+    return TLG_SUCCESS;
+}
+
+tlg::Problem make_problem(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
+                          const void *C, int64_t ldc) {
+    tlg::Problem p;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.A = A;
+    p.lda = lda;
+    p.B = B;
+    p.ldb = ldb;
+    p.C = const_cast<void *>(C);
+    p.ldc = ldc;
+    return p;
+}
+
+tlg_status run(tlg_handle h, int32_t variant, int32_t splits, const tlg::Problem &p, hipStream_t stream) {
+    if (!h) return TLG_ERROR_INVALID_VALUE;
+    tlg_status st = tlg_check_args(p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc);
+    if (st != TLG_SUCCESS) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return TLG_ERROR_HIP;
+    if (dev != h->device) return TLG_ERROR_INVALID_VALUE;  // the handle's device must be current
+    tlg_plan_info info;
+    int64_t k_split = 0;
+    st = plan_impl(p, variant, splits, h->workspace_bytes, &info, &k_split);
+    if (st != TLG_SUCCESS) return st;
+    hipError_t e = hipSuccess;
+    switch (info.variant) {
+        case TLG_VARIANT_NOOP: return TLG_SUCCESS;
+        case TLG_VARIANT_FILL_ZERO: e = tlg::launch_fill_zero(p, stream); break;
+        case TLG_VARIANT_NAIVE: e = tlg::launch_naive(p, stream); break;
+        case TLG_VARIANT_TILED_DMA: e = tlg::launch_tiled_dma(info.config, p, stream); break;
+        case TLG_VARIANT_TILED_GENERAL: e = tlg::launch_tiled_general(info.config, p, stream); break;
+        case TLG_VARIANT_SPLITK:
+            e = tlg::launch_splitk(info.config, info.splits, k_split, p, h->workspace, stream);
+            break;
+        default: return TLG_ERROR_NOT_SUPPORTED;
+    }
+    return e == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+tlg_status tlg_check_args(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
+                          const void *C, int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0) return TLG_ERROR_INVALID_VALUE;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1)) return TLG_ERROR_INVALID_VALUE;
+    if (M == 0 || N == 0) return TLG_SUCCESS;  // nothing is read or written
+    if (!C || !aligned(C, 2)) return TLG_ERROR_INVALID_VALUE;
+    if (K > 0) {
+        if (!A || !B || !aligned(A, 2) || !aligned(B, 2)) return TLG_ERROR_INVALID_VALUE;
+    }
+    return TLG_SUCCESS;
+}
+
+tlg_status tlg_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
+                    const void *C, int64_t ldc, int32_t variant, int32_t splits, int64_t workspace_cap_bytes,
+                    tlg_plan_info *out) {
+    if (!out) return TLG_ERROR_INVALID_VALUE;
+    tlg_status st = tlg_check_args(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != TLG_SUCCESS) return st;
+    tlg::Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc);
+    int64_t k_split = 0;
+    return plan_impl(p, variant, splits, workspace_cap_bytes, out, &k_split);
+}
+
+const char *tlg_plan_config_name(int32_t variant, int32_t config) {
+    switch (variant) {
+        case TLG_VARIANT_TILED_DMA:
+            return (config >= 0 && config < tlg::DMA_CONFIGS) ? tlg::kDmaConfigs[config].name : "";
+        case TLG_VARIANT_TILED_GENERAL:
+            return (config >= 0 && config < tlg::GEN_CONFIGS) ? tlg::kGenConfigs[config].name : "";
+        case TLG_VARIANT_SPLITK:
+            return (config >= 0 && config < tlg::SPLIT_CONFIGS) ? tlg::kSplitConfigs[config].name : "";
+        case TLG_VARIANT_NAIVE: return "naive_16x16";
+        case TLG_VARIANT_FILL_ZERO: return "fill_zero";
+        case TLG_VARIANT_NOOP: return "noop";
+        default: return "";
+    }
+}
+
+int64_t tlg_workspace_bytes(void) { return kWorkspaceBytes; }
+
+int32_t tlg_arch_supported(const char *name) {
+    if (!name) return 0;
+    // "gfx950" exactly, or followed by ':' feature flags
+    return strncmp(name, "gfx950", 6) == 0 && (name[6] == '\0' || name[6] == ':') ? 1 : 0;
+}
+
+tlg_status tlg_create(tlg_handle *out) {
+    if (!out) return TLG_ERROR_INVALID_VALUE;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return TLG_ERROR_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TLG_ERROR_HIP;
+    if (!tlg_arch_supported(prop.gcnArchName)) return TLG_ERROR_NOT_SUPPORTED;
+    tlg_context *ctx = new (std::nothrow) tlg_context;
+    if (!ctx) return TLG_ERROR_OUT_OF_MEMORY;
+    ctx->device = dev;
+    ctx->workspace_bytes = kWorkspaceBytes;
+    ctx->workspace = nullptr;
+    if (hipMalloc((void **)&ctx->workspace, (size_t)kWorkspaceBytes) != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky allocation error
+        delete ctx;
+        return TLG_ERROR_OUT_OF_MEMORY;
+    }
+    *out = ctx;
+    return TLG_SUCCESS;
+}
+
+tlg_status tlg_destroy(tlg_handle h) {
+    if (!h) return TLG_SUCCESS;
+    hipError_t e = hipSuccess;
+    if (h->workspace) e = hipFree(h->workspace);
+    delete h;
+    return e == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
+}
+
+tlg_status tlg_gemm_relu(tlg_handle h, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                         int64_t ldb, void *C, int64_t ldc, hipStream_t stream) {
+    return run(h, TLG_VARIANT_AUTO, 0, make_problem(M, N, K, A, lda, B, ldb, C, ldc), stream);
+}
+
+tlg_status tlg_gemm_relu_variant(tlg_handle h, int32_t variant, int32_t splits, int64_t M, int64_t N, int64_t K,
+                                 const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
+                                 hipStream_t stream) {
+    return run(h, variant, splits, make_problem(M, N, K, A, lda, B, ldb, C, ldc), stream);
+}
+
+const char *tlg_status_string(tlg_status s) {
+    switch (s) {
+        case TLG_SUCCESS: return "TLG_SUCCESS";
+        case TLG_ERROR_INVALID_VALUE: return "TLG_ERROR_INVALID_VALUE: an argument is out of range";
+        case TLG_ERROR_NOT_SUPPORTED: return "TLG_ERROR_NOT_SUPPORTED: the device or request is not supported";
+        case TLG_ERROR_OUT_OF_MEMORY: return "TLG_ERROR_OUT_OF_MEMORY: device memory allocation failed";
+        case TLG_ERROR_HIP: return "TLG_ERROR_HIP: the HIP runtime reported an error";
+        default: return "unknown tlg_status";
+    }
+}
+
+int32_t tlg_version(void) { return kVersion; }
+
+}  // extern "C"

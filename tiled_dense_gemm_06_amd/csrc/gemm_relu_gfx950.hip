@@ -1,0 +1,527 @@
+// gfx950 (MI355X, CDNA4) kernels for C = ReLU(A . B), fp16 in, fp32
+// accumulation, fp16 out: the quick-start kernel of the TileLang article
+// (aiwiki.ai/wiki/tilelang, "Programming model").
+//
+// What each kernel keeps of that kernel, and what it does differently:
+//  * one work-group per BM x BN output tile over a ceil-divided grid, an fp32
+//    accumulator cleared at the start, a K loop over LDS tiles of A and B,
+//    ReLU applied to the fp32 accumulator, then the cast to fp16 (as in the
+//    listing);
+//  * the multi-stage pipeline (T.Pipelined in the listing) is built from
+//    buffer_load_dwordx4 ... lds, which moves 16 bytes per lane from global
+//    memory straight into LDS with no register staging; a stage's loads are
+//    waited for with s_waitcnt vmcnt, so STAGES-1 tiles are in flight while
+//    one is being multiplied;
+//  * out-of-range rows, columns and k are zero-filled by giving those lanes
+//    an out-of-range buffer offset (the hardware then writes zeros);
+//  * LDS tiles are XOR-swizzled at 16-byte granularity (the bank-conflict
+//    minimising layouts of the article's T.gemm), with swizzles chosen for
+//    the 64-bank LDS of gfx950 (tile_layout.h);
+//  * T.gemm becomes v_mfma_f32_32x32x16_f16; the B operand, which is
+//    N-contiguous in memory, is transposed on the way out of LDS with
+//    ds_read_b64_tr_b16;
+//  * the grid order (T.use_swizzle in the article) is XCD-aware and grouped
+//    along M so co-resident work-groups share A rows and B columns in L2;
+//  * for skinny M a split-K variant (two stages: fp32 partials, then an
+//    ordered reduce + ReLU + cast), the two-stage split-K the article reports
+//    SGLang using for small-batch decoding ("Adoption by DeepSeek").
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "tile_layout.h"
+
+namespace tlg {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T) __attribute__((address_space(3))) T *
+
+// Every buffer descriptor covers offsets [0, kRange); a lane given offset
+// kOOB reads zeros. Host code guarantees every real offset is below kRange.
+constexpr uint32_t kRange = 0x7ffffff0u;
+constexpr uint32_t kOOB = 0x7ffffff0u;
+
+struct KArgs {
+    const _Float16 *A;
+    const _Float16 *B;
+    _Float16 *C;
+    float *W;          // split-K partials (split-K kernels only)
+    int M, N, K;
+    int64_t lda, ldb, ldc;
+    int tiles_m, tiles_n, group_m;
+    int k_split;       // K elements per split, a multiple of BK
+};
+
+typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef int int2_t __attribute__((ext_vector_type(2)));
+
+// Buffer descriptor: base address, stride 0, kRange bytes, word 3 = 0x00020000
+// (raw, untyped buffer on gfx9-class parts).
+__device__ __forceinline__ int4_t make_srd(const void *base) {
+    const uint64_t p = (uint64_t)base;
+    int4_t r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xffffu));
+    r[2] = (int)kRange;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from buffer offset `voff` into LDS at lds_base + 16*lane.
+// Issued through inline assembly: the compiler does not see an LDS write here,
+// so it does not add its own conservative vmcnt(0) wait before every later
+// LDS read. The kernels wait for these loads themselves (wait_vmcnt) before
+// the barrier that publishes a stage. M0 needs one wait state after its write.
+__device__ __forceinline__ void dma16(int4_t srd, uint32_t lds_base, uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base),
+        "v"(voff), "s"(srd)
+        : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// All LDS operations of this wave are complete, then the work-group barrier.
+// The "memory" clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ReLU on the fp32 accumulator (everything not > 0 becomes +0, so -0 and NaN
+// give +0), then the fp16 conversion, which rounds to nearest even.
+__device__ __forceinline__ _Float16 relu_to_half(float x) { return (_Float16)(x > 0.0f ? x : 0.0f); }
+
+__device__ __forceinline__ half8_t read_b_frag(LDS_PTR(const char) base, int off_lo, int off_hi) {
+    short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(short4_t))(base + off_lo));
+    short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(short4_t))(base + off_hi));
+    short8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(half8_t, v);
+}
+
+// The tile product of one LDS stage: for each 16-wide k-step, read the
+// operand fragments of every MFMA tile of this wave and accumulate.
+template <class S>
+__device__ __forceinline__ void mma_stage(LDS_PTR(const char) sA, LDS_PTR(const char) sB, int wm0, int wn0, int lane,
+                                          float16_t (&acc)[S::TN][S::TM]) {
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; ++s) {
+        half8_t bf[S::TN], af[S::TM];
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn)
+            bf[tn] = read_b_frag(sB, frag_b_offset<S>(wn0, tn, s, 0, lane), frag_b_offset<S>(wn0, tn, s, 1, lane));
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm)
+            af[tm] = *(LDS_PTR(const half8_t))(sA + frag_a_offset<S>(wm0, tm, s, lane));
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+            for (int tm = 0; tm < S::TM; ++tm)
+                acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[tn], af[tm], acc[tn][tm], 0, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel fed by direct global->LDS loads. Requirements (checked on the
+// host): A, B, C (and W) 16-byte aligned; lda, ldb, ldc, K and N multiples of
+// 8; every in-tile byte offset below kRange. With SPLIT, blockIdx.y is the
+// K split and fp32 partials go to W instead of C.
+// ---------------------------------------------------------------------------
+template <class S, bool SPLIT>
+__global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[S::LDS_BYTES];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
+
+    const int nwg = a.tiles_m * a.tiles_n;
+    int tm_idx, tn_idx;
+    grouped_tile(xcd_remap(blockIdx.x, nwg), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
+    const int m0 = tm_idx * S::BM, n0 = tn_idx * S::BN;
+    const int kbeg = SPLIT ? (int)blockIdx.y * a.k_split : 0;
+    const int kend = SPLIT ? imin(a.K, kbeg + a.k_split) : a.K;
+    const int nk = kend > kbeg ? (kend - kbeg + S::BK - 1) / S::BK : 0;
+
+    // Per-lane load descriptors (constant over the K loop).
+    uint32_t a_off[S::DMA_A];
+    int a_col[S::DMA_A];
+    bool a_ok[S::DMA_A];
+#pragma unroll
+    for (int i = 0; i < S::DMA_A; ++i) {
+        ChunkRef c = dma_a_chunk<S>(wave, i, lane);
+        a_off[i] = (uint32_t)(c.row * a.lda * 2 + c.chunk * 16);
+        a_col[i] = 8 * c.chunk;
+        a_ok[i] = m0 + c.row < a.M;
+    }
+    uint32_t b_off[S::DMA_B];
+    int b_row[S::DMA_B];
+    bool b_ok[S::DMA_B];
+#pragma unroll
+    for (int i = 0; i < S::DMA_B; ++i) {
+        ChunkRef c = dma_b_chunk<S>(wave, i, lane);
+        b_off[i] = (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16);
+        b_row[i] = c.row;
+        b_ok[i] = n0 + 8 * c.chunk < a.N;
+    }
+
+    LDS_PTR(char) lds = (LDS_PTR(char))smem;
+
+    auto issue = [&](int kt, int buf) {
+        const int k0 = kbeg + kt * S::BK;
+        LDS_PTR(char) sA = lds + buf * S::STAGE_BYTES;
+        LDS_PTR(char) sB = sA + S::A_BYTES;
+        const int4_t ra = make_srd(a.A + (int64_t)m0 * a.lda + k0);
+        const int4_t rb = make_srd(a.B + (int64_t)k0 * a.ldb + n0);
+        const uint32_t la = (uint32_t)(uintptr_t)(sA + wave * S::DMA_A * 1024);
+        const uint32_t lb = (uint32_t)(uintptr_t)(sB + wave * S::DMA_B * 1024);
+#pragma unroll
+        for (int i = 0; i < S::DMA_A; ++i) {
+            uint32_t off = (a_ok[i] && k0 + a_col[i] < kend) ? a_off[i] : kOOB;
+            dma16(ra, la + i * 1024, off);
+        }
+#pragma unroll
+        for (int i = 0; i < S::DMA_B; ++i) {
+            uint32_t off = (b_ok[i] && k0 + b_row[i] < kend) ? b_off[i] : kOOB;
+            dma16(rb, lb + i * 1024, off);
+        }
+    };
+
+    float16_t acc[S::TN][S::TM];
+#pragma unroll
+    for (int i = 0; i < S::TN; ++i)
+#pragma unroll
+        for (int j = 0; j < S::TM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    constexpr int kLoadsPerStage = S::DMA_A + S::DMA_B;
+#pragma unroll
+    for (int s = 0; s < S::STAGES - 1; ++s)
+        if (s < nk) issue(s, s);
+
+    int buf = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        // Tile kt has landed once at most the loads of the STAGES-2 later
+        // tiles are still in flight.
+        if (kt + S::STAGES - 2 < nk)
+            wait_vmcnt<(S::STAGES - 2) * kLoadsPerStage>();
+        else
+            wait_vmcnt<0>();
+        barrier_lds();  // every wave's loads of tile kt are in LDS; tile kt-1 is no longer read
+        if (kt + S::STAGES - 1 < nk) {
+            int nb = buf == 0 ? S::STAGES - 1 : buf - 1;  // the buffer tile kt-1 used
+            issue(kt + S::STAGES - 1, nb);
+        }
+        LDS_PTR(const char) sA = lds + buf * S::STAGE_BYTES;
+        mma_stage<S>(sA, sA + S::A_BYTES, wm0, wn0, lane, acc);
+        buf = buf + 1 == S::STAGES ? 0 : buf + 1;
+    }
+
+    // Epilogue: a lane owns four consecutive n of one row m per register quad.
+    // Stores go through a buffer descriptor based at the tile's first element;
+    // lanes outside the M x N window get offset kOOB and the hardware drops
+    // their stores, so the epilogue has no divergent branches.
+    if (SPLIT) {
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            a.W + ((int64_t)blockIdx.y * a.M + m0) * a.N + n0, (short)0, (int)kRange, 0x00020000);
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+            for (int tm = 0; tm < S::TM; ++tm) {
+                const int mr = acc_m(wm0, tm, lane);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nr = acc_n(wn0, tn, 4 * q, lane);
+                    const bool ok = m0 + mr < a.M && n0 + nr < a.N;  // N % 8 == 0: n..n+3 all in range
+                    const uint32_t off = ok ? (uint32_t)((mr * a.N + nr) * 4) : kOOB;
+                    float4_t v = {acc[tn][tm][4 * q], acc[tn][tm][4 * q + 1], acc[tn][tm][4 * q + 2],
+                                  acc[tn][tm][4 * q + 3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int4_t, v), rw, off, 0, 0);
+                }
+            }
+    } else {
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(a.C + (int64_t)m0 * a.ldc + n0, (short)0,
+                                                                            (int)kRange, 0x00020000);
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+            for (int tm = 0; tm < S::TM; ++tm) {
+                const int mr = acc_m(wm0, tm, lane);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nr = acc_n(wn0, tn, 4 * q, lane);
+                    const bool ok = m0 + mr < a.M && n0 + nr < a.N;
+                    const uint32_t off = ok ? (uint32_t)((mr * a.ldc + nr) * 2) : kOOB;
+                    half4_t h = {relu_to_half(acc[tn][tm][4 * q]), relu_to_half(acc[tn][tm][4 * q + 1]),
+                                 relu_to_half(acc[tn][tm][4 * q + 2]), relu_to_half(acc[tn][tm][4 * q + 3])};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(int2_t, h), rc, off, 0, 0);
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel fed through registers: any alignment, any leading dimension,
+// any M, N, K. Each thread gathers 16-byte chunks element by element with
+// bounds checks (out-of-range elements are 0) and writes them to the same
+// swizzled LDS layout; two LDS buffers, the next tile's loads in flight
+// during the current tile's MFMAs.
+// ---------------------------------------------------------------------------
+template <class S>
+__global__ __launch_bounds__(S::NT) void k_tiled_general(const KArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * S::STAGE_BYTES];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
+
+    const int nwg = a.tiles_m * a.tiles_n;
+    int tm_idx, tn_idx;
+    grouped_tile(xcd_remap(blockIdx.x, nwg), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
+    const int m0 = tm_idx * S::BM, n0 = tn_idx * S::BN;
+    const int nk = (a.K + S::BK - 1) / S::BK;
+
+    LDS_PTR(char) lds = (LDS_PTR(char))smem;
+    half8_t ra[S::JA], rb[S::JB];
+
+    auto gload = [&](int kt) {
+        const int k0 = kt * S::BK;
+#pragma unroll
+        for (int j = 0; j < S::JA; ++j) {
+            ChunkRef c = reg_a_chunk<S>(tid, j);
+            const int m = m0 + c.row, k = k0 + 8 * c.chunk;
+            const _Float16 *p = a.A + (int64_t)m * a.lda + k;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ra[j][e] = (m < a.M && k + e < a.K) ? p[e] : (_Float16)0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < S::JB; ++j) {
+            ChunkRef c = reg_b_chunk<S>(tid, j);
+            const int k = k0 + c.row, n = n0 + 8 * c.chunk;
+            const _Float16 *p = a.B + (int64_t)k * a.ldb + n;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rb[j][e] = (k < a.K && n + e < a.N) ? p[e] : (_Float16)0.0f;
+        }
+    };
+    auto swrite = [&](int buf) {
+        LDS_PTR(char) sA = lds + buf * S::STAGE_BYTES;
+        LDS_PTR(char) sB = sA + S::A_BYTES;
+#pragma unroll
+        for (int j = 0; j < S::JA; ++j) {
+            ChunkRef c = reg_a_chunk<S>(tid, j);
+            *(LDS_PTR(half8_t))(sA + lds_a_offset<S>(c.row, c.chunk)) = ra[j];
+        }
+#pragma unroll
+        for (int j = 0; j < S::JB; ++j) {
+            ChunkRef c = reg_b_chunk<S>(tid, j);
+            *(LDS_PTR(half8_t))(sB + lds_b_offset<S>(c.row, c.chunk)) = rb[j];
+        }
+    };
+
+    float16_t acc[S::TN][S::TM];
+#pragma unroll
+    for (int i = 0; i < S::TN; ++i)
+#pragma unroll
+        for (int j = 0; j < S::TM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    if (nk > 0) {
+        gload(0);
+        swrite(0);
+        barrier_lds();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload(kt + 1);
+        LDS_PTR(const char) sA = lds + buf * S::STAGE_BYTES;
+        mma_stage<S>(sA, sA + S::A_BYTES, wm0, wn0, lane, acc);
+        if (kt + 1 < nk) swrite(buf ^ 1);
+        barrier_lds();
+    }
+
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm) {
+            const int m = m0 + acc_m(wm0, tm, lane);
+            if (m >= a.M) continue;
+            _Float16 *crow = a.C + (int64_t)m * a.ldc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = n0 + acc_n(wn0, tn, r, lane);
+                if (n < a.N) crow[n] = relu_to_half(acc[tn][tm][r]);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K stage 2: C[m][n] = rne16(relu(sum over s ascending of W[s][m][n])).
+// Four consecutive n per thread; N % 4 == 0, ldc % 4 == 0, C 8-byte aligned.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ W, int splits, int M, int N,
+                                                       _Float16 *__restrict__ C, int64_t ldc) {
+    const int64_t mn = (int64_t)M * N;
+    const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (idx >= mn) return;
+    float4_t acc = *(const float4_t *)(W + idx);
+    for (int s = 1; s < splits; ++s) {
+        float4_t v = *(const float4_t *)(W + s * mn + idx);
+        acc[0] = acc[0] + v[0];
+        acc[1] = acc[1] + v[1];
+        acc[2] = acc[2] + v[2];
+        acc[3] = acc[3] + v[3];
+    }
+    const int m = (int)(idx / N), n = (int)(idx % N);
+    half4_t h = {relu_to_half(acc[0]), relu_to_half(acc[1]), relu_to_half(acc[2]), relu_to_half(acc[3])};
+    *(half4_t *)(C + (int64_t)m * ldc + n) = h;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-check kernel: one thread per output, k ascending, fp32 accumulator.
+// fp16 x fp16 products are exact in fp32, so a fused or unfused multiply-add
+// gives the same bits and this kernel reproduces the sequential definition
+// exactly.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_naive(const KArgs a) {
+    const int n = blockIdx.x * 16 + (threadIdx.x & 15);
+    const int m = blockIdx.y * 16 + (threadIdx.x >> 4);
+    if (m >= a.M || n >= a.N) return;
+    const _Float16 *arow = a.A + (int64_t)m * a.lda;
+    float acc = 0.0f;
+    for (int k = 0; k < a.K; ++k) acc = __builtin_fmaf((float)arow[k], (float)a.B[(int64_t)k * a.ldb + n], acc);
+    a.C[(int64_t)m * a.ldc + n] = relu_to_half(acc);
+}
+
+// K == 0: the empty sum is +0 and ReLU keeps it.
+__global__ __launch_bounds__(256) void k_fill_zero(_Float16 *C, int M, int N, int64_t ldc) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256)
+        C[(i / N) * ldc + (i % N)] = (_Float16)0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Configurations and launchers
+// ---------------------------------------------------------------------------
+using Dma256 = TileShape<256, 256, 32, 2, 2, 4>;
+using Dma128 = TileShape<128, 128, 32, 2, 2, 4>;
+using Dma64 = TileShape<64, 64, 64, 2, 2, 3>;
+using Gen128 = TileShape<128, 128, 32, 2, 2, 2>;
+using Gen64 = TileShape<64, 64, 32, 2, 2, 2>;
+using Split32x128 = TileShape<32, 128, 64, 1, 4, 4>;
+using Split32x256 = TileShape<32, 256, 64, 1, 4, 3>;
+
+const TileConfig kDmaConfigs[DMA_CONFIGS] = {
+    {Dma256::BM, Dma256::BN, Dma256::BK, Dma256::NT, Dma256::STAGES, "dma_256x256x32_w2x2_s4"},
+    {Dma128::BM, Dma128::BN, Dma128::BK, Dma128::NT, Dma128::STAGES, "dma_128x128x32_w2x2_s4"},
+    {Dma64::BM, Dma64::BN, Dma64::BK, Dma64::NT, Dma64::STAGES, "dma_64x64x64_w2x2_s3"},
+};
+const TileConfig kGenConfigs[GEN_CONFIGS] = {
+    {Gen128::BM, Gen128::BN, Gen128::BK, Gen128::NT, 2, "gen_128x128x32_w2x2"},
+    {Gen64::BM, Gen64::BN, Gen64::BK, Gen64::NT, 2, "gen_64x64x32_w2x2"},
+};
+const TileConfig kSplitConfigs[SPLIT_CONFIGS] = {
+    {Split32x128::BM, Split32x128::BN, Split32x128::BK, Split32x128::NT, Split32x128::STAGES,
+     "splitk_32x128x64_w1x4_s4"},
+    {Split32x256::BM, Split32x256::BN, Split32x256::BK, Split32x256::NT, Split32x256::STAGES,
+     "splitk_32x256x64_w1x4_s3"},
+};
+
+static KArgs make_args(const Problem &p) {
+    KArgs a;
+    a.A = (const _Float16 *)p.A;
+    a.B = (const _Float16 *)p.B;
+    a.C = (_Float16 *)p.C;
+    a.W = nullptr;
+    a.M = (int)p.M;
+    a.N = (int)p.N;
+    a.K = (int)p.K;
+    a.lda = p.lda;
+    a.ldb = p.ldb;
+    a.ldc = p.ldc;
+    a.group_m = 4;
+    a.k_split = (int)p.K;
+    return a;
+}
+
+template <class S, bool SPLIT>
+static hipError_t launch_dma_t(KArgs a, int splits, hipStream_t stream) {
+    a.tiles_m = (a.M + S::BM - 1) / S::BM;
+    a.tiles_n = (a.N + S::BN - 1) / S::BN;
+    dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits);
+    hipLaunchKernelGGL((k_tiled_dma<S, SPLIT>), grid, dim3(S::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class S>
+static hipError_t launch_gen_t(KArgs a, hipStream_t stream) {
+    a.tiles_m = (a.M + S::BM - 1) / S::BM;
+    a.tiles_n = (a.N + S::BN - 1) / S::BN;
+    hipLaunchKernelGGL((k_tiled_general<S>), dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(S::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_tiled_dma(int config, const Problem &p, hipStream_t stream) {
+    KArgs a = make_args(p);
+    switch (config) {
+        case DMA_256x256x32: return launch_dma_t<Dma256, false>(a, 1, stream);
+        case DMA_128x128x32: return launch_dma_t<Dma128, false>(a, 1, stream);
+        case DMA_64x64x64: return launch_dma_t<Dma64, false>(a, 1, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_tiled_general(int config, const Problem &p, hipStream_t stream) {
+    KArgs a = make_args(p);
+    switch (config) {
+        case GEN_128x128x32: return launch_gen_t<Gen128>(a, stream);
+        case GEN_64x64x32: return launch_gen_t<Gen64>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_splitk(int config, int splits, int64_t k_split, const Problem &p, float *workspace,
+                         hipStream_t stream) {
+    KArgs a = make_args(p);
+    a.W = workspace;
+    a.k_split = (int)k_split;
+    hipError_t e;
+    switch (config) {
+        case SPLIT_32x128x64: e = launch_dma_t<Split32x128, true>(a, splits, stream); break;
+        case SPLIT_32x256x64: e = launch_dma_t<Split32x256, true>(a, splits, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    const int64_t quads = (p.M * p.N) / 4;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream,
+                       (const float *)workspace, splits, (int)p.M, (int)p.N, (_Float16 *)p.C, p.ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_naive(const Problem &p, hipStream_t stream) {
+    KArgs a = make_args(p);
+    dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)((p.M + 15) / 16));
+    hipLaunchKernelGGL(k_naive, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(const Problem &p, hipStream_t stream) {
+    const int64_t total = p.M * p.N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, stream, (_Float16 *)p.C, (int)p.M,
+                       (int)p.N, p.ldc);
+    return hipGetLastError();
+}
+
+}  // namespace tlg

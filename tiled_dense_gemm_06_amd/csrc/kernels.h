@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI host code and the gfx950 kernels.
+#ifndef TLG_KERNELS_H
+#define TLG_KERNELS_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace tlg {
+
+// One GEMM+ReLU problem: C (M x N) = ReLU(A (M x K) . B (K x N)), fp16,
+// row-major, leading dimensions in elements.
+struct Problem {
+    int64_t M, N, K;
+    const void *A;
+    int64_t lda;
+    const void *B;
+    int64_t ldb;
+    void *C;
+    int64_t ldc;
+};
+
+// Tile configurations. The index is what tlg_plan reports as `config`.
+struct TileConfig {
+    int bm, bn, bk, threads, stages;
+    const char *name;
+};
+// direct-to-LDS (aligned) configurations
+enum DmaConfig { DMA_256x256x32 = 0, DMA_128x128x32 = 1, DMA_64x64x64 = 2, DMA_CONFIGS = 3 };
+// register-staged (any alignment) configurations
+enum GenConfig { GEN_128x128x32 = 0, GEN_64x64x32 = 1, GEN_CONFIGS = 2 };
+// split-K partial kernels (direct-to-LDS, aligned)
+enum SplitConfig { SPLIT_32x128x64 = 0, SPLIT_32x256x64 = 1, SPLIT_CONFIGS = 2 };
+
+extern const TileConfig kDmaConfigs[DMA_CONFIGS];
+extern const TileConfig kGenConfigs[GEN_CONFIGS];
+extern const TileConfig kSplitConfigs[SPLIT_CONFIGS];
+
+// Launchers: enqueue on `stream`, return the launch status.
+hipError_t launch_tiled_dma(int config, const Problem &p, hipStream_t stream);
+hipError_t launch_tiled_general(int config, const Problem &p, hipStream_t stream);
+// Stage 1 writes fp32 partials W[s][m][n] (M x N packed per split) for
+// splits s covering k in [s*k_split, (s+1)*k_split); stage 2 sums them in
+// ascending s, applies ReLU and the fp16 cast, and writes C.
+hipError_t launch_splitk(int config, int splits, int64_t k_split, const Problem &p, float *workspace,
+                         hipStream_t stream);
+hipError_t launch_naive(const Problem &p, hipStream_t stream);
+hipError_t launch_fill_zero(const Problem &p, hipStream_t stream);
+
+}  // namespace tlg
+
+#endif

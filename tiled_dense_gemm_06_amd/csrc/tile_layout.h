@@ -1,0 +1,183 @@
+// Index arithmetic of the gfx950 GEMM+ReLU kernels: tile shapes, the LDS
+// swizzles, which global chunk each lane of a direct-to-LDS load fetches,
+// where each MFMA operand fragment is read from, and which C elements each
+// lane owns. Everything here is plain integer arithmetic, usable from the
+// kernels and from host-side emulation of the kernels' data movement.
+//
+// Tiling follows the quick-start kernel of the TileLang article
+// (aiwiki.ai/wiki/tilelang, "Programming model"): one work-group per output
+// tile, a K loop over shared-memory (LDS) tiles of A and B, an fp32
+// accumulator fragment in registers, ReLU and the fp16 copy-out at the end.
+// Shapes and layouts here are chosen for gfx950, not taken from that kernel.
+//
+// Facts about gfx950 this file relies on (measured on the device):
+//  * v_mfma_f32_32x32x16_f16: lane l holds, for its first operand, row
+//    (l % 32) and k = 8*(l/32) + e (e = 0..7); for the second operand,
+//    column (l % 32) and the same k; result element r of lane l is row
+//    8*(r/4) + 4*(l/32) + (r%4), column (l % 32).
+//  * ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives
+//    element (i % 4) of the 8-byte chunks addressed by lanes i/4 + 4*j,
+//    j = 0..3. If lane s addresses row (k0 + s/4), columns n0 + 4*(s%4) .. +3
+//    of a row-major (k, n) tile, lane i receives B[k0 + j][n0 + i], j = 0..3.
+//  * buffer_load_dwordx4 ... lds writes lane t's 16 bytes at M0 + 16*t and
+//    writes zeros for a lane whose offset is out of the buffer's range.
+//  * LDS has 64 banks of 4 bytes: a ds_read_b128 is conflict-free when every
+//    16 consecutive lanes touch 16 different 16-byte slots of a 256-byte
+//    window; a ds_read_b64_tr_b16 when every 32 consecutive lanes do.
+#ifndef TLG_TILE_LAYOUT_H
+#define TLG_TILE_LAYOUT_H
+
+#if defined(__HIPCC__)
+#define TLG_HD __host__ __device__ __forceinline__
+#else
+#define TLG_HD inline
+#endif
+
+namespace tlg {
+
+TLG_HD constexpr int imin(int a, int b) { return a < b ? a : b; }
+TLG_HD constexpr int imax(int a, int b) { return a > b ? a : b; }
+
+// Output tile BM x BN, K step BK, WM x WN waves (64 lanes each), STAGES LDS
+// buffers. Each wave owns a (BM/WM) x (BN/WN) block of C made of 32 x 32
+// MFMA tiles.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+struct TileShape {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
+    static constexpr int WAVES = WM * WN, NT = WAVES * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;   // per-wave extents
+    static constexpr int TM = WTM / 32, TN = WTN / 32;   // MFMA tiles per wave
+    static constexpr int RA = BK * 2, RB = BN * 2;       // LDS row bytes of the A and B tiles
+    static constexpr int CA = BK / 8, CB = BN / 8;       // 16-byte chunks per row
+    static constexpr int A_BYTES = BM * RA, B_BYTES = BK * RB;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = STAGE_BYTES * STAGES;
+    static constexpr int ROWS_A_SLAB = 1024 / RA, ROWS_B_SLAB = 1024 / RB; // rows per 1 KiB load
+    static constexpr int SLABS_A = A_BYTES / 1024, SLABS_B = B_BYTES / 1024;
+    static constexpr int DMA_A = SLABS_A / WAVES, DMA_B = SLABS_B / WAVES; // loads per wave per stage
+    static constexpr int KSTEPS = BK / 16;                // MFMA k-steps per stage
+    // register-staged loading: 16-byte chunks per thread per stage
+    static constexpr int JA = BM * CA / NT, JB = BK * CB / NT;
+
+    static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be whole 32x32 MFMA tiles");
+    static_assert(BK % 16 == 0 && BK >= 16, "BK must be a multiple of the MFMA k (16)");
+    static_assert(RA <= 1024 && RB <= 1024 && 1024 % RA == 0 && 1024 % RB == 0, "rows must pack 1 KiB loads");
+    static_assert(SLABS_A % WAVES == 0 && SLABS_B % WAVES == 0, "1 KiB loads must split evenly over waves");
+    static_assert(CB >= 4, "BN must be at least 32");
+    static_assert((BM * CA) % NT == 0 && (BK * CB) % NT == 0, "chunks must split evenly over threads");
+};
+
+// ---- LDS swizzles (16-byte granularity) ----
+// A tile: rows of RA bytes, K-contiguous. Chunk c of row r is stored at chunk
+// position c ^ swz_a(r). Sixteen consecutive rows read at one logical chunk
+// land in 16 distinct 16-byte slots of a 256-byte bank window.
+TLG_HD constexpr int swz_a(int r, int CA) {
+    return (r / imax(1, 16 / CA)) % imin(CA, 16);
+}
+// B tile: rows of RB bytes (one k each), N-contiguous. Chunk c of row k is
+// stored at chunk position c ^ swz_b(k). The four rows x four chunks read by
+// 32 lanes of one transposing read land in 16 distinct slots.
+TLG_HD constexpr int swz_b(int k, int CB) {
+    return 4 * ((k / imax(1, 16 / CB)) & (imin(CB, 16) / 4 - 1));
+}
+
+// ---- direct-to-LDS loads ----
+// Load i (0 <= i < DMA_A) of wave w fills LDS slab (w*DMA_A + i) of the A
+// tile: 1 KiB holding rows [slab*ROWS_A_SLAB, +ROWS_A_SLAB). Lane t writes
+// chunk position t % CA of row slab*ROWS_A_SLAB + t / CA, so it fetches the
+// logical chunk (t % CA) ^ swz_a(row), i.e. columns k0 + 8*chunk .. +7.
+struct ChunkRef {
+    int row;    // row inside the tile (A: m, B: k)
+    int chunk;  // logical 16-byte chunk inside the row
+};
+template <class S>
+TLG_HD ChunkRef dma_a_chunk(int wave, int i, int lane) {
+    int slab = wave * S::DMA_A + i;
+    int row = slab * S::ROWS_A_SLAB + lane / S::CA;
+    int pos = lane % S::CA;
+    return ChunkRef{row, pos ^ swz_a(row, S::CA)};
+}
+template <class S>
+TLG_HD ChunkRef dma_b_chunk(int wave, int i, int lane) {
+    int slab = wave * S::DMA_B + i;
+    int row = slab * S::ROWS_B_SLAB + lane / S::CB;
+    int pos = lane % S::CB;
+    return ChunkRef{row, pos ^ swz_b(row, S::CB)};
+}
+// LDS byte offset (inside a stage's A or B tile) of logical chunk c of row r.
+template <class S>
+TLG_HD int lds_a_offset(int r, int c) { return r * S::RA + 16 * (c ^ swz_a(r, S::CA)); }
+template <class S>
+TLG_HD int lds_b_offset(int k, int c) { return k * S::RB + 16 * (c ^ swz_b(k, S::CB)); }
+
+// Register-staged loading: job j of thread t covers chunk q = t + j*NT.
+template <class S>
+TLG_HD ChunkRef reg_a_chunk(int tid, int j) {
+    int q = tid + j * S::NT;
+    return ChunkRef{q / S::CA, q % S::CA};
+}
+template <class S>
+TLG_HD ChunkRef reg_b_chunk(int tid, int j) {
+    int q = tid + j * S::NT;
+    return ChunkRef{q / S::CB, q % S::CB};
+}
+
+// ---- MFMA operand fragments ----
+// The kernels compute the transposed tile D = B^T A^T with
+// v_mfma_f32_32x32x16_f16: the first operand comes from the B tile (its rows
+// are output columns n), the second from the A tile (output rows m). Then
+// each lane's four consecutive result registers are four consecutive n of
+// one row m, which become one 8-byte store.
+//
+// Second operand (A tile), MFMA tile tm of a wave whose rows start at wm0,
+// k-step s: lane l reads 16 bytes = A[wm0 + 32*tm + l%32][16*s + 8*(l/32) .. +7].
+template <class S>
+TLG_HD int frag_a_offset(int wm0, int tm, int s, int lane) {
+    int r = wm0 + 32 * tm + lane % 32;
+    int c = 2 * s + lane / 32;
+    return lds_a_offset<S>(r, c);
+}
+// First operand (B tile), MFMA tile tn of a wave whose columns start at wn0,
+// k-step s, half h (0: k 0..3 of the lane's 8, 1: k 4..7): the 8-byte
+// address lane l supplies to ds_read_b64_tr_b16. After the read, lane l holds
+// B[16*s + 8*(l/32) + 4*h + j][wn0 + 32*tn + l%32] for j = 0..3.
+template <class S>
+TLG_HD int frag_b_offset(int wn0, int tn, int s, int h, int lane) {
+    int g = lane / 16, i = lane % 16;
+    int k = 16 * s + 8 * (g / 2) + 4 * h + i / 4;
+    int n = wn0 + 32 * tn + 16 * (g % 2) + 4 * (i % 4);
+    return lds_b_offset<S>(k, n / 8) + 2 * (n % 8);
+}
+
+// ---- result ownership ----
+// Result register r of MFMA tile (tn, tm) in lane l is C[m][n] with
+// m = wm0 + 32*tm + l%32 and n = wn0 + 32*tn + 8*(r/4) + 4*(l/32) + r%4.
+TLG_HD int acc_m(int wm0, int tm, int lane) { return wm0 + 32 * tm + lane % 32; }
+TLG_HD int acc_n(int wn0, int tn, int r, int lane) {
+    return wn0 + 32 * tn + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+}
+
+// ---- tile order ----
+// Work-groups are handed to the 8 XCDs of the device round-robin by id, so
+// id p runs on XCD p % 8. Renumber so that each XCD receives a contiguous
+// range of tiles, then walk tiles in groups of group_m tile-rows so that the
+// work-groups resident at one time on one XCD share rows of A and columns of
+// B in that XCD's L2. The map is a bijection on [0, nwg) for any nwg.
+TLG_HD int xcd_remap(int pid, int nwg) {
+    const int nx = 8;
+    int per = nwg / nx, rem = nwg % nx;
+    int x = pid % nx, idx = pid / nx;
+    return x * per + imin(x, rem) + idx;
+}
+TLG_HD void grouped_tile(int q, int tiles_m, int tiles_n, int group_m, int *tm, int *tn) {
+    int width = group_m * tiles_n;
+    int first_m = (q / width) * group_m;
+    int gsz = imin(tiles_m - first_m, group_m);
+    int r = q % width;
+    *tm = first_m + r % gsz;
+    *tn = r / gsz;
+}
+
+}  // namespace tlg
+
+#endif
