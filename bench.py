@@ -86,6 +86,28 @@ def cpu_baseline(w, A, B, target_s: float):
     }
 
 
+def copy_calibration(torch, dev, nbytes: int, steps: int, warmup: int) -> int:
+    """A plain copy of a known size: reads nbytes and writes nbytes per launch.
+    Under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it gives the factor between
+    those counters and real HBM bytes."""
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / max(1, steps)
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": steps + warmup,
+                      "ms_per_copy": ms, "GB_per_s_read_plus_write": 2 * nbytes / ms / 1e6}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +116,14 @@ def main() -> int:
     ap.add_argument("--workload", default="square8192")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample size, in seconds of CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", default="auto",
+                    help="kernel family to time (auto = what tlg_gemm_relu picks; others for comparisons): "
+                         "auto, tiled_pipe, tiled_dma, tiled_general, splitk, naive")
+    ap.add_argument("--config", type=int, default=-1, help="tile configuration index of --variant (-1 = library's choice)")
+    ap.add_argument("--splits", type=int, default=0, help="split-K count for --variant splitk (0 = library's choice)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the GEMM, time a plain device-to-device copy of MIB MiB (the reference "
+                         "kernel for scaling the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -111,11 +141,18 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
-    w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration > 0:
+        return copy_calibration(torch, dev, args.copy_calibration << 20, args.steps, args.warmup)
+    w = wl.WORKLOADS[args.workload]
     A, B = wl.make_inputs(w)
-    plan = tlg.plan(w.M, w.N, w.K)
+    names = {v: k for k, v in tlg._native.VARIANT_NAMES.items()}
+    if args.variant not in names:
+        print(f"bench.py: unknown variant {args.variant}", file=sys.stderr)
+        return 2
+    variant = names[args.variant]
+    plan = tlg.plan(w.M, w.N, w.K, variant=variant, config=args.config, splits=args.splits)
 
     # Rotate among R copies of the inputs and outputs so the working set is
     # more than twice the Infinity Cache: every step reads from HBM.
@@ -131,7 +168,8 @@ def main() -> int:
 
     def step(i):
         j = i % R
-        tlg.gemm_relu(As[j], Bs[j], out=Cs[j], handle=h, stream=stream)
+        tlg.gemm_relu(As[j], Bs[j], out=Cs[j], handle=h, stream=stream, variant=variant, config=args.config,
+                      splits=args.splits)
 
     for i in range(args.warmup):
         step(i)

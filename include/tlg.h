@@ -57,7 +57,8 @@ typedef enum {
     TLG_VARIANT_TILED_DMA = 3,     /* MFMA tiles fed by direct global->LDS loads; needs the aligned fast-path conditions */
     TLG_VARIANT_TILED_GENERAL = 4, /* MFMA tiles fed through registers; any alignment and leading dimension */
     TLG_VARIANT_SPLITK = 5,        /* skinny M: K split across work-groups, fp32 partials, then an ordered reduce + ReLU + cast */
-    TLG_VARIANT_NAIVE = 6          /* one thread per output, sequential k; for cross-checks only, never chosen automatically */
+    TLG_VARIANT_NAIVE = 6,         /* one thread per output, sequential k; for cross-checks only, never chosen automatically */
+    TLG_VARIANT_TILED_PIPE = 7     /* MFMA tiles fed by direct global->LDS loads, loads and LDS reads slotted between MFMAs; aligned, large problems */
 } tlg_variant;
 
 /* What tlg_gemm_relu will launch for a given problem (pure host logic). */
@@ -98,12 +99,16 @@ tlg_status tlg_gemm_relu(tlg_handle h, int64_t M, int64_t N, int64_t K,
                          void *C, int64_t ldc,
                          hipStream_t stream);
 
-/* Same operation as tlg_gemm_relu with a forced kernel family and split
- * count, for tests and measurements: variant is a tlg_variant (AUTO picks as
- * tlg_gemm_relu does); splits <= 0 lets the library choose. Returns
- * TLG_ERROR_NOT_SUPPORTED if the forced variant cannot serve the problem
- * (e.g. DMA tiles on unaligned data) and nothing is enqueued. */
-tlg_status tlg_gemm_relu_variant(tlg_handle h, int32_t variant, int32_t splits,
+/* Same operation as tlg_gemm_relu with a forced kernel family, tile
+ * configuration and split count, for tests and measurements: variant is a
+ * tlg_variant (AUTO picks as tlg_gemm_relu does, and then config must be -1);
+ * config is the index of one of the variant's tile configurations (names from
+ * tlg_plan_config_name) or -1 to let the library choose; splits <= 0 lets the
+ * library choose. Returns TLG_ERROR_INVALID_VALUE for an unknown variant or
+ * configuration, TLG_ERROR_NOT_SUPPORTED if the forced variant cannot serve
+ * the problem (e.g. direct-to-LDS tiles on unaligned data); in both cases
+ * nothing is enqueued. */
+tlg_status tlg_gemm_relu_variant(tlg_handle h, int32_t variant, int32_t config, int32_t splits,
                                  int64_t M, int64_t N, int64_t K,
                                  const void *A, int64_t lda,
                                  const void *B, int64_t ldb,
@@ -117,8 +122,8 @@ tlg_status tlg_check_args(int64_t M, int64_t N, int64_t K,
                           const void *B, int64_t ldb,
                           const void *C, int64_t ldc);
 
-/* The launch plan for a problem (pure host logic, no GPU needed). variant and
- * splits have the meaning of tlg_gemm_relu_variant; workspace_cap_bytes is
+/* The launch plan for a problem (pure host logic, no GPU needed). variant,
+ * config and splits have the meaning of tlg_gemm_relu_variant; workspace_cap_bytes is
  * the workspace available (tlg_workspace_bytes() for a handle). Returns
  * TLG_ERROR_INVALID_VALUE for bad arguments, TLG_ERROR_NOT_SUPPORTED when the
  * forced variant cannot serve the problem. */
@@ -126,7 +131,7 @@ tlg_status tlg_plan(int64_t M, int64_t N, int64_t K,
                     const void *A, int64_t lda,
                     const void *B, int64_t ldb,
                     const void *C, int64_t ldc,
-                    int32_t variant, int32_t splits, int64_t workspace_cap_bytes,
+                    int32_t variant, int32_t config, int32_t splits, int64_t workspace_cap_bytes,
                     tlg_plan_info *out);
 
 /* Name of a tile configuration reported by tlg_plan ("" if unknown). */

@@ -275,6 +275,7 @@ using E128 = TileShape<128, 128, 32, 2, 2, 4>;
 using E64 = TileShape<64, 64, 64, 2, 2, 3>;
 using ES128 = TileShape<32, 128, 64, 1, 4, 4>;
 using ES256 = TileShape<32, 256, 64, 1, 4, 3>;
+using EP64 = TileShape<256, 256, 64, 2, 2, 2>;  // pipelined, 64-deep stages
 
 extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A, long lda, const uint16_t *B,
                              long ldb, uint16_t *C, long ldc, int splits, int k_split, float *W, long *errs) {
@@ -283,6 +284,7 @@ extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A,
         case 0: return emulate<E256>(p, false, errs);
         case 1: return emulate<E128>(p, false, errs);
         case 2: return emulate<E64>(p, false, errs);
+        case 3: return emulate<EP64>(p, false, errs);
         case 10: return emulate<ES128>(p, true, errs);
         case 11: return emulate<ES256>(p, true, errs);
         default: return -1;

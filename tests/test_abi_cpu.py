@@ -66,8 +66,8 @@ def test_check_args(args, expect):
 
 
 def test_plan_shapes_of_the_workloads():
-    assert tlg.plan(8192, 8192, 8192)["config_name"].startswith("dma_256x256")
-    assert tlg.plan(4096, 4096, 4096)["variant_name"] == "tiled_dma"
+    assert tlg.plan(8192, 8192, 8192)["config_name"] == "pipe_256x256x64_w2x2_s2"
+    assert tlg.plan(4096, 4096, 4096)["variant_name"] == "tiled_pipe"
     p = tlg.plan(3001, 2049, 1537)
     assert p["variant_name"] == "tiled_general"  # odd leading dimensions
     p = tlg.plan(16, 14336, 4096)
@@ -98,8 +98,19 @@ def test_forced_variants():
     assert p["variant_name"] == "naive"
     p = tlg.plan(300, 304, 304, variant=tlg.TLG_VARIANT_TILED_GENERAL)
     assert p["variant_name"] == "tiled_general"
+    p = tlg.plan(300, 304, 304, variant=tlg.TLG_VARIANT_TILED_PIPE)  # forced: any aligned shape
+    assert p["variant_name"] == "tiled_pipe" and p["grid"] == 2 * 2
+    with pytest.raises(tlg.TlgError):
+        tlg.plan(300, 300, 300, variant=tlg.TLG_VARIANT_TILED_PIPE)  # N % 8 != 0
     with pytest.raises(tlg.TlgError):
         tlg.plan(4, 4, 4, variant=99)
+    with pytest.raises(tlg.TlgError):  # a configuration needs a forced variant
+        tlg.plan(512, 512, 512, config=0)
+    with pytest.raises(tlg.TlgError):  # no such configuration
+        tlg.plan(512, 512, 512, variant=tlg.TLG_VARIANT_TILED_PIPE, config=99)
+    for cfg in range(2):
+        p = tlg.plan(1024, 1024, 1024, variant=tlg.TLG_VARIANT_TILED_PIPE, config=cfg)
+        assert p["config"] == cfg and p["config_name"].startswith("pipe_256x256")
 
 
 def test_split_counts_cover_k_without_empty_splits():
@@ -117,7 +128,7 @@ def test_split_counts_cover_k_without_empty_splits():
 
 
 def test_workspace_cap_lowers_splits():
-    st, info = nat.tlg_plan(64, 14336, 4096, A16, 4096, A16, 14336, A16, 14336, tlg.TLG_VARIANT_SPLITK, 16,
+    st, info = nat.tlg_plan(64, 14336, 4096, A16, 4096, A16, 14336, A16, 14336, tlg.TLG_VARIANT_SPLITK, -1, 16,
                             2 * 64 * 14336 * 4)
     assert st == 0 and info.splits <= 2 and info.workspace_bytes <= 2 * 64 * 14336 * 4
 

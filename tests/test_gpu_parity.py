@@ -25,6 +25,7 @@ V_DMA = tlg.TLG_VARIANT_TILED_DMA
 V_GEN = tlg.TLG_VARIANT_TILED_GENERAL
 V_SPLIT = tlg.TLG_VARIANT_SPLITK
 V_NAIVE = tlg.TLG_VARIANT_NAIVE
+V_PIPE = tlg.TLG_VARIANT_TILED_PIPE
 
 
 @pytest.fixture(scope="module")
@@ -64,7 +65,7 @@ def variants_for(M, N, K, aligned=True, lda=None, ldb=None, ldc=None):
     out = [V_AUTO, V_GEN, V_NAIVE]
     kw = dict(lda=lda, ldb=ldb, ldc=ldc, aligned=aligned)
     p = tlg.plan(M, N, K, **kw)
-    for v in (V_DMA, V_SPLIT):
+    for v in (V_DMA, V_SPLIT, V_PIPE):
         try:
             tlg.plan(M, N, K, variant=v, **kw)
             out.append(v)
@@ -126,7 +127,7 @@ def test_skinny_without_split(dev):
     w = wl.WORKLOADS["skinny16x14336x4096"]
     A, B = wl.make_random(w.M, w.N, w.K, seed=3, kind="integer_pos")
     ref = oracle.gemm_relu(A, B)
-    for v in (V_DMA, V_GEN):
+    for v in (V_DMA, V_GEN, V_PIPE):
         assert np.array_equal(bits(run(A, B, dev, variant=v)), ref), v
 
 
@@ -161,6 +162,23 @@ def test_large_square_sampled(dev, name):
     Ai, Bi = wl.make_inputs(w, integer=True)
     got = bits(run(Ai, Bi, dev))
     assert np.array_equal(got[rows], oracle.gemm_relu_rows(Ai, Bi, rows))
+
+
+@pytest.mark.parametrize("config", [0, 1])
+@pytest.mark.parametrize("shape", [(300, 264, 200), (513, 520, 72), (1024, 1032, 1000), (256, 256, 8),
+                                   (257, 8, 4104)])
+def test_pipe_configs(dev, config, shape):
+    """Every tile configuration of the pipelined kernel: ragged M and N, K
+    tails inside a stage, K shorter than the pipeline, one-column N."""
+    M, N, K = shape
+    A, B = wl.make_random(M, N, K, seed=M ^ N ^ K, kind="integer_pos")
+    ref = oracle.gemm_relu(A, B)
+    big = torch.full((M + 2, N + 8), float("nan"), dtype=torch.float16, device=dev)
+    tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), out=big[:M, :N], variant=V_PIPE, config=config)
+    torch.cuda.synchronize()
+    allb = bits(big)
+    assert np.array_equal(allb[:M, :N], ref)
+    assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
 
 
 # ---------------------------------------------------------------- writes, padding, edges
@@ -285,7 +303,7 @@ def test_invalid_arguments_enqueue_nothing(dev):
     A = torch.ones((4, 4), dtype=torch.float16, device=dev)
     st = nat.tlg_gemm_relu(h.ptr, 4, 4, 4, A.data_ptr(), 3, A.data_ptr(), 4, C.data_ptr(), 4, None)
     assert st == nat.TLG_ERROR_INVALID_VALUE
-    st = nat.tlg_gemm_relu_variant(h.ptr, V_DMA, 0, 4, 4, 4, A.data_ptr() + 2, 4, A.data_ptr(), 4,
+    st = nat.tlg_gemm_relu_variant(h.ptr, V_DMA, -1, 0, 4, 4, 4, A.data_ptr() + 2, 4, A.data_ptr(), 4,
                                    C.data_ptr(), 4, None)
     assert st == nat.TLG_ERROR_NOT_SUPPORTED
     torch.cuda.synchronize()

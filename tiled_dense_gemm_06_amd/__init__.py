@@ -12,7 +12,7 @@ from __future__ import annotations
 from . import _native
 from ._native import (  # noqa: F401  (re-exported C-ABI names)
     TLG_VARIANT_AUTO, TLG_VARIANT_FILL_ZERO, TLG_VARIANT_NAIVE, TLG_VARIANT_NOOP,
-    TLG_VARIANT_SPLITK, TLG_VARIANT_TILED_DMA, TLG_VARIANT_TILED_GENERAL, TlgError,
+    TLG_VARIANT_SPLITK, TLG_VARIANT_TILED_DMA, TLG_VARIANT_TILED_GENERAL, TLG_VARIANT_TILED_PIPE, TlgError,
     tlg_arch_supported, tlg_check_args, tlg_plan, tlg_plan_config_name, tlg_status_string,
     tlg_version, tlg_workspace_bytes,
 )
@@ -79,13 +79,15 @@ def _check(t, name):
         raise ValueError(f"{name} rows overlap")
 
 
-def gemm_relu(A, B, out=None, *, variant: int = TLG_VARIANT_AUTO, splits: int = 0, stream=None, handle=None):
+def gemm_relu(A, B, out=None, *, variant: int = TLG_VARIANT_AUTO, config: int = -1, splits: int = 0, stream=None,
+              handle=None):
     """C = ReLU(A @ B) for fp16 row-major A (M, K) and B (K, N); returns C (M, N).
 
     ``out`` may be a preallocated fp16 (M, N) tensor (a padded row view is
     fine: only its M x N window is written). The work is enqueued on
     ``stream`` (default: the current stream of A's device) and is
-    asynchronous. ``variant``/``splits`` force a kernel family (tests).
+    asynchronous. ``variant``/``config``/``splits`` force a kernel family, tile
+    configuration and split count (tests and measurements).
     """
     import torch
 
@@ -106,7 +108,7 @@ def gemm_relu(A, B, out=None, *, variant: int = TLG_VARIANT_AUTO, splits: int = 
     h = handle if handle is not None else handle_for(A.device)
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     with torch.cuda.device(A.device):
-        st = _native.tlg_gemm_relu_variant(h.ptr, variant, splits, M, N, K, A.data_ptr(), _ld(A),
+        st = _native.tlg_gemm_relu_variant(h.ptr, variant, config, splits, M, N, K, A.data_ptr(), _ld(A),
                                            B.data_ptr(), _ld(B), out.data_ptr(), _ld(out), s.cuda_stream)
     if st != _native.TLG_SUCCESS:
         raise TlgError(st, "tlg_gemm_relu")
@@ -114,7 +116,7 @@ def gemm_relu(A, B, out=None, *, variant: int = TLG_VARIANT_AUTO, splits: int = 
 
 
 def plan(M, N, K, lda=None, ldb=None, ldc=None, *, aligned: bool = True, variant: int = TLG_VARIANT_AUTO,
-         splits: int = 0) -> dict:
+         config: int = -1, splits: int = 0) -> dict:
     """What gemm_relu would launch for a problem (host logic only, no GPU).
 
     Pointers are stand-ins: 16-byte aligned when ``aligned`` else 2-byte aligned.
@@ -123,7 +125,7 @@ def plan(M, N, K, lda=None, ldb=None, ldc=None, *, aligned: bool = True, variant
     ldb = max(1, N) if ldb is None else ldb
     ldc = max(1, N) if ldc is None else ldc
     base = 1 << 20 if aligned else (1 << 20) + 2
-    st, info = _native.tlg_plan(M, N, K, base, lda, base, ldb, base, ldc, variant, splits)
+    st, info = _native.tlg_plan(M, N, K, base, lda, base, ldb, base, ldc, variant, config, splits)
     if st != _native.TLG_SUCCESS:
         raise TlgError(st, "tlg_plan")
     d = info.as_dict()

@@ -24,11 +24,12 @@ TLG_VARIANT_TILED_DMA = 3
 TLG_VARIANT_TILED_GENERAL = 4
 TLG_VARIANT_SPLITK = 5
 TLG_VARIANT_NAIVE = 6
+TLG_VARIANT_TILED_PIPE = 7
 
 VARIANT_NAMES = {
     TLG_VARIANT_AUTO: "auto", TLG_VARIANT_NOOP: "noop", TLG_VARIANT_FILL_ZERO: "fill_zero",
     TLG_VARIANT_TILED_DMA: "tiled_dma", TLG_VARIANT_TILED_GENERAL: "tiled_general",
-    TLG_VARIANT_SPLITK: "splitk", TLG_VARIANT_NAIVE: "naive",
+    TLG_VARIANT_SPLITK: "splitk", TLG_VARIANT_NAIVE: "naive", TLG_VARIANT_TILED_PIPE: "tiled_pipe",
 }
 
 
@@ -68,11 +69,11 @@ def lib():
         L.tlg_destroy.restype = i32
         L.tlg_gemm_relu.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p]
         L.tlg_gemm_relu.restype = i32
-        L.tlg_gemm_relu_variant.argtypes = [p, i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, p]
+        L.tlg_gemm_relu_variant.argtypes = [p, i32, i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, p]
         L.tlg_gemm_relu_variant.restype = i32
         L.tlg_check_args.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
         L.tlg_check_args.restype = i32
-        L.tlg_plan.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i32, i32, i64,
+        L.tlg_plan.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i32, i32, i32, i64,
                                ctypes.POINTER(tlg_plan_info)]
         L.tlg_plan.restype = i32
         L.tlg_plan_config_name.argtypes = [i32, i32]
@@ -105,19 +106,19 @@ def tlg_gemm_relu(h, M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
     return lib().tlg_gemm_relu(h, M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
-def tlg_gemm_relu_variant(h, variant, splits, M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
-    return lib().tlg_gemm_relu_variant(h, variant, splits, M, N, K, A, lda, B, ldb, C, ldc, stream)
+def tlg_gemm_relu_variant(h, variant, config, splits, M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
+    return lib().tlg_gemm_relu_variant(h, variant, config, splits, M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
 def tlg_check_args(M, N, K, A, lda, B, ldb, C, ldc) -> int:
     return lib().tlg_check_args(M, N, K, A, lda, B, ldb, C, ldc)
 
 
-def tlg_plan(M, N, K, A, lda, B, ldb, C, ldc, variant=TLG_VARIANT_AUTO, splits=0, workspace_cap=None):
+def tlg_plan(M, N, K, A, lda, B, ldb, C, ldc, variant=TLG_VARIANT_AUTO, config=-1, splits=0, workspace_cap=None):
     """Returns (status, tlg_plan_info)."""
     info = tlg_plan_info()
     cap = tlg_workspace_bytes() if workspace_cap is None else workspace_cap
-    st = lib().tlg_plan(M, N, K, A, lda, B, ldb, C, ldc, variant, splits, cap, ctypes.byref(info))
+    st = lib().tlg_plan(M, N, K, A, lda, B, ldb, C, ldc, variant, config, splits, cap, ctypes.byref(info))
     return st, info
 
 

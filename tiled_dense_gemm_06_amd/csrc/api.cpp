@@ -91,10 +91,14 @@ bool choose_splits(const tlg::Problem &p, const tlg::TileConfig &tc, int32_t for
     return true;
 }
 
-tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t splits, int64_t cap, tlg_plan_info *o,
-                     int64_t *k_split_out) {
+// A forced tile configuration index must exist for its variant.
+bool config_ok(int32_t config, int count) { return config < 0 || config < count; }
+
+tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int32_t splits, int64_t cap,
+                     tlg_plan_info *o, int64_t *k_split_out) {
     *k_split_out = 0;
-    if (variant < TLG_VARIANT_AUTO || variant > TLG_VARIANT_NAIVE) return TLG_ERROR_INVALID_VALUE;
+    if (variant < TLG_VARIANT_AUTO || variant > TLG_VARIANT_TILED_PIPE) return TLG_ERROR_INVALID_VALUE;
+    if (variant == TLG_VARIANT_AUTO && config >= 0) return TLG_ERROR_INVALID_VALUE;
     if (p.M == 0 || p.N == 0) {
         fill_info(o, TLG_VARIANT_NOOP, 0, nullptr, 1, 0, 0, 0);
         return TLG_SUCCESS;
@@ -118,7 +122,8 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t splits, int
 
     // split-K for skinny M
     if (variant == TLG_VARIANT_SPLITK || (variant == TLG_VARIANT_AUTO && p.M <= 64 && p.K >= 512)) {
-        const int cfg = tlg::SPLIT_32x128x64;
+        if (!config_ok(config, tlg::SPLIT_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
+        const int cfg = config >= 0 ? config : tlg::SPLIT_32x128x64;
         const tlg::TileConfig &tc = tlg::kSplitConfigs[cfg];
         int s = 1;
         int64_t k_split = 0;
@@ -132,11 +137,28 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t splits, int
         if (variant == TLG_VARIANT_SPLITK) return TLG_ERROR_NOT_SUPPORTED;
     }
 
+    // large aligned problems: the software-pipelined 256 x 256 tiles, when
+    // there are enough tiles to give most CUs one
+    if (variant == TLG_VARIANT_TILED_PIPE || variant == TLG_VARIANT_AUTO) {
+        if (!config_ok(config, tlg::PIPE_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
+        const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64;
+        const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
+        const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
+        if (dma_ok(p, tc.bm, tc.bn, tc.bk) && (variant == TLG_VARIANT_TILED_PIPE || tiles >= 224)) {
+            fill_info(o, TLG_VARIANT_TILED_PIPE, cfg, &tc, 1, 1, tiles, 0);
+            return TLG_SUCCESS;
+        }
+        if (variant == TLG_VARIANT_TILED_PIPE) return TLG_ERROR_NOT_SUPPORTED;
+    }
+
     if (variant == TLG_VARIANT_TILED_DMA || variant == TLG_VARIANT_AUTO) {
+        if (!config_ok(config, tlg::DMA_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
         int cfg;
         const int64_t t256 = ceil_div(p.M, 256) * ceil_div(p.N, 256);
         const int64_t t128 = ceil_div(p.M, 128) * ceil_div(p.N, 128);
-        if (t256 >= 224)
+        if (config >= 0)
+            cfg = config;
+        else if (t256 >= 224)
             cfg = tlg::DMA_256x256x32;
         else if (t128 >= 192)
             cfg = tlg::DMA_128x128x32;
@@ -151,7 +173,10 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t splits, int
     }
 
     // TLG_VARIANT_TILED_GENERAL, or AUTO on data the DMA kernels cannot take
-    const int cfg = ceil_div(p.M, 128) * ceil_div(p.N, 128) >= 192 ? tlg::GEN_128x128x32 : tlg::GEN_64x64x32;
+    if (!config_ok(config, tlg::GEN_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
+    const int cfg = config >= 0 ? config
+                                : (ceil_div(p.M, 128) * ceil_div(p.N, 128) >= 192 ? tlg::GEN_128x128x32
+                                                                                   : tlg::GEN_64x64x32);
     const tlg::TileConfig &tc = tlg::kGenConfigs[cfg];
     fill_info(o, TLG_VARIANT_TILED_GENERAL, cfg, &tc, 1, 1, ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn), 0);
     return TLG_SUCCESS;
@@ -172,7 +197,8 @@ tlg::Problem make_problem(int64_t M, int64_t N, int64_t K, const void *A, int64_
     return p;
 }
 
-tlg_status run(tlg_handle h, int32_t variant, int32_t splits, const tlg::Problem &p, hipStream_t stream) {
+tlg_status run(tlg_handle h, int32_t variant, int32_t config, int32_t splits, const tlg::Problem &p,
+               hipStream_t stream) {
     if (!h) return TLG_ERROR_INVALID_VALUE;
     tlg_status st = tlg_check_args(p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc);
     if (st != TLG_SUCCESS) return st;
@@ -181,7 +207,7 @@ tlg_status run(tlg_handle h, int32_t variant, int32_t splits, const tlg::Problem
     if (dev != h->device) return TLG_ERROR_INVALID_VALUE;  // the handle's device must be current
     tlg_plan_info info;
     int64_t k_split = 0;
-    st = plan_impl(p, variant, splits, h->workspace_bytes, &info, &k_split);
+    st = plan_impl(p, variant, config, splits, h->workspace_bytes, &info, &k_split);
     if (st != TLG_SUCCESS) return st;
     hipError_t e = hipSuccess;
     switch (info.variant) {
@@ -190,6 +216,7 @@ tlg_status run(tlg_handle h, int32_t variant, int32_t splits, const tlg::Problem
         case TLG_VARIANT_NAIVE: e = tlg::launch_naive(p, stream); break;
         case TLG_VARIANT_TILED_DMA: e = tlg::launch_tiled_dma(info.config, p, stream); break;
         case TLG_VARIANT_TILED_GENERAL: e = tlg::launch_tiled_general(info.config, p, stream); break;
+        case TLG_VARIANT_TILED_PIPE: e = tlg::launch_tiled_pipe(info.config, p, stream); break;
         case TLG_VARIANT_SPLITK:
             e = tlg::launch_splitk(info.config, info.splits, k_split, p, h->workspace, stream);
             break;
@@ -215,14 +242,15 @@ tlg_status tlg_check_args(int64_t M, int64_t N, int64_t K, const void *A, int64_
 }
 
 tlg_status tlg_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
-                    const void *C, int64_t ldc, int32_t variant, int32_t splits, int64_t workspace_cap_bytes,
+                    const void *C, int64_t ldc, int32_t variant, int32_t config, int32_t splits,
+                    int64_t workspace_cap_bytes,
                     tlg_plan_info *out) {
     if (!out) return TLG_ERROR_INVALID_VALUE;
     tlg_status st = tlg_check_args(M, N, K, A, lda, B, ldb, C, ldc);
     if (st != TLG_SUCCESS) return st;
     tlg::Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc);
     int64_t k_split = 0;
-    return plan_impl(p, variant, splits, workspace_cap_bytes, out, &k_split);
+    return plan_impl(p, variant, config, splits, workspace_cap_bytes, out, &k_split);
 }
 
 const char *tlg_plan_config_name(int32_t variant, int32_t config) {
@@ -233,6 +261,8 @@ const char *tlg_plan_config_name(int32_t variant, int32_t config) {
             return (config >= 0 && config < tlg::GEN_CONFIGS) ? tlg::kGenConfigs[config].name : "";
         case TLG_VARIANT_SPLITK:
             return (config >= 0 && config < tlg::SPLIT_CONFIGS) ? tlg::kSplitConfigs[config].name : "";
+        case TLG_VARIANT_TILED_PIPE:
+            return (config >= 0 && config < tlg::PIPE_CONFIGS) ? tlg::kPipeConfigs[config].name : "";
         case TLG_VARIANT_NAIVE: return "naive_16x16";
         case TLG_VARIANT_FILL_ZERO: return "fill_zero";
         case TLG_VARIANT_NOOP: return "noop";
@@ -279,13 +309,13 @@ tlg_status tlg_destroy(tlg_handle h) {
 
 tlg_status tlg_gemm_relu(tlg_handle h, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                          int64_t ldb, void *C, int64_t ldc, hipStream_t stream) {
-    return run(h, TLG_VARIANT_AUTO, 0, make_problem(M, N, K, A, lda, B, ldb, C, ldc), stream);
+    return run(h, TLG_VARIANT_AUTO, -1, 0, make_problem(M, N, K, A, lda, B, ldb, C, ldc), stream);
 }
 
-tlg_status tlg_gemm_relu_variant(tlg_handle h, int32_t variant, int32_t splits, int64_t M, int64_t N, int64_t K,
-                                 const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
-                                 hipStream_t stream) {
-    return run(h, variant, splits, make_problem(M, N, K, A, lda, B, ldb, C, ldc), stream);
+tlg_status tlg_gemm_relu_variant(tlg_handle h, int32_t variant, int32_t config, int32_t splits, int64_t M, int64_t N,
+                                 int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+                                 int64_t ldc, hipStream_t stream) {
+    return run(h, variant, config, splits, make_problem(M, N, K, A, lda, B, ldb, C, ldc), stream);
 }
 
 const char *tlg_status_string(tlg_status s) {

@@ -1,0 +1,272 @@
+// Software-pipelined gfx950 kernel for C = ReLU(A . B) on large, aligned
+// problems: the quick-start kernel of the TileLang article
+// (aiwiki.ai/wiki/tilelang, "Programming model") with its T.Pipelined K loop
+// scheduled by hand for one 64-wide wave per SIMD.
+//
+// Data movement and layouts are those of k_tiled_dma (direct global->LDS
+// loads, XOR-swizzled LDS stages, ds_read_b64_tr_b16 for the N-contiguous B
+// operand, v_mfma_f32_32x32x16_f16 with fp32 accumulators). What changes is
+// the order of work inside one K step of a wave. The MFMA pipe of a SIMD has
+// no other wave to switch to, so every instruction that is not an MFMA is
+// slotted between MFMAs, where it costs no matrix-core time: the LDS reads of
+// the next k-step's operand fragments, one or two after each MFMA, and the
+// direct-to-LDS loads of the stage three steps ahead, one every two to four
+// MFMAs (so the load unit is never flooded). One barrier per K step publishes
+// the next stage; the loop is arranged so that nothing is pending in LDS at
+// that point and the first MFMAs after it still have operands in registers.
+//
+// The stream of loads is uniform: stages past the end of K are issued with
+// every lane out of range, which writes zeros into a buffer no wave reads.
+// So every step waits for the same load count and the loop has no branch.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gfx950_ops.h"
+#include "kernels.h"
+#include "tile_layout.h"
+
+namespace tlg {
+
+// Operand fragments of one k-step: TM A fragments (second MFMA operand, one
+// ds_read_b128 each) and TN B fragments (first operand, two transposing
+// 8-byte reads each).
+template <class S>
+struct Frags {
+    half8_t a[S::TM];
+    short4_t blo[S::TN], bhi[S::TN];
+};
+
+// LDS reads of one k-step's fragments, numbered in the order the MFMAs use
+// them (tile i uses b[i / TM] and a[i % TM]): b[0] (two reads), a[0..TM-1],
+// then b[1..TN-1] (two reads each).
+template <class S>
+constexpr int kFragReads = S::TM + 2 * S::TN;
+
+template <class S>
+__device__ __forceinline__ void frag_read(Frags<S> &f, LDS_PTR(const char) sA, LDS_PTR(const char) sB,
+                                          int wm0, int wn0, int s, int lane, int r) {
+    if (r < 2) {
+        LDS_PTR(short4_t) p = (LDS_PTR(short4_t))(sB + frag_b_offset<S>(wn0, 0, s, r, lane));
+        if (r == 0)
+            f.blo[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+        else
+            f.bhi[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+    } else if (r < 2 + S::TM) {
+        const int tm = r - 2;
+        f.a[tm] = *(LDS_PTR(const half8_t))(sA + frag_a_offset<S>(wm0, tm, s, lane));
+    } else {
+        const int tn = 1 + (r - 2 - S::TM) / 2, h = (r - 2 - S::TM) % 2;
+        LDS_PTR(short4_t) p = (LDS_PTR(short4_t))(sB + frag_b_offset<S>(wn0, tn, s, h, lane));
+        if (h == 0)
+            f.blo[tn] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+        else
+            f.bhi[tn] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+    }
+}
+
+template <class S>
+__device__ __forceinline__ void mfma_tile(const Frags<S> &f, int i, float16_t (&acc)[S::TN][S::TM]) {
+    const int tn = i / S::TM, tm = i % S::TM;
+    const half8_t b = __builtin_bit_cast(half8_t, __builtin_shufflevector(f.blo[tn], f.bhi[tn], 0, 1, 2, 3, 4, 5,
+                                                                           6, 7));
+    acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, f.a[tm], acc[tn][tm], 0, 0, 0);
+}
+
+// Nothing may be scheduled across this point (keeps the hand-written order).
+#define TLG_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// One K step of the loop is a fixed sequence of KSTEPS*16 MFMA slots:
+//   slots 0..7        MFMAs 8..15 of the previous stage's last k-step (held in
+//                     f[1]); after them the 12 LDS reads of this stage's
+//                     k-step-0 fragments into f[0], two per slot;
+//   next 16 per ks    k-steps 0..KSTEPS-2: 16 MFMAs on f[ks & 1], with the 12
+//                     reads of k-step ks+1 into f[(ks+1) & 1], one per slot;
+//   last 8 slots      MFMAs 0..7 of the last k-step (f[1]).
+// The LOADS direct-to-LDS loads of stage kt+STAGES-1 go after slots
+// DOFF, DOFF+SPACING, ... Then this wave's loads of stage kt+1 are waited for
+// and the barrier publishes it (and retires stage kt).
+template <class S, int SPACING, int DOFF>
+__global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
+    static_assert(S::TM * S::TN == 16, "schedule written for 16 MFMA tiles per wave");
+    static_assert(S::KSTEPS % 2 == 0, "the last k-step of a stage must use f[1]");
+    static_assert(kFragReads<S> <= 12, "fragment reads must fit under the MFMAs of a k-step");
+    constexpr int LOADS = S::DMA_A + S::DMA_B;  // direct-to-LDS loads per wave per stage
+    constexpr int AHEAD = S::STAGES - 1;        // stages in flight beyond the one being multiplied
+    constexpr int SLOTS = S::KSTEPS * 16;
+    static_assert(AHEAD >= 1 && (AHEAD - 1) * LOADS < 64, "vmcnt range");
+    static_assert(DOFF + (LOADS - 1) * SPACING < SLOTS, "loads must fit in one K step");
+
+    __shared__ __attribute__((aligned(1024))) char smem[S::LDS_BYTES];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
+
+    const int nwg = a.tiles_m * a.tiles_n;
+    int tm_idx, tn_idx;
+    grouped_tile(xcd_remap(blockIdx.x, nwg), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
+    const int m0 = tm_idx * S::BM, n0 = tn_idx * S::BN;
+    const int nk = (a.K + S::BK - 1) / S::BK;
+
+    // Per-lane load descriptors (constant over the K loop): byte offset in the
+    // stage's window, the column (A) or row (B) inside the stage that decides
+    // whether the chunk is inside K, and whether the row/column is inside M/N.
+    uint32_t off[LOADS];
+    int kin[LOADS];
+    bool ok[LOADS];
+#pragma unroll
+    for (int i = 0; i < S::DMA_A; ++i) {
+        ChunkRef c = dma_a_chunk<S>(wave, i, lane);
+        off[i] = (uint32_t)(c.row * a.lda * 2 + c.chunk * 16);
+        kin[i] = 8 * c.chunk;
+        ok[i] = m0 + c.row < a.M;
+    }
+#pragma unroll
+    for (int i = 0; i < S::DMA_B; ++i) {
+        ChunkRef c = dma_b_chunk<S>(wave, i, lane);
+        off[S::DMA_A + i] = (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16);
+        kin[S::DMA_A + i] = c.row;
+        ok[S::DMA_A + i] = n0 + 8 * c.chunk < a.N;
+    }
+
+    LDS_PTR(char) lds = (LDS_PTR(char))smem;
+    const _Float16 *a_tile = a.A + (int64_t)m0 * a.lda;
+    const _Float16 *b_tile = a.B + n0;
+
+    // Load j of stage kt into LDS buffer buf (stages past K load zeros).
+    auto dma = [&](int j, int kt, int buf) {
+        const int k0 = kt * S::BK;
+        const bool in = ok[j] && k0 + kin[j] < a.K;
+        if (j < S::DMA_A) {
+            const int4_t r = make_srd(a_tile + k0);
+            const uint32_t l = (uint32_t)(uintptr_t)(lds + buf * S::STAGE_BYTES + (wave * S::DMA_A + j) * 1024);
+            dma16(r, l, in ? off[j] : kOOB);
+        } else {
+            const int4_t r = make_srd(b_tile + (int64_t)k0 * a.ldb);
+            const uint32_t l = (uint32_t)(uintptr_t)(lds + buf * S::STAGE_BYTES + S::A_BYTES +
+                                                     (wave * S::DMA_B + (j - S::DMA_A)) * 1024);
+            dma16(r, l, in ? off[j] : kOOB);
+        }
+    };
+
+    float16_t acc[S::TN][S::TM];
+#pragma unroll
+    for (int i = 0; i < S::TN; ++i)
+#pragma unroll
+        for (int j = 0; j < S::TM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // f[1] starts at zero: the first step's slots 0..7 add 0 * 0.
+    Frags<S> f[2];
+#pragma unroll
+    for (int t = 0; t < S::TN; ++t) {
+        f[1].blo[t] = short4_t{0, 0, 0, 0};
+        f[1].bhi[t] = short4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int t = 0; t < S::TM; ++t) f[1].a[t] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+
+#pragma unroll
+    for (int s = 0; s < AHEAD; ++s)
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) dma(j, s, s);
+    wait_vmcnt<(AHEAD - 1) * LOADS>();
+    barrier_lds();
+
+    int buf = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int nbuf = buf == 0 ? S::STAGES - 1 : buf - 1;  // stage kt+AHEAD goes where stage kt-1 was
+        LDS_PTR(const char) sA = lds + buf * S::STAGE_BYTES;
+        LDS_PTR(const char) sB = sA + S::A_BYTES;
+        TLG_SCHED_FENCE();
+#pragma unroll
+        for (int q = 0; q < SLOTS; ++q) {
+            if (q < 8) {
+                mfma_tile<S>(f[1], 8 + q, acc);
+#pragma unroll
+                for (int r = 2 * q; r < 2 * q + 2; ++r)
+                    if (r < kFragReads<S>) frag_read<S>(f[0], sA, sB, wm0, wn0, 0, lane, r);
+            } else if (q < 8 + (S::KSTEPS - 1) * 16) {
+                const int ks = (q - 8) / 16, i = (q - 8) % 16;
+                mfma_tile<S>(f[ks & 1], i, acc);
+                if (i < kFragReads<S>) frag_read<S>(f[(ks + 1) & 1], sA, sB, wm0, wn0, ks + 1, lane, i);
+            } else {
+                mfma_tile<S>(f[1], q - 8 - (S::KSTEPS - 1) * 16, acc);
+            }
+            if (q >= DOFF && (q - DOFF) % SPACING == 0 && (q - DOFF) / SPACING < LOADS)
+                dma((q - DOFF) / SPACING, kt + AHEAD, nbuf);
+            TLG_SCHED_FENCE();
+        }
+        wait_vmcnt<(AHEAD - 1) * LOADS>();  // this wave's loads of stage kt+1 are in LDS
+        barrier_lds();                      // ... and every wave's; stage kt is no longer read
+        buf = buf == S::STAGES - 1 ? 0 : buf + 1;
+    }
+#pragma unroll
+    for (int i = 8; i < 16; ++i) mfma_tile<S>(f[1], i, acc);
+    // No load may still be writing LDS when the work-group ends.
+    wait_vmcnt<0>();
+
+    // Epilogue: ReLU, round to nearest even, 8-byte stores of four
+    // consecutive n; lanes outside the window get offset kOOB and the
+    // hardware drops their stores.
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc(a.C + (int64_t)m0 * a.ldc + n0, (short)0, (int)kRange, 0x00020000);
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm) {
+            const int mr = acc_m(wm0, tm, lane);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nr = acc_n(wn0, tn, 4 * q, lane);
+                const bool in = m0 + mr < a.M && n0 + nr < a.N;
+                const uint32_t o = in ? (uint32_t)((mr * a.ldc + nr) * 2) : kOOB;
+                half4_t h = {relu_to_half(acc[tn][tm][4 * q]), relu_to_half(acc[tn][tm][4 * q + 1]),
+                             relu_to_half(acc[tn][tm][4 * q + 2]), relu_to_half(acc[tn][tm][4 * q + 3])};
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(int2_t, h), rc, o, 0, 0);
+            }
+        }
+}
+
+using Pipe256x32 = TileShape<256, 256, 32, 2, 2, 4>;
+using Pipe256x64 = TileShape<256, 256, 64, 2, 2, 2>;
+
+const TileConfig kPipeConfigs[PIPE_CONFIGS] = {
+    {Pipe256x32::BM, Pipe256x32::BN, Pipe256x32::BK, Pipe256x32::NT, Pipe256x32::STAGES, "pipe_256x256x32_w2x2_s4"},
+    {Pipe256x64::BM, Pipe256x64::BN, Pipe256x64::BK, Pipe256x64::NT, Pipe256x64::STAGES, "pipe_256x256x64_w2x2_s2"},
+};
+
+template <class S, int SPACING, int DOFF>
+static hipError_t launch_pipe_t(const Problem &p, hipStream_t stream) {
+    KArgs a;
+    a.A = (const _Float16 *)p.A;
+    a.B = (const _Float16 *)p.B;
+    a.C = (_Float16 *)p.C;
+    a.W = nullptr;
+    a.M = (int)p.M;
+    a.N = (int)p.N;
+    a.K = (int)p.K;
+    a.lda = p.lda;
+    a.ldb = p.ldb;
+    a.ldc = p.ldc;
+    a.group_m = 4;
+    a.k_split = (int)p.K;
+    a.tiles_m = (a.M + S::BM - 1) / S::BM;
+    a.tiles_n = (a.N + S::BN - 1) / S::BN;
+    hipLaunchKernelGGL((k_tiled_pipe<S, SPACING, DOFF>), dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(S::NT), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream) {
+    switch (config) {
+        // four 32-deep stages: loads every 4 slots across the step
+        case PIPE_256x256x32: return launch_pipe_t<Pipe256x32, 4, 3>(p, stream);
+        // two 64-deep stages: the next stage's 16 loads go in early, every 2 slots
+        case PIPE_256x256x64: return launch_pipe_t<Pipe256x64, 2, 1>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace tlg

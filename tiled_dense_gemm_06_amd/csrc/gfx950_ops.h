@@ -1,0 +1,98 @@
+// Device-side building blocks shared by the gfx950 GEMM+ReLU kernels: vector
+// types, buffer descriptors, the direct global->LDS load, wait and barrier
+// helpers, the transposing B-fragment read and the ReLU + fp16 epilogue.
+#ifndef TLG_GFX950_OPS_H
+#define TLG_GFX950_OPS_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tlg {
+
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T) __attribute__((address_space(3))) T *
+
+// Every buffer descriptor covers offsets [0, kRange); a lane given offset
+// kOOB reads zeros. Host code guarantees every real offset is below kRange.
+constexpr uint32_t kRange = 0x7ffffff0u;
+constexpr uint32_t kOOB = 0x7ffffff0u;
+
+struct KArgs {
+    const _Float16 *A;
+    const _Float16 *B;
+    _Float16 *C;
+    float *W;          // split-K partials (split-K kernels only)
+    int M, N, K;
+    int64_t lda, ldb, ldc;
+    int tiles_m, tiles_n, group_m;
+    int k_split;       // K elements per split, a multiple of BK
+};
+
+typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef int int2_t __attribute__((ext_vector_type(2)));
+
+// Buffer descriptor: base address, stride 0, kRange bytes, word 3 = 0x00020000
+// (raw, untyped buffer on gfx9-class parts).
+__device__ __forceinline__ int4_t make_srd(const void *base) {
+    const uint64_t p = (uint64_t)base;
+    int4_t r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xffffu));
+    r[2] = (int)kRange;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from buffer offset `voff` into LDS at lds_base + 16*lane.
+// Issued through inline assembly: the compiler does not see an LDS write here,
+// so it does not add its own conservative vmcnt(0) wait before every later
+// LDS read. The kernels wait for these loads themselves (wait_vmcnt) before
+// the barrier that publishes a stage. M0 needs one wait state after its write.
+__device__ __forceinline__ void dma16(int4_t srd, uint32_t lds_base, uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base),
+        "v"(voff), "s"(srd)
+        : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// All LDS operations of this wave are complete, then the work-group barrier.
+// The wait is the compiler's own s_waitcnt (lgkmcnt(0), encoding 0xC07F on
+// gfx9-class parts: vmcnt and expcnt left at their maxima), so the compiler
+// knows that no LDS read is pending afterwards and adds no wait of its own
+// for them. The barrier is inline assembly with a "memory" clobber, which
+// keeps the compiler from moving memory accesses across it; it repeats the
+// wait so that nothing the compiler might place between the two is left
+// pending at the barrier (the repeated wait costs nothing).
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ReLU on the fp32 accumulator (everything not > 0 becomes +0, so -0 and NaN
+// give +0), then the fp16 conversion, which rounds to nearest even.
+__device__ __forceinline__ _Float16 relu_to_half(float x) { return (_Float16)(x > 0.0f ? x : 0.0f); }
+
+__device__ __forceinline__ half8_t read_b_frag(LDS_PTR(const char) base, int off_lo, int off_hi) {
+    short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(short4_t))(base + off_lo));
+    short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(short4_t))(base + off_hi));
+    short8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(half8_t, v);
+}
+
+}  // namespace tlg
+
+#endif

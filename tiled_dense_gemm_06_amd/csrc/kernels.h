@@ -30,14 +30,18 @@ enum DmaConfig { DMA_256x256x32 = 0, DMA_128x128x32 = 1, DMA_64x64x64 = 2, DMA_C
 enum GenConfig { GEN_128x128x32 = 0, GEN_64x64x32 = 1, GEN_CONFIGS = 2 };
 // split-K partial kernels (direct-to-LDS, aligned)
 enum SplitConfig { SPLIT_32x128x64 = 0, SPLIT_32x256x64 = 1, SPLIT_CONFIGS = 2 };
+// software-pipelined direct-to-LDS kernels (aligned, large problems)
+enum PipeConfig { PIPE_256x256x32 = 0, PIPE_256x256x64 = 1, PIPE_CONFIGS = 2 };
 
 extern const TileConfig kDmaConfigs[DMA_CONFIGS];
 extern const TileConfig kGenConfigs[GEN_CONFIGS];
 extern const TileConfig kSplitConfigs[SPLIT_CONFIGS];
+extern const TileConfig kPipeConfigs[PIPE_CONFIGS];
 
 // Launchers: enqueue on `stream`, return the launch status.
 hipError_t launch_tiled_dma(int config, const Problem &p, hipStream_t stream);
 hipError_t launch_tiled_general(int config, const Problem &p, hipStream_t stream);
+hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream);
 // Stage 1 writes fp32 partials W[s][m][n] (M x N packed per split) for
 // splits s covering k in [s*k_split, (s+1)*k_split); stage 2 sums them in
 // ascending s, applies ReLU and the fp16 cast, and writes C.
