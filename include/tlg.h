@@ -74,10 +74,11 @@ typedef struct {
 } tlg_plan_info;
 
 /* Creates a handle bound to the CURRENT HIP device. Checks that the device
- * is gfx950 (TLG_ERROR_NOT_SUPPORTED otherwise) and allocates the handle's
- * fp32 split-K workspace (TLG_ERROR_OUT_OF_MEMORY on failure). *out is set
- * only on success. One handle may be used by one stream at a time, because
- * calls on it share its workspace. */
+ * is gfx950 (TLG_ERROR_NOT_SUPPORTED otherwise), allocates the handle's
+ * split-K workspace (TLG_ERROR_OUT_OF_MEMORY on failure) and zeroes its
+ * small counter area, waiting for the device to finish that
+ * (TLG_ERROR_HIP on failure). *out is set only on success. One handle may be
+ * used by one stream at a time, because calls on it share its workspace. */
 tlg_status tlg_create(tlg_handle *out);
 
 /* Releases the handle and its workspace. NULL is a no-op. The caller must
@@ -137,7 +138,9 @@ tlg_status tlg_plan(int64_t M, int64_t N, int64_t K,
 /* Name of a tile configuration reported by tlg_plan ("" if unknown). */
 const char *tlg_plan_config_name(int32_t variant, int32_t config);
 
-/* Bytes of fp32 workspace a handle allocates at creation. */
+/* Bytes of workspace a handle allocates at creation (the split-K partials
+ * and the stream-K tile counters). tlg_plan assumes a 256-CU device when it
+ * sizes a stream-K grid; tlg_gemm_relu uses the handle's device. */
 int64_t tlg_workspace_bytes(void);
 
 /* 1 if a device architecture name (as in hipDeviceProp_t::gcnArchName, e.g.

@@ -291,6 +291,46 @@ extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A,
     }
 }
 
+// Stream-K bookkeeping: the ranges partition [0, total); sk_owner finds the
+// range of every iteration; every tile's parts, taken from its first owner to
+// its last, are the consecutive pieces of the tile in ascending k, each
+// assigned to slot 0 (the piece starts its work-group's range) or slot 1 (the
+// piece ends a range that began in an earlier tile), never both slots taken
+// by two split tiles of one work-group in the same slot. Returns the number
+// of violations.
+extern "C" long emu_check_streamk(long total, int G, int ipt) {
+    long bad = 0;
+    if (sk_begin(0, total, G) != 0 || sk_begin(G, total, G) != total) bad++;
+    for (int g = 0; g < G; ++g)
+        if (sk_begin(g + 1, total, G) < sk_begin(g, total, G)) bad++;
+    for (long x = 0; x < total; ++x) {
+        int g = sk_owner(x, total, G);
+        if (g < 0 || g >= G || !(sk_begin(g, total, G) <= x && x < sk_begin(g + 1, total, G))) bad++;
+    }
+    const long tiles = total / ipt;
+    std::vector<int> used(2 * (size_t)G, 0);
+    for (long t = 0; t < tiles; ++t) {
+        const long first = t * ipt, last = first + ipt;  // [first, last)
+        int g0 = sk_owner(first, total, G), g1 = sk_owner(last - 1, total, G);
+        long covered = first;
+        for (int g = g0; g <= g1; ++g) {
+            long b = sk_begin(g, total, G), e = sk_begin(g + 1, total, G);
+            if (b == e) continue;
+            long lo = std::max(b, first), hi = std::min(e, last);
+            if (lo != covered || hi <= lo) bad++;
+            covered = hi;
+            bool whole = lo == first && hi == last;
+            if (whole) { if (g0 != g1) bad++; continue; }
+            int slot = b >= first ? 0 : 1;
+            // the kernel's own rule: slot 0 iff the piece starts the range
+            if ((lo == b) != (slot == 0)) bad++;
+            if (used[2 * g + slot]++) bad++;
+        }
+        if (covered != last) bad++;
+    }
+    return bad;
+}
+
 // xcd_remap must be a bijection on [0, nwg) for every nwg.
 extern "C" long emu_check_remap(int max_nwg) {
     long bad = 0;

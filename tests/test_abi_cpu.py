@@ -70,9 +70,15 @@ def test_plan_shapes_of_the_workloads():
     assert tlg.plan(4096, 4096, 4096)["variant_name"] == "tiled_pipe"
     p = tlg.plan(3001, 2049, 1537)
     assert p["variant_name"] == "tiled_general"  # odd leading dimensions
-    p = tlg.plan(16, 14336, 4096)
-    assert p["variant_name"] == "splitk" and p["splits"] >= 2 and p["kernels"] == 2
-    assert p["workspace_bytes"] == p["splits"] * 16 * 14336 * 4 <= tlg.tlg_workspace_bytes()
+    p = tlg.plan(16, 14336, 4096)  # one work-group per 64 columns, K split among its waves
+    assert p["variant_name"] == "splitk" and p["config_name"] == "splitk_waves_32x64x64_w2_s3"
+    assert p["kernels"] == 1 and p["grid"] == 14336 // 64 and p["workspace_bytes"] == 0
+    p = tlg.plan(16, 14336, 4096, variant=tlg.TLG_VARIANT_SPLITK, config=2)  # stream-K
+    assert p["config_name"].startswith("streamk") and p["kernels"] == 1
+    assert p["grid"] == 2 * 256 and p["splits"] >= 2  # two work-groups per CU, ~4.6 per output tile
+    assert p["workspace_bytes"] == (64 << 10) + p["grid"] * 2 * 32 * 128 * 4 <= tlg.tlg_workspace_bytes()
+    assert tlg.plan(48, 14336, 4096)["config_name"].startswith("streamk")  # M above one strip
+    assert tlg.plan(16, 2048, 4096)["config_name"].startswith("streamk")  # too few strips
     assert tlg.plan(256, 256, 256)["variant_name"] == "tiled_dma"
     assert tlg.plan(5, 7, 0)["variant_name"] == "fill_zero"
     assert tlg.plan(0, 7, 9)["variant_name"] == "noop"
@@ -92,8 +98,10 @@ def test_forced_variants():
         tlg.plan(512, 512, 512, aligned=False, variant=tlg.TLG_VARIANT_TILED_DMA)
     with pytest.raises(tlg.TlgError):
         tlg.plan(16, 14336, 4095, variant=tlg.TLG_VARIANT_SPLITK)
-    p = tlg.plan(16, 14336, 4096, variant=tlg.TLG_VARIANT_SPLITK, splits=8)
-    assert p["splits"] == 8 and p["grid"] == 112 * 8
+    p = tlg.plan(16, 14336, 4096, variant=tlg.TLG_VARIANT_SPLITK, config=0, splits=8)
+    assert p["splits"] == 8 and p["grid"] == 112 * 8 and p["kernels"] == 2
+    p = tlg.plan(16, 256, 64, variant=tlg.TLG_VARIANT_SPLITK)  # stream-K: never more work-groups than iterations
+    assert p["grid"] == 2 * 1 and p["kernels"] == 1
     p = tlg.plan(300, 300, 300, variant=tlg.TLG_VARIANT_NAIVE)
     assert p["variant_name"] == "naive"
     p = tlg.plan(300, 304, 304, variant=tlg.TLG_VARIANT_TILED_GENERAL)
@@ -117,7 +125,7 @@ def test_split_counts_cover_k_without_empty_splits():
     for K in [512, 520, 1000, 4096, 4104, 8192, 65536]:
         for forced in [0, 2, 3, 7, 16, 64]:
             try:
-                p = tlg.plan(16, 1024, K - K % 8, variant=tlg.TLG_VARIANT_SPLITK, splits=forced)
+                p = tlg.plan(16, 1024, K - K % 8, variant=tlg.TLG_VARIANT_SPLITK, config=0, splits=forced)
             except tlg.TlgError:
                 continue
             s, bk = p["splits"], p["block_k"]
@@ -128,9 +136,12 @@ def test_split_counts_cover_k_without_empty_splits():
 
 
 def test_workspace_cap_lowers_splits():
-    st, info = nat.tlg_plan(64, 14336, 4096, A16, 4096, A16, 14336, A16, 14336, tlg.TLG_VARIANT_SPLITK, -1, 16,
-                            2 * 64 * 14336 * 4)
-    assert st == 0 and info.splits <= 2 and info.workspace_bytes <= 2 * 64 * 14336 * 4
+    cap = (64 << 10) + 2 * 64 * 14336 * 4
+    st, info = nat.tlg_plan(64, 14336, 4096, A16, 4096, A16, 14336, A16, 14336, tlg.TLG_VARIANT_SPLITK, 0, 16, cap)
+    assert st == 0 and info.splits <= 2 and info.workspace_bytes <= cap
+    cap = (64 << 10) + 100 * 2 * 32 * 128 * 4  # stream-K: the grid shrinks to fit its partial slots
+    st, info = nat.tlg_plan(64, 14336, 4096, A16, 4096, A16, 14336, A16, 14336, tlg.TLG_VARIANT_SPLITK, 2, 0, cap)
+    assert st == 0 and info.grid == 100 and info.workspace_bytes == cap
 
 
 def test_gemm_relu_rejects_null_handle():

@@ -43,9 +43,9 @@ def bits(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-def run(A, B, dev, variant=V_AUTO, splits=0, out=None):
+def run(A, B, dev, variant=V_AUTO, splits=0, out=None, config=-1):
     Ad, Bd = (to_dev(A, dev), to_dev(B, dev)) if isinstance(A, np.ndarray) else (A, B)
-    C = tlg.gemm_relu(Ad, Bd, out=out, variant=variant, splits=splits)
+    C = tlg.gemm_relu(Ad, Bd, out=out, variant=variant, config=config, splits=splits)
     torch.cuda.synchronize()
     return C
 
@@ -110,17 +110,52 @@ def test_ragged_full_output(dev, kind):
         assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("splits", [0, 1, 2, 4, 8, 16])
-def test_skinny_full_output(dev, splits):
+@pytest.mark.parametrize("config,splits", [(-1, 0), (0, 1), (0, 2), (0, 4), (0, 8), (0, 16), (1, 4), (2, 0), (3, 0)])
+def test_skinny_full_output(dev, config, splits):
     w = wl.WORKLOADS["skinny16x14336x4096"]
     A, B = wl.make_inputs(w)
     ref = oracle.gemm_relu(A, B)
-    v = V_AUTO if splits == 0 else V_SPLIT
-    got = bits(run(A, B, dev, variant=v, splits=splits))
-    assert_close(got, ref, f"skinny splits={splits}")
+    v = V_AUTO if config < 0 else V_SPLIT
+    got = bits(run(A, B, dev, variant=v, config=config, splits=splits))
+    assert_close(got, ref, f"skinny config={config} splits={splits}")
     Ai, Bi = wl.make_inputs(w, integer=True)
-    got = bits(run(Ai, Bi, dev, variant=v, splits=splits))
+    got = bits(run(Ai, Bi, dev, variant=v, config=config, splits=splits))
     assert np.array_equal(got, oracle.gemm_relu(Ai, Bi))
+
+
+@pytest.mark.parametrize("shape", [(16, 14336, 520), (1, 8, 8), (40, 264, 4096), (64, 1024, 2048), (7, 128, 8192),
+                                   (33, 392, 1000), (16, 256, 64)])
+def test_streamk_shapes(dev, shape):
+    """Stream-K on shapes with fewer iterations than work-groups, ragged M and N,
+    K tails, tiles split among many work-groups and whole tiles; C is
+    prefilled with NaN and has padding columns that must stay untouched. Each
+    shape runs twice: the tile counters must be back at zero after a call."""
+    M, N, K = shape
+    A, B = wl.make_random(M, N, K, seed=M + 3 * N + 7 * K, kind="integer_pos")
+    ref = oracle.gemm_relu(A, B)
+    for _ in range(2):
+        big = torch.full((M + 1, N + 8), float("nan"), dtype=torch.float16, device=dev)
+        tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), out=big[:M, :N], variant=V_SPLIT, config=2)
+        torch.cuda.synchronize()
+        allb = bits(big)
+        assert np.array_equal(allb[:M, :N], ref), shape
+        assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+
+
+@pytest.mark.parametrize("shape", [(16, 14336, 520), (1, 8, 8), (32, 264, 4096), (7, 128, 8192), (17, 392, 1000),
+                                   (16, 64, 32), (31, 1032, 264)])
+def test_wave_split_shapes(dev, shape):
+    """K split among the waves of one work-group: fewer K blocks than waves,
+    ragged M and N, K tails, one strip; NaN sentinel and padding columns."""
+    M, N, K = shape
+    A, B = wl.make_random(M, N, K, seed=M + 5 * N + 3 * K, kind="integer_pos")
+    ref = oracle.gemm_relu(A, B)
+    big = torch.full((M + 1, N + 8), float("nan"), dtype=torch.float16, device=dev)
+    tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), out=big[:M, :N], variant=V_SPLIT, config=3)
+    torch.cuda.synchronize()
+    allb = bits(big)
+    assert np.array_equal(allb[:M, :N], ref), shape
+    assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
 
 
 def test_skinny_without_split(dev):

@@ -37,6 +37,8 @@ def emu(tmp_path_factory):
     L.emu_gemm_relu.restype = i
     L.emu_check_remap.argtypes = [i]
     L.emu_check_remap.restype = l
+    L.emu_check_streamk.argtypes = [l, i, i]
+    L.emu_check_streamk.restype = l
     return L
 
 
@@ -55,6 +57,13 @@ def run_emu(L, config, A, B, splits=1, k_split=0):
 
 def test_xcd_remap_is_bijection(emu):
     assert emu.emu_check_remap(2100) == 0
+
+
+@pytest.mark.parametrize("tiles,ipt,G", [(112, 64, 512), (1, 1, 1), (1, 8, 8), (3, 5, 7), (7, 3, 21), (112, 64, 100),
+                                         (4, 128, 512), (512, 2, 512), (37, 11, 96)])
+def test_streamk_ranges(emu, tiles, ipt, G):
+    total = tiles * ipt
+    assert emu.emu_check_streamk(total, min(G, total), ipt) == 0
 
 
 # shapes that satisfy the direct-to-LDS conditions (K % 8 == 0, N % 8 == 0), several tiles, ragged tails

@@ -14,7 +14,8 @@
 
 struct tlg_context {
     int device;
-    float *workspace;
+    int cus;            // compute units of the device
+    float *workspace;   // kCounterBytes of stream-K tile counters, then fp32 partials
     int64_t workspace_bytes;
 };
 
@@ -24,6 +25,10 @@ constexpr int32_t kVersion = 100;  // 0.1.0
 // fp32 split-K partials: 32 MiB covers S x M x N x 4 bytes for the skinny
 // shapes the split path serves (S is lowered when a shape needs more).
 constexpr int64_t kWorkspaceBytes = 32ll << 20;
+// The first 64 KiB of the workspace hold the stream-K per-tile counters
+// (zeroed once at creation; every call leaves them zero); partials follow.
+constexpr int64_t kCounterBytes = 64ll << 10;
+constexpr int kPlanCUs = 256;  // tlg_plan plans for a 256-CU MI355X
 // Largest in-tile byte offset a buffer load may use (see the kernels).
 constexpr int64_t kMaxOffset = 0x7ffffff0ll - 16;
 constexpr int64_t kMaxDim = (1ll << 31) - 1024;
@@ -94,8 +99,9 @@ bool choose_splits(const tlg::Problem &p, const tlg::TileConfig &tc, int32_t for
 // A forced tile configuration index must exist for its variant.
 bool config_ok(int32_t config, int count) { return config < 0 || config < count; }
 
-tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int32_t splits, int64_t cap,
+tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int32_t splits, int64_t cap, int cus,
                      tlg_plan_info *o, int64_t *k_split_out) {
+    cap -= kCounterBytes;
     *k_split_out = 0;
     if (variant < TLG_VARIANT_AUTO || variant > TLG_VARIANT_TILED_PIPE) return TLG_ERROR_INVALID_VALUE;
     if (variant == TLG_VARIANT_AUTO && config >= 0) return TLG_ERROR_INVALID_VALUE;
@@ -123,18 +129,49 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
     // split-K for skinny M
     if (variant == TLG_VARIANT_SPLITK || (variant == TLG_VARIANT_AUTO && p.M <= 64 && p.K >= 512)) {
         if (!config_ok(config, tlg::SPLIT_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
-        const int cfg = config >= 0 ? config : tlg::SPLIT_32x128x64;
-        const tlg::TileConfig &tc = tlg::kSplitConfigs[cfg];
-        int s = 1;
-        int64_t k_split = 0;
-        bool ok = dma_ok(p, tc.bm, tc.bn, tc.bk) && choose_splits(p, tc, splits, cap, &s, &k_split);
-        if (ok && (s > 1 || variant == TLG_VARIANT_SPLITK)) {
-            const int64_t grid = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn) * s;
-            fill_info(o, TLG_VARIANT_SPLITK, cfg, &tc, s, 2, grid, (int64_t)s * p.M * p.N * 4);
-            *k_split_out = k_split;
+        // K split among the waves of a work-group per column strip, when M
+        // fits one strip and there are strips for at least half the CUs
+        const tlg::TileConfig &ts = tlg::kStripConfig;
+        const int64_t strips = ceil_div(p.N, ts.bn);
+        const bool strip_ok = p.M <= ts.bm && dma_ok(p, ts.bm, ts.bn, ts.bk) && strips <= 0x7fffffff;
+        int cfg = config;
+        if (cfg < 0) cfg = strip_ok && 2 * strips >= cus ? tlg::SPLIT_WAVES_32x64x64 : tlg::SPLIT_STREAMK_32x128x64;
+        if (cfg == tlg::SPLIT_WAVES_32x64x64) {
+            if (!strip_ok) return TLG_ERROR_NOT_SUPPORTED;
+            fill_info(o, TLG_VARIANT_SPLITK, cfg, &ts, ts.threads / 64, 1, strips, 0);
             return TLG_SUCCESS;
         }
-        if (variant == TLG_VARIANT_SPLITK) return TLG_ERROR_NOT_SUPPORTED;
+        if (cfg == tlg::SPLIT_STREAMK_32x128x64) {
+            // stream-K: as many work-groups as the CUs hold, each taking an
+            // equal range of the (tile, k) iterations
+            const tlg::TileConfig &tc = tlg::kStreamKConfig;
+            const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
+            const int64_t total = tiles * ceil_div(p.K, tc.bk);
+            const int64_t slot_bytes = 2ll * tc.bm * tc.bn * 4;
+            int64_t grid = (int64_t)cus * tlg::kStreamKBlocksPerCU;
+            if (grid > total) grid = total;
+            if (grid * slot_bytes > cap) grid = cap / slot_bytes;
+            const bool ok = dma_ok(p, tc.bm, tc.bn, tc.bk) && tiles * 4 <= kCounterBytes && grid >= 1 &&
+                            total * grid < (1ll << 62) && total < (1ll << 31);
+            if (ok) {
+                fill_info(o, TLG_VARIANT_SPLITK, cfg, &tc, (int)ceil_div(grid, tiles), 1, grid,
+                          kCounterBytes + grid * slot_bytes);
+                return TLG_SUCCESS;
+            }
+            if (variant == TLG_VARIANT_SPLITK) return TLG_ERROR_NOT_SUPPORTED;
+        } else {
+            const tlg::TileConfig &tc = tlg::kSplitConfigs[cfg];
+            int s = 1;
+            int64_t k_split = 0;
+            bool ok = dma_ok(p, tc.bm, tc.bn, tc.bk) && choose_splits(p, tc, splits, cap, &s, &k_split);
+            if (ok && (s > 1 || variant == TLG_VARIANT_SPLITK)) {
+                const int64_t grid = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn) * s;
+                fill_info(o, TLG_VARIANT_SPLITK, cfg, &tc, s, 2, grid, kCounterBytes + (int64_t)s * p.M * p.N * 4);
+                *k_split_out = k_split;
+                return TLG_SUCCESS;
+            }
+            if (variant == TLG_VARIANT_SPLITK) return TLG_ERROR_NOT_SUPPORTED;
+        }
     }
 
     // large aligned problems: the software-pipelined 256 x 256 tiles, when
@@ -207,7 +244,7 @@ tlg_status run(tlg_handle h, int32_t variant, int32_t config, int32_t splits, co
     if (dev != h->device) return TLG_ERROR_INVALID_VALUE;  // the handle's device must be current
     tlg_plan_info info;
     int64_t k_split = 0;
-    st = plan_impl(p, variant, config, splits, h->workspace_bytes, &info, &k_split);
+    st = plan_impl(p, variant, config, splits, h->workspace_bytes, h->cus, &info, &k_split);
     if (st != TLG_SUCCESS) return st;
     hipError_t e = hipSuccess;
     switch (info.variant) {
@@ -217,9 +254,16 @@ tlg_status run(tlg_handle h, int32_t variant, int32_t config, int32_t splits, co
         case TLG_VARIANT_TILED_DMA: e = tlg::launch_tiled_dma(info.config, p, stream); break;
         case TLG_VARIANT_TILED_GENERAL: e = tlg::launch_tiled_general(info.config, p, stream); break;
         case TLG_VARIANT_TILED_PIPE: e = tlg::launch_tiled_pipe(info.config, p, stream); break;
-        case TLG_VARIANT_SPLITK:
-            e = tlg::launch_splitk(info.config, info.splits, k_split, p, h->workspace, stream);
+        case TLG_VARIANT_SPLITK: {
+            float *partials = h->workspace + kCounterBytes / sizeof(float);
+            if (info.config == tlg::SPLIT_WAVES_32x64x64)
+                e = tlg::launch_skinny_strip(p, stream);
+            else if (info.config == tlg::SPLIT_STREAMK_32x128x64)
+                e = tlg::launch_streamk(p, (int)info.grid, partials, (int *)h->workspace, stream);
+            else
+                e = tlg::launch_splitk(info.config, info.splits, k_split, p, partials, stream);
             break;
+        }
         default: return TLG_ERROR_NOT_SUPPORTED;
     }
     return e == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
@@ -250,7 +294,7 @@ tlg_status tlg_plan(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
     if (st != TLG_SUCCESS) return st;
     tlg::Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc);
     int64_t k_split = 0;
-    return plan_impl(p, variant, config, splits, workspace_cap_bytes, out, &k_split);
+    return plan_impl(p, variant, config, splits, workspace_cap_bytes, kPlanCUs, out, &k_split);
 }
 
 const char *tlg_plan_config_name(int32_t variant, int32_t config) {
@@ -260,7 +304,9 @@ const char *tlg_plan_config_name(int32_t variant, int32_t config) {
         case TLG_VARIANT_TILED_GENERAL:
             return (config >= 0 && config < tlg::GEN_CONFIGS) ? tlg::kGenConfigs[config].name : "";
         case TLG_VARIANT_SPLITK:
-            return (config >= 0 && config < tlg::SPLIT_CONFIGS) ? tlg::kSplitConfigs[config].name : "";
+            if (config == tlg::SPLIT_STREAMK_32x128x64) return tlg::kStreamKConfig.name;
+            if (config == tlg::SPLIT_WAVES_32x64x64) return tlg::kStripConfig.name;
+            return (config >= 0 && config < tlg::SPLIT_TWO_KERNEL_CONFIGS) ? tlg::kSplitConfigs[config].name : "";
         case TLG_VARIANT_TILED_PIPE:
             return (config >= 0 && config < tlg::PIPE_CONFIGS) ? tlg::kPipeConfigs[config].name : "";
         case TLG_VARIANT_NAIVE: return "naive_16x16";
@@ -288,12 +334,21 @@ tlg_status tlg_create(tlg_handle *out) {
     tlg_context *ctx = new (std::nothrow) tlg_context;
     if (!ctx) return TLG_ERROR_OUT_OF_MEMORY;
     ctx->device = dev;
+    ctx->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : kPlanCUs;
     ctx->workspace_bytes = kWorkspaceBytes;
     ctx->workspace = nullptr;
     if (hipMalloc((void **)&ctx->workspace, (size_t)kWorkspaceBytes) != hipSuccess) {
         (void)hipGetLastError();  // clear the sticky allocation error
         delete ctx;
         return TLG_ERROR_OUT_OF_MEMORY;
+    }
+    // the stream-K counters start at zero (each call leaves them zero)
+    if (hipMemset(ctx->workspace, 0, (size_t)kCounterBytes) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(ctx->workspace);
+        delete ctx;
+        return TLG_ERROR_HIP;
     }
     *out = ctx;
     return TLG_SUCCESS;

@@ -34,28 +34,6 @@
 
 namespace tlg {
 
-// The tile product of one LDS stage: for each 16-wide k-step, read the
-// operand fragments of every MFMA tile of this wave and accumulate.
-template <class S>
-__device__ __forceinline__ void mma_stage(LDS_PTR(const char) sA, LDS_PTR(const char) sB, int wm0, int wn0, int lane,
-                                          float16_t (&acc)[S::TN][S::TM]) {
-#pragma unroll
-    for (int s = 0; s < S::KSTEPS; ++s) {
-        half8_t bf[S::TN], af[S::TM];
-#pragma unroll
-        for (int tn = 0; tn < S::TN; ++tn)
-            bf[tn] = read_b_frag(sB, frag_b_offset<S>(wn0, tn, s, 0, lane), frag_b_offset<S>(wn0, tn, s, 1, lane));
-#pragma unroll
-        for (int tm = 0; tm < S::TM; ++tm)
-            af[tm] = *(LDS_PTR(const half8_t))(sA + frag_a_offset<S>(wm0, tm, s, lane));
-#pragma unroll
-        for (int tn = 0; tn < S::TN; ++tn)
-#pragma unroll
-            for (int tm = 0; tm < S::TM; ++tm)
-                acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[tn], af[tm], acc[tn][tm], 0, 0, 0);
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Tiled kernel fed by direct global->LDS loads. Requirements (checked on the
 // host): A, B, C (and W) 16-byte aligned; lda, ldb, ldc, K and N multiples of
@@ -356,7 +334,7 @@ const TileConfig kGenConfigs[GEN_CONFIGS] = {
     {Gen128::BM, Gen128::BN, Gen128::BK, Gen128::NT, 2, "gen_128x128x32_w2x2"},
     {Gen64::BM, Gen64::BN, Gen64::BK, Gen64::NT, 2, "gen_64x64x32_w2x2"},
 };
-const TileConfig kSplitConfigs[SPLIT_CONFIGS] = {
+const TileConfig kSplitConfigs[SPLIT_TWO_KERNEL_CONFIGS] = {
     {Split32x128::BM, Split32x128::BN, Split32x128::BK, Split32x128::NT, Split32x128::STAGES,
      "splitk_32x128x64_w1x4_s4"},
     {Split32x256::BM, Split32x256::BN, Split32x256::BK, Split32x256::NT, Split32x256::STAGES,

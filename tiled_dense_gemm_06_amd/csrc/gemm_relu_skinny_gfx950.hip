@@ -1,0 +1,171 @@
+// Skinny problems (M <= 32, many columns): split-K inside one work-group.
+//
+// The two-stage split-K of the TileLang article (aiwiki.ai/wiki/tilelang,
+// "Adoption by DeepSeek": K partitioned for small-batch decoding, partial
+// results reduced afterwards), arranged so that the reduction never leaves a
+// work-group. With M this small the kernel is bound by reading B once from
+// HBM, so it is built for memory-level parallelism rather than for the
+// matrix cores:
+//  * one work-group per 64-column strip of B and C;
+//  * its waves split the strip's K blocks (wave w of W takes blocks w,
+//    w + W, ...), each with a private ring of direct-to-LDS loads, so no wave
+//    ever waits for another inside the K loop and W x STAGES blocks per
+//    work-group are in flight;
+//  * each wave multiplies its blocks with v_mfma_f32_32x32x16_f16 (B
+//    transposed on the way out of LDS by ds_read_b64_tr_b16, M padded to 32
+//    with zero rows that cost no memory traffic);
+//  * at the end the waves' partial tiles meet in LDS and are summed in wave
+//    order (a fixed order, so results are deterministic), then ReLU and the
+//    round-to-nearest-even fp16 cast.
+// Block depth, stage count and waves were chosen by measurement on MI355X
+// (64-deep blocks keep every row piece of B a whole 128-byte line).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gfx950_ops.h"
+#include "kernels.h"
+#include "tile_layout.h"
+
+namespace tlg {
+
+// Wait until at most `n` blocks of this wave are still loading (n < STAGES).
+template <int LOADS, int STAGES>
+__device__ __forceinline__ void wait_blocks(int n) {
+    static_assert(STAGES <= 4, "waits written for up to four stages");
+    if (STAGES > 3 && n >= 3)
+        wait_vmcnt<(STAGES > 3 ? 3 : 0) * LOADS>();
+    else if (STAGES > 2 && n >= 2)
+        wait_vmcnt<(STAGES > 2 ? 2 : 0) * LOADS>();
+    else if (n >= 1)
+        wait_vmcnt<LOADS>();
+    else
+        wait_vmcnt<0>();
+}
+
+template <class S, int W>
+__global__ __launch_bounds__(W * 64) void k_skinny_strip(const KArgs a) {
+    static_assert(S::WAVES == 1, "one wave per ring");
+    constexpr int LOADS = S::DMA_A + S::DMA_B;  // loads per block per wave
+    constexpr int RING = S::STAGES * S::STAGE_BYTES;
+    constexpr int TILE = S::BM * S::BN;
+    static_assert(TILE * 4 <= RING, "partials fit in the rings");
+    __shared__ __attribute__((aligned(1024))) char smem[W * RING];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = blockIdx.x * S::BN;
+    const int nkb = (a.K + S::BK - 1) / S::BK;                         // K blocks of the strip
+    const int mine = nkb > wave ? (nkb - wave + W - 1) / W : 0;        // this wave's blocks
+
+    LDS_PTR(char) ring = (LDS_PTR(char))smem + wave * RING;
+
+    // Block j of this wave (block wave + W j of the strip) into stage buffer buf.
+    auto issue = [&](int j, int buf) {
+        const int k0 = (wave + W * j) * S::BK;
+        const int4_t ra = make_srd(a.A + k0);
+        const int4_t rb = make_srd(a.B + (int64_t)k0 * a.ldb + n0);
+        LDS_PTR(char) st = ring + buf * S::STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < S::DMA_A; ++i) {
+            const ChunkRef c = dma_a_chunk<S>(0, i, lane);
+            const bool in = c.row < a.M && k0 + 8 * c.chunk < a.K;
+            dma16(ra, (uint32_t)(uintptr_t)(st + i * 1024), in ? (uint32_t)(c.row * a.lda * 2 + c.chunk * 16) : kOOB);
+        }
+#pragma unroll
+        for (int i = 0; i < S::DMA_B; ++i) {
+            const ChunkRef c = dma_b_chunk<S>(0, i, lane);
+            const bool in = n0 + 8 * c.chunk < a.N && k0 + c.row < a.K;
+            dma16(rb, (uint32_t)(uintptr_t)(st + S::A_BYTES + i * 1024),
+                  in ? (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16) : kOOB);
+        }
+    };
+
+    float16_t acc[S::TN][S::TM];
+#pragma unroll
+    for (int i = 0; i < S::TN; ++i)
+#pragma unroll
+        for (int j = 0; j < S::TM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+#pragma unroll
+    for (int s = 0; s < S::STAGES; ++s)
+        if (s < mine) issue(s, s);
+    int buf = 0;
+    for (int j = 0; j < mine; ++j) {
+        // this wave's blocks still in flight behind block j may keep loading
+        wait_blocks<LOADS, S::STAGES>(imin(S::STAGES - 1, mine - 1 - j));
+        LDS_PTR(const char) st = ring + buf * S::STAGE_BYTES;
+        mma_stage<S>(st, st + S::A_BYTES, 0, 0, lane, acc);
+        // every read of this buffer is complete before the block STAGES ahead
+        // is loaded into it (compiler-visible lgkmcnt(0))
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        if (j + S::STAGES < mine) issue(j + S::STAGES, buf);
+        buf = buf + 1 == S::STAGES ? 0 : buf + 1;
+    }
+
+    // The waves' partial tiles meet in LDS (the rings are no longer used),
+    // laid out [wave][m][n] fp32.
+    __syncthreads();
+    float *part = (float *)smem;
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm) {
+            const int mr = acc_m(0, tm, lane);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nr = acc_n(0, tn, 4 * q, lane);
+                float4_t v = {acc[tn][tm][4 * q], acc[tn][tm][4 * q + 1], acc[tn][tm][4 * q + 2],
+                              acc[tn][tm][4 * q + 3]};
+                *(float4_t *)(part + wave * TILE + mr * S::BN + nr) = v;
+            }
+        }
+    __syncthreads();
+    // Thread t finishes four consecutive columns: sum over the waves in order.
+    for (int e = 4 * tid; e < TILE; e += 4 * W * 64) {
+        const int m = e / S::BN, n = e % S::BN;
+        if (m >= a.M || n0 + n >= a.N) continue;
+        float4_t s = *(const float4_t *)(part + e);
+#pragma unroll
+        for (int w = 1; w < W; ++w) {
+            const float4_t v = *(const float4_t *)(part + w * TILE + e);
+            s[0] = s[0] + v[0];
+            s[1] = s[1] + v[1];
+            s[2] = s[2] + v[2];
+            s[3] = s[3] + v[3];
+        }
+        half4_t h = {relu_to_half(s[0]), relu_to_half(s[1]), relu_to_half(s[2]), relu_to_half(s[3])};
+        *(half4_t *)(a.C + (int64_t)m * a.ldc + n0 + n) = h;
+    }
+}
+
+using Strip32x64 = TileShape<32, 64, 64, 1, 1, 3>;
+constexpr int kStripWaves = 2;
+
+const TileConfig kStripConfig = {Strip32x64::BM, Strip32x64::BN, Strip32x64::BK, kStripWaves * 64,
+                                 Strip32x64::STAGES, "splitk_waves_32x64x64_w2_s3"};
+
+hipError_t launch_skinny_strip(const Problem &p, hipStream_t stream) {
+    KArgs a;
+    a.A = (const _Float16 *)p.A;
+    a.B = (const _Float16 *)p.B;
+    a.C = (_Float16 *)p.C;
+    a.W = nullptr;
+    a.M = (int)p.M;
+    a.N = (int)p.N;
+    a.K = (int)p.K;
+    a.lda = p.lda;
+    a.ldb = p.ldb;
+    a.ldc = p.ldc;
+    a.tiles_m = 1;
+    a.tiles_n = (int)((p.N + Strip32x64::BN - 1) / Strip32x64::BN);
+    a.group_m = 1;
+    a.k_split = (int)p.K;
+    hipLaunchKernelGGL((k_skinny_strip<Strip32x64, kStripWaves>), dim3((unsigned)a.tiles_n), dim3(kStripWaves * 64), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace tlg

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tile_layout.h"
+
 namespace tlg {
 
 
@@ -91,6 +93,28 @@ __device__ __forceinline__ half8_t read_b_frag(LDS_PTR(const char) base, int off
     short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(short4_t))(base + off_hi));
     short8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(half8_t, v);
+}
+
+// The tile product of one LDS stage: for each 16-wide k-step, read the
+// operand fragments of every MFMA tile of this wave and accumulate.
+template <class S>
+__device__ __forceinline__ void mma_stage(LDS_PTR(const char) sA, LDS_PTR(const char) sB, int wm0, int wn0, int lane,
+                                          float16_t (&acc)[S::TN][S::TM]) {
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; ++s) {
+        half8_t bf[S::TN], af[S::TM];
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn)
+            bf[tn] = read_b_frag(sB, frag_b_offset<S>(wn0, tn, s, 0, lane), frag_b_offset<S>(wn0, tn, s, 1, lane));
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm)
+            af[tm] = *(LDS_PTR(const half8_t))(sA + frag_a_offset<S>(wm0, tm, s, lane));
+#pragma unroll
+        for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+            for (int tm = 0; tm < S::TM; ++tm)
+                acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[tn], af[tm], acc[tn][tm], 0, 0, 0);
+    }
 }
 
 }  // namespace tlg

@@ -29,13 +29,17 @@ enum DmaConfig { DMA_256x256x32 = 0, DMA_128x128x32 = 1, DMA_64x64x64 = 2, DMA_C
 // register-staged (any alignment) configurations
 enum GenConfig { GEN_128x128x32 = 0, GEN_64x64x32 = 1, GEN_CONFIGS = 2 };
 // split-K partial kernels (direct-to-LDS, aligned)
-enum SplitConfig { SPLIT_32x128x64 = 0, SPLIT_32x256x64 = 1, SPLIT_CONFIGS = 2 };
+// (indices 0 and 1: two kernels, partials then an ordered reduce; index 2:
+// one stream-K kernel that finishes split tiles itself; index 3: 64-column
+// strips, K split among work-groups and their waves, M <= 32)
+enum SplitConfig { SPLIT_32x128x64 = 0, SPLIT_32x256x64 = 1, SPLIT_TWO_KERNEL_CONFIGS = 2,
+                   SPLIT_STREAMK_32x128x64 = 2, SPLIT_WAVES_32x64x64 = 3, SPLIT_CONFIGS = 4 };
 // software-pipelined direct-to-LDS kernels (aligned, large problems)
 enum PipeConfig { PIPE_256x256x32 = 0, PIPE_256x256x64 = 1, PIPE_CONFIGS = 2 };
 
 extern const TileConfig kDmaConfigs[DMA_CONFIGS];
 extern const TileConfig kGenConfigs[GEN_CONFIGS];
-extern const TileConfig kSplitConfigs[SPLIT_CONFIGS];
+extern const TileConfig kSplitConfigs[SPLIT_TWO_KERNEL_CONFIGS];
 extern const TileConfig kPipeConfigs[PIPE_CONFIGS];
 
 // Launchers: enqueue on `stream`, return the launch status.
@@ -47,6 +51,17 @@ hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream);
 // ascending s, applies ReLU and the fp16 cast, and writes C.
 hipError_t launch_splitk(int config, int splits, int64_t k_split, const Problem &p, float *workspace,
                          hipStream_t stream);
+// Stream-K split of K for skinny problems: `grid` work-groups take equal
+// ranges of the (tile, k) iteration sequence; split tiles are finished in the
+// same kernel through `partials` (grid x 2 x BM x BN fp32) and `counters`
+// (one int per tile, zero on entry and on exit).
+extern const TileConfig kStreamKConfig;
+constexpr int kStreamKBlocksPerCU = 2;  // 80 KiB of LDS per work-group, 160 KiB per CU
+hipError_t launch_streamk(const Problem &p, int grid, float *partials, int *counters, hipStream_t stream);
+// Skinny strips (M <= 32): one work-group per 64 columns, K split among its
+// waves and reduced in LDS in wave order.
+extern const TileConfig kStripConfig;
+hipError_t launch_skinny_strip(const Problem &p, hipStream_t stream);
 hipError_t launch_naive(const Problem &p, hipStream_t stream);
 hipError_t launch_fill_zero(const Problem &p, hipStream_t stream);
 

@@ -27,6 +27,8 @@
 #ifndef TLG_TILE_LAYOUT_H
 #define TLG_TILE_LAYOUT_H
 
+#include <stdint.h>
+
 #if defined(__HIPCC__)
 #define TLG_HD __host__ __device__ __forceinline__
 #else
@@ -177,6 +179,13 @@ TLG_HD void grouped_tile(int q, int tiles_m, int tiles_n, int group_m, int *tm, 
     *tm = first_m + r % gsz;
     *tn = r / gsz;
 }
+
+// ---- stream-K ranges ----
+// total iterations are split among G work-groups: work-group g takes
+// [sk_begin(g), sk_begin(g + 1)); sk_owner(x) is the work-group whose range
+// holds iteration x (the largest g with sk_begin(g) <= x).
+TLG_HD int64_t sk_begin(int g, int64_t total, int G) { return (int64_t)g * total / G; }
+TLG_HD int sk_owner(int64_t x, int64_t total, int G) { return (int)(((x + 1) * (int64_t)G - 1) / total); }
 
 }  // namespace tlg
 
