@@ -98,59 +98,18 @@ void run_dma(const Problem &p, bool split, Errs &er, std::vector<int> &cover) {
             }
             const int m0 = tmi * S::BM, n0 = tni * S::BN;
             const int kbeg = split ? y * p.k_split : 0;
-            const int kend = split ? std::min(p.K, kbeg + p.k_split) : p.K;
+            // the tiled kernels' loads stop at kmain (K, or the largest multiple
+            // of 8 below K when K or N is not a multiple of 8)
+            const int kmain = (p.K % 8 == 0 && p.N % 8 == 0) ? p.K : 8 * ((p.K - 1) / 8);
+            const int kend = split ? std::min(p.K, kbeg + p.k_split) : kmain;
             const int nk = kend > kbeg ? (kend - kbeg + S::BK - 1) / S::BK : 0;
             // accumulators: [wave][tn][tm][lane][16]
             std::vector<float> acc((size_t)S::WAVES * S::TN * S::TM * 64 * 16, 0.0f);
-            for (int kt = 0; kt < nk; ++kt) {
-                const int k0 = kbeg + kt * S::BK;
-                std::fill(lds.begin(), lds.end(), 0xAB);
-                std::fill(lds_w.begin(), lds_w.end(), 0);
-                for (int w = 0; w < S::WAVES; ++w)
-                    for (int lane = 0; lane < 64; ++lane) {
-                        for (int i = 0; i < S::DMA_A; ++i) {
-                            ChunkRef c = dma_a_chunk<S>(w, i, lane);
-                            int dst = (w * S::DMA_A + i) * 1024 + lane * 16;
-                            bool ok = m0 + c.row < p.M && k0 + 8 * c.chunk < kend;
-                            for (int b = 0; b < 16; ++b) {
-                                if (dst + b >= S::A_BYTES) { er.lds_oob++; continue; }
-                                if (lds_w[dst + b]++) er.lds_multi++;
-                            }
-                            for (int e = 0; e < 8; ++e) {
-                                uint16_t v = 0;
-                                if (ok) {
-                                    long row = m0 + c.row, col = k0 + 8 * c.chunk + e;
-                                    if (row >= p.M || col >= p.K || col >= p.lda) er.oob_global++;
-                                    else v = p.A[row * p.lda + col];
-                                }
-                                memcpy(&lds[dst + 2 * e], &v, 2);
-                            }
-                        }
-                        for (int i = 0; i < S::DMA_B; ++i) {
-                            ChunkRef c = dma_b_chunk<S>(w, i, lane);
-                            int dst = S::A_BYTES + (w * S::DMA_B + i) * 1024 + lane * 16;
-                            bool ok = n0 + 8 * c.chunk < p.N && k0 + c.row < kend;
-                            for (int b = 0; b < 16; ++b) {
-                                if (dst + b >= S::STAGE_BYTES) { er.lds_oob++; continue; }
-                                if (lds_w[dst + b]++) er.lds_multi++;
-                            }
-                            for (int e = 0; e < 8; ++e) {
-                                uint16_t v = 0;
-                                if (ok) {
-                                    long row = k0 + c.row, col = n0 + 8 * c.chunk + e;
-                                    if (row >= p.K || col >= p.N || col >= p.ldb) er.oob_global++;
-                                    else v = p.B[row * p.ldb + col];
-                                }
-                                memcpy(&lds[dst + 2 * e], &v, 2);
-                            }
-                        }
-                    }
-                for (int b = 0; b < S::STAGE_BYTES; ++b)
-                    if (lds_w[b] != 1) er.lds_multi++;
-                // fragments and MFMAs
+            // fragments and MFMAs of the first nsteps k-steps of the stage in `lds`
+            auto mfma_from_lds = [&](int nsteps) {
                 for (int w = 0; w < S::WAVES; ++w) {
                     const int wm0 = (w / S::WN) * S::WTM, wn0 = (w % S::WN) * S::WTN;
-                    for (int s = 0; s < S::KSTEPS; ++s) {
+                    for (int s = 0; s < nsteps; ++s) {
                         // bf[tn][lane][8], af[tm][lane][8]
                         std::vector<float> bf((size_t)S::TN * 64 * 8), af((size_t)S::TM * 64 * 8);
                         for (int tn = 0; tn < S::TN; ++tn)
@@ -215,6 +174,78 @@ void run_dma(const Problem &p, bool split, Errs &er, std::vector<int> &cover) {
                                     }
                     }
                 }
+                        };
+            for (int kt = 0; kt < nk; ++kt) {
+                const int k0 = kbeg + kt * S::BK;
+                std::fill(lds.begin(), lds.end(), 0xAB);
+                std::fill(lds_w.begin(), lds_w.end(), 0);
+                for (int w = 0; w < S::WAVES; ++w)
+                    for (int lane = 0; lane < 64; ++lane) {
+                        for (int i = 0; i < S::DMA_A; ++i) {
+                            ChunkRef c = dma_a_chunk<S>(w, i, lane);
+                            int dst = (w * S::DMA_A + i) * 1024 + lane * 16;
+                            bool ok = m0 + c.row < p.M && k0 + 8 * c.chunk < kend;
+                            for (int b = 0; b < 16; ++b) {
+                                if (dst + b >= S::A_BYTES) { er.lds_oob++; continue; }
+                                if (lds_w[dst + b]++) er.lds_multi++;
+                            }
+                            for (int e = 0; e < 8; ++e) {
+                                uint16_t v = 0;
+                                if (ok) {
+                                    long row = m0 + c.row, col = k0 + 8 * c.chunk + e;
+                                    if (row >= p.M || col >= p.K || col >= p.lda) er.oob_global++;
+                                    else v = p.A[row * p.lda + col];
+                                }
+                                memcpy(&lds[dst + 2 * e], &v, 2);
+                            }
+                        }
+                        for (int i = 0; i < S::DMA_B; ++i) {
+                            ChunkRef c = dma_b_chunk<S>(w, i, lane);
+                            int dst = S::A_BYTES + (w * S::DMA_B + i) * 1024 + lane * 16;
+                            bool ok = n0 + 8 * c.chunk < p.N && k0 + c.row < kend;
+                            for (int b = 0; b < 16; ++b) {
+                                if (dst + b >= S::STAGE_BYTES) { er.lds_oob++; continue; }
+                                if (lds_w[dst + b]++) er.lds_multi++;
+                            }
+                            for (int e = 0; e < 8; ++e) {
+                                uint16_t v = 0;
+                                if (ok) {
+                                    long row = k0 + c.row, col = n0 + 8 * c.chunk + e;
+                                    // past column N only when N is not a multiple of 8, and then at
+                                    // most into the next row, which must exist
+                                    long idx = row * p.ldb + col;
+                                    if (row >= p.K || (col >= p.N && p.N % 8 == 0) ||
+                                        idx >= (long)(p.K - 1) * p.ldb + p.N)
+                                        er.oob_global++;
+                                    else v = p.B[idx];
+                                }
+                                memcpy(&lds[dst + 2 * e], &v, 2);
+                            }
+                        }
+                    }
+                for (int b = 0; b < S::STAGE_BYTES; ++b)
+                    if (lds_w[b] != 1) er.lds_multi++;
+                mfma_from_lds(S::KSTEPS);
+            }
+            // rows kmain .. K-1: one zero-padded 16-deep block staged element by
+            // element (A chunks 0-1 of every row, B rows 0-15), one k-step
+            if (!split && kmain < p.K) {
+                std::fill(lds.begin(), lds.end(), 0xAB);
+                for (int row = 0; row < S::BM; ++row)
+                    for (int chunk = 0; chunk < 2; ++chunk)
+                        for (int e = 0; e < 8; ++e) {
+                            long m = m0 + row, k = kmain + 8 * chunk + e;
+                            uint16_t v = (m < p.M && k < p.K) ? p.A[m * p.lda + k] : 0;
+                            memcpy(&lds[lds_a_offset<S>(row, chunk) + 2 * e], &v, 2);
+                        }
+                for (int row = 0; row < 16; ++row)
+                    for (int chunk = 0; chunk < S::CB; ++chunk)
+                        for (int e = 0; e < 8; ++e) {
+                            long k = kmain + row, n = n0 + 8 * chunk + e;
+                            uint16_t v = (k < p.K && n < p.N) ? p.B[k * p.ldb + n] : 0;
+                            memcpy(&lds[S::A_BYTES + lds_b_offset<S>(row, chunk) + 2 * e], &v, 2);
+                        }
+                mfma_from_lds(1);
             }
             // epilogue
             for (int w = 0; w < S::WAVES; ++w) {

@@ -68,8 +68,8 @@ def test_check_args(args, expect):
 def test_plan_shapes_of_the_workloads():
     assert tlg.plan(8192, 8192, 8192)["config_name"] == "pipe_256x256x64_w2x2_s2"
     assert tlg.plan(4096, 4096, 4096)["variant_name"] == "tiled_pipe"
-    p = tlg.plan(3001, 2049, 1537)
-    assert p["variant_name"] == "tiled_general"  # odd leading dimensions
+    p = tlg.plan(3001, 2049, 1537)  # odd sizes and leading dimensions: direct-to-LDS loads, staged K tail
+    assert p["variant_name"] == "tiled_dma" and p["config_name"] == "dma_128x128x32_w2x2_s4"
     p = tlg.plan(16, 14336, 4096)  # one work-group per 64 columns, K split among its waves
     assert p["variant_name"] == "splitk" and p["config_name"] == "splitk_waves_32x64x64_w2_s3"
     assert p["kernels"] == 1 and p["grid"] == 14336 // 64 and p["workspace_bytes"] == 0
@@ -85,17 +85,25 @@ def test_plan_shapes_of_the_workloads():
     assert tlg.plan(7, 0, 9)["variant_name"] == "noop"
 
 
-def test_plan_alignment_decides_dma():
-    assert tlg.plan(512, 512, 512, aligned=False)["variant_name"] == "tiled_general"
-    assert tlg.plan(512, 512, 512, lda=520)["variant_name"] == "tiled_dma"
-    assert tlg.plan(512, 512, 512, lda=513)["variant_name"] == "tiled_general"
-    assert tlg.plan(512, 516, 512)["variant_name"] == "tiled_general"  # N % 8 != 0
-    assert tlg.plan(512, 512, 500)["variant_name"] == "tiled_general"  # K % 8 != 0
+def test_plan_alignment_and_edges():
+    # the tiled direct-to-LDS kernels take any 2-byte aligned data
+    for kw in [dict(aligned=False), dict(lda=520), dict(lda=513), {}, dict(ldc=515)]:
+        assert tlg.plan(512, 512, 512, **kw)["variant_name"] == "tiled_dma", kw
+    assert tlg.plan(512, 516, 512)["variant_name"] == "tiled_dma"  # N % 8 != 0
+    assert tlg.plan(512, 512, 500)["variant_name"] == "tiled_dma"  # K % 8 != 0
+    # a chunk crossing the N edge must stay inside the next row of B
+    assert tlg.plan(512, 5, 512)["variant_name"] == "tiled_general"
+    assert tlg.plan(512, 5, 512, ldb=8)["variant_name"] == "tiled_dma"
+    # the skinny kernels need aligned data
+    assert tlg.plan(16, 14336, 4096)["variant_name"] == "splitk"
+    assert tlg.plan(16, 14336, 4096, aligned=False)["variant_name"] != "splitk"
+    assert tlg.plan(16, 14336, 4095)["variant_name"] != "splitk"
 
 
 def test_forced_variants():
-    with pytest.raises(tlg.TlgError):
-        tlg.plan(512, 512, 512, aligned=False, variant=tlg.TLG_VARIANT_TILED_DMA)
+    with pytest.raises(tlg.TlgError):  # chunks crossing N would leave the next row of B
+        tlg.plan(512, 5, 512, variant=tlg.TLG_VARIANT_TILED_DMA)
+    assert tlg.plan(512, 512, 512, aligned=False, variant=tlg.TLG_VARIANT_TILED_DMA)["variant_name"] == "tiled_dma"
     with pytest.raises(tlg.TlgError):
         tlg.plan(16, 14336, 4095, variant=tlg.TLG_VARIANT_SPLITK)
     p = tlg.plan(16, 14336, 4096, variant=tlg.TLG_VARIANT_SPLITK, config=0, splits=8)
@@ -106,10 +114,12 @@ def test_forced_variants():
     assert p["variant_name"] == "naive"
     p = tlg.plan(300, 304, 304, variant=tlg.TLG_VARIANT_TILED_GENERAL)
     assert p["variant_name"] == "tiled_general"
-    p = tlg.plan(300, 304, 304, variant=tlg.TLG_VARIANT_TILED_PIPE)  # forced: any aligned shape
+    p = tlg.plan(300, 304, 304, variant=tlg.TLG_VARIANT_TILED_PIPE)  # forced: any shape
     assert p["variant_name"] == "tiled_pipe" and p["grid"] == 2 * 2
+    p = tlg.plan(300, 300, 301, aligned=False, variant=tlg.TLG_VARIANT_TILED_PIPE)
+    assert p["variant_name"] == "tiled_pipe"
     with pytest.raises(tlg.TlgError):
-        tlg.plan(300, 300, 300, variant=tlg.TLG_VARIANT_TILED_PIPE)  # N % 8 != 0
+        tlg.plan(300, 7, 300, variant=tlg.TLG_VARIANT_TILED_PIPE)  # ldb < 8 with N % 8 != 0
     with pytest.raises(tlg.TlgError):
         tlg.plan(4, 4, 4, variant=99)
     with pytest.raises(tlg.TlgError):  # a configuration needs a forced variant

@@ -101,13 +101,15 @@ def test_ragged_full_output(dev, kind):
         A, B = wl.make_random(w.M, w.N, w.K, seed=w.seed, kind="integer_pos")
     ref = oracle.gemm_relu(A, B)
     got = bits(run(A, B, dev))
-    assert tlg.plan(w.M, w.N, w.K)["variant_name"] == "tiled_general"
+    assert tlg.plan(w.M, w.N, w.K)["variant_name"] == "tiled_dma"
     if kind == "normal":
         assert_close(got, ref, "ragged")
         # the cross-check kernel is the sequential definition: bit-exact on any input
         assert np.array_equal(bits(run(A, B, dev, variant=V_NAIVE)), ref)
     else:
         assert np.array_equal(got, ref)
+        for v in (V_GEN, V_PIPE):  # the other families on the same ragged data
+            assert np.array_equal(bits(run(A, B, dev, variant=v)), ref), v
 
 
 @pytest.mark.parametrize("config,splits", [(-1, 0), (0, 1), (0, 2), (0, 4), (0, 8), (0, 16), (1, 4), (2, 0), (3, 0)])
@@ -251,6 +253,26 @@ def test_padded_inputs_never_read(dev, pad_a, pad_b):
     for v in variants_for(M, N, K, lda=K + pad_a, ldb=N + pad_b):
         got = bits(run(Ap[:, :K], Bp[:, :N], dev, variant=v))
         assert np.array_equal(got, ref), (pad_a, pad_b, v)
+
+
+@pytest.mark.parametrize("variant", ["dma", "pipe"])
+def test_unaligned_base_pointers(dev, variant):
+    """Views that start one element into their storage (2-byte aligned
+    pointers, odd leading dimensions) through the direct-to-LDS kernels."""
+    v = V_DMA if variant == "dma" else V_PIPE
+    M, N, K = 300, 259, 203
+    A, B = wl.make_random(M, N, K, seed=21, kind="integer_pos")
+    ref = oracle.gemm_relu(A, B)
+    As = torch.zeros((M, K + 3), dtype=torch.float16, device=dev)
+    Bs = torch.zeros((K, N + 3), dtype=torch.float16, device=dev)
+    As[:, 1:K + 1] = to_dev(A, dev)
+    Bs[:, 1:N + 1] = to_dev(B, dev)
+    big = torch.full((M, N + 3), float("nan"), dtype=torch.float16, device=dev)
+    tlg.gemm_relu(As[:, 1:K + 1], Bs[:, 1:N + 1], out=big[:, 1:N + 1], variant=v)
+    torch.cuda.synchronize()
+    allb = bits(big)
+    assert np.array_equal(allb[:, 1:N + 1], ref)
+    assert np.all(np.isnan(allb[:, 0].view(np.float16))) and np.all(np.isnan(allb[:, N + 1:].view(np.float16)))
 
 
 def test_random_ragged_sweep(dev):

@@ -80,6 +80,23 @@ def test_dma_tiles_match_oracle_integer(emu, config, shape):
     assert np.array_equal(C, oracle.gemm_relu(A, B))
 
 
+RAGGED = [(301, 259, 203), (65, 9, 17), (130, 264, 97), (33, 41, 8), (257, 131, 1), (64, 64, 65), (3, 263, 72)]
+
+
+@pytest.mark.parametrize("config", sorted(DMA_CONFIGS))
+@pytest.mark.parametrize("shape", RAGGED)
+def test_ragged_tiles_match_oracle_integer(emu, config, shape):
+    """K or N not a multiple of 8, odd leading dimensions: the loads stop at
+    the largest multiple of 8 below K, a chunk crossing the N edge reads into
+    the next row of B (never past the last row), and the last rows come from
+    a staged zero-padded block."""
+    M, N, K = shape
+    A, B = wl.make_random(M, N, K, seed=M * 7 + N * 3 + K, kind="integer_pos")
+    C, errs = run_emu(emu, config, A, B)
+    assert all(v == 0 for v in errs.values()), errs
+    assert np.array_equal(C, oracle.gemm_relu(A, B))
+
+
 @pytest.mark.parametrize("config", sorted(DMA_CONFIGS))
 def test_dma_tiles_uniform_within_tolerance(emu, config):
     A, B = wl.make_random(130, 264, 96, seed=5)

@@ -35,18 +35,32 @@ constexpr int64_t kMaxDim = (1ll << 31) - 1024;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Conditions for the direct-to-LDS kernels: 16-byte aligned pointers,
-// leading dimensions, K and N multiples of 8 (so every 16-byte chunk lies
-// wholly inside or wholly outside the matrix), and in-tile offsets that fit
-// a buffer descriptor.
-bool dma_ok(const tlg::Problem &p, int bm, int bn, int bk) {
-    if (!aligned(p.A, 16) || !aligned(p.B, 16) || !aligned(p.C, 16)) return false;
-    if (p.lda % 8 || p.ldb % 8 || p.ldc % 8 || p.K % 8 || p.N % 8) return false;
+// In-tile byte offsets of the direct-to-LDS kernels fit a buffer descriptor.
+bool offsets_ok(const tlg::Problem &p, int bm, int bn, int bk) {
     if ((int64_t)bm * p.lda * 2 > kMaxOffset) return false;  // A tile loads
     if ((int64_t)bk * p.ldb * 2 > kMaxOffset) return false;  // B tile loads
     if ((int64_t)bm * p.ldc * 2 + (int64_t)bn * 2 > kMaxOffset) return false;  // C tile stores
     if ((int64_t)bm * p.N * 4 + (int64_t)bn * 4 > kMaxOffset) return false;    // split-K partial stores
     return true;
+}
+
+// The tiled and pipelined direct-to-LDS kernels take any 2-byte aligned data
+// (gfx950 buffer loads and stores accept any 2-byte aligned offset). When K
+// or N is not a multiple of 8 the loads stop at the largest multiple of 8
+// below K and the last rows come from a staged block; a 16-byte chunk that
+// crosses the N edge of B must then stay inside the next row (ldb >= 8).
+bool dma_ok(const tlg::Problem &p, int bm, int bn, int bk) {
+    if (p.N % 8 != 0 && p.ldb < 8) return false;
+    return offsets_ok(p, bm, bn, bk);
+}
+
+// The split-K, stream-K and strip kernels also need every 16-byte chunk
+// wholly inside or outside the matrix: 16-byte aligned pointers, leading
+// dimensions, K and N multiples of 8.
+bool dma_ok_aligned(const tlg::Problem &p, int bm, int bn, int bk) {
+    if (!aligned(p.A, 16) || !aligned(p.B, 16) || !aligned(p.C, 16)) return false;
+    if (p.lda % 8 || p.ldb % 8 || p.ldc % 8 || p.K % 8 || p.N % 8) return false;
+    return offsets_ok(p, bm, bn, bk);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -133,7 +147,7 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
         // fits one strip and there are strips for at least half the CUs
         const tlg::TileConfig &ts = tlg::kStripConfig;
         const int64_t strips = ceil_div(p.N, ts.bn);
-        const bool strip_ok = p.M <= ts.bm && dma_ok(p, ts.bm, ts.bn, ts.bk) && strips <= 0x7fffffff;
+        const bool strip_ok = p.M <= ts.bm && dma_ok_aligned(p, ts.bm, ts.bn, ts.bk) && strips <= 0x7fffffff;
         int cfg = config;
         if (cfg < 0) cfg = strip_ok && 2 * strips >= cus ? tlg::SPLIT_WAVES_32x64x64 : tlg::SPLIT_STREAMK_32x128x64;
         if (cfg == tlg::SPLIT_WAVES_32x64x64) {
@@ -151,7 +165,7 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
             int64_t grid = (int64_t)cus * tlg::kStreamKBlocksPerCU;
             if (grid > total) grid = total;
             if (grid * slot_bytes > cap) grid = cap / slot_bytes;
-            const bool ok = dma_ok(p, tc.bm, tc.bn, tc.bk) && tiles * 4 <= kCounterBytes && grid >= 1 &&
+            const bool ok = dma_ok_aligned(p, tc.bm, tc.bn, tc.bk) && tiles * 4 <= kCounterBytes && grid >= 1 &&
                             total * grid < (1ll << 62) && total < (1ll << 31);
             if (ok) {
                 fill_info(o, TLG_VARIANT_SPLITK, cfg, &tc, (int)ceil_div(grid, tiles), 1, grid,
@@ -163,7 +177,7 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
             const tlg::TileConfig &tc = tlg::kSplitConfigs[cfg];
             int s = 1;
             int64_t k_split = 0;
-            bool ok = dma_ok(p, tc.bm, tc.bn, tc.bk) && choose_splits(p, tc, splits, cap, &s, &k_split);
+            bool ok = dma_ok_aligned(p, tc.bm, tc.bn, tc.bk) && choose_splits(p, tc, splits, cap, &s, &k_split);
             if (ok && (s > 1 || variant == TLG_VARIANT_SPLITK)) {
                 const int64_t grid = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn) * s;
                 fill_info(o, TLG_VARIANT_SPLITK, cfg, &tc, s, 2, grid, kCounterBytes + (int64_t)s * p.M * p.N * 4);

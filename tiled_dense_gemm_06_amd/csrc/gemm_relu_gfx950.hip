@@ -53,7 +53,7 @@ __global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
     grouped_tile(xcd_remap(blockIdx.x, nwg), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
     const int m0 = tm_idx * S::BM, n0 = tn_idx * S::BN;
     const int kbeg = SPLIT ? (int)blockIdx.y * a.k_split : 0;
-    const int kend = SPLIT ? imin(a.K, kbeg + a.k_split) : a.K;
+    const int kend = SPLIT ? imin(a.K, kbeg + a.k_split) : a.kmain;
     const int nk = kend > kbeg ? (kend - kbeg + S::BK - 1) / S::BK : 0;
 
     // Per-lane load descriptors (constant over the K loop).
@@ -131,10 +131,16 @@ __global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
         buf = buf + 1 == S::STAGES ? 0 : buf + 1;
     }
 
+    // Rows kmain .. K-1 (ragged K or N): one zero-padded block staged element
+    // by element into buffer 0 once every wave is done with the stages.
+    if (!SPLIT && a.kmain < a.K) {
+        barrier_lds();
+        stage_tail<S>(a, m0, n0, lds, lds + S::A_BYTES, tid);
+        barrier_lds();
+        mma_kstep<S>(lds, lds + S::A_BYTES, 0, wm0, wn0, lane, acc);
+    }
+
     // Epilogue: a lane owns four consecutive n of one row m per register quad.
-    // Stores go through a buffer descriptor based at the tile's first element;
-    // lanes outside the M x N window get offset kOOB and the hardware drops
-    // their stores, so the epilogue has no divergent branches.
     if (SPLIT) {
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
             a.W + ((int64_t)blockIdx.y * a.M + m0) * a.N + n0, (short)0, (int)kRange, 0x00020000);
@@ -154,34 +160,22 @@ __global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
                 }
             }
     } else {
-        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(a.C + (int64_t)m0 * a.ldc + n0, (short)0,
-                                                                            (int)kRange, 0x00020000);
-#pragma unroll
-        for (int tn = 0; tn < S::TN; ++tn)
-#pragma unroll
-            for (int tm = 0; tm < S::TM; ++tm) {
-                const int mr = acc_m(wm0, tm, lane);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int nr = acc_n(wn0, tn, 4 * q, lane);
-                    const bool ok = m0 + mr < a.M && n0 + nr < a.N;
-                    const uint32_t off = ok ? (uint32_t)((mr * a.ldc + nr) * 2) : kOOB;
-                    half4_t h = {relu_to_half(acc[tn][tm][4 * q]), relu_to_half(acc[tn][tm][4 * q + 1]),
-                                 relu_to_half(acc[tn][tm][4 * q + 2]), relu_to_half(acc[tn][tm][4 * q + 3])};
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(int2_t, h), rc, off, 0, 0);
-                }
-            }
+        store_c_tile<S>(a, m0, n0, wm0, wn0, lane, acc);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Tiled kernel fed through registers: any alignment, any leading dimension,
-// any M, N, K. Each thread gathers 16-byte chunks element by element with
-// bounds checks (out-of-range elements are 0) and writes them to the same
-// swizzled LDS layout; two LDS buffers, the next tile's loads in flight
-// during the current tile's MFMAs.
+// any M, N, K. Each thread moves 16-byte chunks: a chunk wholly inside the
+// matrix is one 16-byte buffer load (gfx950 buffer loads accept any 2-byte
+// aligned offset, so odd leading dimensions and pointers need no special
+// case; FAST = false drops this when in-tile offsets would not fit 32 bits),
+// a chunk that crosses the M, N or K edge is gathered element by element with
+// bounds checks (out-of-range elements are 0). Chunks are written to the same
+// swizzled LDS layout as the direct-to-LDS kernels; two LDS buffers, the next
+// tile's loads in flight during the current tile's MFMAs.
 // ---------------------------------------------------------------------------
-template <class S>
+template <class S, bool FAST>
 __global__ __launch_bounds__(S::NT) void k_tiled_general(const KArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[2 * S::STAGE_BYTES];
     const int tid = threadIdx.x;
@@ -200,21 +194,35 @@ __global__ __launch_bounds__(S::NT) void k_tiled_general(const KArgs a) {
 
     auto gload = [&](int kt) {
         const int k0 = kt * S::BK;
+        const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.A + (int64_t)m0 * a.lda + k0), (short)0, (int)kRange, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.B + (int64_t)k0 * a.ldb + n0), (short)0, (int)kRange, 0x00020000);
 #pragma unroll
         for (int j = 0; j < S::JA; ++j) {
             ChunkRef c = reg_a_chunk<S>(tid, j);
             const int m = m0 + c.row, k = k0 + 8 * c.chunk;
-            const _Float16 *p = a.A + (int64_t)m * a.lda + k;
+            if (FAST && m < a.M && k + 8 <= a.K) {
+                ra[j] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rA, (uint32_t)((c.row * a.lda + 8 * c.chunk) * 2), 0, 0));
+            } else {
+                const _Float16 *p = a.A + (int64_t)m * a.lda + k;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ra[j][e] = (m < a.M && k + e < a.K) ? p[e] : (_Float16)0.0f;
+                for (int e = 0; e < 8; ++e) ra[j][e] = (m < a.M && k + e < a.K) ? p[e] : (_Float16)0.0f;
+            }
         }
 #pragma unroll
         for (int j = 0; j < S::JB; ++j) {
             ChunkRef c = reg_b_chunk<S>(tid, j);
             const int k = k0 + c.row, n = n0 + 8 * c.chunk;
-            const _Float16 *p = a.B + (int64_t)k * a.ldb + n;
+            if (FAST && k < a.K && n + 8 <= a.N) {
+                rb[j] = __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rB, (uint32_t)((c.row * a.ldb + 8 * c.chunk) * 2), 0, 0));
+            } else {
+                const _Float16 *p = a.B + (int64_t)k * a.ldb + n;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) rb[j][e] = (k < a.K && n + e < a.N) ? p[e] : (_Float16)0.0f;
+                for (int e = 0; e < 8; ++e) rb[j][e] = (k < a.K && n + e < a.N) ? p[e] : (_Float16)0.0f;
+            }
         }
     };
     auto swrite = [&](int buf) {
@@ -355,6 +363,7 @@ static KArgs make_args(const Problem &p) {
     a.ldc = p.ldc;
     a.group_m = 4;
     a.k_split = (int)p.K;
+    a.kmain = (p.K % 8 == 0 && p.N % 8 == 0) ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
     return a;
 }
 
@@ -371,7 +380,14 @@ template <class S>
 static hipError_t launch_gen_t(KArgs a, hipStream_t stream) {
     a.tiles_m = (a.M + S::BM - 1) / S::BM;
     a.tiles_n = (a.N + S::BN - 1) / S::BN;
-    hipLaunchKernelGGL((k_tiled_general<S>), dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(S::NT), 0, stream, a);
+    // the 16-byte loads address a tile through 32-bit offsets
+    const bool fast = (int64_t)S::BM * a.lda * 2 < (int64_t)kRange && (int64_t)S::BK * a.ldb * 2 < (int64_t)kRange;
+    if (fast)
+        hipLaunchKernelGGL((k_tiled_general<S, true>), dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(S::NT), 0, stream,
+                           a);
+    else
+        hipLaunchKernelGGL((k_tiled_general<S, false>), dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(S::NT), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     int tm_idx, tn_idx;
     grouped_tile(xcd_remap(blockIdx.x, nwg), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
     const int m0 = tm_idx * S::BM, n0 = tn_idx * S::BN;
-    const int nk = (a.K + S::BK - 1) / S::BK;
+    const int nk = (a.kmain + S::BK - 1) / S::BK;
 
     // Per-lane load descriptors (constant over the K loop): byte offset in the
     // stage's window, the column (A) or row (B) inside the stage that decides
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     // Load j of stage kt into LDS buffer buf (stages past K load zeros).
     auto dma = [&](int j, int kt, int buf) {
         const int k0 = kt * S::BK;
-        const bool in = ok[j] && k0 + kin[j] < a.K;
+        const bool in = ok[j] && k0 + kin[j] < a.kmain;
         if (j < S::DMA_A) {
             const int4_t r = make_srd(a_tile + k0);
             const uint32_t l = (uint32_t)(uintptr_t)(lds + buf * S::STAGE_BYTES + (wave * S::DMA_A + j) * 1024);
@@ -207,26 +207,16 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     // No load may still be writing LDS when the work-group ends.
     wait_vmcnt<0>();
 
-    // Epilogue: ReLU, round to nearest even, 8-byte stores of four
-    // consecutive n; lanes outside the window get offset kOOB and the
-    // hardware drops their stores.
-    const __amdgpu_buffer_rsrc_t rc =
-        __builtin_amdgcn_make_buffer_rsrc(a.C + (int64_t)m0 * a.ldc + n0, (short)0, (int)kRange, 0x00020000);
-#pragma unroll
-    for (int tn = 0; tn < S::TN; ++tn)
-#pragma unroll
-        for (int tm = 0; tm < S::TM; ++tm) {
-            const int mr = acc_m(wm0, tm, lane);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int nr = acc_n(wn0, tn, 4 * q, lane);
-                const bool in = m0 + mr < a.M && n0 + nr < a.N;
-                const uint32_t o = in ? (uint32_t)((mr * a.ldc + nr) * 2) : kOOB;
-                half4_t h = {relu_to_half(acc[tn][tm][4 * q]), relu_to_half(acc[tn][tm][4 * q + 1]),
-                             relu_to_half(acc[tn][tm][4 * q + 2]), relu_to_half(acc[tn][tm][4 * q + 3])};
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(int2_t, h), rc, o, 0, 0);
-            }
-        }
+    // Rows kmain .. K-1 (ragged K or N): one zero-padded block staged element
+    // by element into buffer 0 once every wave is done with the stages.
+    if (a.kmain < a.K) {
+        barrier_lds();
+        stage_tail<S>(a, m0, n0, lds, lds + S::A_BYTES, tid);
+        barrier_lds();
+        mma_kstep<S>(lds, lds + S::A_BYTES, 0, wm0, wn0, lane, acc);
+    }
+
+    store_c_tile<S>(a, m0, n0, wm0, wn0, lane, acc);
 }
 
 using Pipe256x32 = TileShape<256, 256, 32, 2, 2, 4>;
@@ -252,6 +242,7 @@ static hipError_t launch_pipe_t(const Problem &p, hipStream_t stream) {
     a.ldc = p.ldc;
     a.group_m = 4;
     a.k_split = (int)p.K;
+    a.kmain = (p.K % 8 == 0 && p.N % 8 == 0) ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
     a.tiles_m = (a.M + S::BM - 1) / S::BM;
     a.tiles_n = (a.N + S::BN - 1) / S::BN;
     hipLaunchKernelGGL((k_tiled_pipe<S, SPACING, DOFF>), dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(S::NT), 0,

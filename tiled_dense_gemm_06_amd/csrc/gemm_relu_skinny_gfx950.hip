@@ -163,6 +163,7 @@ hipError_t launch_skinny_strip(const Problem &p, hipStream_t stream) {
     a.tiles_n = (int)((p.N + Strip32x64::BN - 1) / Strip32x64::BN);
     a.group_m = 1;
     a.k_split = (int)p.K;
+    a.kmain = (int)p.K;
     hipLaunchKernelGGL((k_skinny_strip<Strip32x64, kStripWaves>), dim3((unsigned)a.tiles_n), dim3(kStripWaves * 64), 0,
                        stream, a);
     return hipGetLastError();

@@ -34,6 +34,11 @@ struct KArgs {
     int64_t lda, ldb, ldc;
     int tiles_m, tiles_n, group_m;
     int k_split;       // K elements per split, a multiple of BK
+    // K rows the direct-to-LDS loads cover (tiled and pipelined kernels): K
+    // when K and N are multiples of 8; otherwise the largest multiple of 8
+    // below K, and the last 1..8 rows are added from a zero-padded block
+    // staged element by element (see stage_tail).
+    int kmain;
 };
 
 typedef int int4_t __attribute__((ext_vector_type(4)));
@@ -95,26 +100,95 @@ __device__ __forceinline__ half8_t read_b_frag(LDS_PTR(const char) base, int off
     return __builtin_bit_cast(half8_t, v);
 }
 
-// The tile product of one LDS stage: for each 16-wide k-step, read the
-// operand fragments of every MFMA tile of this wave and accumulate.
+// One 16-wide k-step s of an LDS stage: read the operand fragments of every
+// MFMA tile of this wave and accumulate.
+template <class S>
+__device__ __forceinline__ void mma_kstep(LDS_PTR(const char) sA, LDS_PTR(const char) sB, int s, int wm0, int wn0,
+                                          int lane, float16_t (&acc)[S::TN][S::TM]) {
+    half8_t bf[S::TN], af[S::TM];
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn)
+        bf[tn] = read_b_frag(sB, frag_b_offset<S>(wn0, tn, s, 0, lane), frag_b_offset<S>(wn0, tn, s, 1, lane));
+#pragma unroll
+    for (int tm = 0; tm < S::TM; ++tm) af[tm] = *(LDS_PTR(const half8_t))(sA + frag_a_offset<S>(wm0, tm, s, lane));
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm)
+            acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[tn], af[tm], acc[tn][tm], 0, 0, 0);
+}
+
+// The tile product of one LDS stage.
 template <class S>
 __device__ __forceinline__ void mma_stage(LDS_PTR(const char) sA, LDS_PTR(const char) sB, int wm0, int wn0, int lane,
                                           float16_t (&acc)[S::TN][S::TM]) {
 #pragma unroll
-    for (int s = 0; s < S::KSTEPS; ++s) {
-        half8_t bf[S::TN], af[S::TM];
+    for (int s = 0; s < S::KSTEPS; ++s) mma_kstep<S>(sA, sB, s, wm0, wn0, lane, acc);
+}
+
+// Rows kmain .. K-1 of the sum (1 to 8 of them) as one 16-deep block in the
+// stage layout of LDS buffer (sA, sB): element-wise loads with bounds checks,
+// zeros outside the matrices, so one MFMA k-step adds them. Used when K or N
+// is not a multiple of 8: the direct-to-LDS loads then stop at kmain, so no
+// 16-byte chunk they fetch crosses the K edge of A, and a chunk crossing the
+// N edge of B reads at most into the next row of B (needs ldb >= 8), whose
+// values only reach output columns >= N, which are never stored.
+template <class S>
+__device__ __forceinline__ void stage_tail(const KArgs &a, int m0, int n0, LDS_PTR(char) sA, LDS_PTR(char) sB,
+                                           int tid) {
+    for (int q = tid; q < S::BM * 2; q += S::NT) {
+        const int row = q / 2, chunk = q % 2;
+        const int m = m0 + row, k = a.kmain + 8 * chunk;
+        half8_t v;
 #pragma unroll
-        for (int tn = 0; tn < S::TN; ++tn)
-            bf[tn] = read_b_frag(sB, frag_b_offset<S>(wn0, tn, s, 0, lane), frag_b_offset<S>(wn0, tn, s, 1, lane));
-#pragma unroll
-        for (int tm = 0; tm < S::TM; ++tm)
-            af[tm] = *(LDS_PTR(const half8_t))(sA + frag_a_offset<S>(wm0, tm, s, lane));
-#pragma unroll
-        for (int tn = 0; tn < S::TN; ++tn)
-#pragma unroll
-            for (int tm = 0; tm < S::TM; ++tm)
-                acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[tn], af[tm], acc[tn][tm], 0, 0, 0);
+        for (int e = 0; e < 8; ++e) v[e] = (m < a.M && k + e < a.K) ? a.A[(int64_t)m * a.lda + k + e] : (_Float16)0.0f;
+        *(LDS_PTR(half8_t))(sA + lds_a_offset<S>(row, chunk)) = v;
     }
+    for (int q = tid; q < 16 * S::CB; q += S::NT) {
+        const int row = q / S::CB, chunk = q % S::CB;
+        const int k = a.kmain + row, n = n0 + 8 * chunk;
+        half8_t v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (k < a.K && n + e < a.N) ? a.B[(int64_t)k * a.ldb + n + e] : (_Float16)0.0f;
+        *(LDS_PTR(half8_t))(sB + lds_b_offset<S>(row, chunk)) = v;
+    }
+}
+
+// Epilogue of an output tile: ReLU, round to nearest even, 8-byte stores of
+// the four consecutive n a lane holds per register quad (any 2-byte aligned
+// address works); a quad that crosses column N is stored element by element;
+// lanes outside the window get offset kOOB and the hardware drops their
+// stores.
+template <class S>
+__device__ __forceinline__ void store_c_tile(const KArgs &a, int m0, int n0, int wm0, int wn0, int lane,
+                                             const float16_t (&acc)[S::TN][S::TM]) {
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc(a.C + (int64_t)m0 * a.ldc + n0, (short)0, (int)kRange, 0x00020000);
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm) {
+            const int mr = acc_m(wm0, tm, lane);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nr = acc_n(wn0, tn, 4 * q, lane);
+                const bool row_in = m0 + mr < a.M;
+                half4_t h = {relu_to_half(acc[tn][tm][4 * q]), relu_to_half(acc[tn][tm][4 * q + 1]),
+                             relu_to_half(acc[tn][tm][4 * q + 2]), relu_to_half(acc[tn][tm][4 * q + 3])};
+                const uint32_t base = (uint32_t)((mr * a.ldc + nr) * 2);
+                if (n0 + nr + 4 <= a.N || !row_in) {
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(int2_t, h), rc, row_in ? base : kOOB, 0, 0);
+                } else {
+                    // each element converted and stored on its own (the 16-bit
+                    // buffer-store builtin fed from an odd element of a half
+                    // vector was observed to store the even element instead)
+                    _Float16 *crow = a.C + (int64_t)(m0 + mr) * a.ldc + n0 + nr;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n0 + nr + e < a.N) crow[e] = relu_to_half(acc[tn][tm][4 * q + e]);
+                }
+            }
+        }
 }
 
 }  // namespace tlg
