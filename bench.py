@@ -17,7 +17,6 @@ Prints one JSON line: the contract fields, plus
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -33,56 +32,32 @@ METRIC = "GEMM+ReLU TFLOPS (fp16 in, fp32 acc) at 8192³ and % of fp16 MFMA peak
 PEAK_MFMA_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20  # MI355X Infinity Cache; rotated buffers exceed twice this
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_06_amd", "csrc", f)
-                  for f in ("gemm_relu_gfx950.hip", "tile_layout.h", "api.cpp")]
-
-
-def kernel_source_digest() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
-
-
-def measured_traffic(workload: str):
-    """HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters,
-    scaled by the copy-kernel calibration, if they were taken on the current
-    kernel sources; otherwise None."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_sha256") != kernel_source_digest():
-        return None
-    w = t.get("workloads", {}).get(workload)
-    if not w:
-        return None
-    return w.get("bytes_per_launch")
-
-
 def cpu_baseline(w, A, B, target_s: float):
-    """The oracle as it stands, on whole sampled output rows of the workload."""
+    """The oracle as it stands, on whole sampled output rows of the workload.
+
+    The oracle splits rows across its threads, so the sample is whole batches
+    of one row per thread, grown until one call takes at least half of
+    target_s seconds of wall time (the last call is the one reported)."""
     import numpy as np
 
     import oracle
 
     threads = oracle.default_threads()
-    rows = np.arange(min(2, w.M))
-    t0 = time.perf_counter()
-    oracle.gemm_relu_rows(A, B, rows)
-    per_row = (time.perf_counter() - t0) / len(rows)
-    n = int(max(1, min(w.M, math.ceil(target_s / max(per_row, 1e-6)))))
-    rows = np.linspace(0, w.M - 1, n).astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.gemm_relu_rows(A, B, rows)
-    dt = time.perf_counter() - t0
+    n = min(threads, w.M)
+    while True:  # grow the sample (4x a round) until it takes about target_s
+        rows = np.linspace(0, w.M - 1, n).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.gemm_relu_rows(A, B, rows)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 2 or n >= w.M:
+            break
+        n = int(min(w.M, max(n + threads, n * min(8.0, target_s / max(dt, 1e-6)))))
+        n = min(w.M, -(-n // threads) * threads)
     flop = 2.0 * n * w.N * w.K
     return {
         "value": flop / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
-        "sample": f"{n} of {w.M} output rows ({n}x{w.N}x{w.K} multiply-adds), {dt:.2f} s wall",
+        "sample": f"{n} of {w.M} output rows ({n}x{w.N}x{w.K} multiply-adds, all K), {dt:.2f} s wall "
+                  f"on {threads} threads",
     }
 
 
@@ -114,7 +89,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square8192")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample size, in seconds of CPU work")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle sample size: about this many seconds of wall time on the host's cores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant", default="auto",
                     help="kernel family to time (auto = what tlg_gemm_relu picks; others for comparisons): "
@@ -137,6 +113,7 @@ def main() -> int:
 
     import tiled_dense_gemm_06_amd as tlg
     from tiled_dense_gemm_06_amd import workloads as wl
+    from tiled_dense_gemm_06_amd.profiling import measured_traffic
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -200,7 +177,7 @@ def main() -> int:
         achieved = w.flop / avg_launch_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_MFMA_TFLOPS}
-    roof["traffic"] = measured_traffic(w.name)
+    roof["traffic"] = measured_traffic(w.name) if args.variant == "auto" else None
     roof["kernel"] = plan["config_name"]
     roof["launch_ms_avg"] = avg_launch_s * 1e3
     roof["launch_ms_min"] = float(np.min(per_launch_ms))
