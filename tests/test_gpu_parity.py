@@ -112,7 +112,8 @@ def test_ragged_full_output(dev, kind):
             assert np.array_equal(bits(run(A, B, dev, variant=v)), ref), v
 
 
-@pytest.mark.parametrize("config,splits", [(-1, 0), (0, 1), (0, 2), (0, 4), (0, 8), (0, 16), (1, 4), (2, 0), (3, 0)])
+@pytest.mark.parametrize("config,splits", [(-1, 0), (0, 1), (0, 2), (0, 4), (0, 8), (0, 16), (1, 4), (2, 0), (3, 0),
+                                           (3, 2), (3, 5), (3, 16)])
 def test_skinny_full_output(dev, config, splits):
     w = wl.WORKLOADS["skinny16x14336x4096"]
     A, B = wl.make_inputs(w)
@@ -144,20 +145,24 @@ def test_streamk_shapes(dev, shape):
         assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
 
 
+@pytest.mark.parametrize("parts", [1, 3])
 @pytest.mark.parametrize("shape", [(16, 14336, 520), (1, 8, 8), (32, 264, 4096), (7, 128, 8192), (17, 392, 1000),
                                    (16, 64, 32), (31, 1032, 264)])
-def test_wave_split_shapes(dev, shape):
-    """K split among the waves of one work-group: fewer K blocks than waves,
-    ragged M and N, K tails, one strip; NaN sentinel and padding columns."""
+def test_wave_split_shapes(dev, shape, parts):
+    """K split among the waves of a work-group (and among `parts`
+    work-groups per strip): fewer K blocks than waves or parts, ragged M and
+    N, K tails, one strip; NaN sentinel and padding columns. Each case runs
+    twice: the strip counters must be back at zero after a call."""
     M, N, K = shape
     A, B = wl.make_random(M, N, K, seed=M + 5 * N + 3 * K, kind="integer_pos")
     ref = oracle.gemm_relu(A, B)
-    big = torch.full((M + 1, N + 8), float("nan"), dtype=torch.float16, device=dev)
-    tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), out=big[:M, :N], variant=V_SPLIT, config=3)
-    torch.cuda.synchronize()
-    allb = bits(big)
-    assert np.array_equal(allb[:M, :N], ref), shape
-    assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+    for _ in range(2):
+        big = torch.full((M + 1, N + 8), float("nan"), dtype=torch.float16, device=dev)
+        tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), out=big[:M, :N], variant=V_SPLIT, config=3, splits=parts)
+        torch.cuda.synchronize()
+        allb = bits(big)
+        assert np.array_equal(allb[:M, :N], ref), shape
+        assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
 
 
 def test_skinny_without_split(dev):

@@ -152,7 +152,16 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
         if (cfg < 0) cfg = strip_ok && 2 * strips >= cus ? tlg::SPLIT_WAVES_32x64x64 : tlg::SPLIT_STREAMK_32x128x64;
         if (cfg == tlg::SPLIT_WAVES_32x64x64) {
             if (!strip_ok) return TLG_ERROR_NOT_SUPPORTED;
-            fill_info(o, TLG_VARIANT_SPLITK, cfg, &ts, ts.threads / 64, 1, strips, 0);
+            // parts per strip: forced, else one
+            int64_t parts = splits > 0 ? splits : 1;
+            const int64_t nkb = ceil_div(p.K, ts.bk);
+            if (parts > nkb) parts = nkb > 0 ? nkb : 1;
+            const int64_t slot_bytes = (int64_t)ts.bm * ts.bn * 4;
+            if (parts > 1 && strips * parts * slot_bytes > cap) parts = cap / (strips * slot_bytes);
+            if (parts < 1) parts = 1;
+            if (parts > 1 && strips * 4 > kCounterBytes) parts = 1;
+            const int64_t ws = parts > 1 ? kCounterBytes + strips * parts * slot_bytes : 0;
+            fill_info(o, TLG_VARIANT_SPLITK, cfg, &ts, (int)parts, 1, strips * parts, ws);
             return TLG_SUCCESS;
         }
         if (cfg == tlg::SPLIT_STREAMK_32x128x64) {
@@ -271,7 +280,7 @@ tlg_status run(tlg_handle h, int32_t variant, int32_t config, int32_t splits, co
         case TLG_VARIANT_SPLITK: {
             float *partials = h->workspace + kCounterBytes / sizeof(float);
             if (info.config == tlg::SPLIT_WAVES_32x64x64)
-                e = tlg::launch_skinny_strip(p, stream);
+                e = tlg::launch_skinny_strip(p, info.splits, partials, (int *)h->workspace, stream);
             else if (info.config == tlg::SPLIT_STREAMK_32x128x64)
                 e = tlg::launch_streamk(p, (int)info.grid, partials, (int *)h->workspace, stream);
             else

@@ -42,6 +42,11 @@ __device__ __forceinline__ void wait_blocks(int n) {
         wait_vmcnt<0>();
 }
 
+// Cache policy of the partial-strip stores and loads: sc1, device scope.
+constexpr int kPartialScope = 16;
+
+// Grid: strips x parts (a.k_split parts per strip, adjacent work-groups share
+// a strip). Part p takes the strip's K blocks [p*nkb/parts, (p+1)*nkb/parts).
 template <class S, int W>
 __global__ __launch_bounds__(W * 64) void k_skinny_strip(const KArgs a) {
     static_assert(S::WAVES == 1, "one wave per ring");
@@ -54,15 +59,19 @@ __global__ __launch_bounds__(W * 64) void k_skinny_strip(const KArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n0 = blockIdx.x * S::BN;
+    const int parts = a.k_split, strip = blockIdx.x / parts, part = blockIdx.x - strip * parts;
+    const int n0 = strip * S::BN;
     const int nkb = (a.K + S::BK - 1) / S::BK;                         // K blocks of the strip
-    const int mine = nkb > wave ? (nkb - wave + W - 1) / W : 0;        // this wave's blocks
+    const int kb0 = (int)((int64_t)part * nkb / parts);                // this part's blocks [kb0, kb1)
+    const int kb1 = (int)((int64_t)(part + 1) * nkb / parts);
+    const int nmine = kb1 - kb0;
+    const int mine = nmine > wave ? (nmine - wave + W - 1) / W : 0;    // this wave's blocks
 
     LDS_PTR(char) ring = (LDS_PTR(char))smem + wave * RING;
 
-    // Block j of this wave (block wave + W j of the strip) into stage buffer buf.
+    // Block j of this wave (block kb0 + wave + W j of the strip) into stage buffer buf.
     auto issue = [&](int j, int buf) {
-        const int k0 = (wave + W * j) * S::BK;
+        const int k0 = (kb0 + wave + W * j) * S::BK;
         const int4_t ra = make_srd(a.A + k0);
         const int4_t rb = make_srd(a.B + (int64_t)k0 * a.ldb + n0);
         LDS_PTR(char) st = ring + buf * S::STAGE_BYTES;
@@ -108,7 +117,7 @@ __global__ __launch_bounds__(W * 64) void k_skinny_strip(const KArgs a) {
     // The waves' partial tiles meet in LDS (the rings are no longer used),
     // laid out [wave][m][n] fp32.
     __syncthreads();
-    float *part = (float *)smem;
+    float *lds_part = (float *)smem;
 #pragma unroll
     for (int tn = 0; tn < S::TN; ++tn)
 #pragma unroll
@@ -119,26 +128,89 @@ __global__ __launch_bounds__(W * 64) void k_skinny_strip(const KArgs a) {
                 const int nr = acc_n(0, tn, 4 * q, lane);
                 float4_t v = {acc[tn][tm][4 * q], acc[tn][tm][4 * q + 1], acc[tn][tm][4 * q + 2],
                               acc[tn][tm][4 * q + 3]};
-                *(float4_t *)(part + wave * TILE + mr * S::BN + nr) = v;
+                *(float4_t *)(lds_part + wave * TILE + mr * S::BN + nr) = v;
             }
         }
     __syncthreads();
-    // Thread t finishes four consecutive columns: sum over the waves in order.
-    for (int e = 4 * tid; e < TILE; e += 4 * W * 64) {
-        const int m = e / S::BN, n = e % S::BN;
-        if (m >= a.M || n0 + n >= a.N) continue;
-        float4_t s = *(const float4_t *)(part + e);
+    // Thread t owns groups of four consecutive columns: sum over the waves in order.
+    constexpr int GROUPS = TILE / (4 * W * 64);
+    static_assert(TILE % (4 * W * 64) == 0, "whole groups per thread");
+    float4_t sum[GROUPS];
+#pragma unroll
+    for (int r = 0; r < GROUPS; ++r) {
+        const int e = 4 * (tid + r * W * 64);
+        float4_t s = *(const float4_t *)(lds_part + e);
 #pragma unroll
         for (int w = 1; w < W; ++w) {
-            const float4_t v = *(const float4_t *)(part + w * TILE + e);
+            const float4_t v = *(const float4_t *)(lds_part + w * TILE + e);
             s[0] = s[0] + v[0];
             s[1] = s[1] + v[1];
             s[2] = s[2] + v[2];
             s[3] = s[3] + v[3];
         }
-        half4_t h = {relu_to_half(s[0]), relu_to_half(s[1]), relu_to_half(s[2]), relu_to_half(s[3])};
-        *(half4_t *)(a.C + (int64_t)m * a.ldc + n0 + n) = h;
+        sum[r] = s;
     }
+    auto store_groups = [&](const float4_t (&v)[GROUPS]) {
+#pragma unroll
+        for (int r = 0; r < GROUPS; ++r) {
+            const int e = 4 * (tid + r * W * 64);
+            const int m = e / S::BN, n = e % S::BN;
+            if (m >= a.M || n0 + n >= a.N) continue;
+            half4_t h = {relu_to_half(v[r][0]), relu_to_half(v[r][1]), relu_to_half(v[r][2]), relu_to_half(v[r][3])};
+            *(half4_t *)(a.C + (int64_t)m * a.ldc + n0 + n) = h;
+        }
+    };
+    if (parts == 1) {
+        store_groups(sum);
+        return;
+    }
+
+    // Split strip: this part's sum goes to its slot (device-scope stores),
+    // then, once every store of the work-group is done, it is counted in;
+    // the part that completes the count adds the slots in part order
+    // (its own from registers), applies ReLU and the cast, and resets the
+    // counter for the next call.
+    float *slots = a.W + (int64_t)strip * parts * TILE;
+    {
+        const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(slots + (int64_t)part * TILE, (short)0,
+                                                                            (int)kRange, 0x00020000);
+#pragma unroll
+        for (int r = 0; r < GROUPS; ++r) {
+            const int e = 4 * (tid + r * W * 64);
+            if (e / S::BN >= a.M) continue;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int4_t, sum[r]), rp, (uint32_t)(e * 4), 0,
+                                                   kPartialScope);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are done
+    __syncthreads();
+    int *s_last = (int *)smem;  // LDS is free: the sums are in registers
+    if (tid == 0)
+        s_last[0] = __hip_atomic_fetch_add(&a.cnt[strip], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    parts - 1;
+    __syncthreads();
+    if (!s_last[0]) return;
+    float4_t tot[GROUPS];
+#pragma unroll
+    for (int r = 0; r < GROUPS; ++r) tot[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = 0; q < parts; ++q) {
+        const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(slots + (int64_t)q * TILE, (short)0,
+                                                                            (int)kRange, 0x00020000);
+#pragma unroll
+        for (int r = 0; r < GROUPS; ++r) {
+            const int e = 4 * (tid + r * W * 64);
+            float4_t v = sum[r];
+            if (q != part)
+                v = __builtin_bit_cast(float4_t,
+                                       __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)(e * 4), 0, kPartialScope));
+            tot[r][0] = tot[r][0] + v[0];
+            tot[r][1] = tot[r][1] + v[1];
+            tot[r][2] = tot[r][2] + v[2];
+            tot[r][3] = tot[r][3] + v[3];
+        }
+    }
+    store_groups(tot);
+    if (tid == 0) __hip_atomic_store(&a.cnt[strip], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 using Strip32x64 = TileShape<32, 64, 64, 1, 1, 3>;
@@ -147,12 +219,13 @@ constexpr int kStripWaves = 2;
 const TileConfig kStripConfig = {Strip32x64::BM, Strip32x64::BN, Strip32x64::BK, kStripWaves * 64,
                                  Strip32x64::STAGES, "splitk_waves_32x64x64_w2_s3"};
 
-hipError_t launch_skinny_strip(const Problem &p, hipStream_t stream) {
+hipError_t launch_skinny_strip(const Problem &p, int parts, float *partials, int *counters, hipStream_t stream) {
     KArgs a;
     a.A = (const _Float16 *)p.A;
     a.B = (const _Float16 *)p.B;
     a.C = (_Float16 *)p.C;
-    a.W = nullptr;
+    a.W = partials;
+    a.cnt = counters;
     a.M = (int)p.M;
     a.N = (int)p.N;
     a.K = (int)p.K;
@@ -162,10 +235,10 @@ hipError_t launch_skinny_strip(const Problem &p, hipStream_t stream) {
     a.tiles_m = 1;
     a.tiles_n = (int)((p.N + Strip32x64::BN - 1) / Strip32x64::BN);
     a.group_m = 1;
-    a.k_split = (int)p.K;
+    a.k_split = parts;
     a.kmain = (int)p.K;
-    hipLaunchKernelGGL((k_skinny_strip<Strip32x64, kStripWaves>), dim3((unsigned)a.tiles_n), dim3(kStripWaves * 64), 0,
-                       stream, a);
+    hipLaunchKernelGGL((k_skinny_strip<Strip32x64, kStripWaves>), dim3((unsigned)(a.tiles_n * parts)),
+                       dim3(kStripWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 

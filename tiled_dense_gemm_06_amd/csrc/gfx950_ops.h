@@ -30,6 +30,7 @@ struct KArgs {
     const _Float16 *B;
     _Float16 *C;
     float *W;          // split-K partials (split-K kernels only)
+    int *cnt;          // per-tile counters of the skinny kernel's split strips (zero between calls)
     int M, N, K;
     int64_t lda, ldb, ldc;
     int tiles_m, tiles_n, group_m;

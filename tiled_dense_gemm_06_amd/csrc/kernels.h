@@ -58,10 +58,12 @@ hipError_t launch_splitk(int config, int splits, int64_t k_split, const Problem 
 extern const TileConfig kStreamKConfig;
 constexpr int kStreamKBlocksPerCU = 2;  // 80 KiB of LDS per work-group, 160 KiB per CU
 hipError_t launch_streamk(const Problem &p, int grid, float *partials, int *counters, hipStream_t stream);
-// Skinny strips (M <= 32): one work-group per 64 columns, K split among its
-// waves and reduced in LDS in wave order.
+// Skinny strips (M <= 32): `parts` work-groups per 64 columns, each taking a
+// contiguous part of K split among its waves and reduced in LDS in wave
+// order; with parts > 1 the parts meet through `partials` (strips x parts x
+// 32 x 64 fp32) and `counters` (one int per strip, zero on entry and exit).
 extern const TileConfig kStripConfig;
-hipError_t launch_skinny_strip(const Problem &p, hipStream_t stream);
+hipError_t launch_skinny_strip(const Problem &p, int parts, float *partials, int *counters, hipStream_t stream);
 hipError_t launch_naive(const Problem &p, hipStream_t stream);
 hipError_t launch_fill_zero(const Problem &p, hipStream_t stream);
 
