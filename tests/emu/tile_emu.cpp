@@ -374,3 +374,73 @@ extern "C" long emu_check_remap(int max_nwg) {
     }
     return bad;
 }
+
+// The LDS epilogue of the pipelined kernel for one wave block (EP64 shape):
+// every result register is followed through the conversion into 32-bit
+// pairs, the lane-pair exchange (v_permlane32_swap: the upper 32 lanes of its
+// first operand trade places with the lower 32 lanes of its second), the
+// write to LDS and the read-back, and must reach the C position that
+// acc_m/acc_n assign to it; every LDS piece is written once, and each group
+// of 16 lanes touches 16 distinct 16-byte slots of a 256-byte window on both
+// sides. Returns the number of violations.
+extern "C" long emu_check_epilogue() {
+    using S = EP64;
+    long bad = 0;
+    const int CH = S::WTN / 8;
+    for (int wave = 0; wave < S::WAVES; ++wave) {
+        const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
+        // LDS of the wave block: per half, the (m, n) it holds (-1: never written)
+        std::vector<long> lds((size_t)S::WTM * S::WTN, -1);
+        auto tag = [&](int m, int n) { return (long)m * 65536 + n; };
+        for (int tn = 0; tn < S::TN; ++tn)
+            for (int tm = 0; tm < S::TM; ++tm) {
+                // d[lane][i]: the two halves (as tags) of 32-bit register i
+                long d[64][8][2];
+                for (int l = 0; l < 64; ++l)
+                    for (int i = 0; i < 8; ++i)
+                        for (int h = 0; h < 2; ++h)
+                            d[l][i][h] = tag(acc_m(wm0, tm, l), acc_n(wn0, tn, 2 * i + h, l));
+                for (int pr = 0; pr < 2; ++pr) {
+                    long v[64][4][2];
+                    for (int w = 0; w < 2; ++w) {  // the two exchanges: registers (4pr+w, 4pr+2+w)
+                        const int xi = 4 * pr + w, yi = 4 * pr + 2 + w;
+                        for (int l = 0; l < 64; ++l)
+                            for (int h = 0; h < 2; ++h) {
+                                const long x = l < 32 ? d[l][xi][h] : d[l - 32][yi][h];
+                                const long y = l < 32 ? d[l + 32][xi][h] : d[l][yi][h];
+                                v[l][w][h] = x;       // result 0 -> dword w of the piece
+                                v[l][2 + w][h] = y;   // result 1 -> dword 2+w
+                            }
+                    }
+                    std::vector<int> slot_seen(64, -1);
+                    for (int l = 0; l < 64; ++l) {
+                        const int row = epi_piece_row(tm, l), c = epi_piece_index(tn, pr, l);
+                        const int off = epi_lds_offset<S>(row, c);
+                        if (off < 0 || off + 16 > S::WTM * S::WTN * 2 || off % 16) { bad++; continue; }
+                        const int slot = (off % 256) / 16;
+                        if (slot_seen[16 * (l / 16) + slot]++ != -1) bad++;
+                        for (int e = 0; e < 8; ++e) {
+                            long &t = lds[off / 2 + e];
+                            if (t != -1) bad++;
+                            t = v[l][e / 2][e % 2];
+                        }
+                    }
+                }
+            }
+        for (long t : lds)
+            if (t == -1) bad++;
+        // read-back
+        for (int k = 0; k < S::WTM / (64 / CH); ++k) {
+            std::vector<int> slot_seen(64, -1);
+            for (int l = 0; l < 64; ++l) {
+                const int row = epi_read_row<S>(k, l), c = epi_read_piece<S>(l);
+                const int off = epi_lds_offset<S>(row, c);
+                const int slot = (off % 256) / 16;
+                if (slot_seen[16 * (l / 16) + slot]++ != -1) bad++;
+                for (int e = 0; e < 8; ++e)
+                    if (lds[off / 2 + e] != tag(wm0 + row, wn0 + 8 * c + e)) bad++;
+            }
+        }
+    }
+    return bad;
+}

@@ -206,9 +206,9 @@ def test_large_square_sampled(dev, name):
     assert np.array_equal(got[rows], oracle.gemm_relu_rows(Ai, Bi, rows))
 
 
-@pytest.mark.parametrize("config", [0, 1])
+@pytest.mark.parametrize("config", [0, 1, 2])
 @pytest.mark.parametrize("shape", [(300, 264, 200), (513, 520, 72), (1024, 1032, 1000), (256, 256, 8),
-                                   (257, 8, 4104)])
+                                   (257, 8, 4104), (301, 259, 203)])
 def test_pipe_configs(dev, config, shape):
     """Every tile configuration of the pipelined kernel: ragged M and N, K
     tails inside a stage, K shorter than the pipeline, one-column N."""

@@ -39,6 +39,8 @@ def emu(tmp_path_factory):
     L.emu_check_remap.restype = l
     L.emu_check_streamk.argtypes = [l, i, i]
     L.emu_check_streamk.restype = l
+    L.emu_check_epilogue.argtypes = []
+    L.emu_check_epilogue.restype = l
     return L
 
 
@@ -64,6 +66,13 @@ def test_xcd_remap_is_bijection(emu):
 def test_streamk_ranges(emu, tiles, ipt, G):
     total = tiles * ipt
     assert emu.emu_check_streamk(total, min(G, total), ipt) == 0
+
+
+def test_lds_epilogue_index_math(emu):
+    """The pipelined kernel's C epilogue through LDS: every result register
+    reaches its own C position, each LDS piece is written once, and neither
+    the writes nor the read-back have bank conflicts."""
+    assert emu.emu_check_epilogue() == 0
 
 
 # shapes that satisfy the direct-to-LDS conditions (K % 8 == 0, N % 8 == 0), several tiles, ragged tails

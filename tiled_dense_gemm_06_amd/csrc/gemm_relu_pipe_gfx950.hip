@@ -75,6 +75,66 @@ __device__ __forceinline__ void mfma_tile(const Frags<S> &f, int i, float16_t (&
 // Nothing may be scheduled across this point (keeps the hand-written order).
 #define TLG_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// Epilogue through LDS, for a wave block of 128 x 128: ReLU and the fp16
+// conversion, then the two 8-byte halves of each 16-byte row piece, held by
+// lanes l and l+32, are brought into one lane (v_permlane32_swap exchanges
+// the upper 32 lanes of its first operand with the lower 32 lanes of its
+// second), the pieces go to this wave's 32 KB of LDS (rows of 256 bytes,
+// 16-byte position XOR-ed with the row mod 16: conflict-free for every 16
+// lanes), and come back as whole 256-byte row segments for 16-byte buffer
+// stores (rows >= M dropped by the range check, a piece crossing column N
+// stored element by element). The caller makes sure no wave still reads or
+// loads into this LDS.
+template <class S>
+__device__ __forceinline__ void store_c_tile_lds(const KArgs &a, int m0, int n0, int wave, int lane,
+                                                 const float16_t (&acc)[S::TN][S::TM], LDS_PTR(char) lds) {
+    static_assert(S::WTM == 128 && S::WTN == 128, "written for 128 x 128 wave blocks");
+    constexpr int PITCH = S::WTN * 2, CH = S::WTN / 8;
+    static_assert(S::WAVES * S::WTM * PITCH <= S::STAGES * S::STAGE_BYTES, "C tile must fit the stages' LDS");
+    LDS_PTR(char) q = lds + wave * S::WTM * PITCH;
+    const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm) {
+            uint32_t d[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const half2_t h = {relu_to_half(acc[tn][tm][2 * i]), relu_to_half(acc[tn][tm][2 * i + 1])};
+                d[i] = __builtin_bit_cast(uint32_t, h);
+            }
+            const int row = epi_piece_row(tm, lane);
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                // quads 2*pr and 2*pr+1 (registers 4 apart): lane l < 32 ends up
+                // with columns 16*pr + 0..7 of its row, lane l+32 with 16*pr + 8..15
+                const auto s0 = __builtin_amdgcn_permlane32_swap(d[4 * pr], d[4 * pr + 2], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(d[4 * pr + 1], d[4 * pr + 3], false, false);
+                const int4_t v = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+                *(LDS_PTR(int4_t))(q + epi_lds_offset<S>(row, epi_piece_index(tn, pr, lane))) = v;
+            }
+        }
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc(a.C + (int64_t)m0 * a.ldc + n0, (short)0, (int)kRange, 0x00020000);
+    constexpr int ROWS = 64 / CH;  // rows per wave instruction
+#pragma unroll
+    for (int k = 0; k < S::WTM / ROWS; ++k) {
+        const int row = epi_read_row<S>(k, lane), c = epi_read_piece<S>(lane);
+        const int4_t v = *(LDS_PTR(const int4_t))(q + epi_lds_offset<S>(row, c));
+        const int mr = wm0 + row, nr = wn0 + 8 * c;
+        const bool row_in = m0 + mr < a.M;
+        if (n0 + nr + 8 <= a.N || !row_in) {
+            __builtin_amdgcn_raw_buffer_store_b128(v, rc, row_in ? (uint32_t)((mr * a.ldc + nr) * 2) : kOOB, 0, 0);
+        } else {
+            const half8_t h = __builtin_bit_cast(half8_t, v);
+            _Float16 *crow = a.C + (int64_t)(m0 + mr) * a.ldc + n0 + nr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n0 + nr + e < a.N) crow[e] = h[e];
+        }
+    }
+}
+
 // One K step of the loop is a fixed sequence of KSTEPS*16 MFMA slots:
 //   slots 0..7        MFMAs 8..15 of the previous stage's last k-step (held in
 //                     f[1]); after them the 12 LDS reads of this stage's
@@ -82,21 +142,32 @@ __device__ __forceinline__ void mfma_tile(const Frags<S> &f, int i, float16_t (&
 //   next 16 per ks    k-steps 0..KSTEPS-2: 16 MFMAs on f[ks & 1], with the 12
 //                     reads of k-step ks+1 into f[(ks+1) & 1], one per slot;
 //   last 8 slots      MFMAs 0..7 of the last k-step (f[1]).
-// The LOADS direct-to-LDS loads of stage kt+STAGES-1 go after slots
-// DOFF, DOFF+SPACING, ... Then this wave's loads of stage kt+1 are waited for
-// and the barrier publishes it (and retires stage kt).
-template <class S, int SPACING, int DOFF>
+// The LOADS direct-to-LDS loads go after slots DOFF, DOFF+SPACING, ...: the
+// B tile of stage kt+STAGES-1 and the A tile of stage kt+ASTAGES-1 (A may
+// have one LDS buffer more than B, which gives its loads a step more to
+// arrive; they are then issued after the B loads). Then this wave's loads of
+// stage kt+1 are waited for and the barrier publishes it (and retires stage
+// kt). The C tile leaves through LDS (store_c_tile_lds).
+template <class S, int SPACING, int DOFF, int ASTAGES>
 __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     static_assert(S::TM * S::TN == 16, "schedule written for 16 MFMA tiles per wave");
     static_assert(S::KSTEPS % 2 == 0, "the last k-step of a stage must use f[1]");
     static_assert(kFragReads<S> <= 12, "fragment reads must fit under the MFMAs of a k-step");
     constexpr int LOADS = S::DMA_A + S::DMA_B;  // direct-to-LDS loads per wave per stage
-    constexpr int AHEAD = S::STAGES - 1;        // stages in flight beyond the one being multiplied
+    constexpr int AHEAD = S::STAGES - 1;        // B stages in flight beyond the one being multiplied
+    constexpr int AHEAD_A = ASTAGES - 1;        // A stages likewise
+    static_assert(ASTAGES == S::STAGES || ASTAGES == S::STAGES + 1, "A has at most one buffer more than B");
+    constexpr bool B_FIRST = ASTAGES > S::STAGES;  // B loads of a step before its A loads
+    // loads issued after the last one of the next stage: those of later stages
+    constexpr int WAIT = (AHEAD_A - 1) * S::DMA_A + (AHEAD - 1) * S::DMA_B;
     constexpr int SLOTS = S::KSTEPS * 16;
-    static_assert(AHEAD >= 1 && (AHEAD - 1) * LOADS < 64, "vmcnt range");
+    static_assert(AHEAD >= 1 && WAIT < 64, "vmcnt range");
     static_assert(DOFF + (LOADS - 1) * SPACING < SLOTS, "loads must fit in one K step");
+    constexpr int B_REGION = ASTAGES * S::A_BYTES;  // A buffers first, then the B buffers
+    constexpr int LDS_BYTES = B_REGION + S::STAGES * S::B_BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS of one work-group");
 
-    __shared__ __attribute__((aligned(1024))) char smem[S::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -133,17 +204,18 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     const _Float16 *a_tile = a.A + (int64_t)m0 * a.lda;
     const _Float16 *b_tile = a.B + n0;
 
-    // Load j of stage kt into LDS buffer buf (stages past K load zeros).
+    // Load j of stage kt into LDS buffer buf of its operand (stages past K
+    // load zeros); j < DMA_A loads A, the others B.
     auto dma = [&](int j, int kt, int buf) {
         const int k0 = kt * S::BK;
         const bool in = ok[j] && k0 + kin[j] < a.kmain;
         if (j < S::DMA_A) {
             const int4_t r = make_srd(a_tile + k0);
-            const uint32_t l = (uint32_t)(uintptr_t)(lds + buf * S::STAGE_BYTES + (wave * S::DMA_A + j) * 1024);
+            const uint32_t l = (uint32_t)(uintptr_t)(lds + buf * S::A_BYTES + (wave * S::DMA_A + j) * 1024);
             dma16(r, l, in ? off[j] : kOOB);
         } else {
             const int4_t r = make_srd(b_tile + (int64_t)k0 * a.ldb);
-            const uint32_t l = (uint32_t)(uintptr_t)(lds + buf * S::STAGE_BYTES + S::A_BYTES +
+            const uint32_t l = (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES +
                                                      (wave * S::DMA_B + (j - S::DMA_A)) * 1024);
             dma16(r, l, in ? off[j] : kOOB);
         }
@@ -168,17 +240,23 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     for (int t = 0; t < S::TM; ++t) f[1].a[t] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
 
 #pragma unroll
-    for (int s = 0; s < AHEAD; ++s)
+    for (int s = 0; s < AHEAD_A; ++s) {
 #pragma unroll
-        for (int j = 0; j < LOADS; ++j) dma(j, s, s);
-    wait_vmcnt<(AHEAD - 1) * LOADS>();
+        for (int j = 0; j < S::DMA_A; ++j) dma(j, s, s);
+        if (s < AHEAD)
+#pragma unroll
+            for (int j = S::DMA_A; j < LOADS; ++j) dma(j, s, s);
+    }
+    wait_vmcnt<WAIT>();
     barrier_lds();
 
-    int buf = 0;
+    int bbuf = 0, abuf = 0;
     for (int kt = 0; kt < nk; ++kt) {
-        const int nbuf = buf == 0 ? S::STAGES - 1 : buf - 1;  // stage kt+AHEAD goes where stage kt-1 was
-        LDS_PTR(const char) sA = lds + buf * S::STAGE_BYTES;
-        LDS_PTR(const char) sB = sA + S::A_BYTES;
+        // stage kt+AHEAD of B (kt+AHEAD_A of A) goes where stage kt-1 was
+        const int nbbuf = bbuf == 0 ? S::STAGES - 1 : bbuf - 1;
+        const int nabuf = abuf == 0 ? ASTAGES - 1 : abuf - 1;
+        LDS_PTR(const char) sA = lds + abuf * S::A_BYTES;
+        LDS_PTR(const char) sB = lds + B_REGION + bbuf * S::B_BYTES;
         TLG_SCHED_FENCE();
 #pragma unroll
         for (int q = 0; q < SLOTS; ++q) {
@@ -194,13 +272,20 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
             } else {
                 mfma_tile<S>(f[1], q - 8 - (S::KSTEPS - 1) * 16, acc);
             }
-            if (q >= DOFF && (q - DOFF) % SPACING == 0 && (q - DOFF) / SPACING < LOADS)
-                dma((q - DOFF) / SPACING, kt + AHEAD, nbuf);
+            if (q >= DOFF && (q - DOFF) % SPACING == 0 && (q - DOFF) / SPACING < LOADS) {
+                const int n = (q - DOFF) / SPACING;
+                const int j = !B_FIRST ? n : n < S::DMA_B ? S::DMA_A + n : n - S::DMA_B;
+                if (j < S::DMA_A)
+                    dma(j, kt + AHEAD_A, nabuf);
+                else
+                    dma(j, kt + AHEAD, nbbuf);
+            }
             TLG_SCHED_FENCE();
         }
-        wait_vmcnt<(AHEAD - 1) * LOADS>();  // this wave's loads of stage kt+1 are in LDS
-        barrier_lds();                      // ... and every wave's; stage kt is no longer read
-        buf = buf == S::STAGES - 1 ? 0 : buf + 1;
+        wait_vmcnt<WAIT>();  // this wave's loads of stage kt+1 are in LDS
+        barrier_lds();       // ... and every wave's; stage kt is no longer read
+        bbuf = bbuf == S::STAGES - 1 ? 0 : bbuf + 1;
+        abuf = abuf == ASTAGES - 1 ? 0 : abuf + 1;
     }
 #pragma unroll
     for (int i = 8; i < 16; ++i) mfma_tile<S>(f[1], i, acc);
@@ -211,12 +296,13 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     // by element into buffer 0 once every wave is done with the stages.
     if (a.kmain < a.K) {
         barrier_lds();
-        stage_tail<S>(a, m0, n0, lds, lds + S::A_BYTES, tid);
+        stage_tail<S>(a, m0, n0, lds, lds + B_REGION, tid);
         barrier_lds();
-        mma_kstep<S>(lds, lds + S::A_BYTES, 0, wm0, wn0, lane, acc);
+        mma_kstep<S>(lds, lds + B_REGION, 0, wm0, wn0, lane, acc);
     }
 
-    store_c_tile<S>(a, m0, n0, wm0, wn0, lane, acc);
+    barrier_lds();  // every wave is done with the stages (and the tail block)
+    store_c_tile_lds<S>(a, m0, n0, wave, lane, acc, lds);
 }
 
 using Pipe256x32 = TileShape<256, 256, 32, 2, 2, 4>;
@@ -225,9 +311,10 @@ using Pipe256x64 = TileShape<256, 256, 64, 2, 2, 2>;
 const TileConfig kPipeConfigs[PIPE_CONFIGS] = {
     {Pipe256x32::BM, Pipe256x32::BN, Pipe256x32::BK, Pipe256x32::NT, Pipe256x32::STAGES, "pipe_256x256x32_w2x2_s4"},
     {Pipe256x64::BM, Pipe256x64::BN, Pipe256x64::BK, Pipe256x64::NT, Pipe256x64::STAGES, "pipe_256x256x64_w2x2_s2"},
+    {Pipe256x64::BM, Pipe256x64::BN, Pipe256x64::BK, Pipe256x64::NT, Pipe256x64::STAGES, "pipe_256x256x64_w2x2_s2_a3"},
 };
 
-template <class S, int SPACING, int DOFF>
+template <class S, int SPACING, int DOFF, int ASTAGES>
 static hipError_t launch_pipe_t(const Problem &p, hipStream_t stream) {
     KArgs a;
     a.A = (const _Float16 *)p.A;
@@ -245,17 +332,19 @@ static hipError_t launch_pipe_t(const Problem &p, hipStream_t stream) {
     a.kmain = (p.K % 8 == 0 && p.N % 8 == 0) ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
     a.tiles_m = (a.M + S::BM - 1) / S::BM;
     a.tiles_n = (a.N + S::BN - 1) / S::BN;
-    hipLaunchKernelGGL((k_tiled_pipe<S, SPACING, DOFF>), dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(S::NT), 0,
-                       stream, a);
+    hipLaunchKernelGGL((k_tiled_pipe<S, SPACING, DOFF, ASTAGES>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
+                       dim3(S::NT), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream) {
     switch (config) {
         // four 32-deep stages: loads every 4 slots across the step
-        case PIPE_256x256x32: return launch_pipe_t<Pipe256x32, 4, 3>(p, stream);
+        case PIPE_256x256x32: return launch_pipe_t<Pipe256x32, 4, 3, 4>(p, stream);
         // two 64-deep stages: the next stage's 16 loads go in early, every 2 slots
-        case PIPE_256x256x64: return launch_pipe_t<Pipe256x64, 2, 1>(p, stream);
+        case PIPE_256x256x64: return launch_pipe_t<Pipe256x64, 2, 1, 2>(p, stream);
+        // the same with a third A buffer (160 KiB of LDS): A is loaded two steps ahead
+        case PIPE_256x256x64_A3: return launch_pipe_t<Pipe256x64, 2, 1, 3>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

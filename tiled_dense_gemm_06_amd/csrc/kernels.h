@@ -35,7 +35,7 @@ enum GenConfig { GEN_128x128x32 = 0, GEN_64x64x32 = 1, GEN_CONFIGS = 2 };
 enum SplitConfig { SPLIT_32x128x64 = 0, SPLIT_32x256x64 = 1, SPLIT_TWO_KERNEL_CONFIGS = 2,
                    SPLIT_STREAMK_32x128x64 = 2, SPLIT_WAVES_32x64x64 = 3, SPLIT_CONFIGS = 4 };
 // software-pipelined direct-to-LDS kernels (aligned, large problems)
-enum PipeConfig { PIPE_256x256x32 = 0, PIPE_256x256x64 = 1, PIPE_CONFIGS = 2 };
+enum PipeConfig { PIPE_256x256x32 = 0, PIPE_256x256x64 = 1, PIPE_256x256x64_A3 = 2, PIPE_CONFIGS = 3 };
 
 extern const TileConfig kDmaConfigs[DMA_CONFIGS];
 extern const TileConfig kGenConfigs[GEN_CONFIGS];

@@ -159,6 +159,27 @@ TLG_HD int acc_n(int wn0, int tn, int r, int lane) {
     return wn0 + 32 * tn + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
 }
 
+// ---- epilogue through LDS ----
+// A wave's block of C (WTM x WTN fp16) in LDS: rows of 2*WTN bytes, the
+// 16-byte piece c (columns 8c .. 8c+7) of row r at piece position
+// c ^ (r % (WTN/8)). Writes of 16 lanes (16 rows, one c) and reads of 16
+// lanes (one row, 16 pieces) then touch 16 distinct 16-byte slots of a
+// 256-byte bank window.
+template <class S>
+TLG_HD int epi_lds_offset(int row, int c) {
+    return row * S::WTN * 2 + 16 * (c ^ (row % (S::WTN / 8)));
+}
+// After the lane-pair exchange, lane l holds piece pr (0 or 1) of MFMA tile
+// (tn, tm): row 32*tm + l%32 of the wave block, piece 4*tn + 2*pr + l/32.
+TLG_HD int epi_piece_row(int tm, int lane) { return 32 * tm + lane % 32; }
+TLG_HD int epi_piece_index(int tn, int pr, int lane) { return 4 * tn + 2 * pr + lane / 32; }
+// Read-back instruction k: lane l takes piece l % (WTN/8) of row
+// k * (64 / (WTN/8)) + l / (WTN/8).
+template <class S>
+TLG_HD int epi_read_row(int k, int lane) { return k * (64 / (S::WTN / 8)) + lane / (S::WTN / 8); }
+template <class S>
+TLG_HD int epi_read_piece(int lane) { return lane % (S::WTN / 8); }
+
 // ---- tile order ----
 // Work-groups are handed to the 8 XCDs of the device round-robin by id, so
 // id p runs on XCD p % 8. Renumber so that each XCD receives a contiguous

@@ -15,6 +15,14 @@ Usage (after the counter runs, on the CSV files rocprofv3 wrote)::
 It records, under the digest of the library's kernel sources, the scaled
 fetch and write bytes per launch in ``profiles/traffic.json``; ``bench.py``
 reports them only while the kernel sources still have that digest.
+
+``summary`` writes the Markdown summary of one workload's profile (the
+kernel-trace statistics of a command, and the scaled counter bytes when
+given) for ``profiles/``::
+
+    python -m tiled_dense_gemm_06_amd.profiling summary --workload square8192 \
+        --kernel k_tiled_pipe --trace DIR --trace-cmd "..." [--fetch F.csv --write W.csv \
+        --copy-fetch CF.csv --copy-write CW.csv --copy-mib 512 --counter-cmd "..."] --out FILE
 """
 from __future__ import annotations
 
@@ -101,6 +109,63 @@ def measured_traffic(workload: str):
     return None if not rec else rec.get("bytes_per_launch")
 
 
+PEAK_MFMA_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def _stats_rows(trace_dir: str):
+    with open(os.path.join(trace_dir, "run_kernel_stats.csv")) as f:
+        return list(csv.DictReader(f))
+
+
+def summary(args) -> str:
+    from . import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    rows = _stats_rows(args.trace)
+    main = [r for r in rows if args.kernel in r["Name"]]
+    if not main:
+        raise ValueError(f"no kernel matching {args.kernel!r} in {args.trace}")
+    r0 = max(main, key=lambda r: int(r["Calls"]))
+    avg_ns = float(r0["AverageNs"])
+    lines = [f"# {args.title or args.kernel} — workload {w.name}", ""]
+    lines += ["Kernel trace (from the repository root, on one MI355X):", "", "    " + args.trace_cmd, ""]
+    lines += ["| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']):,.0f} | {float(r['MinNs']):,.0f} | "
+                     f"{float(r['MaxNs']):,.0f} |")
+    lines.append("")
+    if args.note:
+        lines += [args.note, ""]
+    tflops = w.flop / (avg_ns * 1e-9) / 1e12
+    gbs = w.alg_bytes / (avg_ns * 1e-9) / 1e9
+    lines.append(f"From the trace average ({avg_ns / 1e3:,.1f} us per launch): {tflops:,.1f} TFLOP/s "
+                 f"({100 * tflops / PEAK_MFMA_TFLOPS:.1f} % of the {PEAK_MFMA_TFLOPS} TFLOP/s fp16 dense peak), "
+                 f"{gbs:,.0f} GB/s of algorithmic bytes ({w.alg_bytes:,} B: A, B and C once; "
+                 f"{100 * gbs / PEAK_HBM_GBS:.1f} % of {PEAK_HBM_GBS:.0f} GB/s).")
+    lines.append("")
+    if args.fetch:
+        copy_bytes = args.copy_mib << 20
+        ff = copy_bytes / (counter_values(args.copy_fetch, "FETCH_SIZE", COPY_KERNEL)[-1] * 1024.0)
+        wf = copy_bytes / (counter_values(args.copy_write, "WRITE_SIZE", COPY_KERNEL)[-1] * 1024.0)
+        fetch = mean(counter_values(args.fetch, "FETCH_SIZE", args.kernel)) * 1024.0 * ff
+        write = mean(counter_values(args.write, "WRITE_SIZE", args.kernel)) * 1024.0 * wf
+        lines += ["HBM counters, one pass each (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch):", "",
+                  "    " + args.counter_cmd.replace("COUNTERDIR", "fetch").replace("COUNTER", "FETCH_SIZE"),
+                  "    " + args.counter_cmd.replace("COUNTERDIR", "write").replace("COUNTER", "WRITE_SIZE"), "",
+                  f"scaled by a plain {args.copy_mib} MiB device copy measured the same way "
+                  f"(`python3 bench.py --copy-calibration {args.copy_mib} --steps 3 --warmup 1` under each "
+                  f"counter): fetch factor {ff:.4f}, write factor {wf:.4f}.", "",
+                  "| per launch | bytes | x algorithmic |", "|---|---|---|",
+                  f"| fetched from beyond L2 | {fetch:,.0f} | {fetch / w.alg_bytes:.2f} |",
+                  f"| written | {write:,.0f} | {write / w.alg_bytes:.2f} |",
+                  f"| total (`traffic`) | {fetch + write:,.0f} | {(fetch + write) / w.alg_bytes:.2f} |", ""]
+    text = "\n".join(lines)
+    with open(args.out, "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -112,8 +177,25 @@ def main():
     t.add_argument("--copy-fetch", required=True)
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-mib", type=int, required=True)
+    m = sub.add_parser("summary")
+    m.add_argument("--workload", required=True)
+    m.add_argument("--kernel", required=True, help="substring of the kernel name")
+    m.add_argument("--title", default="")
+    m.add_argument("--trace", required=True, help="rocprofv3 --kernel-trace --stats output directory")
+    m.add_argument("--trace-cmd", required=True)
+    m.add_argument("--note", default="")
+    m.add_argument("--fetch")
+    m.add_argument("--write")
+    m.add_argument("--copy-fetch")
+    m.add_argument("--copy-write")
+    m.add_argument("--copy-mib", type=int, default=512)
+    m.add_argument("--counter-cmd", default="")
+    m.add_argument("--out", required=True)
     args = ap.parse_args()
-    print(json.dumps(traffic(args)))
+    if args.cmd == "traffic":
+        print(json.dumps(traffic(args)))
+    else:
+        summary(args)
 
 
 if __name__ == "__main__":
