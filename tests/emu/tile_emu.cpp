@@ -375,7 +375,8 @@ extern "C" long emu_check_remap(int max_nwg) {
     return bad;
 }
 
-// The LDS epilogue of the pipelined kernel for one wave block (EP64 shape):
+// The LDS epilogue (pipelined and direct-to-LDS kernels) for every wave block
+// of tile shape S:
 // every result register is followed through the conversion into 32-bit
 // pairs, the lane-pair exchange (v_permlane32_swap: the upper 32 lanes of its
 // first operand trade places with the lower 32 lanes of its second), the
@@ -383,8 +384,8 @@ extern "C" long emu_check_remap(int max_nwg) {
 // acc_m/acc_n assign to it; every LDS piece is written once, and each group
 // of 16 lanes touches 16 distinct 16-byte slots of a 256-byte window on both
 // sides. Returns the number of violations.
-extern "C" long emu_check_epilogue() {
-    using S = EP64;
+template <class S>
+long check_epilogue() {
     long bad = 0;
     const int CH = S::WTN / 8;
     for (int wave = 0; wave < S::WAVES; ++wave) {
@@ -443,4 +444,14 @@ extern "C" long emu_check_epilogue() {
         }
     }
     return bad;
+}
+
+extern "C" long emu_check_epilogue(int config) {
+    switch (config) {
+        case 0: return check_epilogue<E256>();
+        case 1: return check_epilogue<E128>();
+        case 2: return check_epilogue<E64>();
+        case 3: return check_epilogue<EP64>();
+        default: return -1;
+    }
 }

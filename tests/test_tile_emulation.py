@@ -39,7 +39,7 @@ def emu(tmp_path_factory):
     L.emu_check_remap.restype = l
     L.emu_check_streamk.argtypes = [l, i, i]
     L.emu_check_streamk.restype = l
-    L.emu_check_epilogue.argtypes = []
+    L.emu_check_epilogue.argtypes = [i]
     L.emu_check_epilogue.restype = l
     return L
 
@@ -68,11 +68,13 @@ def test_streamk_ranges(emu, tiles, ipt, G):
     assert emu.emu_check_streamk(total, min(G, total), ipt) == 0
 
 
-def test_lds_epilogue_index_math(emu):
-    """The pipelined kernel's C epilogue through LDS: every result register
-    reaches its own C position, each LDS piece is written once, and neither
-    the writes nor the read-back have bank conflicts."""
-    assert emu.emu_check_epilogue() == 0
+@pytest.mark.parametrize("config", sorted(DMA_CONFIGS))
+def test_lds_epilogue_index_math(emu, config):
+    """The C epilogue through LDS (wave blocks of 128, 64 and 32 columns):
+    every result register reaches its own C position, each LDS piece is
+    written once, and neither the writes nor the read-back have bank
+    conflicts."""
+    assert emu.emu_check_epilogue(config) == 0
 
 
 # shapes that satisfy the direct-to-LDS conditions (K % 8 == 0, N % 8 == 0), several tiles, ragged tails

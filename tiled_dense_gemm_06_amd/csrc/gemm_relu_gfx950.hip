@@ -140,7 +140,8 @@ __global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
         mma_kstep<S>(lds, lds + S::A_BYTES, 0, wm0, wn0, lane, acc);
     }
 
-    // Epilogue: a lane owns four consecutive n of one row m per register quad.
+    // Epilogue: split-K partials go out as fp32 (a lane owns four consecutive
+    // n of one row m per register quad); C goes through LDS.
     if (SPLIT) {
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
             a.W + ((int64_t)blockIdx.y * a.M + m0) * a.N + n0, (short)0, (int)kRange, 0x00020000);
@@ -160,7 +161,8 @@ __global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
                 }
             }
     } else {
-        store_c_tile<S>(a, m0, n0, wm0, wn0, lane, acc);
+        barrier_lds();  // every wave is done with the stages (and the tail block)
+        store_c_tile_lds<S>(a, m0, n0, wave, lane, acc, lds);
     }
 }
 

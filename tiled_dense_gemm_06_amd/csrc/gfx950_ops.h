@@ -193,6 +193,65 @@ __device__ __forceinline__ void store_c_tile(const KArgs &a, int m0, int n0, int
         }
 }
 
+// Epilogue through LDS: ReLU and the fp16 conversion, then the two 8-byte
+// halves of each 16-byte row piece, held by lanes l and l+32, are brought
+// into one lane (v_permlane32_swap exchanges the upper 32 lanes of its first
+// operand with the lower 32 lanes of its second), the pieces go to this
+// wave's WTM x WTN block of LDS (layout: epi_lds_offset, conflict-free for
+// every 16 lanes), and come back as whole row segments of the wave block for
+// 16-byte buffer stores (rows >= M dropped by the range check, a piece
+// crossing column N stored element by element). The caller makes sure no
+// wave still reads or loads into the first BM*BN*2 bytes of LDS.
+template <class S>
+__device__ __forceinline__ void store_c_tile_lds(const KArgs &a, int m0, int n0, int wave, int lane,
+                                                 const float16_t (&acc)[S::TN][S::TM], LDS_PTR(char) lds) {
+    constexpr int PITCH = S::WTN * 2, CH = S::WTN / 8;
+    static_assert(CH == 4 || CH == 8 || CH == 16, "wave blocks 32, 64 or 128 columns wide");
+    static_assert(S::WAVES * S::WTM * PITCH <= S::STAGES * S::STAGE_BYTES, "C tile must fit the stages' LDS");
+    LDS_PTR(char) q = lds + wave * S::WTM * PITCH;
+    const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm) {
+            uint32_t d[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const half2_t h = {relu_to_half(acc[tn][tm][2 * i]), relu_to_half(acc[tn][tm][2 * i + 1])};
+                d[i] = __builtin_bit_cast(uint32_t, h);
+            }
+            const int row = epi_piece_row(tm, lane);
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                // quads 2*pr and 2*pr+1 (registers 4 apart): lane l < 32 ends up
+                // with columns 16*pr + 0..7 of its row, lane l+32 with 16*pr + 8..15
+                const auto s0 = __builtin_amdgcn_permlane32_swap(d[4 * pr], d[4 * pr + 2], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(d[4 * pr + 1], d[4 * pr + 3], false, false);
+                const int4_t v = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+                *(LDS_PTR(int4_t))(q + epi_lds_offset<S>(row, epi_piece_index(tn, pr, lane))) = v;
+            }
+        }
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc(a.C + (int64_t)m0 * a.ldc + n0, (short)0, (int)kRange, 0x00020000);
+    constexpr int ROWS = 64 / CH;  // rows per wave instruction
+#pragma unroll
+    for (int k = 0; k < S::WTM / ROWS; ++k) {
+        const int row = epi_read_row<S>(k, lane), c = epi_read_piece<S>(lane);
+        const int4_t v = *(LDS_PTR(const int4_t))(q + epi_lds_offset<S>(row, c));
+        const int mr = wm0 + row, nr = wn0 + 8 * c;
+        const bool row_in = m0 + mr < a.M;
+        if (n0 + nr + 8 <= a.N || !row_in) {
+            __builtin_amdgcn_raw_buffer_store_b128(v, rc, row_in ? (uint32_t)((mr * a.ldc + nr) * 2) : kOOB, 0, 0);
+        } else {
+            const half8_t h = __builtin_bit_cast(half8_t, v);
+            _Float16 *crow = a.C + (int64_t)(m0 + mr) * a.ldc + n0 + nr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n0 + nr + e < a.N) crow[e] = h[e];
+        }
+    }
+}
+
 }  // namespace tlg
 
 #endif

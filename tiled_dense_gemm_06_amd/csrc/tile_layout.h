@@ -160,14 +160,16 @@ TLG_HD int acc_n(int wn0, int tn, int r, int lane) {
 }
 
 // ---- epilogue through LDS ----
-// A wave's block of C (WTM x WTN fp16) in LDS: rows of 2*WTN bytes, the
-// 16-byte piece c (columns 8c .. 8c+7) of row r at piece position
-// c ^ (r % (WTN/8)). Writes of 16 lanes (16 rows, one c) and reads of 16
-// lanes (one row, 16 pieces) then touch 16 distinct 16-byte slots of a
-// 256-byte bank window.
+// A wave's block of C (WTM x WTN fp16) in LDS: rows of 2*WTN bytes (CH =
+// WTN/8 pieces of 16 bytes), the piece c (columns 8c .. 8c+7) of row r at
+// piece position c ^ ((r / (16/CH)) % CH). A 256-byte bank window holds
+// 16/CH rows, so writes of 16 lanes (16 rows, one c) and reads of 16 lanes
+// (16/CH consecutive rows, all their pieces) touch 16 distinct 16-byte slots
+// of a window (CH = 4, 8 or 16).
 template <class S>
 TLG_HD int epi_lds_offset(int row, int c) {
-    return row * S::WTN * 2 + 16 * (c ^ (row % (S::WTN / 8)));
+    constexpr int CH = S::WTN / 8;
+    return row * S::WTN * 2 + 16 * (c ^ ((row / (16 / CH)) % CH));
 }
 // After the lane-pair exchange, lane l holds piece pr (0 or 1) of MFMA tile
 // (tn, tm): row 32*tm + l%32 of the wave block, piece 4*tn + 2*pr + l/32.
