@@ -66,7 +66,7 @@ def test_check_args(args, expect):
 
 
 def test_plan_shapes_of_the_workloads():
-    assert tlg.plan(8192, 8192, 8192)["config_name"] == "pipe_256x256x64_w2x2_s2_a3"
+    assert tlg.plan(8192, 8192, 8192)["config_name"] == "pipe_256x256x64_w2x4_s2_a3"
     assert tlg.plan(4096, 4096, 4096)["variant_name"] == "tiled_pipe"
     p = tlg.plan(3001, 2049, 1537)  # odd sizes and leading dimensions: direct-to-LDS loads, staged K tail
     assert p["variant_name"] == "tiled_dma" and p["config_name"] == "dma_128x128x32_w2x2_s4"
@@ -126,7 +126,7 @@ def test_forced_variants():
         tlg.plan(512, 512, 512, config=0)
     with pytest.raises(tlg.TlgError):  # no such configuration
         tlg.plan(512, 512, 512, variant=tlg.TLG_VARIANT_TILED_PIPE, config=99)
-    for cfg in range(3):
+    for cfg in range(5):
         p = tlg.plan(1024, 1024, 1024, variant=tlg.TLG_VARIANT_TILED_PIPE, config=cfg)
         assert p["config"] == cfg and p["config_name"].startswith("pipe_256x256")
 

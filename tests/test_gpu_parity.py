@@ -206,7 +206,7 @@ def test_large_square_sampled(dev, name):
     assert np.array_equal(got[rows], oracle.gemm_relu_rows(Ai, Bi, rows))
 
 
-@pytest.mark.parametrize("config", [0, 1, 2])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("shape", [(300, 264, 200), (513, 520, 72), (1024, 1032, 1000), (256, 256, 8),
                                    (257, 8, 4104), (301, 259, 203)])
 def test_pipe_configs(dev, config, shape):
@@ -217,6 +217,23 @@ def test_pipe_configs(dev, config, shape):
     ref = oracle.gemm_relu(A, B)
     big = torch.full((M + 2, N + 8), float("nan"), dtype=torch.float16, device=dev)
     tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), out=big[:M, :N], variant=V_PIPE, config=config)
+    torch.cuda.synchronize()
+    allb = bits(big)
+    assert np.array_equal(allb[:M, :N], ref)
+    assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+
+
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("shape", [(300, 264, 200), (513, 520, 72), (1024, 1032, 1000), (257, 8, 4104),
+                                   (301, 259, 203)])
+def test_dma_configs(dev, config, shape):
+    """Every tile configuration of the direct-to-LDS kernel (four and eight
+    waves): ragged M and N, K tails, the LDS epilogue's edge pieces."""
+    M, N, K = shape
+    A, B = wl.make_random(M, N, K, seed=M ^ N ^ K ^ 7, kind="integer_pos")
+    ref = oracle.gemm_relu(A, B)
+    big = torch.full((M + 2, N + 8), float("nan"), dtype=torch.float16, device=dev)
+    tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), out=big[:M, :N], variant=V_DMA, config=config)
     torch.cuda.synchronize()
     allb = bits(big)
     assert np.array_equal(allb[:M, :N], ref)

@@ -201,7 +201,7 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
     // there are enough tiles to give most CUs one
     if (variant == TLG_VARIANT_TILED_PIPE || variant == TLG_VARIANT_AUTO) {
         if (!config_ok(config, tlg::PIPE_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
-        const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64_A3;
+        const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64_W8_A3;
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
         if (dma_ok(p, tc.bm, tc.bn, tc.bk) && (variant == TLG_VARIANT_TILED_PIPE || tiles >= 224)) {

@@ -330,6 +330,8 @@ __global__ __launch_bounds__(256) void k_fill_zero(_Float16 *C, int M, int N, in
 using Dma256 = TileShape<256, 256, 32, 2, 2, 4>;
 using Dma128 = TileShape<128, 128, 32, 2, 2, 4>;
 using Dma64 = TileShape<64, 64, 64, 2, 2, 3>;
+using Dma256w8 = TileShape<256, 256, 64, 2, 4, 2>;
+using Dma256w8x32 = TileShape<256, 256, 32, 2, 4, 4>;
 using Gen128 = TileShape<128, 128, 32, 2, 2, 2>;
 using Gen64 = TileShape<64, 64, 32, 2, 2, 2>;
 using Split32x128 = TileShape<32, 128, 64, 1, 4, 4>;
@@ -339,6 +341,9 @@ const TileConfig kDmaConfigs[DMA_CONFIGS] = {
     {Dma256::BM, Dma256::BN, Dma256::BK, Dma256::NT, Dma256::STAGES, "dma_256x256x32_w2x2_s4"},
     {Dma128::BM, Dma128::BN, Dma128::BK, Dma128::NT, Dma128::STAGES, "dma_128x128x32_w2x2_s4"},
     {Dma64::BM, Dma64::BN, Dma64::BK, Dma64::NT, Dma64::STAGES, "dma_64x64x64_w2x2_s3"},
+    {Dma256w8::BM, Dma256w8::BN, Dma256w8::BK, Dma256w8::NT, Dma256w8::STAGES, "dma_256x256x64_w2x4_s2"},
+    {Dma256w8x32::BM, Dma256w8x32::BN, Dma256w8x32::BK, Dma256w8x32::NT, Dma256w8x32::STAGES,
+     "dma_256x256x32_w2x4_s4"},
 };
 const TileConfig kGenConfigs[GEN_CONFIGS] = {
     {Gen128::BM, Gen128::BN, Gen128::BK, Gen128::NT, 2, "gen_128x128x32_w2x2"},
@@ -399,6 +404,8 @@ hipError_t launch_tiled_dma(int config, const Problem &p, hipStream_t stream) {
         case DMA_256x256x32: return launch_dma_t<Dma256, false>(a, 1, stream);
         case DMA_128x128x32: return launch_dma_t<Dma128, false>(a, 1, stream);
         case DMA_64x64x64: return launch_dma_t<Dma64, false>(a, 1, stream);
+        case DMA_256x256x64_W8: return launch_dma_t<Dma256w8, false>(a, 1, stream);
+        case DMA_256x256x32_W8: return launch_dma_t<Dma256w8x32, false>(a, 1, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -75,13 +75,17 @@ __device__ __forceinline__ void mfma_tile(const Frags<S> &f, int i, float16_t (&
 // Nothing may be scheduled across this point (keeps the hand-written order).
 #define TLG_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// One K step of the loop is a fixed sequence of KSTEPS*16 MFMA slots:
-//   slots 0..7        MFMAs 8..15 of the previous stage's last k-step (held in
-//                     f[1]); after them the 12 LDS reads of this stage's
+// One K step of the loop is a fixed sequence of KSTEPS*T MFMA slots, T =
+// TM*TN the wave's MFMA tiles (16 for four waves of 128 x 128, 8 for eight
+// waves of 128 x 64), H = T/2:
+//   slots 0..H-1      MFMAs H..T-1 of the previous stage's last k-step (held
+//                     in f[1]); after them the LDS reads of this stage's
 //                     k-step-0 fragments into f[0], two per slot;
-//   next 16 per ks    k-steps 0..KSTEPS-2: 16 MFMAs on f[ks & 1], with the 12
+//   next T per ks     k-steps 0..KSTEPS-2: T MFMAs on f[ks & 1], with the
 //                     reads of k-step ks+1 into f[(ks+1) & 1], one per slot;
-//   last 8 slots      MFMAs 0..7 of the last k-step (f[1]).
+//   last H slots      MFMAs 0..H-1 of the last k-step (f[1]).
+// With eight waves two share each SIMD and the hardware interleaves their
+// slots, which covers one wave's waits with the other's MFMAs.
 // The LOADS direct-to-LDS loads go after slots DOFF, DOFF+SPACING, ...: the
 // B tile of stage kt+STAGES-1 and the A tile of stage kt+ASTAGES-1 (A may
 // have one LDS buffer more than B, which gives its loads a step more to
@@ -90,9 +94,10 @@ __device__ __forceinline__ void mfma_tile(const Frags<S> &f, int i, float16_t (&
 // kt). The C tile leaves through LDS (store_c_tile_lds).
 template <class S, int SPACING, int DOFF, int ASTAGES>
 __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
-    static_assert(S::TM * S::TN == 16, "schedule written for 16 MFMA tiles per wave");
-    static_assert(S::KSTEPS % 2 == 0, "the last k-step of a stage must use f[1]");
-    static_assert(kFragReads<S> <= 12, "fragment reads must fit under the MFMAs of a k-step");
+    constexpr int T = S::TM * S::TN;  // MFMA tiles of a wave (MFMAs per k-step)
+    constexpr int H = T / 2;
+    static_assert(T % 2 == 0 && S::KSTEPS % 2 == 0, "the last k-step of a stage must use f[1]");
+    static_assert(kFragReads<S> <= T && kFragReads<S> <= 2 * H, "fragment reads must fit under the MFMAs of a k-step");
     constexpr int LOADS = S::DMA_A + S::DMA_B;  // direct-to-LDS loads per wave per stage
     constexpr int AHEAD = S::STAGES - 1;        // B stages in flight beyond the one being multiplied
     constexpr int AHEAD_A = ASTAGES - 1;        // A stages likewise
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     constexpr bool B_FIRST = ASTAGES > S::STAGES;  // B loads of a step before its A loads
     // loads issued after the last one of the next stage: those of later stages
     constexpr int WAIT = (AHEAD_A - 1) * S::DMA_A + (AHEAD - 1) * S::DMA_B;
-    constexpr int SLOTS = S::KSTEPS * 16;
+    constexpr int SLOTS = S::KSTEPS * T;
     static_assert(AHEAD >= 1 && WAIT < 64, "vmcnt range");
     static_assert(DOFF + (LOADS - 1) * SPACING < SLOTS, "loads must fit in one K step");
     constexpr int B_REGION = ASTAGES * S::A_BYTES;  // A buffers first, then the B buffers
@@ -200,17 +205,17 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
         TLG_SCHED_FENCE();
 #pragma unroll
         for (int q = 0; q < SLOTS; ++q) {
-            if (q < 8) {
-                mfma_tile<S>(f[1], 8 + q, acc);
+            if (q < H) {
+                mfma_tile<S>(f[1], H + q, acc);
 #pragma unroll
                 for (int r = 2 * q; r < 2 * q + 2; ++r)
                     if (r < kFragReads<S>) frag_read<S>(f[0], sA, sB, wm0, wn0, 0, lane, r);
-            } else if (q < 8 + (S::KSTEPS - 1) * 16) {
-                const int ks = (q - 8) / 16, i = (q - 8) % 16;
+            } else if (q < H + (S::KSTEPS - 1) * T) {
+                const int ks = (q - H) / T, i = (q - H) % T;
                 mfma_tile<S>(f[ks & 1], i, acc);
                 if (i < kFragReads<S>) frag_read<S>(f[(ks + 1) & 1], sA, sB, wm0, wn0, ks + 1, lane, i);
             } else {
-                mfma_tile<S>(f[1], q - 8 - (S::KSTEPS - 1) * 16, acc);
+                mfma_tile<S>(f[1], q - H - (S::KSTEPS - 1) * T, acc);
             }
             if (q >= DOFF && (q - DOFF) % SPACING == 0 && (q - DOFF) / SPACING < LOADS) {
                 const int n = (q - DOFF) / SPACING;
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
         abuf = abuf == ASTAGES - 1 ? 0 : abuf + 1;
     }
 #pragma unroll
-    for (int i = 8; i < 16; ++i) mfma_tile<S>(f[1], i, acc);
+    for (int i = H; i < T; ++i) mfma_tile<S>(f[1], i, acc);
     // No load may still be writing LDS when the work-group ends.
     wait_vmcnt<0>();
 
@@ -247,11 +252,16 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
 
 using Pipe256x32 = TileShape<256, 256, 32, 2, 2, 4>;
 using Pipe256x64 = TileShape<256, 256, 64, 2, 2, 2>;
+using Pipe256x64w8 = TileShape<256, 256, 64, 2, 4, 2>;  // eight waves, two per SIMD
 
 const TileConfig kPipeConfigs[PIPE_CONFIGS] = {
     {Pipe256x32::BM, Pipe256x32::BN, Pipe256x32::BK, Pipe256x32::NT, Pipe256x32::STAGES, "pipe_256x256x32_w2x2_s4"},
     {Pipe256x64::BM, Pipe256x64::BN, Pipe256x64::BK, Pipe256x64::NT, Pipe256x64::STAGES, "pipe_256x256x64_w2x2_s2"},
     {Pipe256x64::BM, Pipe256x64::BN, Pipe256x64::BK, Pipe256x64::NT, Pipe256x64::STAGES, "pipe_256x256x64_w2x2_s2_a3"},
+    {Pipe256x64w8::BM, Pipe256x64w8::BN, Pipe256x64w8::BK, Pipe256x64w8::NT, Pipe256x64w8::STAGES,
+     "pipe_256x256x64_w2x4_s2"},
+    {Pipe256x64w8::BM, Pipe256x64w8::BN, Pipe256x64w8::BK, Pipe256x64w8::NT, Pipe256x64w8::STAGES,
+     "pipe_256x256x64_w2x4_s2_a3"},
 };
 
 template <class S, int SPACING, int DOFF, int ASTAGES>
@@ -285,6 +295,9 @@ hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream) {
         case PIPE_256x256x64: return launch_pipe_t<Pipe256x64, 2, 1, 2>(p, stream);
         // the same with a third A buffer (160 KiB of LDS): A is loaded two steps ahead
         case PIPE_256x256x64_A3: return launch_pipe_t<Pipe256x64, 2, 1, 3>(p, stream);
+        // eight waves (two per SIMD, 128 x 64 each): 8 loads per wave and stage
+        case PIPE_256x256x64_W8: return launch_pipe_t<Pipe256x64w8, 2, 1, 2>(p, stream);
+        case PIPE_256x256x64_W8_A3: return launch_pipe_t<Pipe256x64w8, 2, 1, 3>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -25,7 +25,14 @@ struct TileConfig {
     const char *name;
 };
 // direct-to-LDS (aligned) configurations
-enum DmaConfig { DMA_256x256x32 = 0, DMA_128x128x32 = 1, DMA_64x64x64 = 2, DMA_CONFIGS = 3 };
+enum DmaConfig {
+    DMA_256x256x32 = 0,
+    DMA_128x128x32 = 1,
+    DMA_64x64x64 = 2,
+    DMA_256x256x64_W8 = 3,  // eight waves, two per SIMD
+    DMA_256x256x32_W8 = 4,
+    DMA_CONFIGS = 5
+};
 // register-staged (any alignment) configurations
 enum GenConfig { GEN_128x128x32 = 0, GEN_64x64x32 = 1, GEN_CONFIGS = 2 };
 // split-K partial kernels (direct-to-LDS, aligned)
@@ -35,7 +42,14 @@ enum GenConfig { GEN_128x128x32 = 0, GEN_64x64x32 = 1, GEN_CONFIGS = 2 };
 enum SplitConfig { SPLIT_32x128x64 = 0, SPLIT_32x256x64 = 1, SPLIT_TWO_KERNEL_CONFIGS = 2,
                    SPLIT_STREAMK_32x128x64 = 2, SPLIT_WAVES_32x64x64 = 3, SPLIT_CONFIGS = 4 };
 // software-pipelined direct-to-LDS kernels (aligned, large problems)
-enum PipeConfig { PIPE_256x256x32 = 0, PIPE_256x256x64 = 1, PIPE_256x256x64_A3 = 2, PIPE_CONFIGS = 3 };
+enum PipeConfig {
+    PIPE_256x256x32 = 0,
+    PIPE_256x256x64 = 1,
+    PIPE_256x256x64_A3 = 2,
+    PIPE_256x256x64_W8 = 3,  // eight waves, two per SIMD
+    PIPE_256x256x64_W8_A3 = 4,
+    PIPE_CONFIGS = 5
+};
 
 extern const TileConfig kDmaConfigs[DMA_CONFIGS];
 extern const TileConfig kGenConfigs[GEN_CONFIGS];
