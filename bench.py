@@ -97,6 +97,11 @@ def main() -> int:
                          "auto, tiled_pipe, tiled_dma, tiled_general, splitk, naive")
     ap.add_argument("--config", type=int, default=-1, help="tile configuration index of --variant (-1 = library's choice)")
     ap.add_argument("--splits", type=int, default=0, help="split-K count for --variant splitk (0 = library's choice)")
+    ap.add_argument("--trans-b", action="store_true",
+                    help="pass B transposed (an N x K row-major copy) through tlg_gemm_relu_bt")
+    ap.add_argument("--grouped", type=int, default=0, metavar="G",
+                    help="split M into G row blocks (2 <= G <= 16) and run them as one tlg_gemm_relu_grouped "
+                         "call (the blocks share B); the work per step is unchanged")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, time a plain device-to-device copy of MIB MiB (the reference "
                          "kernel for scaling the HBM byte counters)")
@@ -129,7 +134,25 @@ def main() -> int:
         print(f"bench.py: unknown variant {args.variant}", file=sys.stderr)
         return 2
     variant = names[args.variant]
-    plan = tlg.plan(w.M, w.N, w.K, variant=variant, config=args.config, splits=args.splits)
+    if args.grouped and not 2 <= args.grouped <= 16:
+        print("bench.py: --grouped takes 2 .. 16", file=sys.stderr)
+        return 2
+    if (args.trans_b or args.grouped) and (variant != tlg.TLG_VARIANT_AUTO or args.splits):
+        print("bench.py: --trans-b / --grouped take only --config", file=sys.stderr)
+        return 2
+    if args.trans_b:
+        B = np.ascontiguousarray(B.T)
+    if args.grouped:
+        # the grouped call picks its tile by the total tile count of the blocks
+        rows = [(w.M * g // args.grouped, w.M * (g + 1) // args.grouped) for g in range(args.grouped)]
+        t256 = sum(-(-(r1 - r0) // 256) * -(-w.N // 256) for r0, r1 in rows)
+        t128 = sum(-(-(r1 - r0) // 128) * -(-w.N // 128) for r0, r1 in rows)
+        gcfg = args.config if args.config >= 0 else (0 if t256 >= 224 else 1 if t128 >= 192 else 2)
+        plan = {"config_name": tlg.tlg_plan_config_name(tlg.TLG_VARIANT_TILED_DMA, gcfg), "variant_name": "grouped",
+                "splits": 1}
+    else:
+        plan = tlg.plan(w.M, w.N, w.K, variant=variant, config=args.config, splits=args.splits,
+                        trans_b=args.trans_b)
 
     # Rotate among R copies of the inputs and outputs so the working set is
     # more than twice the Infinity Cache: every step reads from HBM.
@@ -145,8 +168,13 @@ def main() -> int:
 
     def step(i):
         j = i % R
-        tlg.gemm_relu(As[j], Bs[j], out=Cs[j], handle=h, stream=stream, variant=variant, config=args.config,
-                      splits=args.splits)
+        if args.grouped:
+            tlg.gemm_relu_grouped([As[j][r0:r1] for r0, r1 in rows], [Bs[j]] * len(rows),
+                                  [Cs[j][r0:r1] for r0, r1 in rows], trans_b=args.trans_b, config=args.config,
+                                  handle=h, stream=stream)
+        else:
+            tlg.gemm_relu(As[j], Bs[j], out=Cs[j], handle=h, stream=stream, variant=variant, config=args.config,
+                          splits=args.splits, trans_b=args.trans_b)
 
     for i in range(args.warmup):
         step(i)
@@ -177,7 +205,8 @@ def main() -> int:
         achieved = w.flop / avg_launch_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_MFMA_TFLOPS}
-    roof["traffic"] = measured_traffic(w.name) if args.variant == "auto" else None
+    plain = args.variant == "auto" and args.config < 0 and not (args.trans_b or args.grouped)
+    roof["traffic"] = measured_traffic(w.name) if plain else None
     roof["kernel"] = plan["config_name"]
     roof["launch_ms_avg"] = avg_launch_s * 1e3
     roof["launch_ms_min"] = float(np.min(per_launch_ms))
@@ -190,6 +219,7 @@ def main() -> int:
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "seed": w.seed, "inputs": w.description,
                    "lda": w.K, "ldb": w.N, "ldc": w.N, "kernel": plan["config_name"],
                    "variant": plan["variant_name"], "splits": plan["splits"], "rotated_buffers": R,
+                   "trans_b": bool(args.trans_b), "grouped": args.grouped,
                    "accumulate": "f32", "epilogue": "relu, round-to-nearest-even to f16"},
         "roofline": roof,
         "pct_of_fp16_peak": 100.0 * tflops / PEAK_MFMA_TFLOPS,

@@ -153,6 +153,72 @@ const char *tlg_status_string(tlg_status s);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int32_t tlg_version(void);
 
+/* ---- layout and batching variants ----
+ * The same operation with B given transposed, and several problems in one
+ * launch. The TileLang article (aiwiki.ai/wiki/tilelang, "Backend Coverage",
+ * key technical milestones) lists a grouped GEMM with a transposed B matrix
+ * among the kernels built with the DSL; the operation of each problem is
+ * still the quick-start matmul_relu. */
+
+/* C = ReLU(A . Bt^T): Bt is the N x K fp16 row-major matrix (B transposed),
+ * ldbt >= max(1, K); everything else as tlg_gemm_relu. B's tiles are loaded
+ * and read like A's: by the pipelined kernel when the problem has at least
+ * 224 output tiles of 256 x 256, else by the direct-to-LDS tiled kernel (tile
+ * by tile count). TLG_ERROR_NOT_SUPPORTED when a tile's byte offsets exceed
+ * 2 GB (e.g. ldbt * 256 * 2 >= 2^31); nothing is enqueued then. */
+tlg_status tlg_gemm_relu_bt(tlg_handle h, int64_t M, int64_t N, int64_t K,
+                            const void *A, int64_t lda,
+                            const void *Bt, int64_t ldbt,
+                            void *C, int64_t ldc,
+                            hipStream_t stream);
+
+/* tlg_gemm_relu_bt with a forced kernel family and tile configuration, for
+ * tests and measurements: variant TLG_VARIANT_AUTO (then config must be -1),
+ * TLG_VARIANT_TILED_DMA (configs 0..2) or TLG_VARIANT_TILED_PIPE (configs 2
+ * and 4, the ones with a third A buffer); config -1 lets the library choose
+ * inside the family. */
+tlg_status tlg_gemm_relu_bt_variant(tlg_handle h, int32_t variant, int32_t config, int64_t M, int64_t N, int64_t K,
+                                    const void *A, int64_t lda,
+                                    const void *Bt, int64_t ldbt,
+                                    void *C, int64_t ldc,
+                                    hipStream_t stream);
+
+/* What tlg_gemm_relu_bt(_variant) would launch (host only, no GPU). */
+tlg_status tlg_plan_bt(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                       const void *Bt, int64_t ldbt, const void *C, int64_t ldc,
+                       int32_t variant, int32_t config, tlg_plan_info *out);
+
+/* One problem of a grouped call: C (M x N) = ReLU(A (M x K) . B), B being
+ * K x N (ldb >= N) or, for a transposed call, N x K (ldb >= K). */
+typedef struct {
+    int64_t M, N, K;
+    const void *A;
+    int64_t lda;
+    const void *B;
+    int64_t ldb;
+    void *C;
+    int64_t ldc;
+} tlg_gemm_desc;
+
+#define TLG_GROUP_MAX 16
+
+/* count independent problems (0 <= count <= TLG_GROUP_MAX; descs is a host
+ * array the call reads before it returns) in one launch of the direct-to-LDS
+ * tiled kernel: the work-groups of all problems share the device, so many
+ * small problems (e.g. the experts of a mixture-of-experts layer) fill it
+ * together. trans_b: 0 for K x N B matrices, 1 for N x K (transposed) ones,
+ * the same for every problem. Each problem is checked as by tlg_check_args
+ * (or its transposed form); any failure returns TLG_ERROR_INVALID_VALUE (or
+ * TLG_ERROR_NOT_SUPPORTED for offsets beyond 2 GB) and enqueues nothing.
+ * Problems with M or N = 0 are skipped, K = 0 writes +0. The C windows must
+ * not overlap each other or any A or B. count = 0 is a no-op. */
+tlg_status tlg_gemm_relu_grouped(tlg_handle h, int32_t count, const tlg_gemm_desc *descs, int32_t trans_b,
+                                 hipStream_t stream);
+
+/* tlg_gemm_relu_grouped with a forced tile configuration (-1: library's choice). */
+tlg_status tlg_gemm_relu_grouped_variant(tlg_handle h, int32_t config, int32_t count, const tlg_gemm_desc *descs,
+                                         int32_t trans_b, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

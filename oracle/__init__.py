@@ -86,6 +86,8 @@ def _bits(x: np.ndarray) -> np.ndarray:
 def _check_2d(x: np.ndarray, name: str) -> int:
     if x.ndim != 2:
         raise ValueError(f"{name} must be 2-D")
+    if x.size == 0:
+        return max(1, x.shape[1])  # nothing is read; an empty array's strides carry no layout
     if x.strides[1] != 2 or (x.shape[0] > 1 and x.strides[0] % 2):
         raise ValueError(f"{name} must be row-major with unit column stride")
     return x.strides[0] // 2 if x.shape[0] > 1 else max(1, x.shape[1])
@@ -172,3 +174,17 @@ def gemm_relu_elems(A: np.ndarray, B: np.ndarray, ii, jj) -> np.ndarray:
     _load().oracle_gemm_relu_f16_elems(K, A.ctypes.data, lda, B.ctypes.data, ldb, ii.size,
                                        ii.ctypes.data, jj.ctypes.data, out.ctypes.data)
     return out
+
+
+def gemm_relu_bt(A: np.ndarray, Bt: np.ndarray, threads: int | None = None) -> np.ndarray:
+    """C = ReLU(A . Bt^T) for B given transposed (Bt is N x K): the same
+    definition, with B read as Bt^T. The transpose is a copy of the bit
+    patterns (no arithmetic); the sums are those of ``gemm_relu``."""
+    Bt = np.asarray(Bt)
+    return gemm_relu(A, np.ascontiguousarray(Bt.T), threads)
+
+
+def gemm_relu_grouped(problems, trans_b: bool = False, threads: int | None = None) -> list:
+    """Each problem (A, B) of a grouped call on its own: a list of C bit arrays."""
+    f = gemm_relu_bt if trans_b else gemm_relu
+    return [f(A, B, threads) for A, B in problems]

@@ -76,6 +76,7 @@ struct Problem {
     float *W;  // split mode: partials (splits x M x N)
     int k_split;
     int splits;
+    bool bt = false;  // B given transposed: N x K row-major
 };
 
 // slot of a 16-byte access in a 256-byte bank window (64 banks x 4 bytes)
@@ -100,7 +101,7 @@ void run_dma(const Problem &p, bool split, Errs &er, std::vector<int> &cover) {
             const int kbeg = split ? y * p.k_split : 0;
             // the tiled kernels' loads stop at kmain (K, or the largest multiple
             // of 8 below K when K or N is not a multiple of 8)
-            const int kmain = (p.K % 8 == 0 && p.N % 8 == 0) ? p.K : 8 * ((p.K - 1) / 8);
+            const int kmain = (p.K % 8 == 0 && (p.bt || p.N % 8 == 0)) ? p.K : 8 * ((p.K - 1) / 8);
             const int kend = split ? std::min(p.K, kbeg + p.k_split) : kmain;
             const int nk = kend > kbeg ? (kend - kbeg + S::BK - 1) / S::BK : 0;
             // accumulators: [wave][tn][tm][lane][16]
@@ -112,7 +113,28 @@ void run_dma(const Problem &p, bool split, Errs &er, std::vector<int> &cover) {
                     for (int s = 0; s < nsteps; ++s) {
                         // bf[tn][lane][8], af[tm][lane][8]
                         std::vector<float> bf((size_t)S::TN * 64 * 8), af((size_t)S::TM * 64 * 8);
-                        for (int tn = 0; tn < S::TN; ++tn)
+                        if (p.bt) {  // B tile held like A: A-style reads from the B region
+                            for (int tn = 0; tn < S::TN; ++tn) {
+                                int addr[64];
+                                for (int l = 0; l < 64; ++l) {
+                                    addr[l] = frag_a_offset<S>(wn0, tn, s, l);
+                                    if (addr[l] < 0 || addr[l] + 16 > S::B_BYTES || addr[l] % 16) er.lds_oob++;
+                                }
+                                for (int q = 0; q < 4; ++q) {
+                                    int used[16] = {0};
+                                    for (int l = 16 * q; l < 16 * q + 16; ++l)
+                                        if (used[slot16(addr[l])]++) er.bank_conflict++;
+                                }
+                                for (int l = 0; l < 64; ++l)
+                                    for (int e = 0; e < 8; ++e) {
+                                        uint16_t v = 0;
+                                        if (addr[l] >= 0 && addr[l] + 16 <= S::B_BYTES)
+                                            memcpy(&v, &lds[S::A_BYTES + addr[l] + 2 * e], 2);
+                                        bf[((size_t)tn * 64 + l) * 8 + e] = h2f(v);
+                                    }
+                            }
+                        }
+                        for (int tn = 0; tn < (p.bt ? 0 : S::TN); ++tn)
                             for (int h = 0; h < 2; ++h) {
                                 int addr[64];
                                 for (int l = 0; l < 64; ++l) {
@@ -199,7 +221,25 @@ void run_dma(const Problem &p, bool split, Errs &er, std::vector<int> &cover) {
                                 memcpy(&lds[dst + 2 * e], &v, 2);
                             }
                         }
-                        for (int i = 0; i < S::DMA_B; ++i) {
+                        for (int i = 0; i < S::DMA_B && p.bt; ++i) {  // rows n of the transposed B
+                            ChunkRef c = dma_a_chunk<S>(w, i, lane);
+                            int dst = S::A_BYTES + (w * S::DMA_B + i) * 1024 + lane * 16;
+                            bool ok = n0 + c.row < p.N && k0 + 8 * c.chunk < kend;
+                            for (int b = 0; b < 16; ++b) {
+                                if (dst + b >= S::STAGE_BYTES) { er.lds_oob++; continue; }
+                                if (lds_w[dst + b]++) er.lds_multi++;
+                            }
+                            for (int e = 0; e < 8; ++e) {
+                                uint16_t v = 0;
+                                if (ok) {
+                                    long row = n0 + c.row, col = k0 + 8 * c.chunk + e;
+                                    if (row >= p.N || col >= p.K || col >= p.ldb) er.oob_global++;
+                                    else v = p.B[row * p.ldb + col];
+                                }
+                                memcpy(&lds[dst + 2 * e], &v, 2);
+                            }
+                        }
+                        for (int i = 0; i < S::DMA_B && !p.bt; ++i) {
                             ChunkRef c = dma_b_chunk<S>(w, i, lane);
                             int dst = S::A_BYTES + (w * S::DMA_B + i) * 1024 + lane * 16;
                             bool ok = n0 + 8 * c.chunk < p.N && k0 + c.row < kend;
@@ -238,7 +278,14 @@ void run_dma(const Problem &p, bool split, Errs &er, std::vector<int> &cover) {
                             uint16_t v = (m < p.M && k < p.K) ? p.A[m * p.lda + k] : 0;
                             memcpy(&lds[lds_a_offset<S>(row, chunk) + 2 * e], &v, 2);
                         }
-                for (int row = 0; row < 16; ++row)
+                for (int row = 0; row < S::BN && p.bt; ++row)  // transposed B: rows n, like A
+                    for (int chunk = 0; chunk < 2; ++chunk)
+                        for (int e = 0; e < 8; ++e) {
+                            long n = n0 + row, k = kmain + 8 * chunk + e;
+                            uint16_t v = (n < p.N && k < p.K) ? p.B[n * p.ldb + k] : 0;
+                            memcpy(&lds[S::A_BYTES + lds_a_offset<S>(row, chunk) + 2 * e], &v, 2);
+                        }
+                for (int row = 0; row < (p.bt ? 0 : 16); ++row)
                     for (int chunk = 0; chunk < S::CB; ++chunk)
                         for (int e = 0; e < 8; ++e) {
                             long k = kmain + row, n = n0 + 8 * chunk + e;
@@ -322,6 +369,22 @@ extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A,
         case 5: return emulate<E256w8x32>(p, false, errs);
         case 10: return emulate<ES128>(p, true, errs);
         case 11: return emulate<ES256>(p, true, errs);
+        default: return -1;
+    }
+}
+
+// Transposed B (Bt is N x K row-major): direct-to-LDS configurations 0..2 and
+// the stage layouts of the pipelined kernel (3, 4).
+extern "C" int emu_gemm_relu_bt(int config, int M, int N, int K, const uint16_t *A, long lda, const uint16_t *Bt,
+                                long ldbt, uint16_t *C, long ldc, long *errs) {
+    Problem p{M, N, K, A, lda, Bt, ldbt, C, ldc, nullptr, 0, 1};
+    p.bt = true;
+    switch (config) {
+        case 0: return emulate<E256>(p, false, errs);
+        case 1: return emulate<E128>(p, false, errs);
+        case 2: return emulate<E64>(p, false, errs);
+        case 3: return emulate<EP64>(p, false, errs);    // pipelined, four waves
+        case 4: return emulate<E256w8>(p, false, errs);  // pipelined, eight waves
         default: return -1;
     }
 }

@@ -41,6 +41,8 @@ def emu(tmp_path_factory):
     L.emu_check_streamk.argtypes = [l, i, i]
     L.emu_check_streamk.restype = l
     L.emu_check_epilogue.argtypes = [i]
+    L.emu_gemm_relu_bt.argtypes = [i, i, i, i, p, l, p, l, p, l, p]
+    L.emu_gemm_relu_bt.restype = i
     L.emu_check_epilogue.restype = l
     return L
 
@@ -80,6 +82,25 @@ def test_lds_epilogue_index_math(emu, config):
 
 # shapes that satisfy the direct-to-LDS conditions (K % 8 == 0, N % 8 == 0), several tiles, ragged tails
 SHAPES = [(64, 64, 64), (200, 136, 88), (257, 264, 520), (70, 512, 40), (1, 8, 8), (300, 40, 16)]
+
+
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("shape", SHAPES + [(301, 259, 203), (65, 70, 9), (130, 129, 1)])
+def test_transposed_b_tiles_match_oracle_integer(emu, config, shape):
+    """B given transposed (N x K): its tile is loaded and read like A's; the
+    ragged K tail is staged the same way. Any K and N work."""
+    M, N, K = shape
+    A, B = wl.make_random(M, N, K, seed=M + 3 * N + K, kind="integer_pos" if K > 100 else "integer")
+    Bt = np.ascontiguousarray(B.T)
+    C = np.full((M, N), 0xFFFF, np.uint16)
+    errs = np.zeros(8, np.int64)
+    A16, Bt16 = np.ascontiguousarray(A.view(np.uint16)), Bt.view(np.uint16)
+    rc = emu.emu_gemm_relu_bt(config, M, N, K, A16.ctypes.data, K, Bt16.ctypes.data, K, C.ctypes.data, N,
+                              errs.ctypes.data)
+    assert rc == 0
+    errs = dict(zip(ERR_NAMES, errs.tolist()))
+    assert all(v == 0 for v in errs.values()), errs
+    assert np.array_equal(C, oracle.gemm_relu(A, B))
 
 
 @pytest.mark.parametrize("config", sorted(DMA_CONFIGS))

@@ -17,7 +17,7 @@ from ._native import (  # noqa: F401  (re-exported C-ABI names)
     tlg_version, tlg_workspace_bytes,
 )
 
-__all__ = ["gemm_relu", "Handle", "handle_for", "plan"]
+__all__ = ["gemm_relu", "gemm_relu_grouped", "Handle", "handle_for", "plan"]
 
 
 class Handle:
@@ -59,7 +59,7 @@ def handle_for(device) -> Handle:
 def _ld(t) -> int:
     """Leading dimension (elements) of a row-major 2-D tensor."""
     rows, cols = t.shape
-    if rows <= 1:
+    if rows <= 1 or t.numel() == 0:
         return max(1, cols)
     return t.stride(0)
 
@@ -73,61 +73,115 @@ def _check(t, name):
         raise ValueError(f"{name} must be 2-D")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU")
+    if t.numel() == 0:
+        return  # no element is read or written; an empty tensor's strides carry no layout
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit stride along its rows (row-major)")
     if t.shape[0] > 1 and t.stride(0) < max(1, t.shape[1]):
         raise ValueError(f"{name} rows overlap")
 
 
-def gemm_relu(A, B, out=None, *, variant: int = TLG_VARIANT_AUTO, config: int = -1, splits: int = 0, stream=None,
-              handle=None):
+def _out_for(out, M, N, device):
+    import torch
+
+    if out is None:
+        return torch.empty((M, N), dtype=torch.float16, device=device)
+    _check(out, "out")
+    if tuple(out.shape) != (M, N) or out.device != device:
+        raise ValueError("out has the wrong shape or device")
+    return out
+
+
+def gemm_relu(A, B, out=None, *, trans_b: bool = False, variant: int = TLG_VARIANT_AUTO, config: int = -1,
+              splits: int = 0, stream=None, handle=None):
     """C = ReLU(A @ B) for fp16 row-major A (M, K) and B (K, N); returns C (M, N).
 
-    ``out`` may be a preallocated fp16 (M, N) tensor (a padded row view is
-    fine: only its M x N window is written). The work is enqueued on
-    ``stream`` (default: the current stream of A's device) and is
+    With ``trans_b`` B is given transposed, as an (N, K) row-major tensor, and
+    C = ReLU(A @ B.T). ``out`` may be a preallocated fp16 (M, N) tensor (a
+    padded row view is fine: only its M x N window is written). The work is
+    enqueued on ``stream`` (default: the current stream of A's device) and is
     asynchronous. ``variant``/``config``/``splits`` force a kernel family, tile
-    configuration and split count (tests and measurements).
+    configuration and split count (tests and measurements; with ``trans_b``
+    the families are the direct-to-LDS and pipelined ones, without splits).
     """
     import torch
 
     _check(A, "A")
     _check(B, "B")
     M, K = A.shape
-    K2, N = B.shape
+    if trans_b:
+        N, K2 = B.shape
+    else:
+        K2, N = B.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
     if A.device != B.device:
         raise ValueError("A and B are on different devices")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
-    else:
-        _check(out, "out")
-        if tuple(out.shape) != (M, N) or out.device != A.device:
-            raise ValueError("out has the wrong shape or device")
+    out = _out_for(out, M, N, A.device)
     h = handle if handle is not None else handle_for(A.device)
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     with torch.cuda.device(A.device):
-        st = _native.tlg_gemm_relu_variant(h.ptr, variant, config, splits, M, N, K, A.data_ptr(), _ld(A),
-                                           B.data_ptr(), _ld(B), out.data_ptr(), _ld(out), s.cuda_stream)
+        if trans_b:
+            st = _native.tlg_gemm_relu_bt_variant(h.ptr, variant, config, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(),
+                                                  _ld(B), out.data_ptr(), _ld(out), s.cuda_stream)
+        else:
+            st = _native.tlg_gemm_relu_variant(h.ptr, variant, config, splits, M, N, K, A.data_ptr(), _ld(A),
+                                               B.data_ptr(), _ld(B), out.data_ptr(), _ld(out), s.cuda_stream)
     if st != _native.TLG_SUCCESS:
-        raise TlgError(st, "tlg_gemm_relu")
+        raise TlgError(st, "tlg_gemm_relu_bt" if trans_b else "tlg_gemm_relu")
     return out
 
 
+def gemm_relu_grouped(As, Bs, outs=None, *, trans_b: bool = False, config: int = -1, stream=None, handle=None):
+    """C_i = ReLU(A_i @ B_i) (or A_i @ B_i.T with ``trans_b``) for up to 16
+    problems in one launch; returns the list of C_i."""
+    import torch
+
+    if len(As) != len(Bs) or (outs is not None and len(outs) != len(As)):
+        raise ValueError("As, Bs and outs differ in length")
+    if len(As) > _native.TLG_GROUP_MAX:
+        raise ValueError(f"at most {_native.TLG_GROUP_MAX} problems per call")
+    if not As:
+        return []
+    dev = As[0].device
+    descs, res = [], []
+    for i, (A, B) in enumerate(zip(As, Bs)):
+        _check(A, "A")
+        _check(B, "B")
+        if A.device != dev or B.device != dev:
+            raise ValueError("all operands must be on one device")
+        M, K = A.shape
+        N, K2 = B.shape if trans_b else (B.shape[1], B.shape[0])
+        if K != K2:
+            raise ValueError(f"problem {i}: inner dimensions differ: {K} vs {K2}")
+        C = _out_for(None if outs is None else outs[i], M, N, dev)
+        res.append(C)
+        descs.append((M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), C.data_ptr(), _ld(C)))
+    h = handle if handle is not None else handle_for(dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = _native.tlg_gemm_relu_grouped_variant(h.ptr, config, descs, 1 if trans_b else 0, s.cuda_stream)
+    if st != _native.TLG_SUCCESS:
+        raise TlgError(st, "tlg_gemm_relu_grouped")
+    return res
+
+
 def plan(M, N, K, lda=None, ldb=None, ldc=None, *, aligned: bool = True, variant: int = TLG_VARIANT_AUTO,
-         config: int = -1, splits: int = 0) -> dict:
+         config: int = -1, splits: int = 0, trans_b: bool = False) -> dict:
     """What gemm_relu would launch for a problem (host logic only, no GPU).
 
     Pointers are stand-ins: 16-byte aligned when ``aligned`` else 2-byte aligned.
     """
     lda = max(1, K) if lda is None else lda
-    ldb = max(1, N) if ldb is None else ldb
+    ldb = (max(1, K) if trans_b else max(1, N)) if ldb is None else ldb
     ldc = max(1, N) if ldc is None else ldc
     base = 1 << 20 if aligned else (1 << 20) + 2
-    st, info = _native.tlg_plan(M, N, K, base, lda, base, ldb, base, ldc, variant, config, splits)
+    if trans_b:
+        st, info = _native.tlg_plan_bt(M, N, K, base, lda, base, ldb, base, ldc, variant, config)
+    else:
+        st, info = _native.tlg_plan(M, N, K, base, lda, base, ldb, base, ldc, variant, config, splits)
     if st != _native.TLG_SUCCESS:
-        raise TlgError(st, "tlg_plan")
+        raise TlgError(st, "tlg_plan_bt" if trans_b else "tlg_plan")
     d = info.as_dict()
     d["variant_name"] = _native.VARIANT_NAMES.get(info.variant, "?")
     d["config_name"] = _native.tlg_plan_config_name(info.variant, info.config)

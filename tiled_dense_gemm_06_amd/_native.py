@@ -45,6 +45,18 @@ class tlg_plan_info(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+TLG_GROUP_MAX = 16
+
+
+class tlg_gemm_desc(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("A", ctypes.c_void_p), ("lda", ctypes.c_int64),
+        ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64),
+        ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64),
+    ]
+
+
 class TlgError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -86,6 +98,16 @@ def lib():
         L.tlg_status_string.restype = ctypes.c_char_p
         L.tlg_version.argtypes = []
         L.tlg_version.restype = i32
+        L.tlg_gemm_relu_bt.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p]
+        L.tlg_gemm_relu_bt.restype = i32
+        L.tlg_gemm_relu_bt_variant.argtypes = [p, i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, p]
+        L.tlg_gemm_relu_bt_variant.restype = i32
+        L.tlg_plan_bt.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i32, i32, ctypes.POINTER(tlg_plan_info)]
+        L.tlg_plan_bt.restype = i32
+        L.tlg_gemm_relu_grouped.argtypes = [p, i32, ctypes.POINTER(tlg_gemm_desc), i32, p]
+        L.tlg_gemm_relu_grouped.restype = i32
+        L.tlg_gemm_relu_grouped_variant.argtypes = [p, i32, i32, ctypes.POINTER(tlg_gemm_desc), i32, p]
+        L.tlg_gemm_relu_grouped_variant.restype = i32
         _lib = L
     return _lib
 
@@ -108,6 +130,37 @@ def tlg_gemm_relu(h, M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
 
 def tlg_gemm_relu_variant(h, variant, config, splits, M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
     return lib().tlg_gemm_relu_variant(h, variant, config, splits, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def tlg_gemm_relu_bt(h, M, N, K, A, lda, Bt, ldbt, C, ldc, stream) -> int:
+    return lib().tlg_gemm_relu_bt(h, M, N, K, A, lda, Bt, ldbt, C, ldc, stream)
+
+
+def tlg_gemm_relu_bt_variant(h, variant, config, M, N, K, A, lda, Bt, ldbt, C, ldc, stream) -> int:
+    return lib().tlg_gemm_relu_bt_variant(h, variant, config, M, N, K, A, lda, Bt, ldbt, C, ldc, stream)
+
+
+def tlg_plan_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, variant=TLG_VARIANT_AUTO, config=-1):
+    """Returns (status, tlg_plan_info)."""
+    info = tlg_plan_info()
+    st = lib().tlg_plan_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, variant, config, ctypes.byref(info))
+    return st, info
+
+
+def _descs(descs):
+    arr = (tlg_gemm_desc * max(1, len(descs)))()
+    for i, d in enumerate(descs):
+        arr[i] = tlg_gemm_desc(*d)
+    return arr
+
+
+def tlg_gemm_relu_grouped(h, descs, trans_b, stream) -> int:
+    """descs: sequence of (M, N, K, A, lda, B, ldb, C, ldc) tuples."""
+    return lib().tlg_gemm_relu_grouped(h, len(descs), _descs(descs), trans_b, stream)
+
+
+def tlg_gemm_relu_grouped_variant(h, config, descs, trans_b, stream) -> int:
+    return lib().tlg_gemm_relu_grouped_variant(h, config, len(descs), _descs(descs), trans_b, stream)
 
 
 def tlg_check_args(M, N, K, A, lda, B, ldb, C, ldc) -> int:

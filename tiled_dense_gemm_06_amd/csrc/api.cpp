@@ -292,6 +292,136 @@ tlg_status run(tlg_handle h, int32_t variant, int32_t config, int32_t splits, co
     return e == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
 }
 
+// ---- transposed B and grouped calls ----
+
+tlg_status check_args_bt(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *Bt, int64_t ldbt,
+                         const void *C, int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0) return TLG_ERROR_INVALID_VALUE;
+    if (lda < (K > 1 ? K : 1) || ldbt < (K > 1 ? K : 1) || ldc < (N > 1 ? N : 1)) return TLG_ERROR_INVALID_VALUE;
+    if (M == 0 || N == 0) return TLG_SUCCESS;
+    if (!C || !aligned(C, 2)) return TLG_ERROR_INVALID_VALUE;
+    if (K > 0) {
+        if (!A || !Bt || !aligned(A, 2) || !aligned(Bt, 2)) return TLG_ERROR_INVALID_VALUE;
+    }
+    return TLG_SUCCESS;
+}
+
+// In-tile byte offsets with a transposed B (its tile is bn rows of ldb).
+bool offsets_ok_bt(const tlg::Problem &p, int bm, int bn) {
+    if ((int64_t)bm * p.lda * 2 > kMaxOffset) return false;
+    if ((int64_t)bn * p.ldb * 2 > kMaxOffset) return false;
+    if ((int64_t)bm * p.ldc * 2 + (int64_t)bn * 2 > kMaxOffset) return false;
+    return true;
+}
+
+// Direct-to-LDS configuration by tile count (the transposed-B and grouped
+// calls use the square configurations 0..2 only).
+int dma_config_by_tiles(int64_t t256, int64_t t128) {
+    if (t256 >= 224) return tlg::DMA_256x256x32;
+    if (t128 >= 192) return tlg::DMA_128x128x32;
+    return tlg::DMA_64x64x64;
+}
+constexpr int kSquareDmaConfigs = 3;
+
+tlg_status plan_bt(const tlg::Problem &p, int32_t variant, int32_t config, tlg_plan_info *o) {
+    if (variant != TLG_VARIANT_AUTO && variant != TLG_VARIANT_TILED_DMA && variant != TLG_VARIANT_TILED_PIPE)
+        return TLG_ERROR_INVALID_VALUE;
+    if (variant == TLG_VARIANT_AUTO && config != -1) return TLG_ERROR_INVALID_VALUE;
+    if (variant == TLG_VARIANT_TILED_DMA && (config < -1 || config >= kSquareDmaConfigs))
+        return TLG_ERROR_INVALID_VALUE;
+    if (variant == TLG_VARIANT_TILED_PIPE && config != -1 && config != tlg::PIPE_256x256x64_A3 &&
+        config != tlg::PIPE_256x256x64_W8_A3)
+        return TLG_ERROR_INVALID_VALUE;
+    if (p.M == 0 || p.N == 0) {
+        fill_info(o, TLG_VARIANT_NOOP, 0, nullptr, 1, 0, 0, 0);
+        return TLG_SUCCESS;
+    }
+    if (p.K == 0) {
+        fill_info(o, TLG_VARIANT_FILL_ZERO, 0, nullptr, 1, 1, ceil_div(p.M * p.N, 256 * 8), 0);
+        return TLG_SUCCESS;
+    }
+    const int64_t t256 = ceil_div(p.M, 256) * ceil_div(p.N, 256);
+    if (variant == TLG_VARIANT_TILED_PIPE || (variant == TLG_VARIANT_AUTO && t256 >= 224)) {
+        const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64_W8_A3;
+        const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
+        if (offsets_ok_bt(p, tc.bm, tc.bn)) {
+            fill_info(o, TLG_VARIANT_TILED_PIPE, cfg, &tc, 1, 1, t256, 0);
+            return TLG_SUCCESS;
+        }
+        if (variant == TLG_VARIANT_TILED_PIPE) return TLG_ERROR_NOT_SUPPORTED;
+    }
+    const int cfg = config >= 0 && variant == TLG_VARIANT_TILED_DMA
+                        ? config
+                        : dma_config_by_tiles(t256, ceil_div(p.M, 128) * ceil_div(p.N, 128));
+    const tlg::TileConfig &tc = tlg::kDmaConfigs[cfg];
+    if (!offsets_ok_bt(p, tc.bm, tc.bn)) return TLG_ERROR_NOT_SUPPORTED;
+    fill_info(o, TLG_VARIANT_TILED_DMA, cfg, &tc, 1, 1, ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn), 0);
+    return TLG_SUCCESS;
+}
+
+tlg_status device_ok(tlg_handle h) {
+    if (!h) return TLG_ERROR_INVALID_VALUE;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return TLG_ERROR_HIP;
+    return dev == h->device ? TLG_SUCCESS : TLG_ERROR_INVALID_VALUE;
+}
+
+tlg_status run_bt(tlg_handle h, int32_t variant, int32_t config, tlg::Problem p, hipStream_t stream) {
+    tlg_status st = device_ok(h);
+    if (st != TLG_SUCCESS) return st;
+    st = check_args_bt(p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc);
+    if (st != TLG_SUCCESS) return st;
+    p.trans_b = true;
+    tlg_plan_info info;
+    st = plan_bt(p, variant, config, &info);
+    if (st != TLG_SUCCESS) return st;
+    hipError_t e = hipSuccess;
+    switch (info.variant) {
+        case TLG_VARIANT_NOOP: return TLG_SUCCESS;
+        case TLG_VARIANT_FILL_ZERO: e = tlg::launch_fill_zero(p, stream); break;
+        case TLG_VARIANT_TILED_DMA: e = tlg::launch_tiled_dma(info.config, p, stream); break;
+        case TLG_VARIANT_TILED_PIPE: e = tlg::launch_tiled_pipe(info.config, p, stream); break;
+        default: return TLG_ERROR_NOT_SUPPORTED;
+    }
+    return e == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
+}
+
+tlg_status run_grouped(tlg_handle h, int32_t config, int32_t count, const tlg_gemm_desc *descs, int32_t trans_b,
+                       hipStream_t stream) {
+    tlg_status st = device_ok(h);
+    if (st != TLG_SUCCESS) return st;
+    if (count < 0 || count > TLG_GROUP_MAX || (trans_b != 0 && trans_b != 1)) return TLG_ERROR_INVALID_VALUE;
+    if (config < -1 || config >= kSquareDmaConfigs) return TLG_ERROR_INVALID_VALUE;
+    if (count == 0) return TLG_SUCCESS;
+    if (!descs) return TLG_ERROR_INVALID_VALUE;
+    tlg::Problem ps[TLG_GROUP_MAX];
+    int n = 0;
+    int64_t t256 = 0, t128 = 0;
+    for (int i = 0; i < count; ++i) {
+        const tlg_gemm_desc &d = descs[i];
+        st = trans_b ? check_args_bt(d.M, d.N, d.K, d.A, d.lda, d.B, d.ldb, d.C, d.ldc)
+                     : tlg_check_args(d.M, d.N, d.K, d.A, d.lda, d.B, d.ldb, d.C, d.ldc);
+        if (st != TLG_SUCCESS) return st;
+        if (d.M == 0 || d.N == 0) continue;
+        tlg::Problem p = make_problem(d.M, d.N, d.K, d.A, d.lda, d.B, d.ldb, d.C, d.ldc);
+        p.trans_b = trans_b != 0;
+        ps[n++] = p;
+        t256 += ceil_div(d.M, 256) * ceil_div(d.N, 256);
+        t128 += ceil_div(d.M, 128) * ceil_div(d.N, 128);
+    }
+    if (n == 0) return TLG_SUCCESS;
+    const int cfg = config >= 0 ? config : dma_config_by_tiles(t256, t128);
+    const tlg::TileConfig &tc = tlg::kDmaConfigs[cfg];
+    int64_t tiles = 0;
+    for (int i = 0; i < n; ++i) {
+        const bool ok = trans_b ? offsets_ok_bt(ps[i], tc.bm, tc.bn) : dma_ok(ps[i], tc.bm, tc.bn, tc.bk);
+        if (!ok) return TLG_ERROR_NOT_SUPPORTED;
+        tiles += ceil_div(ps[i].M, tc.bm) * ceil_div(ps[i].N, tc.bn);
+    }
+    if (tiles > 0x7fffffff) return TLG_ERROR_NOT_SUPPORTED;
+    return tlg::launch_tiled_dma_grouped(cfg, ps, n, stream) == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -408,5 +538,36 @@ const char *tlg_status_string(tlg_status s) {
 }
 
 int32_t tlg_version(void) { return kVersion; }
+
+tlg_status tlg_gemm_relu_bt(tlg_handle h, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *Bt,
+                            int64_t ldbt, void *C, int64_t ldc, hipStream_t stream) {
+    return run_bt(h, TLG_VARIANT_AUTO, -1, make_problem(M, N, K, A, lda, Bt, ldbt, C, ldc), stream);
+}
+
+tlg_status tlg_gemm_relu_bt_variant(tlg_handle h, int32_t variant, int32_t config, int64_t M, int64_t N, int64_t K,
+                                    const void *A, int64_t lda, const void *Bt, int64_t ldbt, void *C, int64_t ldc,
+                                    hipStream_t stream) {
+    return run_bt(h, variant, config, make_problem(M, N, K, A, lda, Bt, ldbt, C, ldc), stream);
+}
+
+tlg_status tlg_plan_bt(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *Bt, int64_t ldbt,
+                       const void *C, int64_t ldc, int32_t variant, int32_t config, tlg_plan_info *out) {
+    if (!out) return TLG_ERROR_INVALID_VALUE;
+    tlg_status st = check_args_bt(M, N, K, A, lda, Bt, ldbt, C, ldc);
+    if (st != TLG_SUCCESS) return st;
+    tlg::Problem p = make_problem(M, N, K, A, lda, Bt, ldbt, C, ldc);
+    p.trans_b = true;
+    return plan_bt(p, variant, config, out);
+}
+
+tlg_status tlg_gemm_relu_grouped(tlg_handle h, int32_t count, const tlg_gemm_desc *descs, int32_t trans_b,
+                                 hipStream_t stream) {
+    return run_grouped(h, -1, count, descs, trans_b, stream);
+}
+
+tlg_status tlg_gemm_relu_grouped_variant(tlg_handle h, int32_t config, int32_t count, const tlg_gemm_desc *descs,
+                                         int32_t trans_b, hipStream_t stream) {
+    return run_grouped(h, config, count, descs, trans_b, stream);
+}
 
 }  // extern "C"

@@ -36,27 +36,24 @@ namespace tlg {
 
 // ---------------------------------------------------------------------------
 // Tiled kernel fed by direct global->LDS loads. Requirements (checked on the
-// host): A, B, C (and W) 16-byte aligned; lda, ldb, ldc, K and N multiples of
-// 8; every in-tile byte offset below kRange. With SPLIT, blockIdx.y is the
-// K split and fp32 partials go to W instead of C.
+// host): every in-tile byte offset below kRange (2-byte aligned pointers and
+// any leading dimension work; ragged K or N take the staged tail block).
+// With SPLIT, blockIdx.y is the K split and fp32 partials go to W instead of
+// C. BT: B is given transposed (N x K row-major, ldb >= K), its tile is
+// loaded and read exactly like A's (BM == BN).
 // ---------------------------------------------------------------------------
-template <class S, bool SPLIT>
-__global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[S::LDS_BYTES];
+template <class S, bool SPLIT, bool BT>
+__device__ __forceinline__ void tile_dma(const KArgs &a, int m0, int n0, int kbeg, int kend, LDS_PTR(char) lds) {
+    static_assert(!BT || (S::BM == S::BN && !SPLIT), "transposed B: square tiles, no split");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
-
-    const int nwg = a.tiles_m * a.tiles_n;
-    int tm_idx, tn_idx;
-    grouped_tile(xcd_remap(blockIdx.x, nwg), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
-    const int m0 = tm_idx * S::BM, n0 = tn_idx * S::BN;
-    const int kbeg = SPLIT ? (int)blockIdx.y * a.k_split : 0;
-    const int kend = SPLIT ? imin(a.K, kbeg + a.k_split) : a.kmain;
     const int nk = kend > kbeg ? (kend - kbeg + S::BK - 1) / S::BK : 0;
 
-    // Per-lane load descriptors (constant over the K loop).
+    // Per-lane load descriptors (constant over the K loop): byte offset in
+    // the stage's window, the k offset that decides whether the chunk is
+    // inside K, and whether the row (or column) is inside M (N).
     uint32_t a_off[S::DMA_A];
     int a_col[S::DMA_A];
     bool a_ok[S::DMA_A];
@@ -68,24 +65,29 @@ __global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
         a_ok[i] = m0 + c.row < a.M;
     }
     uint32_t b_off[S::DMA_B];
-    int b_row[S::DMA_B];
+    int b_k[S::DMA_B];
     bool b_ok[S::DMA_B];
 #pragma unroll
     for (int i = 0; i < S::DMA_B; ++i) {
-        ChunkRef c = dma_b_chunk<S>(wave, i, lane);
-        b_off[i] = (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16);
-        b_row[i] = c.row;
-        b_ok[i] = n0 + 8 * c.chunk < a.N;
+        if (BT) {  // rows n of the transposed B tile, as A's rows m
+            ChunkRef c = dma_a_chunk<S>(wave, i, lane);
+            b_off[i] = (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16);
+            b_k[i] = 8 * c.chunk;
+            b_ok[i] = n0 + c.row < a.N;
+        } else {
+            ChunkRef c = dma_b_chunk<S>(wave, i, lane);
+            b_off[i] = (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16);
+            b_k[i] = c.row;
+            b_ok[i] = n0 + 8 * c.chunk < a.N;
+        }
     }
-
-    LDS_PTR(char) lds = (LDS_PTR(char))smem;
 
     auto issue = [&](int kt, int buf) {
         const int k0 = kbeg + kt * S::BK;
         LDS_PTR(char) sA = lds + buf * S::STAGE_BYTES;
         LDS_PTR(char) sB = sA + S::A_BYTES;
         const int4_t ra = make_srd(a.A + (int64_t)m0 * a.lda + k0);
-        const int4_t rb = make_srd(a.B + (int64_t)k0 * a.ldb + n0);
+        const int4_t rb = make_srd(BT ? a.B + (int64_t)n0 * a.ldb + k0 : a.B + (int64_t)k0 * a.ldb + n0);
         const uint32_t la = (uint32_t)(uintptr_t)(sA + wave * S::DMA_A * 1024);
         const uint32_t lb = (uint32_t)(uintptr_t)(sB + wave * S::DMA_B * 1024);
 #pragma unroll
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < S::DMA_B; ++i) {
-            uint32_t off = (b_ok[i] && k0 + b_row[i] < kend) ? b_off[i] : kOOB;
+            uint32_t off = (b_ok[i] && k0 + b_k[i] < kend) ? b_off[i] : kOOB;
             dma16(rb, lb + i * 1024, off);
         }
     };
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
             issue(kt + S::STAGES - 1, nb);
         }
         LDS_PTR(const char) sA = lds + buf * S::STAGE_BYTES;
-        mma_stage<S>(sA, sA + S::A_BYTES, wm0, wn0, lane, acc);
+        mma_stage<S, BT>(sA, sA + S::A_BYTES, wm0, wn0, lane, acc);
         buf = buf + 1 == S::STAGES ? 0 : buf + 1;
     }
 
@@ -135,9 +137,9 @@ __global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
     // by element into buffer 0 once every wave is done with the stages.
     if (!SPLIT && a.kmain < a.K) {
         barrier_lds();
-        stage_tail<S>(a, m0, n0, lds, lds + S::A_BYTES, tid);
+        stage_tail<S, BT>(a, m0, n0, lds, lds + S::A_BYTES, tid);
         barrier_lds();
-        mma_kstep<S>(lds, lds + S::A_BYTES, 0, wm0, wn0, lane, acc);
+        mma_kstep<S, BT>(lds, lds + S::A_BYTES, 0, wm0, wn0, lane, acc);
     }
 
     // Epilogue: split-K partials go out as fp32 (a lane owns four consecutive
@@ -164,6 +166,32 @@ __global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
         barrier_lds();  // every wave is done with the stages (and the tail block)
         store_c_tile_lds<S>(a, m0, n0, wave, lane, acc, lds);
     }
+}
+
+template <class S, bool SPLIT, bool BT>
+__global__ __launch_bounds__(S::NT) void k_tiled_dma(const KArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[S::LDS_BYTES];
+    const int nwg = a.tiles_m * a.tiles_n;
+    int tm_idx, tn_idx;
+    grouped_tile(xcd_remap(blockIdx.x, nwg), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
+    const int kbeg = SPLIT ? (int)blockIdx.y * a.k_split : 0;
+    const int kend = SPLIT ? imin(a.K, kbeg + a.k_split) : a.kmain;
+    tile_dma<S, SPLIT, BT>(a, tm_idx * S::BM, tn_idx * S::BN, kbeg, kend, (LDS_PTR(char))smem);
+}
+
+// Several independent problems in one launch: work-group ids are dealt to
+// the XCDs as in the single-problem kernel, then split by problem in order
+// (tile_start holds the running tile counts).
+template <class S, bool BT>
+__global__ __launch_bounds__(S::NT) void k_tiled_dma_grouped(const GroupArgs g) {
+    __shared__ __attribute__((aligned(1024))) char smem[S::LDS_BYTES];
+    const int v = xcd_remap(blockIdx.x, g.tile_start[g.count]);
+    int p = 0;
+    while (p + 1 < g.count && v >= g.tile_start[p + 1]) ++p;
+    const KArgs &a = g.p[p];
+    int tm_idx, tn_idx;
+    grouped_tile(v - g.tile_start[p], a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
+    tile_dma<S, false, BT>(a, tm_idx * S::BM, tn_idx * S::BN, 0, a.kmain, (LDS_PTR(char))smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -356,7 +384,7 @@ const TileConfig kSplitConfigs[SPLIT_TWO_KERNEL_CONFIGS] = {
      "splitk_32x256x64_w1x4_s3"},
 };
 
-static KArgs make_args(const Problem &p) {
+static KArgs make_args(const Problem &p, bool bt = false) {
     KArgs a;
     a.A = (const _Float16 *)p.A;
     a.B = (const _Float16 *)p.B;
@@ -370,16 +398,37 @@ static KArgs make_args(const Problem &p) {
     a.ldc = p.ldc;
     a.group_m = 4;
     a.k_split = (int)p.K;
-    a.kmain = (p.K % 8 == 0 && p.N % 8 == 0) ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
+    // direct-to-LDS loads stop at the last multiple of 8 below K when a
+    // 16-byte chunk could cross the end of a row (K-contiguous A or
+    // transposed B: K % 8; N-contiguous B: N % 8)
+    const bool whole = p.K % 8 == 0 && (bt || p.N % 8 == 0);
+    a.kmain = whole ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
     return a;
 }
 
-template <class S, bool SPLIT>
+template <class S, bool SPLIT, bool BT = false>
 static hipError_t launch_dma_t(KArgs a, int splits, hipStream_t stream) {
     a.tiles_m = (a.M + S::BM - 1) / S::BM;
     a.tiles_n = (a.N + S::BN - 1) / S::BN;
     dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits);
-    hipLaunchKernelGGL((k_tiled_dma<S, SPLIT>), grid, dim3(S::NT), 0, stream, a);
+    hipLaunchKernelGGL((k_tiled_dma<S, SPLIT, BT>), grid, dim3(S::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class S, bool BT>
+static hipError_t launch_grouped_t(const Problem *ps, int count, hipStream_t stream) {
+    GroupArgs g;
+    g.count = count;
+    g.tile_start[0] = 0;
+    for (int i = 0; i < count; ++i) {
+        KArgs a = make_args(ps[i], BT);
+        a.tiles_m = (a.M + S::BM - 1) / S::BM;
+        a.tiles_n = (a.N + S::BN - 1) / S::BN;
+        g.p[i] = a;
+        g.tile_start[i + 1] = g.tile_start[i] + a.tiles_m * a.tiles_n;
+    }
+    if (g.tile_start[count] == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_tiled_dma_grouped<S, BT>), dim3((unsigned)g.tile_start[count]), dim3(S::NT), 0, stream, g);
     return hipGetLastError();
 }
 
@@ -399,13 +448,38 @@ static hipError_t launch_gen_t(KArgs a, hipStream_t stream) {
 }
 
 hipError_t launch_tiled_dma(int config, const Problem &p, hipStream_t stream) {
-    KArgs a = make_args(p);
+    KArgs a = make_args(p, p.trans_b);
+    if (p.trans_b) {
+        switch (config) {
+            case DMA_256x256x32: return launch_dma_t<Dma256, false, true>(a, 1, stream);
+            case DMA_128x128x32: return launch_dma_t<Dma128, false, true>(a, 1, stream);
+            case DMA_64x64x64: return launch_dma_t<Dma64, false, true>(a, 1, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (config) {
         case DMA_256x256x32: return launch_dma_t<Dma256, false>(a, 1, stream);
         case DMA_128x128x32: return launch_dma_t<Dma128, false>(a, 1, stream);
         case DMA_64x64x64: return launch_dma_t<Dma64, false>(a, 1, stream);
         case DMA_256x256x64_W8: return launch_dma_t<Dma256w8, false>(a, 1, stream);
         case DMA_256x256x32_W8: return launch_dma_t<Dma256w8x32, false>(a, 1, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_tiled_dma_grouped(int config, const Problem *ps, int count, hipStream_t stream) {
+    static_assert(sizeof(GroupArgs) <= 4096, "kernel arguments");
+    if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
+    const bool bt = ps[0].trans_b;
+    for (int i = 1; i < count; ++i)
+        if (ps[i].trans_b != bt) return hipErrorInvalidValue;
+    switch (config) {
+        case DMA_256x256x32:
+            return bt ? launch_grouped_t<Dma256, true>(ps, count, stream) : launch_grouped_t<Dma256, false>(ps, count, stream);
+        case DMA_128x128x32:
+            return bt ? launch_grouped_t<Dma128, true>(ps, count, stream) : launch_grouped_t<Dma128, false>(ps, count, stream);
+        case DMA_64x64x64:
+            return bt ? launch_grouped_t<Dma64, true>(ps, count, stream) : launch_grouped_t<Dma64, false>(ps, count, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -38,13 +38,25 @@ struct Frags {
 
 // LDS reads of one k-step's fragments, numbered in the order the MFMAs use
 // them (tile i uses b[i / TM] and a[i % TM]): b[0] (two reads), a[0..TM-1],
-// then b[1..TN-1] (two reads each).
-template <class S>
-constexpr int kFragReads = S::TM + 2 * S::TN;
+// then b[1..TN-1] (two reads each). BT (B given transposed, its tile held
+// like A's): one 16-byte read per B fragment, b[0], a[0..TM-1], b[1..TN-1].
+template <class S, bool BT = false>
+constexpr int kFragReads = S::TM + (BT ? 1 : 2) * S::TN;
 
-template <class S>
+template <class S, bool BT>
 __device__ __forceinline__ void frag_read(Frags<S> &f, LDS_PTR(const char) sA, LDS_PTR(const char) sB,
                                           int wm0, int wn0, int s, int lane, int r) {
+    if (BT) {
+        if (r >= 1 && r < 1 + S::TM) {
+            f.a[r - 1] = *(LDS_PTR(const half8_t))(sA + frag_a_offset<S>(wm0, r - 1, s, lane));
+        } else {
+            const int tn = r == 0 ? 0 : r - S::TM;
+            const short8_t v = *(LDS_PTR(const short8_t))(sB + frag_a_offset<S>(wn0, tn, s, lane));
+            f.blo[tn] = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+            f.bhi[tn] = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+        }
+        return;
+    }
     if (r < 2) {
         LDS_PTR(short4_t) p = (LDS_PTR(short4_t))(sB + frag_b_offset<S>(wn0, 0, s, r, lane));
         if (r == 0)
@@ -92,12 +104,14 @@ __device__ __forceinline__ void mfma_tile(const Frags<S> &f, int i, float16_t (&
 // arrive; they are then issued after the B loads). Then this wave's loads of
 // stage kt+1 are waited for and the barrier publishes it (and retires stage
 // kt). The C tile leaves through LDS (store_c_tile_lds).
-template <class S, int SPACING, int DOFF, int ASTAGES>
+template <class S, int SPACING, int DOFF, int ASTAGES, bool BT>
 __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     constexpr int T = S::TM * S::TN;  // MFMA tiles of a wave (MFMAs per k-step)
     constexpr int H = T / 2;
     static_assert(T % 2 == 0 && S::KSTEPS % 2 == 0, "the last k-step of a stage must use f[1]");
-    static_assert(kFragReads<S> <= T && kFragReads<S> <= 2 * H, "fragment reads must fit under the MFMAs of a k-step");
+    constexpr int READS = kFragReads<S, BT>;
+    static_assert(READS <= T && READS <= 2 * H, "fragment reads must fit under the MFMAs of a k-step");
+    static_assert(!BT || S::BM == S::BN, "transposed B is held in the A layout");
     constexpr int LOADS = S::DMA_A + S::DMA_B;  // direct-to-LDS loads per wave per stage
     constexpr int AHEAD = S::STAGES - 1;        // B stages in flight beyond the one being multiplied
     constexpr int AHEAD_A = ASTAGES - 1;        // A stages likewise
@@ -139,15 +153,15 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < S::DMA_B; ++i) {
-        ChunkRef c = dma_b_chunk<S>(wave, i, lane);
+        ChunkRef c = BT ? dma_a_chunk<S>(wave, i, lane) : dma_b_chunk<S>(wave, i, lane);
         off[S::DMA_A + i] = (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16);
-        kin[S::DMA_A + i] = c.row;
-        ok[S::DMA_A + i] = n0 + 8 * c.chunk < a.N;
+        kin[S::DMA_A + i] = BT ? 8 * c.chunk : c.row;          // transposed B: rows n, chunks along K
+        ok[S::DMA_A + i] = BT ? n0 + c.row < a.N : n0 + 8 * c.chunk < a.N;
     }
 
     LDS_PTR(char) lds = (LDS_PTR(char))smem;
     const _Float16 *a_tile = a.A + (int64_t)m0 * a.lda;
-    const _Float16 *b_tile = a.B + n0;
+    const _Float16 *b_tile = BT ? a.B + (int64_t)n0 * a.ldb : a.B + n0;
 
     // Load j of stage kt into LDS buffer buf of its operand (stages past K
     // load zeros); j < DMA_A loads A, the others B.
@@ -159,7 +173,7 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
             const uint32_t l = (uint32_t)(uintptr_t)(lds + buf * S::A_BYTES + (wave * S::DMA_A + j) * 1024);
             dma16(r, l, in ? off[j] : kOOB);
         } else {
-            const int4_t r = make_srd(b_tile + (int64_t)k0 * a.ldb);
+            const int4_t r = make_srd(BT ? b_tile + k0 : b_tile + (int64_t)k0 * a.ldb);
             const uint32_t l = (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES +
                                                      (wave * S::DMA_B + (j - S::DMA_A)) * 1024);
             dma16(r, l, in ? off[j] : kOOB);
@@ -209,11 +223,11 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
                 mfma_tile<S>(f[1], H + q, acc);
 #pragma unroll
                 for (int r = 2 * q; r < 2 * q + 2; ++r)
-                    if (r < kFragReads<S>) frag_read<S>(f[0], sA, sB, wm0, wn0, 0, lane, r);
+                    if (r < READS) frag_read<S, BT>(f[0], sA, sB, wm0, wn0, 0, lane, r);
             } else if (q < H + (S::KSTEPS - 1) * T) {
                 const int ks = (q - H) / T, i = (q - H) % T;
                 mfma_tile<S>(f[ks & 1], i, acc);
-                if (i < kFragReads<S>) frag_read<S>(f[(ks + 1) & 1], sA, sB, wm0, wn0, ks + 1, lane, i);
+                if (i < READS) frag_read<S, BT>(f[(ks + 1) & 1], sA, sB, wm0, wn0, ks + 1, lane, i);
             } else {
                 mfma_tile<S>(f[1], q - H - (S::KSTEPS - 1) * T, acc);
             }
@@ -241,9 +255,9 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     // by element into buffer 0 once every wave is done with the stages.
     if (a.kmain < a.K) {
         barrier_lds();
-        stage_tail<S>(a, m0, n0, lds, lds + B_REGION, tid);
+        stage_tail<S, BT>(a, m0, n0, lds, lds + B_REGION, tid);
         barrier_lds();
-        mma_kstep<S>(lds, lds + B_REGION, 0, wm0, wn0, lane, acc);
+        mma_kstep<S, BT>(lds, lds + B_REGION, 0, wm0, wn0, lane, acc);
     }
 
     barrier_lds();  // every wave is done with the stages (and the tail block)
@@ -264,7 +278,7 @@ const TileConfig kPipeConfigs[PIPE_CONFIGS] = {
      "pipe_256x256x64_w2x4_s2_a3"},
 };
 
-template <class S, int SPACING, int DOFF, int ASTAGES>
+template <class S, int SPACING, int DOFF, int ASTAGES, bool BT = false>
 static hipError_t launch_pipe_t(const Problem &p, hipStream_t stream) {
     KArgs a;
     a.A = (const _Float16 *)p.A;
@@ -279,15 +293,25 @@ static hipError_t launch_pipe_t(const Problem &p, hipStream_t stream) {
     a.ldc = p.ldc;
     a.group_m = 4;
     a.k_split = (int)p.K;
-    a.kmain = (p.K % 8 == 0 && p.N % 8 == 0) ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
+    // loads stop at the last multiple of 8 below K when a 16-byte chunk
+    // could cross the end of a row (K % 8; N % 8 too for an N-contiguous B)
+    const bool whole = p.K % 8 == 0 && (BT || p.N % 8 == 0);
+    a.kmain = whole ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
     a.tiles_m = (a.M + S::BM - 1) / S::BM;
     a.tiles_n = (a.N + S::BN - 1) / S::BN;
-    hipLaunchKernelGGL((k_tiled_pipe<S, SPACING, DOFF, ASTAGES>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
+    hipLaunchKernelGGL((k_tiled_pipe<S, SPACING, DOFF, ASTAGES, BT>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
                        dim3(S::NT), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream) {
+    if (p.trans_b) {
+        switch (config) {
+            case PIPE_256x256x64_A3: return launch_pipe_t<Pipe256x64, 2, 1, 3, true>(p, stream);
+            case PIPE_256x256x64_W8_A3: return launch_pipe_t<Pipe256x64w8, 2, 1, 3, true>(p, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (config) {
         // four 32-deep stages: loads every 4 slots across the step
         case PIPE_256x256x32: return launch_pipe_t<Pipe256x32, 4, 3, 4>(p, stream);

@@ -43,6 +43,14 @@ struct KArgs {
     int kmain;
 };
 
+// Arguments of a grouped launch: problem p owns work-group ids (after the
+// XCD renumbering) tile_start[p] .. tile_start[p+1]-1.
+struct GroupArgs {
+    int count;
+    int tile_start[17];
+    KArgs p[16];
+};
+
 typedef int int4_t __attribute__((ext_vector_type(4)));
 typedef int int2_t __attribute__((ext_vector_type(2)));
 
@@ -103,14 +111,17 @@ __device__ __forceinline__ half8_t read_b_frag(LDS_PTR(const char) base, int off
 }
 
 // One 16-wide k-step s of an LDS stage: read the operand fragments of every
-// MFMA tile of this wave and accumulate.
-template <class S>
+// MFMA tile of this wave and accumulate. BT: the B tile is held like the A
+// tile (rows n, K-contiguous; B given transposed), so its fragments are read
+// the way A's are.
+template <class S, bool BT = false>
 __device__ __forceinline__ void mma_kstep(LDS_PTR(const char) sA, LDS_PTR(const char) sB, int s, int wm0, int wn0,
                                           int lane, float16_t (&acc)[S::TN][S::TM]) {
     half8_t bf[S::TN], af[S::TM];
 #pragma unroll
     for (int tn = 0; tn < S::TN; ++tn)
-        bf[tn] = read_b_frag(sB, frag_b_offset<S>(wn0, tn, s, 0, lane), frag_b_offset<S>(wn0, tn, s, 1, lane));
+        bf[tn] = BT ? *(LDS_PTR(const half8_t))(sB + frag_a_offset<S>(wn0, tn, s, lane))
+                    : read_b_frag(sB, frag_b_offset<S>(wn0, tn, s, 0, lane), frag_b_offset<S>(wn0, tn, s, 1, lane));
 #pragma unroll
     for (int tm = 0; tm < S::TM; ++tm) af[tm] = *(LDS_PTR(const half8_t))(sA + frag_a_offset<S>(wm0, tm, s, lane));
 #pragma unroll
@@ -121,11 +132,11 @@ __device__ __forceinline__ void mma_kstep(LDS_PTR(const char) sA, LDS_PTR(const 
 }
 
 // The tile product of one LDS stage.
-template <class S>
+template <class S, bool BT = false>
 __device__ __forceinline__ void mma_stage(LDS_PTR(const char) sA, LDS_PTR(const char) sB, int wm0, int wn0, int lane,
                                           float16_t (&acc)[S::TN][S::TM]) {
 #pragma unroll
-    for (int s = 0; s < S::KSTEPS; ++s) mma_kstep<S>(sA, sB, s, wm0, wn0, lane, acc);
+    for (int s = 0; s < S::KSTEPS; ++s) mma_kstep<S, BT>(sA, sB, s, wm0, wn0, lane, acc);
 }
 
 // Rows kmain .. K-1 of the sum (1 to 8 of them) as one 16-deep block in the
@@ -135,7 +146,9 @@ __device__ __forceinline__ void mma_stage(LDS_PTR(const char) sA, LDS_PTR(const 
 // 16-byte chunk they fetch crosses the K edge of A, and a chunk crossing the
 // N edge of B reads at most into the next row of B (needs ldb >= 8), whose
 // values only reach output columns >= N, which are never stored.
-template <class S>
+// BT (B given transposed, N x K): the B block is staged like the A block,
+// rows n, k = kmain .. kmain+15 (needs BM == BN).
+template <class S, bool BT = false>
 __device__ __forceinline__ void stage_tail(const KArgs &a, int m0, int n0, LDS_PTR(char) sA, LDS_PTR(char) sB,
                                            int tid) {
     for (int q = tid; q < S::BM * 2; q += S::NT) {
@@ -145,6 +158,19 @@ __device__ __forceinline__ void stage_tail(const KArgs &a, int m0, int n0, LDS_P
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (m < a.M && k + e < a.K) ? a.A[(int64_t)m * a.lda + k + e] : (_Float16)0.0f;
         *(LDS_PTR(half8_t))(sA + lds_a_offset<S>(row, chunk)) = v;
+    }
+    if (BT) {
+        static_assert(!BT || S::BM == S::BN, "transposed B is staged in the A layout");
+        for (int q = tid; q < S::BN * 2; q += S::NT) {
+            const int row = q / 2, chunk = q % 2;
+            const int n = n0 + row, k = a.kmain + 8 * chunk;
+            half8_t v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = (n < a.N && k + e < a.K) ? a.B[(int64_t)n * a.ldb + k + e] : (_Float16)0.0f;
+            *(LDS_PTR(half8_t))(sB + lds_a_offset<S>(row, chunk)) = v;
+        }
+        return;
     }
     for (int q = tid; q < 16 * S::CB; q += S::NT) {
         const int row = q / S::CB, chunk = q % S::CB;

@@ -8,7 +8,8 @@
 namespace tlg {
 
 // One GEMM+ReLU problem: C (M x N) = ReLU(A (M x K) . B (K x N)), fp16,
-// row-major, leading dimensions in elements.
+// row-major, leading dimensions in elements. trans_b: B is given as its
+// transpose, N x K row-major (ldb >= K).
 struct Problem {
     int64_t M, N, K;
     const void *A;
@@ -17,7 +18,11 @@ struct Problem {
     int64_t ldb;
     void *C;
     int64_t ldc;
+    bool trans_b = false;
 };
+
+// Most problems one grouped launch takes.
+constexpr int kGroupMax = 16;
 
 // Tile configurations. The index is what tlg_plan reports as `config`.
 struct TileConfig {
@@ -58,6 +63,9 @@ extern const TileConfig kPipeConfigs[PIPE_CONFIGS];
 
 // Launchers: enqueue on `stream`, return the launch status.
 hipError_t launch_tiled_dma(int config, const Problem &p, hipStream_t stream);
+// count (1 .. kGroupMax) problems, all with the same trans_b, in one launch
+// of the direct-to-LDS kernel (each must pass the direct-to-LDS checks)
+hipError_t launch_tiled_dma_grouped(int config, const Problem *ps, int count, hipStream_t stream);
 hipError_t launch_tiled_general(int config, const Problem &p, hipStream_t stream);
 hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream);
 // Stage 1 writes fp32 partials W[s][m][n] (M x N packed per split) for
