@@ -77,8 +77,13 @@ def test_plan_shapes_of_the_workloads():
     assert p["config_name"].startswith("streamk") and p["kernels"] == 1
     assert p["grid"] == 2 * 256 and p["splits"] >= 2  # two work-groups per CU, ~4.6 per output tile
     assert p["workspace_bytes"] == (64 << 10) + p["grid"] * 2 * 32 * 128 * 4 <= tlg.tlg_workspace_bytes()
-    assert tlg.plan(48, 14336, 4096)["config_name"].startswith("streamk")  # M above one strip
-    assert tlg.plan(16, 2048, 4096)["config_name"].startswith("streamk")  # too few strips
+    assert tlg.plan(48, 14336, 4096)["config_name"] == "dma_64x64x64_w2x2_s3"  # M above one strip, tiles enough
+    assert tlg.plan(48, 4096, 4096)["config_name"].startswith("streamk")  # M above one strip, few tiles
+    p = tlg.plan(16, 2048, 4096)  # few strips: K split among work-groups too, up to the CUs
+    assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 8 and p["grid"] == 32 * 8
+    p = tlg.plan(1, 4096, 4096)
+    assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 64 * 4
+    assert tlg.plan(3072, 3072, 3072)["config_name"] == "pipe_256x256x64_w2x4_s2_a3"  # 144 tiles of 256 x 256
     assert tlg.plan(256, 256, 256)["variant_name"] == "tiled_dma"
     assert tlg.plan(5, 7, 0)["variant_name"] == "fill_zero"
     assert tlg.plan(0, 7, 9)["variant_name"] == "noop"
@@ -108,8 +113,10 @@ def test_forced_variants():
         tlg.plan(16, 14336, 4095, variant=tlg.TLG_VARIANT_SPLITK)
     p = tlg.plan(16, 14336, 4096, variant=tlg.TLG_VARIANT_SPLITK, config=0, splits=8)
     assert p["splits"] == 8 and p["grid"] == 112 * 8 and p["kernels"] == 2
-    p = tlg.plan(16, 256, 64, variant=tlg.TLG_VARIANT_SPLITK)  # stream-K: never more work-groups than iterations
-    assert p["grid"] == 2 * 1 and p["kernels"] == 1
+    p = tlg.plan(16, 256, 64, variant=tlg.TLG_VARIANT_SPLITK, config=2)  # stream-K: never more work-groups
+    assert p["grid"] == 2 * 1 and p["kernels"] == 1                         # than iterations
+    p = tlg.plan(16, 256, 64, variant=tlg.TLG_VARIANT_SPLITK)  # strips: never more parts than K blocks
+    assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["grid"] == 4 and p["splits"] == 1
     p = tlg.plan(300, 300, 300, variant=tlg.TLG_VARIANT_NAIVE)
     assert p["variant_name"] == "naive"
     p = tlg.plan(300, 304, 304, variant=tlg.TLG_VARIANT_TILED_GENERAL)
@@ -159,3 +166,48 @@ def test_gemm_relu_rejects_null_handle():
     st = nat.tlg_gemm_relu(None, 4, 4, 4, A16, 4, A16, 4, A16, 4, None)
     assert st == nat.TLG_ERROR_INVALID_VALUE
     assert nat.tlg_destroy(None) == 0
+
+
+_TABLE = os.path.join(os.path.dirname(tlg.__file__), "csrc", "tune_table.inc")
+_ENTRY = re.compile(r"^\s*\{(-?\d+), (-?\d+), (-?\d+), (-?\d+), (-?\d+), (-?\d+), (-?\d+)\},\s*//\s*(\d+)x(\d+)x(\d+):")
+
+
+def _tune_entries():
+    out = []
+    with open(_TABLE) as f:
+        for line in f:
+            m = _ENTRY.match(line)
+            if m:
+                v = [int(x) for x in m.groups()]
+                out.append((tuple(v[:7]), tuple(v[7:])))
+    return out
+
+
+def _clog2(x):
+    return 0 if x <= 1 else (x - 1).bit_length()
+
+
+def test_tuned_table_entries_are_taken():
+    """Every measured entry of the compiled-in table decides the plan of its
+    own shape (the class key matches the shape), and an entry the problem
+    cannot take (unaligned pointers for a direct-to-LDS kernel) falls back to
+    the heuristic instead of failing."""
+    entries = _tune_entries()
+    for (lm, ln, lk, rg, variant, config, splits), (M, N, K) in entries:
+        assert (lm, ln, lk, rg) == (_clog2(M), _clog2(N), _clog2(K), 1 if (K % 8 or N % 8) else 0)
+        p = tlg.plan(M, N, K)
+        assert (p["variant"], p["config"]) == (variant, config), (M, N, K, p)
+        if splits:
+            assert p["splits"] == splits
+        forced = tlg.plan(M, N, K, variant=variant, config=config, splits=splits)
+        assert (forced["grid"], forced["splits"]) == (p["grid"], p["splits"])
+        q = tlg.plan(M, N, K, aligned=False)  # the tuned kernel needs 16-byte aligned data
+        assert q["variant_name"] in ("tiled_dma", "tiled_general")
+
+
+def test_tuned_classes_of_the_table():
+    # the two measured skinny classes: two-kernel split-K instead of stream-K
+    assert tlg.plan(48, 4096, 14336)["config_name"] == "splitk_32x128x64_w1x4_s4"
+    assert tlg.plan(64, 4096, 8192)["config_name"] == "splitk_32x128x64_w1x4_s4"
+    # a neighbouring class keeps the heuristic's choice
+    assert tlg.plan(48, 4096, 4096)["config_name"].startswith("streamk")

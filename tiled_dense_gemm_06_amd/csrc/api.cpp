@@ -65,6 +65,26 @@ bool dma_ok_aligned(const tlg::Problem &p, int bm, int bn, int bk) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Tuned choices by shape class (see tiled_dense_gemm_06_amd/autotune.py).
+struct TuneEntry {
+    int lm, ln, lk, ragged;  // ceil(log2) of M, N, K; K or N not a multiple of 8
+    int variant, config, splits;
+};
+#include "tune_table.inc"
+
+int clog2(int64_t x) {
+    int l = 0;
+    while (l < 62 && (int64_t(1) << l) < x) ++l;
+    return l;
+}
+
+const TuneEntry *tune_lookup(const tlg::Problem &p) {
+    const int lm = clog2(p.M), ln = clog2(p.N), lk = clog2(p.K), rg = (p.K % 8 || p.N % 8) ? 1 : 0;
+    for (const TuneEntry &e : kTuneTable)
+        if (e.lm == lm && e.ln == ln && e.lk == lk && e.ragged == rg && e.variant != TLG_VARIANT_AUTO) return &e;
+    return nullptr;
+}
+
 void fill_info(tlg_plan_info *o, int variant, int config, const tlg::TileConfig *tc, int splits, int kernels,
                int64_t grid, int64_t ws) {
     memset(o, 0, sizeof *o);
@@ -140,8 +160,24 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
         return TLG_SUCCESS;
     }
 
-    // split-K for skinny M
-    if (variant == TLG_VARIANT_SPLITK || (variant == TLG_VARIANT_AUTO && p.M <= 64 && p.K >= 512)) {
+    // a tuned choice for the shape's class, if it can serve this problem
+    if (variant == TLG_VARIANT_AUTO) {
+        if (const TuneEntry *e = tune_lookup(p)) {
+            if (plan_impl(p, e->variant, e->config, e->splits, cap + kCounterBytes, cus, o, k_split_out) ==
+                TLG_SUCCESS)
+                return TLG_SUCCESS;
+            *k_split_out = 0;
+        }
+    }
+
+    // split-K for skinny M: by default when M fits one strip (M <= 32,
+    // aligned), or M <= 64 with 64 x 64 tiles for fewer than half the CUs;
+    // with more tiles the tiled kernels measured faster (64x14336x4096:
+    // 32 us on 64 x 64 tiles, 63 us stream-K)
+    const bool strip_fits = p.M <= tlg::kStripConfig.bm &&
+                            dma_ok_aligned(p, tlg::kStripConfig.bm, tlg::kStripConfig.bn, tlg::kStripConfig.bk);
+    const bool few_tiles = p.M <= 64 && ceil_div(p.N, 64) * 2 < cus;
+    if (variant == TLG_VARIANT_SPLITK || (variant == TLG_VARIANT_AUTO && (strip_fits || few_tiles) && p.K >= 512)) {
         if (!config_ok(config, tlg::SPLIT_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
         // K split among the waves of a work-group per column strip, when M
         // fits one strip and there are strips for at least half the CUs
@@ -149,11 +185,14 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
         const int64_t strips = ceil_div(p.N, ts.bn);
         const bool strip_ok = p.M <= ts.bm && dma_ok_aligned(p, ts.bm, ts.bn, ts.bk) && strips <= 0x7fffffff;
         int cfg = config;
-        if (cfg < 0) cfg = strip_ok && 2 * strips >= cus ? tlg::SPLIT_WAVES_32x64x64 : tlg::SPLIT_STREAMK_32x128x64;
+        if (cfg < 0) cfg = strip_ok ? tlg::SPLIT_WAVES_32x64x64 : tlg::SPLIT_STREAMK_32x128x64;
         if (cfg == tlg::SPLIT_WAVES_32x64x64) {
             if (!strip_ok) return TLG_ERROR_NOT_SUPPORTED;
-            // parts per strip: forced, else one
-            int64_t parts = splits > 0 ? splits : 1;
+            // parts per strip: forced, else as many as fit the CUs whole
+            // (1x4096x4096: 4 parts 12 us vs 1 part 23 us; 16x14336x4096:
+            // 1 part 25 us vs 2 parts 29 us), at most 8
+            int64_t parts = splits > 0 ? splits : (strips >= cus ? 1 : cus / strips);
+            if (splits <= 0 && parts > 8) parts = 8;
             const int64_t nkb = ceil_div(p.K, ts.bk);
             if (parts > nkb) parts = nkb > 0 ? nkb : 1;
             const int64_t slot_bytes = (int64_t)ts.bm * ts.bn * 4;
@@ -204,7 +243,9 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
         const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64_W8_A3;
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
-        if (dma_ok(p, tc.bm, tc.bn, tc.bk) && (variant == TLG_VARIANT_TILED_PIPE || tiles >= 224)) {
+        // 128 tiles of 256 x 256 (half the CUs) measured faster than the
+        // 128 x 128 tiles already (3072^3: 72 vs 101 us)
+        if (dma_ok(p, tc.bm, tc.bn, tc.bk) && (variant == TLG_VARIANT_TILED_PIPE || tiles >= 128)) {
             fill_info(o, TLG_VARIANT_TILED_PIPE, cfg, &tc, 1, 1, tiles, 0);
             return TLG_SUCCESS;
         }
