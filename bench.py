@@ -206,7 +206,7 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_MFMA_TFLOPS}
     plain = args.variant == "auto" and args.config < 0 and not (args.trans_b or args.grouped)
-    roof["traffic"] = measured_traffic(w.name) if plain else None
+    roof["traffic"] = measured_traffic(w.name, plan["config_name"]) if plain else None
     roof["kernel"] = plan["config_name"]
     roof["launch_ms_avg"] = avg_launch_s * 1e3
     roof["launch_ms_min"] = float(np.min(per_launch_ms))

@@ -9,12 +9,14 @@ counter bytes, separately for reads and writes.
 Usage (after the counter runs, on the CSV files rocprofv3 wrote)::
 
     python -m tiled_dense_gemm_06_amd.profiling traffic --workload square8192 \\
-        --kernel k_tiled_pipe --fetch F.csv --write W.csv \\
+        --kernel k_tiled_pipe --config pipe_256x256x64_w2x4_s2_a3 --fetch F.csv --write W.csv \\
         --copy-fetch CF.csv --copy-write CW.csv --copy-mib 512
 
-It records, under the digest of the library's kernel sources, the scaled
-fetch and write bytes per launch in ``profiles/traffic.json``; ``bench.py``
-reports them only while the kernel sources still have that digest.
+It records the scaled fetch and write bytes per launch in
+``profiles/traffic.json``, with the tile configuration that ran and the
+digest of that kernel's device sources (its own ``.hip`` file and the two
+device headers); ``bench.py`` reports them only while the workload still
+runs that configuration and those sources still have that digest.
 
 ``summary`` writes the Markdown summary of one workload's profile (the
 kernel-trace statistics of a command, and the scaled counter bytes when
@@ -28,7 +30,6 @@ from __future__ import annotations
 
 import argparse
 import csv
-import glob
 import hashlib
 import json
 import os
@@ -39,14 +40,29 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_KERNEL = "copyBuffer"
 
 
-def kernel_sources() -> list[str]:
-    return sorted(glob.glob(os.path.join(HERE, "csrc", "*"))) + [os.path.join(ROOT, "include", "tlg.h")]
+# the file each kernel's device code lives in (besides the device headers)
+KERNEL_FILES = {
+    "k_tiled_pipe": "gemm_relu_pipe_gfx950.hip",
+    "k_tiled_dma": "gemm_relu_gfx950.hip",
+    "k_tiled_general": "gemm_relu_gfx950.hip",
+    "k_skinny_strip": "gemm_relu_skinny_gfx950.hip",
+    "k_streamk": "gemm_relu_streamk_gfx950.hip",
+    "k_mx": "gemm_relu_mx_gfx950.hip",
+}
+DEVICE_HEADERS = ["gfx950_ops.h", "tile_layout.h"]
 
 
-def kernel_source_digest() -> str:
-    """sha256 over every source the kernels are built from."""
+def kernel_sources(kernel: str) -> list[str]:
+    """The sources a kernel's device code is built from."""
+    if kernel not in KERNEL_FILES:
+        raise KeyError(f"unknown kernel {kernel!r}; known: {sorted(KERNEL_FILES)}")
+    return [os.path.join(HERE, "csrc", f) for f in [KERNEL_FILES[kernel]] + DEVICE_HEADERS]
+
+
+def kernel_source_digest(kernel: str) -> str:
+    """sha256 over the sources a kernel's device code is built from."""
     h = hashlib.sha256()
-    for p in kernel_sources():
+    for p in kernel_sources(kernel):
         h.update(os.path.basename(p).encode())
         with open(p, "rb") as f:
             h.update(f.read())
@@ -83,11 +99,12 @@ def traffic(args) -> dict:
             data = json.load(f)
     except (OSError, ValueError):
         data = {}
-    digest = kernel_source_digest()
-    if data.get("kernel_source_sha256") != digest:
-        data = {"kernel_source_sha256": digest, "workloads": {}}
+    if "kernel_source_sha256" in data:  # records of the earlier whole-library digest
+        data = {}
+    data.setdefault("workloads", {})
     data["calibration"] = {"copy_bytes": copy_bytes, "fetch_factor": fetch_factor, "write_factor": write_factor}
-    rec = {"kernel": args.kernel, "fetch_bytes": fetch, "write_bytes": write, "bytes_per_launch": fetch + write}
+    rec = {"kernel": args.kernel, "config": args.config, "sources_sha256": kernel_source_digest(args.kernel),
+           "fetch_bytes": fetch, "write_bytes": write, "bytes_per_launch": fetch + write}
     data["workloads"][args.workload] = rec
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
@@ -96,17 +113,20 @@ def traffic(args) -> dict:
     return rec
 
 
-def measured_traffic(workload: str):
-    """Scaled HBM bytes per launch for a workload, if taken on the current kernel sources; else None."""
+def measured_traffic(workload: str, config: str):
+    """Scaled HBM bytes per launch for a workload, if they were taken with the
+    tile configuration ``config`` on the kernel's current sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    if data.get("kernel_source_sha256") != kernel_source_digest():
-        return None
     rec = data.get("workloads", {}).get(workload)
-    return None if not rec else rec.get("bytes_per_launch")
+    if not rec or rec.get("config") != config or rec.get("kernel") not in KERNEL_FILES:
+        return None
+    if rec.get("sources_sha256") != kernel_source_digest(rec["kernel"]):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 PEAK_MFMA_TFLOPS = 2516.6
@@ -171,7 +191,8 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--workload", required=True)
-    t.add_argument("--kernel", required=True, help="substring of the kernel name")
+    t.add_argument("--kernel", required=True, choices=sorted(KERNEL_FILES), help="the kernel (name prefix)")
+    t.add_argument("--config", required=True, help="the tile configuration that ran (tlg.plan's config_name)")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--copy-fetch", required=True)
