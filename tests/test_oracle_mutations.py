@@ -50,3 +50,41 @@ def test_pins_catch_planted_mistake(name, old, new, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"), "-k", QUICK],
                        env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
     assert r.returncode == 1, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
+
+
+# ---------------------------------------------------------------- the block-scaled oracle
+
+MX_SRC = os.path.join(ROOT, "oracle", "oracle_mx.c")
+
+# (The order of the two E2M1 codes inside a byte is not among them: A and B
+# share it, so swapping it pairs the same elements and leaves every sum, and
+# every result, unchanged; a byte never straddles a 32-element block.)
+MX_MUTATIONS = [
+    ("scale_bias", "return ldexp(1.0, (int)e - 127);", "return ldexp(1.0, (int)e - 128);"),
+    ("scale_of_neighbour_block", "oracle_mx_scale(SA[i * ldsa + b])",
+     "oracle_mx_scale(SA[i * ldsa + (b ^ 1) % (K / 32)])"),
+    ("last_element_of_block_dropped", "k < 32 * b + 32; k++", "k < 32 * b + 31; k++"),
+    ("e4m3_bias", "return minifloat(code, 4, 3, 7);", "return minifloat(code, 4, 3, 8);"),
+    ("e5m2_bias", "return minifloat(code, 5, 2, 15);", "return minifloat(code, 5, 2, 16);"),
+    ("e2m1_bias", "return minifloat(code & 0xfu, 2, 1, 1);", "return minifloat(code & 0xfu, 2, 1, 0);"),
+    ("subnormal_exponent", "v = ldexp((double)f, 1 - bias - mb);", "v = ldexp((double)f, -bias - mb);"),
+    ("sign_ignored", "return sign ? -v : v;", "return v;"),
+    ("relu_missing", "static double relu64(double x) { return (x > 0.0) ? x : 0.0; }",
+     "static double relu64(double x) { return x; }"),
+    ("ties_away", "if (rem > half || (rem == half && (q & 1ull))) q += 1ull;", "if (rem >= half) q += 1ull;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MX_MUTATIONS, ids=[m[0] for m in MX_MUTATIONS])
+def test_mx_pins_catch_planted_mistake(name, old, new, tmp_path):
+    src = open(MX_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique or missing: {name}"
+    mutant_c = tmp_path / "oracle_mx_mutant.c"
+    mutant_c.write_text(src.replace(old, new))
+    so = tmp_path / f"liboracle_mx_{name}.so"
+    subprocess.run(["gcc", *oracle.CFLAGS, str(mutant_c), "-o", str(so), "-lm"], check=True)
+    env = dict(os.environ, TLG_ORACLE_MX_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_mx_pins.py")],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"

@@ -115,3 +115,64 @@ def make_random(M: int, N: int, K: int, seed: int, kind: str = "uniform"):
 
 def sha256(x: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(x).tobytes()).hexdigest()
+
+
+# ---------------------------------------------------------------------------
+# Block-scaled (MX) inputs: element codes and E8M0 scale bytes, drawn as bit
+# fields (no decoding and no GEMM arithmetic here).
+#
+# Recipe: ``numpy.random.default_rng(seed)``; A's codes, then B's codes, then
+# A's scales, then B's scales, each in the calls below, row-major. B is drawn
+# as its transpose, N x K (the block-scaled path takes B that way).
+#  * kind "random": per element a sign bit (uniform), an exponent field
+#    (uniform over bias-3 .. bias+3 for the 8-bit formats, over 0..3 for
+#    E2M1), and a fraction field (uniform); then one element in 16 gets
+#    exponent field 0 (zero or subnormal). Scales uniform over
+#    127-spread .. 127+spread (2^-spread .. 2^spread).
+#  * kind "small_int": elements -2, -1, 0, 1, 2 (uniform), encoded as
+#    sign | (bias + log2|v|) << fraction bits, 0 as code 0; all scales 127
+#    (2^0), so every sum is an integer that fp32 holds exactly.
+# E2M1 codes are packed two per byte: element 2t in the low nibble.
+# ---------------------------------------------------------------------------
+
+MX_FORMATS = {"e4m3": (4, 3), "e5m2": (5, 2), "e2m1": (2, 1)}  # exponent bits, fraction bits
+MX_BLOCK = 32
+
+
+def _mx_codes(rng: np.random.Generator, shape, fmt: str, kind: str) -> np.ndarray:
+    eb, mb = MX_FORMATS[fmt]
+    bias = (1 << (eb - 1)) - 1
+    sign = rng.integers(0, 2, size=shape, dtype=np.int64) << (eb + mb)
+    if kind == "small_int":
+        mag = rng.integers(0, 3, size=shape, dtype=np.int64)  # |v| = 0, 1, 2
+        expf = np.where(mag == 0, 0, bias + (mag == 2))
+        codes = np.where(mag == 0, 0, sign | (expf << mb))
+    elif kind == "random":
+        lo, hi = (0, (1 << eb) - 1) if fmt == "e2m1" else (bias - 3, bias + 3)
+        expf = rng.integers(lo, hi + 1, size=shape, dtype=np.int64)
+        frac = rng.integers(0, 1 << mb, size=shape, dtype=np.int64)
+        expf = np.where(rng.integers(0, 16, size=shape) == 0, 0, expf)
+        codes = sign | (expf << mb) | frac
+    else:
+        raise ValueError(kind)
+    codes = codes.astype(np.uint8)
+    if fmt == "e2m1":
+        codes = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return np.ascontiguousarray(codes)
+
+
+def make_mx_inputs(fmt: str, M: int, N: int, K: int, seed: int, kind: str = "random", spread: int = 2):
+    """(A, SA, Bt, SB): A codes (M, K) and Bt codes (N, K) as uint8 (E2M1:
+    (M, K/2) and (N, K/2) packed bytes), scales (M, K/32) and (N, K/32)."""
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    rng = np.random.default_rng(seed)
+    A = _mx_codes(rng, (M, K), fmt, kind)
+    Bt = _mx_codes(rng, (N, K), fmt, kind)
+    if kind == "small_int":
+        SA = np.full((M, K // MX_BLOCK), 127, np.uint8)
+        SB = np.full((N, K // MX_BLOCK), 127, np.uint8)
+    else:
+        SA = rng.integers(127 - spread, 128 + spread, size=(M, K // MX_BLOCK)).astype(np.uint8)
+        SB = rng.integers(127 - spread, 128 + spread, size=(N, K // MX_BLOCK)).astype(np.uint8)
+    return A, SA, Bt, SB
