@@ -61,6 +61,98 @@ def cpu_baseline(w, A, B, target_s: float):
     }
 
 
+# dense block-scaled MFMA peaks of MI355X (AMD's published dense figures)
+PEAK_MX_TFLOPS = {"e4m3": 5000.0, "e5m2": 5000.0, "e2m1": 10100.0}
+
+
+def mx_cpu_baseline(fmt, w, A, SA, Bt, SB, target_s: float):
+    """The block-scaled oracle as it stands, on whole sampled output rows."""
+    import numpy as np
+
+    import oracle
+    import oracle.mx as omx
+
+    threads = oracle.default_threads()
+    n = min(threads, w.M)
+    while True:
+        rows = np.linspace(0, w.M - 1, n).astype(np.int64)
+        t0 = time.perf_counter()
+        omx.gemm_relu_mx_rows(fmt, A, SA, Bt, SB, rows)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 2 or n >= w.M:
+            break
+        n = int(min(w.M, max(n + threads, n * min(8.0, target_s / max(dt, 1e-6)))))
+        n = min(w.M, -(-n // threads) * threads)
+    return {
+        "value": 2.0 * n * w.N * w.K / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+        "sample": f"{n} of {w.M} output rows ({n}x{w.N}x{w.K} block-scaled multiply-adds, all K), "
+                  f"{dt:.2f} s wall on {threads} threads",
+    }
+
+
+def bench_mx(args, torch, tlg, wl, dev) -> int:
+    """The block-scaled path (tlg_gemm_relu_mx) on the workload's shape."""
+    import numpy as np
+
+    fmt = args.mx
+    w = wl.WORKLOADS[args.workload]
+    if w.K % 128:
+        print("bench.py: the block-scaled path needs K % 128 == 0", file=sys.stderr)
+        return 2
+    A, SA, Bt, SB = wl.make_mx_inputs(fmt, w.M, w.N, w.K, seed=w.seed, kind="random")
+    plan = tlg.plan_mx(fmt, w.M, w.N, w.K, config=args.config)
+    bits = 4 if fmt == "e2m1" else 8
+    alg_bytes = (w.M + w.N) * w.K * bits // 8 + (w.M + w.N) * (w.K // 32) + 2 * w.M * w.N
+    R = max(2, math.ceil(2 * MALL_BYTES / alg_bytes) + 1)
+    ins = [torch.from_numpy(x).to(dev) for x in (A, SA, Bt, SB)]
+    sets = [ins] + [[x.clone() for x in ins] for _ in range(R - 1)]
+    Cs = [torch.empty((w.M, w.N), dtype=torch.float16, device=dev) for _ in range(R)]
+    h = tlg.handle_for(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        a, sa, b, sb = sets[i % R]
+        tlg.gemm_relu_mx(fmt, a, sa, b, sb, out=Cs[i % R], config=args.config, handle=h, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = starts[0].elapsed_time(ends[-1]) / K
+    avg_launch_s = float(np.mean(per_launch_ms)) / 1e3
+    tflops = w.flop / (ms_per_step / 1e3) / 1e12
+    peak = PEAK_MX_TFLOPS[fmt]
+    achieved = w.flop / avg_launch_s / 1e12
+    out = {
+        "metric": f"block-scaled GEMM+ReLU TFLOPS ({fmt} codes, one E8M0 scale per 32 k, fp32 acc, fp16 out)",
+        "value": tflops, "unit": "TFLOPS", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": fmt, "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "seed": w.seed,
+                   "inputs": "random codes (exponents bias-3..bias+3, 1 in 16 zero/subnormal), scales 2^-2..2^2",
+                   "kernel": plan["config_name"], "rotated_buffers": R, "alg_bytes": alg_bytes,
+                   "accumulate": "f32", "epilogue": "relu, round-to-nearest-even to f16"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None, "kernel": plan["config_name"],
+                     "launch_ms_avg": avg_launch_s * 1e3, "launch_ms_min": float(np.min(per_launch_ms))},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = mx_cpu_baseline(fmt, w, A, SA, Bt, SB, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def copy_calibration(torch, dev, nbytes: int, steps: int, warmup: int) -> int:
     """A plain copy of a known size: reads nbytes and writes nbytes per launch.
     Under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it gives the factor between
@@ -102,6 +194,8 @@ def main() -> int:
     ap.add_argument("--grouped", type=int, default=0, metavar="G",
                     help="split M into G row blocks (2 <= G <= 16) and run them as one tlg_gemm_relu_grouped "
                          "call (the blocks share B); the work per step is unchanged")
+    ap.add_argument("--mx", choices=["e4m3", "e5m2", "e2m1"],
+                    help="time the block-scaled path (tlg_gemm_relu_mx) with these element codes instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, time a plain device-to-device copy of MIB MiB (the reference "
                          "kernel for scaling the HBM byte counters)")
@@ -127,6 +221,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.copy_calibration > 0:
         return copy_calibration(torch, dev, args.copy_calibration << 20, args.steps, args.warmup)
+    if args.mx:
+        return bench_mx(args, torch, tlg, wl, dev)
     w = wl.WORKLOADS[args.workload]
     A, B = wl.make_inputs(w)
     names = {v: k for k, v in tlg._native.VARIANT_NAMES.items()}

@@ -219,6 +219,72 @@ tlg_status tlg_gemm_relu_grouped(tlg_handle h, int32_t count, const tlg_gemm_des
 tlg_status tlg_gemm_relu_grouped_variant(tlg_handle h, int32_t config, int32_t count, const tlg_gemm_desc *descs,
                                          int32_t trans_b, hipStream_t stream);
 
+/* ---- Block-scaled (MX) element formats ----
+ *
+ * The TileLang article ("Backends and hardware support") names FP4 E2M1
+ * matrix cores on CDNA4 (gfx950) and a block-scaled MMA path; the TileLang
+ * forum post ("Backend Coverage", milestone list) names MXFP8 block-scaled
+ * GEMM with a transposed B. Neither page defines the formats; they are read
+ * as the OCP Microscaling (MX) formats:
+ *
+ *   C[i][j] = fp16_rne( ReLU( sum over blocks b = 0 .. K/32-1 of
+ *               2^(SA[i][b]-127) * 2^(SB[j][b]-127)
+ *               * sum over k = 32b .. 32b+31 of a[i][k] * b[j][k] ) )
+ *
+ * with a and b decoded from their element codes, the sum accumulated in fp32
+ * on the matrix cores, ReLU on the fp32 value and the fp16 copy-out rounding
+ * to nearest even (the quick-start kernel's epilogue). Scale bytes are E8M0
+ * (255 is NaN; ReLU then gives +0). Element codes that are NaN or infinite
+ * give results the hardware defines (not specified here).
+ *
+ * Layout (all row-major):
+ *   A  M x K element codes, lda elements per row (lda >= K);
+ *   B  N x K element codes: B is given TRANSPOSED, so both operands are
+ *      K-contiguous like their scale blocks (ldb >= K);
+ *   SA M x K/32 scale bytes, ldsa bytes per row (ldsa >= K/32);
+ *   SB N x K/32 scale bytes, ldsb bytes per row;
+ *   C  M x N fp16, ldc elements per row (ldc >= N); only the M x N window
+ *      is written.
+ * 8-bit codes take one byte each; E2M1 codes are packed two per byte,
+ * element 2t in the low nibble of byte t of the row (lda, ldb even).
+ *
+ * Requirements: K a multiple of 32 (else TLG_ERROR_INVALID_VALUE); K a
+ * multiple of 128, A and B 16-byte aligned with rows a multiple of 16 bytes,
+ * SA and SB 4-byte aligned with ldsa, ldsb multiples of 4, and C 2-byte
+ * aligned (else TLG_ERROR_NOT_SUPPORTED). The caller owns every buffer;
+ * nothing is allocated; the call is asynchronous on `stream`. M == 0 or
+ * N == 0 is a no-op, K == 0 writes +0. */
+typedef enum {
+    TLG_MX_E4M3 = 1, /* 8-bit: 1 sign, 4 exponent (bias 7), 3 fraction bits; S.1111.111 is NaN */
+    TLG_MX_E5M2 = 2, /* 8-bit: 1 sign, 5 exponent (bias 15), 2 fraction bits; IEEE-style inf/NaN */
+    TLG_MX_E2M1 = 3  /* 4-bit: 1 sign, 2 exponent (bias 1), 1 fraction bit; packed two per byte */
+} tlg_mx_format;
+
+#define TLG_MX_BLOCK 32
+
+/* C = ReLU(block-scaled A . B^T) as above, with the library's tile choice. */
+tlg_status tlg_gemm_relu_mx(tlg_handle h, int32_t format, int64_t M, int64_t N, int64_t K, const void *A,
+                            int64_t lda, const void *SA, int64_t ldsa, const void *B, int64_t ldb, const void *SB,
+                            int64_t ldsb, void *C, int64_t ldc, hipStream_t stream);
+
+/* tlg_gemm_relu_mx with a forced tile configuration (-1: library's choice;
+ * 0: 256 x 256 tiles, eight waves; 1: 128 x 128 tiles, four waves). */
+tlg_status tlg_gemm_relu_mx_variant(tlg_handle h, int32_t config, int32_t format, int64_t M, int64_t N, int64_t K,
+                                    const void *A, int64_t lda, const void *SA, int64_t ldsa, const void *B,
+                                    int64_t ldb, const void *SB, int64_t ldsb, void *C, int64_t ldc,
+                                    hipStream_t stream);
+
+/* What tlg_gemm_relu_mx(_variant) would launch (host only, no device call):
+ * the same checks and status codes; out->variant is TLG_VARIANT_TILED_DMA
+ * (the block-scaled kernel), TLG_VARIANT_NOOP or TLG_VARIANT_FILL_ZERO, and
+ * tlg_plan_mx_config_name names the configuration. */
+tlg_status tlg_plan_mx(int32_t format, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SA,
+                       int64_t ldsa, const void *B, int64_t ldb, const void *SB, int64_t ldsb, const void *C,
+                       int64_t ldc, int32_t config, tlg_plan_info *out);
+
+/* Name of a block-scaled tile configuration ("" if out of range). */
+const char *tlg_plan_mx_config_name(int32_t config);
+
 #ifdef __cplusplus
 }
 #endif

@@ -211,3 +211,39 @@ def test_tuned_classes_of_the_table():
     assert tlg.plan(64, 4096, 8192)["config_name"] == "splitk_32x128x64_w1x4_s4"
     # a neighbouring class keeps the heuristic's choice
     assert tlg.plan(48, 4096, 4096)["config_name"].startswith("streamk")
+
+
+def test_plan_block_scaled():
+    p = tlg.plan_mx("e4m3", 8192, 8192, 8192)
+    assert p["config_name"] == "mx_256x256_w2x4_s2" and p["grid"] == 32 * 32 and p["block_k"] == 128
+    p = tlg.plan_mx("e2m1", 8192, 8192, 8192)
+    assert p["config_name"] == "mx_256x256_w2x4_s2" and p["block_k"] == 256  # 4-bit codes: 256 per stage
+    p = tlg.plan_mx("e5m2", 300, 200, 384)
+    assert p["config_name"] == "mx_128x128_w2x2_s3" and p["grid"] == 3 * 2 and p["threads"] == 256
+    assert tlg.plan_mx("e4m3", 300, 200, 384, config=0)["grid"] == 2 * 1
+    assert tlg.plan_mx("e4m3", 0, 5, 128)["variant_name"] == "noop"
+    assert tlg.plan_mx("e4m3", 5, 5, 0)["variant_name"] == "fill_zero"
+    S, NS, INV = tlg.TlgError, nat.TLG_ERROR_NOT_SUPPORTED, nat.TLG_ERROR_INVALID_VALUE
+    cases = [
+        (dict(fmt="e4m3", M=64, N=64, K=100), INV),              # K not whole blocks of 32
+        (dict(fmt="e4m3", M=64, N=64, K=96), NS),                # K not a multiple of 128
+        (dict(fmt="e4m3", M=64, N=64, K=256, aligned=False), NS),
+        (dict(fmt="e4m3", M=64, N=64, K=256, lda=264), NS),      # rows not a multiple of 16 bytes
+        (dict(fmt="e2m1", M=64, N=64, K=256, lda=264), NS),      # 132-byte rows
+        (dict(fmt="e2m1", M=64, N=64, K=256, lda=257), INV),     # packed codes: even leading dimension
+        (dict(fmt="e4m3", M=64, N=64, K=256, ldsa=9), NS),       # scale rows not whole dwords
+        (dict(fmt="e4m3", M=64, N=64, K=256, ldsb=7), INV),      # scale rows shorter than K/32
+        (dict(fmt="e4m3", M=64, N=64, K=256, lda=128), INV),     # lda < K
+        (dict(fmt="e4m3", M=64, N=64, K=256, config=2), INV),
+    ]
+    for kw, status in cases:
+        kw = dict(kw)
+        fmt, M, N, K = kw.pop("fmt"), kw.pop("M"), kw.pop("N"), kw.pop("K")
+        with pytest.raises(S) as e:
+            tlg.plan_mx(fmt, M, N, K, **kw)
+        assert e.value.status == status, (fmt, M, N, K, kw)
+    with pytest.raises(ValueError):
+        tlg.plan_mx("e3m2", 64, 64, 256)
+    st, _ = nat.tlg_plan_mx(7, 64, 64, 256, 1 << 20, 256, 1 << 20, 8, 1 << 20, 256, 1 << 20, 8, 1 << 20, 64)
+    assert st == INV
+    assert nat.tlg_plan_mx_config_name(0) == "mx_256x256_w2x4_s2" and nat.tlg_plan_mx_config_name(2) == ""

@@ -17,7 +17,7 @@ from ._native import (  # noqa: F401  (re-exported C-ABI names)
     tlg_version, tlg_workspace_bytes,
 )
 
-__all__ = ["gemm_relu", "gemm_relu_grouped", "Handle", "handle_for", "plan"]
+__all__ = ["gemm_relu", "gemm_relu_grouped", "gemm_relu_mx", "Handle", "handle_for", "plan", "plan_mx"]
 
 
 class Handle:
@@ -185,4 +185,76 @@ def plan(M, N, K, lda=None, ldb=None, ldc=None, *, aligned: bool = True, variant
     d = info.as_dict()
     d["variant_name"] = _native.VARIANT_NAMES.get(info.variant, "?")
     d["config_name"] = _native.tlg_plan_config_name(info.variant, info.config)
+    return d
+
+
+def _mx_format(fmt) -> int:
+    f = _native.MX_FORMATS.get(fmt, fmt) if isinstance(fmt, str) else int(fmt)
+    if f not in _native.MX_FORMATS.values():
+        raise ValueError(f"unknown block-scaled format {fmt!r} (e4m3, e5m2 or e2m1)")
+    return f
+
+
+def _mx_ld(t, what, per_byte) -> int:
+    """Leading dimension in codes of a row-major 2-D uint8 tensor of packed codes."""
+    import torch
+
+    if t.dtype != torch.uint8 or t.dim() != 2:
+        raise TypeError(f"{what} must be a 2-D uint8 tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be on a GPU")
+    if t.numel() and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{what} must have unit stride along its rows (row-major)")
+    rows, cols = t.shape
+    ld = max(1, cols) if rows <= 1 or t.numel() == 0 else t.stride(0)
+    return ld * per_byte
+
+
+def gemm_relu_mx(fmt, A, SA, Bt, SB, out=None, *, config: int = -1, stream=None, handle=None):
+    """Block-scaled C = ReLU(A . Bt^T) (fp16 out) for element codes A (M, K)
+    and Bt (N, K) (``fmt`` "e4m3", "e5m2", or "e2m1" with two codes per byte,
+    so the uint8 tensors are (M, K/2) and (N, K/2)) and E8M0 scale bytes SA
+    (M, K/32), SB (N, K/32), all uint8 on the GPU. ``config`` forces a tile
+    configuration (0: 256 x 256, 1: 128 x 128)."""
+    import torch
+
+    f = _mx_format(fmt)
+    per = 2 if f == _native.TLG_MX_E2M1 else 1
+    lda, ldb = _mx_ld(A, "A", per), _mx_ld(Bt, "Bt", per)
+    ldsa, ldsb = _mx_ld(SA, "SA", 1), _mx_ld(SB, "SB", 1)
+    M, K = A.shape[0], A.shape[1] * per
+    N = Bt.shape[0]
+    if Bt.shape[1] * per != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {Bt.shape[1] * per}")
+    if tuple(SA.shape) != (M, K // 32) or tuple(SB.shape) != (N, K // 32):
+        raise ValueError("scale tensors must be (M, K/32) and (N, K/32)")
+    out = _out_for(out, M, N, A.device)
+    h = handle if handle is not None else handle_for(A.device)
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    with torch.cuda.device(A.device):
+        st = _native.tlg_gemm_relu_mx_variant(h.ptr, config, f, M, N, K, A.data_ptr(), lda, SA.data_ptr(), ldsa,
+                                              Bt.data_ptr(), ldb, SB.data_ptr(), ldsb, out.data_ptr(), _ld(out),
+                                              s.cuda_stream)
+    if st != _native.TLG_SUCCESS:
+        raise TlgError(st, "tlg_gemm_relu_mx")
+    return out
+
+
+def plan_mx(fmt, M, N, K, *, config: int = -1, lda=None, ldb=None, ldsa=None, ldsb=None, ldc=None,
+            aligned: bool = True) -> dict:
+    """What gemm_relu_mx would launch (host logic only). Pointers are stand-ins,
+    16-byte aligned when ``aligned`` else only 2-byte aligned."""
+    f = _mx_format(fmt)
+    lda = max(1, K) if lda is None else lda
+    ldb = max(1, K) if ldb is None else ldb
+    ldsa = max(1, K // 32) if ldsa is None else ldsa
+    ldsb = max(1, K // 32) if ldsb is None else ldsb
+    ldc = max(1, N) if ldc is None else ldc
+    base = 1 << 20 if aligned else (1 << 20) + 2
+    st, info = _native.tlg_plan_mx(f, M, N, K, base, lda, 1 << 20, ldsa, base, ldb, 1 << 20, ldsb, base, ldc, config)
+    if st != _native.TLG_SUCCESS:
+        raise TlgError(st, "tlg_plan_mx")
+    d = info.as_dict()
+    d["variant_name"] = _native.VARIANT_NAMES.get(info.variant, "?")
+    d["config_name"] = _native.tlg_plan_mx_config_name(info.config) if info.variant == TLG_VARIANT_TILED_DMA else ""
     return d

@@ -47,6 +47,13 @@ class tlg_plan_info(ctypes.Structure):
 
 TLG_GROUP_MAX = 16
 
+# tlg_mx_format
+TLG_MX_E4M3 = 1
+TLG_MX_E5M2 = 2
+TLG_MX_E2M1 = 3
+TLG_MX_BLOCK = 32
+MX_FORMATS = {"e4m3": TLG_MX_E4M3, "e5m2": TLG_MX_E5M2, "e2m1": TLG_MX_E2M1}
+
 
 class tlg_gemm_desc(ctypes.Structure):
     _fields_ = [
@@ -108,6 +115,16 @@ def lib():
         L.tlg_gemm_relu_grouped.restype = i32
         L.tlg_gemm_relu_grouped_variant.argtypes = [p, i32, i32, ctypes.POINTER(tlg_gemm_desc), i32, p]
         L.tlg_gemm_relu_grouped_variant.restype = i32
+        L.tlg_gemm_relu_mx.argtypes = [p, i32, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i64, p]
+        L.tlg_gemm_relu_mx.restype = i32
+        L.tlg_gemm_relu_mx_variant.argtypes = [p, i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i64,
+                                               p]
+        L.tlg_gemm_relu_mx_variant.restype = i32
+        L.tlg_plan_mx.argtypes = [i32, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i64, i32,
+                                  ctypes.POINTER(tlg_plan_info)]
+        L.tlg_plan_mx.restype = i32
+        L.tlg_plan_mx_config_name.argtypes = [i32]
+        L.tlg_plan_mx_config_name.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -193,3 +210,23 @@ def tlg_status_string(status: int) -> str:
 
 def tlg_version() -> int:
     return int(lib().tlg_version())
+
+
+def tlg_gemm_relu_mx(h, fmt, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc, stream) -> int:
+    return lib().tlg_gemm_relu_mx(h, fmt, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc, stream)
+
+
+def tlg_gemm_relu_mx_variant(h, config, fmt, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc, stream) -> int:
+    return lib().tlg_gemm_relu_mx_variant(h, config, fmt, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc,
+                                          stream)
+
+
+def tlg_plan_mx(fmt, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc, config=-1):
+    """Returns (status, tlg_plan_info)."""
+    info = tlg_plan_info()
+    st = lib().tlg_plan_mx(fmt, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc, config, ctypes.byref(info))
+    return st, info
+
+
+def tlg_plan_mx_config_name(config: int) -> str:
+    return lib().tlg_plan_mx_config_name(config).decode()

@@ -463,6 +463,99 @@ tlg_status run_grouped(tlg_handle h, int32_t config, int32_t count, const tlg_ge
     return tlg::launch_tiled_dma_grouped(cfg, ps, n, stream) == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
 }
 
+// ---- block-scaled (MX) calls ----
+
+int mx_codes_per_byte(int32_t format) { return format == TLG_MX_E2M1 ? 2 : 1; }
+
+tlg_status check_args_mx(int32_t format, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SA,
+                         int64_t ldsa, const void *B, int64_t ldb, const void *SB, int64_t ldsb, const void *C,
+                         int64_t ldc) {
+    if (format != TLG_MX_E4M3 && format != TLG_MX_E5M2 && format != TLG_MX_E2M1) return TLG_ERROR_INVALID_VALUE;
+    if (M < 0 || N < 0 || K < 0 || K % TLG_MX_BLOCK) return TLG_ERROR_INVALID_VALUE;
+    const int64_t kb = K / TLG_MX_BLOCK;
+    if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (N > 1 ? N : 1)) return TLG_ERROR_INVALID_VALUE;
+    if (ldsa < (kb > 1 ? kb : 1) || ldsb < (kb > 1 ? kb : 1)) return TLG_ERROR_INVALID_VALUE;
+    if (format == TLG_MX_E2M1 && (lda % 2 || ldb % 2)) return TLG_ERROR_INVALID_VALUE;
+    if (M == 0 || N == 0) return TLG_SUCCESS;
+    if (!C || !aligned(C, 2)) return TLG_ERROR_INVALID_VALUE;
+    if (K > 0 && (!A || !B || !SA || !SB)) return TLG_ERROR_INVALID_VALUE;
+    return TLG_SUCCESS;
+}
+
+tlg_status plan_mx(const tlg::MxProblem &p, int32_t config, tlg_plan_info *o) {
+    if (config < -1 || config >= tlg::MX_CONFIGS) return TLG_ERROR_INVALID_VALUE;
+    if (p.M == 0 || p.N == 0) {
+        fill_info(o, TLG_VARIANT_NOOP, 0, nullptr, 1, 0, 0, 0);
+        return TLG_SUCCESS;
+    }
+    if (p.K == 0) {
+        fill_info(o, TLG_VARIANT_FILL_ZERO, 0, nullptr, 1, 1, ceil_div(p.M * p.N, 256 * 8), 0);
+        return TLG_SUCCESS;
+    }
+    // stages of 128 codes (four scale blocks): K a multiple of 128; 16-byte
+    // chunks wholly inside a row; scale dwords aligned
+    const int epb = mx_codes_per_byte(p.format);
+    if (p.K % 128 || p.M > kMaxDim || p.N > kMaxDim || p.K > kMaxDim) return TLG_ERROR_NOT_SUPPORTED;
+    if (!aligned(p.A, 16) || !aligned(p.B, 16) || (p.lda / epb) % 16 || (p.ldb / epb) % 16)
+        return TLG_ERROR_NOT_SUPPORTED;
+    if (!aligned(p.SA, 4) || !aligned(p.SB, 4) || p.ldsa % 4 || p.ldsb % 4) return TLG_ERROR_NOT_SUPPORTED;
+    const int64_t t256 = ceil_div(p.M, 256) * ceil_div(p.N, 256);
+    const int cfg = config >= 0 ? config : (t256 >= 128 ? tlg::MX_256x256_W8 : tlg::MX_128x128_W4);
+    const tlg::TileConfig &tc = tlg::kMxConfigs[cfg];
+    if ((int64_t)tc.bm * (p.lda / epb) + 128 > kMaxOffset || (int64_t)tc.bn * (p.ldb / epb) + 128 > kMaxOffset ||
+        (int64_t)tc.bm * p.ldsa > kMaxOffset || (int64_t)tc.bn * p.ldsb > kMaxOffset ||
+        (int64_t)tc.bm * p.ldc * 2 + (int64_t)tc.bn * 2 > kMaxOffset)
+        return TLG_ERROR_NOT_SUPPORTED;
+    const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
+    if (tiles > 0x7fffffff) return TLG_ERROR_NOT_SUPPORTED;
+    fill_info(o, TLG_VARIANT_TILED_DMA, cfg, &tc, 1, 1, tiles, 0);
+    o->block_k = tc.bk * epb;  // codes of K per stage
+    return TLG_SUCCESS;
+}
+
+tlg::MxProblem make_mx_problem(int32_t format, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                               const void *SA, int64_t ldsa, const void *B, int64_t ldb, const void *SB,
+                               int64_t ldsb, const void *C, int64_t ldc) {
+    tlg::MxProblem p;
+    p.format = format;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.A = A;
+    p.lda = lda;
+    p.SA = SA;
+    p.ldsa = ldsa;
+    p.B = B;
+    p.ldb = ldb;
+    p.SB = SB;
+    p.ldsb = ldsb;
+    p.C = const_cast<void *>(C);
+    p.ldc = ldc;
+    return p;
+}
+
+tlg_status run_mx(tlg_handle h, int32_t config, const tlg::MxProblem &p, hipStream_t stream) {
+    tlg_status st = device_ok(h);
+    if (st != TLG_SUCCESS) return st;
+    st = check_args_mx(p.format, p.M, p.N, p.K, p.A, p.lda, p.SA, p.ldsa, p.B, p.ldb, p.SB, p.ldsb, p.C, p.ldc);
+    if (st != TLG_SUCCESS) return st;
+    tlg_plan_info info;
+    st = plan_mx(p, config, &info);
+    if (st != TLG_SUCCESS) return st;
+    hipError_t e = hipSuccess;
+    switch (info.variant) {
+        case TLG_VARIANT_NOOP: return TLG_SUCCESS;
+        case TLG_VARIANT_FILL_ZERO: {
+            tlg::Problem z = make_problem(p.M, p.N, 0, nullptr, 1, nullptr, p.N, p.C, p.ldc);
+            e = tlg::launch_fill_zero(z, stream);
+            break;
+        }
+        case TLG_VARIANT_TILED_DMA: e = tlg::launch_mx(info.config, p, stream); break;
+        default: return TLG_ERROR_NOT_SUPPORTED;
+    }
+    return e == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -609,6 +702,32 @@ tlg_status tlg_gemm_relu_grouped(tlg_handle h, int32_t count, const tlg_gemm_des
 tlg_status tlg_gemm_relu_grouped_variant(tlg_handle h, int32_t config, int32_t count, const tlg_gemm_desc *descs,
                                          int32_t trans_b, hipStream_t stream) {
     return run_grouped(h, config, count, descs, trans_b, stream);
+}
+
+tlg_status tlg_gemm_relu_mx(tlg_handle h, int32_t format, int64_t M, int64_t N, int64_t K, const void *A,
+                            int64_t lda, const void *SA, int64_t ldsa, const void *B, int64_t ldb, const void *SB,
+                            int64_t ldsb, void *C, int64_t ldc, hipStream_t stream) {
+    return run_mx(h, -1, make_mx_problem(format, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc), stream);
+}
+
+tlg_status tlg_gemm_relu_mx_variant(tlg_handle h, int32_t config, int32_t format, int64_t M, int64_t N, int64_t K,
+                                    const void *A, int64_t lda, const void *SA, int64_t ldsa, const void *B,
+                                    int64_t ldb, const void *SB, int64_t ldsb, void *C, int64_t ldc,
+                                    hipStream_t stream) {
+    return run_mx(h, config, make_mx_problem(format, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc), stream);
+}
+
+tlg_status tlg_plan_mx(int32_t format, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SA,
+                       int64_t ldsa, const void *B, int64_t ldb, const void *SB, int64_t ldsb, const void *C,
+                       int64_t ldc, int32_t config, tlg_plan_info *out) {
+    if (!out) return TLG_ERROR_INVALID_VALUE;
+    tlg_status st = check_args_mx(format, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc);
+    if (st != TLG_SUCCESS) return st;
+    return plan_mx(make_mx_problem(format, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc), config, out);
+}
+
+const char *tlg_plan_mx_config_name(int32_t config) {
+    return (config >= 0 && config < tlg::MX_CONFIGS) ? tlg::kMxConfigs[config].name : "";
 }
 
 }  // extern "C"

@@ -86,6 +86,28 @@ hipError_t launch_streamk(const Problem &p, int grid, float *partials, int *coun
 // 32 x 64 fp32) and `counters` (one int per strip, zero on entry and exit).
 extern const TileConfig kStripConfig;
 hipError_t launch_skinny_strip(const Problem &p, int parts, float *partials, int *counters, hipStream_t stream);
+// Block-scaled (MX) problem: A (M x K codes) and B (N x K codes, i.e. B
+// transposed), their scale bytes (M x K/32, N x K/32), fp16 C. Leading
+// dimensions of A and B in elements (codes), of the scales in bytes, of C
+// in elements. format: 1 E4M3, 2 E5M2, 3 E2M1 (two codes per byte).
+struct MxProblem {
+    int format;
+    int64_t M, N, K;
+    const void *A;
+    int64_t lda;
+    const void *SA;
+    int64_t ldsa;
+    const void *B;
+    int64_t ldb;
+    const void *SB;
+    int64_t ldsb;
+    void *C;
+    int64_t ldc;
+};
+enum MxConfig { MX_256x256_W8 = 0, MX_128x128_W4 = 1, MX_CONFIGS = 2 };
+extern const TileConfig kMxConfigs[MX_CONFIGS];  // bk: bytes of K per stage and row
+hipError_t launch_mx(int config, const MxProblem &p, hipStream_t stream);
+
 hipError_t launch_naive(const Problem &p, hipStream_t stream);
 hipError_t launch_fill_zero(const Problem &p, hipStream_t stream);
 

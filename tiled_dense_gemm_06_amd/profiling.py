@@ -131,6 +131,7 @@ def measured_traffic(workload: str, config: str):
 
 PEAK_MFMA_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
+PEAK_MX_TFLOPS = {"e4m3": 5000.0, "e5m2": 5000.0, "e2m1": 10100.0}  # dense block-scaled MFMA
 
 
 def _stats_rows(trace_dir: str):
@@ -142,6 +143,14 @@ def summary(args) -> str:
     from . import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
+    # block-scaled (--mx): codes of 1 or 1/2 byte, one scale byte per 32 k, fp16 C
+    if args.mx:
+        bits = 4 if args.mx == "e2m1" else 8
+        alg_bytes = (w.M + w.N) * w.K * bits // 8 + (w.M + w.N) * (w.K // 32) + 2 * w.M * w.N
+        peak, peak_name = PEAK_MX_TFLOPS[args.mx], f"{args.mx} block-scaled dense"
+        what = f"{args.mx} codes of A and B, their scale bytes and fp16 C once"
+    else:
+        alg_bytes, peak, peak_name, what = w.alg_bytes, PEAK_MFMA_TFLOPS, "fp16 dense", "A, B and C once"
     rows = _stats_rows(args.trace)
     main = [r for r in rows if args.kernel in r["Name"]]
     if not main:
@@ -158,10 +167,10 @@ def summary(args) -> str:
     if args.note:
         lines += [args.note, ""]
     tflops = w.flop / (avg_ns * 1e-9) / 1e12
-    gbs = w.alg_bytes / (avg_ns * 1e-9) / 1e9
+    gbs = alg_bytes / (avg_ns * 1e-9) / 1e9
     lines.append(f"From the trace average ({avg_ns / 1e3:,.1f} us per launch): {tflops:,.1f} TFLOP/s "
-                 f"({100 * tflops / PEAK_MFMA_TFLOPS:.1f} % of the {PEAK_MFMA_TFLOPS} TFLOP/s fp16 dense peak), "
-                 f"{gbs:,.0f} GB/s of algorithmic bytes ({w.alg_bytes:,} B: A, B and C once; "
+                 f"({100 * tflops / peak:.1f} % of the {peak} TFLOP/s {peak_name} peak), "
+                 f"{gbs:,.0f} GB/s of algorithmic bytes ({alg_bytes:,} B: {what}; "
                  f"{100 * gbs / PEAK_HBM_GBS:.1f} % of {PEAK_HBM_GBS:.0f} GB/s).")
     lines.append("")
     if args.fetch:
@@ -177,9 +186,9 @@ def summary(args) -> str:
                   f"(`python3 bench.py --copy-calibration {args.copy_mib} --steps 3 --warmup 1` under each "
                   f"counter): fetch factor {ff:.4f}, write factor {wf:.4f}.", "",
                   "| per launch | bytes | x algorithmic |", "|---|---|---|",
-                  f"| fetched from beyond L2 | {fetch:,.0f} | {fetch / w.alg_bytes:.2f} |",
-                  f"| written | {write:,.0f} | {write / w.alg_bytes:.2f} |",
-                  f"| total (`traffic`) | {fetch + write:,.0f} | {(fetch + write) / w.alg_bytes:.2f} |", ""]
+                  f"| fetched from beyond L2 | {fetch:,.0f} | {fetch / alg_bytes:.2f} |",
+                  f"| written | {write:,.0f} | {write / alg_bytes:.2f} |",
+                  f"| total (`traffic`) | {fetch + write:,.0f} | {(fetch + write) / alg_bytes:.2f} |", ""]
     text = "\n".join(lines)
     with open(args.out, "w") as f:
         f.write(text)
@@ -211,6 +220,7 @@ def main():
     m.add_argument("--copy-write")
     m.add_argument("--copy-mib", type=int, default=512)
     m.add_argument("--counter-cmd", default="")
+    m.add_argument("--mx", choices=sorted(PEAK_MX_TFLOPS), help="the block-scaled path with these codes")
     m.add_argument("--out", required=True)
     args = ap.parse_args()
     if args.cmd == "traffic":
