@@ -58,7 +58,8 @@ typedef enum {
     TLG_VARIANT_TILED_GENERAL = 4, /* MFMA tiles fed through registers; any alignment and leading dimension */
     TLG_VARIANT_SPLITK = 5,        /* skinny M: K split across work-groups, fp32 partials, then an ordered reduce + ReLU + cast */
     TLG_VARIANT_NAIVE = 6,         /* one thread per output, sequential k; for cross-checks only, never chosen automatically */
-    TLG_VARIANT_TILED_PIPE = 7     /* MFMA tiles fed by direct global->LDS loads, loads and LDS reads slotted between MFMAs; aligned, large problems */
+    TLG_VARIANT_TILED_PIPE = 7,    /* MFMA tiles fed by direct global->LDS loads, loads and LDS reads slotted between MFMAs; aligned, large problems */
+    TLG_VARIANT_PINGPONG = 8       /* wave-role schedule: two groups of waves alternate loads + LDS reads and MFMAs (forced only) */
 } tlg_variant;
 
 /* What tlg_gemm_relu will launch for a given problem (pure host logic). */

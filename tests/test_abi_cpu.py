@@ -247,3 +247,19 @@ def test_plan_block_scaled():
     st, _ = nat.tlg_plan_mx(7, 64, 64, 256, 1 << 20, 256, 1 << 20, 8, 1 << 20, 256, 1 << 20, 8, 1 << 20, 64)
     assert st == INV
     assert nat.tlg_plan_mx_config_name(0) == "mx_256x256_w2x4_s2" and nat.tlg_plan_mx_config_name(2) == ""
+
+
+def test_plan_pingpong_forced_only():
+    p = tlg.plan(8192, 8192, 8192, variant=tlg.TLG_VARIANT_PINGPONG)
+    assert p["variant_name"] == "pingpong" and p["config_name"] == "pingpong_256x256x32_w2x4_s4"
+    assert p["grid"] == 32 * 32 and p["threads"] == 512 and p["block_k"] == 32
+    assert tlg.plan(8192, 8192, 8192)["variant_name"] == "tiled_pipe"  # not the default
+    assert tlg.plan(301, 259, 203, variant=tlg.TLG_VARIANT_PINGPONG, trans_b=True)["grid"] == 2 * 2
+    assert tlg.plan(300, 300, 301, aligned=False, variant=tlg.TLG_VARIANT_PINGPONG)["grid"] == 4
+    with pytest.raises(tlg.TlgError):
+        tlg.plan(300, 7, 300, variant=tlg.TLG_VARIANT_PINGPONG)  # ldb < 8 with N % 8 != 0
+    with pytest.raises(tlg.TlgError):
+        tlg.plan(512, 512, 512, variant=tlg.TLG_VARIANT_PINGPONG, config=1)
+    assert tlg.tlg_plan_config_name(tlg.TLG_VARIANT_PINGPONG, 0) == "pingpong_256x256x32_w2x4_s4"
+    with pytest.raises(tlg.TlgError):
+        tlg.plan(64, 64, 64, variant=tlg.TLG_VARIANT_PINGPONG + 1)

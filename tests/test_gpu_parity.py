@@ -246,6 +246,32 @@ def test_pipe_configs(dev, config, shape):
     assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
 
 
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("shape", [(300, 264, 200), (513, 520, 72), (1024, 1032, 1000), (256, 256, 8),
+                                   (301, 259, 203), (512, 512, 32), (512, 512, 64), (512, 256, 96), (2, 8, 4104)])
+def test_pingpong(dev, shape, trans_b):
+    """The wave-role (ping-pong) schedule: ragged M and N, K tails inside a
+    stage, K of one, two and three stages (fewer than the pipeline depth),
+    long K, B given either way. Integer inputs: exact; C prefilled with NaN
+    and padded, the padding untouched. Then uniform inputs within the
+    tolerance on the same shape."""
+    M, N, K = shape
+    print(f"pingpong {shape} trans_b={trans_b}", flush=True)
+    A, B = wl.make_random(M, N, K, seed=M ^ N ^ K, kind="integer_pos")
+    ref = oracle.gemm_relu(A, B)
+    Bd = to_dev(np.ascontiguousarray(B.T) if trans_b else B, dev)
+    big = torch.full((M + 2, N + 8), float("nan"), dtype=torch.float16, device=dev)
+    tlg.gemm_relu(to_dev(A, dev), Bd, out=big[:M, :N], variant=tlg.TLG_VARIANT_PINGPONG, trans_b=trans_b)
+    torch.cuda.synchronize()
+    allb = bits(big)
+    assert np.array_equal(allb[:M, :N], ref)
+    assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+    A, B = wl.make_random(M, N, K, seed=M + N + K, kind="uniform")
+    Bd = to_dev(np.ascontiguousarray(B.T) if trans_b else B, dev)
+    got = bits(tlg.gemm_relu(to_dev(A, dev), Bd, variant=tlg.TLG_VARIANT_PINGPONG, trans_b=trans_b))
+    assert_close(got, oracle.gemm_relu(A, B), f"pingpong {shape} {trans_b}")
+
+
 @pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("shape", [(300, 264, 200), (513, 520, 72), (1024, 1032, 1000), (257, 8, 4104),
                                    (301, 259, 203)])

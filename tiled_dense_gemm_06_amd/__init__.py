@@ -11,7 +11,7 @@ from __future__ import annotations
 
 from . import _native
 from ._native import (  # noqa: F401  (re-exported C-ABI names)
-    TLG_VARIANT_AUTO, TLG_VARIANT_FILL_ZERO, TLG_VARIANT_NAIVE, TLG_VARIANT_NOOP,
+    TLG_VARIANT_AUTO, TLG_VARIANT_FILL_ZERO, TLG_VARIANT_NAIVE, TLG_VARIANT_NOOP, TLG_VARIANT_PINGPONG,
     TLG_VARIANT_SPLITK, TLG_VARIANT_TILED_DMA, TLG_VARIANT_TILED_GENERAL, TLG_VARIANT_TILED_PIPE, TlgError,
     tlg_arch_supported, tlg_check_args, tlg_plan, tlg_plan_config_name, tlg_status_string,
     tlg_version, tlg_workspace_bytes,

@@ -25,11 +25,13 @@ TLG_VARIANT_TILED_GENERAL = 4
 TLG_VARIANT_SPLITK = 5
 TLG_VARIANT_NAIVE = 6
 TLG_VARIANT_TILED_PIPE = 7
+TLG_VARIANT_PINGPONG = 8
 
 VARIANT_NAMES = {
     TLG_VARIANT_AUTO: "auto", TLG_VARIANT_NOOP: "noop", TLG_VARIANT_FILL_ZERO: "fill_zero",
     TLG_VARIANT_TILED_DMA: "tiled_dma", TLG_VARIANT_TILED_GENERAL: "tiled_general",
     TLG_VARIANT_SPLITK: "splitk", TLG_VARIANT_NAIVE: "naive", TLG_VARIANT_TILED_PIPE: "tiled_pipe",
+    TLG_VARIANT_PINGPONG: "pingpong",
 }
 
 

@@ -137,7 +137,7 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
                      tlg_plan_info *o, int64_t *k_split_out) {
     cap -= kCounterBytes;
     *k_split_out = 0;
-    if (variant < TLG_VARIANT_AUTO || variant > TLG_VARIANT_TILED_PIPE) return TLG_ERROR_INVALID_VALUE;
+    if (variant < TLG_VARIANT_AUTO || variant > TLG_VARIANT_PINGPONG) return TLG_ERROR_INVALID_VALUE;
     if (variant == TLG_VARIANT_AUTO && config >= 0) return TLG_ERROR_INVALID_VALUE;
     if (p.M == 0 || p.N == 0) {
         fill_info(o, TLG_VARIANT_NOOP, 0, nullptr, 1, 0, 0, 0);
@@ -157,6 +157,16 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
         if (ceil_div(p.M, 16) > 65535) return TLG_ERROR_NOT_SUPPORTED;
         fill_info(o, TLG_VARIANT_NAIVE, 0, nullptr, 1, 1, ceil_div(p.M, 16) * ceil_div(p.N, 16), 0);
         o->threads = 256;
+        return TLG_SUCCESS;
+    }
+
+    // the wave-role (ping-pong) schedule: forced only (see its measurements)
+    if (variant == TLG_VARIANT_PINGPONG) {
+        if (!config_ok(config, tlg::PINGPONG_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
+        const int cfg = config >= 0 ? config : tlg::PINGPONG_256x256x32;
+        const tlg::TileConfig &tc = tlg::kPingPongConfigs[cfg];
+        if (!dma_ok(p, tc.bm, tc.bn, tc.bk)) return TLG_ERROR_NOT_SUPPORTED;
+        fill_info(o, TLG_VARIANT_PINGPONG, cfg, &tc, 1, 1, ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn), 0);
         return TLG_SUCCESS;
     }
 
@@ -318,6 +328,7 @@ tlg_status run(tlg_handle h, int32_t variant, int32_t config, int32_t splits, co
         case TLG_VARIANT_TILED_DMA: e = tlg::launch_tiled_dma(info.config, p, stream); break;
         case TLG_VARIANT_TILED_GENERAL: e = tlg::launch_tiled_general(info.config, p, stream); break;
         case TLG_VARIANT_TILED_PIPE: e = tlg::launch_tiled_pipe(info.config, p, stream); break;
+        case TLG_VARIANT_PINGPONG: e = tlg::launch_pingpong(info.config, p, stream); break;
         case TLG_VARIANT_SPLITK: {
             float *partials = h->workspace + kCounterBytes / sizeof(float);
             if (info.config == tlg::SPLIT_WAVES_32x64x64)
@@ -365,7 +376,8 @@ int dma_config_by_tiles(int64_t t256, int64_t t128) {
 constexpr int kSquareDmaConfigs = 3;
 
 tlg_status plan_bt(const tlg::Problem &p, int32_t variant, int32_t config, tlg_plan_info *o) {
-    if (variant != TLG_VARIANT_AUTO && variant != TLG_VARIANT_TILED_DMA && variant != TLG_VARIANT_TILED_PIPE)
+    if (variant != TLG_VARIANT_AUTO && variant != TLG_VARIANT_TILED_DMA && variant != TLG_VARIANT_TILED_PIPE &&
+        variant != TLG_VARIANT_PINGPONG)
         return TLG_ERROR_INVALID_VALUE;
     if (variant == TLG_VARIANT_AUTO && config != -1) return TLG_ERROR_INVALID_VALUE;
     if (variant == TLG_VARIANT_TILED_DMA && (config < -1 || config >= kSquareDmaConfigs))
@@ -382,6 +394,14 @@ tlg_status plan_bt(const tlg::Problem &p, int32_t variant, int32_t config, tlg_p
         return TLG_SUCCESS;
     }
     const int64_t t256 = ceil_div(p.M, 256) * ceil_div(p.N, 256);
+    if (variant == TLG_VARIANT_PINGPONG) {
+        if (config < -1 || config >= tlg::PINGPONG_CONFIGS) return TLG_ERROR_INVALID_VALUE;
+        const int cfg = config >= 0 ? config : tlg::PINGPONG_256x256x32;
+        const tlg::TileConfig &tc = tlg::kPingPongConfigs[cfg];
+        if (!offsets_ok_bt(p, tc.bm, tc.bn)) return TLG_ERROR_NOT_SUPPORTED;
+        fill_info(o, TLG_VARIANT_PINGPONG, cfg, &tc, 1, 1, t256, 0);
+        return TLG_SUCCESS;
+    }
     if (variant == TLG_VARIANT_TILED_PIPE || (variant == TLG_VARIANT_AUTO && t256 >= 224)) {
         const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64_W8_A3;
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
@@ -422,6 +442,7 @@ tlg_status run_bt(tlg_handle h, int32_t variant, int32_t config, tlg::Problem p,
         case TLG_VARIANT_FILL_ZERO: e = tlg::launch_fill_zero(p, stream); break;
         case TLG_VARIANT_TILED_DMA: e = tlg::launch_tiled_dma(info.config, p, stream); break;
         case TLG_VARIANT_TILED_PIPE: e = tlg::launch_tiled_pipe(info.config, p, stream); break;
+        case TLG_VARIANT_PINGPONG: e = tlg::launch_pingpong(info.config, p, stream); break;
         default: return TLG_ERROR_NOT_SUPPORTED;
     }
     return e == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
@@ -596,6 +617,8 @@ const char *tlg_plan_config_name(int32_t variant, int32_t config) {
             return (config >= 0 && config < tlg::SPLIT_TWO_KERNEL_CONFIGS) ? tlg::kSplitConfigs[config].name : "";
         case TLG_VARIANT_TILED_PIPE:
             return (config >= 0 && config < tlg::PIPE_CONFIGS) ? tlg::kPipeConfigs[config].name : "";
+        case TLG_VARIANT_PINGPONG:
+            return (config >= 0 && config < tlg::PINGPONG_CONFIGS) ? tlg::kPingPongConfigs[config].name : "";
         case TLG_VARIANT_NAIVE: return "naive_16x16";
         case TLG_VARIANT_FILL_ZERO: return "fill_zero";
         case TLG_VARIANT_NOOP: return "noop";

@@ -56,7 +56,12 @@ enum PipeConfig {
     PIPE_CONFIGS = 5
 };
 
+// wave-role (ping-pong) schedule: two groups of waves alternate between
+// loads + fragment reads and MFMAs, slot by slot
+enum PingPongConfig { PINGPONG_256x256x32 = 0, PINGPONG_CONFIGS = 1 };
+
 extern const TileConfig kDmaConfigs[DMA_CONFIGS];
+extern const TileConfig kPingPongConfigs[PINGPONG_CONFIGS];
 extern const TileConfig kGenConfigs[GEN_CONFIGS];
 extern const TileConfig kSplitConfigs[SPLIT_TWO_KERNEL_CONFIGS];
 extern const TileConfig kPipeConfigs[PIPE_CONFIGS];
@@ -68,6 +73,7 @@ hipError_t launch_tiled_dma(int config, const Problem &p, hipStream_t stream);
 hipError_t launch_tiled_dma_grouped(int config, const Problem *ps, int count, hipStream_t stream);
 hipError_t launch_tiled_general(int config, const Problem &p, hipStream_t stream);
 hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream);
+hipError_t launch_pingpong(int config, const Problem &p, hipStream_t stream);
 // Stage 1 writes fp32 partials W[s][m][n] (M x N packed per split) for
 // splits s covering k in [s*k_split, (s+1)*k_split); stage 2 sums them in
 // ascending s, applies ReLU and the fp16 cast, and writes C.

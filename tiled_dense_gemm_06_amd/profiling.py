@@ -48,6 +48,7 @@ KERNEL_FILES = {
     "k_skinny_strip": "gemm_relu_skinny_gfx950.hip",
     "k_streamk": "gemm_relu_streamk_gfx950.hip",
     "k_mx": "gemm_relu_mx_gfx950.hip",
+    "k_pingpong": "gemm_relu_pingpong_gfx950.hip",
 }
 DEVICE_HEADERS = ["gfx950_ops.h", "tile_layout.h"]
 
