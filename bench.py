@@ -94,6 +94,8 @@ def bench_mx(args, torch, tlg, wl, dev) -> int:
     """The block-scaled path (tlg_gemm_relu_mx) on the workload's shape."""
     import numpy as np
 
+    from tiled_dense_gemm_06_amd.profiling import measured_traffic
+
     fmt = args.mx
     w = wl.WORKLOADS[args.workload]
     if w.K % 128:
@@ -143,7 +145,10 @@ def bench_mx(args, torch, tlg, wl, dev) -> int:
                    "kernel": plan["config_name"], "rotated_buffers": R, "alg_bytes": alg_bytes,
                    "accumulate": "f32", "epilogue": "relu, round-to-nearest-even to f16"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None, "kernel": plan["config_name"],
+                     "frac": achieved / peak,
+                     "traffic": measured_traffic(f"{w.name}_mx_{fmt}", plan["config_name"]) if args.config < 0
+                     else None,
+                     "kernel": plan["config_name"],
                      "launch_ms_avg": avg_launch_s * 1e3, "launch_ms_min": float(np.min(per_launch_ms))},
         "wall_s_timed": wall,
     }
