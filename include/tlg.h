@@ -164,7 +164,7 @@ int32_t tlg_version(void);
 /* C = ReLU(A . Bt^T): Bt is the N x K fp16 row-major matrix (B transposed),
  * ldbt >= max(1, K); everything else as tlg_gemm_relu. B's tiles are loaded
  * and read like A's: by the pipelined kernel when the problem has at least
- * 224 output tiles of 256 x 256, else by the direct-to-LDS tiled kernel (tile
+ * 128 output tiles of 256 x 256, else by the direct-to-LDS tiled kernel (tile
  * by tile count). TLG_ERROR_NOT_SUPPORTED when a tile's byte offsets exceed
  * 2 GB (e.g. ldbt * 256 * 2 >= 2^31); nothing is enqueued then. */
 tlg_status tlg_gemm_relu_bt(tlg_handle h, int64_t M, int64_t N, int64_t K,
