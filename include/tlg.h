@@ -269,7 +269,9 @@ tlg_status tlg_gemm_relu_mx(tlg_handle h, int32_t format, int64_t M, int64_t N, 
                             int64_t ldsb, void *C, int64_t ldc, hipStream_t stream);
 
 /* tlg_gemm_relu_mx with a forced tile configuration (-1: library's choice;
- * 0: 256 x 256 tiles, eight waves; 1: 128 x 128 tiles, four waves). */
+ * 0: 256 x 256 tiles, eight waves; 1: 128 x 128 tiles, four waves;
+ * 2: 256 x 256, eight waves, software-pipelined; 3: 256 x 256, four waves,
+ * software-pipelined, 8-bit codes only, else TLG_ERROR_NOT_SUPPORTED). */
 tlg_status tlg_gemm_relu_mx_variant(tlg_handle h, int32_t config, int32_t format, int64_t M, int64_t N, int64_t K,
                                     const void *A, int64_t lda, const void *SA, int64_t ldsa, const void *B,
                                     int64_t ldb, const void *SB, int64_t ldsb, void *C, int64_t ldc,

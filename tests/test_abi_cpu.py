@@ -234,7 +234,8 @@ def test_plan_block_scaled():
         (dict(fmt="e4m3", M=64, N=64, K=256, ldsa=9), NS),       # scale rows not whole dwords
         (dict(fmt="e4m3", M=64, N=64, K=256, ldsb=7), INV),      # scale rows shorter than K/32
         (dict(fmt="e4m3", M=64, N=64, K=256, lda=128), INV),     # lda < K
-        (dict(fmt="e4m3", M=64, N=64, K=256, config=2), INV),
+        (dict(fmt="e4m3", M=64, N=64, K=256, config=4), INV),
+        (dict(fmt="e2m1", M=64, N=64, K=256, config=3), NS),        # four-wave pipelined: 8-bit only
     ]
     for kw, status in cases:
         kw = dict(kw)
@@ -246,7 +247,7 @@ def test_plan_block_scaled():
         tlg.plan_mx("e3m2", 64, 64, 256)
     st, _ = nat.tlg_plan_mx(7, 64, 64, 256, 1 << 20, 256, 1 << 20, 8, 1 << 20, 256, 1 << 20, 8, 1 << 20, 64)
     assert st == INV
-    assert nat.tlg_plan_mx_config_name(0) == "mx_256x256_w2x4_s2" and nat.tlg_plan_mx_config_name(2) == ""
+    assert nat.tlg_plan_mx_config_name(0) == "mx_256x256_w2x4_s2" and nat.tlg_plan_mx_config_name(4) == ""
 
 
 def test_plan_pingpong_forced_only():

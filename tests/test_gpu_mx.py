@@ -85,7 +85,7 @@ def assert_mx_close(fmt, got, A, SA, Bt, SB, rows=None, what=""):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("config", [-1, 0, 1])
+@pytest.mark.parametrize("config", [-1, 0, 1, 2, 3])
 @pytest.mark.parametrize("shape", [(256, 256, 256), (300, 200, 384), (1, 8, 128), (129, 257, 512),
                                    (520, 264, 1152)])
 def test_mx_integer_exact(dev, fmt, config, shape):
@@ -93,6 +93,8 @@ def test_mx_integer_exact(dev, fmt, config, shape):
     fp32, so the fp16 results must equal the oracle's bit for bit. Ragged M
     and N (several tiles and a partial one), one row, K of 1 to 9 stages."""
     M, N, K = shape
+    if config == 3 and fmt == "e2m1":
+        pytest.skip("the four-wave pipelined configuration takes 8-bit codes only")
     print(f"mx exact {fmt} config={config} {shape}", flush=True)
     A, SA, Bt, SB = wl.make_mx_inputs(fmt, M, N, K, seed=M + 3 * N + 5 * K, kind="small_int")
     got = bits(run(fmt, A, SA, Bt, SB, dev, config))
@@ -100,12 +102,14 @@ def test_mx_integer_exact(dev, fmt, config, shape):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("config", [-1, 0, 1])
+@pytest.mark.parametrize("config", [-1, 0, 1, 2, 3])
 @pytest.mark.parametrize("shape", [(300, 264, 256), (513, 520, 1024), (256, 256, 128), (64, 1000, 2048)])
 def test_mx_random_scaled(dev, fmt, config, shape):
     """Random codes over a band of exponents (and zeros/subnormals) with
     random block scales 2^-2 .. 2^2: every element of C within the bound."""
     M, N, K = shape
+    if config == 3 and fmt == "e2m1":
+        pytest.skip("the four-wave pipelined configuration takes 8-bit codes only")
     print(f"mx random {fmt} config={config} {shape}", flush=True)
     A, SA, Bt, SB = wl.make_mx_inputs(fmt, M, N, K, seed=7 * M + N + K, kind="random")
     got = bits(run(fmt, A, SA, Bt, SB, dev, config))
@@ -125,7 +129,7 @@ def test_mx_scale_mapping_per_block(dev, fmt):
     SB = rng.integers(123, 132, size=(N, K // 32)).astype(np.uint8)
     ref = omx.gemm_relu_mx(fmt, A, SA, Bt, SB)
     assert np.all(np.isfinite(ref.view(np.float16)))
-    for config in (0, 1):
+    for config in (0, 1, 2) + ((3,) if fmt != "e2m1" else ()):
         got = bits(run(fmt, A, SA, Bt, SB, dev, config))
         assert np.array_equal(got, ref), (fmt, config)
 
@@ -146,7 +150,7 @@ def test_mx_padded_strides_and_untouched_padding(dev, fmt):
     SAp[:, :K // 32] = to_dev(SA, dev)
     SBp[:, :K // 32] = to_dev(SB, dev)
     big = torch.full((M + 3, N + 9), float("nan"), dtype=torch.float16, device=dev)
-    for config in (0, 1):
+    for config in (0, 1, 2) + ((3,) if fmt != "e2m1" else ()):
         big.fill_(float("nan"))
         tlg.gemm_relu_mx(fmt, Ap[:, :K // per], SAp[:, :K // 32], Bp[:, :K // per], SBp[:, :K // 32],
                          out=big[:M, :N], config=config)

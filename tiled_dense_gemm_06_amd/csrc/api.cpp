@@ -524,6 +524,9 @@ tlg_status plan_mx(const tlg::MxProblem &p, int32_t config, tlg_plan_info *o) {
     if (!aligned(p.SA, 4) || !aligned(p.SB, 4) || p.ldsa % 4 || p.ldsb % 4) return TLG_ERROR_NOT_SUPPORTED;
     const int64_t t256 = ceil_div(p.M, 256) * ceil_div(p.N, 256);
     const int cfg = config >= 0 ? config : (t256 >= 128 ? tlg::MX_256x256_W8 : tlg::MX_128x128_W4);
+    // the four-wave pipelined form holds 8-bit fragments only (4-bit ones
+    // would not stay in registers)
+    if (cfg == tlg::MX_PIPE_256x256_W4 && p.format == TLG_MX_E2M1) return TLG_ERROR_NOT_SUPPORTED;
     const tlg::TileConfig &tc = tlg::kMxConfigs[cfg];
     if ((int64_t)tc.bm * (p.lda / epb) + 128 > kMaxOffset || (int64_t)tc.bn * (p.ldb / epb) + 128 > kMaxOffset ||
         (int64_t)tc.bm * p.ldsa > kMaxOffset || (int64_t)tc.bn * p.ldsb > kMaxOffset ||

@@ -37,6 +37,9 @@ namespace tlg {
 
 typedef int int8v_t __attribute__((ext_vector_type(8)));
 
+// Nothing may be scheduled across this point (keeps the hand-written order).
+#define TLG_MX_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 struct MxArgs {
     const uint8_t *A;   // M x K codes, lda bytes per row
     const uint8_t *B;   // N x K codes (B transposed), ldb bytes per row
@@ -268,15 +271,257 @@ __global__ __launch_bounds__(S::NT) void k_mx(const MxArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Software-pipelined form: the slot program of the fp16 pipelined kernel
+// (one K step = KSTEPS*T MFMA slots, T = TM*TN tiles of the wave, H = T/2):
+// the first H slots finish the previous stage's last 64-deep step (tiles
+// H..T-1) while this stage's first fragments and its scale dwords are read;
+// each later step's fragments are read under the MFMAs of the step before;
+// the direct-to-LDS loads of the next stage (tiles and scales) go out every
+// SPACING slots; one vmcnt wait and one barrier per stage. Scales of the
+// stage being finished ("prev") and of the new one ("cur") are both held,
+// and cur becomes prev at the end of the step.
+// ---------------------------------------------------------------------------
+
+template <class S, int FMT>
+struct MxFrags {
+    int8v_t a[S::TM], b[S::TN];
+};
+
+template <class S, int FMT>
+struct MxScales {
+    uint32_t a[S::TM][MxShape<S, FMT>::SBR / 4], b[S::TN][MxShape<S, FMT>::SBR / 4];
+};
+
+// Reads of one 64-deep step J: 8-bit codes take two 16-byte reads per
+// fragment (r even: bytes 0..15, odd: 16..31), 4-bit codes one; fragments
+// in the order the MFMAs use them: b[0], a[0..TM-1], b[1..TN-1].
+template <class S, int FMT>
+constexpr int kMxFragReads = (FMT == 4 ? 1 : 2) * (S::TM + S::TN);
+
+template <class S, int FMT>
+__device__ __forceinline__ void mx_frag_read(MxFrags<S, FMT> &f, LDS_PTR(const char) sA, LDS_PTR(const char) sB,
+                                             int wm0, int wn0, int J, int lane, int r) {
+    constexpr bool B8 = FMT != 4;
+    constexpr int PER = B8 ? 2 : 1;
+    const int fi = r / PER, part = r % PER, half = lane / 32;
+    const bool is_a = fi >= 1 && fi < 1 + S::TM;
+    const int t = is_a ? fi - 1 : (fi == 0 ? 0 : fi - S::TM);
+    const int row = (is_a ? wm0 : wn0) + 32 * t + lane % 32;
+    const int chunk = B8 ? 4 * J + 2 * part + half : 2 * J + half;
+    const int4_t x = *(LDS_PTR(const int4_t))((is_a ? sA : sB) + lds_a_offset<S>(row, chunk));
+    int8v_t &d = is_a ? f.a[t] : f.b[t];
+    if (!B8) {
+        d = int8v_t{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+    } else if (part == 0) {
+        d[0] = x[0], d[1] = x[1], d[2] = x[2], d[3] = x[3];
+    } else {
+        d[4] = x[0], d[5] = x[1], d[6] = x[2], d[7] = x[3];
+    }
+}
+
+// Scale dwords of one row (A: r < TM) or column (B) of the wave for a stage,
+// shifted so that byte 0 is block l/32 of each 64-deep step pair.
+template <class S, int FMT>
+__device__ __forceinline__ void mx_scale_read(MxScales<S, FMT> &c, LDS_PTR(const char) st, int wm0, int wn0,
+                                              int lane, int r) {
+    using X = MxShape<S, FMT>;
+    const int sh = 8 * (lane / 32);
+    const bool is_a = r < S::TM;
+    const int t = is_a ? r : r - S::TM;
+    LDS_PTR(const char) base = st + S::STAGE_BYTES + (is_a ? 0 : X::SC_A) +
+                               ((is_a ? wm0 : wn0) + 32 * t + lane % 32) * X::SBR;
+    if (X::SBR == 4) {
+        const uint32_t v = *(LDS_PTR(const uint32_t))base;
+        (is_a ? c.a[t] : c.b[t])[0] = v >> sh;
+    } else {
+        const int2_t v = *(LDS_PTR(const int2_t))base;
+        (is_a ? c.a[t] : c.b[t])[0] = (uint32_t)v[0] >> sh;
+        (is_a ? c.a[t] : c.b[t])[X::SBR / 4 - 1] = (uint32_t)v[1] >> sh;
+    }
+}
+
+// MFMA tile i of 64-deep step J from fragments f and scales c.
+template <class S, int FMT>
+__device__ __forceinline__ void mx_mfma_tile(const MxFrags<S, FMT> &f, const MxScales<S, FMT> &c, int J, int i,
+                                             float16_t (&acc)[S::TN][S::TM]) {
+    constexpr bool B8 = FMT != 4;
+    const int tn = i / S::TM, tm = i % S::TM;
+    const int dw = B8 ? 0 : J / 2;
+    const int sb = (int)c.b[tn][dw], sa = (int)c.a[tm][dw];
+    if ((B8 ? J : J % 2) == 0)
+        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[tn], f.a[tm], acc[tn][tm], FMT, FMT, 0, sb,
+                                                                      0, sa);
+    else
+        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[tn], f.a[tm], acc[tn][tm], FMT, FMT, 2, sb,
+                                                                      2, sa);
+}
+
+template <class S, int FMT>
+__global__ __launch_bounds__(S::NT) void k_mx_pipe(const MxArgs a) {
+    using X = MxShape<S, FMT>;
+    constexpr int T = S::TM * S::TN, H = T / 2;
+    constexpr int KS = X::KSTEPS;
+    constexpr int READS = kMxFragReads<S, FMT>;
+    constexpr int SREADS = S::TM + S::TN;        // scale reads per stage
+    constexpr int R0 = READS + SREADS;           // reads under the first H slots
+    constexpr int PER0 = (R0 + H - 1) / H;       // ... per slot
+    constexpr int PER = (READS + T - 1) / T;     // reads per slot under a full step
+    constexpr int SLOTS = KS * T;
+    constexpr int LOADS = X::LOADS;
+    constexpr int SPACING = SLOTS >= 2 * LOADS + 2 ? 2 : 1;
+    constexpr int DOFF = 1;
+    static_assert(S::STAGES == 2 && KS % 2 == 0 && T % 2 == 0, "two stages; the last step uses f[1]");
+    static_assert(DOFF + (LOADS - 1) * SPACING < SLOTS, "loads must fit in one K step");
+    __shared__ __attribute__((aligned(1024))) char smem[S::STAGES * X::STAGE];
+    LDS_PTR(char) lds = (LDS_PTR(char))smem;
+    const int nwg = a.tiles_m * a.tiles_n;
+    int tm_idx, tn_idx;
+    grouped_tile(xcd_remap(blockIdx.x, nwg), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
+    const int m0 = tm_idx * S::BM, n0 = tn_idx * S::BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
+    const int nk = (a.K + X::KPS - 1) / X::KPS;
+    const int nkb = a.K / 32;
+
+    // load j of a stage: j < DMA_A an A chunk, then B chunks, then scale dwords
+    uint32_t off[LOADS];
+    int kin[LOADS];
+    bool ok[LOADS];
+#pragma unroll
+    for (int i = 0; i < S::DMA_A; ++i) {
+        const ChunkRef c = dma_a_chunk<S>(wave, i, lane);
+        off[i] = (uint32_t)(c.row * a.lda + 16 * c.chunk);
+        kin[i] = 16 * X::EPB * c.chunk;
+        ok[i] = m0 + c.row < a.M;
+    }
+#pragma unroll
+    for (int i = 0; i < S::DMA_B; ++i) {
+        const ChunkRef c = dma_a_chunk<S>(wave, i, lane);
+        off[S::DMA_A + i] = (uint32_t)(c.row * a.ldb + 16 * c.chunk);
+        kin[S::DMA_A + i] = 16 * X::EPB * c.chunk;
+        ok[S::DMA_A + i] = n0 + c.row < a.N;
+    }
+    const int slab0 = wave * X::SPW;
+    const bool sc_b = slab0 >= X::NSA;
+    const int64_t lds_s = sc_b ? a.ldsb : a.ldsa;
+    const int lim_s = sc_b ? a.N - n0 : a.M - m0;
+#pragma unroll
+    for (int i = 0; i < X::SPW; ++i) {
+        const int q = ((slab0 + i) % X::NSA) * 64 + lane;
+        const int row = q / (X::SBR / 4), d = q % (X::SBR / 4);
+        off[S::DMA_A + S::DMA_B + i] = (uint32_t)(row * lds_s + 4 * d);
+        kin[S::DMA_A + S::DMA_B + i] = 4 * d;  // blocks, not codes
+        ok[S::DMA_A + S::DMA_B + i] = row < lim_s;
+    }
+    auto dma = [&](int j, int kt) {
+        const int k0 = kt * X::KPS;
+        const int64_t k0b = k0 / X::EPB;
+        const int kb0 = k0 / 32;
+        LDS_PTR(char) st = lds + (kt & 1) * X::STAGE;
+        if (j < S::DMA_A) {
+            const int4_t r = make_srd(a.A + (int64_t)m0 * a.lda + k0b);
+            dma16(r, (uint32_t)(uintptr_t)(st + (wave * S::DMA_A + j) * 1024),
+                  ok[j] && k0 + kin[j] < a.K ? off[j] : kOOB);
+        } else if (j < S::DMA_A + S::DMA_B) {
+            const int4_t r = make_srd(a.B + (int64_t)n0 * a.ldb + k0b);
+            dma16(r, (uint32_t)(uintptr_t)(st + S::A_BYTES + (wave * S::DMA_B + j - S::DMA_A) * 1024),
+                  ok[j] && k0 + kin[j] < a.K ? off[j] : kOOB);
+        } else {
+            const int i = j - S::DMA_A - S::DMA_B;
+            const int4_t r = make_srd(sc_b ? a.SB + (int64_t)n0 * a.ldsb + kb0 : a.SA + (int64_t)m0 * a.ldsa + kb0);
+            dma4(r, (uint32_t)(uintptr_t)(st + S::STAGE_BYTES + (sc_b ? X::SC_A : 0) + ((slab0 + i) % X::NSA) * 256),
+                 ok[j] && kb0 + kin[j] < nkb ? off[j] : kOOB);
+        }
+    };
+
+    float16_t acc[S::TN][S::TM];
+#pragma unroll
+    for (int i = 0; i < S::TN; ++i)
+#pragma unroll
+        for (int j = 0; j < S::TM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    MxFrags<S, FMT> f[2];
+    MxScales<S, FMT> prev, cur;
+#pragma unroll
+    for (int t = 0; t < S::TN; ++t) {
+        f[1].b[t] = int8v_t{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int d = 0; d < X::SBR / 4; ++d) prev.b[t][d] = 0;
+    }
+#pragma unroll
+    for (int t = 0; t < S::TM; ++t) {
+        f[1].a[t] = int8v_t{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int d = 0; d < X::SBR / 4; ++d) prev.a[t][d] = 0;
+    }
+
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) dma(j, 0);
+    wait_vmcnt<0>();
+    barrier_lds();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        LDS_PTR(const char) st = lds + (kt & 1) * X::STAGE;
+        LDS_PTR(const char) sA = st;
+        LDS_PTR(const char) sB = st + S::A_BYTES;
+        TLG_MX_FENCE();
+#pragma unroll
+        for (int q = 0; q < SLOTS; ++q) {
+            if (q < H) {
+                mx_mfma_tile<S, FMT>(f[1], prev, KS - 1, H + q, acc);
+#pragma unroll
+                for (int r = PER0 * q; r < PER0 * q + PER0; ++r) {
+                    if (r < SREADS)
+                        mx_scale_read<S, FMT>(cur, st, wm0, wn0, lane, r);
+                    else if (r < R0)
+                        mx_frag_read<S, FMT>(f[0], sA, sB, wm0, wn0, 0, lane, r - SREADS);
+                }
+            } else if (q < H + (KS - 1) * T) {
+                const int ks = (q - H) / T, i = (q - H) % T;
+                mx_mfma_tile<S, FMT>(f[ks & 1], cur, ks, i, acc);
+#pragma unroll
+                for (int r = PER * i; r < PER * i + PER; ++r)
+                    if (r < READS) mx_frag_read<S, FMT>(f[(ks + 1) & 1], sA, sB, wm0, wn0, ks + 1, lane, r);
+            } else {
+                mx_mfma_tile<S, FMT>(f[1], cur, KS - 1, q - H - (KS - 1) * T, acc);
+            }
+            if (q >= DOFF && (q - DOFF) % SPACING == 0 && (q - DOFF) / SPACING < LOADS)
+                dma((q - DOFF) / SPACING, kt + 1);
+            TLG_MX_FENCE();
+        }
+        wait_vmcnt<0>();  // this wave's loads of stage kt+1 are in LDS
+        barrier_lds();    // ... and every wave's; stage kt is no longer read
+        prev = cur;
+    }
+#pragma unroll
+    for (int i = H; i < T; ++i) mx_mfma_tile<S, FMT>(f[1], prev, KS - 1, i, acc);
+
+    barrier_lds();
+    KArgs c{};
+    c.C = a.C;
+    c.M = a.M;
+    c.N = a.N;
+    c.ldc = a.ldc;
+    store_c_tile_lds<S>(c, m0, n0, wave, lane, acc, lds);
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 
 using Mx256 = TileShape<256, 256, 64, 2, 4, 2>;  // eight waves (two per SIMD), 128 x 64 each
 using Mx128 = TileShape<128, 128, 64, 2, 2, 3>;  // four waves, 64 x 64 each
 
+using Mx256w4 = TileShape<256, 256, 64, 2, 2, 2>;  // four waves, 128 x 128 each
+
 const TileConfig kMxConfigs[MX_CONFIGS] = {
     {256, 256, 128, Mx256::NT, Mx256::STAGES, "mx_256x256_w2x4_s2"},
     {128, 128, 128, Mx128::NT, Mx128::STAGES, "mx_128x128_w2x2_s3"},
+    {256, 256, 128, Mx256::NT, Mx256::STAGES, "mx_pipe_256x256_w2x4_s2"},
+    {256, 256, 128, Mx256w4::NT, Mx256w4::STAGES, "mx_pipe_256x256_w2x2_s2"},
 };
 
 template <class S, int FMT>
@@ -285,12 +530,26 @@ static hipError_t launch_mx_t(const MxArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <class S>
+template <class S, int FMT>
+static hipError_t launch_mx_pipe_t(const MxArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((k_mx_pipe<S, FMT>), dim3(a.tiles_m * a.tiles_n), dim3(S::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class S, int FMT, bool PIPE>
+static hipError_t launch_mx_kind(const MxArgs &a, hipStream_t stream) {
+    if constexpr (PIPE)
+        return launch_mx_pipe_t<S, FMT>(a, stream);
+    else
+        return launch_mx_t<S, FMT>(a, stream);
+}
+
+template <class S, bool PIPE>
 static hipError_t launch_mx_fmt(int hw_format, const MxArgs &a, hipStream_t stream) {
     switch (hw_format) {
-        case 0: return launch_mx_t<S, 0>(a, stream);
-        case 1: return launch_mx_t<S, 1>(a, stream);
-        case 4: return launch_mx_t<S, 4>(a, stream);
+        case 0: return launch_mx_kind<S, 0, PIPE>(a, stream);
+        case 1: return launch_mx_kind<S, 1, PIPE>(a, stream);
+        case 4: return launch_mx_kind<S, 4, PIPE>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -317,7 +576,12 @@ hipError_t launch_mx(int config, const MxProblem &p, hipStream_t stream) {
     a.tiles_m = (int)((p.M + tc.bm - 1) / tc.bm);
     a.tiles_n = (int)((p.N + tc.bn - 1) / tc.bn);
     a.group_m = 4;
-    return config == MX_256x256_W8 ? launch_mx_fmt<Mx256>(hw, a, stream) : launch_mx_fmt<Mx128>(hw, a, stream);
+    switch (config) {
+        case MX_256x256_W8: return launch_mx_fmt<Mx256, false>(hw, a, stream);
+        case MX_128x128_W4: return launch_mx_fmt<Mx128, false>(hw, a, stream);
+        case MX_PIPE_256x256_W8: return launch_mx_fmt<Mx256, true>(hw, a, stream);
+        default: return launch_mx_fmt<Mx256w4, true>(hw, a, stream);
+    }
 }
 
 }  // namespace tlg

@@ -110,7 +110,7 @@ struct MxProblem {
     void *C;
     int64_t ldc;
 };
-enum MxConfig { MX_256x256_W8 = 0, MX_128x128_W4 = 1, MX_CONFIGS = 2 };
+enum MxConfig { MX_256x256_W8 = 0, MX_128x128_W4 = 1, MX_PIPE_256x256_W8 = 2, MX_PIPE_256x256_W4 = 3, MX_CONFIGS = 4 };
 extern const TileConfig kMxConfigs[MX_CONFIGS];  // bk: bytes of K per stage and row
 hipError_t launch_mx(int config, const MxProblem &p, hipStream_t stream);
 
