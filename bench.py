@@ -112,9 +112,24 @@ def bench_mx(args, torch, tlg, wl, dev) -> int:
     h = tlg.handle_for(dev)
     stream = torch.cuda.current_stream(dev)
 
+    G = args.grouped
+    if G and not 2 <= G <= 16:
+        print("bench.py: --grouped takes 2 .. 16", file=sys.stderr)
+        return 2
+    rows = [(w.M * g // G, w.M * (g + 1) // G) for g in range(G)] if G else []
+    if G:  # the grouped call picks its tile by the blocks' total tile count
+        t256 = sum(-(-(r1 - r0) // 256) * -(-w.N // 256) for r0, r1 in rows)
+        gcfg = args.config if args.config >= 0 else (0 if t256 >= 128 else 1)
+        plan = {"config_name": tlg._native.tlg_plan_mx_config_name(gcfg)}
+
     def step(i):
         a, sa, b, sb = sets[i % R]
-        tlg.gemm_relu_mx(fmt, a, sa, b, sb, out=Cs[i % R], config=args.config, handle=h, stream=stream)
+        if G:
+            tlg.gemm_relu_mx_grouped(fmt, [a[r0:r1] for r0, r1 in rows], [sa[r0:r1] for r0, r1 in rows], [b] * G,
+                                     [sb] * G, [Cs[i % R][r0:r1] for r0, r1 in rows], config=args.config, handle=h,
+                                     stream=stream)
+        else:
+            tlg.gemm_relu_mx(fmt, a, sa, b, sb, out=Cs[i % R], config=args.config, handle=h, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -142,12 +157,12 @@ def bench_mx(args, torch, tlg, wl, dev) -> int:
         "dtype": fmt, "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "seed": w.seed,
                    "inputs": "random codes (exponents bias-3..bias+3, 1 in 16 zero/subnormal), scales 2^-2..2^2",
-                   "kernel": plan["config_name"], "rotated_buffers": R, "alg_bytes": alg_bytes,
+                   "kernel": plan["config_name"], "grouped": G, "rotated_buffers": R, "alg_bytes": alg_bytes,
                    "accumulate": "f32", "epilogue": "relu, round-to-nearest-even to f16"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak,
-                     "traffic": measured_traffic(f"{w.name}_mx_{fmt}", plan["config_name"]) if args.config < 0
-                     else None,
+                     "traffic": measured_traffic(f"{w.name}_mx_{fmt}", plan["config_name"])
+                     if args.config < 0 and not G else None,
                      "kernel": plan["config_name"],
                      "launch_ms_avg": avg_launch_s * 1e3, "launch_ms_min": float(np.min(per_launch_ms))},
         "wall_s_timed": wall,

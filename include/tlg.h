@@ -288,6 +288,41 @@ tlg_status tlg_plan_mx(int32_t format, int64_t M, int64_t N, int64_t K, const vo
 /* Name of a block-scaled tile configuration ("" if out of range). */
 const char *tlg_plan_mx_config_name(int32_t config);
 
+/* One problem of a grouped block-scaled call: the arguments of
+ * tlg_gemm_relu_mx (all problems of a call share the element format). */
+typedef struct {
+    int64_t M, N, K;
+    const void *A;
+    int64_t lda;
+    const void *SA;
+    int64_t ldsa;
+    const void *B;
+    int64_t ldb;
+    const void *SB;
+    int64_t ldsb;
+    void *C;
+    int64_t ldc;
+} tlg_mx_desc;
+
+/* Grouped block-scaled GEMM+ReLU with B transposed (the TileLang forum
+ * post's "Backend Coverage" milestone list names an MXFP8 grouped GEMM with
+ * block scaling and a transposed B): count (0 .. TLG_GROUP_MAX) independent
+ * problems, each as tlg_gemm_relu_mx, in ONE launch of the block-scaled
+ * kernel. The descriptor array is read on the host during the call (it may
+ * be freed afterwards); nothing is allocated. Every descriptor is checked as
+ * tlg_gemm_relu_mx checks its arguments (TLG_ERROR_INVALID_VALUE /
+ * TLG_ERROR_NOT_SUPPORTED); any failure enqueues nothing. Problems with
+ * M == 0 or N == 0 are skipped; K == 0 problems are not accepted here
+ * (TLG_ERROR_NOT_SUPPORTED). The C windows must not overlap each other or
+ * any input. */
+tlg_status tlg_gemm_relu_mx_grouped(tlg_handle h, int32_t format, int32_t count, const tlg_mx_desc *descs,
+                                    hipStream_t stream);
+
+/* tlg_gemm_relu_mx_grouped with a forced tile configuration (-1: library's
+ * choice by total tile count; 0: 256 x 256; 1: 128 x 128). */
+tlg_status tlg_gemm_relu_mx_grouped_variant(tlg_handle h, int32_t config, int32_t format, int32_t count,
+                                            const tlg_mx_desc *descs, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

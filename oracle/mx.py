@@ -159,3 +159,8 @@ def gemm_relu_mx_rows(fmt, A, SA, Bt, SB, rows, threads=None) -> np.ndarray:
     """Rows ``rows`` of the result: a (len(rows), N) uint16 array."""
     rows = np.asarray(rows, dtype=np.int64)
     return gemm_relu_mx(fmt, np.ascontiguousarray(A[rows]), np.ascontiguousarray(SA[rows]), Bt, SB, threads)
+
+
+def gemm_relu_mx_grouped(fmt, problems, threads=None) -> list:
+    """Each (A, SA, Bt, SB) problem of a grouped call on its own."""
+    return [gemm_relu_mx(fmt, A, SA, Bt, SB, threads) for A, SA, Bt, SB in problems]

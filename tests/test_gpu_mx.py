@@ -200,3 +200,43 @@ def test_mx_square8192_sampled(dev, fmt):
     rows = np.array([0, 1, 255, 256, 4095, 4096, 8190, 8191] +
                     np.random.default_rng(5).choice(M, 8, replace=False).tolist())
     assert_mx_close(fmt, got, A, SA, Bt, SB, rows=rows, what=f"square8192 {fmt}")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("config", [-1, 0, 1])
+def test_mx_grouped(dev, fmt, config):
+    """Several block-scaled problems of different shapes (ragged M and N,
+    K of 1 to 5 stages, one empty) in one launch: integer codes with block
+    scales 2^-4..2^4 (every sum exact in fp32, so bit-exact), each problem
+    against the oracle on its own; C prefilled with NaN, padding untouched."""
+    shapes = [(300, 264, 256), (1, 8, 128), (129, 520, 640), (0, 64, 128), (256, 256, 384), (70, 33, 128)]
+    rng = np.random.default_rng(17)
+    probs = []
+    for i, (M, N, K) in enumerate(shapes):
+        A, _, Bt, _ = wl.make_mx_inputs(fmt, M, N, K, seed=40 + i, kind="small_int")
+        SA = rng.integers(123, 132, size=(M, K // 32)).astype(np.uint8)
+        SB = rng.integers(123, 132, size=(N, K // 32)).astype(np.uint8)
+        probs.append((A, SA, Bt, SB))
+    refs = omx.gemm_relu_mx_grouped(fmt, probs)
+    bigs = [torch.full((M + 1, N + 8), float("nan"), dtype=torch.float16, device=dev) for M, N, _ in shapes]
+    outs = [b[:M, :N] for b, (M, N, _) in zip(bigs, shapes)]
+    dev_in = [[to_dev(x, dev) for x in p] for p in probs]
+    tlg.gemm_relu_mx_grouped(fmt, *[[p[j] for p in dev_in] for j in range(4)], outs=outs, config=config)
+    torch.cuda.synchronize()
+    for (M, N, K), b, ref in zip(shapes, bigs, refs):
+        allb = bits(b)
+        assert np.array_equal(allb[:M, :N], ref), (fmt, config, (M, N, K))
+        assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+
+
+def test_mx_grouped_rejects_bad_calls(dev):
+    A, SA, Bt, SB = (to_dev(x, dev) for x in wl.make_mx_inputs("e4m3", 64, 64, 256, seed=1))
+    with pytest.raises(ValueError):
+        tlg.gemm_relu_mx_grouped("e4m3", [A] * 17, [SA] * 17, [Bt] * 17, [SB] * 17)
+    with pytest.raises(tlg.TlgError) as e:  # one problem with K % 128 != 0 fails the whole call
+        tlg.gemm_relu_mx_grouped("e4m3", [A, A[:, :96]], [SA, SA[:, :3]], [Bt, Bt[:, :96]], [SB, SB[:, :3]])
+    assert e.value.status == tlg._native.TLG_ERROR_NOT_SUPPORTED
+    assert tlg.gemm_relu_mx_grouped("e4m3", [], [], [], []) == []
+    st = tlg._native.tlg_gemm_relu_mx_grouped_variant(tlg.handle_for(dev).ptr, 2, tlg._native.TLG_MX_E4M3, [],
+                                                      torch.cuda.current_stream().cuda_stream)
+    assert st == tlg._native.TLG_ERROR_INVALID_VALUE

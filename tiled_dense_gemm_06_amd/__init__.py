@@ -17,7 +17,8 @@ from ._native import (  # noqa: F401  (re-exported C-ABI names)
     tlg_version, tlg_workspace_bytes,
 )
 
-__all__ = ["gemm_relu", "gemm_relu_grouped", "gemm_relu_mx", "Handle", "handle_for", "plan", "plan_mx"]
+__all__ = ["gemm_relu", "gemm_relu_grouped", "gemm_relu_mx", "gemm_relu_mx_grouped", "Handle", "handle_for", "plan",
+           "plan_mx"]
 
 
 class Handle:
@@ -238,6 +239,46 @@ def gemm_relu_mx(fmt, A, SA, Bt, SB, out=None, *, config: int = -1, stream=None,
     if st != _native.TLG_SUCCESS:
         raise TlgError(st, "tlg_gemm_relu_mx")
     return out
+
+
+def gemm_relu_mx_grouped(fmt, As, SAs, Bts, SBs, outs=None, *, config: int = -1, stream=None, handle=None):
+    """Up to 16 block-scaled problems (arguments as gemm_relu_mx, one format)
+    in one launch; returns the list of fp16 C_i."""
+    import torch
+
+    f = _mx_format(fmt)
+    per = 2 if f == _native.TLG_MX_E2M1 else 1
+    n = len(As)
+    if not (len(SAs) == len(Bts) == len(SBs) == n) or (outs is not None and len(outs) != n):
+        raise ValueError("As, SAs, Bts, SBs and outs differ in length")
+    if n > _native.TLG_GROUP_MAX:
+        raise ValueError(f"at most {_native.TLG_GROUP_MAX} problems per call")
+    if n == 0:
+        return []
+    dev = As[0].device
+    descs, res = [], []
+    for i in range(n):
+        A, SA, Bt, SB = As[i], SAs[i], Bts[i], SBs[i]
+        if any(t.device != dev for t in (A, SA, Bt, SB)):
+            raise ValueError("all operands must be on one device")
+        lda, ldb = _mx_ld(A, "A", per), _mx_ld(Bt, "Bt", per)
+        ldsa, ldsb = _mx_ld(SA, "SA", 1), _mx_ld(SB, "SB", 1)
+        M, K, N = A.shape[0], A.shape[1] * per, Bt.shape[0]
+        if Bt.shape[1] * per != K:
+            raise ValueError(f"problem {i}: inner dimensions differ")
+        if tuple(SA.shape) != (M, K // 32) or tuple(SB.shape) != (N, K // 32):
+            raise ValueError(f"problem {i}: scale tensors must be (M, K/32) and (N, K/32)")
+        C = _out_for(None if outs is None else outs[i], M, N, dev)
+        res.append(C)
+        descs.append((M, N, K, A.data_ptr(), lda, SA.data_ptr(), ldsa, Bt.data_ptr(), ldb, SB.data_ptr(), ldsb,
+                      C.data_ptr(), _ld(C)))
+    h = handle if handle is not None else handle_for(dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = _native.tlg_gemm_relu_mx_grouped_variant(h.ptr, config, f, descs, s.cuda_stream)
+    if st != _native.TLG_SUCCESS:
+        raise TlgError(st, "tlg_gemm_relu_mx_grouped")
+    return res
 
 
 def plan_mx(fmt, M, N, K, *, config: int = -1, lda=None, ldb=None, ldsa=None, ldsb=None, ldc=None,

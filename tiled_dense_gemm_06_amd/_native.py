@@ -66,6 +66,15 @@ class tlg_gemm_desc(ctypes.Structure):
     ]
 
 
+class tlg_mx_desc(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("SA", ctypes.c_void_p), ("ldsa", ctypes.c_int64),
+        ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64), ("SB", ctypes.c_void_p), ("ldsb", ctypes.c_int64),
+        ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64),
+    ]
+
+
 class TlgError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -125,6 +134,10 @@ def lib():
         L.tlg_plan_mx.argtypes = [i32, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i64, i32,
                                   ctypes.POINTER(tlg_plan_info)]
         L.tlg_plan_mx.restype = i32
+        L.tlg_gemm_relu_mx_grouped.argtypes = [p, i32, i32, ctypes.POINTER(tlg_mx_desc), p]
+        L.tlg_gemm_relu_mx_grouped.restype = i32
+        L.tlg_gemm_relu_mx_grouped_variant.argtypes = [p, i32, i32, i32, ctypes.POINTER(tlg_mx_desc), p]
+        L.tlg_gemm_relu_mx_grouped_variant.restype = i32
         L.tlg_plan_mx_config_name.argtypes = [i32]
         L.tlg_plan_mx_config_name.restype = ctypes.c_char_p
         _lib = L
@@ -232,3 +245,19 @@ def tlg_plan_mx(fmt, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc, config
 
 def tlg_plan_mx_config_name(config: int) -> str:
     return lib().tlg_plan_mx_config_name(config).decode()
+
+
+def _mx_descs(descs):
+    arr = (tlg_mx_desc * max(1, len(descs)))()
+    for i, d in enumerate(descs):
+        arr[i] = tlg_mx_desc(*d)
+    return arr
+
+
+def tlg_gemm_relu_mx_grouped(h, fmt, descs, stream) -> int:
+    """descs: (M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc) tuples."""
+    return lib().tlg_gemm_relu_mx_grouped(h, fmt, len(descs), _mx_descs(descs), stream)
+
+
+def tlg_gemm_relu_mx_grouped_variant(h, config, fmt, descs, stream) -> int:
+    return lib().tlg_gemm_relu_mx_grouped_variant(h, config, fmt, len(descs), _mx_descs(descs), stream)

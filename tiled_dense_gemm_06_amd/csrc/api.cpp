@@ -582,6 +582,41 @@ tlg_status run_mx(tlg_handle h, int32_t config, const tlg::MxProblem &p, hipStre
     return e == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
 }
 
+tlg_status run_mx_grouped(tlg_handle h, int32_t config, int32_t format, int32_t count, const tlg_mx_desc *descs,
+                          hipStream_t stream) {
+    tlg_status st = device_ok(h);
+    if (st != TLG_SUCCESS) return st;
+    if (count < 0 || count > TLG_GROUP_MAX) return TLG_ERROR_INVALID_VALUE;
+    if (config != -1 && config != tlg::MX_256x256_W8 && config != tlg::MX_128x128_W4) return TLG_ERROR_INVALID_VALUE;
+    if (format != TLG_MX_E4M3 && format != TLG_MX_E5M2 && format != TLG_MX_E2M1) return TLG_ERROR_INVALID_VALUE;
+    if (count == 0) return TLG_SUCCESS;
+    if (!descs) return TLG_ERROR_INVALID_VALUE;
+    tlg::MxProblem ps[TLG_GROUP_MAX];
+    int n = 0;
+    int64_t t256 = 0;
+    for (int i = 0; i < count; ++i) {
+        const tlg_mx_desc &d = descs[i];
+        st = check_args_mx(format, d.M, d.N, d.K, d.A, d.lda, d.SA, d.ldsa, d.B, d.ldb, d.SB, d.ldsb, d.C, d.ldc);
+        if (st != TLG_SUCCESS) return st;
+        if (d.M == 0 || d.N == 0) continue;
+        if (d.K == 0) return TLG_ERROR_NOT_SUPPORTED;
+        ps[n++] = make_mx_problem(format, d.M, d.N, d.K, d.A, d.lda, d.SA, d.ldsa, d.B, d.ldb, d.SB, d.ldsb, d.C,
+                                  d.ldc);
+        t256 += ceil_div(d.M, 256) * ceil_div(d.N, 256);
+    }
+    if (n == 0) return TLG_SUCCESS;
+    const int cfg = config >= 0 ? config : (t256 >= 128 ? tlg::MX_256x256_W8 : tlg::MX_128x128_W4);
+    int64_t tiles = 0;
+    for (int i = 0; i < n; ++i) {
+        tlg_plan_info info;
+        st = plan_mx(ps[i], cfg, &info);  // the single-problem checks (alignment, K % 128, offsets)
+        if (st != TLG_SUCCESS) return st;
+        tiles += info.grid;
+    }
+    if (tiles > 0x7fffffff) return TLG_ERROR_NOT_SUPPORTED;
+    return tlg::launch_mx_grouped(cfg, ps, n, stream) == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -752,6 +787,16 @@ tlg_status tlg_plan_mx(int32_t format, int64_t M, int64_t N, int64_t K, const vo
     tlg_status st = check_args_mx(format, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc);
     if (st != TLG_SUCCESS) return st;
     return plan_mx(make_mx_problem(format, M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, C, ldc), config, out);
+}
+
+tlg_status tlg_gemm_relu_mx_grouped(tlg_handle h, int32_t format, int32_t count, const tlg_mx_desc *descs,
+                                    hipStream_t stream) {
+    return run_mx_grouped(h, -1, format, count, descs, stream);
+}
+
+tlg_status tlg_gemm_relu_mx_grouped_variant(tlg_handle h, int32_t config, int32_t format, int32_t count,
+                                            const tlg_mx_desc *descs, hipStream_t stream) {
+    return run_mx_grouped(h, config, format, count, descs, stream);
 }
 
 const char *tlg_plan_mx_config_name(int32_t config) {

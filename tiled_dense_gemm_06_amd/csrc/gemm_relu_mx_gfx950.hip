@@ -160,15 +160,8 @@ __device__ __forceinline__ void mx_stage(LDS_PTR(const char) st, int wm0, int wn
 // scales; out-of-range rows, columns, k chunks and scale dwords read zeros
 // (a zero scale byte is 2^-127 and multiplies only zero codes there).
 template <class S, int FMT>
-__global__ __launch_bounds__(S::NT) void k_mx(const MxArgs a) {
+__device__ __forceinline__ void mx_tile(const MxArgs &a, int m0, int n0, LDS_PTR(char) lds) {
     using X = MxShape<S, FMT>;
-    __shared__ __attribute__((aligned(1024))) char smem[S::STAGES * X::STAGE];
-    LDS_PTR(char) lds = (LDS_PTR(char))smem;
-    const int nwg = a.tiles_m * a.tiles_n;
-    int tm_idx, tn_idx;
-    grouped_tile(xcd_remap(blockIdx.x, nwg), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
-    const int m0 = tm_idx * S::BM, n0 = tn_idx * S::BN;
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -268,6 +261,36 @@ __global__ __launch_bounds__(S::NT) void k_mx(const MxArgs a) {
     c.N = a.N;
     c.ldc = a.ldc;
     store_c_tile_lds<S>(c, m0, n0, wave, lane, acc, lds);
+}
+
+template <class S, int FMT>
+__global__ __launch_bounds__(S::NT) void k_mx(const MxArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[S::STAGES * MxShape<S, FMT>::STAGE];
+    const int nwg = a.tiles_m * a.tiles_n;
+    int tm_idx, tn_idx;
+    grouped_tile(xcd_remap(blockIdx.x, nwg), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
+    mx_tile<S, FMT>(a, tm_idx * S::BM, tn_idx * S::BN, (LDS_PTR(char))smem);
+}
+
+// Several independent block-scaled problems in one launch: work-group ids
+// are dealt to the XCDs as in the single-problem kernel, then split by
+// problem in order (tile_start holds the running tile counts).
+struct MxGroupArgs {
+    int count;
+    int tile_start[kGroupMax + 1];
+    MxArgs p[kGroupMax];
+};
+
+template <class S, int FMT>
+__global__ __launch_bounds__(S::NT) void k_mx_grouped(const MxGroupArgs g) {
+    __shared__ __attribute__((aligned(1024))) char smem[S::STAGES * MxShape<S, FMT>::STAGE];
+    const int v = xcd_remap(blockIdx.x, g.tile_start[g.count]);
+    int p = 0;
+    while (p + 1 < g.count && v >= g.tile_start[p + 1]) ++p;
+    const MxArgs &a = g.p[p];
+    int tm_idx, tn_idx;
+    grouped_tile(v - g.tile_start[p], a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
+    mx_tile<S, FMT>(a, tm_idx * S::BM, tn_idx * S::BN, (LDS_PTR(char))smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -554,11 +577,10 @@ static hipError_t launch_mx_fmt(int hw_format, const MxArgs &a, hipStream_t stre
     }
 }
 
-hipError_t launch_mx(int config, const MxProblem &p, hipStream_t stream) {
-    if (config < 0 || config >= MX_CONFIGS) return hipErrorInvalidValue;
-    const int hw = p.format == 1 ? 0 : p.format == 2 ? 1 : p.format == 3 ? 4 : -1;
-    const int epb = hw == 4 ? 2 : 1;
-    const TileConfig &tc = kMxConfigs[config];
+static int mx_hw_format(int format) { return format == 1 ? 0 : format == 2 ? 1 : format == 3 ? 4 : -1; }
+
+static MxArgs mx_args(const TileConfig &tc, const MxProblem &p) {
+    const int epb = mx_hw_format(p.format) == 4 ? 2 : 1;
     MxArgs a;
     a.A = (const uint8_t *)p.A;
     a.B = (const uint8_t *)p.B;
@@ -576,6 +598,46 @@ hipError_t launch_mx(int config, const MxProblem &p, hipStream_t stream) {
     a.tiles_m = (int)((p.M + tc.bm - 1) / tc.bm);
     a.tiles_n = (int)((p.N + tc.bn - 1) / tc.bn);
     a.group_m = 4;
+    return a;
+}
+
+template <class S, int FMT>
+static hipError_t launch_mx_grouped_t(const MxGroupArgs &g, hipStream_t stream) {
+    hipLaunchKernelGGL((k_mx_grouped<S, FMT>), dim3(g.tile_start[g.count]), dim3(S::NT), 0, stream, g);
+    return hipGetLastError();
+}
+
+template <class S>
+static hipError_t launch_mx_grouped_fmt(int hw_format, const MxGroupArgs &g, hipStream_t stream) {
+    switch (hw_format) {
+        case 0: return launch_mx_grouped_t<S, 0>(g, stream);
+        case 1: return launch_mx_grouped_t<S, 1>(g, stream);
+        case 4: return launch_mx_grouped_t<S, 4>(g, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_mx_grouped(int config, const MxProblem *ps, int count, hipStream_t stream) {
+    if ((config != MX_256x256_W8 && config != MX_128x128_W4) || count < 1 || count > kGroupMax)
+        return hipErrorInvalidValue;
+    const TileConfig &tc = kMxConfigs[config];
+    MxGroupArgs g;
+    g.count = count;
+    g.tile_start[0] = 0;
+    for (int i = 0; i < count; ++i) {
+        if (ps[i].format != ps[0].format) return hipErrorInvalidValue;
+        g.p[i] = mx_args(tc, ps[i]);
+        g.tile_start[i + 1] = g.tile_start[i] + g.p[i].tiles_m * g.p[i].tiles_n;
+    }
+    const int hw = mx_hw_format(ps[0].format);
+    return config == MX_256x256_W8 ? launch_mx_grouped_fmt<Mx256>(hw, g, stream)
+                                   : launch_mx_grouped_fmt<Mx128>(hw, g, stream);
+}
+
+hipError_t launch_mx(int config, const MxProblem &p, hipStream_t stream) {
+    if (config < 0 || config >= MX_CONFIGS) return hipErrorInvalidValue;
+    const int hw = mx_hw_format(p.format);
+    const MxArgs a = mx_args(kMxConfigs[config], p);
     switch (config) {
         case MX_256x256_W8: return launch_mx_fmt<Mx256, false>(hw, a, stream);
         case MX_128x128_W4: return launch_mx_fmt<Mx128, false>(hw, a, stream);

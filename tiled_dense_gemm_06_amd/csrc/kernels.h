@@ -113,6 +113,9 @@ struct MxProblem {
 enum MxConfig { MX_256x256_W8 = 0, MX_128x128_W4 = 1, MX_PIPE_256x256_W8 = 2, MX_PIPE_256x256_W4 = 3, MX_CONFIGS = 4 };
 extern const TileConfig kMxConfigs[MX_CONFIGS];  // bk: bytes of K per stage and row
 hipError_t launch_mx(int config, const MxProblem &p, hipStream_t stream);
+// count (1 .. kGroupMax) block-scaled problems of one format in one launch
+// (configurations MX_256x256_W8 and MX_128x128_W4)
+hipError_t launch_mx_grouped(int config, const MxProblem *ps, int count, hipStream_t stream);
 
 hipError_t launch_naive(const Problem &p, hipStream_t stream);
 hipError_t launch_fill_zero(const Problem &p, hipStream_t stream);
