@@ -156,10 +156,10 @@ int32_t tlg_version(void);
 
 /* ---- layout and batching variants ----
  * The same operation with B given transposed, and several problems in one
- * launch. The TileLang article (aiwiki.ai/wiki/tilelang, "Backend Coverage",
- * key technical milestones) lists a grouped GEMM with a transposed B matrix
- * among the kernels built with the DSL; the operation of each problem is
- * still the quick-start matmul_relu. */
+ * launch. The forum post "TileLang: Writing Near-Hardware-Limit GPU Kernels
+ * in 70 Lines of Python" (zhichai.net, "Key Technical Milestones") lists a
+ * grouped GEMM with a transposed B matrix among the kernels built with the
+ * DSL; the operation of each problem is still the quick-start matmul_relu. */
 
 /* C = ReLU(A . Bt^T): Bt is the N x K fp16 row-major matrix (B transposed),
  * ldbt >= max(1, K); everything else as tlg_gemm_relu. B's tiles are loaded
@@ -222,11 +222,13 @@ tlg_status tlg_gemm_relu_grouped_variant(tlg_handle h, int32_t config, int32_t c
 
 /* ---- Block-scaled (MX) element formats ----
  *
- * The TileLang article ("Backends and hardware support") names FP4 E2M1
- * matrix cores on CDNA4 (gfx950) and a block-scaled MMA path; the TileLang
- * forum post ("Backend Coverage", milestone list) names MXFP8 block-scaled
- * GEMM with a transposed B. Neither page defines the formats; they are read
- * as the OCP Microscaling (MX) formats:
+ * The project page "TileLang: a tile-level DSL for writing GPU kernels in
+ * Python" (hysenlabs.com, "Three backends under one language dialect") names
+ * FP4 E2M1 matrix cores on CDNA4 (gfx950) and a block-scaled MMA path; the
+ * forum post "TileLang: Writing Near-Hardware-Limit GPU Kernels in 70 Lines
+ * of Python" (zhichai.net, "Key Technical Milestones") names MXFP8 grouped
+ * GEMM with block scaling and a transposed B. Neither page defines the
+ * formats; they are read as the OCP Microscaling (MX) formats:
  *
  *   C[i][j] = fp16_rne( ReLU( sum over blocks b = 0 .. K/32-1 of
  *               2^(SA[i][b]-127) * 2^(SB[j][b]-127)
@@ -304,9 +306,9 @@ typedef struct {
     int64_t ldc;
 } tlg_mx_desc;
 
-/* Grouped block-scaled GEMM+ReLU with B transposed (the TileLang forum
- * post's "Backend Coverage" milestone list names an MXFP8 grouped GEMM with
- * block scaling and a transposed B): count (0 .. TLG_GROUP_MAX) independent
+/* Grouped block-scaled GEMM+ReLU with B transposed (the forum post's "Key
+ * Technical Milestones" list names an MXFP8 grouped GEMM with block scaling
+ * and a transposed B): count (0 .. TLG_GROUP_MAX) independent
  * problems, each as tlg_gemm_relu_mx, in ONE launch of the block-scaled
  * kernel. The descriptor array is read on the host during the call (it may
  * be freed afterwards); nothing is allocated. Every descriptor is checked as

@@ -5,10 +5,11 @@ CPU-baseline leg of the benchmark may import this module. It shares no code
 with the GPU path or with the float16 oracle.
 
 The arithmetic is in ``oracle_mx.c`` (its header states the definition and
-the readings behind it: the TileLang article, "Backends and hardware
-support", names FP4 E2M1 matrix cores on gfx950 and block-scaled MMA; the
-forum post's "Backend Coverage" milestones name MXFP8 block-scaled GEMM with
-a transposed B; neither defines the scale semantics, which are read as the
+the readings behind it: the hysenlabs.com project page on TileLang, "Three
+backends under one language dialect", names FP4 E2M1 matrix cores on gfx950
+and block-scaled MMA; the zhichai.net forum post on TileLang, "Key
+Technical Milestones", names MXFP8 grouped GEMM with block scaling and a
+transposed B; neither defines the scale semantics, which are read as the
 OCP Microscaling formats: 32 elements along K share one E8M0 scale).
 
 Arrays: A is (M, K) codes and B is (N, K) codes (B given transposed), as

@@ -9,11 +9,13 @@
  * links, loads or calls it. It shares no source, header, table or helper with
  * the GPU path (nor with the float16 oracle next to it).
  *
- * Where this comes from. The TileLang article (aiwiki.ai/wiki/tilelang,
- * "Backends and hardware support") names FP4 E2M1 matrix cores on CDNA4
- * (gfx950) and a block-scaled MMA path, and the forum post on TileLang
- * ("Backend Coverage" and its milestone list) names MXFP8 block-scaled GEMM
- * with a transposed B. Neither page defines the element codes or the scale
+ * Where this comes from. The project page "TileLang: a tile-level DSL for
+ * writing GPU kernels in Python" (hysenlabs.com, "Three backends under one
+ * language dialect") names FP4 E2M1 matrix cores on CDNA4 (gfx950) and a
+ * block-scaled MMA path; the forum post "TileLang: Writing Near-Hardware-
+ * Limit GPU Kernels in 70 Lines of Python" (zhichai.net, "Key Technical
+ * Milestones") names MXFP8 grouped GEMM with block scaling and a
+ * transposed B. Neither page defines the element codes or the scale
  * semantics; the plainest reading is the OCP Microscaling (MX) formats,
  * which both names refer to:
  *   - a block is 32 consecutive elements along K of one row of A (or of one

@@ -6,9 +6,11 @@ hand-worked cases under tests/golden/, and invariants of the definition.
 The definition pinned (stated in full in oracle/oracle_mx.c): blocks of 32
 elements along K share one E8M0 scale 2^(e-127); C = ReLU(sum over blocks of
 scale_a * scale_b * block dot product), rounded once to fp16. It is the
-reading of the block-scaled GEMM the TileLang article names ("Backends and
-hardware support": FP4 E2M1 matrix cores on gfx950, block-scaled MMA) and
-the TileLang forum post lists ("Backend Coverage": MXFP8 block-scaled GEMM).
+reading of the block-scaled GEMM named by the hysenlabs.com project page on
+TileLang ("Three backends under one language dialect": FP4 E2M1 matrix
+cores on gfx950, block-scaled MMA) and listed by the zhichai.net forum post
+on TileLang ("Key Technical Milestones": MXFP8 grouped GEMM with block
+scaling and a transposed B).
 """
 import numpy as np
 import pytest

@@ -9,7 +9,9 @@ library (``csrc/tune_table.inc``). The library consults the table for the
 shape's class (ceil(log2) of M, N and K, and whether K or N is ragged)
 before its heuristic, and falls back to the heuristic when the tuned choice
 cannot serve a problem (e.g. unaligned pointers). This is the "search over
-heuristics" the TileLang article's autotuning section describes, done once
+heuristics" of the project page "TileLang: a tile-level DSL for writing GPU
+kernels in Python" (hysenlabs.com, "Autotuning, cache behavior and the cost
+of a search"), done once
 per device type instead of per call.
 
     python -m tiled_dense_gemm_06_amd.autotune --out tiled_dense_gemm_06_amd/csrc/tune_table.inc

@@ -2,10 +2,13 @@
 // C = ReLU(A . B): 8-bit (E4M3, E5M2) or 4-bit (E2M1) element codes, one
 // E8M0 scale per 32 elements along K, fp32 accumulation on the matrix cores,
 // ReLU and the fp16 copy-out of the quick-start kernel (TileLang article,
-// aiwiki.ai/wiki/tilelang, "Programming model"). The article's "Backends
-// and hardware support" section names FP4 E2M1 matrix cores on gfx950 and a
-// block-scaled MMA path; the TileLang forum post's "Backend Coverage"
-// milestones name MXFP8 block-scaled GEMM with a transposed B.
+// aiwiki.ai/wiki/tilelang, "Programming model"). The project page "TileLang:
+// a tile-level DSL for writing GPU kernels in Python" (hysenlabs.com,
+// "Three backends under one language dialect") names FP4 E2M1 matrix cores
+// on CDNA4 (gfx950) and a block-scaled MMA path; the forum post "TileLang:
+// Writing Near-Hardware-Limit GPU Kernels in 70 Lines of Python"
+// (zhichai.net, "Key Technical Milestones") names MXFP8 grouped GEMM with
+// block scaling and a transposed B.
 //
 // Design (gfx950 first):
 //  * the product is v_mfma_scale_f32_32x32x64_f8f6f4: 64 k per instruction,

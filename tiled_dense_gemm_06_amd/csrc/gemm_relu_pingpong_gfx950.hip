@@ -1,8 +1,11 @@
 // gfx950 wave-role ("ping-pong") schedule for C = ReLU(A . B), fp16 in,
 // fp32 accumulation, fp16 out: the quick-start kernel of the TileLang
 // article (aiwiki.ai/wiki/tilelang, "Programming model"), with the
-// producer/consumer specialisation its "Scheduling" discussion credits to
-// TileLang's automatic warp specialisation, re-cut for CDNA4.
+// producer/consumer wave specialisation that the article's "Compiler and
+// scheduling automation" section describes TileLang doing automatically
+// (and that the forum post "TileLang: Writing Near-Hardware-Limit GPU
+// Kernels in 70 Lines of Python", "Key Technical Milestones", lists), re-cut
+// for CDNA4.
 //
 // A 256 x 256 output tile, eight waves, two per SIMD: waves 0-3 (group 0,
 // rows 0..127 of the tile) and waves 4-7 (group 1, rows 128..255), one of
