@@ -8,11 +8,11 @@ built-in heuristic by more than a margin as a table compiled into the
 library (``csrc/tune_table.inc``). The library consults the table for the
 shape's class (ceil(log2) of M, N and K, and whether K or N is ragged)
 before its heuristic, and falls back to the heuristic when the tuned choice
-cannot serve a problem (e.g. unaligned pointers). This is the "search over
-heuristics" of the project page "TileLang: a tile-level DSL for writing GPU
-kernels in Python" (hysenlabs.com, "Autotuning, cache behavior and the cost
-of a search"), done once
-per device type instead of per call.
+cannot serve a problem (e.g. unaligned pointers). The project page
+"TileLang: a tile-level DSL for writing GPU kernels in Python" (hysenlabs.com,
+"Autotuning, cache behavior and the cost of a search") describes TileLang
+preferring a measured search to fixed rules; here the search runs once per
+device type, offline, instead of per call.
 
     python -m tiled_dense_gemm_06_amd.autotune --out tiled_dense_gemm_06_amd/csrc/tune_table.inc
 
