@@ -1,4 +1,5 @@
-// CPU emulation of the data movement of the gfx950 GEMM+ReLU kernels
+// CPU emulation of the data movement of the gfx950 GEMM+ReLU kernels (fp16
+// and, at the end of the file, the block-scaled kernel)
 // (test-only). It uses the kernels' own index arithmetic (tile_layout.h) and
 // models, lane by lane:
 //   * the direct-to-LDS loads (16 bytes per lane, zeros for out-of-range
@@ -523,4 +524,227 @@ extern "C" long emu_check_epilogue(int config) {
         case 5: return check_epilogue<E256w8x32>();
         default: return -1;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Block-scaled (MX) kernel k_mx: direct-to-LDS loads of 128 bytes of K per
+// row and stage (16-byte chunks, A and B (given N x K) tiles alike), the
+// stage's scale dwords (buffer_load_dword ... lds, one per lane, spread over
+// the waves), the 16-byte fragment reads and scale reads of each 64-deep
+// step, and v_mfma_scale_f32_32x32x64_f8f6f4 with its measured layouts: an
+// 8-bit operand lane l holds k = 16*(l/32)+e and 32+16*(l/32)+e (e < 16),
+// bytes 0..15 of lanes l%32 and l%32+32 are scaled by lane l%32's scale byte
+// and bytes 16..31 by lane l%32+32's; a 4-bit lane holds 32 consecutive k,
+// k = 32*(l/32)+e, scaled by its own scale byte.
+// ---------------------------------------------------------------------------
+namespace {
+
+double emu_minifloat(unsigned code, int eb, int mb, int bias) {
+    unsigned s = (code >> (eb + mb)) & 1, e = (code >> mb) & ((1u << eb) - 1), f = code & ((1u << mb) - 1);
+    double v = e == 0 ? std::ldexp((double)f, 1 - bias - mb) : std::ldexp((double)((1u << mb) + f), (int)e - bias - mb);
+    return s ? -v : v;
+}
+
+// hw format code: 0 E4M3, 1 E5M2, 4 E2M1 (finite codes only)
+double emu_decode(int hw, unsigned c) {
+    if (hw == 0) return emu_minifloat(c & 0xff, 4, 3, 7);
+    if (hw == 1) return emu_minifloat(c & 0xff, 5, 2, 15);
+    return emu_minifloat(c & 0xf, 2, 1, 1);
+}
+
+struct MxProb {
+    int M, N, K, hw;
+    const uint8_t *A, *B, *SA, *SB;  // codes (A: M rows, B: N rows), scales
+    long lda, ldb, ldsa, ldsb;       // bytes per row
+    uint16_t *C;
+    long ldc;
+};
+
+template <class S>
+void run_mx(const MxProb &p, Errs &er, std::vector<int> &cover) {
+    const int EPB = p.hw == 4 ? 2 : 1;
+    const int KPS = S::RA * EPB, SBR = KPS / 32, KSTEPS = KPS / 64;
+    const int SC_A = S::BM * SBR, SC_B = S::BN * SBR;
+    const int STAGE = S::STAGE_BYTES + SC_A + SC_B;
+    const int NSA = SC_A / 256, NSB = SC_B / 256, SPW = (NSA + NSB) / S::WAVES;
+    if ((NSA + NSB) % S::WAVES || SPW < 1 || NSA % SPW || S::RA != 128) { er.lds_oob++; return; }
+    const int tiles_m = (p.M + S::BM - 1) / S::BM, tiles_n = (p.N + S::BN - 1) / S::BN, nwg = tiles_m * tiles_n;
+    const int nk = (p.K + KPS - 1) / KPS, nkb = p.K / 32;
+    std::vector<uint8_t> lds(STAGE);
+    std::vector<int> lds_w(STAGE);
+    std::vector<int> seen(nwg, 0);
+    for (int pid = 0; pid < nwg; ++pid) {
+        int tmi, tni;
+        grouped_tile(xcd_remap(pid, nwg), tiles_m, tiles_n, 4, &tmi, &tni);
+        if (tmi < 0 || tmi >= tiles_m || tni < 0 || tni >= tiles_n || seen[tmi * tiles_n + tni]++) {
+            er.tile_dup++;
+            continue;
+        }
+        const int m0 = tmi * S::BM, n0 = tni * S::BN;
+        std::vector<double> acc((size_t)S::WAVES * S::TN * S::TM * 64 * 16, 0.0);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int k0 = kt * KPS, kb0 = k0 / 32;
+            const long k0b = k0 / EPB;
+            std::fill(lds.begin(), lds.end(), 0xAB);
+            std::fill(lds_w.begin(), lds_w.end(), 0);
+            for (int w = 0; w < S::WAVES; ++w)
+                for (int lane = 0; lane < 64; ++lane) {
+                    for (int op = 0; op < 2; ++op)  // A then B, rows m or n
+                        for (int i = 0; i < (op ? S::DMA_B : S::DMA_A); ++i) {
+                            const ChunkRef c = dma_a_chunk<S>(w, i, lane);
+                            const int dst = (op ? S::A_BYTES : 0) + (w * (op ? S::DMA_B : S::DMA_A) + i) * 1024 + 16 * lane;
+                            const int r0 = op ? n0 : m0, lim = op ? p.N : p.M;
+                            const bool ok = r0 + c.row < lim && k0 + 16 * EPB * c.chunk < p.K;
+                            for (int b = 0; b < 16; ++b) {
+                                if (dst + b >= S::STAGE_BYTES) { er.lds_oob++; continue; }
+                                if (lds_w[dst + b]++) er.lds_multi++;
+                                uint8_t v = 0;
+                                if (ok) {
+                                    const long row = r0 + c.row, byte = k0b + 16 * c.chunk + b;
+                                    if (byte >= (long)p.K / EPB || byte >= (op ? p.ldb : p.lda)) er.oob_global++;
+                                    else v = (op ? p.B : p.A)[row * (op ? p.ldb : p.lda) + byte];
+                                }
+                                lds[dst + b] = v;
+                            }
+                        }
+                    for (int i = 0; i < SPW; ++i) {  // scale dwords
+                        const int slab = w * SPW + i;
+                        const bool sb = slab >= NSA;
+                        const int q = (slab % NSA) * 64 + lane, row = q / (SBR / 4), d = q % (SBR / 4);
+                        const int dst = S::STAGE_BYTES + (sb ? SC_A : 0) + (slab % NSA) * 256 + 4 * lane;
+                        const int r0 = sb ? n0 : m0, lim = sb ? p.N : p.M;
+                        const bool ok = r0 + row < lim && kb0 + 4 * d < nkb;
+                        for (int b = 0; b < 4; ++b) {
+                            if (dst + b >= STAGE) { er.lds_oob++; continue; }
+                            if (lds_w[dst + b]++) er.lds_multi++;
+                            uint8_t v = 0;
+                            if (ok) {
+                                const long col = kb0 + 4 * d + b;
+                                if (col >= nkb || col >= (sb ? p.ldsb : p.ldsa)) er.oob_global++;
+                                else v = (sb ? p.SB : p.SA)[(r0 + row) * (sb ? p.ldsb : p.ldsa) + col];
+                            }
+                            lds[dst + b] = v;
+                        }
+                    }
+                }
+            for (int b = 0; b < STAGE; ++b)
+                if (lds_w[b] != 1) er.lds_multi++;
+            // fragments, scales and MFMAs of every 64-deep step
+            for (int w = 0; w < S::WAVES; ++w) {
+                const int wm0 = (w / S::WN) * S::WTM, wn0 = (w % S::WN) * S::WTN;
+                for (int J = 0; J < KSTEPS; ++J) {
+                    // vals[op][t][lane][32] decoded codes, sc[op][t][lane] scale values
+                    std::vector<double> vals((size_t)2 * 4 * 64 * 32, 0.0), sc((size_t)2 * 4 * 64, 0.0);
+                    for (int op = 0; op < 2; ++op)  // 0: B operand (first, columns), 1: A operand (rows)
+                        for (int t = 0; t < (op ? S::TM : S::TN); ++t) {
+                            const int base = op ? 0 : S::A_BYTES, w0 = op ? wm0 : wn0;
+                            for (int part = 0; part < (EPB == 1 ? 2 : 1); ++part) {
+                                int addr[64];
+                                for (int l = 0; l < 64; ++l) {
+                                    const int row = w0 + 32 * t + l % 32, half = l / 32;
+                                    const int chunk = EPB == 1 ? 4 * J + 2 * part + half : 2 * J + half;
+                                    addr[l] = lds_a_offset<S>(row, chunk);
+                                    if (addr[l] < 0 || addr[l] + 16 > S::A_BYTES || addr[l] % 16) er.lds_oob++;
+                                }
+                                for (int q = 0; q < 4; ++q) {
+                                    int used[16] = {0};
+                                    for (int l = 16 * q; l < 16 * q + 16; ++l)
+                                        if (used[slot16(addr[l])]++) er.bank_conflict++;
+                                }
+                                for (int l = 0; l < 64; ++l)
+                                    for (int b = 0; b < 16; ++b) {
+                                        const uint8_t byte = lds[base + addr[l] + b];
+                                        if (EPB == 1) {
+                                            vals[(((size_t)op * 4 + t) * 64 + l) * 32 + 16 * part + b] = emu_decode(p.hw, byte);
+                                        } else {
+                                            vals[(((size_t)op * 4 + t) * 64 + l) * 32 + 2 * b] = emu_decode(p.hw, byte & 0xf);
+                                            vals[(((size_t)op * 4 + t) * 64 + l) * 32 + 2 * b + 1] = emu_decode(p.hw, byte >> 4);
+                                        }
+                                    }
+                            }
+                            // the kernel's scale selection: the row's dword DW of the
+                            // stage, shifted right by 8*(l/32), byte OPSEL of it
+                            const int DW = EPB == 1 ? 0 : J / 2, OPSEL = EPB == 1 ? 2 * J : 2 * (J % 2);
+                            for (int l = 0; l < 64; ++l) {
+                                const int row = w0 + 32 * t + l % 32;
+                                const int a = S::STAGE_BYTES + (op ? 0 : SC_A) + row * SBR + 4 * DW;
+                                if (a + 4 > STAGE || a % 4) { er.lds_oob++; continue; }
+                                uint32_t dword;
+                                memcpy(&dword, &lds[a], 4);
+                                const uint32_t byte = ((dword >> (8 * (l / 32))) >> (8 * OPSEL)) & 0xff;
+                                sc[((size_t)op * 4 + t) * 64 + l] = std::ldexp(1.0, (int)byte - 127);
+                            }
+                        }
+                    for (int tn = 0; tn < S::TN; ++tn)
+                        for (int tm = 0; tm < S::TM; ++tm)
+                            for (int l = 0; l < 64; ++l)
+                                for (int r = 0; r < 16; ++r) {
+                                    const int i = 8 * (r / 4) + 4 * (l / 32) + r % 4, j = l % 32;
+                                    double d = 0;
+                                    auto X = [&](int lane, int e) { return vals[(((size_t)0 * 4 + tn) * 64 + lane) * 32 + e]; };
+                                    auto Y = [&](int lane, int e) { return vals[(((size_t)1 * 4 + tm) * 64 + lane) * 32 + e]; };
+                                    auto sX = [&](int lane) { return sc[((size_t)0 * 4 + tn) * 64 + lane]; };
+                                    auto sY = [&](int lane) { return sc[((size_t)1 * 4 + tm) * 64 + lane]; };
+                                    if (EPB == 1) {
+                                        for (int blk = 0; blk < 2; ++blk) {
+                                            double s = 0;
+                                            for (int h = 0; h < 2; ++h)
+                                                for (int e = 0; e < 16; ++e) s += X(i + 32 * h, 16 * blk + e) * Y(j + 32 * h, 16 * blk + e);
+                                            d += sX(i + 32 * blk) * sY(j + 32 * blk) * s;
+                                        }
+                                    } else {
+                                        for (int h = 0; h < 2; ++h) {
+                                            double s = 0;
+                                            for (int e = 0; e < 32; ++e) s += X(i + 32 * h, e) * Y(j + 32 * h, e);
+                                            d += sX(i + 32 * h) * sY(j + 32 * h) * s;
+                                        }
+                                    }
+                                    acc[((((size_t)w * S::TN + tn) * S::TM + tm) * 64 + l) * 16 + r] += d;
+                                }
+                }
+            }
+        }
+        for (int w = 0; w < S::WAVES; ++w) {
+            const int wm0 = (w / S::WN) * S::WTM, wn0 = (w % S::WN) * S::WTN;
+            for (int tn = 0; tn < S::TN; ++tn)
+                for (int tm = 0; tm < S::TM; ++tm)
+                    for (int l = 0; l < 64; ++l)
+                        for (int r = 0; r < 16; ++r) {
+                            const int m = m0 + acc_m(wm0, tm, l), n = n0 + acc_n(wn0, tn, r, l);
+                            const double v = acc[((((size_t)w * S::TN + tn) * S::TM + tm) * 64 + l) * 16 + r];
+                            if (m >= p.M || n >= p.N) continue;
+                            p.C[(size_t)m * p.ldc + n] = f2h((float)(v > 0.0 ? v : 0.0));
+                            cover[(size_t)m * p.N + n]++;
+                        }
+        }
+    }
+}
+
+}  // namespace
+
+// config 0: 256 x 256, eight waves, two stages; 1: 128 x 128, four waves.
+// hw: 0 E4M3, 1 E5M2, 4 E2M1. Leading dimensions in bytes. Returns 0, and
+// the error counts in errs[0..7] (global out of range, LDS written twice or
+// never, LDS out of range, bank conflicts, C written twice, C missing, C
+// outside, tile mapping).
+extern "C" int emu_gemm_relu_mx(int config, int hw, int M, int N, int K, const uint8_t *A, long lda, const uint8_t *SA,
+                                long ldsa, const uint8_t *B, long ldb, const uint8_t *SB, long ldsb, uint16_t *C,
+                                long ldc, long *errs) {
+    MxProb p{M, N, K, hw, A, B, SA, SB, lda, ldb, ldsa, ldsb, C, ldc};
+    Errs er;
+    std::vector<int> cover((size_t)M * N, 0);
+    if (config == 0)
+        run_mx<TileShape<256, 256, 64, 2, 4, 2>>(p, er, cover);
+    else if (config == 1)
+        run_mx<TileShape<128, 128, 64, 2, 2, 3>>(p, er, cover);
+    else
+        return -1;
+    for (int c : cover) {
+        if (c == 0) er.c_missing++;
+        if (c > 1) er.c_multi++;
+    }
+    long v[8] = {er.oob_global, er.lds_multi, er.lds_oob, er.bank_conflict, er.c_multi, er.c_missing, er.c_outside,
+                 er.tile_dup};
+    memcpy(errs, v, sizeof v);
+    return 0;
 }
