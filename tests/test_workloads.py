@@ -1,5 +1,6 @@
 """The seeded input generator: shapes, dtypes, determinism and value ranges."""
 import numpy as np
+import pytest
 
 from tiled_dense_gemm_06_amd import workloads as wl
 
@@ -31,3 +32,37 @@ def test_distributions():
     assert set(np.unique(Ai).tolist()) <= {-2.0, -1.0, 0.0, 1.0, 2.0}
     P, Q = wl.make_random(8, 9, 10, 0, kind="integer_pos")
     assert set(np.unique(P).tolist()) <= {0.0, 1.0, 2.0, 3.0}
+
+
+def test_mx_inputs_recipe():
+    """Block-scaled inputs: fixed by the seed, the stated shapes (E2M1 packed
+    two per byte), finite codes only, scales in the stated band, and the
+    small-integer kind decoding to -2..2 with unit scales."""
+    import torch
+
+    for fmt in ("e4m3", "e5m2", "e2m1"):
+        A, SA, Bt, SB = wl.make_mx_inputs(fmt, 33, 40, 256, seed=7)
+        A2, SA2, Bt2, SB2 = wl.make_mx_inputs(fmt, 33, 40, 256, seed=7)
+        assert all(np.array_equal(x, y) for x, y in ((A, A2), (SA, SA2), (Bt, Bt2), (SB, SB2)))
+        per = 2 if fmt == "e2m1" else 1
+        assert A.shape == (33, 256 // per) and Bt.shape == (40, 256 // per) and A.dtype == np.uint8
+        assert SA.shape == (33, 8) and SB.shape == (40, 8)
+        assert SA.min() >= 125 and SA.max() <= 129 and SB.min() >= 125 and SB.max() <= 129
+        if fmt != "e2m1":
+            dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+            v = torch.from_numpy(np.concatenate([A.ravel(), Bt.ravel()])).view(dt).double().numpy()
+            assert np.all(np.isfinite(v))
+            assert (v == 0).mean() < 0.2 and np.abs(v).max() <= 16
+        A, SA, Bt, SB = wl.make_mx_inputs(fmt, 9, 11, 128, seed=3, kind="small_int")
+        assert np.all(SA == 127) and np.all(SB == 127)
+        codes = np.concatenate([A.ravel() & 0xF, A.ravel() >> 4]) if fmt == "e2m1" else A.ravel()
+        if fmt == "e2m1":
+            allowed = {0x0, 0x2, 0x4, 0x8, 0xA, 0xC}   # +-0, +-1, +-2
+        else:
+            eb, mb = wl.MX_FORMATS[fmt]
+            bias = (1 << (eb - 1)) - 1
+            one, two = bias << mb, (bias + 1) << mb
+            allowed = {0, one, two, 0x80 | one, 0x80 | two, 0x80}
+        assert set(np.unique(codes).tolist()) <= allowed
+    with pytest.raises(ValueError):
+        wl.make_mx_inputs("e4m3", 4, 4, 100, seed=0)
