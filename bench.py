@@ -32,6 +32,18 @@ METRIC = "GEMM+ReLU TFLOPS (fp16 in, fp32 acc) at 8192³ and % of fp16 MFMA peak
 PEAK_MFMA_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20  # MI355X Infinity Cache; rotated buffers exceed twice this
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "" where unavailable."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(w, A, B, target_s: float):
     """The oracle as it stands, on whole sampled output rows of the workload.
 
@@ -55,7 +67,7 @@ def cpu_baseline(w, A, B, target_s: float):
         n = min(w.M, -(-n // threads) * threads)
     flop = 2.0 * n * w.N * w.K
     return {
-        "value": flop / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+        "value": flop / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle", "cpu": cpu_model(),
         "sample": f"{n} of {w.M} output rows ({n}x{w.N}x{w.K} multiply-adds, all K), {dt:.2f} s wall "
                   f"on {threads} threads",
     }
@@ -85,6 +97,7 @@ def mx_cpu_baseline(fmt, w, A, SA, Bt, SB, target_s: float):
         n = min(w.M, -(-n // threads) * threads)
     return {
         "value": 2.0 * n * w.N * w.K / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+        "cpu": cpu_model(),
         "sample": f"{n} of {w.M} output rows ({n}x{w.N}x{w.K} block-scaled multiply-adds, all K), "
                   f"{dt:.2f} s wall on {threads} threads",
     }
