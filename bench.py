@@ -132,7 +132,7 @@ def bench_mx(args, torch, tlg, wl, dev) -> int:
     rows = [(w.M * g // G, w.M * (g + 1) // G) for g in range(G)] if G else []
     if G:  # the grouped call picks its tile by the blocks' total tile count
         t256 = sum(-(-(r1 - r0) // 256) * -(-w.N // 256) for r0, r1 in rows)
-        gcfg = args.config if args.config >= 0 else (0 if t256 >= 128 else 1)
+        gcfg = args.config if args.config >= 0 else (0 if t256 > 128 else 1)
         plan = {"config_name": tlg._native.tlg_plan_mx_config_name(gcfg)}
 
     def step(i):
