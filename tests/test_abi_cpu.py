@@ -80,7 +80,7 @@ def test_plan_shapes_of_the_workloads():
     assert tlg.plan(48, 14336, 4096)["config_name"] == "dma_64x64x64_w2x2_s3"  # M above one strip, tiles enough
     assert tlg.plan(48, 4096, 4096)["config_name"].startswith("streamk")  # M above one strip, few tiles
     p = tlg.plan(16, 2048, 4096)  # few strips: K split among work-groups too, up to the CUs
-    assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 8 and p["grid"] == 32 * 8
+    assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 32 * 4
     p = tlg.plan(1, 4096, 4096)
     assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 64 * 4
     assert tlg.plan(3072, 3072, 3072)["config_name"] == "pipe_256x256x64_w2x4_s2_a3"  # 144 tiles of 256 x 256

@@ -200,9 +200,10 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
             if (!strip_ok) return TLG_ERROR_NOT_SUPPORTED;
             // parts per strip: forced, else as many as fit the CUs whole
             // (1x4096x4096: 4 parts 12 us vs 1 part 23 us; 16x14336x4096:
-            // 1 part 25 us vs 2 parts 29 us), at most 8
+            // 1 part 25 us vs 2 parts 29 us), at most 4 (16x2048x4096: 4
+            // parts 10.3 us vs 8 parts 10.9 us)
             int64_t parts = splits > 0 ? splits : (strips >= cus ? 1 : cus / strips);
-            if (splits <= 0 && parts > 8) parts = 8;
+            if (splits <= 0 && parts > 4) parts = 4;
             const int64_t nkb = ceil_div(p.K, ts.bk);
             if (parts > nkb) parts = nkb > 0 ? nkb : 1;
             const int64_t slot_bytes = (int64_t)ts.bm * ts.bn * 4;
