@@ -357,6 +357,8 @@ using ES256 = TileShape<32, 256, 64, 1, 4, 3>;
 using EP64 = TileShape<256, 256, 64, 2, 2, 2>;  // pipelined, 64-deep stages
 using E256w8 = TileShape<256, 256, 64, 2, 4, 2>;
 using E256w8x32 = TileShape<256, 256, 32, 2, 4, 4>;
+using EP256x128 = TileShape<256, 128, 64, 2, 2, 3>;  // pipelined half tiles
+using EP128x256 = TileShape<128, 256, 64, 1, 4, 3>;
 
 extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A, long lda, const uint16_t *B,
                              long ldb, uint16_t *C, long ldc, int splits, int k_split, float *W, long *errs) {
@@ -368,6 +370,8 @@ extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A,
         case 3: return emulate<EP64>(p, false, errs);
         case 4: return emulate<E256w8>(p, false, errs);
         case 5: return emulate<E256w8x32>(p, false, errs);
+        case 6: return emulate<EP256x128>(p, false, errs);
+        case 7: return emulate<EP128x256>(p, false, errs);
         case 10: return emulate<ES128>(p, true, errs);
         case 11: return emulate<ES256>(p, true, errs);
         default: return -1;
@@ -522,6 +526,8 @@ extern "C" long emu_check_epilogue(int config) {
         case 3: return check_epilogue<EP64>();
         case 4: return check_epilogue<E256w8>();
         case 5: return check_epilogue<E256w8x32>();
+        case 6: return check_epilogue<EP256x128>();
+        case 7: return check_epilogue<EP128x256>();
         default: return -1;
     }
 }

@@ -68,8 +68,13 @@ def test_check_args(args, expect):
 def test_plan_shapes_of_the_workloads():
     assert tlg.plan(8192, 8192, 8192)["config_name"] == "pipe_256x256x64_w2x4_s2_a3"
     assert tlg.plan(4096, 4096, 4096)["variant_name"] == "tiled_pipe"
-    p = tlg.plan(3001, 2049, 1537)  # odd sizes and leading dimensions: direct-to-LDS loads, staged K tail
-    assert p["variant_name"] == "tiled_dma" and p["config_name"] == "dma_128x128x32_w2x2_s4"
+    # odd sizes and leading dimensions: direct-to-LDS loads, staged K tail; the
+    # tuned table gives this class the pipelined 128 x 256 tiles (216 of them)
+    p = tlg.plan(3001, 2049, 1537)
+    assert p["variant_name"] == "tiled_pipe" and p["config_name"] == "pipe_128x256x64_w1x4_s3" and p["grid"] == 216
+    # the same shape without the table's entry: the heuristic's 128 x 128 tiles
+    p = tlg.plan(3001, 2049, 1537, variant=tlg.TLG_VARIANT_TILED_DMA)
+    assert p["config_name"] == "dma_128x128x32_w2x2_s4"
     p = tlg.plan(16, 14336, 4096)  # one work-group per 64 columns, K split among its waves
     assert p["variant_name"] == "splitk" and p["config_name"] == "splitk_waves_32x64x64_w2_s3"
     assert p["kernels"] == 1 and p["grid"] == 14336 // 64 and p["workspace_bytes"] == 0
@@ -201,14 +206,23 @@ def test_tuned_table_entries_are_taken():
             assert p["splits"] == splits
         forced = tlg.plan(M, N, K, variant=variant, config=config, splits=splits)
         assert (forced["grid"], forced["splits"]) == (p["grid"], p["splits"])
-        q = tlg.plan(M, N, K, aligned=False)  # the tuned kernel needs 16-byte aligned data
-        assert q["variant_name"] in ("tiled_dma", "tiled_general")
+        q = tlg.plan(M, N, K, aligned=False)
+        if variant == tlg.TLG_VARIANT_SPLITK:  # split-K kernels need 16-byte aligned data: the heuristic
+            assert q["variant_name"] in ("tiled_dma", "tiled_general")
+        else:  # the direct-to-LDS tile kernels load unaligned rows too
+            assert (q["variant"], q["config"]) == (variant, config)
 
 
 def test_tuned_classes_of_the_table():
     # the two measured skinny classes: two-kernel split-K instead of stream-K
     assert tlg.plan(48, 4096, 14336)["config_name"] == "splitk_32x128x64_w1x4_s4"
     assert tlg.plan(64, 4096, 8192)["config_name"] == "splitk_32x128x64_w1x4_s4"
+    # mid-size and ragged classes: pipelined 128 x 256 tiles; decode-like
+    # 8 x 8192 x 8192: stream-K over strips
+    assert tlg.plan(1024, 4096, 16384)["config_name"] == "pipe_128x256x64_w1x4_s3"
+    assert tlg.plan(3001, 2049, 1537)["config_name"] == "pipe_128x256x64_w1x4_s3"
+    p = tlg.plan(8, 8192, 8192)
+    assert p["config_name"] == "strip_sk_32x64x64_w2_s3" and p["grid"] == 256
     # a neighbouring class keeps the heuristic's choice
     assert tlg.plan(48, 4096, 4096)["config_name"].startswith("streamk")
 

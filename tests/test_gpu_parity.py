@@ -102,19 +102,20 @@ def test_ragged_full_output(dev, kind):
         A, B = wl.make_random(w.M, w.N, w.K, seed=w.seed, kind="integer_pos")
     ref = oracle.gemm_relu(A, B)
     got = bits(run(A, B, dev))
-    assert tlg.plan(w.M, w.N, w.K)["variant_name"] == "tiled_dma"
+    assert tlg.plan(w.M, w.N, w.K)["variant_name"] == "tiled_pipe"
     if kind == "normal":
         assert_close(got, ref, "ragged")
         # the cross-check kernel is the sequential definition: bit-exact on any input
         assert np.array_equal(bits(run(A, B, dev, variant=V_NAIVE)), ref)
     else:
         assert np.array_equal(got, ref)
-        for v in (V_GEN, V_PIPE):  # the other families on the same ragged data
+        for v in (V_GEN, V_PIPE, V_DMA):  # the other families on the same ragged data
             assert np.array_equal(bits(run(A, B, dev, variant=v)), ref), v
 
 
 @pytest.mark.parametrize("config,splits", [(-1, 0), (0, 1), (0, 2), (0, 4), (0, 8), (0, 16), (1, 4), (2, 0), (3, 0),
-                                           (3, 2), (3, 5), (3, 16)])
+                                           (3, 2), (3, 5), (3, 16), (4, 0), (5, 0), (6, 0), (6, 1), (7, 0), (8, 0),
+                                           (8, 1), (9, 0), (10, 0)])
 def test_skinny_full_output(dev, config, splits):
     w = wl.WORKLOADS["skinny16x14336x4096"]
     A, B = wl.make_inputs(w)
@@ -146,23 +147,25 @@ def test_streamk_shapes(dev, shape):
         assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
 
 
+@pytest.mark.parametrize("config", [3, 4, 5, 6, 7, 8, 9, 10])
 @pytest.mark.parametrize("parts", [1, 3])
 @pytest.mark.parametrize("shape", [(16, 14336, 520), (1, 8, 8), (32, 264, 4096), (7, 128, 8192), (17, 392, 1000),
                                    (16, 64, 32), (31, 1032, 264)])
-def test_wave_split_shapes(dev, shape, parts):
+def test_wave_split_shapes(dev, shape, parts, config):
     """K split among the waves of a work-group (and among `parts`
-    work-groups per strip): fewer K blocks than waves or parts, ragged M and
-    N, K tails, one strip; NaN sentinel and padding columns. Each case runs
+    work-groups per strip), for every strip configuration (strip width,
+    waves, stages): fewer K blocks than waves or parts, ragged M and N, K
+    tails, one strip; NaN sentinel and padding columns. Each case runs
     twice: the strip counters must be back at zero after a call."""
     M, N, K = shape
     A, B = wl.make_random(M, N, K, seed=M + 5 * N + 3 * K, kind="integer_pos")
     ref = oracle.gemm_relu(A, B)
     for _ in range(2):
         big = torch.full((M + 1, N + 8), float("nan"), dtype=torch.float16, device=dev)
-        tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), out=big[:M, :N], variant=V_SPLIT, config=3, splits=parts)
+        tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), out=big[:M, :N], variant=V_SPLIT, config=config, splits=parts)
         torch.cuda.synchronize()
         allb = bits(big)
-        assert np.array_equal(allb[:M, :N], ref), shape
+        assert np.array_equal(allb[:M, :N], ref), (shape, config)
         assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
 
 
@@ -229,7 +232,7 @@ def test_large_square_sampled(dev, name):
     assert np.array_equal(got[rows], oracle.gemm_relu_rows(Ai, Bi, rows))
 
 
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("shape", [(300, 264, 200), (513, 520, 72), (1024, 1032, 1000), (256, 256, 8),
                                    (257, 8, 4104), (301, 259, 203)])
 def test_pipe_configs(dev, config, shape):
@@ -407,8 +410,8 @@ def test_padded_inputs_never_read(dev, pad_a, pad_b):
         assert np.array_equal(got, ref), (pad_a, pad_b, v)
 
 
-@pytest.mark.parametrize("variant", ["dma", "pipe"])
-def test_unaligned_base_pointers(dev, variant):
+@pytest.mark.parametrize("variant,config", [("dma", -1), ("pipe", -1), ("pipe", 5), ("pipe", 6)])
+def test_unaligned_base_pointers(dev, variant, config):
     """Views that start one element into their storage (2-byte aligned
     pointers, odd leading dimensions) through the direct-to-LDS kernels."""
     v = V_DMA if variant == "dma" else V_PIPE
@@ -420,7 +423,7 @@ def test_unaligned_base_pointers(dev, variant):
     As[:, 1:K + 1] = to_dev(A, dev)
     Bs[:, 1:N + 1] = to_dev(B, dev)
     big = torch.full((M, N + 3), float("nan"), dtype=torch.float16, device=dev)
-    tlg.gemm_relu(As[:, 1:K + 1], Bs[:, 1:N + 1], out=big[:, 1:N + 1], variant=v)
+    tlg.gemm_relu(As[:, 1:K + 1], Bs[:, 1:N + 1], out=big[:, 1:N + 1], variant=v, config=config)
     torch.cuda.synchronize()
     allb = bits(big)
     assert np.array_equal(allb[:, 1:N + 1], ref)

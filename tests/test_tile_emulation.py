@@ -22,9 +22,9 @@ CSRC = os.path.join(ROOT, "tiled_dense_gemm_06_amd", "csrc")
 
 ERR_NAMES = ["oob_global", "lds_multi", "lds_oob", "bank_conflict", "c_multi", "c_missing", "c_outside", "tile_dup"]
 # config ids understood by emu_gemm_relu (mirroring the kernels' tile tables; 3 is
-# the 64-deep two-stage layout of the pipelined kernel)
+# the 64-deep two-stage layout of the pipelined kernel, 6 and 7 its half tiles)
 DMA_CONFIGS = {0: (256, 256, 32), 1: (128, 128, 32), 2: (64, 64, 64), 3: (256, 256, 64), 4: (256, 256, 64),
-               5: (256, 256, 32)}
+               5: (256, 256, 32), 6: (256, 128, 64), 7: (128, 256, 64)}
 SPLIT_CONFIGS = {10: (32, 128, 64), 11: (32, 256, 64)}
 
 

@@ -23,6 +23,8 @@ from __future__ import annotations
 import argparse
 import json
 import math
+import os
+import re
 import sys
 import time
 
@@ -54,11 +56,13 @@ def candidates(tlg, M, N, K):
     """(variant, config, splits) triples the library accepts for this shape."""
     out = []
     trials = [(tlg.TLG_VARIANT_AUTO, -1, 0)]
-    trials += [(tlg.TLG_VARIANT_TILED_PIPE, c, 0) for c in range(5)]
+    trials += [(tlg.TLG_VARIANT_TILED_PIPE, c, 0) for c in range(7)]
     trials += [(tlg.TLG_VARIANT_TILED_DMA, c, 0) for c in range(5)]
     if M <= 64:
+        # two-kernel split-K (0, 1), stream-K tiles (2), strips with 1..8
+        # parts (3), the other strip shapes (4..8), stream-K strips (9, 10)
         trials += [(tlg.TLG_VARIANT_SPLITK, 3, s) for s in (1, 2, 4, 8)]
-        trials += [(tlg.TLG_VARIANT_SPLITK, c, 0) for c in (0, 1, 2)]
+        trials += [(tlg.TLG_VARIANT_SPLITK, c, 0) for c in (0, 1, 2) + tuple(range(4, 11))]
     for v, c, s in trials:
         try:
             p = tlg.plan(M, N, K, variant=v, config=c, splits=s)
@@ -124,6 +128,7 @@ def sweep(shapes, log=print):
             and r["splits"] in (0, auto_plan["splits"]))]
         best = min(others, key=lambda r: r["us"]) if others else auto
         results.append({"shape": [M, N, K], "class": list(shape_class(M, N, K)), "auto": auto, "best": best,
+                        "auto_splits": auto_plan["splits"],
                         "all": rows})
         log(f"{M}x{N}x{K}: auto {auto['name']} {auto['us']:.1f} us, best {best['name']} (splits {best['splits']}) "
             f"{best['us']:.1f} us")
@@ -132,25 +137,102 @@ def sweep(shapes, log=print):
     return results
 
 
-def table_text(results, device: str) -> str:
+def class_groups(results):
+    """Measured shapes grouped by their shape class, in measurement order."""
+    groups = {}
+    for r in results:
+        groups.setdefault(tuple(r["class"]), []).append(r)
+    return groups
+
+
+def class_choice(rs):
+    """The entry for one class: among the choices that differ from the
+    heuristic's on some shape of the class, the (variant, config, splits)
+    with the least total time over the class's measured shapes, kept if that
+    total beats the heuristic's by MARGIN and no shape of the class runs more
+    than 2 % slower than with the heuristic; else None. The heuristic's time
+    on a shape is the best of its own timing and forced runs of the same
+    choice. Returns (key, name, total us, heuristic total us)."""
+    def key(row):
+        return (row["variant"], row["config"], row["splits"])
+
+    def same(r, k):  # k is what the heuristic runs on shape r
+        return (r["auto"]["variant"], r["auto"]["config"]) == k[:2] and k[2] in (0, r.get("auto_splits", 0))
+
+    base = [min([r["auto"]["us"]] + [x["us"] for x in r["all"] if not x["auto"] and same(r, key(x))]) for r in rs]
+    common = None
+    for r in rs:
+        ks = {key(x) for x in r["all"] if not x["auto"]}
+        common = ks if common is None else common & ks
+    best = None
+    for k in sorted(common or ()):
+        if all(same(r, k) for r in rs):
+            continue
+        us = [min(x["us"] for x in r["all"] if not x["auto"] and key(x) == k) for r in rs]
+        if best is None or sum(us) < best[1]:
+            best = (k, sum(us), us)
+    if best is None:
+        return None
+    k, total, us = best
+    if total > sum(base) * (1 - MARGIN) or any(u > b * 1.02 for u, b in zip(us, base)):
+        return None
+    name = next(x["name"] for x in rs[0]["all"] if key(x) == k)
+    return k, name, total, sum(base)
+
+
+_ENTRY = re.compile(r"^\s*\{(-?\d+), (-?\d+), (-?\d+), (-?\d+), (-?\d+), (-?\d+), (-?\d+)\},")
+
+
+def previous_entries(path: str) -> list:
+    """(class, (variant, config, splits), line) of each entry of an existing table."""
+    out = []
+    if not path or not os.path.exists(path):
+        return out
+    with open(path) as f:
+        for line in f:
+            m = _ENTRY.match(line)
+            if m:
+                v = [int(x) for x in m.groups()]
+                if v[0] >= 0:
+                    out.append((tuple(v[:4]), tuple(v[4:]), line.rstrip("\n")))
+    return out
+
+
+def table_text(results, device: str, previous=()) -> str:
     lines = ["// Tuned kernel choices by shape class, written by",
              "//   python -m tiled_dense_gemm_06_amd.autotune",
              f"// on {device}. Class: ceil(log2) of M, N, K and whether K or N is not a",
              f"// multiple of 8. An entry is kept when it beat the heuristic by more than {MARGIN:.0%};",
-             "// each comment gives the measured shape and both times.",
+             "// each comment gives the measured shape and both times. Entries of the previous",
+             "// table stay while their kernel is still the one chosen for their class.",
              "static const TuneEntry kTuneTable[] = {"]
-    seen = set()
     n = 0
-    for r in results:
-        cls = tuple(r["class"])
-        a, b = r["auto"], r["best"]
-        if cls in seen or b is a or b["us"] > a["us"] * (1 - MARGIN):
+    new_classes = set()
+    for cls, rs in class_groups(results).items():
+        pick = class_choice(rs)
+        if pick is None:
             continue
-        seen.add(cls)
-        M, N, K = r["shape"]
-        lines.append(f"    {{{cls[0]}, {cls[1]}, {cls[2]}, {cls[3]}, {b['variant']}, {b['config']}, {b['splits']}}},"
-                     f"  // {M}x{N}x{K}: {b['name']} {b['us']:.1f} us vs {a['name']} {a['us']:.1f} us")
+        new_classes.add(cls)
+        key, name, ours, theirs = pick
+        first = "x".join(map(str, rs[0]["shape"]))
+        more = "".join(f", {'x'.join(map(str, r['shape']))}" for r in rs[1:])
+        lines.append(f"    {{{cls[0]}, {cls[1]}, {cls[2]}, {cls[3]}, {key[0]}, {key[1]}, {key[2]}}},"
+                     f"  // {first}: {name} {ours:.1f} us vs {rs[0]['auto']['name']} {theirs:.1f} us"
+                     + (f" (totals over {first}{more})" if more else ""))
         n += 1
+    # The sweep runs against the library as built, so a class the table
+    # already serves measures the tuned kernel as "the heuristic". Such an
+    # entry stays (with its original measurement) while its kernel is still
+    # what the library ran on every measured shape of the class and no new
+    # entry replaced it.
+    groups = class_groups(results)
+    for cls, key, line in previous:
+        rs = groups.get(cls, [])
+        if cls in new_classes or not rs:
+            continue
+        if all((r["auto"]["variant"], r["auto"]["config"]) == key[:2] for r in rs):
+            lines.append(line)
+            n += 1
     if n == 0:
         lines.append("    {-1, -1, -1, -1, 0, -1, 0},  // no shape beat the heuristic by the margin")
     lines.append("};")
@@ -162,18 +244,32 @@ def main():
     ap.add_argument("--out", required=True, help="the table to write (csrc/tune_table.inc)")
     ap.add_argument("--json", help="also write every timing here")
     ap.add_argument("--quick", action="store_true", help="the first four shapes only")
+    ap.add_argument("--previous", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc",
+                                                       "tune_table.inc"),
+                    help="the table the library was built with (its entries are kept while still chosen)")
+    ap.add_argument("--from-json", help="no sweep: write the table from the timings a sweep saved with --json")
     args = ap.parse_args()
+    previous = previous_entries(args.previous)
+    if args.from_json:
+        with open(args.from_json) as f:
+            saved = json.load(f)
+        text = table_text(saved["results"], saved["device"], previous)
+        with open(args.out, "w") as f:
+            f.write(text)
+        return 0
     import torch
 
     shapes = SHAPES[:4] if args.quick else SHAPES
     t0 = time.time()
     res = sweep(shapes, log=lambda s: print(s, flush=True))
     name = torch.cuda.get_device_properties(0).gcnArchName.split(":")[0]
+    device = f"{name}, {len(shapes)} shapes, {time.time() - t0:.0f} s"
+    text = table_text(res, device, previous)
     with open(args.out, "w") as f:
-        f.write(table_text(res, f"{name}, {len(shapes)} shapes, {time.time() - t0:.0f} s"))
+        f.write(text)
     if args.json:
         with open(args.json, "w") as f:
-            json.dump(res, f, indent=1)
+            json.dump({"device": device, "results": res}, f, indent=1)
     return 0
 
 

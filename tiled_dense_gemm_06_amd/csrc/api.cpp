@@ -191,12 +191,17 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
         if (!config_ok(config, tlg::SPLIT_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
         // K split among the waves of a work-group per column strip, when M
         // fits one strip and there are strips for at least half the CUs
-        const tlg::TileConfig &ts = tlg::kStripConfig;
-        const int64_t strips = ceil_div(p.N, ts.bn);
-        const bool strip_ok = p.M <= ts.bm && dma_ok_aligned(p, ts.bm, ts.bn, ts.bk) && strips <= 0x7fffffff;
         int cfg = config;
-        if (cfg < 0) cfg = strip_ok ? tlg::SPLIT_WAVES_32x64x64 : tlg::SPLIT_STREAMK_32x128x64;
-        if (cfg == tlg::SPLIT_WAVES_32x64x64) {
+        if (cfg < 0) {
+            const tlg::TileConfig &t0 = tlg::kStripConfig;
+            const bool ok0 = p.M <= t0.bm && dma_ok_aligned(p, t0.bm, t0.bn, t0.bk) &&
+                             ceil_div(p.N, t0.bn) <= 0x7fffffff;
+            cfg = ok0 ? tlg::SPLIT_WAVES_32x64x64 : tlg::SPLIT_STREAMK_32x128x64;
+        }
+        if (tlg::is_strip_config(cfg)) {
+            const tlg::TileConfig &ts = tlg::kStripConfigs[cfg - tlg::SPLIT_WAVES_32x64x64];
+            const int64_t strips = ceil_div(p.N, ts.bn);
+            const bool strip_ok = p.M <= ts.bm && dma_ok_aligned(p, ts.bm, ts.bn, ts.bk) && strips <= 0x7fffffff;
             if (!strip_ok) return TLG_ERROR_NOT_SUPPORTED;
             // parts per strip: forced, else as many as fit the CUs whole
             // (1x4096x4096: 4 parts 12 us vs 1 part 23 us; 16x14336x4096:
@@ -212,6 +217,24 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
             if (parts > 1 && strips * 4 > kCounterBytes) parts = 1;
             const int64_t ws = parts > 1 ? kCounterBytes + strips * parts * slot_bytes : 0;
             fill_info(o, TLG_VARIANT_SPLITK, cfg, &ts, (int)parts, 1, strips * parts, ws);
+            return TLG_SUCCESS;
+        }
+        if (tlg::is_strip_sk_config(cfg)) {
+            // stream-K over strips: one (three-stage) or two (two-stage)
+            // work-groups per CU, each taking an equal range of the strips'
+            // K blocks; needs at least one range per strip
+            const int j = cfg - tlg::SPLIT_STRIP_SK_32x64x64;
+            const tlg::TileConfig &ts = tlg::kStripSkConfigs[j];
+            const int64_t strips = ceil_div(p.N, ts.bn);
+            const int64_t total = strips * ceil_div(p.K, ts.bk);
+            int64_t grid = (int64_t)cus * (j == 0 ? 1 : 2);
+            if (grid > total) grid = total;
+            const int64_t slot_bytes = 2ll * ts.bm * ts.bn * 4;
+            const bool ok = p.M <= ts.bm && dma_ok_aligned(p, ts.bm, ts.bn, ts.bk) && strips <= grid &&
+                            strips * 4 <= kCounterBytes && grid * slot_bytes <= cap && total < (1ll << 40);
+            if (!ok) return TLG_ERROR_NOT_SUPPORTED;
+            fill_info(o, TLG_VARIANT_SPLITK, cfg, &ts, (int)ceil_div(grid, strips), 1, grid,
+                      kCounterBytes + grid * slot_bytes);
             return TLG_SUCCESS;
         }
         if (cfg == tlg::SPLIT_STREAMK_32x128x64) {
@@ -332,8 +355,12 @@ tlg_status run(tlg_handle h, int32_t variant, int32_t config, int32_t splits, co
         case TLG_VARIANT_PINGPONG: e = tlg::launch_pingpong(info.config, p, stream); break;
         case TLG_VARIANT_SPLITK: {
             float *partials = h->workspace + kCounterBytes / sizeof(float);
-            if (info.config == tlg::SPLIT_WAVES_32x64x64)
-                e = tlg::launch_skinny_strip(p, info.splits, partials, (int *)h->workspace, stream);
+            if (tlg::is_strip_sk_config(info.config))
+                e = tlg::launch_skinny_strip_sk(info.config - tlg::SPLIT_STRIP_SK_32x64x64, p, (int)info.grid,
+                                                partials, (int *)h->workspace, stream);
+            else if (tlg::is_strip_config(info.config))
+                e = tlg::launch_skinny_strip(info.config - tlg::SPLIT_WAVES_32x64x64, p, info.splits, partials,
+                                             (int *)h->workspace, stream);
             else if (info.config == tlg::SPLIT_STREAMK_32x128x64)
                 e = tlg::launch_streamk(p, (int)info.grid, partials, (int *)h->workspace, stream);
             else
@@ -657,7 +684,9 @@ const char *tlg_plan_config_name(int32_t variant, int32_t config) {
             return (config >= 0 && config < tlg::GEN_CONFIGS) ? tlg::kGenConfigs[config].name : "";
         case TLG_VARIANT_SPLITK:
             if (config == tlg::SPLIT_STREAMK_32x128x64) return tlg::kStreamKConfig.name;
-            if (config == tlg::SPLIT_WAVES_32x64x64) return tlg::kStripConfig.name;
+            if (tlg::is_strip_config(config)) return tlg::kStripConfigs[config - tlg::SPLIT_WAVES_32x64x64].name;
+            if (tlg::is_strip_sk_config(config))
+                return tlg::kStripSkConfigs[config - tlg::SPLIT_STRIP_SK_32x64x64].name;
             return (config >= 0 && config < tlg::SPLIT_TWO_KERNEL_CONFIGS) ? tlg::kSplitConfigs[config].name : "";
         case TLG_VARIANT_TILED_PIPE:
             return (config >= 0 && config < tlg::PIPE_CONFIGS) ? tlg::kPipeConfigs[config].name : "";

@@ -267,6 +267,10 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
 using Pipe256x32 = TileShape<256, 256, 32, 2, 2, 4>;
 using Pipe256x64 = TileShape<256, 256, 64, 2, 2, 2>;
 using Pipe256x64w8 = TileShape<256, 256, 64, 2, 4, 2>;  // eight waves, two per SIMD
+// half tiles (four waves of 128 x 64, three stages): twice the tiles of
+// 256 x 256 for problems that leave CUs idle at that size
+using Pipe256x128 = TileShape<256, 128, 64, 2, 2, 3>;
+using Pipe128x256 = TileShape<128, 256, 64, 1, 4, 3>;
 
 const TileConfig kPipeConfigs[PIPE_CONFIGS] = {
     {Pipe256x32::BM, Pipe256x32::BN, Pipe256x32::BK, Pipe256x32::NT, Pipe256x32::STAGES, "pipe_256x256x32_w2x2_s4"},
@@ -276,6 +280,10 @@ const TileConfig kPipeConfigs[PIPE_CONFIGS] = {
      "pipe_256x256x64_w2x4_s2"},
     {Pipe256x64w8::BM, Pipe256x64w8::BN, Pipe256x64w8::BK, Pipe256x64w8::NT, Pipe256x64w8::STAGES,
      "pipe_256x256x64_w2x4_s2_a3"},
+    {Pipe256x128::BM, Pipe256x128::BN, Pipe256x128::BK, Pipe256x128::NT, Pipe256x128::STAGES,
+     "pipe_256x128x64_w2x2_s3"},
+    {Pipe128x256::BM, Pipe128x256::BN, Pipe128x256::BK, Pipe128x256::NT, Pipe128x256::STAGES,
+     "pipe_128x256x64_w1x4_s3"},
 };
 
 template <class S, int SPACING, int DOFF, int ASTAGES, bool BT = false>
@@ -322,6 +330,9 @@ hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream) {
         // eight waves (two per SIMD, 128 x 64 each): 8 loads per wave and stage
         case PIPE_256x256x64_W8: return launch_pipe_t<Pipe256x64w8, 2, 1, 2>(p, stream);
         case PIPE_256x256x64_W8_A3: return launch_pipe_t<Pipe256x64w8, 2, 1, 3>(p, stream);
+        // half tiles: 12 loads per wave and stage, every 2 slots
+        case PIPE_256x128x64: return launch_pipe_t<Pipe256x128, 2, 1, 3>(p, stream);
+        case PIPE_128x256x64: return launch_pipe_t<Pipe128x256, 2, 1, 3>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

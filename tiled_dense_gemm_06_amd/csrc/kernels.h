@@ -42,10 +42,18 @@ enum DmaConfig {
 enum GenConfig { GEN_128x128x32 = 0, GEN_64x64x32 = 1, GEN_CONFIGS = 2 };
 // split-K partial kernels (direct-to-LDS, aligned)
 // (indices 0 and 1: two kernels, partials then an ordered reduce; index 2:
-// one stream-K kernel that finishes split tiles itself; index 3: 64-column
-// strips, K split among work-groups and their waves, M <= 32)
+// one stream-K kernel that finishes split tiles itself; indices 3 and up:
+// column strips, K split among work-groups and their waves, M <= 32)
 enum SplitConfig { SPLIT_32x128x64 = 0, SPLIT_32x256x64 = 1, SPLIT_TWO_KERNEL_CONFIGS = 2,
-                   SPLIT_STREAMK_32x128x64 = 2, SPLIT_WAVES_32x64x64 = 3, SPLIT_CONFIGS = 4 };
+                   SPLIT_STREAMK_32x128x64 = 2, SPLIT_WAVES_32x64x64 = 3, SPLIT_WAVES_32x64x64_W4 = 4,
+                   SPLIT_WAVES_32x64x64_S4 = 5, SPLIT_WAVES_32x128x64 = 6, SPLIT_WAVES_32x128x64_W4 = 7,
+                   SPLIT_WAVES_32x256x32 = 8, SPLIT_STRIP_SK_32x64x64 = 9, SPLIT_STRIP_SK_32x64x64_S2 = 10,
+                   SPLIT_CONFIGS = 11 };
+// strip configuration j is split configuration SPLIT_WAVES_32x64x64 + j
+constexpr int STRIP_CONFIGS = SPLIT_STRIP_SK_32x64x64 - SPLIT_WAVES_32x64x64;
+inline bool is_strip_config(int config) { return config >= SPLIT_WAVES_32x64x64 && config < SPLIT_STRIP_SK_32x64x64; }
+// stream-K strip configuration j is split configuration SPLIT_STRIP_SK_32x64x64 + j
+inline bool is_strip_sk_config(int config) { return config >= SPLIT_STRIP_SK_32x64x64 && config < SPLIT_CONFIGS; }
 // software-pipelined direct-to-LDS kernels (aligned, large problems)
 enum PipeConfig {
     PIPE_256x256x32 = 0,
@@ -53,7 +61,9 @@ enum PipeConfig {
     PIPE_256x256x64_A3 = 2,
     PIPE_256x256x64_W8 = 3,  // eight waves, two per SIMD
     PIPE_256x256x64_W8_A3 = 4,
-    PIPE_CONFIGS = 5
+    PIPE_256x128x64 = 5,  // four waves of 128 x 64, three stages
+    PIPE_128x256x64 = 6,
+    PIPE_CONFIGS = 7
 };
 
 // wave-role (ping-pong) schedule: two groups of waves alternate between
@@ -86,12 +96,23 @@ hipError_t launch_splitk(int config, int splits, int64_t k_split, const Problem 
 extern const TileConfig kStreamKConfig;
 constexpr int kStreamKBlocksPerCU = 2;  // 80 KiB of LDS per work-group, 160 KiB per CU
 hipError_t launch_streamk(const Problem &p, int grid, float *partials, int *counters, hipStream_t stream);
-// Skinny strips (M <= 32): `parts` work-groups per 64 columns, each taking a
-// contiguous part of K split among its waves and reduced in LDS in wave
-// order; with parts > 1 the parts meet through `partials` (strips x parts x
-// 32 x 64 fp32) and `counters` (one int per strip, zero on entry and exit).
-extern const TileConfig kStripConfig;
-hipError_t launch_skinny_strip(const Problem &p, int parts, float *partials, int *counters, hipStream_t stream);
+// Skinny strips (M <= 32): `parts` work-groups per strip of bn columns, each
+// taking a contiguous part of K split among its waves and reduced in LDS in
+// wave order; with parts > 1 the parts meet through `partials` (strips x
+// parts x bm x bn fp32) and `counters` (one int per strip, zero on entry and
+// exit). `config` indexes kStripConfigs; kStripConfig is the default.
+extern const TileConfig kStripConfigs[STRIP_CONFIGS];
+extern const TileConfig &kStripConfig;
+hipError_t launch_skinny_strip(int config, const Problem &p, int parts, float *partials, int *counters,
+                               hipStream_t stream);
+// Stream-K over strips (M <= 32, at most `grid` strips): the strips' K blocks
+// in one strip-major sequence, split into `grid` equal ranges; a strip split
+// between ranges is finished in the kernel through `partials` (grid x 2 x
+// bm x bn fp32) and `counters` (one int per strip, zero on entry and exit).
+constexpr int STRIP_SK_CONFIGS = 2;
+extern const TileConfig kStripSkConfigs[STRIP_SK_CONFIGS];
+hipError_t launch_skinny_strip_sk(int config, const Problem &p, int grid, float *partials, int *counters,
+                                  hipStream_t stream);
 // Block-scaled (MX) problem: A (M x K codes) and B (N x K codes, i.e. B
 // transposed), their scale bytes (M x K/32, N x K/32), fp16 C. Leading
 // dimensions of A and B in elements (codes), of the scales in bytes, of C
