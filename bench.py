@@ -7,10 +7,16 @@ already resident in HBM. The default workload is M = N = K = 8192 with
 U[-1,1] inputs from seed 4. The other workloads are accepted with
 --workload for measurement runs; the parity tests cover them all.
 
+The timed steps are captured in a HIP graph and one replay is timed between
+two HIP events on the launch stream (--eager: each step launched from the
+host between its own pair of events instead).
+
 Prints one JSON line: the contract fields, plus
   roofline     - the dominant kernel's achieved rate (algorithmic FLOP or bytes
                  per launch / its average launch duration from HIP events on
-                 the stream it runs on) against the MI355X peak;
+                 the stream it runs on: the replay time over the steps, or the
+                 mean of the per-launch event pairs with --eager) against the
+                 MI355X peak;
   cpu_baseline - the CPU oracle timed on a bounded sample of the same workload
                  (sampled output rows), in the same unit.
 """
@@ -32,6 +38,54 @@ METRIC = "GEMM+ReLU TFLOPS (fp16 in, fp32 acc) at 8192³ and % of fp16 MFMA peak
 PEAK_MFMA_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20  # MI355X Infinity Cache; rotated buffers exceed twice this
+def time_steps(torch, step, steps: int, warmup: int, graph: bool) -> dict:
+    """Run `warmup` untimed steps, then time `steps` steps on the current stream.
+
+    step(i, stream) enqueues step i on `stream`. With graph=True the timed
+    steps are captured once into a HIP graph and replayed (one untimed
+    replay, then one timed replay between two events on the launch stream),
+    so the device runs them back to back without the host's per-call launch
+    cost; every launch's average duration is then the replay time / steps.
+    With graph=False each step is bracketed by its own pair of events."""
+    import numpy as np
+
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i, stream)
+    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            for i in range(steps):
+                step(i, cs)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = e0.elapsed_time(e1) / steps
+        del g
+        return {"ms_per_step": ms, "launch_ms_avg": ms, "launch_ms_min": None, "wall": wall, "timing": "hip_graph"}
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step(i, stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return {"ms_per_step": starts[0].elapsed_time(ends[-1]) / steps,
+            "launch_ms_avg": float(np.mean(per_launch_ms)), "launch_ms_min": float(np.min(per_launch_ms)),
+            "wall": wall, "timing": "events_per_launch"}
+
+
 def cpu_model() -> str:
     """The host CPU's model name (/proc/cpuinfo), or "" where unavailable."""
     try:
@@ -123,7 +177,6 @@ def bench_mx(args, torch, tlg, wl, dev) -> int:
     sets = [ins] + [[x.clone() for x in ins] for _ in range(R - 1)]
     Cs = [torch.empty((w.M, w.N), dtype=torch.float16, device=dev) for _ in range(R)]
     h = tlg.handle_for(dev)
-    stream = torch.cuda.current_stream(dev)
 
     G = args.grouped
     if G and not 2 <= G <= 16:
@@ -135,7 +188,7 @@ def bench_mx(args, torch, tlg, wl, dev) -> int:
         gcfg = args.config if args.config >= 0 else (0 if t256 > 128 else 1)
         plan = {"config_name": tlg._native.tlg_plan_mx_config_name(gcfg)}
 
-    def step(i):
+    def step(i, stream):
         a, sa, b, sb = sets[i % R]
         if G:
             tlg.gemm_relu_mx_grouped(fmt, [a[r0:r1] for r0, r1 in rows], [sa[r0:r1] for r0, r1 in rows], [b] * G,
@@ -144,22 +197,11 @@ def bench_mx(args, torch, tlg, wl, dev) -> int:
         else:
             tlg.gemm_relu_mx(fmt, a, sa, b, sb, out=Cs[i % R], config=args.config, handle=h, stream=stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
     K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    t0 = time.perf_counter()
-    for i in range(K):
-        starts[i].record(stream)
-        step(i)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_per_step = starts[0].elapsed_time(ends[-1]) / K
-    avg_launch_s = float(np.mean(per_launch_ms)) / 1e3
+    tm = time_steps(torch, step, K, args.warmup, graph=not args.eager)
+    wall = tm["wall"]
+    ms_per_step = tm["ms_per_step"]
+    avg_launch_s = tm["launch_ms_avg"] / 1e3
     tflops = w.flop / (ms_per_step / 1e3) / 1e12
     peak = PEAK_MX_TFLOPS[fmt]
     achieved = w.flop / avg_launch_s / 1e12
@@ -171,13 +213,14 @@ def bench_mx(args, torch, tlg, wl, dev) -> int:
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "seed": w.seed,
                    "inputs": "random codes (exponents bias-3..bias+3, 1 in 16 zero/subnormal), scales 2^-2..2^2",
                    "kernel": plan["config_name"], "grouped": G, "rotated_buffers": R, "alg_bytes": alg_bytes,
+                   "timing": tm["timing"],
                    "accumulate": "f32", "epilogue": "relu, round-to-nearest-even to f16"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak,
                      "traffic": measured_traffic(f"{w.name}_mx_{fmt}", plan["config_name"])
                      if args.config < 0 and not G else None,
                      "kernel": plan["config_name"],
-                     "launch_ms_avg": avg_launch_s * 1e3, "launch_ms_min": float(np.min(per_launch_ms))},
+                     "launch_ms_avg": avg_launch_s * 1e3, "launch_ms_min": tm["launch_ms_min"]},
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:
@@ -229,6 +272,10 @@ def main() -> int:
                          "call (the blocks share B); the work per step is unchanged")
     ap.add_argument("--mx", choices=["e4m3", "e5m2", "e2m1"],
                     help="time the block-scaled path (tlg_gemm_relu_mx) with these element codes instead")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the timed steps one by one from the host, each between its own pair of events "
+                         "(default: capture them in a HIP graph and time one replay, which removes the host's "
+                         "per-call launch cost)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, time a plain device-to-device copy of MIB MiB (the reference "
                          "kernel for scaling the HBM byte counters)")
@@ -293,9 +340,8 @@ def main() -> int:
     Bs = [Bd0] + [Bd0.clone() for _ in range(R - 1)]
     Cs = [torch.empty((w.M, w.N), dtype=torch.float16, device=dev) for _ in range(R)]
     h = tlg.handle_for(dev)
-    stream = torch.cuda.current_stream(dev)
 
-    def step(i):
+    def step(i, stream):
         j = i % R
         if args.grouped:
             tlg.gemm_relu_grouped([As[j][r0:r1] for r0, r1 in rows], [Bs[j]] * len(rows),
@@ -305,25 +351,11 @@ def main() -> int:
             tlg.gemm_relu(As[j], Bs[j], out=Cs[j], handle=h, stream=stream, variant=variant, config=args.config,
                           splits=args.splits, trans_b=args.trans_b)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
     K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        starts[i].record(stream)
-        step(i)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    span_ms = starts[0].elapsed_time(ends[-1])
-    ms_per_step = span_ms / K
-    avg_launch_s = float(np.mean(per_launch_ms)) / 1e3
+    tm = time_steps(torch, step, K, args.warmup, graph=not args.eager)
+    wall = tm["wall"]
+    ms_per_step = tm["ms_per_step"]
+    avg_launch_s = tm["launch_ms_avg"] / 1e3
 
     tflops = w.flop / (ms_per_step / 1e3) / 1e12
     if plan["variant_name"] == "splitk" or w.flop / w.alg_bytes < 314.6:
@@ -338,7 +370,7 @@ def main() -> int:
     roof["traffic"] = measured_traffic(w.name, plan["config_name"]) if plain else None
     roof["kernel"] = plan["config_name"]
     roof["launch_ms_avg"] = avg_launch_s * 1e3
-    roof["launch_ms_min"] = float(np.min(per_launch_ms))
+    roof["launch_ms_min"] = tm["launch_ms_min"]
 
     props = torch.cuda.get_device_properties(dev)
     out = {
@@ -348,7 +380,7 @@ def main() -> int:
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "seed": w.seed, "inputs": w.description,
                    "lda": w.K, "ldb": w.N, "ldc": w.N, "kernel": plan["config_name"],
                    "variant": plan["variant_name"], "splits": plan["splits"], "rotated_buffers": R,
-                   "trans_b": bool(args.trans_b), "grouped": args.grouped,
+                   "trans_b": bool(args.trans_b), "grouped": args.grouped, "timing": tm["timing"],
                    "accumulate": "f32", "epilogue": "relu, round-to-nearest-even to f16"},
         "roofline": roof,
         "pct_of_fp16_peak": 100.0 * tflops / PEAK_MFMA_TFLOPS,

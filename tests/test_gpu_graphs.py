@@ -1,0 +1,89 @@
+"""HIP-graph capture and replay of the library's calls (bench.py times its steps
+this way, and callers that launch many small problems do the same).
+
+Every kernel family is captured, including the split-K forms that keep tile
+or strip counters in the handle's workspace and rely on each call leaving
+them at zero: a graph of three calls is replayed several times, with other
+eager calls of the library and host synchronisations between the replays,
+and every replay's outputs (cleared to NaN before it) must equal the oracle
+bit for bit on integer-valued inputs, as the eager calls do.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import tiled_dense_gemm_06_amd as tlg
+from tiled_dense_gemm_06_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+V_AUTO = tlg.TLG_VARIANT_AUTO
+V_DMA = tlg.TLG_VARIANT_TILED_DMA
+V_PIPE = tlg.TLG_VARIANT_TILED_PIPE
+V_SPLIT = tlg.TLG_VARIANT_SPLITK
+
+# (M, N, K), variant, config, splits
+CASES = [
+    ((512, 512, 264), V_PIPE, -1, 0),          # pipelined 256 x 256
+    ((301, 259, 203), V_PIPE, 6, 0),           # pipelined 128 x 256, ragged, K tail
+    ((300, 264, 200), V_DMA, -1, 0),           # direct-to-LDS tiles
+    ((16, 2048, 4096), V_SPLIT, 3, 4),         # strips in 4 parts: strip counters and partial slots
+    ((16, 14336, 520), V_SPLIT, 9, 0),         # stream-K over strips: strip counters
+    ((40, 264, 4096), V_SPLIT, 2, 0),          # stream-K tiles: tile counters
+    ((48, 1024, 2048), V_SPLIT, 0, 4),         # two kernels: partials, then the ordered reduce
+    ((16, 8192, 1024), V_AUTO, -1, 0),         # the default skinny path
+]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def bits(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("shape,variant,config,splits", CASES)
+def test_graph_replays_match_oracle(dev, shape, variant, config, splits):
+    M, N, K = shape
+    print(f"graph {shape} variant={variant} config={config} splits={splits}", flush=True)
+    ins = [wl.make_random(M, N, K, seed=M + 7 * N + 13 * K + s, kind="integer") for s in range(3)]
+    refs = [oracle.gemm_relu(A, B) for A, B in ins]
+    As = [torch.from_numpy(A).to(dev) for A, _ in ins]
+    Bs = [torch.from_numpy(B).to(dev) for _, B in ins]
+    Cs = [torch.full((M, N), float("nan"), dtype=torch.float16, device=dev) for _ in range(3)]
+    h = tlg.handle_for(dev)
+
+    def calls():
+        for A, B, C in zip(As, Bs, Cs):
+            tlg.gemm_relu(A, B, out=C, handle=h, variant=variant, config=config, splits=splits)
+
+    calls()  # eager first (the handle exists before the capture)
+    torch.cuda.synchronize()
+    for C, ref in zip(Cs, refs):
+        assert np.array_equal(bits(C), ref), "eager"
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    # other eager work of the library between replays (uses the same handle)
+    Ao, Bo = wl.make_random(64, 1024, 512, seed=99, kind="integer")
+    Aod, Bod = torch.from_numpy(Ao).to(dev), torch.from_numpy(Bo).to(dev)
+    ref_o = oracle.gemm_relu(Ao, Bo)
+    for rep in range(4):
+        for C in Cs:
+            C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (C, ref) in enumerate(zip(Cs, refs)):
+            assert np.array_equal(bits(C), ref), f"replay {rep}, call {i}"
+        Co = tlg.gemm_relu(Aod, Bod, handle=h, variant=V_SPLIT)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(Co), ref_o), f"eager call after replay {rep}"
+    del g
