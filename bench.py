@@ -86,6 +86,34 @@ def time_steps(torch, step, steps: int, warmup: int, graph: bool) -> dict:
             "wall": wall, "timing": "events_per_launch"}
 
 
+def gpu_sysfs_info(props) -> dict:
+    """Peak shader clock (the top level of pp_dpm_sclk, MHz) and the compute and
+    memory partition modes of the device, read from its PCI sysfs node; None
+    for whatever the node does not show."""
+    out = {"sclk_peak_mhz": None, "compute_partition": None, "memory_partition": None}
+    try:
+        node = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+    except AttributeError:
+        return out
+
+    def read(name):
+        try:
+            with open(os.path.join(node, name)) as f:
+                return f.read()
+        except OSError:
+            return None
+
+    levels = read("pp_dpm_sclk")
+    if levels:
+        mhz = [int(tok[:-3]) for tok in levels.split() if tok.lower().endswith("mhz") and tok[:-3].isdigit()]
+        out["sclk_peak_mhz"] = max(mhz) if mhz else None
+    for key, name in (("compute_partition", "current_compute_partition"),
+                      ("memory_partition", "current_memory_partition")):
+        v = read(name)
+        out[key] = v.strip() if v else None
+    return out
+
+
 def cpu_model() -> str:
     """The host CPU's model name (/proc/cpuinfo), or "" where unavailable."""
     try:
@@ -386,7 +414,7 @@ def main() -> int:
         "pct_of_fp16_peak": 100.0 * tflops / PEAK_MFMA_TFLOPS,
         "wall_s_timed": wall,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
-                   "cus": props.multi_processor_count},
+                   "cus": props.multi_processor_count, **gpu_sysfs_info(props)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
