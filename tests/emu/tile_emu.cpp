@@ -401,6 +401,62 @@ extern "C" int emu_gemm_relu_bt(int config, int M, int N, int K, const uint16_t 
 // piece ends a range that began in an earlier tile), never both slots taken
 // by two split tiles of one work-group in the same slot. Returns the number
 // of violations.
+// Stream-K over strips (G >= strips): every range touches at most two
+// strips, its parts cover each block exactly once, the blocks counted into a
+// strip add up to nkb exactly when its last part arrives, a part is whole
+// only when it is the strip's only part, and the slot a finisher reads for a
+// contributor (slot 0 iff the contributor's range starts inside the strip)
+// is the one that contributor wrote its part of this strip to.
+extern "C" long emu_check_strip_sk(int strips, int nkb, int G) {
+    long bad = 0;
+    const int64_t T = (int64_t)strips * nkb;
+    if (G > T) G = (int)T;
+    std::vector<int> seen((size_t)T, 0);
+    std::vector<int64_t> counted((size_t)strips, 0);
+    std::vector<int> parts((size_t)strips, 0), whole((size_t)strips, 0);
+    std::vector<int> slot_strip(2 * (size_t)G, -1);  // strip each written slot holds
+    for (int g = 0; g < G; ++g) {
+        const int64_t beg = sk_begin(g, T, G), end = sk_begin(g + 1, T, G);
+        if (beg == end) continue;
+        if (end - beg > nkb) bad++;
+        const StripSegments sg = strip_segments(beg, end, nkb);
+        if (sg.s0 < 0 || sg.s0 >= strips || (sg.two && sg.s0 + 1 >= strips)) { bad++; continue; }
+        if (end > sg.bound + nkb) bad++;  // a third strip would be lost
+        for (int q = 0; q < (sg.two ? 2 : 1); ++q) {
+            const int s = sg.s0 + q;
+            const int64_t lo = q == 0 ? beg : sg.bound, n = strip_part_blocks(sg, beg, end, q);
+            if (n <= 0) bad++;
+            for (int64_t u = lo; u < lo + n; ++u) {
+                if (u / nkb != s) bad++;
+                seen[(size_t)u]++;
+            }
+            counted[(size_t)s] += n;
+            parts[(size_t)s]++;
+            if (strip_part_whole(sg, beg, end, nkb, q)) whole[(size_t)s]++;
+            else slot_strip[2 * (size_t)g + q] = s;
+        }
+    }
+    for (int64_t u = 0; u < T; ++u)
+        if (seen[(size_t)u] != 1) bad++;
+    for (int s = 0; s < strips; ++s) {
+        if (counted[(size_t)s] != nkb) bad++;
+        if (whole[(size_t)s] != (parts[(size_t)s] == 1 ? 1 : 0)) bad++;
+        if (parts[(size_t)s] == 1) continue;
+        const int64_t first = (int64_t)s * nkb;
+        const int g0 = sk_owner(first, T, G), g1 = sk_owner(first + nkb - 1, T, G);
+        int found = 0;
+        for (int gg = g0; gg <= g1; ++gg) {
+            const int64_t gb = sk_begin(gg, T, G);
+            if (sk_begin(gg + 1, T, G) == gb) continue;
+            const int slot = gb >= first ? 0 : 1;
+            if (slot_strip[2 * (size_t)gg + slot] != s) bad++;
+            found++;
+        }
+        if (found != parts[(size_t)s]) bad++;
+    }
+    return bad;
+}
+
 extern "C" long emu_check_streamk(long total, int G, int ipt) {
     long bad = 0;
     if (sk_begin(0, total, G) != 0 || sk_begin(G, total, G) != total) bad++;

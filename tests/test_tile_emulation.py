@@ -40,6 +40,8 @@ def emu(tmp_path_factory):
     L.emu_check_remap.restype = l
     L.emu_check_streamk.argtypes = [l, i, i]
     L.emu_check_streamk.restype = l
+    L.emu_check_strip_sk.argtypes = [i, i, i]
+    L.emu_check_strip_sk.restype = l
     L.emu_check_epilogue.argtypes = [i]
     L.emu_gemm_relu_bt.argtypes = [i, i, i, i, p, l, p, l, p, l, p]
     L.emu_gemm_relu_bt.restype = i
@@ -69,6 +71,15 @@ def test_xcd_remap_is_bijection(emu):
 def test_streamk_ranges(emu, tiles, ipt, G):
     total = tiles * ipt
     assert emu.emu_check_streamk(total, min(G, total), ipt) == 0
+
+
+@pytest.mark.parametrize("strips,nkb,G", [(224, 64, 256), (224, 64, 512), (128, 128, 256), (5, 64, 256),
+                                          (1, 1, 256), (1, 7, 1), (3, 1, 256), (100, 7, 256), (256, 64, 256),
+                                          (17, 3, 40), (64, 16, 512), (255, 9, 256)])
+def test_strip_streamk_segments(emu, strips, nkb, G):
+    """The stream-K strip kernel's ranges, parts, counts and partial slots
+    (its segment arithmetic from the shared index header)."""
+    assert emu.emu_check_strip_sk(strips, nkb, G) == 0
 
 
 @pytest.mark.parametrize("config", sorted(DMA_CONFIGS))

@@ -248,9 +248,10 @@ __global__ __launch_bounds__(W * 64) void k_skinny_sk(const KArgs a) {
     const int64_t T = (int64_t)a.tiles_n * nkb;
     const int64_t beg = sk_begin(g, T, G), end = sk_begin(g + 1, T, G);
     if (beg == end) return;  // (whole work-group: before any barrier)
-    const int s0 = (int)(beg / nkb);                  // first strip of the range
-    const int64_t bound = (int64_t)(s0 + 1) * nkb;    // first block of the next strip
-    const bool two = end > bound;                     // the range reaches a second strip
+    const StripSegments sg = strip_segments(beg, end, nkb);
+    const int s0 = sg.s0;                             // first strip of the range
+    const int64_t bound = sg.bound;                   // first block of the next strip
+    const bool two = sg.two;                          // the range reaches a second strip
     const int len = (int)(end - beg);
     const int mine = len > wave ? (len - wave + W - 1) / W : 0;  // this wave's blocks
 
@@ -376,8 +377,8 @@ __global__ __launch_bounds__(W * 64) void k_skinny_sk(const KArgs a) {
     // segments: 0 = [beg, min(end, bound)) of strip s0; 1 = [bound, end) of strip s0 + 1
     const int nseg = two ? 2 : 1;
     bool split[2];
-    split[0] = !(beg == (int64_t)s0 * nkb && end >= bound);
-    split[1] = !(end == bound + nkb);
+    split[0] = !strip_part_whole(sg, beg, end, nkb, 0);
+    split[1] = !strip_part_whole(sg, beg, end, nkb, 1);
     bool any_split = false;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(W * 64) void k_skinny_sk(const KArgs a) {
         for (int q = 0; q < 2; ++q) {
             s_last[q] = 0;
             if (q < nseg && split[q]) {
-                const int cnt = q == 0 ? (int)((end < bound ? end : bound) - beg) : (int)(end - bound);
+                const int cnt = (int)strip_part_blocks(sg, beg, end, q);
                 const int old =
                     __hip_atomic_fetch_add(&a.cnt[s0 + q], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 s_last[q] = old + cnt == nkb;

@@ -210,6 +210,33 @@ TLG_HD void grouped_tile(int q, int tiles_m, int tiles_n, int group_m, int *tm, 
 TLG_HD int64_t sk_begin(int g, int64_t total, int G) { return (int64_t)g * total / G; }
 TLG_HD int sk_owner(int64_t x, int64_t total, int G) { return (int)(((x + 1) * (int64_t)G - 1) / total); }
 
+// ---- stream-K over strips ----
+// The strips' K blocks (nkb per strip) in one strip-major sequence; a range
+// [beg, end) of it that is at most nkb long touches at most two strips: its
+// first strip s0 from beg up to min(end, bound), and, if two, strip s0 + 1
+// from bound (the first block of s0 + 1) up to end. A part of a strip is
+// whole when it covers all nkb blocks; the blocks a part adds to its strip's
+// counter are part_blocks.
+struct StripSegments {
+    int s0;         // first strip of the range
+    int64_t bound;  // first block of strip s0 + 1
+    bool two;       // the range reaches strip s0 + 1
+};
+TLG_HD StripSegments strip_segments(int64_t beg, int64_t end, int nkb) {
+    StripSegments r;
+    r.s0 = (int)(beg / nkb);
+    r.bound = (int64_t)(r.s0 + 1) * nkb;
+    r.two = end > r.bound;
+    return r;
+}
+// part q (0: strip s0, 1: strip s0 + 1) of the range
+TLG_HD int64_t strip_part_blocks(const StripSegments &sg, int64_t beg, int64_t end, int q) {
+    return q == 0 ? (end < sg.bound ? end : sg.bound) - beg : end - sg.bound;
+}
+TLG_HD bool strip_part_whole(const StripSegments &sg, int64_t beg, int64_t end, int nkb, int q) {
+    return q == 0 ? beg == sg.bound - nkb && end >= sg.bound : end == sg.bound + nkb;
+}
+
 }  // namespace tlg
 
 #endif
