@@ -148,10 +148,19 @@ def cpu_baseline(w, A, B, target_s: float):
         n = int(min(w.M, max(n + threads, n * min(8.0, target_s / max(dt, 1e-6)))))
         n = min(w.M, -(-n // threads) * threads)
     flop = 2.0 * n * w.N * w.K
+    # and the whole 256^3 problem on one thread (the oracle's result does not
+    # depend on the thread count)
+    from tiled_dense_gemm_06_amd import workloads as wl
+
+    A1, B1 = wl.make_inputs(wl.WORKLOADS["square256"])
+    t1 = time.perf_counter()
+    oracle.gemm_relu(A1, B1, threads=1)
+    dt1 = time.perf_counter() - t1
     return {
         "value": flop / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle", "cpu": cpu_model(),
         "sample": f"{n} of {w.M} output rows ({n}x{w.N}x{w.K} multiply-adds, all K), {dt:.2f} s wall "
                   f"on {threads} threads",
+        "single_thread_square256": {"seconds": dt1, "value": 2.0 * 256 ** 3 / dt1 / 1e12, "unit": "TFLOPS"},
     }
 
 

@@ -175,9 +175,9 @@ tlg_status tlg_gemm_relu_bt(tlg_handle h, int64_t M, int64_t N, int64_t K,
 
 /* tlg_gemm_relu_bt with a forced kernel family and tile configuration, for
  * tests and measurements: variant TLG_VARIANT_AUTO (then config must be -1),
- * TLG_VARIANT_TILED_DMA (configs 0..2) or TLG_VARIANT_TILED_PIPE (configs 2
- * and 4, the ones with a third A buffer); config -1 lets the library choose
- * inside the family. */
+ * TLG_VARIANT_TILED_DMA (configs 0..2) or TLG_VARIANT_TILED_PIPE (configs 2,
+ * 4 and 7, the 256 x 256 ones with a third A buffer); config -1 lets the
+ * library choose inside the family. */
 tlg_status tlg_gemm_relu_bt_variant(tlg_handle h, int32_t variant, int32_t config, int64_t M, int64_t N, int64_t K,
                                     const void *A, int64_t lda,
                                     const void *Bt, int64_t ldbt,

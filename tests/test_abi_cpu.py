@@ -66,7 +66,7 @@ def test_check_args(args, expect):
 
 
 def test_plan_shapes_of_the_workloads():
-    assert tlg.plan(8192, 8192, 8192)["config_name"] == "pipe_256x256x64_w2x4_s2_a3"
+    assert tlg.plan(8192, 8192, 8192)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
     assert tlg.plan(4096, 4096, 4096)["variant_name"] == "tiled_pipe"
     # odd sizes and leading dimensions: direct-to-LDS loads, staged K tail; the
     # tuned table gives this class the pipelined 128 x 256 tiles (216 of them)
@@ -88,7 +88,7 @@ def test_plan_shapes_of_the_workloads():
     assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 32 * 4
     p = tlg.plan(1, 4096, 4096)
     assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 64 * 4
-    assert tlg.plan(3072, 3072, 3072)["config_name"] == "pipe_256x256x64_w2x4_s2_a3"  # 144 tiles of 256 x 256
+    assert tlg.plan(3072, 3072, 3072)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"  # 144 tiles of 256 x 256
     assert tlg.plan(256, 256, 256)["variant_name"] == "tiled_dma"
     assert tlg.plan(5, 7, 0)["variant_name"] == "fill_zero"
     assert tlg.plan(0, 7, 9)["variant_name"] == "noop"

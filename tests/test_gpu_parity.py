@@ -232,7 +232,7 @@ def test_large_square_sampled(dev, name):
     assert np.array_equal(got[rows], oracle.gemm_relu_rows(Ai, Bi, rows))
 
 
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6, 7])
 @pytest.mark.parametrize("shape", [(300, 264, 200), (513, 520, 72), (1024, 1032, 1000), (256, 256, 8),
                                    (257, 8, 4104), (301, 259, 203)])
 def test_pipe_configs(dev, config, shape):
@@ -295,7 +295,7 @@ def test_dma_configs(dev, config, shape):
 # ---------------------------------------------------------------- transposed B, grouped calls
 
 @pytest.mark.parametrize("variant,config", [(V_AUTO, -1), (V_DMA, 0), (V_DMA, 1), (V_DMA, 2), (V_PIPE, 2),
-                                            (V_PIPE, 4)])
+                                            (V_PIPE, 4), (V_PIPE, 7)])
 @pytest.mark.parametrize("shape", [(300, 264, 200), (513, 520, 72), (1024, 1032, 1000), (301, 259, 203),
                                    (16, 2048, 512), (257, 8, 4104), (65, 70, 9), (130, 129, 1)])
 def test_transposed_b(dev, variant, config, shape):

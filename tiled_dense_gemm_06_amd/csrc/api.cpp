@@ -274,7 +274,7 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
     // there are enough tiles to give most CUs one
     if (variant == TLG_VARIANT_TILED_PIPE || variant == TLG_VARIANT_AUTO) {
         if (!config_ok(config, tlg::PIPE_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
-        const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64_W8_A3;
+        const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64_W8_A3_EARLY;
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
         // 128 tiles of 256 x 256 (half the CUs) measured faster than the
@@ -411,7 +411,7 @@ tlg_status plan_bt(const tlg::Problem &p, int32_t variant, int32_t config, tlg_p
     if (variant == TLG_VARIANT_TILED_DMA && (config < -1 || config >= kSquareDmaConfigs))
         return TLG_ERROR_INVALID_VALUE;
     if (variant == TLG_VARIANT_TILED_PIPE && config != -1 && config != tlg::PIPE_256x256x64_A3 &&
-        config != tlg::PIPE_256x256x64_W8_A3)
+        config != tlg::PIPE_256x256x64_W8_A3 && config != tlg::PIPE_256x256x64_W8_A3_EARLY)
         return TLG_ERROR_INVALID_VALUE;
     if (p.M == 0 || p.N == 0) {
         fill_info(o, TLG_VARIANT_NOOP, 0, nullptr, 1, 0, 0, 0);
@@ -433,7 +433,7 @@ tlg_status plan_bt(const tlg::Problem &p, int32_t variant, int32_t config, tlg_p
     // the same boundary as the plain call: 256 x 256 pipelined tiles from 128
     // tiles up (half the CUs; 3072^3 measured 72 vs 101 us on 128 x 128 tiles)
     if (variant == TLG_VARIANT_TILED_PIPE || (variant == TLG_VARIANT_AUTO && t256 >= 128)) {
-        const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64_W8_A3;
+        const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64_W8_A3_EARLY;
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         if (offsets_ok_bt(p, tc.bm, tc.bn)) {
             fill_info(o, TLG_VARIANT_TILED_PIPE, cfg, &tc, 1, 1, t256, 0);

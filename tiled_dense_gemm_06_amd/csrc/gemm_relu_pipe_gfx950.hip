@@ -104,7 +104,13 @@ __device__ __forceinline__ void mfma_tile(const Frags<S> &f, int i, float16_t (&
 // arrive; they are then issued after the B loads). Then this wave's loads of
 // stage kt+1 are waited for and the barrier publishes it (and retires stage
 // kt). The C tile leaves through LDS (store_c_tile_lds).
-template <class S, int SPACING, int DOFF, int ASTAGES, bool BT>
+// EARLY (the default eight-wave form): the wait and the barrier come before
+// the last H slots instead of after them. Those slots read no LDS of stage
+// kt (the last k-step's fragments were read during the k-step before), so
+// the barrier can already publish stage kt+1 there, and the reads of its
+// k-step-0 fragments into f[0] move from the next stage's first H slots into
+// these, half a k-step earlier than they are needed.
+template <class S, int SPACING, int DOFF, int ASTAGES, bool BT, bool EARLY = false>
 __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     constexpr int T = S::TM * S::TN;  // MFMA tiles of a wave (MFMAs per k-step)
     constexpr int H = T / 2;
@@ -208,6 +214,10 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     }
     wait_vmcnt<WAIT>();
     barrier_lds();
+    if (EARLY) {
+#pragma unroll
+        for (int r = 0; r < READS; ++r) frag_read<S, BT>(f[0], lds, lds + B_REGION, wm0, wn0, 0, lane, r);
+    }
 
     int bbuf = 0, abuf = 0;
     for (int kt = 0; kt < nk; ++kt) {
@@ -216,20 +226,35 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
         const int nabuf = abuf == 0 ? ASTAGES - 1 : abuf - 1;
         LDS_PTR(const char) sA = lds + abuf * S::A_BYTES;
         LDS_PTR(const char) sB = lds + B_REGION + bbuf * S::B_BYTES;
+        // (EARLY) stage kt+1's buffers
+        LDS_PTR(const char) sA1 = lds + (abuf == ASTAGES - 1 ? 0 : abuf + 1) * S::A_BYTES;
+        LDS_PTR(const char) sB1 = lds + B_REGION + (bbuf == S::STAGES - 1 ? 0 : bbuf + 1) * S::B_BYTES;
         TLG_SCHED_FENCE();
 #pragma unroll
         for (int q = 0; q < SLOTS; ++q) {
             if (q < H) {
                 mfma_tile<S>(f[1], H + q, acc);
+                if (!EARLY) {
 #pragma unroll
-                for (int r = 2 * q; r < 2 * q + 2; ++r)
-                    if (r < READS) frag_read<S, BT>(f[0], sA, sB, wm0, wn0, 0, lane, r);
+                    for (int r = 2 * q; r < 2 * q + 2; ++r)
+                        if (r < READS) frag_read<S, BT>(f[0], sA, sB, wm0, wn0, 0, lane, r);
+                }
             } else if (q < H + (S::KSTEPS - 1) * T) {
                 const int ks = (q - H) / T, i = (q - H) % T;
                 mfma_tile<S>(f[ks & 1], i, acc);
                 if (i < READS) frag_read<S, BT>(f[(ks + 1) & 1], sA, sB, wm0, wn0, ks + 1, lane, i);
             } else {
-                mfma_tile<S>(f[1], q - H - (S::KSTEPS - 1) * T, acc);
+                const int u = q - H - (S::KSTEPS - 1) * T;
+                if (EARLY && u == 0) {
+                    wait_vmcnt<WAIT>();  // this wave's loads of stage kt+1 are in LDS
+                    barrier_lds();       // ... and every wave's; no wave reads stage kt any more
+                }
+                mfma_tile<S>(f[1], u, acc);
+                if (EARLY) {
+#pragma unroll
+                    for (int r = 2 * u; r < 2 * u + 2; ++r)
+                        if (r < READS) frag_read<S, BT>(f[0], sA1, sB1, wm0, wn0, 0, lane, r);
+                }
             }
             if (q >= DOFF && (q - DOFF) % SPACING == 0 && (q - DOFF) / SPACING < LOADS) {
                 const int n = (q - DOFF) / SPACING;
@@ -241,8 +266,10 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
             }
             TLG_SCHED_FENCE();
         }
-        wait_vmcnt<WAIT>();  // this wave's loads of stage kt+1 are in LDS
-        barrier_lds();       // ... and every wave's; stage kt is no longer read
+        if (!EARLY) {
+            wait_vmcnt<WAIT>();  // this wave's loads of stage kt+1 are in LDS
+            barrier_lds();       // ... and every wave's; stage kt is no longer read
+        }
         bbuf = bbuf == S::STAGES - 1 ? 0 : bbuf + 1;
         abuf = abuf == ASTAGES - 1 ? 0 : abuf + 1;
     }
@@ -284,9 +311,11 @@ const TileConfig kPipeConfigs[PIPE_CONFIGS] = {
      "pipe_256x128x64_w2x2_s3"},
     {Pipe128x256::BM, Pipe128x256::BN, Pipe128x256::BK, Pipe128x256::NT, Pipe128x256::STAGES,
      "pipe_128x256x64_w1x4_s3"},
+    {Pipe256x64w8::BM, Pipe256x64w8::BN, Pipe256x64w8::BK, Pipe256x64w8::NT, Pipe256x64w8::STAGES,
+     "pipe_256x256x64_w2x4_s2_a3_early"},
 };
 
-template <class S, int SPACING, int DOFF, int ASTAGES, bool BT = false>
+template <class S, int SPACING, int DOFF, int ASTAGES, bool BT = false, bool EARLY = false>
 static hipError_t launch_pipe_t(const Problem &p, hipStream_t stream) {
     KArgs a;
     a.A = (const _Float16 *)p.A;
@@ -307,7 +336,7 @@ static hipError_t launch_pipe_t(const Problem &p, hipStream_t stream) {
     a.kmain = whole ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
     a.tiles_m = (a.M + S::BM - 1) / S::BM;
     a.tiles_n = (a.N + S::BN - 1) / S::BN;
-    hipLaunchKernelGGL((k_tiled_pipe<S, SPACING, DOFF, ASTAGES, BT>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
+    hipLaunchKernelGGL((k_tiled_pipe<S, SPACING, DOFF, ASTAGES, BT, EARLY>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
                        dim3(S::NT), 0, stream, a);
     return hipGetLastError();
 }
@@ -317,6 +346,7 @@ hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream) {
         switch (config) {
             case PIPE_256x256x64_A3: return launch_pipe_t<Pipe256x64, 2, 1, 3, true>(p, stream);
             case PIPE_256x256x64_W8_A3: return launch_pipe_t<Pipe256x64w8, 2, 1, 3, true>(p, stream);
+            case PIPE_256x256x64_W8_A3_EARLY: return launch_pipe_t<Pipe256x64w8, 2, 1, 3, true, true>(p, stream);
             default: return hipErrorInvalidValue;
         }
     }
@@ -333,6 +363,8 @@ hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream) {
         // half tiles: 12 loads per wave and stage, every 2 slots
         case PIPE_256x128x64: return launch_pipe_t<Pipe256x128, 2, 1, 3>(p, stream);
         case PIPE_128x256x64: return launch_pipe_t<Pipe128x256, 2, 1, 3>(p, stream);
+        // eight waves, the stage barrier before the last half k-step (the default)
+        case PIPE_256x256x64_W8_A3_EARLY: return launch_pipe_t<Pipe256x64w8, 2, 1, 3, false, true>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

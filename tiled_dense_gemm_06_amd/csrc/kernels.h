@@ -63,7 +63,8 @@ enum PipeConfig {
     PIPE_256x256x64_W8_A3 = 4,
     PIPE_256x128x64 = 5,  // four waves of 128 x 64, three stages
     PIPE_128x256x64 = 6,
-    PIPE_CONFIGS = 7
+    PIPE_256x256x64_W8_A3_EARLY = 7,  // stage barrier before the last half k-step (the default)
+    PIPE_CONFIGS = 8
 };
 
 // wave-role (ping-pong) schedule: two groups of waves alternate between

@@ -9,7 +9,7 @@ counter bytes, separately for reads and writes.
 Usage (after the counter runs, on the CSV files rocprofv3 wrote)::
 
     python -m tiled_dense_gemm_06_amd.profiling traffic --workload square8192 \\
-        --kernel k_tiled_pipe --config pipe_256x256x64_w2x4_s2_a3 --fetch F.csv --write W.csv \\
+        --kernel k_tiled_pipe --config pipe_256x256x64_w2x4_s2_a3_early --fetch F.csv --write W.csv \\
         --copy-fetch CF.csv --copy-write CW.csv --copy-mib 512
 
 It records the scaled fetch and write bytes per launch in
