@@ -358,11 +358,15 @@ def main() -> int:
     if args.grouped:
         # the grouped call picks its tile by the total tile count of the blocks
         rows = [(w.M * g // args.grouped, w.M * (g + 1) // args.grouped) for g in range(args.grouped)]
+        # (the library's rule: the pipelined 256 x 256 kernel, grouped
+        # configuration 3, from 128 such tiles in total, else direct-to-LDS
+        # tiles 0..2 by tile count)
         t256 = sum(-(-(r1 - r0) // 256) * -(-w.N // 256) for r0, r1 in rows)
         t128 = sum(-(-(r1 - r0) // 128) * -(-w.N // 128) for r0, r1 in rows)
-        gcfg = args.config if args.config >= 0 else (0 if t256 >= 224 else 1 if t128 >= 192 else 2)
-        plan = {"config_name": tlg.tlg_plan_config_name(tlg.TLG_VARIANT_TILED_DMA, gcfg), "variant_name": "grouped",
-                "splits": 1}
+        gcfg = args.config if args.config >= 0 else (3 if t256 >= 128 else 1 if t128 >= 192 else 2)
+        name = (tlg.tlg_plan_config_name(tlg.TLG_VARIANT_TILED_PIPE, 7) if gcfg == 3
+                else tlg.tlg_plan_config_name(tlg.TLG_VARIANT_TILED_DMA, gcfg))
+        plan = {"config_name": name, "variant_name": "grouped", "splits": 1}
     else:
         plan = tlg.plan(w.M, w.N, w.K, variant=variant, config=args.config, splits=args.splits,
                         trans_b=args.trans_b)

@@ -216,7 +216,11 @@ typedef struct {
 tlg_status tlg_gemm_relu_grouped(tlg_handle h, int32_t count, const tlg_gemm_desc *descs, int32_t trans_b,
                                  hipStream_t stream);
 
-/* tlg_gemm_relu_grouped with a forced tile configuration (-1: library's choice). */
+/* tlg_gemm_relu_grouped with a forced tile configuration: -1 the library's
+ * choice (the pipelined kernel from 128 tiles of 256 x 256 in total, else
+ * the direct-to-LDS tiles by tile count); 0, 1, 2 the direct-to-LDS
+ * 256 x 256 x 32, 128 x 128 x 32 and 64 x 64 x 64 tiles; 3 the eight-wave
+ * pipelined 256 x 256 x 64 kernel. */
 tlg_status tlg_gemm_relu_grouped_variant(tlg_handle h, int32_t config, int32_t count, const tlg_gemm_desc *descs,
                                          int32_t trans_b, hipStream_t stream);
 

@@ -330,7 +330,7 @@ def test_transposed_b_uniform_and_strided(dev):
 
 
 @pytest.mark.parametrize("trans_b", [False, True])
-@pytest.mark.parametrize("config", [-1, 0, 1, 2])
+@pytest.mark.parametrize("config", [-1, 0, 1, 2, 3])
 def test_grouped(dev, trans_b, config):
     """Several problems (mixed sizes, an empty one, K = 0, ragged edges) in one
     launch: each equals its own oracle result bit for bit, guard bands intact."""
@@ -349,6 +349,32 @@ def test_grouped(dev, trans_b, config):
         bigs.append(big)
         outs.append(big[:M, :N])
     tlg.gemm_relu_grouped(As, Bs, outs, trans_b=trans_b, config=config)
+    torch.cuda.synchronize()
+    refs = oracle.gemm_relu_grouped(probs, trans_b=trans_b)
+    for (M, N, K), big, ref in zip(shapes, bigs, refs):
+        allb = bits(big)
+        assert np.array_equal(allb[:M, :N], ref), (M, N, K)
+        assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+def test_grouped_large(dev, trans_b):
+    """Problems with 128 tiles of 256 x 256 in total, where the library's choice
+    is the pipelined kernel (ragged M, N and K among them): bit-exact per
+    problem, guard bands intact."""
+    shapes = [(1024, 2048, 264), (1000, 2049, 264), (1024, 2048, 200), (1031, 1800, 136)]
+    probs, As, Bs, bigs, outs = [], [], [], [], []
+    for i, (M, N, K) in enumerate(shapes):
+        A, B = wl.make_random(M, N, K, seed=200 + i, kind="integer_pos")
+        Bx = np.ascontiguousarray(B.T) if trans_b else B
+        probs.append((A, Bx))
+        As.append(to_dev(A, dev))
+        Bs.append(to_dev(Bx, dev))
+        big = torch.full((M + 2, N + 8), float("nan"), dtype=torch.float16, device=dev)
+        bigs.append(big)
+        outs.append(big[:M, :N])
+    assert sum(-(-M // 256) * -(-N // 256) for M, N, _ in shapes) >= 128
+    tlg.gemm_relu_grouped(As, Bs, outs, trans_b=trans_b)
     torch.cuda.synchronize()
     refs = oracle.gemm_relu_grouped(probs, trans_b=trans_b)
     for (M, N, K), big, ref in zip(shapes, bigs, refs):

@@ -402,6 +402,9 @@ int dma_config_by_tiles(int64_t t256, int64_t t128) {
     return tlg::DMA_64x64x64;
 }
 constexpr int kSquareDmaConfigs = 3;
+// grouped calls: configurations 0..2 are those direct-to-LDS ones, 3 the
+// eight-wave pipelined 256 x 256 kernel
+constexpr int kGroupedPipe = kSquareDmaConfigs;
 
 tlg_status plan_bt(const tlg::Problem &p, int32_t variant, int32_t config, tlg_plan_info *o) {
     if (variant != TLG_VARIANT_AUTO && variant != TLG_VARIANT_TILED_DMA && variant != TLG_VARIANT_TILED_PIPE &&
@@ -483,7 +486,7 @@ tlg_status run_grouped(tlg_handle h, int32_t config, int32_t count, const tlg_ge
     tlg_status st = device_ok(h);
     if (st != TLG_SUCCESS) return st;
     if (count < 0 || count > TLG_GROUP_MAX || (trans_b != 0 && trans_b != 1)) return TLG_ERROR_INVALID_VALUE;
-    if (config < -1 || config >= kSquareDmaConfigs) return TLG_ERROR_INVALID_VALUE;
+    if (config < -1 || config > kGroupedPipe) return TLG_ERROR_INVALID_VALUE;
     if (count == 0) return TLG_SUCCESS;
     if (!descs) return TLG_ERROR_INVALID_VALUE;
     tlg::Problem ps[TLG_GROUP_MAX];
@@ -502,6 +505,17 @@ tlg_status run_grouped(tlg_handle h, int32_t config, int32_t count, const tlg_ge
         t128 += ceil_div(d.M, 128) * ceil_div(d.N, 128);
     }
     if (n == 0) return TLG_SUCCESS;
+    // the pipelined 256 x 256 kernel from the same total tile count as a
+    // single call (128 tiles of 256 x 256), when every problem can take it
+    bool pipe = config == kGroupedPipe || (config == -1 && t256 >= 128);
+    if (pipe) {
+        const tlg::TileConfig &tp = tlg::kPipeConfigs[tlg::PIPE_256x256x64_W8_A3_EARLY];
+        bool ok = t256 <= 0x7fffffff;
+        for (int i = 0; i < n && ok; ++i)
+            ok = trans_b ? offsets_ok_bt(ps[i], tp.bm, tp.bn) : dma_ok(ps[i], tp.bm, tp.bn, tp.bk);
+        if (ok) return tlg::launch_tiled_pipe_grouped(ps, n, stream) == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
+        if (config == kGroupedPipe) return TLG_ERROR_NOT_SUPPORTED;
+    }
     const int cfg = config >= 0 ? config : dma_config_by_tiles(t256, t128);
     const tlg::TileConfig &tc = tlg::kDmaConfigs[cfg];
     int64_t tiles = 0;

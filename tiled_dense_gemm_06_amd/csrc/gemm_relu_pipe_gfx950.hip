@@ -110,8 +110,14 @@ __device__ __forceinline__ void mfma_tile(const Frags<S> &f, int i, float16_t (&
 // the barrier can already publish stage kt+1 there, and the reads of its
 // k-step-0 fragments into f[0] move from the next stage's first H slots into
 // these, half a k-step earlier than they are needed.
-template <class S, int SPACING, int DOFF, int ASTAGES, bool BT, bool EARLY = false>
-__global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
+template <class S, int ASTAGES>
+constexpr int pipe_lds_bytes() {
+    return ASTAGES * S::A_BYTES + S::STAGES * S::B_BYTES;  // A buffers first, then the B buffers
+}
+
+// One output tile (tm_idx, tn_idx) of problem a, with the work-group's LDS.
+template <class S, int SPACING, int DOFF, int ASTAGES, bool BT, bool EARLY>
+__device__ __forceinline__ void pipe_tile(const KArgs &a, int tm_idx, int tn_idx, LDS_PTR(char) lds) {
     constexpr int T = S::TM * S::TN;  // MFMA tiles of a wave (MFMAs per k-step)
     constexpr int H = T / 2;
     static_assert(T % 2 == 0 && S::KSTEPS % 2 == 0, "the last k-step of a stage must use f[1]");
@@ -129,18 +135,12 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     static_assert(AHEAD >= 1 && WAIT < 64, "vmcnt range");
     static_assert(DOFF + (LOADS - 1) * SPACING < SLOTS, "loads must fit in one K step");
     constexpr int B_REGION = ASTAGES * S::A_BYTES;  // A buffers first, then the B buffers
-    constexpr int LDS_BYTES = B_REGION + S::STAGES * S::B_BYTES;
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS of one work-group");
+    static_assert(pipe_lds_bytes<S, ASTAGES>() <= 160 * 1024, "LDS of one work-group");
 
-    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
-
-    const int nwg = a.tiles_m * a.tiles_n;
-    int tm_idx, tn_idx;
-    grouped_tile(xcd_remap(blockIdx.x, nwg), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
     const int m0 = tm_idx * S::BM, n0 = tn_idx * S::BN;
     const int nk = (a.kmain + S::BK - 1) / S::BK;
 
@@ -165,7 +165,6 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
         ok[S::DMA_A + i] = BT ? n0 + c.row < a.N : n0 + 8 * c.chunk < a.N;
     }
 
-    LDS_PTR(char) lds = (LDS_PTR(char))smem;
     const _Float16 *a_tile = a.A + (int64_t)m0 * a.lda;
     const _Float16 *b_tile = BT ? a.B + (int64_t)n0 * a.ldb : a.B + n0;
 
@@ -291,6 +290,29 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     store_c_tile_lds<S>(a, m0, n0, wave, lane, acc, lds);
 }
 
+template <class S, int SPACING, int DOFF, int ASTAGES, bool BT, bool EARLY = false>
+__global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[pipe_lds_bytes<S, ASTAGES>()];
+    int tm_idx, tn_idx;
+    grouped_tile(xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
+    pipe_tile<S, SPACING, DOFF, ASTAGES, BT, EARLY>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
+}
+
+// Grouped problems in one launch: after the XCD renumbering, work-group ids
+// tile_start[p] .. tile_start[p+1]-1 take problem p's tiles in its grouped
+// order (the table travels as the kernel argument).
+template <class S, int SPACING, int DOFF, int ASTAGES, bool BT, bool EARLY>
+__global__ __launch_bounds__(S::NT) void k_tiled_pipe_grouped(const GroupArgs g) {
+    __shared__ __attribute__((aligned(1024))) char smem[pipe_lds_bytes<S, ASTAGES>()];
+    const int v = xcd_remap(blockIdx.x, g.tile_start[g.count]);
+    int p = 0;
+    while (p + 1 < g.count && v >= g.tile_start[p + 1]) ++p;
+    const KArgs &a = g.p[p];
+    int tm_idx, tn_idx;
+    grouped_tile(v - g.tile_start[p], a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
+    pipe_tile<S, SPACING, DOFF, ASTAGES, BT, EARLY>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
+}
+
 using Pipe256x32 = TileShape<256, 256, 32, 2, 2, 4>;
 using Pipe256x64 = TileShape<256, 256, 64, 2, 2, 2>;
 using Pipe256x64w8 = TileShape<256, 256, 64, 2, 4, 2>;  // eight waves, two per SIMD
@@ -315,8 +337,8 @@ const TileConfig kPipeConfigs[PIPE_CONFIGS] = {
      "pipe_256x256x64_w2x4_s2_a3_early"},
 };
 
-template <class S, int SPACING, int DOFF, int ASTAGES, bool BT = false, bool EARLY = false>
-static hipError_t launch_pipe_t(const Problem &p, hipStream_t stream) {
+template <class S, bool BT>
+static KArgs pipe_args(const Problem &p) {
     KArgs a;
     a.A = (const _Float16 *)p.A;
     a.B = (const _Float16 *)p.B;
@@ -336,9 +358,42 @@ static hipError_t launch_pipe_t(const Problem &p, hipStream_t stream) {
     a.kmain = whole ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
     a.tiles_m = (a.M + S::BM - 1) / S::BM;
     a.tiles_n = (a.N + S::BN - 1) / S::BN;
+    return a;
+}
+
+template <class S, int SPACING, int DOFF, int ASTAGES, bool BT = false, bool EARLY = false>
+static hipError_t launch_pipe_t(const Problem &p, hipStream_t stream) {
+    const KArgs a = pipe_args<S, BT>(p);
     hipLaunchKernelGGL((k_tiled_pipe<S, SPACING, DOFF, ASTAGES, BT, EARLY>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
                        dim3(S::NT), 0, stream, a);
     return hipGetLastError();
+}
+
+template <bool BT>
+static hipError_t launch_pipe_grouped_t(const Problem *ps, int count, hipStream_t stream) {
+    using S = Pipe256x64w8;
+    GroupArgs g;
+    g.count = count;
+    g.tile_start[0] = 0;
+    for (int i = 0; i < count; ++i) {
+        g.p[i] = pipe_args<S, BT>(ps[i]);
+        g.tile_start[i + 1] = g.tile_start[i] + g.p[i].tiles_m * g.p[i].tiles_n;
+    }
+    if (g.tile_start[count] == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_tiled_pipe_grouped<S, 2, 1, 3, BT, true>), dim3((unsigned)g.tile_start[count]),
+                       dim3(S::NT), 0, stream, g);
+    return hipGetLastError();
+}
+
+// The eight-wave early-barrier configuration over up to kGroupMax problems
+// (all with the same trans_b).
+hipError_t launch_tiled_pipe_grouped(const Problem *ps, int count, hipStream_t stream) {
+    static_assert(sizeof(GroupArgs) <= 4096, "kernel arguments");
+    if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
+    const bool bt = ps[0].trans_b;
+    for (int i = 1; i < count; ++i)
+        if (ps[i].trans_b != bt) return hipErrorInvalidValue;
+    return bt ? launch_pipe_grouped_t<true>(ps, count, stream) : launch_pipe_grouped_t<false>(ps, count, stream);
 }
 
 hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream) {
