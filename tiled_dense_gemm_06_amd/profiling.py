@@ -140,6 +140,24 @@ def _stats_rows(trace_dir: str):
         return list(csv.DictReader(f))
 
 
+def _median_ns(trace_dir: str) -> dict:
+    """Median dispatch duration (ns) per kernel name, from the per-dispatch
+    trace (run_kernel_trace.csv), if the trace directory holds one."""
+    path = os.path.join(trace_dir, "run_kernel_trace.csv")
+    if not os.path.exists(path):
+        return {}
+    durs = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            durs.setdefault(row["Kernel_Name"], []).append(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+    out = {}
+    for name, d in durs.items():
+        d.sort()
+        n = len(d)
+        out[name] = d[n // 2] if n % 2 else 0.5 * (d[n // 2 - 1] + d[n // 2])
+    return out
+
+
 def summary(args) -> str:
     from . import workloads as wl
 
@@ -153,6 +171,7 @@ def summary(args) -> str:
     else:
         alg_bytes, peak, peak_name, what = w.alg_bytes, PEAK_MFMA_TFLOPS, "fp16 dense", "A, B and C once"
     rows = _stats_rows(args.trace)
+    med = _median_ns(args.trace)
     main = [r for r in rows if args.kernel in r["Name"]]
     if not main:
         raise ValueError(f"no kernel matching {args.kernel!r} in {args.trace}")
@@ -160,10 +179,11 @@ def summary(args) -> str:
     avg_ns = float(r0["AverageNs"])
     lines = [f"# {args.title or args.kernel} — workload {w.name}", ""]
     lines += ["Kernel trace (from the repository root, on one MI355X):", "", "    " + args.trace_cmd, ""]
-    lines += ["| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|"]
+    lines += ["| kernel | calls | avg ns | median ns | min ns | max ns |", "|---|---|---|---|---|---|"]
     for r in rows:
-        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']):,.0f} | {float(r['MinNs']):,.0f} | "
-                     f"{float(r['MaxNs']):,.0f} |")
+        m = med.get(r["Name"])
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']):,.0f} | "
+                     f"{'' if m is None else f'{m:,.0f}'} | {float(r['MinNs']):,.0f} | {float(r['MaxNs']):,.0f} |")
     lines.append("")
     if args.note:
         lines += [args.note, ""]
@@ -173,6 +193,13 @@ def summary(args) -> str:
                  f"({100 * tflops / peak:.1f} % of the {peak} TFLOP/s {peak_name} peak), "
                  f"{gbs:,.0f} GB/s of algorithmic bytes ({alg_bytes:,} B: {what}; "
                  f"{100 * gbs / PEAK_HBM_GBS:.1f} % of {PEAK_HBM_GBS:.0f} GB/s).")
+    m0 = med.get(r0["Name"])
+    if m0:
+        lines.append("")
+        lines.append(f"From the trace median ({m0 / 1e3:,.1f} us per launch): "
+                     f"{w.flop / (m0 * 1e-9) / 1e12:,.1f} TFLOP/s ({100 * w.flop / (m0 * 1e-9) / 1e12 / peak:.1f} %), "
+                     f"{alg_bytes / (m0 * 1e-9) / 1e9:,.0f} GB/s "
+                     f"({100 * alg_bytes / (m0 * 1e-9) / 1e9 / PEAK_HBM_GBS:.1f} % of {PEAK_HBM_GBS:.0f} GB/s).")
     lines.append("")
     if args.fetch:
         copy_bytes = args.copy_mib << 20
