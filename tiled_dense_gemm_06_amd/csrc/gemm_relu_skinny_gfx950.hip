@@ -28,6 +28,18 @@
 
 namespace tlg {
 
+// Direct-to-LDS 16-byte load of B with the non-temporal policy: every byte
+// of B is read once, and the hint measured about 1 % faster here
+// (16 x 14336 x 4096: 24.51 vs 24.76 us; sc1, or sc1 with nt, no better).
+__device__ __forceinline__ void dma16_nt(int4_t srd, uint32_t lds_base, uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(lds_base),
+        "v"(voff), "s"(srd)
+        : "memory", "m0");
+}
+
 // Wait until at most `n` blocks of this wave are still loading (n < STAGES).
 template <int LOADS, int STAGES>
 __device__ __forceinline__ void wait_blocks(int n) {
@@ -85,8 +97,8 @@ __global__ __launch_bounds__(W * 64) void k_skinny_strip(const KArgs a) {
         for (int i = 0; i < S::DMA_B; ++i) {
             const ChunkRef c = dma_b_chunk<S>(0, i, lane);
             const bool in = n0 + 8 * c.chunk < a.N && k0 + c.row < a.K;
-            dma16(rb, (uint32_t)(uintptr_t)(st + S::A_BYTES + i * 1024),
-                  in ? (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16) : kOOB);
+            dma16_nt(rb, (uint32_t)(uintptr_t)(st + S::A_BYTES + i * 1024),
+                     in ? (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16) : kOOB);
         }
     };
 
@@ -277,8 +289,8 @@ __global__ __launch_bounds__(W * 64) void k_skinny_sk(const KArgs a) {
         for (int i = 0; i < S::DMA_B; ++i) {
             const ChunkRef c = dma_b_chunk<S>(0, i, lane);
             const bool in = n0 + 8 * c.chunk < a.N && k0 + c.row < a.K;
-            dma16(rb, (uint32_t)(uintptr_t)(st + S::A_BYTES + i * 1024),
-                  in ? (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16) : kOOB);
+            dma16_nt(rb, (uint32_t)(uintptr_t)(st + S::A_BYTES + i * 1024),
+                     in ? (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16) : kOOB);
         }
     };
 
