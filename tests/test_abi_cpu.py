@@ -278,3 +278,35 @@ def test_plan_pingpong_forced_only():
     assert tlg.tlg_plan_config_name(tlg.TLG_VARIANT_PINGPONG, 0) == "pingpong_256x256x32_w2x4_s4"
     with pytest.raises(tlg.TlgError):
         tlg.plan(64, 64, 64, variant=tlg.TLG_VARIANT_PINGPONG + 1)
+
+
+def test_strip_configurations_plan():
+    """Every strip configuration of the split-K family (forced): its name,
+    its strips x parts grid for 16 x 14336 x 4096 (224 64-column, 112
+    128-column, 56 256-column strips, parts filling the CUs), the partial
+    workspace of split strips; the stream-K strips take one range per CU
+    (two for the two-stage form) and need at least one range per strip; M
+    above one strip is refused."""
+    V = tlg.TLG_VARIANT_SPLITK
+    want = {3: ("splitk_waves_32x64x64_w2_s3", 224, 1), 4: ("splitk_waves_32x64x64_w4_s3", 224, 1),
+            5: ("splitk_waves_32x64x64_w2_s4", 224, 1), 6: ("splitk_waves_32x128x64_w2_s3", 224, 2),
+            7: ("splitk_waves_32x128x64_w4_s2", 224, 2), 8: ("splitk_waves_32x256x32_w2_s3", 224, 4),
+            9: ("strip_sk_32x64x64_w2_s3", 256, None), 10: ("strip_sk_32x64x64_w2_s2", 512, None)}
+    for c, (name, grid, parts) in want.items():
+        p = tlg.plan(16, 14336, 4096, variant=V, config=c)
+        assert (p["config_name"], p["grid"]) == (name, grid), c
+        assert tlg.tlg_plan_config_name(V, c) == name
+        if parts is not None:
+            assert p["splits"] == parts
+            bn = p["block_n"]
+            assert p["workspace_bytes"] == (0 if parts == 1 else (64 << 10) + (14336 // bn) * parts * 32 * bn * 4)
+        else:  # two partial slots per range
+            assert p["workspace_bytes"] == (64 << 10) + grid * 2 * 32 * 64 * 4
+    for c in want:
+        with pytest.raises(tlg.TlgError):
+            tlg.plan(48, 14336, 4096, variant=V, config=c)
+    with pytest.raises(tlg.TlgError):  # 300 strips, 256 ranges: a range would cross three strips
+        tlg.plan(16, 64 * 300, 4096, variant=V, config=9)
+    assert tlg.plan(16, 64 * 300, 4096, variant=V, config=10)["grid"] == 512
+    with pytest.raises(tlg.TlgError):
+        tlg.plan(16, 14336, 4096, variant=V, config=11)
