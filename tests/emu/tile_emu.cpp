@@ -359,6 +359,7 @@ using E256w8 = TileShape<256, 256, 64, 2, 4, 2>;
 using E256w8x32 = TileShape<256, 256, 32, 2, 4, 4>;
 using EP256x128 = TileShape<256, 128, 64, 2, 2, 3>;  // pipelined half tiles
 using EP128x256 = TileShape<128, 256, 64, 1, 4, 3>;
+using EStrip64 = TileShape<64, 64, 64, 1, 1, 3>;  // one wave per 64 x 64 strip ring
 
 extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A, long lda, const uint16_t *B,
                              long ldb, uint16_t *C, long ldc, int splits, int k_split, float *W, long *errs) {
@@ -372,6 +373,7 @@ extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A,
         case 5: return emulate<E256w8x32>(p, false, errs);
         case 6: return emulate<EP256x128>(p, false, errs);
         case 7: return emulate<EP128x256>(p, false, errs);
+        case 8: return emulate<EStrip64>(p, false, errs);
         case 10: return emulate<ES128>(p, true, errs);
         case 11: return emulate<ES256>(p, true, errs);
         default: return -1;

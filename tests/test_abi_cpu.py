@@ -82,8 +82,14 @@ def test_plan_shapes_of_the_workloads():
     assert p["config_name"].startswith("streamk") and p["kernels"] == 1
     assert p["grid"] == 2 * 256 and p["splits"] >= 2  # two work-groups per CU, ~4.6 per output tile
     assert p["workspace_bytes"] == (64 << 10) + p["grid"] * 2 * 32 * 128 * 4 <= tlg.tlg_workspace_bytes()
-    assert tlg.plan(48, 14336, 4096)["config_name"] == "dma_64x64x64_w2x2_s3"  # M above one strip, tiles enough
-    assert tlg.plan(48, 4096, 4096)["config_name"].startswith("streamk")  # M above one strip, few tiles
+    # 32 < M <= 64, aligned: 64-row strips from K = 2048 up, tiles below
+    assert tlg.plan(48, 14336, 4096)["config_name"] == "splitk_waves_64x64x64_w2_s3"
+    assert tlg.plan(48, 4096, 4096)["config_name"] == "splitk_waves_64x64x64_w2_s3"
+    assert tlg.plan(64, 1024, 2048)["config_name"] == "splitk_waves_64x64x64_w2_s3"
+    assert tlg.plan(48, 4096, 1024)["variant_name"] == "tiled_dma"
+    assert tlg.plan(65, 4096, 4096)["variant_name"] != "splitk"
+    # unaligned (the split-K kernels load 16-byte pieces): tiles
+    assert tlg.plan(48, 4100, 4096)["variant_name"] == "tiled_dma"
     p = tlg.plan(16, 2048, 4096)  # few strips: K split among work-groups too, up to the CUs
     assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 32 * 4
     p = tlg.plan(1, 4096, 4096)
@@ -214,17 +220,17 @@ def test_tuned_table_entries_are_taken():
 
 
 def test_tuned_classes_of_the_table():
-    # the two measured skinny classes: two-kernel split-K instead of stream-K
-    assert tlg.plan(48, 4096, 14336)["config_name"] == "splitk_32x128x64_w1x4_s4"
-    assert tlg.plan(64, 4096, 8192)["config_name"] == "splitk_32x128x64_w1x4_s4"
+    # the two measured skinny classes with 32 < M <= 64: 64-row strips (B read once)
+    assert tlg.plan(48, 4096, 14336)["config_name"] == "splitk_waves_64x64x64_w2_s3"
+    assert tlg.plan(64, 4096, 8192)["config_name"] == "splitk_waves_64x64x64_w2_s3"
     # mid-size and ragged classes: pipelined 128 x 256 tiles; decode-like
     # 8 x 8192 x 8192: stream-K over strips
     assert tlg.plan(1024, 4096, 16384)["config_name"] == "pipe_128x256x64_w1x4_s3"
     assert tlg.plan(3001, 2049, 1537)["config_name"] == "pipe_128x256x64_w1x4_s3"
     p = tlg.plan(8, 8192, 8192)
     assert p["config_name"] == "strip_sk_32x64x64_w2_s3" and p["grid"] == 256
-    # a neighbouring class keeps the heuristic's choice
-    assert tlg.plan(48, 4096, 4096)["config_name"].startswith("streamk")
+    # a neighbouring class (shorter K) keeps the heuristic's choice
+    assert tlg.plan(48, 4096, 1024)["variant_name"] == "tiled_dma"
 
 
 def test_plan_block_scaled():
@@ -291,7 +297,8 @@ def test_strip_configurations_plan():
     want = {3: ("splitk_waves_32x64x64_w2_s3", 224, 1), 4: ("splitk_waves_32x64x64_w4_s3", 224, 1),
             5: ("splitk_waves_32x64x64_w2_s4", 224, 1), 6: ("splitk_waves_32x128x64_w2_s3", 224, 2),
             7: ("splitk_waves_32x128x64_w4_s2", 224, 2), 8: ("splitk_waves_32x256x32_w2_s3", 224, 4),
-            9: ("strip_sk_32x64x64_w2_s3", 256, None), 10: ("strip_sk_32x64x64_w2_s2", 512, None)}
+            9: ("splitk_waves_64x64x64_w2_s3", 224, 1),
+            10: ("strip_sk_32x64x64_w2_s3", 256, None), 11: ("strip_sk_32x64x64_w2_s2", 512, None)}
     for c, (name, grid, parts) in want.items():
         p = tlg.plan(16, 14336, 4096, variant=V, config=c)
         assert (p["config_name"], p["grid"]) == (name, grid), c
@@ -299,14 +306,19 @@ def test_strip_configurations_plan():
         if parts is not None:
             assert p["splits"] == parts
             bn = p["block_n"]
-            assert p["workspace_bytes"] == (0 if parts == 1 else (64 << 10) + (14336 // bn) * parts * 32 * bn * 4)
+            bm = p["block_m"]
+            assert p["workspace_bytes"] == (0 if parts == 1 else (64 << 10) + (14336 // bn) * parts * bm * bn * 4)
         else:  # two partial slots per range
             assert p["workspace_bytes"] == (64 << 10) + grid * 2 * 32 * 64 * 4
-    for c in want:
+    for c in want:  # M above the strip's rows
         with pytest.raises(tlg.TlgError):
-            tlg.plan(48, 14336, 4096, variant=V, config=c)
+            tlg.plan(65 if c == 9 else 48, 14336, 4096, variant=V, config=c)
+    # the 64-row strip: 48 x 4096 x 14336 in 64 strips of 4 parts, B read once
+    p = tlg.plan(48, 4096, 14336, variant=V, config=9)
+    assert (p["block_m"], p["grid"], p["splits"]) == (64, 256, 4)
+    assert p["workspace_bytes"] == (64 << 10) + 64 * 4 * 64 * 64 * 4
     with pytest.raises(tlg.TlgError):  # 300 strips, 256 ranges: a range would cross three strips
-        tlg.plan(16, 64 * 300, 4096, variant=V, config=9)
-    assert tlg.plan(16, 64 * 300, 4096, variant=V, config=10)["grid"] == 512
+        tlg.plan(16, 64 * 300, 4096, variant=V, config=10)
+    assert tlg.plan(16, 64 * 300, 4096, variant=V, config=11)["grid"] == 512
     with pytest.raises(tlg.TlgError):
-        tlg.plan(16, 14336, 4096, variant=V, config=11)
+        tlg.plan(16, 14336, 4096, variant=V, config=12)

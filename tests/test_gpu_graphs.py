@@ -30,9 +30,10 @@ CASES = [
     ((301, 259, 203), V_PIPE, 6, 0),           # pipelined 128 x 256, ragged, K tail
     ((300, 264, 200), V_DMA, -1, 0),           # direct-to-LDS tiles
     ((16, 2048, 4096), V_SPLIT, 3, 4),         # strips in 4 parts: strip counters and partial slots
-    ((16, 14336, 520), V_SPLIT, 9, 0),         # stream-K over strips: strip counters
+    ((16, 14336, 520), V_SPLIT, 10, 0),         # stream-K over strips: strip counters
     ((40, 264, 4096), V_SPLIT, 2, 0),          # stream-K tiles: tile counters
     ((48, 1024, 2048), V_SPLIT, 0, 4),         # two kernels: partials, then the ordered reduce
+    ((48, 4096, 1024), V_SPLIT, 9, 4),         # 64-row strips in 4 parts
     ((16, 8192, 1024), V_AUTO, -1, 0),         # the default skinny path
 ]
 

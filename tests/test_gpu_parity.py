@@ -115,7 +115,7 @@ def test_ragged_full_output(dev, kind):
 
 @pytest.mark.parametrize("config,splits", [(-1, 0), (0, 1), (0, 2), (0, 4), (0, 8), (0, 16), (1, 4), (2, 0), (3, 0),
                                            (3, 2), (3, 5), (3, 16), (4, 0), (5, 0), (6, 0), (6, 1), (7, 0), (8, 0),
-                                           (8, 1), (9, 0), (10, 0)])
+                                           (8, 1), (9, 0), (9, 2), (10, 0), (11, 0)])
 def test_skinny_full_output(dev, config, splits):
     w = wl.WORKLOADS["skinny16x14336x4096"]
     A, B = wl.make_inputs(w)
@@ -147,7 +147,7 @@ def test_streamk_shapes(dev, shape):
         assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
 
 
-@pytest.mark.parametrize("config", [3, 4, 5, 6, 7, 8, 9, 10])
+@pytest.mark.parametrize("config", [3, 4, 5, 6, 7, 8, 9, 10, 11])
 @pytest.mark.parametrize("parts", [1, 3])
 @pytest.mark.parametrize("shape", [(16, 14336, 520), (1, 8, 8), (32, 264, 4096), (7, 128, 8192), (17, 392, 1000),
                                    (16, 64, 32), (31, 1032, 264)])
@@ -166,6 +166,27 @@ def test_wave_split_shapes(dev, shape, parts, config):
         torch.cuda.synchronize()
         allb = bits(big)
         assert np.array_equal(allb[:M, :N], ref), (shape, config)
+        assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+
+
+@pytest.mark.parametrize("parts", [0, 1, 4])
+@pytest.mark.parametrize("shape", [(48, 4096, 1000), (64, 264, 4096), (33, 392, 520), (63, 1032, 264), (40, 64, 8192),
+                                   (64, 4096, 14336)])
+def test_strip64_shapes(dev, shape, parts):
+    """The 64-row strip (32 < M <= 64, one pass over B): ragged M and N, K
+    tails, one strip, strips split among 4 work-groups, planned parts; NaN
+    sentinel and padding columns; each case twice (strip counters back at
+    zero). Exact on integer inputs; the largest shape on sampled rows."""
+    M, N, K = shape
+    print(f"strip64 {shape} parts={parts}", flush=True)
+    A, B = wl.make_random(M, N, K, seed=M + 9 * N + 5 * K, kind="integer")
+    ref = oracle.gemm_relu(A, B)
+    for _ in range(2):
+        big = torch.full((M + 1, N + 8), float("nan"), dtype=torch.float16, device=dev)
+        tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), out=big[:M, :N], variant=V_SPLIT, config=9, splits=parts)
+        torch.cuda.synchronize()
+        allb = bits(big)
+        assert np.array_equal(allb[:M, :N], ref), (shape, parts)
         assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
 
 

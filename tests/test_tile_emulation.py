@@ -124,6 +124,19 @@ def test_dma_tiles_match_oracle_integer(emu, config, shape):
     assert np.array_equal(C, oracle.gemm_relu(A, B))
 
 
+@pytest.mark.parametrize("shape", [(48, 64, 128), (64, 136, 520), (33, 392, 64), (1, 8, 8), (63, 200, 1000)])
+def test_one_wave_strip_tile_matches_oracle_integer(emu, shape):
+    """The 64-row strip's ring layout (one wave loads and multiplies a whole
+    64 x 64 x 64 block: eight 1 KiB loads of A and of B, 2 x 2 MFMA tiles),
+    emulated over the problem's strips: loads in bounds, each LDS byte written
+    once, no bank conflicts, exact result."""
+    M, N, K = shape
+    A, B = wl.make_random(M, N, K, seed=M + 2 * N + K, kind="integer_pos" if K > 100 else "integer")
+    C, errs = run_emu(emu, 8, A, B)
+    assert all(v == 0 for v in errs.values()), errs
+    assert np.array_equal(C, oracle.gemm_relu(A, B))
+
+
 RAGGED = [(301, 259, 203), (65, 9, 17), (130, 264, 97), (33, 41, 8), (257, 131, 1), (64, 64, 65), (3, 263, 72)]
 
 

@@ -180,14 +180,20 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
         }
     }
 
-    // split-K for skinny M: by default when M fits one strip (M <= 32,
-    // aligned), or M <= 64 with 64 x 64 tiles for fewer than half the CUs;
-    // with more tiles the tiled kernels measured faster (64x14336x4096:
-    // 32 us on 64 x 64 tiles, 63 us stream-K)
+    // split-K for skinny M: by default when M fits one 32-row strip
+    // (aligned); for 32 < M <= 64 on aligned data, 64-row strips from
+    // K = 2048 up (one pass over B: 48x4096x4096 14.9 us vs 22.5 on 64 x 64
+    // tiles and 27.9 stream-K, 48x14336x4096 29.6 vs 31.1, 64x1024x8192
+    // 19.2 vs 42.0; at K = 1024 the tiles win, 7.8 vs 10.4); unaligned
+    // M <= 64 with 64 x 64 tiles for fewer than half the CUs: stream-K
     const bool strip_fits = p.M <= tlg::kStripConfig.bm &&
                             dma_ok_aligned(p, tlg::kStripConfig.bm, tlg::kStripConfig.bn, tlg::kStripConfig.bk);
+    const tlg::TileConfig &t64 = tlg::kStripConfigs[tlg::SPLIT_WAVES_64x64x64 - tlg::SPLIT_WAVES_32x64x64];
+    const bool strip64_fits = !strip_fits && p.M <= t64.bm && dma_ok_aligned(p, t64.bm, t64.bn, t64.bk) &&
+                              ceil_div(p.N, t64.bn) <= 0x7fffffff;
     const bool few_tiles = p.M <= 64 && ceil_div(p.N, 64) * 2 < cus;
-    if (variant == TLG_VARIANT_SPLITK || (variant == TLG_VARIANT_AUTO && (strip_fits || few_tiles) && p.K >= 512)) {
+    const bool auto_split = strip_fits || (strip64_fits ? p.K >= 2048 : few_tiles);
+    if (variant == TLG_VARIANT_SPLITK || (variant == TLG_VARIANT_AUTO && auto_split && p.K >= 512)) {
         if (!config_ok(config, tlg::SPLIT_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
         // K split among the waves of a work-group per column strip, when M
         // fits one strip and there are strips for at least half the CUs
@@ -196,7 +202,7 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
             const tlg::TileConfig &t0 = tlg::kStripConfig;
             const bool ok0 = p.M <= t0.bm && dma_ok_aligned(p, t0.bm, t0.bn, t0.bk) &&
                              ceil_div(p.N, t0.bn) <= 0x7fffffff;
-            cfg = ok0 ? tlg::SPLIT_WAVES_32x64x64 : tlg::SPLIT_STREAMK_32x128x64;
+            cfg = ok0 ? tlg::SPLIT_WAVES_32x64x64 : strip64_fits ? tlg::SPLIT_WAVES_64x64x64 : tlg::SPLIT_STREAMK_32x128x64;
         }
         if (tlg::is_strip_config(cfg)) {
             const tlg::TileConfig &ts = tlg::kStripConfigs[cfg - tlg::SPLIT_WAVES_32x64x64];

@@ -1,4 +1,4 @@
-// Skinny problems (M <= 32, many columns): split-K inside one work-group.
+// Skinny problems (M <= 64, many columns): split-K inside one work-group.
 //
 // The two-stage split-K of the TileLang article (aiwiki.ai/wiki/tilelang,
 // "Adoption by DeepSeek": K partitioned for small-batch decoding, partial
@@ -465,13 +465,16 @@ __global__ __launch_bounds__(W * 64) void k_skinny_sk(const KArgs a) {
 // Strip configurations: one wave per ring, W rings per work-group. Index
 // 0 is the default; the others trade more bytes in flight per work-group
 // (four waves, four stages) or wider strips (whole 256- or 512-byte row
-// pieces of B per request, with more parts per strip) for LDS.
+// pieces of B per request, with more parts per strip) for LDS. The 64-row
+// strip serves 32 < M <= 64 with one pass over B (32-row tiles would read
+// each strip of B twice).
 using Strip32x64 = TileShape<32, 64, 64, 1, 1, 3>;
 using Strip32x64S4 = TileShape<32, 64, 64, 1, 1, 4>;
 using Strip32x64S2 = TileShape<32, 64, 64, 1, 1, 2>;
 using Strip32x128 = TileShape<32, 128, 64, 1, 1, 3>;
 using Strip32x128S2 = TileShape<32, 128, 64, 1, 1, 2>;
 using Strip32x256 = TileShape<32, 256, 32, 1, 1, 3>;
+using Strip64x64 = TileShape<64, 64, 64, 1, 1, 3>;
 
 #define TLG_STRIP_CFG(S, W, name) {S::BM, S::BN, S::BK, (W) * 64, S::STAGES, name}
 const TileConfig kStripConfigs[STRIP_CONFIGS] = {
@@ -481,6 +484,7 @@ const TileConfig kStripConfigs[STRIP_CONFIGS] = {
     TLG_STRIP_CFG(Strip32x128, 2, "splitk_waves_32x128x64_w2_s3"),
     TLG_STRIP_CFG(Strip32x128S2, 4, "splitk_waves_32x128x64_w4_s2"),
     TLG_STRIP_CFG(Strip32x256, 2, "splitk_waves_32x256x32_w2_s3"),
+    TLG_STRIP_CFG(Strip64x64, 2, "splitk_waves_64x64x64_w2_s3"),
 };
 #undef TLG_STRIP_CFG
 const TileConfig &kStripConfig = kStripConfigs[0];
@@ -556,6 +560,7 @@ hipError_t launch_skinny_strip(int config, const Problem &p, int parts, float *p
         case 3: return launch_strip_t<Strip32x128, 2>(p, parts, partials, counters, stream);
         case 4: return launch_strip_t<Strip32x128S2, 4>(p, parts, partials, counters, stream);
         case 5: return launch_strip_t<Strip32x256, 2>(p, parts, partials, counters, stream);
+        case 6: return launch_strip_t<Strip64x64, 2>(p, parts, partials, counters, stream);
         default: return hipErrorInvalidValue;
     }
 }

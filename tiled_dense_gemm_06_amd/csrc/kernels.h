@@ -47,8 +47,8 @@ enum GenConfig { GEN_128x128x32 = 0, GEN_64x64x32 = 1, GEN_CONFIGS = 2 };
 enum SplitConfig { SPLIT_32x128x64 = 0, SPLIT_32x256x64 = 1, SPLIT_TWO_KERNEL_CONFIGS = 2,
                    SPLIT_STREAMK_32x128x64 = 2, SPLIT_WAVES_32x64x64 = 3, SPLIT_WAVES_32x64x64_W4 = 4,
                    SPLIT_WAVES_32x64x64_S4 = 5, SPLIT_WAVES_32x128x64 = 6, SPLIT_WAVES_32x128x64_W4 = 7,
-                   SPLIT_WAVES_32x256x32 = 8, SPLIT_STRIP_SK_32x64x64 = 9, SPLIT_STRIP_SK_32x64x64_S2 = 10,
-                   SPLIT_CONFIGS = 11 };
+                   SPLIT_WAVES_32x256x32 = 8, SPLIT_WAVES_64x64x64 = 9, SPLIT_STRIP_SK_32x64x64 = 10,
+                   SPLIT_STRIP_SK_32x64x64_S2 = 11, SPLIT_CONFIGS = 12 };
 // strip configuration j is split configuration SPLIT_WAVES_32x64x64 + j
 constexpr int STRIP_CONFIGS = SPLIT_STRIP_SK_32x64x64 - SPLIT_WAVES_32x64x64;
 inline bool is_strip_config(int config) { return config >= SPLIT_WAVES_32x64x64 && config < SPLIT_STRIP_SK_32x64x64; }
