@@ -12,6 +12,7 @@ def test_registry_shapes():
     w = wl.WORKLOADS["square8192"]
     assert w.flop == 1_099_511_627_776 and w.alg_bytes == 402_653_184
     assert wl.WORKLOADS["skinny16x14336x4096"].alg_bytes == 118_030_336
+    assert "decode48x4096x14336" not in wl.ORDER and wl.WORKLOADS["decode48x4096x14336"].alg_bytes == 2 * (48 * 14336 + 14336 * 4096 + 48 * 4096)
 
 
 def test_deterministic_and_typed():

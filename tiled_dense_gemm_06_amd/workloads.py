@@ -69,6 +69,10 @@ WORKLOADS = {
                  "M=16 N=14336 K=4096, A U[-1,1], B N(0, std 0.02) from seed 3"),
         Workload("square8192", 8192, 8192, 8192, 4, _U, _U,
                  "M=N=K=8192, U[-1,1] from seed 4"),
+        # not one of the pages' configurations: a decode batch between one and
+        # two 32-row MFMA blocks, measured with bench.py --workload
+        Workload("decode48x4096x14336", 48, 4096, 14336, 5, _U, Dist("normal", 0.02),
+                 "M=48 N=4096 K=14336, A U[-1,1], B N(0, std 0.02) from seed 5"),
     ]
 }
 
