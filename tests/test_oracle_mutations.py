@@ -88,3 +88,77 @@ def test_mx_pins_catch_planted_mistake(name, old, new, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_mx_pins.py")],
                        env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
     assert r.returncode == 1, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
+
+
+# ---------------------------------------------------------------- the layout and batching wrappers
+# Broken copies of oracle.gemm_relu_bt, oracle.gemm_relu_grouped and
+# oracle.mx.gemm_relu_mx_grouped, each with one plausible bookkeeping mistake;
+# the wrapper pins must reject every one.
+
+from test_oracle_wrapper_pins import check_bt, check_grouped, check_mx_grouped  # noqa: E402
+
+import numpy as np  # noqa: E402
+
+import oracle.mx as omx  # noqa: E402
+
+
+def _bt_dropped_transpose(A, Bt, threads=None):
+    return oracle.gemm_relu(A, np.ascontiguousarray(Bt), threads)
+
+
+def _bt_a_for_b(A, Bt, threads=None):
+    # B taken from A's buffer (operands mixed up): right shape when M == N
+    return oracle.gemm_relu(A, np.ascontiguousarray(A.T if A.shape[0] == Bt.shape[0] else Bt.T), threads)
+
+
+def _grouped_reversed(problems, trans_b=False, threads=None):
+    return list(reversed(oracle.gemm_relu_grouped(problems, trans_b, threads)))
+
+
+def _grouped_ignores_trans_b(problems, trans_b=False, threads=None):
+    return [oracle.gemm_relu(A, B, threads) for A, B in problems]
+
+
+def _grouped_b_of_next_problem(problems, trans_b=False, threads=None):
+    f = oracle.gemm_relu_bt if trans_b else oracle.gemm_relu
+    out = []
+    for t, (A, _) in enumerate(problems):
+        B = problems[(t + 1) % len(problems)][1]
+        out.append(f(A, B, threads))
+    return out
+
+
+def _mx_grouped_rotated(fmt, problems, threads=None):
+    res = omx.gemm_relu_mx_grouped(fmt, problems, threads)
+    return res[1:] + res[:1]
+
+
+def _mx_grouped_scales_of_next(fmt, problems, threads=None):
+    out = []
+    for t, (A, SA, Bt, SB) in enumerate(problems):
+        SAn, SBn = problems[(t + 1) % len(problems)][1], problems[(t + 1) % len(problems)][3]
+        if SAn.shape != SA.shape or SBn.shape != SB.shape:
+            SAn, SBn = SA, SB[::-1].copy()
+        out.append(omx.gemm_relu_mx(fmt, A, SAn, Bt, SBn, threads))
+    return out
+
+
+@pytest.mark.parametrize("mutant", [_bt_dropped_transpose, _bt_a_for_b], ids=lambda f: f.__name__)
+def test_bt_pin_catches_planted_mistake(mutant):
+    with pytest.raises((AssertionError, ValueError)):
+        check_bt(mutant)
+
+
+@pytest.mark.parametrize("mutant", [_grouped_reversed, _grouped_ignores_trans_b, _grouped_b_of_next_problem],
+                         ids=lambda f: f.__name__)
+def test_grouped_pin_catches_planted_mistake(mutant):
+    with pytest.raises((AssertionError, ValueError)):
+        check_grouped(mutant)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("mutant", [_mx_grouped_rotated, _mx_grouped_scales_of_next], ids=lambda f: f.__name__)
+def test_mx_grouped_pin_catches_planted_mistake(mutant, fmt):
+    pytest.importorskip("torch")
+    with pytest.raises((AssertionError, ValueError)):
+        check_mx_grouped(mutant, fmt)
