@@ -322,3 +322,38 @@ def test_strip_configurations_plan():
     assert tlg.plan(16, 64 * 300, 4096, variant=V, config=11)["grid"] == 512
     with pytest.raises(tlg.TlgError):
         tlg.plan(16, 14336, 4096, variant=V, config=12)
+
+
+def test_zero_k_plans_of_every_call_refuse_sizes_beyond_the_limit():
+    """K == 0 plans the fill kernel (256 threads, at most 65536 work-groups);
+    sizes beyond the library's limit are refused before M * N is formed, in
+    the plain, transposed-B and block-scaled planners alike."""
+    big = (1 << 40)
+    for M, N in ((big, 8), (8, big), ((1 << 31) - 1024 + 1, 1)):
+        st, _ = nat.tlg_plan(M, N, 0, A16, 1, A16, N, A16, N)
+        assert st == nat.TLG_ERROR_NOT_SUPPORTED, (M, N)
+        st, _ = nat.tlg_plan_bt(M, N, 0, A16, 1, A16, 1, A16, N, 0, -1)
+        assert st == nat.TLG_ERROR_NOT_SUPPORTED, (M, N)
+        with pytest.raises(tlg.TlgError):
+            tlg.plan_mx("e4m3", M, N, 0)
+    for f in (lambda: tlg.plan(5, 7, 0), lambda: tlg.plan(5, 7, 0, trans_b=True),
+              lambda: tlg.plan_mx("e4m3", 5, 7, 0)):
+        p = f()
+        assert p["variant_name"] == "fill_zero" and p["threads"] == 256 and p["grid"] == 1
+    assert tlg.plan(4096, 4096, 0)["grid"] == 65536
+
+
+def test_streamk_plan_of_huge_forced_shapes_does_not_overflow():
+    """Forced stream-K on sizes with more tiles than counters: refused, and
+    the iteration count is never formed from a tile count that large."""
+    st, _ = nat.tlg_plan(1 << 30, 1 << 24, 1 << 25, A16, 1 << 25, A16, 1 << 24, A16, 1 << 24,
+                         tlg.TLG_VARIANT_SPLITK, 2, 0)
+    assert st == nat.TLG_ERROR_NOT_SUPPORTED
+
+
+def test_status_string_of_any_int():
+    L = ctypes.CDLL(nat.LIB_PATH)
+    L.tlg_status_string.argtypes = [ctypes.c_int]
+    L.tlg_status_string.restype = ctypes.c_char_p
+    for v in (-2, -1, 5, 7, 1 << 20):
+        assert L.tlg_status_string(v) == b"unknown tlg_status"

@@ -60,7 +60,8 @@ def candidates(tlg, M, N, K):
     trials += [(tlg.TLG_VARIANT_TILED_DMA, c, 0) for c in range(5)]
     if M <= 64:
         # two-kernel split-K (0, 1), stream-K tiles (2), strips with 1..8
-        # parts (3), the other strip shapes (4..8), stream-K strips (9, 10)
+        # parts (3), the other strip shapes (4..8), the 64-row strip (9),
+        # stream-K strips (10, 11)
         trials += [(tlg.TLG_VARIANT_SPLITK, 3, s) for s in (1, 2, 4, 8)]
         trials += [(tlg.TLG_VARIANT_SPLITK, c, 0) for c in (0, 1, 2) + tuple(range(4, 12))]
     for v, c, s in trials:

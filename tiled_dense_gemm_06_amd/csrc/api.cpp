@@ -86,6 +86,19 @@ const TuneEntry *tune_lookup(const tlg::Problem &p) {
 }
 
 void fill_info(tlg_plan_info *o, int variant, int config, const tlg::TileConfig *tc, int splits, int kernels,
+               int64_t grid, int64_t ws);
+
+// K == 0: C = +0 by the fill kernel (256 threads per work-group, at most
+// 65536 work-groups striding over the window). M and N must already be
+// known to be at most kMaxDim, so M * N cannot overflow.
+void fill_zero_info(tlg_plan_info *o, int64_t M, int64_t N) {
+    int64_t blocks = (M * N + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    fill_info(o, TLG_VARIANT_FILL_ZERO, 0, nullptr, 1, 1, blocks, 0);
+    o->threads = 256;
+}
+
+void fill_info(tlg_plan_info *o, int variant, int config, const tlg::TileConfig *tc, int splits, int kernels,
                int64_t grid, int64_t ws) {
     memset(o, 0, sizeof *o);
     o->variant = variant;
@@ -148,9 +161,7 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
     if (variant == TLG_VARIANT_AUTO && p.K == 0) variant = TLG_VARIANT_FILL_ZERO;
     if (variant == TLG_VARIANT_FILL_ZERO) {
         if (p.K != 0) return TLG_ERROR_NOT_SUPPORTED;
-        int64_t blocks = ceil_div(p.M * p.N, 256);
-        if (blocks > 65536) blocks = 65536;
-        fill_info(o, TLG_VARIANT_FILL_ZERO, 0, nullptr, 1, 1, blocks, 0);
+        fill_zero_info(o, p.M, p.N);
         return TLG_SUCCESS;
     }
     if (variant == TLG_VARIANT_NAIVE) {
@@ -248,12 +259,15 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
             // equal range of the (tile, k) iterations
             const tlg::TileConfig &tc = tlg::kStreamKConfig;
             const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
-            const int64_t total = tiles * ceil_div(p.K, tc.bk);
+            // one counter per tile (at most 16384 tiles, so the iteration
+            // count below stays far from overflow)
+            const bool counters_fit = tiles * 4 <= kCounterBytes;
+            const int64_t total = counters_fit ? tiles * ceil_div(p.K, tc.bk) : 0;
             const int64_t slot_bytes = 2ll * tc.bm * tc.bn * 4;
             int64_t grid = (int64_t)cus * tlg::kStreamKBlocksPerCU;
             if (grid > total) grid = total;
             if (grid * slot_bytes > cap) grid = cap / slot_bytes;
-            const bool ok = dma_ok_aligned(p, tc.bm, tc.bn, tc.bk) && tiles * 4 <= kCounterBytes && grid >= 1 &&
+            const bool ok = dma_ok_aligned(p, tc.bm, tc.bn, tc.bk) && counters_fit && grid >= 1 &&
                             total * grid < (1ll << 62) && total < (1ll << 31);
             if (ok) {
                 fill_info(o, TLG_VARIANT_SPLITK, cfg, &tc, (int)ceil_div(grid, tiles), 1, grid,
@@ -426,8 +440,9 @@ tlg_status plan_bt(const tlg::Problem &p, int32_t variant, int32_t config, tlg_p
         fill_info(o, TLG_VARIANT_NOOP, 0, nullptr, 1, 0, 0, 0);
         return TLG_SUCCESS;
     }
+    if (p.M > kMaxDim || p.N > kMaxDim || p.K > kMaxDim) return TLG_ERROR_NOT_SUPPORTED;
     if (p.K == 0) {
-        fill_info(o, TLG_VARIANT_FILL_ZERO, 0, nullptr, 1, 1, ceil_div(p.M * p.N, 256 * 8), 0);
+        fill_zero_info(o, p.M, p.N);
         return TLG_SUCCESS;
     }
     const int64_t t256 = ceil_div(p.M, 256) * ceil_div(p.N, 256);
@@ -559,14 +574,15 @@ tlg_status plan_mx(const tlg::MxProblem &p, int32_t config, tlg_plan_info *o) {
         fill_info(o, TLG_VARIANT_NOOP, 0, nullptr, 1, 0, 0, 0);
         return TLG_SUCCESS;
     }
+    if (p.M > kMaxDim || p.N > kMaxDim || p.K > kMaxDim) return TLG_ERROR_NOT_SUPPORTED;
     if (p.K == 0) {
-        fill_info(o, TLG_VARIANT_FILL_ZERO, 0, nullptr, 1, 1, ceil_div(p.M * p.N, 256 * 8), 0);
+        fill_zero_info(o, p.M, p.N);
         return TLG_SUCCESS;
     }
     // stages of 128 codes (four scale blocks): K a multiple of 128; 16-byte
     // chunks wholly inside a row; scale dwords aligned
     const int epb = mx_codes_per_byte(p.format);
-    if (p.K % 128 || p.M > kMaxDim || p.N > kMaxDim || p.K > kMaxDim) return TLG_ERROR_NOT_SUPPORTED;
+    if (p.K % 128) return TLG_ERROR_NOT_SUPPORTED;
     if (!aligned(p.A, 16) || !aligned(p.B, 16) || (p.lda / epb) % 16 || (p.ldb / epb) % 16)
         return TLG_ERROR_NOT_SUPPORTED;
     if (!aligned(p.SA, 4) || !aligned(p.SB, 4) || p.ldsa % 4 || p.ldsb % 4) return TLG_ERROR_NOT_SUPPORTED;
@@ -745,9 +761,10 @@ tlg_status tlg_create(tlg_handle *out) {
         delete ctx;
         return TLG_ERROR_OUT_OF_MEMORY;
     }
-    // the stream-K counters start at zero (each call leaves them zero)
-    if (hipMemset(ctx->workspace, 0, (size_t)kCounterBytes) != hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess) {
+    // the stream-K counters start at zero (each call leaves them zero); the
+    // clear runs on the null stream, so waiting on that stream is enough
+    if (hipMemsetAsync(ctx->workspace, 0, (size_t)kCounterBytes, nullptr) != hipSuccess ||
+        hipStreamSynchronize(nullptr) != hipSuccess) {
         (void)hipGetLastError();
         (void)hipFree(ctx->workspace);
         delete ctx;
@@ -777,7 +794,11 @@ tlg_status tlg_gemm_relu_variant(tlg_handle h, int32_t variant, int32_t config, 
 }
 
 const char *tlg_status_string(tlg_status s) {
-    switch (s) {
+    // a C caller may pass any int: read the argument's bytes as an int
+    // instead of loading an enum value that may be out of its range
+    int v;
+    memcpy(&v, &s, sizeof v);
+    switch (v) {
         case TLG_SUCCESS: return "TLG_SUCCESS";
         case TLG_ERROR_INVALID_VALUE: return "TLG_ERROR_INVALID_VALUE: an argument is out of range";
         case TLG_ERROR_NOT_SUPPORTED: return "TLG_ERROR_NOT_SUPPORTED: the device or request is not supported";
