@@ -154,6 +154,39 @@ const char *tlg_status_string(tlg_status s);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int32_t tlg_version(void);
 
+/* ---- allocation-free call ----
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. */
+
+/* Bytes of the library's static per-device scratch array used by
+ * tlg_gemm_relu_noalloc (64 KiB of split-kernel counters, 8 MiB of fp32
+ * partials). */
+#define TLG_NOALLOC_SCRATCH_BYTES ((int64_t)(64 << 10) + ((int64_t)8 << 20))
+
+/* tlg_gemm_relu without a handle, allocating nothing: same operation,
+ * arguments, checks and errors as tlg_gemm_relu on the CURRENT device (the
+ * library's own choice of kernel). The split kernels' counters and partials
+ * live in a static device array of TLG_NOALLOC_SCRATCH_BYTES that every GPU
+ * the library runs on holds until the process ends; its address is looked
+ * up on the first call on each device (which also checks that the device is
+ * gfx950: TLG_ERROR_NOT_SUPPORTED otherwise). No hipMalloc, hipFree or other
+ * allocating call is made, on the first call or later. Kernels are planned
+ * to fit the scratch (fewer K splits than tlg_gemm_relu where a handle's
+ * larger workspace would allow more); a plan that could not fit it is
+ * refused with TLG_ERROR_NOT_SUPPORTED, nothing enqueued. The counter area
+ * is cleared by a kernel on `stream` before each split kernel that uses it.
+ * All calls on one GPU share its scratch array: calls that may overlap in
+ * time on one GPU (other streams, other threads) race and must be ordered
+ * by the caller. */
+tlg_status tlg_gemm_relu_noalloc(int64_t M, int64_t N, int64_t K,
+                                 const void *A, int64_t lda,
+                                 const void *B, int64_t ldb,
+                                 void *C, int64_t ldc,
+                                 hipStream_t stream);
+
+/* TLG_NOALLOC_SCRATCH_BYTES, as built into the library. */
+int64_t tlg_noalloc_scratch_bytes(void);
+
 /* ---- layout and batching variants ----
  * The same operation with B given transposed, and several problems in one
  * launch. The forum post "TileLang: Writing Near-Hardware-Limit GPU Kernels

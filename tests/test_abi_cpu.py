@@ -357,3 +357,13 @@ def test_status_string_of_any_int():
     L.tlg_status_string.restype = ctypes.c_char_p
     for v in (-2, -1, 5, 7, 1 << 20):
         assert L.tlg_status_string(v) == b"unknown tlg_status"
+
+
+def test_noalloc_entry_point_checks_arguments_without_a_gpu():
+    """tlg_gemm_relu_noalloc checks its arguments as tlg_gemm_relu does,
+    before any device call: bad arguments give TLG_ERROR_INVALID_VALUE."""
+    assert nat.tlg_noalloc_scratch_bytes() == (64 << 10) + (8 << 20)
+    bad = [(-1, 4, 4, A16, 4, A16, 4, A16, 4), (4, 4, 4, A16, 3, A16, 4, A16, 4), (4, 4, 4, 0, 4, A16, 4, A16, 4),
+           (4, 4, 4, A16 + 1, 4, A16, 4, A16, 4), (4, 4, 4, A16, 4, A16, 4, A16, 3)]
+    for args in bad:
+        assert nat.tlg_gemm_relu_noalloc(*args, 0) == nat.TLG_ERROR_INVALID_VALUE, args

@@ -99,6 +99,10 @@ def lib():
         L.tlg_destroy.restype = i32
         L.tlg_gemm_relu.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p]
         L.tlg_gemm_relu.restype = i32
+        L.tlg_gemm_relu_noalloc.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+        L.tlg_gemm_relu_noalloc.restype = i32
+        L.tlg_noalloc_scratch_bytes.argtypes = []
+        L.tlg_noalloc_scratch_bytes.restype = i64
         L.tlg_gemm_relu_variant.argtypes = [p, i32, i32, i32, i64, i64, i64, p, i64, p, i64, p, i64, p]
         L.tlg_gemm_relu_variant.restype = i32
         L.tlg_check_args.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
@@ -158,6 +162,14 @@ def tlg_destroy(h: int) -> int:
 
 def tlg_gemm_relu(h, M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
     return lib().tlg_gemm_relu(h, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def tlg_gemm_relu_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
+    return lib().tlg_gemm_relu_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def tlg_noalloc_scratch_bytes() -> int:
+    return int(lib().tlg_noalloc_scratch_bytes())
 
 
 def tlg_gemm_relu_variant(h, variant, config, splits, M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:

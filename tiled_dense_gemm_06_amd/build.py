@@ -12,7 +12,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtlg.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("api.cpp", "gemm_relu_gfx950.hip", "gemm_relu_pipe_gfx950.hip",
                                                  "gemm_relu_streamk_gfx950.hip", "gemm_relu_skinny_gfx950.hip",
-                                                 "gemm_relu_mx_gfx950.hip", "gemm_relu_pingpong_gfx950.hip")]
+                                                 "gemm_relu_mx_gfx950.hip", "gemm_relu_pingpong_gfx950.hip",
+                                                 "noalloc.hip")]
 
 # gfx950 only. Packed fp32 instructions are disabled for every GPU code path
 # (the host pass reports the feature as unknown, which is harmless).

@@ -25,9 +25,10 @@ constexpr int32_t kVersion = 100;  // 0.1.0
 // fp32 split-K partials: 32 MiB covers S x M x N x 4 bytes for the skinny
 // shapes the split path serves (S is lowered when a shape needs more).
 constexpr int64_t kWorkspaceBytes = 32ll << 20;
-// The first 64 KiB of the workspace hold the stream-K per-tile counters
-// (zeroed once at creation; every call leaves them zero); partials follow.
-constexpr int64_t kCounterBytes = 64ll << 10;
+// The first kCounterBytes (64 KiB) of the workspace hold the stream-K
+// per-tile counters (zeroed once at creation; every call leaves them zero);
+// partials follow.
+using tlg::kCounterBytes;
 constexpr int kPlanCUs = 256;  // tlg_plan plans for a 256-CU MI355X
 // Largest in-tile byte offset a buffer load may use (see the kernels).
 constexpr int64_t kMaxOffset = 0x7ffffff0ll - 16;
@@ -352,19 +353,30 @@ tlg::Problem make_problem(int64_t M, int64_t N, int64_t K, const void *A, int64_
     return p;
 }
 
-tlg_status run(tlg_handle h, int32_t variant, int32_t config, int32_t splits, const tlg::Problem &p,
-               hipStream_t stream) {
-    if (!h) return TLG_ERROR_INVALID_VALUE;
+}  // namespace
+
+namespace tlg {
+
+// Plans one call for a device with `cus` compute units and a workspace of
+// `workspace_bytes` at `workspace` (its first kCounterBytes the split
+// kernels' counters), then enqueues it. With clear_counters the counter area
+// is cleared on the stream before a split kernel that uses it.
+tlg_status run_with_workspace(float *workspace, int64_t workspace_bytes, int cus, bool clear_counters,
+                              int32_t variant, int32_t config, int32_t splits, const Problem &p,
+                              hipStream_t stream) {
     tlg_status st = tlg_check_args(p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc);
     if (st != TLG_SUCCESS) return st;
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) return TLG_ERROR_HIP;
-    if (dev != h->device) return TLG_ERROR_INVALID_VALUE;  // the handle's device must be current
     tlg_plan_info info;
     int64_t k_split = 0;
-    st = plan_impl(p, variant, config, splits, h->workspace_bytes, h->cus, &info, &k_split);
+    st = plan_impl(p, variant, config, splits, workspace_bytes, cus, &info, &k_split);
     if (st != TLG_SUCCESS) return st;
+    if (info.workspace_bytes > workspace_bytes) return TLG_ERROR_NOT_SUPPORTED;
+    float *const ws = workspace;
     hipError_t e = hipSuccess;
+    if (clear_counters && info.variant == TLG_VARIANT_SPLITK && info.workspace_bytes > 0) {
+        e = launch_clear_words((int *)ws, kCounterBytes / 4, stream);
+        if (e != hipSuccess) return TLG_ERROR_HIP;
+    }
     switch (info.variant) {
         case TLG_VARIANT_NOOP: return TLG_SUCCESS;
         case TLG_VARIANT_FILL_ZERO: e = tlg::launch_fill_zero(p, stream); break;
@@ -374,15 +386,15 @@ tlg_status run(tlg_handle h, int32_t variant, int32_t config, int32_t splits, co
         case TLG_VARIANT_TILED_PIPE: e = tlg::launch_tiled_pipe(info.config, p, stream); break;
         case TLG_VARIANT_PINGPONG: e = tlg::launch_pingpong(info.config, p, stream); break;
         case TLG_VARIANT_SPLITK: {
-            float *partials = h->workspace + kCounterBytes / sizeof(float);
+            float *partials = ws + kCounterBytes / sizeof(float);
             if (tlg::is_strip_sk_config(info.config))
                 e = tlg::launch_skinny_strip_sk(info.config - tlg::SPLIT_STRIP_SK_32x64x64, p, (int)info.grid,
-                                                partials, (int *)h->workspace, stream);
+                                                partials, (int *)ws, stream);
             else if (tlg::is_strip_config(info.config))
                 e = tlg::launch_skinny_strip(info.config - tlg::SPLIT_WAVES_32x64x64, p, info.splits, partials,
-                                             (int *)h->workspace, stream);
+                                             (int *)ws, stream);
             else if (info.config == tlg::SPLIT_STREAMK_32x128x64)
-                e = tlg::launch_streamk(p, (int)info.grid, partials, (int *)h->workspace, stream);
+                e = tlg::launch_streamk(p, (int)info.grid, partials, (int *)ws, stream);
             else
                 e = tlg::launch_splitk(info.config, info.splits, k_split, p, partials, stream);
             break;
@@ -390,6 +402,27 @@ tlg_status run(tlg_handle h, int32_t variant, int32_t config, int32_t splits, co
         default: return TLG_ERROR_NOT_SUPPORTED;
     }
     return e == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
+}
+
+tlg::Problem make_problem_c(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
+                            void *C, int64_t ldc) {
+    return make_problem(M, N, K, A, lda, B, ldb, C, ldc);
+}
+
+}  // namespace tlg
+
+namespace {
+
+tlg_status run(tlg_handle h, int32_t variant, int32_t config, int32_t splits, const tlg::Problem &p,
+               hipStream_t stream) {
+    if (!h) return TLG_ERROR_INVALID_VALUE;
+    tlg_status st = tlg_check_args(p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc);
+    if (st != TLG_SUCCESS) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return TLG_ERROR_HIP;
+    if (dev != h->device) return TLG_ERROR_INVALID_VALUE;  // the handle's device must be current
+    return tlg::run_with_workspace(h->workspace, h->workspace_bytes, h->cus, false, variant, config, splits, p,
+                                   stream);
 }
 
 // ---- transposed B and grouped calls ----

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
+#include "tlg.h"
+
 namespace tlg {
 
 // One GEMM+ReLU problem: C (M x N) = ReLU(A (M x K) . B (K x N)), fp16,
@@ -144,6 +146,24 @@ hipError_t launch_mx_grouped(int config, const MxProblem *ps, int count, hipStre
 
 hipError_t launch_naive(const Problem &p, hipStream_t stream);
 hipError_t launch_fill_zero(const Problem &p, hipStream_t stream);
+// Sets `words` 32-bit words at `p` to zero (a kernel, so that it can be
+// captured in a graph like the calls it precedes).
+hipError_t launch_clear_words(int *p, int64_t words, hipStream_t stream);
+
+// The first kCounterBytes of a workspace hold the split kernels' per-tile and
+// per-strip counters; fp32 partials follow.
+constexpr int64_t kCounterBytes = 64ll << 10;
+
+// Plans one call (C = ReLU(A . B), any variant) for a device with `cus`
+// compute units and `workspace_bytes` of workspace at `workspace` (device
+// memory, counters first), and enqueues it on `stream`. With clear_counters
+// the counter area is cleared on the stream before a split kernel that uses
+// it. The caller has checked that the device is current and supported.
+tlg_status run_with_workspace(float *workspace, int64_t workspace_bytes, int cus, bool clear_counters,
+                              int32_t variant, int32_t config, int32_t splits, const Problem &p,
+                              hipStream_t stream);
+tlg::Problem make_problem_c(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
+                            void *C, int64_t ldc);
 
 }  // namespace tlg
 
