@@ -17,6 +17,12 @@ Prints one JSON line: the contract fields, plus
                  the stream it runs on: the replay time over the steps, or the
                  mean of the per-launch event pairs with --eager) against the
                  MI355X peak;
+  skinny       - (default run) the HBM-bound workload M = 16, N = 14336,
+                 K = 4096 timed the same way after the main steps: us per
+                 call, algorithmic GB/s and the fraction of 8 TB/s;
+  vendor_reference - (default run at 8192^3) this library's call and the
+                 vendor BLAS's plain fp16 matmul interleaved on the same
+                 inputs, after the timed steps;
   cpu_baseline - the CPU oracle timed on a bounded sample of the same workload
                  (sampled output rows), in the same unit.
 """
@@ -84,6 +90,98 @@ def time_steps(torch, step, steps: int, warmup: int, graph: bool) -> dict:
     return {"ms_per_step": starts[0].elapsed_time(ends[-1]) / steps,
             "launch_ms_avg": float(np.mean(per_launch_ms)), "launch_ms_min": float(np.min(per_launch_ms)),
             "wall": wall, "timing": "events_per_launch"}
+
+
+def rotated_inputs(torch, w, dev, A, B):
+    """R copies of the workload's A, B and C, R chosen so that the working set
+    is more than twice the Infinity Cache: every step reads from HBM."""
+    R = max(2, math.ceil(2 * MALL_BYTES / w.alg_bytes) + 1)
+    Ad0 = torch.from_numpy(A).to(dev)
+    Bd0 = torch.from_numpy(B).to(dev)
+    As = [Ad0] + [Ad0.clone() for _ in range(R - 1)]
+    Bs = [Bd0] + [Bd0.clone() for _ in range(R - 1)]
+    Cs = [torch.empty((w.M, w.N), dtype=torch.float16, device=dev) for _ in range(R)]
+    return R, As, Bs, Cs
+
+
+def skinny_record(torch, tlg, wl, dev, steps: int, warmup: int) -> dict:
+    """The HBM-bound workload (M = 16, N = 14336, K = 4096) in the default
+    plan, graph-timed on rotated inputs: microseconds per call, algorithmic
+    bytes per second and the fraction of the 8 TB/s HBM peak."""
+    w = wl.WORKLOADS["skinny16x14336x4096"]
+    A, B = wl.make_inputs(w)
+    R, As, Bs, Cs = rotated_inputs(torch, w, dev, A, B)
+    h = tlg.handle_for(dev)
+
+    def step(i, stream):
+        tlg.gemm_relu(As[i % R], Bs[i % R], out=Cs[i % R], handle=h, stream=stream)
+
+    tm = time_steps(torch, step, steps, warmup, graph=True)
+    us = tm["launch_ms_avg"] * 1e3
+    gbs = w.alg_bytes / (us * 1e-6) / 1e9
+    plan = tlg.plan(w.M, w.N, w.K)
+    return {"workload": w.name, "us_per_call": us, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS, "alg_bytes": w.alg_bytes, "steps": steps, "timing": tm["timing"],
+            "rotated_buffers": R, "kernel": plan["config_name"], "strip_columns": plan["block_n"],
+            "work_groups": plan["grid"]}
+
+
+def vendor_reference(torch, tlg, w, As, Bs, Cs, R: int, rounds: int, calls: int) -> dict:
+    """Outside the timed region: this library's default call and the vendor
+    BLAS (torch.matmul, which dispatches to hipBLASLt on this GPU; fp16 in,
+    fp16 out, no ReLU, so it does less than this path) on the same rotated
+    inputs, interleaved round by round (the order alternates) so that both
+    see the same clock and thermal state. Each round times `calls`
+    back-to-back calls of one side between two events; reported per call.
+    Also the vendor's fused bias + ReLU form (torch._addmm_activation with a
+    zero bias) when this torch build provides it."""
+    import numpy as np
+
+    dev = As[0].device
+    h = tlg.handle_for(dev)
+    stream = torch.cuda.current_stream(dev)
+    Vs = [torch.empty_like(c) for c in Cs[:R]]
+    bias = torch.zeros((w.N,), dtype=torch.float16, device=dev)
+
+    def ours(i):
+        tlg.gemm_relu(As[i % R], Bs[i % R], out=Cs[i % R], handle=h, stream=stream)
+
+    def vendor(i):
+        torch.matmul(As[i % R], Bs[i % R], out=Vs[i % R])
+
+    def vendor_relu(i):
+        Vs[i % R] = torch._addmm_activation(bias, As[i % R], Bs[i % R], use_gelu=False)
+
+    sides = {"tlg": ours, "vendor_matmul": vendor}
+    try:
+        vendor_relu(0)
+        torch.cuda.synchronize()
+        sides["vendor_addmm_relu"] = vendor_relu
+    except Exception:  # noqa: BLE001 - optional torch entry point
+        pass
+    for f in sides.values():  # warm-up (and the vendor's heuristics)
+        for i in range(3):
+            f(i)
+    torch.cuda.synchronize()
+    times = {k: [] for k in sides}
+    names = list(sides)
+    for r in range(rounds):
+        order = names if r % 2 == 0 else names[::-1]
+        for k in order:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(calls):
+                sides[k](i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[k].append(e0.elapsed_time(e1) / calls * 1e3)
+    out = {"rounds": rounds, "calls_per_round": calls, "unit": "us_per_call",
+           "backend": "torch.matmul (hipBLASLt), fp16 out, no ReLU"}
+    for k, v in times.items():
+        out[k] = {"best": float(np.min(v)), "median": float(np.median(v)),
+                  "tflops_best": w.flop / (np.min(v) * 1e-6) / 1e12}
+    out["tlg_vs_vendor_matmul_best"] = out["vendor_matmul"]["best"] / out["tlg"]["best"]
+    return out
 
 
 def gpu_sysfs_info(props) -> dict:
@@ -297,6 +395,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle sample size: about this many seconds of wall time on the host's cores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the records the default run adds after its timed steps (the skinny workload's "
+                         "HBM-bound record and the interleaved vendor-BLAS reference at 8192^3)")
     ap.add_argument("--variant", default="auto",
                     help="kernel family to time (auto = what tlg_gemm_relu picks; others for comparisons): "
                          "auto, tiled_pipe, tiled_dma, tiled_general, splitk, naive")
@@ -373,13 +474,7 @@ def main() -> int:
 
     # Rotate among R copies of the inputs and outputs so the working set is
     # more than twice the Infinity Cache: every step reads from HBM.
-    per_copy = w.alg_bytes
-    R = max(2, math.ceil(2 * MALL_BYTES / per_copy) + 1)
-    Ad0 = torch.from_numpy(A).to(dev)
-    Bd0 = torch.from_numpy(B).to(dev)
-    As = [Ad0] + [Ad0.clone() for _ in range(R - 1)]
-    Bs = [Bd0] + [Bd0.clone() for _ in range(R - 1)]
-    Cs = [torch.empty((w.M, w.N), dtype=torch.float16, device=dev) for _ in range(R)]
+    R, As, Bs, Cs = rotated_inputs(torch, w, dev, A, B)
     h = tlg.handle_for(dev)
 
     def step(i, stream):
@@ -429,6 +524,15 @@ def main() -> int:
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, **gpu_sysfs_info(props)},
     }
+    default_run = plain and args.variant == "auto" and not args.eager and not args.no_extras
+    if default_run and w.name == "square8192":
+        # both outside the timed region above
+        out["vendor_reference"] = vendor_reference(torch, tlg, w, As, Bs, Cs, R, rounds=4,
+                                                   calls=max(10, min(K, 40)))
+    del As, Bs, Cs
+    if default_run and w.name != "skinny16x14336x4096":
+        torch.cuda.empty_cache()
+        out["skinny"] = skinny_record(torch, tlg, wl, dev, steps=max(K, 200), warmup=max(args.warmup, 20))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -81,3 +81,29 @@ def test_bench_json_line(extra):
     assert roof["traffic"] is None or roof["traffic"] > w.alg_bytes
     cb = out["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["unit"] == "TFLOPS" and cb["cores"] >= 1 and cb["value"] > 0
+    if extra:
+        assert "skinny" not in out and "vendor_reference" not in out
+    else:
+        sk = out["skinny"]  # the HBM-bound workload, after the timed steps
+        s4 = wl.WORKLOADS["skinny16x14336x4096"]
+        assert sk["workload"] == s4.name and sk["unit"] == "GB/s" and sk["peak"] == 8000.0
+        assert sk["achieved"] == pytest.approx(s4.alg_bytes / (sk["us_per_call"] * 1e-6) / 1e9, rel=1e-6)
+        assert sk["frac"] == pytest.approx(sk["achieved"] / 8000.0)
+        assert sk["timing"] == "hip_graph" and sk["rotated_buffers"] >= 5
+
+
+@pytest.mark.gpu
+def test_bench_vendor_reference_at_8192():
+    """The default 8192^3 run adds the interleaved vendor-BLAS reference:
+    per-call times of both sides over the same rounds."""
+    cmd = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1",
+           "--no-cpu-baseline"]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = json.loads([ln for ln in r.stdout.splitlines() if ln.strip()][-1])
+    vr = out["vendor_reference"]
+    assert vr["rounds"] >= 2 and vr["calls_per_round"] >= 10
+    for side in ("tlg", "vendor_matmul"):
+        assert 0 < vr[side]["best"] <= vr[side]["median"]
+    assert vr["tlg_vs_vendor_matmul_best"] == pytest.approx(vr["vendor_matmul"]["best"] / vr["tlg"]["best"])
+    assert "skinny" in out and "cpu_baseline" not in out
