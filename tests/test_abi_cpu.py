@@ -66,8 +66,13 @@ def test_check_args(args, expect):
 
 
 def test_plan_shapes_of_the_workloads():
-    assert tlg.plan(8192, 8192, 8192)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
-    assert tlg.plan(4096, 4096, 4096)["variant_name"] == "tiled_pipe"
+    # K a multiple of 64 and N of 8: the 16 x 16 x 32 MFMA tiles
+    assert tlg.plan(8192, 8192, 8192)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3"
+    assert tlg.plan(4096, 4096, 4096)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3"
+    # otherwise the eight-wave 32 x 32 x 16 tiles
+    assert tlg.plan(4096, 4096, 4104)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
+    assert tlg.plan(4096, 4100, 4096, aligned=True, ldb=4104, ldc=4104)["config_name"] == \
+        "pipe_256x256x64_w2x4_s2_a3_early"
     # odd sizes and leading dimensions: direct-to-LDS loads, staged K tail; the
     # tuned table gives this class the pipelined 128 x 256 tiles (216 of them)
     p = tlg.plan(3001, 2049, 1537)
@@ -94,7 +99,12 @@ def test_plan_shapes_of_the_workloads():
     assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 32 * 4
     p = tlg.plan(1, 4096, 4096)
     assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 64 * 4
-    assert tlg.plan(3072, 3072, 3072)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"  # 144 tiles of 256 x 256
+    assert tlg.plan(3072, 3072, 3072)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3"  # 144 tiles of 256 x 256
+    # forced 16 x 16 x 32 tiles need K a multiple of 64 and N of 8
+    with pytest.raises(tlg.TlgError):
+        tlg.plan(300, 264, 200, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10)
+    with pytest.raises(tlg.TlgError):
+        tlg.plan(300, 260, 256, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10, ldb=264, ldc=264)
     assert tlg.plan(256, 256, 256)["variant_name"] == "tiled_dma"
     assert tlg.plan(5, 7, 0)["variant_name"] == "fill_zero"
     assert tlg.plan(0, 7, 9)["variant_name"] == "noop"

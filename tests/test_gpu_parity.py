@@ -244,7 +244,7 @@ def test_large_square_cross_check_kernel(dev, name):
     assert_close(got, naive, f"{name} full output vs cross-check kernel")
 
 
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
 @pytest.mark.parametrize("shape", [(300, 264, 200), (513, 520, 72), (1024, 1032, 1000), (256, 256, 8),
                                    (257, 8, 4104), (301, 259, 203)])
 def test_pipe_configs(dev, config, shape):
@@ -558,3 +558,41 @@ def test_invalid_arguments_enqueue_nothing(dev):
     assert st == nat.TLG_ERROR_NOT_SUPPORTED
     torch.cuda.synchronize()
     assert torch.all(C == 7.0)
+
+
+@pytest.mark.parametrize("config", [10, 11, 12])
+@pytest.mark.parametrize("shape", [(300, 264, 192), (513, 520, 64), (1024, 1032, 1024), (256, 256, 64), (257, 8, 4096),
+                                   (200, 264, 128), (129, 1000, 320), (512, 768, 2048)])
+def test_pipe16_configs(dev, config, shape):
+    """The 16 x 16 x 32 MFMA tiles (K a multiple of 64, N of 8): ragged M and
+    N, one-stage K, long K, one-column-chunk N; integer inputs exact, C in a
+    NaN-filled padded buffer whose padding stays NaN; then uniform inputs
+    within the tolerance."""
+    M, N, K = shape
+    print(f"pipe16 {shape} config={config}", flush=True)
+    A, B = wl.make_random(M, N, K, seed=M ^ N ^ K, kind="integer_pos")
+    ref = oracle.gemm_relu(A, B)
+    big = torch.full((M + 2, N + 8), float("nan"), dtype=torch.float16, device=dev)
+    tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), out=big[:M, :N], variant=V_PIPE, config=config)
+    torch.cuda.synchronize()
+    allb = bits(big)
+    assert np.array_equal(allb[:M, :N], ref)
+    assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+    A, B = wl.make_random(M, N, K, seed=M + N + K, kind="uniform")
+    got = bits(tlg.gemm_relu(to_dev(A, dev), to_dev(B, dev), variant=V_PIPE, config=config))
+    assert_close(got, oracle.gemm_relu(A, B), f"pipe16 {shape} {config}")
+
+
+@pytest.mark.parametrize("config", [10, 11, 12])
+def test_pipe16_square4096_full(dev, config):
+    """The 16 x 16 x 32 tiles on the 4096^3 workload, the whole output against
+    the oracle: integer inputs exact, own inputs within the tolerance."""
+    w = wl.WORKLOADS["square4096"]
+    for integer in (True, False):
+        A, B = wl.make_inputs(w, integer=integer)
+        got = bits(run(A, B, dev, variant=V_PIPE, config=config))
+        ref = oracle.gemm_relu(A, B)
+        if integer:
+            assert np.array_equal(got, ref), config
+        else:
+            assert_close(got, ref, f"pipe16 4096 config {config}")

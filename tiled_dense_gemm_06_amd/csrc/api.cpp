@@ -295,12 +295,20 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
     // there are enough tiles to give most CUs one
     if (variant == TLG_VARIANT_TILED_PIPE || variant == TLG_VARIANT_AUTO) {
         if (!config_ok(config, tlg::PIPE_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
-        const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64_W8_A3_EARLY;
+        // the 16 x 16 x 32 MFMA tiles take K in whole 64-deep stages and
+        // whole 16-byte chunks of B's rows; they are the default where they
+        // can serve (8192^3 804 vs 834 us, 4096^3 109.2 vs 112.4 us for the
+        // eight-wave 32 x 32 x 16 tiles, interleaved on one MI355X: the
+        // smaller MFMA spends less energy per FLOP, which the power-limited
+        // clock turns into speed)
+        const bool k64 = p.K % 64 == 0 && p.N % 8 == 0;
+        const int cfg = config >= 0 ? config : k64 ? tlg::PIPE16_256x256x64_A3 : tlg::PIPE_256x256x64_W8_A3_EARLY;
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
+        const bool shape_ok = cfg < tlg::PIPE16_FIRST || k64;
         // 128 tiles of 256 x 256 (half the CUs) measured faster than the
         // 128 x 128 tiles already (3072^3: 72 vs 101 us)
-        if (dma_ok(p, tc.bm, tc.bn, tc.bk) && (variant == TLG_VARIANT_TILED_PIPE || tiles >= 128)) {
+        if (shape_ok && dma_ok(p, tc.bm, tc.bn, tc.bk) && (variant == TLG_VARIANT_TILED_PIPE || tiles >= 128)) {
             fill_info(o, TLG_VARIANT_TILED_PIPE, cfg, &tc, 1, 1, tiles, 0);
             return TLG_SUCCESS;
         }

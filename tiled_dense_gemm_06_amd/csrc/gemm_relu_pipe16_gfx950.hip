@@ -1,0 +1,381 @@
+// Software-pipelined gfx950 kernel for C = ReLU(A . B) on 16 x 16 x 32 MFMA
+// tiles: the quick-start kernel of the TileLang article
+// (aiwiki.ai/wiki/tilelang, "Programming model") with its T.Pipelined K loop
+// scheduled by hand.
+//
+// Why a second MFMA shape. These parts run matrix-heavy kernels at a
+// power-limited clock, so what a GEMM can sustain is set by the energy it
+// spends per FLOP. Measured on one MI355X with nothing but MFMAs on random
+// fp16 operands, two waves per SIMD, equal matrix-core occupancy (0.92):
+// v_mfma_f32_16x16x32_f16 held 1.93 GHz and 1.88 PFLOP/s where
+// v_mfma_f32_32x32x16_f16 held 1.67 GHz and 1.62 PFLOP/s. (Per FLOP the
+// 16 x 16 form moves about a fifth fewer operand and accumulator registers:
+// 16 + 16 against 8 + 32 per 32768 FLOP.)
+//
+// Layout and schedule. A 256 x 256 output tile per work-group of four waves,
+// one per SIMD, each wave 128 x 128 = 8 x 8 MFMA tiles with their 256 fp32
+// accumulators; 64-deep LDS stages fed by direct global->LDS loads (A
+// K-contiguous, B N-contiguous and read back transposed by
+// ds_read_b64_tr_b16), XOR-swizzled so every fragment read is free of bank
+// conflicts. One K step is a fixed sequence of 128 MFMA slots (two 32-deep
+// k-steps of 64 MFMAs); between MFMAs sit the LDS reads of the next k-step's
+// fragments and, every SPACING slots, one direct-to-LDS load of a later
+// stage, so a lone wave per SIMD never waits on an operand. K must be a
+// multiple of the stage depth (and N of 8): then every stage is wholly inside
+// K or wholly past it and whether a load reads memory is decided per stage
+// by the buffer descriptor's range, on the scalar unit. The C tile leaves
+// through LDS as whole 256-byte row segments.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gfx950_ops.h"
+#include "kernels.h"
+#include "tile_layout.h"
+
+namespace tlg {
+
+// Operand fragments of one 32-deep k-step: TM A fragments (one ds_read_b128
+// each) and TN B fragments (two transposing 8-byte reads each).
+template <class S>
+struct Frags16 {
+    half8_t a[S::TM];
+    short4_t blo[S::TN], bhi[S::TN];
+};
+
+// The fragment reads of one k-step, in the order the MFMAs use them (tile i
+// uses b[i / TM] and a[i % TM]): b[0] (two reads), a[0..TM-1], then
+// b[1..TN-1] (two reads each).
+template <class S>
+constexpr int kFragReads16 = S::TM + 2 * S::TN;
+
+// Per-lane parts of the fragment addresses (frag_a16_lane, frag_b16_lane):
+// A for each k-step parity, B for each fragment column; the rest of each
+// address is a constant in the read's offset field.
+template <class S>
+struct FragLanes16 {
+    uint32_t a[2];
+    uint32_t b[S::TN];
+};
+
+template <class S>
+__device__ __forceinline__ void frag_read16(Frags16<S> &f, LDS_PTR(const char) sA, LDS_PTR(const char) sB,
+                                            const FragLanes16<S> &o, int s, int r) {
+    if (r < 2) {
+        LDS_PTR(short4_t) p = (LDS_PTR(short4_t))(sB + o.b[0] + (32 * s + 4 * r) * S::RB);
+        if (r == 0)
+            f.blo[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+        else
+            f.bhi[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+    } else if (r < 2 + S::TM) {
+        const int tm = r - 2;
+        f.a[tm] = *(LDS_PTR(const half8_t))(sA + o.a[s & 1] + tm * 16 * S::RA);
+    } else {
+        const int tn = 1 + (r - 2 - S::TM) / 2, h = (r - 2 - S::TM) % 2;
+        LDS_PTR(short4_t) p = (LDS_PTR(short4_t))(sB + o.b[tn] + (32 * s + 4 * h) * S::RB);
+        if (h == 0)
+            f.blo[tn] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+        else
+            f.bhi[tn] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+    }
+}
+
+// The MFMA is written out so that each accumulator tuple stays in its own
+// four AGPRs and is accumulated in place: with 256 accumulators, 128
+// fragment registers and the addresses live at once, the compiler's own
+// register assignment for the builtin copies accumulators between AGPRs and
+// VGPRs around every MFMA. Register hazards the compiler cannot see here are
+// excluded by the schedule: a fragment register is rewritten, and an
+// accumulator used again, only 64 MFMA slots after its last use, and the
+// epilogue waits explicitly before it reads the accumulators
+// (mfma16_results_ready). The compiler still makes every MFMA wait for the
+// LDS reads of its operands.
+template <class S>
+__device__ __forceinline__ void mfma16_tile(const Frags16<S> &f, int i, float4_t (&acc)[S::TN][S::TM]) {
+    const int tn = i / S::TM, tm = i % S::TM;
+    const half8_t b =
+        __builtin_bit_cast(half8_t, __builtin_shufflevector(f.blo[tn], f.bhi[tn], 0, 1, 2, 3, 4, 5, 6, 7));
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc[tn][tm]) : "v"(b), "v"(f.a[tm]));
+}
+
+// Wait states between the last MFMAs and any other instruction reading
+// their results (more than the 18 a 16 x 16 x 32 f16 MFMA needs).
+__device__ __forceinline__ void mfma16_results_ready() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+#define TLG_SCHED_FENCE16() __builtin_amdgcn_sched_barrier(0)
+
+template <class S, int ASTAGES>
+constexpr int pipe16_lds_bytes() {
+    return ASTAGES * S::A_BYTES + S::STAGES * S::B_BYTES;  // A buffers first, then the B buffers
+}
+
+// Epilogue: ReLU and the fp16 conversion of each lane's four consecutive n of
+// one row, written as 8-byte pieces into this wave's WTM x WTN block of LDS
+// (epi16_offset), then read back as whole row segments for 16-byte stores
+// (rows >= M dropped by the buffer range check; a piece crossing column N is
+// stored element by element). The caller makes sure no wave still reads or
+// loads into the first WAVES * WTM * WTN * 2 bytes of LDS.
+template <class S>
+__device__ __forceinline__ void store_c_tile16_lds(const KArgs &a, int m0, int n0, int wave, int lane,
+                                                   const float4_t (&acc)[S::TN][S::TM], LDS_PTR(char) lds) {
+    constexpr int PIECES = S::WTN / 8;  // 16-byte pieces per row of the wave block
+    static_assert(PIECES == 16, "epilogue layout written for 128-column wave blocks");
+    LDS_PTR(char) q = lds + wave * S::WTM * S::WTN * 2;
+    const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm) {
+            const half4_t h = {relu_to_half(acc[tn][tm][0]), relu_to_half(acc[tn][tm][1]),
+                               relu_to_half(acc[tn][tm][2]), relu_to_half(acc[tn][tm][3])};
+            const int row = 16 * tm + lane % 16, col = 16 * tn + 4 * (lane / 16);
+            *(LDS_PTR(half4_t))(q + epi16_offset<S>(row, col / 8) + 2 * (col % 8)) = h;
+        }
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc(a.C + (int64_t)m0 * a.ldc + n0, (short)0, (int)kRange, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < S::WTM / (64 / PIECES); ++k) {
+        const int row = k * (64 / PIECES) + lane / PIECES, piece = lane % PIECES;
+        const int4_t v = *(LDS_PTR(const int4_t))(q + epi16_offset<S>(row, piece));
+        const int mr = wm0 + row, nr = wn0 + 8 * piece;
+        const bool row_in = m0 + mr < a.M;
+        if (n0 + nr + 8 <= a.N || !row_in) {
+            __builtin_amdgcn_raw_buffer_store_b128(v, rc, row_in ? (uint32_t)((mr * a.ldc + nr) * 2) : kOOB, 0, 0);
+        } else {
+            const half8_t hv = __builtin_bit_cast(half8_t, v);
+            _Float16 *crow = a.C + (int64_t)(m0 + mr) * a.ldc + n0 + nr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n0 + nr + e < a.N) crow[e] = hv[e];
+        }
+    }
+}
+
+// One K step is a fixed sequence of KSTEPS*T MFMA slots, T = TM*TN (64), H = T/2:
+//   slots 0..H-1      MFMAs H..T-1 of the previous stage's last k-step (f[1]);
+//                     after them (not EARLY) the reads of this stage's
+//                     k-step-0 fragments into f[0], one per slot;
+//   next T per ks     k-steps 0..KSTEPS-2: T MFMAs on f[ks & 1], with the
+//                     reads of k-step ks+1 into f[(ks+1) & 1], one per slot;
+//   last H slots      MFMAs 0..H-1 of the last k-step (f[1]).
+// The direct-to-LDS loads go after slots DOFF, DOFF+SPACING, ...: the tile of
+// stage kt+STAGES-1 of B and of stage kt+ASTAGES-1 of A, the operand loaded
+// fewer stages ahead first. Then this wave's loads of stage kt+1 are waited
+// for and the barrier publishes it (and retires stage kt). EARLY: the wait and
+// the barrier come before the last H slots (which read no LDS of stage kt),
+// and the reads of stage kt+1's k-step-0 fragments move into those slots.
+template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
+__device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_idx, LDS_PTR(char) lds) {
+    constexpr int T = S::TM * S::TN;
+    constexpr int H = T / 2;
+    static_assert(T % 2 == 0 && S::KSTEPS % 2 == 0, "the last k-step of a stage must use f[1]");
+    constexpr int READS = kFragReads16<S>;
+    static_assert(READS <= H, "fragment reads must fit under half the MFMAs of a k-step");
+    constexpr int LOADS = S::DMA_A + S::DMA_B;
+    constexpr int AHEAD = S::STAGES - 1;
+    constexpr int AHEAD_A = ASTAGES - 1;
+    static_assert(ASTAGES >= S::STAGES - 1 && ASTAGES <= S::STAGES + 1, "A and B differ by at most one buffer");
+    constexpr bool B_FIRST = ASTAGES > S::STAGES;
+    constexpr int WAIT = (AHEAD_A - 1) * S::DMA_A + (AHEAD - 1) * S::DMA_B;
+    constexpr int SLOTS = S::KSTEPS * T;
+    static_assert(AHEAD >= 1 && AHEAD_A >= 1 && WAIT < 64, "vmcnt range");
+    static_assert(DOFF + (LOADS - 1) * SPACING < SLOTS - H, "loads must be issued before the stage's wait");
+    constexpr int B_REGION = ASTAGES * S::A_BYTES;
+    static_assert(pipe16_lds_bytes<S, ASTAGES>() <= 160 * 1024, "LDS of one work-group");
+    static_assert(S::WAVES * S::WTM * S::WTN * 2 <= pipe16_lds_bytes<S, ASTAGES>(), "the C tile fits the LDS");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
+    const int m0 = tm_idx * S::BM, n0 = tn_idx * S::BN;
+    const int nk = a.K / S::BK;  // K is a multiple of BK
+
+    // Loads. A: load i of this wave covers LDS slab (wave*DMA_A + i), rows
+    // 8*slab .. +7 of the tile; its descriptor starts at the slab's first row
+    // and ends after row M - 1 (rows past M read zeros), and the lane's offset
+    // inside the slab depends only on the slab's parity (the swizzle of rows 16
+    // apart repeats). B: load i covers slab (wave*DMA_B + i), rows 2*slab and
+    // 2*slab + 1 of the stage; the slab's start is the instruction's scalar
+    // offset, and the lane's offset (kOOB for a column chunk past N) takes one
+    // of four forms, by the slab's swizzle pattern.
+    static_assert(S::ROWS_A_SLAB == 8 && S::ROWS_B_SLAB == 2 && S::CA == 8, "64-deep A rows, 256-column B rows");
+    uint32_t voff_a[2], voff_b[4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        voff_a[q] = (uint32_t)((lane / 8) * a.lda * 2 + 16 * ((lane % 8) ^ ((4 * q + lane / 16) % 8)));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int k = 2 * (q % 2) + 8 * (q / 2) + lane / 32;  // a row with the pattern's swizzle
+        const int chunk = (lane % 32) ^ swz_b16(k);
+        voff_b[q] = n0 + 8 * chunk < a.N ? (uint32_t)((lane / 32) * a.ldb * 2 + 16 * chunk) : kOOB;
+    }
+    uint32_t nrec_a[S::DMA_A];  // bytes of the slab's rows inside M
+#pragma unroll
+    for (int i = 0; i < S::DMA_A; ++i) {
+        const int64_t rows = (int64_t)a.M - m0 - (int64_t)(wave * S::DMA_A + i) * 8;
+        const int64_t bytes = rows <= 0 ? 0 : rows * a.lda * 2;
+        nrec_a[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(bytes > (int64_t)kRange ? (int64_t)kRange : bytes));
+    }
+    const _Float16 *a_tile = a.A + (int64_t)m0 * a.lda;
+    const _Float16 *b_tile = a.B + n0;
+    FragLanes16<S> fo;
+    fo.a[0] = (uint32_t)frag_a16_lane<S>(wm0, 0, lane);
+    fo.a[1] = (uint32_t)frag_a16_lane<S>(wm0, 1, lane);
+#pragma unroll
+    for (int tn = 0; tn < S::TN; ++tn) fo.b[tn] = (uint32_t)frag_b16_lane<S>(wn0, tn, lane);
+
+    // Load j of stage kt into buffer buf of its operand; past the end of K
+    // the descriptor's range is 0 bytes, so every lane writes zeros.
+    auto dma = [&](int j, int kt, int buf) {
+        const int k0 = kt * S::BK;
+        if (j < S::DMA_A) {
+            const int slab = wave * S::DMA_A + j;
+            int4_t r = make_srd(a_tile + (int64_t)slab * 8 * a.lda + k0);
+            r[2] = kt < nk ? (int)nrec_a[j] : 0;
+            dma16(r, (uint32_t)(uintptr_t)(lds + buf * S::A_BYTES + slab * 1024), voff_a[slab % 2]);
+        } else {
+            const int slab = wave * S::DMA_B + (j - S::DMA_A);
+            int4_t r = make_srd(b_tile + (int64_t)k0 * a.ldb);
+            if (kt >= nk) r[2] = 0;
+            dma16_soff(r, (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES + slab * 1024),
+                       voff_b[(slab % 2) + 2 * ((slab / 4) % 2)], (uint32_t)(slab * 2 * a.ldb * 2));
+        }
+    };
+
+    float4_t acc[S::TN][S::TM];
+#pragma unroll
+    for (int i = 0; i < S::TN; ++i)
+#pragma unroll
+        for (int j = 0; j < S::TM; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // f[1] starts at zero: the first step's first H slots add 0 * 0.
+    Frags16<S> f[2];
+#pragma unroll
+    for (int t = 0; t < S::TN; ++t) {
+        f[1].blo[t] = short4_t{0, 0, 0, 0};
+        f[1].bhi[t] = short4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int t = 0; t < S::TM; ++t) f[1].a[t] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+
+#pragma unroll
+    for (int s = 0; s < (AHEAD_A > AHEAD ? AHEAD_A : AHEAD); ++s) {
+        if (B_FIRST && s < AHEAD)
+#pragma unroll
+            for (int j = S::DMA_A; j < LOADS; ++j) dma(j, s, s);
+        if (s < AHEAD_A)
+#pragma unroll
+            for (int j = 0; j < S::DMA_A; ++j) dma(j, s, s);
+        if (!B_FIRST && s < AHEAD)
+#pragma unroll
+            for (int j = S::DMA_A; j < LOADS; ++j) dma(j, s, s);
+    }
+    wait_vmcnt<WAIT>();
+    barrier_lds();
+    if (EARLY) {
+#pragma unroll
+        for (int r = 0; r < READS; ++r) frag_read16<S>(f[0], lds, lds + B_REGION, fo, 0, r);
+    }
+
+    int bbuf = 0, abuf = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int nbbuf = bbuf == 0 ? S::STAGES - 1 : bbuf - 1;
+        const int nabuf = abuf == 0 ? ASTAGES - 1 : abuf - 1;
+        LDS_PTR(const char) sA = lds + abuf * S::A_BYTES;
+        LDS_PTR(const char) sB = lds + B_REGION + bbuf * S::B_BYTES;
+        LDS_PTR(const char) sA1 = lds + (abuf == ASTAGES - 1 ? 0 : abuf + 1) * S::A_BYTES;
+        LDS_PTR(const char) sB1 = lds + B_REGION + (bbuf == S::STAGES - 1 ? 0 : bbuf + 1) * S::B_BYTES;
+        TLG_SCHED_FENCE16();
+#pragma unroll
+        for (int q = 0; q < SLOTS; ++q) {
+            if (q < H) {
+                mfma16_tile<S>(f[1], H + q, acc);
+                if (!EARLY && q < READS) frag_read16<S>(f[0], sA, sB, fo, 0, q);
+            } else if (q < H + (S::KSTEPS - 1) * T) {
+                const int ks = (q - H) / T, i = (q - H) % T;
+                mfma16_tile<S>(f[ks & 1], i, acc);
+                if (i < READS) frag_read16<S>(f[(ks + 1) & 1], sA, sB, fo, ks + 1, i);
+            } else {
+                const int u = q - H - (S::KSTEPS - 1) * T;
+                if (EARLY && u == 0) {
+                    wait_vmcnt<WAIT>();  // this wave's loads of stage kt+1 are in LDS
+                    barrier_lds();       // ... and every wave's; no wave reads stage kt any more
+                }
+                mfma16_tile<S>(f[1], u, acc);
+                if (EARLY && u < READS) frag_read16<S>(f[0], sA1, sB1, fo, 0, u);
+            }
+            if (q >= DOFF && (q - DOFF) % SPACING == 0 && (q - DOFF) / SPACING < LOADS) {
+                const int n = (q - DOFF) / SPACING;
+                const int j = !B_FIRST ? n : n < S::DMA_B ? S::DMA_A + n : n - S::DMA_B;
+                if (j < S::DMA_A)
+                    dma(j, kt + AHEAD_A, nabuf);
+                else
+                    dma(j, kt + AHEAD, nbbuf);
+            }
+            TLG_SCHED_FENCE16();
+        }
+        if (!EARLY) {
+            wait_vmcnt<WAIT>();
+            barrier_lds();
+        }
+        bbuf = bbuf == S::STAGES - 1 ? 0 : bbuf + 1;
+        abuf = abuf == ASTAGES - 1 ? 0 : abuf + 1;
+    }
+#pragma unroll
+    for (int i = H; i < T; ++i) mfma16_tile<S>(f[1], i, acc);
+    mfma16_results_ready();
+    wait_vmcnt<0>();  // no load may still be writing LDS when the work-group ends
+    barrier_lds();    // every wave is done with the stages
+    store_c_tile16_lds<S>(a, m0, n0, wave, lane, acc, lds);
+}
+
+template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
+__global__ __launch_bounds__(S::NT) void k_tiled_pipe16(const KArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[pipe16_lds_bytes<S, ASTAGES>()];
+    int tm_idx, tn_idx;
+    grouped_tile(xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
+    pipe16_tile<S, SPACING, DOFF, ASTAGES, EARLY>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
+}
+
+using Pipe16w4 = TileShape16<256, 256, 64, 2, 2, 2>;    // four waves of 128 x 128, two B buffers
+using Pipe16w4B3 = TileShape16<256, 256, 64, 2, 2, 3>;  // three B buffers
+
+template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
+static hipError_t launch_pipe16_t(const Problem &p, hipStream_t stream) {
+    if (p.K % S::BK || p.N % 8 || p.trans_b) return hipErrorInvalidValue;
+    KArgs a;
+    a.A = (const _Float16 *)p.A;
+    a.B = (const _Float16 *)p.B;
+    a.C = (_Float16 *)p.C;
+    a.W = nullptr;
+    a.cnt = nullptr;
+    a.M = (int)p.M;
+    a.N = (int)p.N;
+    a.K = (int)p.K;
+    a.lda = p.lda;
+    a.ldb = p.ldb;
+    a.ldc = p.ldc;
+    a.group_m = 4;
+    a.k_split = (int)p.K;
+    a.kmain = (int)p.K;
+    a.tiles_m = (a.M + S::BM - 1) / S::BM;
+    a.tiles_n = (a.N + S::BN - 1) / S::BN;
+    hipLaunchKernelGGL((k_tiled_pipe16<S, SPACING, DOFF, ASTAGES, EARLY>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
+                       dim3(S::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_tiled_pipe16(int config, const Problem &p, hipStream_t stream) {
+    switch (config) {
+        // 16 loads per wave and stage, every four slots from slot 1 (the
+        // 128-slot step leaves its last 64 slots free of loads)
+        case PIPE16_256x256x64_A3: return launch_pipe16_t<Pipe16w4, 4, 1, 3, false>(p, stream);
+        case PIPE16_256x256x64_A3_EARLY: return launch_pipe16_t<Pipe16w4, 4, 1, 3, true>(p, stream);
+        case PIPE16_256x256x64_B3: return launch_pipe16_t<Pipe16w4B3, 4, 1, 2, false>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace tlg

@@ -116,7 +116,13 @@ constexpr int pipe_lds_bytes() {
 }
 
 // One output tile (tm_idx, tn_idx) of problem a, with the work-group's LDS.
-template <class S, int SPACING, int DOFF, int ASTAGES, bool BT, bool EARLY>
+// FULLK (kmain a multiple of BK): every stage is either wholly inside K or
+// wholly past it, so whether a load reads memory is decided per stage, on
+// the scalar unit, by the buffer descriptor's range (0 bytes past the end of
+// K); each lane's offset is fixed for the whole loop. This keeps the chain of
+// vector compares and selects out of the slot program, where with one wave
+// per SIMD it would hold up the next MFMA's issue.
+template <class S, int SPACING, int DOFF, int ASTAGES, bool BT, bool EARLY, bool FULLK>
 __device__ __forceinline__ void pipe_tile(const KArgs &a, int tm_idx, int tn_idx, LDS_PTR(char) lds) {
     constexpr int T = S::TM * S::TN;  // MFMA tiles of a wave (MFMAs per k-step)
     constexpr int H = T / 2;
@@ -127,12 +133,15 @@ __device__ __forceinline__ void pipe_tile(const KArgs &a, int tm_idx, int tn_idx
     constexpr int LOADS = S::DMA_A + S::DMA_B;  // direct-to-LDS loads per wave per stage
     constexpr int AHEAD = S::STAGES - 1;        // B stages in flight beyond the one being multiplied
     constexpr int AHEAD_A = ASTAGES - 1;        // A stages likewise
-    static_assert(ASTAGES == S::STAGES || ASTAGES == S::STAGES + 1, "A has at most one buffer more than B");
+    static_assert(ASTAGES >= S::STAGES - 1 && ASTAGES <= S::STAGES + 1, "A and B differ by at most one buffer");
+    // Within a step the loads of the operand loaded fewer stages ahead go
+    // first, so the loads still allowed in flight at the step's wait are
+    // exactly the latest ones (the WAIT count below).
     constexpr bool B_FIRST = ASTAGES > S::STAGES;  // B loads of a step before its A loads
     // loads issued after the last one of the next stage: those of later stages
     constexpr int WAIT = (AHEAD_A - 1) * S::DMA_A + (AHEAD - 1) * S::DMA_B;
     constexpr int SLOTS = S::KSTEPS * T;
-    static_assert(AHEAD >= 1 && WAIT < 64, "vmcnt range");
+    static_assert(AHEAD >= 1 && AHEAD_A >= 1 && WAIT < 64, "vmcnt range");
     static_assert(DOFF + (LOADS - 1) * SPACING < SLOTS, "loads must fit in one K step");
     constexpr int B_REGION = ASTAGES * S::A_BYTES;  // A buffers first, then the B buffers
     static_assert(pipe_lds_bytes<S, ASTAGES>() <= 160 * 1024, "LDS of one work-group");
@@ -167,11 +176,25 @@ __device__ __forceinline__ void pipe_tile(const KArgs &a, int tm_idx, int tn_idx
 
     const _Float16 *a_tile = a.A + (int64_t)m0 * a.lda;
     const _Float16 *b_tile = BT ? a.B + (int64_t)n0 * a.ldb : a.B + n0;
+    uint32_t voff[LOADS];  // (FULLK) the offset, or kOOB for a row or column outside M or N
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) voff[i] = ok[i] ? off[i] : kOOB;
 
     // Load j of stage kt into LDS buffer buf of its operand (stages past K
     // load zeros); j < DMA_A loads A, the others B.
     auto dma = [&](int j, int kt, int buf) {
         const int k0 = kt * S::BK;
+        if (FULLK) {
+            int4_t r = j < S::DMA_A ? make_srd(a_tile + k0)
+                                    : make_srd(BT ? b_tile + k0 : b_tile + (int64_t)k0 * a.ldb);
+            if (kt >= nk) r[2] = 0;  // past the end of K: every lane out of range, zeros
+            const uint32_t l =
+                j < S::DMA_A ? (uint32_t)(uintptr_t)(lds + buf * S::A_BYTES + (wave * S::DMA_A + j) * 1024)
+                             : (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES +
+                                                     (wave * S::DMA_B + (j - S::DMA_A)) * 1024);
+            dma16(r, l, voff[j]);
+            return;
+        }
         const bool in = ok[j] && k0 + kin[j] < a.kmain;
         if (j < S::DMA_A) {
             const int4_t r = make_srd(a_tile + k0);
@@ -204,9 +227,10 @@ __device__ __forceinline__ void pipe_tile(const KArgs &a, int tm_idx, int tn_idx
     for (int t = 0; t < S::TM; ++t) f[1].a[t] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
 
 #pragma unroll
-    for (int s = 0; s < AHEAD_A; ++s) {
+    for (int s = 0; s < (AHEAD_A > AHEAD ? AHEAD_A : AHEAD); ++s) {
+        if (s < AHEAD_A)
 #pragma unroll
-        for (int j = 0; j < S::DMA_A; ++j) dma(j, s, s);
+            for (int j = 0; j < S::DMA_A; ++j) dma(j, s, s);
         if (s < AHEAD)
 #pragma unroll
             for (int j = S::DMA_A; j < LOADS; ++j) dma(j, s, s);
@@ -290,18 +314,18 @@ __device__ __forceinline__ void pipe_tile(const KArgs &a, int tm_idx, int tn_idx
     store_c_tile_lds<S>(a, m0, n0, wave, lane, acc, lds);
 }
 
-template <class S, int SPACING, int DOFF, int ASTAGES, bool BT, bool EARLY = false>
+template <class S, int SPACING, int DOFF, int ASTAGES, bool BT, bool EARLY, bool FULLK>
 __global__ __launch_bounds__(S::NT) void k_tiled_pipe(const KArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[pipe_lds_bytes<S, ASTAGES>()];
     int tm_idx, tn_idx;
     grouped_tile(xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
-    pipe_tile<S, SPACING, DOFF, ASTAGES, BT, EARLY>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
+    pipe_tile<S, SPACING, DOFF, ASTAGES, BT, EARLY, FULLK>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
 }
 
 // Grouped problems in one launch: after the XCD renumbering, work-group ids
 // tile_start[p] .. tile_start[p+1]-1 take problem p's tiles in its grouped
 // order (the table travels as the kernel argument).
-template <class S, int SPACING, int DOFF, int ASTAGES, bool BT, bool EARLY>
+template <class S, int SPACING, int DOFF, int ASTAGES, bool BT, bool EARLY, bool FULLK>
 __global__ __launch_bounds__(S::NT) void k_tiled_pipe_grouped(const GroupArgs g) {
     __shared__ __attribute__((aligned(1024))) char smem[pipe_lds_bytes<S, ASTAGES>()];
     const int v = xcd_remap(blockIdx.x, g.tile_start[g.count]);
@@ -310,12 +334,16 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe_grouped(const GroupArgs g)
     const KArgs &a = g.p[p];
     int tm_idx, tn_idx;
     grouped_tile(v - g.tile_start[p], a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
-    pipe_tile<S, SPACING, DOFF, ASTAGES, BT, EARLY>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
+    pipe_tile<S, SPACING, DOFF, ASTAGES, BT, EARLY, FULLK>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
 }
 
 using Pipe256x32 = TileShape<256, 256, 32, 2, 2, 4>;
 using Pipe256x64 = TileShape<256, 256, 64, 2, 2, 2>;
 using Pipe256x64w8 = TileShape<256, 256, 64, 2, 4, 2>;  // eight waves, two per SIMD
+// three B buffers beside two A buffers (B, whose lines are shared by fewer
+// work-groups of an XCD, is loaded two steps ahead)
+using Pipe256x64B3 = TileShape<256, 256, 64, 2, 2, 3>;
+using Pipe256x64w8B3 = TileShape<256, 256, 64, 2, 4, 3>;
 // half tiles (four waves of 128 x 64, three stages): twice the tiles of
 // 256 x 256 for problems that leave CUs idle at that size
 using Pipe256x128 = TileShape<256, 128, 64, 2, 2, 3>;
@@ -335,6 +363,14 @@ const TileConfig kPipeConfigs[PIPE_CONFIGS] = {
      "pipe_128x256x64_w1x4_s3"},
     {Pipe256x64w8::BM, Pipe256x64w8::BN, Pipe256x64w8::BK, Pipe256x64w8::NT, Pipe256x64w8::STAGES,
      "pipe_256x256x64_w2x4_s2_a3_early"},
+    {Pipe256x64w8B3::BM, Pipe256x64w8B3::BN, Pipe256x64w8B3::BK, Pipe256x64w8B3::NT, Pipe256x64w8B3::STAGES,
+     "pipe_256x256x64_w2x4_s3_a2_early"},
+    {Pipe256x64B3::BM, Pipe256x64B3::BN, Pipe256x64B3::BK, Pipe256x64B3::NT, Pipe256x64B3::STAGES,
+     "pipe_256x256x64_w2x2_s3_a2"},
+    // 16 x 16 x 32 MFMA tiles, four waves (gemm_relu_pipe16_gfx950.hip)
+    {256, 256, 64, 256, 2, "pipe16_256x256x64_w2x2_s2_a3"},
+    {256, 256, 64, 256, 2, "pipe16_256x256x64_w2x2_s2_a3_early"},
+    {256, 256, 64, 256, 3, "pipe16_256x256x64_w2x2_s3_a2"},
 };
 
 template <class S, bool BT>
@@ -364,8 +400,12 @@ static KArgs pipe_args(const Problem &p) {
 template <class S, int SPACING, int DOFF, int ASTAGES, bool BT = false, bool EARLY = false>
 static hipError_t launch_pipe_t(const Problem &p, hipStream_t stream) {
     const KArgs a = pipe_args<S, BT>(p);
-    hipLaunchKernelGGL((k_tiled_pipe<S, SPACING, DOFF, ASTAGES, BT, EARLY>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
-                       dim3(S::NT), 0, stream, a);
+    const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+    if (a.kmain % S::BK == 0)
+        hipLaunchKernelGGL((k_tiled_pipe<S, SPACING, DOFF, ASTAGES, BT, EARLY, true>), grid, dim3(S::NT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_tiled_pipe<S, SPACING, DOFF, ASTAGES, BT, EARLY, false>), grid, dim3(S::NT), 0, stream,
+                           a);
     return hipGetLastError();
 }
 
@@ -380,8 +420,13 @@ static hipError_t launch_pipe_grouped_t(const Problem *ps, int count, hipStream_
         g.tile_start[i + 1] = g.tile_start[i] + g.p[i].tiles_m * g.p[i].tiles_n;
     }
     if (g.tile_start[count] == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_tiled_pipe_grouped<S, 2, 1, 3, BT, true>), dim3((unsigned)g.tile_start[count]),
-                       dim3(S::NT), 0, stream, g);
+    bool fullk = true;
+    for (int i = 0; i < count; ++i) fullk = fullk && g.p[i].kmain % S::BK == 0;
+    const dim3 grid((unsigned)g.tile_start[count]);
+    if (fullk)
+        hipLaunchKernelGGL((k_tiled_pipe_grouped<S, 2, 1, 3, BT, true, true>), grid, dim3(S::NT), 0, stream, g);
+    else
+        hipLaunchKernelGGL((k_tiled_pipe_grouped<S, 2, 1, 3, BT, true, false>), grid, dim3(S::NT), 0, stream, g);
     return hipGetLastError();
 }
 
@@ -397,6 +442,7 @@ hipError_t launch_tiled_pipe_grouped(const Problem *ps, int count, hipStream_t s
 }
 
 hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream) {
+    if (config >= PIPE16_FIRST) return launch_tiled_pipe16(config, p, stream);
     if (p.trans_b) {
         switch (config) {
             case PIPE_256x256x64_A3: return launch_pipe_t<Pipe256x64, 2, 1, 3, true>(p, stream);
@@ -420,6 +466,9 @@ hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream) {
         case PIPE_128x256x64: return launch_pipe_t<Pipe128x256, 2, 1, 3>(p, stream);
         // eight waves, the stage barrier before the last half k-step (the default)
         case PIPE_256x256x64_W8_A3_EARLY: return launch_pipe_t<Pipe256x64w8, 2, 1, 3, false, true>(p, stream);
+        // two A buffers and three B buffers
+        case PIPE_256x256x64_W8_B3_EARLY: return launch_pipe_t<Pipe256x64w8B3, 2, 1, 2, false, true>(p, stream);
+        case PIPE_256x256x64_B3: return launch_pipe_t<Pipe256x64B3, 2, 1, 2>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

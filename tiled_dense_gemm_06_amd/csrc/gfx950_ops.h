@@ -80,6 +80,17 @@ __device__ __forceinline__ void dma16(int4_t srd, uint32_t lds_base, uint32_t vo
         : "memory", "m0");
 }
 
+// The same with a scalar offset added to every lane's (the instruction's
+// soffset operand).
+__device__ __forceinline__ void dma16_soff(int4_t srd, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_base),
+        "v"(voff), "s"(srd), "s"(soff)
+        : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");

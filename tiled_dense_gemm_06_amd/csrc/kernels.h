@@ -66,7 +66,15 @@ enum PipeConfig {
     PIPE_256x128x64 = 5,  // four waves of 128 x 64, three stages
     PIPE_128x256x64 = 6,
     PIPE_256x256x64_W8_A3_EARLY = 7,  // stage barrier before the last half k-step (the default)
-    PIPE_CONFIGS = 8
+    PIPE_256x256x64_W8_B3_EARLY = 8,  // two A buffers, three B buffers
+    PIPE_256x256x64_B3 = 9,           // four waves, two A buffers, three B buffers
+    // v_mfma_f32_16x16x32_f16 tiles (K a multiple of 64, N of 8, B not
+    // transposed): four waves of 128 x 128
+    PIPE16_FIRST = 10,
+    PIPE16_256x256x64_A3 = 10,
+    PIPE16_256x256x64_A3_EARLY = 11,
+    PIPE16_256x256x64_B3 = 12,
+    PIPE_CONFIGS = 13
 };
 
 // wave-role (ping-pong) schedule: two groups of waves alternate between
@@ -86,6 +94,9 @@ hipError_t launch_tiled_dma(int config, const Problem &p, hipStream_t stream);
 hipError_t launch_tiled_dma_grouped(int config, const Problem *ps, int count, hipStream_t stream);
 hipError_t launch_tiled_general(int config, const Problem &p, hipStream_t stream);
 hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream);
+// the 16 x 16 x 32 MFMA configurations (PIPE16_FIRST and up); K a multiple
+// of 64, N of 8, B not transposed (hipErrorInvalidValue otherwise)
+hipError_t launch_tiled_pipe16(int config, const Problem &p, hipStream_t stream);
 // count (1 .. kGroupMax) problems, all with the same trans_b, in one launch
 // of the eight-wave early-barrier pipelined kernel (each must pass its checks)
 hipError_t launch_tiled_pipe_grouped(const Problem *ps, int count, hipStream_t stream);

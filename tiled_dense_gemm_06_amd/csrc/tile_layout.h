@@ -182,6 +182,88 @@ TLG_HD int epi_read_row(int k, int lane) { return k * (64 / (S::WTN / 8)) + lane
 template <class S>
 TLG_HD int epi_read_piece(int lane) { return lane % (S::WTN / 8); }
 
+// ---- tiles of v_mfma_f32_16x16x32_f16 ----
+// Facts relied on (same conventions as for the 32 x 32 instruction above):
+// lane l holds, for its first operand, row (l % 16) and k = 8*(l/16) + e
+// (e = 0..7); for its second operand, column (l % 16) and the same k; result
+// element r of lane l is row 4*(l/16) + r, column (l % 16).
+// The kernels again compute D = B^T A^T: the first operand comes from the B
+// tile (output columns n), the second from the A tile (output rows m), so
+// each lane's four result registers are four consecutive n of one row m.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+struct TileShape16 : TileShape<BM_, BN_, BK_, WM_, WN_, STAGES_> {
+    using Base = TileShape<BM_, BN_, BK_, WM_, WN_, STAGES_>;
+    static constexpr int TM = Base::WTM / 16, TN = Base::WTN / 16;  // MFMA tiles per wave
+    static constexpr int KSTEPS = BK_ / 32;                          // 32-deep k-steps per stage
+    static_assert(BK_ % 32 == 0, "BK must be a multiple of the MFMA k (32)");
+    static_assert(Base::CB == 32, "the B swizzle below is written for 256-column B tiles");
+};
+// B tile swizzle for the 16 x 16 fragments: chunk c of row k at position
+// c ^ swz_b16(k). A transposing read by 32 lanes covers rows 8g + 4h + q
+// (g = 0, 1; q = 0..3) and two adjacent chunks; (q, g) select 8 distinct even
+// offsets 4q ^ 2g, so the 32 lanes land in 16 distinct slots of a 256-byte
+// window. Direct-to-LDS writes are linear, so any XOR swizzle suits them.
+TLG_HD constexpr int swz_b16(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)); }
+template <class S>
+TLG_HD int lds_b16_offset(int k, int c) { return k * S::RB + 16 * (c ^ swz_b16(k)); }
+template <class S>
+TLG_HD ChunkRef dma_b16_chunk(int wave, int i, int lane) {
+    int slab = wave * S::DMA_B + i;
+    int row = slab * S::ROWS_B_SLAB + lane / S::CB;
+    int pos = lane % S::CB;
+    return ChunkRef{row, pos ^ swz_b16(row)};
+}
+// Second operand (A tile), MFMA tile tm, 32-deep k-step s: lane l reads 16
+// bytes = A[wm0 + 16*tm + l%16][32*s + 8*(l/16) .. +7].
+template <class S>
+TLG_HD int frag_a16_offset(int wm0, int tm, int s, int lane) {
+    return lds_a_offset<S>(wm0 + 16 * tm + lane % 16, 4 * s + lane / 16);
+}
+// First operand (B tile), MFMA tile tn, k-step s, half h: the 8-byte address
+// lane l supplies to ds_read_b64_tr_b16. After the read, lane l holds
+// B[32*s + 8*(l/16) + 4*h + j][wn0 + 16*tn + l%16] for j = 0..3.
+template <class S>
+TLG_HD int frag_b16_offset(int wn0, int tn, int s, int h, int lane) {
+    int g = lane / 16, i = lane % 16;
+    int k = 32 * s + 8 * g + 4 * h + i / 4;
+    int n = wn0 + 16 * tn + 4 * (i % 4);
+    return lds_b16_offset<S>(k, n / 8) + 2 * (n % 8);
+}
+// The same offsets split into a per-lane part and a constant (for 64-deep
+// A rows and 256-column B rows, wm0 and wn0 multiples of 128): the A swizzle
+// of rows 16 apart is the same, so frag_a16_offset(wm0, tm, s, lane) =
+// frag_a16_lane(wm0, s, lane) + tm * 16 * RA; the B swizzle depends on the
+// lane alone, so frag_b16_offset(wn0, tn, s, h, lane) =
+// frag_b16_lane(wn0, tn, lane) + (32*s + 4*h) * RB. A kernel keeps the lane
+// parts in registers and the constants go into the LDS instructions' offset
+// field.
+template <class S>
+TLG_HD int frag_a16_lane(int wm0, int s, int lane) {
+    static_assert(S::CA == 8, "64-deep A rows");
+    const int g = lane / 16, w = (lane % 16) / 2;
+    return (wm0 + lane % 16) * S::RA + 16 * ((g ^ w) & 3) + 64 * (s ^ (w >> 2));
+}
+template <class S>
+TLG_HD int frag_b16_lane(int wn0, int tn, int lane) {
+    static_assert(S::CB == 32, "256-column B rows");
+    const int g = lane / 16, i = lane % 16;
+    const int z = (4 * (i / 4)) ^ (2 * (g & 1));
+    return (8 * g + i / 4) * S::RB + 16 * (wn0 / 8 + (i % 4) / 2) + 8 * (i % 2) + 16 * ((2 * tn) ^ z);
+}
+// Result register r of MFMA tile (tn, tm) in lane l is C[m][n] with
+// m = wm0 + 16*tm + l%16 and n = wn0 + 16*tn + 4*(l/16) + r.
+TLG_HD int acc16_m(int wm0, int tm, int lane) { return wm0 + 16 * tm + lane % 16; }
+TLG_HD int acc16_n(int wn0, int tn, int r, int lane) { return wn0 + 16 * tn + 4 * (lane / 16) + r; }
+// Epilogue block of a wave (WTM x WTN fp16, rows of 2*WTN bytes, 16 pieces
+// of 16 bytes per row for WTN = 128): piece c of row r at position
+// c ^ (r % 16). The 8-byte result pieces of 16 rows written by one
+// instruction and the 16-byte pieces of 4 whole rows read back by one
+// instruction are both spread over distinct banks.
+template <class S>
+TLG_HD int epi16_offset(int row, int piece) {
+    return row * S::WTN * 2 + 16 * (piece ^ (row % 16));
+}
+
 // ---- tile order ----
 // Work-groups are handed to the 8 XCDs of the device round-robin by id, so
 // id p runs on XCD p % 8. Renumber so that each XCD receives a contiguous

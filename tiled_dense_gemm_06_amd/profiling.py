@@ -43,6 +43,7 @@ COPY_KERNEL = "copyBuffer"
 # the file each kernel's device code lives in (besides the device headers)
 KERNEL_FILES = {
     "k_tiled_pipe": "gemm_relu_pipe_gfx950.hip",
+    "k_tiled_pipe16": "gemm_relu_pipe16_gfx950.hip",
     "k_tiled_dma": "gemm_relu_gfx950.hip",
     "k_tiled_general": "gemm_relu_gfx950.hip",
     "k_skinny_strip": "gemm_relu_skinny_gfx950.hip",
