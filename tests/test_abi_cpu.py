@@ -67,8 +67,8 @@ def test_check_args(args, expect):
 
 def test_plan_shapes_of_the_workloads():
     # K a multiple of 64 and N of 8: the 16 x 16 x 32 MFMA tiles
-    assert tlg.plan(8192, 8192, 8192)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3"
-    assert tlg.plan(4096, 4096, 4096)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3"
+    assert tlg.plan(8192, 8192, 8192)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
+    assert tlg.plan(4096, 4096, 4096)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
     # otherwise the eight-wave 32 x 32 x 16 tiles
     assert tlg.plan(4096, 4096, 4104)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
     assert tlg.plan(4096, 4100, 4096, aligned=True, ldb=4104, ldc=4104)["config_name"] == \
@@ -99,7 +99,7 @@ def test_plan_shapes_of_the_workloads():
     assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 32 * 4
     p = tlg.plan(1, 4096, 4096)
     assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 64 * 4
-    assert tlg.plan(3072, 3072, 3072)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3"  # 144 tiles of 256 x 256
+    assert tlg.plan(3072, 3072, 3072)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"  # 144 tiles of 256 x 256
     # forced 16 x 16 x 32 tiles need K a multiple of 64 and N of 8
     with pytest.raises(tlg.TlgError):
         tlg.plan(300, 264, 200, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10)

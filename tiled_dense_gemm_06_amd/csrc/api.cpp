@@ -300,9 +300,12 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
         // can serve (8192^3 804 vs 834 us, 4096^3 109.2 vs 112.4 us for the
         // eight-wave 32 x 32 x 16 tiles, interleaved on one MI355X: the
         // smaller MFMA spends less energy per FLOP, which the power-limited
-        // clock turns into speed)
+        // clock turns into speed), with their loads every eight MFMA slots
+        // (medians over ten interleaved rounds against every four: 8192^3
+        // 805 vs 819 us, 4096^3 108.6 vs 111.5, 3072^3 68.9 vs 75.4,
+        // 8192x8192x4096 418.7 vs 432.5)
         const bool k64 = p.K % 64 == 0 && p.N % 8 == 0;
-        const int cfg = config >= 0 ? config : k64 ? tlg::PIPE16_256x256x64_A3 : tlg::PIPE_256x256x64_W8_A3_EARLY;
+        const int cfg = config >= 0 ? config : k64 ? tlg::PIPE16_256x256x64_A3_SP8 : tlg::PIPE_256x256x64_W8_A3_EARLY;
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
         const bool shape_ok = cfg < tlg::PIPE16_FIRST || k64;

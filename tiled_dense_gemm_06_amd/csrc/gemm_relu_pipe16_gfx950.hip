@@ -180,7 +180,7 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
     constexpr int WAIT = (AHEAD_A - 1) * S::DMA_A + (AHEAD - 1) * S::DMA_B;
     constexpr int SLOTS = S::KSTEPS * T;
     static_assert(AHEAD >= 1 && AHEAD_A >= 1 && WAIT < 64, "vmcnt range");
-    static_assert(DOFF + (LOADS - 1) * SPACING < SLOTS - H, "loads must be issued before the stage's wait");
+    static_assert(DOFF + (LOADS - 1) * SPACING < (EARLY ? SLOTS - H : SLOTS), "loads must be issued before the stage's wait");
     constexpr int B_REGION = ASTAGES * S::A_BYTES;
     static_assert(pipe16_lds_bytes<S, ASTAGES>() <= 160 * 1024, "LDS of one work-group");
     static_assert(S::WAVES * S::WTM * S::WTN * 2 <= pipe16_lds_bytes<S, ASTAGES>(), "the C tile fits the LDS");
@@ -374,6 +374,15 @@ hipError_t launch_tiled_pipe16(int config, const Problem &p, hipStream_t stream)
         case PIPE16_256x256x64_A3: return launch_pipe16_t<Pipe16w4, 4, 1, 3, false>(p, stream);
         case PIPE16_256x256x64_A3_EARLY: return launch_pipe16_t<Pipe16w4, 4, 1, 3, true>(p, stream);
         case PIPE16_256x256x64_B3: return launch_pipe16_t<Pipe16w4B3, 4, 1, 2, false>(p, stream);
+        // the same loads every two or every six slots
+        case PIPE16_256x256x64_A3_SP2: return launch_pipe16_t<Pipe16w4, 2, 1, 3, false>(p, stream);
+        case PIPE16_256x256x64_A3_SP6: return launch_pipe16_t<Pipe16w4, 6, 1, 3, false>(p, stream);
+        case PIPE16_256x256x64_A3_EARLY_SP2: return launch_pipe16_t<Pipe16w4, 2, 1, 3, true>(p, stream);
+        case PIPE16_256x256x64_A3_SP7: return launch_pipe16_t<Pipe16w4, 7, 1, 3, false>(p, stream);
+        case PIPE16_256x256x64_A3_SP8: return launch_pipe16_t<Pipe16w4, 8, 1, 3, false>(p, stream);
+        case PIPE16_256x256x64_A3_SP6_D5: return launch_pipe16_t<Pipe16w4, 6, 5, 3, false>(p, stream);
+        case PIPE16_256x256x64_B3_SP6: return launch_pipe16_t<Pipe16w4B3, 6, 1, 2, false>(p, stream);
+        case PIPE16_256x256x64_A3_EARLY_SP6: return launch_pipe16_t<Pipe16w4, 6, 1, 3, true>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -371,6 +371,14 @@ const TileConfig kPipeConfigs[PIPE_CONFIGS] = {
     {256, 256, 64, 256, 2, "pipe16_256x256x64_w2x2_s2_a3"},
     {256, 256, 64, 256, 2, "pipe16_256x256x64_w2x2_s2_a3_early"},
     {256, 256, 64, 256, 3, "pipe16_256x256x64_w2x2_s3_a2"},
+    {256, 256, 64, 256, 2, "pipe16_256x256x64_w2x2_s2_a3_sp2"},
+    {256, 256, 64, 256, 2, "pipe16_256x256x64_w2x2_s2_a3_sp6"},
+    {256, 256, 64, 256, 2, "pipe16_256x256x64_w2x2_s2_a3_early_sp2"},
+    {256, 256, 64, 256, 2, "pipe16_256x256x64_w2x2_s2_a3_sp7"},
+    {256, 256, 64, 256, 2, "pipe16_256x256x64_w2x2_s2_a3_sp8"},
+    {256, 256, 64, 256, 2, "pipe16_256x256x64_w2x2_s2_a3_sp6_d5"},
+    {256, 256, 64, 256, 3, "pipe16_256x256x64_w2x2_s3_a2_sp6"},
+    {256, 256, 64, 256, 2, "pipe16_256x256x64_w2x2_s2_a3_early_sp6"},
 };
 
 template <class S, bool BT>

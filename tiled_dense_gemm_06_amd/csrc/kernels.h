@@ -74,7 +74,15 @@ enum PipeConfig {
     PIPE16_256x256x64_A3 = 10,
     PIPE16_256x256x64_A3_EARLY = 11,
     PIPE16_256x256x64_B3 = 12,
-    PIPE_CONFIGS = 13
+    PIPE16_256x256x64_A3_SP2 = 13,
+    PIPE16_256x256x64_A3_SP6 = 14,
+    PIPE16_256x256x64_A3_EARLY_SP2 = 15,
+    PIPE16_256x256x64_A3_SP7 = 16,
+    PIPE16_256x256x64_A3_SP8 = 17,
+    PIPE16_256x256x64_A3_SP6_D5 = 18,
+    PIPE16_256x256x64_B3_SP6 = 19,
+    PIPE16_256x256x64_A3_EARLY_SP6 = 20,
+    PIPE_CONFIGS = 21
 };
 
 // wave-role (ping-pong) schedule: two groups of waves alternate between
