@@ -560,12 +560,16 @@ def test_invalid_arguments_enqueue_nothing(dev):
     assert torch.all(C == 7.0)
 
 
-@pytest.mark.parametrize("config", list(range(10, 21)))
+@pytest.mark.parametrize("config", list(range(10, 23)))
 @pytest.mark.parametrize("shape", [(300, 264, 192), (513, 520, 64), (1024, 1032, 1024), (256, 256, 64), (257, 8, 4096),
-                                   (200, 264, 128), (129, 1000, 320), (512, 768, 2048)])
+                                   (200, 264, 128), (129, 1000, 320), (512, 768, 2048),
+                                   (300, 264, 200), (513, 520, 72), (301, 259, 203), (256, 256, 8), (257, 9, 4104),
+                                   (130, 1031, 1537), (64, 256, 40)])
 def test_pipe16_configs(dev, config, shape):
-    """The 16 x 16 x 32 MFMA tiles (K a multiple of 64, N of 8): ragged M and
-    N, one-stage K, long K, one-column-chunk N; integer inputs exact, C in a
+    """The 16 x 16 x 32 MFMA tiles: ragged M and N, one-stage K, long K,
+    one-column-chunk N, and K that is not whole 64-deep stages (the masked
+    stage after the loop), K or N not a multiple of 8 (the element-wise block
+    of the last rows), K shorter than one stage; integer inputs exact, C in a
     NaN-filled padded buffer whose padding stays NaN; then uniform inputs
     within the tolerance."""
     M, N, K = shape

@@ -308,7 +308,7 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
         const int cfg = config >= 0 ? config : k64 ? tlg::PIPE16_256x256x64_A3_SP8 : tlg::PIPE_256x256x64_W8_A3_EARLY;
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
-        const bool shape_ok = cfg < tlg::PIPE16_FIRST || k64;
+        const bool shape_ok = cfg < tlg::PIPE16_FIRST || !p.trans_b;
         // 128 tiles of 256 x 256 (half the CUs) measured faster than the
         // 128 x 128 tiles already (3072^3: 72 vs 101 us)
         if (shape_ok && dma_ok(p, tc.bm, tc.bn, tc.bk) && (variant == TLG_VARIANT_TILED_PIPE || tiles >= 128)) {

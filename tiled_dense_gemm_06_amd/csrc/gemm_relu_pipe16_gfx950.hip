@@ -119,8 +119,7 @@ constexpr int pipe16_lds_bytes() {
 template <class S>
 __device__ __forceinline__ void store_c_tile16_lds(const KArgs &a, int m0, int n0, int wave, int lane,
                                                    const float4_t (&acc)[S::TN][S::TM], LDS_PTR(char) lds) {
-    constexpr int PIECES = S::WTN / 8;  // 16-byte pieces per row of the wave block
-    static_assert(PIECES == 16, "epilogue layout written for 128-column wave blocks");
+    constexpr int PIECES = S::WTN / 8;  // 16-byte pieces per row of the wave block (8 or 16)
     LDS_PTR(char) q = lds + wave * S::WTM * S::WTN * 2;
     const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
 #pragma unroll
@@ -149,6 +148,80 @@ __device__ __forceinline__ void store_c_tile16_lds(const KArgs &a, int m0, int n
             for (int e = 0; e < 8; ++e)
                 if (n0 + nr + e < a.N) crow[e] = hv[e];
         }
+    }
+}
+
+// The tile product of a 32-deep k-step s of the stage held in (sA, sB).
+template <class S>
+__device__ __forceinline__ void mma16_kstep(LDS_PTR(const char) sA, LDS_PTR(const char) sB, const FragLanes16<S> &fo,
+                                            int s, float4_t (&acc)[S::TN][S::TM]) {
+    Frags16<S> f;
+#pragma unroll
+    for (int r = 0; r < kFragReads16<S>; ++r) frag_read16<S>(f, sA, sB, fo, s, r);
+#pragma unroll
+    for (int i = 0; i < S::TM * S::TN; ++i) mfma16_tile<S>(f, i, acc);
+}
+
+// Rows of K past the loop's whole stages, after every wave is done with the
+// stages. (1) Rows [64*(kmain/64), kmain) when kmain is not whole stages: one
+// stage of direct-to-LDS loads into buffer 0 with every lane's chunk checked
+// against kmain and against M or N, then both k-steps. (2) Rows [kmain, K) (1
+// to 8 of them, when K or N is not a multiple of 8): one zero-padded 32-deep
+// block staged element by element with bounds checks, then one k-step.
+template <class S, int ASTAGES>
+__device__ __forceinline__ void pipe16_k_tail(const KArgs &a, int m0, int n0, int wave, int lane, int wm0, int wn0,
+                                           const FragLanes16<S> &fo, float4_t (&acc)[S::TN][S::TM],
+                                           LDS_PTR(char) lds) {
+    constexpr int B_REGION = ASTAGES * S::A_BYTES;
+    const int tid = threadIdx.x;
+    const int kfull = (a.kmain / S::BK) * S::BK;
+    if (kfull < a.kmain) {
+        barrier_lds();  // no wave reads buffer 0 any more
+        const int4_t ra = make_srd(a.A + (int64_t)m0 * a.lda + kfull);
+        const int4_t rb = make_srd(a.B + (int64_t)kfull * a.ldb + n0);
+#pragma unroll
+        for (int i = 0; i < S::DMA_A; ++i) {
+            const ChunkRef c = dma_a_chunk<S>(wave, i, lane);
+            const bool in = m0 + c.row < a.M && kfull + 8 * c.chunk < a.kmain;
+            dma16(ra, (uint32_t)(uintptr_t)(lds + (wave * S::DMA_A + i) * 1024),
+                  in ? (uint32_t)(c.row * a.lda * 2 + c.chunk * 16) : kOOB);
+        }
+#pragma unroll
+        for (int i = 0; i < S::DMA_B; ++i) {
+            const ChunkRef c = dma_b16_chunk<S>(wave, i, lane);
+            const bool in = kfull + c.row < a.kmain && n0 + 8 * c.chunk < a.N;
+            dma16(rb, (uint32_t)(uintptr_t)(lds + B_REGION + (wave * S::DMA_B + i) * 1024),
+                  in ? (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16) : kOOB);
+        }
+        wait_vmcnt<0>();
+        barrier_lds();
+#pragma unroll
+        for (int s = 0; s < S::KSTEPS; ++s) mma16_kstep<S>(lds, lds + B_REGION, fo, s, acc);
+    }
+    if (a.kmain < a.K) {
+        barrier_lds();
+        // A: rows m of the tile, logical chunks 0..3 (k = kmain + 8c .. +7)
+        for (int q = tid; q < S::BM * 4; q += S::NT) {
+            const int row = q / 4, chunk = q % 4;
+            const int m = m0 + row, k = a.kmain + 8 * chunk;
+            half8_t v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = (m < a.M && k + e < a.K) ? a.A[(int64_t)m * a.lda + k + e] : (_Float16)0.0f;
+            *(LDS_PTR(half8_t))(lds + lds_a_offset<S>(row, chunk)) = v;
+        }
+        // B: rows k = kmain .. kmain+31 of the block, all BN columns
+        for (int q = tid; q < 32 * S::CB; q += S::NT) {
+            const int row = q / S::CB, chunk = q % S::CB;
+            const int k = a.kmain + row, n = n0 + 8 * chunk;
+            half8_t v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = (k < a.K && n + e < a.N) ? a.B[(int64_t)k * a.ldb + n + e] : (_Float16)0.0f;
+            *(LDS_PTR(half8_t))(lds + B_REGION + lds_b16_offset<S>(row, chunk)) = v;
+        }
+        barrier_lds();
+        mma16_kstep<S>(lds, lds + B_REGION, fo, 0, acc);
     }
 }
 
@@ -190,7 +263,13 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave / S::WN) * S::WTM, wn0 = (wave % S::WN) * S::WTN;
     const int m0 = tm_idx * S::BM, n0 = tn_idx * S::BN;
-    const int nk = a.K / S::BK;  // K is a multiple of BK
+    // The loop covers the whole 64-deep stages of K's rows [0, kmain); kmain
+    // is K, or the largest multiple of 8 below K when K or N is not a
+    // multiple of 8 (then no 16-byte chunk the loads fetch crosses the end of
+    // an A row, and a chunk crossing column N of B reads into the next row,
+    // whose values reach only columns >= N, which are never stored). The rows
+    // past the last whole stage are added after the loop (pipe16_k_tail).
+    const int nk = a.kmain / S::BK;
 
     // Loads. A: load i of this wave covers LDS slab (wave*DMA_A + i), rows
     // 8*slab .. +7 of the tile; its descriptor starts at the slab's first row
@@ -325,9 +404,10 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
     }
 #pragma unroll
     for (int i = H; i < T; ++i) mfma16_tile<S>(f[1], i, acc);
+    wait_vmcnt<0>();  // no load may still be writing LDS
+    if (nk * S::BK < a.K) pipe16_k_tail<S, ASTAGES>(a, m0, n0, wave, lane, wm0, wn0, fo, acc, lds);
     mfma16_results_ready();
-    wait_vmcnt<0>();  // no load may still be writing LDS when the work-group ends
-    barrier_lds();    // every wave is done with the stages
+    barrier_lds();  // every wave is done with the stages
     store_c_tile16_lds<S>(a, m0, n0, wave, lane, acc, lds);
 }
 
@@ -341,10 +421,13 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe16(const KArgs a) {
 
 using Pipe16w4 = TileShape16<256, 256, 64, 2, 2, 2>;    // four waves of 128 x 128, two B buffers
 using Pipe16w4B3 = TileShape16<256, 256, 64, 2, 2, 3>;  // three B buffers
+// 128 x 256 tiles, four waves of 128 x 64: twice the tiles of 256 x 256 for
+// problems that would leave CUs idle at that size
+using Pipe16h = TileShape16<128, 256, 64, 1, 4, 3>;
 
 template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
 static hipError_t launch_pipe16_t(const Problem &p, hipStream_t stream) {
-    if (p.K % S::BK || p.N % 8 || p.trans_b) return hipErrorInvalidValue;
+    if (p.trans_b) return hipErrorInvalidValue;
     KArgs a;
     a.A = (const _Float16 *)p.A;
     a.B = (const _Float16 *)p.B;
@@ -359,7 +442,7 @@ static hipError_t launch_pipe16_t(const Problem &p, hipStream_t stream) {
     a.ldc = p.ldc;
     a.group_m = 4;
     a.k_split = (int)p.K;
-    a.kmain = (int)p.K;
+    a.kmain = p.K % 8 == 0 && p.N % 8 == 0 ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
     a.tiles_m = (a.M + S::BM - 1) / S::BM;
     a.tiles_n = (a.N + S::BN - 1) / S::BN;
     hipLaunchKernelGGL((k_tiled_pipe16<S, SPACING, DOFF, ASTAGES, EARLY>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
@@ -383,6 +466,9 @@ hipError_t launch_tiled_pipe16(int config, const Problem &p, hipStream_t stream)
         case PIPE16_256x256x64_A3_SP6_D5: return launch_pipe16_t<Pipe16w4, 6, 5, 3, false>(p, stream);
         case PIPE16_256x256x64_B3_SP6: return launch_pipe16_t<Pipe16w4B3, 6, 1, 2, false>(p, stream);
         case PIPE16_256x256x64_A3_EARLY_SP6: return launch_pipe16_t<Pipe16w4, 6, 1, 3, true>(p, stream);
+        // 12 loads per wave and stage over the 64-slot step
+        case PIPE16_128x256x64_A3: return launch_pipe16_t<Pipe16h, 4, 1, 3, false>(p, stream);
+        case PIPE16_128x256x64_A4: return launch_pipe16_t<Pipe16h, 4, 1, 4, false>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

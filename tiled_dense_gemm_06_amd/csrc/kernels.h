@@ -82,7 +82,9 @@ enum PipeConfig {
     PIPE16_256x256x64_A3_SP6_D5 = 18,
     PIPE16_256x256x64_B3_SP6 = 19,
     PIPE16_256x256x64_A3_EARLY_SP6 = 20,
-    PIPE_CONFIGS = 21
+    PIPE16_128x256x64_A3 = 21,  // four waves of 128 x 64
+    PIPE16_128x256x64_A4 = 22,
+    PIPE_CONFIGS = 23
 };
 
 // wave-role (ping-pong) schedule: two groups of waves alternate between
@@ -102,8 +104,8 @@ hipError_t launch_tiled_dma(int config, const Problem &p, hipStream_t stream);
 hipError_t launch_tiled_dma_grouped(int config, const Problem *ps, int count, hipStream_t stream);
 hipError_t launch_tiled_general(int config, const Problem &p, hipStream_t stream);
 hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream);
-// the 16 x 16 x 32 MFMA configurations (PIPE16_FIRST and up); K a multiple
-// of 64, N of 8, B not transposed (hipErrorInvalidValue otherwise)
+// the 16 x 16 x 32 MFMA configurations (PIPE16_FIRST and up); B not
+// transposed (hipErrorInvalidValue otherwise)
 hipError_t launch_tiled_pipe16(int config, const Problem &p, hipStream_t stream);
 // count (1 .. kGroupMax) problems, all with the same trans_b, in one launch
 // of the eight-wave early-barrier pipelined kernel (each must pass its checks)

@@ -246,22 +246,22 @@ TLG_HD int frag_a16_lane(int wm0, int s, int lane) {
 template <class S>
 TLG_HD int frag_b16_lane(int wn0, int tn, int lane) {
     static_assert(S::CB == 32, "256-column B rows");
-    const int g = lane / 16, i = lane % 16;
-    const int z = (4 * (i / 4)) ^ (2 * (g & 1));
-    return (8 * g + i / 4) * S::RB + 16 * (wn0 / 8 + (i % 4) / 2) + 8 * (i % 2) + 16 * ((2 * tn) ^ z);
+    return frag_b16_offset<S>(wn0, tn, 0, 0, lane);
 }
 // Result register r of MFMA tile (tn, tm) in lane l is C[m][n] with
 // m = wm0 + 16*tm + l%16 and n = wn0 + 16*tn + 4*(l/16) + r.
 TLG_HD int acc16_m(int wm0, int tm, int lane) { return wm0 + 16 * tm + lane % 16; }
 TLG_HD int acc16_n(int wn0, int tn, int r, int lane) { return wn0 + 16 * tn + 4 * (lane / 16) + r; }
-// Epilogue block of a wave (WTM x WTN fp16, rows of 2*WTN bytes, 16 pieces
-// of 16 bytes per row for WTN = 128): piece c of row r at position
-// c ^ (r % 16). The 8-byte result pieces of 16 rows written by one
-// instruction and the 16-byte pieces of 4 whole rows read back by one
-// instruction are both spread over distinct banks.
+// Epilogue block of a wave (WTM x WTN fp16, rows of 2*WTN bytes; 16 pieces of
+// 16 bytes per row for WTN = 128, 8 for WTN = 64): piece c of row r at
+// position c ^ (r % 16), or c ^ ((r / 2) % 8) when two rows share a 256-byte
+// window. The 8-byte result pieces of 16 rows written by one instruction and
+// the 16-byte pieces of whole rows read back by one instruction are both
+// spread over distinct banks.
 template <class S>
 TLG_HD int epi16_offset(int row, int piece) {
-    return row * S::WTN * 2 + 16 * (piece ^ (row % 16));
+    static_assert(S::WTN == 128 || S::WTN == 64, "wave blocks 64 or 128 columns wide");
+    return row * S::WTN * 2 + 16 * (piece ^ (S::WTN == 128 ? row % 16 : (row / 2) % 8));
 }
 
 // ---- tile order ----
