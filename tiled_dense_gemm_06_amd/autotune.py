@@ -36,7 +36,8 @@ SHAPES = [
     (4096, 14336, 4096), (14336, 4096, 4096), (2048, 8192, 1024), (8192, 2048, 8192), (1024, 4096, 16384),
     # skinny M
     (1, 4096, 4096), (16, 14336, 4096), (32, 14336, 4096), (64, 14336, 4096), (16, 4096, 14336),
-    (48, 4096, 14336), (16, 2048, 4096), (8, 8192, 8192), (64, 4096, 8192),
+    (48, 4096, 14336), (16, 2048, 4096), (8, 8192, 8192), (64, 4096, 8192), (48, 1024, 1024), (48, 1024, 1536),
+    (64, 1024, 2048),
     (128, 4096, 4096), (256, 8192, 4096),
     # ragged
     (3001, 2049, 1537), (1000, 1000, 1000), (777, 555, 333), (5000, 3000, 2000),
