@@ -52,3 +52,33 @@ def test_summary_reports_median_and_scaled_traffic(tmp_path):
     # fetch factor 2 (copy read 512 MiB, counter 256 MiB), write factor 1
     assert f"| fetched from beyond L2 | {3 * 2 ** 20 * 2:,} |" in text
     assert f"| written | {2 ** 20:,} |" in text
+
+
+def test_counters_derives_clock_occupancy_and_conflicts(tmp_path):
+    # two dispatches of one kernel, 1 ms each, at 1.5 GHz on 8 XCDs with the
+    # 1024 SIMDs' matrix cores busy 60 % of the cycles; one copy dispatch that
+    # the kernel filter must skip
+    header = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size",
+              "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp",
+              "End_Timestamp"]
+    cycles = 1.5e6 * 8  # GRBM_GUI_ACTIVE over 8 XCDs for 1 ms at 1.5 GHz
+    rows = []
+    for d in (1, 2):
+        res = [d, KERNEL, 1024 * 256, 256, 65536, 0, 128, 256, 96]
+        t0 = 10_000_000 * d
+        for name, v in (("GRBM_GUI_ACTIVE", cycles), ("SQ_VALU_MFMA_BUSY_CYCLES", 0.6 * 1024 * cycles / 8),
+                        ("SQ_INSTS_LDS", 1000.0), ("SQ_LDS_BANK_CONFLICT", 250.0)):
+            rows.append(res + [name, v, t0, t0 + 1_000_000])
+    rows.append([3, "__amd_rocclr_copyBuffer", 512, 512, 0, 0, 8, 0, 32, "GRBM_GUI_ACTIVE", 5.0, 0, 10])
+    _write(tmp_path / "sq.csv", header, rows)
+    out = tmp_path / "counters.md"
+    args = argparse.Namespace(workload="square256", kernel="k_tiled_dma", title="", pmc=[str(tmp_path / "sq.csv")],
+                              pass_cmds=["rocprofv3 --pmc ..."], note="a note", out=str(out))
+    text = pr.counters(args)
+    assert os.path.exists(out)
+    assert "1024 work-groups" in text and "128 VGPRs and 256 AGPRs" in text and "65,536 bytes of LDS" in text
+    assert "| GRBM_GUI_ACTIVE | 12,000,000 | 2 | 1,000,000 |" in text
+    assert "sustained shader clock: 1.500 GHz" in text
+    assert "matrix cores busy: 60.0 %" in text and "37.5 % of the 2.4 GHz dense peak" in text
+    assert "bank-conflict cycles per LDS instruction: 0.250" in text
+    assert text.rstrip().endswith("a note")

@@ -18,6 +18,13 @@ digest of that kernel's device sources (its own ``.hip`` file and the two
 device headers); ``bench.py`` reports them only while the workload still
 runs that configuration and those sources still have that digest.
 
+``counters`` writes the Markdown summary of counter passes of one kernel
+(the sustained clock, matrix-core occupancy, LDS bank conflicts and the
+kernel's resources) for ``profiles/``::
+
+    python -m tiled_dense_gemm_06_amd.profiling counters --workload square8192 \
+        --kernel k_tiled_pipe16 --pmc DIR/run_counter_collection.csv --pass-cmd "..." --out FILE
+
 ``summary`` writes the Markdown summary of one workload's profile (the
 kernel-trace statistics of a command, and the scaled counter bytes when
 given) for ``profiles/``::
@@ -224,6 +231,79 @@ def summary(args) -> str:
     return text
 
 
+def _dispatches(path: str, kernel_substr: str) -> list[dict]:
+    """Per-dispatch counter values, duration (ns) and resources of the
+    dispatches of one kernel in a rocprofv3 --pmc CSV file."""
+    per = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if kernel_substr not in row["Kernel_Name"]:
+                continue
+            d = per.setdefault(row["Dispatch_Id"], {
+                "name": row["Kernel_Name"], "ns": int(row["End_Timestamp"]) - int(row["Start_Timestamp"]),
+                "vgpr": int(row["VGPR_Count"]), "agpr": int(row["Accum_VGPR_Count"]),
+                "sgpr": int(row["SGPR_Count"]), "lds": int(row["LDS_Block_Size"]),
+                "scratch": int(row["Scratch_Size"]), "wg": int(row["Workgroup_Size"]),
+                "grid": int(row["Grid_Size"]), "counters": {}})
+            d["counters"][row["Counter_Name"]] = float(row["Counter_Value"])
+    if not per:
+        raise ValueError(f"no dispatch of a kernel matching {kernel_substr!r} in {path}")
+    return list(per.values())
+
+
+def counters(args) -> str:
+    """Markdown summary of counter passes of one kernel on one workload: mean
+    per dispatch of every counter, and what follows from them: the sustained
+    shader clock (GRBM_GUI_ACTIVE summed over the 8 XCDs, per dispatch
+    duration), the matrix-core occupancy (SQ_VALU_MFMA_BUSY_CYCLES summed over
+    the 1024 SIMDs, per SIMD-cycle of the dispatch), LDS bank-conflict cycles
+    per LDS instruction; and the kernel's resources from the same records."""
+    from . import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    lines = [f"# {args.title or args.kernel} — counters, workload {w.name}", "",
+             "Counter passes (from the repository root, on one MI355X; one rocprofv3 run per pass):", ""]
+    lines += ["    " + c for c in args.pass_cmds]
+    lines += [""]
+    merged = {}
+    res = None
+    for path in args.pmc:
+        ds = _dispatches(path, args.kernel)
+        res = res or ds[0]
+        for k in ds[0]["counters"]:
+            merged[k] = (mean([d["counters"][k] for d in ds]), mean([d["ns"] for d in ds]), len(ds))
+    lines += [f"Kernel: `{res['name']}`", "",
+              f"Resources per work-group of {res['wg']} threads ({res['grid'] // max(1, res['wg'])} work-groups): "
+              f"{res['vgpr']} VGPRs and {res['agpr']} AGPRs per lane (as the trace reports them), {res['sgpr']} SGPRs, "
+              f"{res['lds']:,} bytes of LDS, {res['scratch']} bytes of scratch per lane.", "",
+              "| counter | mean per dispatch | dispatches | mean dispatch ns |", "|---|---|---|---|"]
+    for k in sorted(merged):
+        v, ns, n = merged[k]
+        lines.append(f"| {k} | {v:,.0f} | {n} | {ns:,.0f} |")
+    lines.append("")
+    derived = []
+    if "GRBM_GUI_ACTIVE" in merged:
+        gui, ns, _ = merged["GRBM_GUI_ACTIVE"]
+        ghz = gui / 8 / ns
+        derived.append(f"sustained shader clock: {ghz:.3f} GHz (GRBM_GUI_ACTIVE / 8 XCDs / dispatch ns)")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in merged:
+            busy = merged["SQ_VALU_MFMA_BUSY_CYCLES"][0] / 1024 / (gui / 8)
+            derived.append(f"matrix cores busy: {100 * busy:.1f} % of the SIMD-cycles of the dispatch "
+                           f"(SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / GPU-busy cycles per XCD); at the sustained "
+                           f"clock that is {busy * ghz / 2.4 * 100:.1f} % of the 2.4 GHz dense peak")
+    if "SQ_LDS_BANK_CONFLICT" in merged and "SQ_INSTS_LDS" in merged and merged["SQ_INSTS_LDS"][0] > 0:
+        derived.append(f"LDS bank-conflict cycles per LDS instruction: "
+                       f"{merged['SQ_LDS_BANK_CONFLICT'][0] / merged['SQ_INSTS_LDS'][0]:.3f}")
+    if derived:
+        lines += ["Derived:", ""] + [f"* {x}" for x in derived] + [""]
+    if args.note:
+        lines += [args.note, ""]
+    text = "\n".join(lines)
+    with open(args.out, "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -251,9 +331,20 @@ def main():
     m.add_argument("--counter-cmd", default="")
     m.add_argument("--mx", choices=sorted(PEAK_MX_TFLOPS), help="the block-scaled path with these codes")
     m.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--kernel", required=True, help="substring of the kernel name")
+    c.add_argument("--title", default="")
+    c.add_argument("--pmc", action="append", required=True, help="a rocprofv3 --pmc counter_collection CSV")
+    c.add_argument("--pass-cmd", action="append", default=[], dest="pass_cmds",
+                   help="the command of each counter pass")
+    c.add_argument("--note", default="")
+    c.add_argument("--out", required=True)
     args = ap.parse_args()
     if args.cmd == "traffic":
         print(json.dumps(traffic(args)))
+    elif args.cmd == "counters":
+        counters(args)
     else:
         summary(args)
 
