@@ -100,11 +100,13 @@ def test_plan_shapes_of_the_workloads():
     p = tlg.plan(1, 4096, 4096)
     assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 64 * 4
     assert tlg.plan(3072, 3072, 3072)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"  # 144 tiles of 256 x 256
-    # forced 16 x 16 x 32 tiles need K a multiple of 64 and N of 8
+    # forced 16 x 16 x 32 tiles take any K and N (whole stages, then a masked
+    # stage and a zero-padded block); they refuse a transposed B
+    assert tlg.plan(300, 264, 200, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10)["config_name"] == \
+        "pipe16_256x256x64_w2x2_s2_a3"
+    assert tlg.plan(300, 260, 256, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10, ldb=264, ldc=264)["grid"] == 4
     with pytest.raises(tlg.TlgError):
-        tlg.plan(300, 264, 200, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10)
-    with pytest.raises(tlg.TlgError):
-        tlg.plan(300, 260, 256, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10, ldb=264, ldc=264)
+        tlg.plan(512, 512, 512, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10, trans_b=True)
     assert tlg.plan(256, 256, 256)["variant_name"] == "tiled_dma"
     assert tlg.plan(5, 7, 0)["variant_name"] == "fill_zero"
     assert tlg.plan(0, 7, 9)["variant_name"] == "noop"
