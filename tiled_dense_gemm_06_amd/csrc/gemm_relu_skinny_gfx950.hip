@@ -54,7 +54,9 @@ __device__ __forceinline__ void wait_blocks(int n) {
         wait_vmcnt<0>();
 }
 
-// Cache policy of the partial-strip stores and loads: sc1, device scope.
+// Cache policy of the partial-strip stores and loads: sc1, device scope
+// (the same combining scheme, and the same ordering argument, as the
+// stream-K tiles' partials, kDeviceScope).
 constexpr int kPartialScope = 16;
 
 // Grid: strips x parts (a.k_split parts per strip, adjacent work-groups share

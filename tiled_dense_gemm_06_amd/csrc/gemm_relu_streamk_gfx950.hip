@@ -47,6 +47,17 @@ struct SKArgs {
 };
 
 // Cache policy of the partial-tile stores and loads: sc1, device scope.
+// Partials from work-groups on different XCDs meet through these bits alone.
+// On gfx950 an sc1 load or store is coherent at device scope (it is how the
+// compiler implements a relaxed agent-scope atomic load or store), so each
+// partial lives in one device-wide modification order and no XCD's L2 holds
+// a stale copy of it. The order between a part's partials and its count
+// comes from the wait for store completion (vmcnt(0) in every thread, then
+// the work-group barrier) before the count's atomic is issued; the reading
+// part issues its partial loads only after its own count has returned the
+// total. Nothing else is read across work-groups, so the L2 write-back and
+// invalidate that an agent-scope release/acquire pair adds (measured: 5 to
+// 40 % longer calls on the split shapes) are not needed.
 constexpr int kDeviceScope = 16;
 
 template <class S>
