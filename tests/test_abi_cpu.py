@@ -69,10 +69,16 @@ def test_plan_shapes_of_the_workloads():
     # K a multiple of 64 and N of 8: the 16 x 16 x 32 MFMA tiles
     assert tlg.plan(8192, 8192, 8192)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
     assert tlg.plan(4096, 4096, 4096)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
-    # otherwise the eight-wave 32 x 32 x 16 tiles
-    assert tlg.plan(4096, 4096, 4104)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
+    # and for any K from 256 tiles of 256 x 256 up
+    assert tlg.plan(4096, 4096, 4104)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
+    assert tlg.plan(8192, 8192, 8200)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
+    # otherwise the eight-wave 32 x 32 x 16 tiles: a K tail below 256 tiles,
+    # one wave with a nearly empty second (272 tiles), N not a multiple of 8
+    assert tlg.plan(3072, 3072, 3080)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
+    assert tlg.plan(4096, 4104, 4096)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
     assert tlg.plan(4096, 4100, 4096, aligned=True, ldb=4104, ldc=4104)["config_name"] == \
         "pipe_256x256x64_w2x4_s2_a3_early"
+    assert tlg.plan(8192, 8192, 8192, trans_b=True)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
     # odd sizes and leading dimensions: direct-to-LDS loads, staged K tail; the
     # tuned table gives this class the pipelined 128 x 256 tiles (216 of them)
     p = tlg.plan(3001, 2049, 1537)

@@ -244,6 +244,23 @@ def test_large_square_cross_check_kernel(dev, name):
     assert_close(got, naive, f"{name} full output vs cross-check kernel")
 
 
+@pytest.mark.parametrize("kind", ["integer", "uniform"])
+@pytest.mark.parametrize("shape", [(4096, 4096, 4104), (4096, 4104, 4096), (3072, 3072, 3080)])
+def test_planned_large_k_and_tile_count_edges(dev, shape, kind):
+    """The default plan where the choice between the 16 x 16 x 32 and the
+    32 x 32 x 16 pipelined tiles turns on a K tail and on the tile count, the
+    whole output against the oracle: a K tail at 256 tiles, 272 tiles, and a
+    K tail below 256 tiles."""
+    M, N, K = shape
+    A, B = wl.make_random(M, N, K, seed=M ^ N ^ K, kind=kind)
+    ref = oracle.gemm_relu(A, B)
+    got = bits(run(A, B, dev))
+    if kind == "integer":
+        assert np.array_equal(got, ref)
+    else:
+        assert_close(got, ref, f"{shape} default plan ({tlg.plan(M, N, K)['config_name']})")
+
+
 @pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
 @pytest.mark.parametrize("shape", [(300, 264, 200), (513, 520, 72), (1024, 1032, 1000), (256, 256, 8),
                                    (257, 8, 4104), (301, 259, 203)])

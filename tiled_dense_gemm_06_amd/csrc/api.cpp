@@ -295,17 +295,24 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
     // there are enough tiles to give most CUs one
     if (variant == TLG_VARIANT_TILED_PIPE || variant == TLG_VARIANT_AUTO) {
         if (!config_ok(config, tlg::PIPE_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
-        // the 16 x 16 x 32 MFMA tiles take K in whole 64-deep stages and
-        // whole 16-byte chunks of B's rows; they are the default where they
-        // can serve (8192^3 804 vs 834 us, 4096^3 109.2 vs 112.4 us for the
-        // eight-wave 32 x 32 x 16 tiles, interleaved on one MI355X: the
+        // The 16 x 16 x 32 MFMA tiles (loads every eight MFMA slots) against
+        // the eight-wave 32 x 32 x 16 tiles, interleaved on one MI355X: the
         // smaller MFMA spends less energy per FLOP, which the power-limited
-        // clock turns into speed), with their loads every eight MFMA slots
-        // (medians over ten interleaved rounds against every four: 8192^3
-        // 805 vs 819 us, 4096^3 108.6 vs 111.5, 3072^3 68.9 vs 75.4,
-        // 8192x8192x4096 418.7 vs 432.5)
-        const bool k64 = p.K % 64 == 0 && p.N % 8 == 0;
-        const int cfg = config >= 0 ? config : k64 ? tlg::PIPE16_256x256x64_A3_SP8 : tlg::PIPE_256x256x64_W8_A3_EARLY;
+        // clock turns into speed (8192^3 804 vs 834 us, 4096^3 109.2 vs
+        // 112.4, 8192x4096x8192 401.6 vs 429.5, 6144^3 406.7 vs 415.5,
+        // 3072^3 74.8 vs 76.9). They are the default for N a multiple of 8
+        // (whole 16-byte chunks of B's rows) and K in whole 64-deep stages,
+        // or any K from 256 tiles up (a masked last stage: 8192x8192x8200
+        // 806.9 vs 888.8, 4096x4096x4104 114.7 vs 119.6, 6144x6144x6152
+        // 420.4 vs 442.9); below 256 tiles a K tail favours the 32 x 32 x 16
+        // tiles (3072x3072x3080 77.0 vs 79.7, 5000x3000x2000 65.0 vs 70.2),
+        // and so does one wave of tiles with a nearly empty second one (272
+        // tiles: 4096x4104x4096 174.9 vs 183.9, 4096x4352x4096 173.2 vs
+        // 178.0).
+        const int64_t tiles256 = ceil_div(p.M, 256) * ceil_div(p.N, 256);
+        const bool use16 = p.N % 8 == 0 && !p.trans_b && (p.K % 64 == 0 || tiles256 >= 256) &&
+                           !(tiles256 > 256 && tiles256 < 320);
+        const int cfg = config >= 0 ? config : use16 ? tlg::PIPE16_256x256x64_A3_SP8 : tlg::PIPE_256x256x64_W8_A3_EARLY;
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
         const bool shape_ok = cfg < tlg::PIPE16_FIRST || !p.trans_b;
