@@ -20,11 +20,12 @@
 // conflicts. One K step is a fixed sequence of 128 MFMA slots (two 32-deep
 // k-steps of 64 MFMAs); between MFMAs sit the LDS reads of the next k-step's
 // fragments and, every SPACING slots, one direct-to-LDS load of a later
-// stage, so a lone wave per SIMD never waits on an operand. K must be a
-// multiple of the stage depth (and N of 8): then every stage is wholly inside
-// K or wholly past it and whether a load reads memory is decided per stage
-// by the buffer descriptor's range, on the scalar unit. The C tile leaves
-// through LDS as whole 256-byte row segments.
+// stage, so a lone wave per SIMD never waits on an operand. The loop runs
+// over whole stages only, so every stage in it is wholly inside K and no load
+// in the slot program needs a range check; the rows of K past the last whole
+// stage are added after the loop (one stage loaded with per-lane ranges, then
+// a zero-padded block staged element by element). The C tile leaves through
+// LDS as whole 256-byte row segments.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -68,8 +68,8 @@ enum PipeConfig {
     PIPE_256x256x64_W8_A3_EARLY = 7,  // stage barrier before the last half k-step (the default)
     PIPE_256x256x64_W8_B3_EARLY = 8,  // two A buffers, three B buffers
     PIPE_256x256x64_B3 = 9,           // four waves, two A buffers, three B buffers
-    // v_mfma_f32_16x16x32_f16 tiles (K a multiple of 64, N of 8, B not
-    // transposed): four waves of 128 x 128
+    // v_mfma_f32_16x16x32_f16 tiles (any K and N, B not transposed): four
+    // waves of 128 x 128 (128 x 256 tiles: four waves of 128 x 64)
     PIPE16_FIRST = 10,
     PIPE16_256x256x64_A3 = 10,
     PIPE16_256x256x64_A3_EARLY = 11,
