@@ -8,8 +8,8 @@
 //   * the operand fragment reads (ds_read_b128 and ds_read_b64_tr_b16 with
 //     their measured lane semantics), checking LDS bounds and that each read
 //     is free of bank conflicts on a 64-bank LDS;
-//   * v_mfma_f32_32x32x16_f16 with its measured operand and result layouts
-//     (fp32 products, fp32 sums);
+//   * v_mfma_f32_32x32x16_f16 and v_mfma_f32_16x16x32_f16 with their
+//     measured operand and result layouts (fp32 products, fp32 sums);
 //   * the epilogue (ReLU and round-to-nearest-even fp16, or fp32 partials),
 //     checking that every element of the M x N window is written exactly once
 //     and nothing outside it.
@@ -319,6 +319,306 @@ void run_dma(const Problem &p, bool split, Errs &er, std::vector<int> &cover) {
         if (seen[t] != 1) er.tile_dup++;
 }
 
+// The 16 x 16 x 32 pipelined kernel (gemm_relu_pipe16_gfx950.hip), with its
+// own load offsets (p16_a_lane_bytes, p16_b_lane_bytes, p16_b_slab_bytes and
+// the buffer ranges it sets), fragment address parts (frag_a16_lane,
+// frag_b16_lane), v_mfma_f32_16x16x32_f16 with its measured layouts, the K
+// tail (a masked stage, then a zero-padded 32-deep block) and the LDS-staged
+// epilogue (epi16_offset).
+template <class S>
+void run_pipe16(const Problem &p, Errs &er, std::vector<int> &cover) {
+    const int tiles_m = (p.M + S::BM - 1) / S::BM, tiles_n = (p.N + S::BN - 1) / S::BN;
+    const int nwg = tiles_m * tiles_n;
+    std::vector<int> seen(nwg, 0);
+    const int STAGE = S::A_BYTES + S::B_BYTES;
+    std::vector<uint8_t> lds(STAGE);
+    std::vector<int> lds_w(STAGE);
+    const int kmain = (p.K % 8 == 0 && p.N % 8 == 0) ? p.K : 8 * ((p.K - 1) / 8);
+    const int nk = kmain / S::BK;
+    const long b_end = (long)(p.K - 1) * p.ldb + p.N;  // elements of B the caller owns
+    // a global element read by a direct-to-LDS load, given by its logical
+    // position (row, col) and the element index the load's address gives:
+    // the two must agree, the position must lie inside the matrix and inside
+    // K's rows [0, kend)
+    auto read_a = [&](long row, long col, long idx, int kend) -> uint16_t {
+        if (idx != row * p.lda + col || row < 0 || row >= p.M || col < 0 || col >= kend) {
+            er.oob_global++;
+            return 0;
+        }
+        return p.A[idx];
+    };
+    auto read_b = [&](long row, long col, long idx, int kend) -> uint16_t {
+        // past column N only when N is not a multiple of 8, then into the
+        // row's padding or the next row, never past the caller's last element
+        if (idx != row * p.ldb + col || row < 0 || row >= kend || (col >= p.N && p.N % 8 == 0) || idx >= b_end) {
+            er.oob_global++;
+            return 0;
+        }
+        return p.B[idx];
+    };
+    auto mark = [&](int dst, int n, int limit) {
+        for (int b = 0; b < n; ++b) {
+            if (dst + b < 0 || dst + b >= limit) { er.lds_oob++; continue; }
+            if (lds_w[dst + b]++) er.lds_multi++;
+        }
+    };
+    for (int pid = 0; pid < nwg; ++pid) {
+        int tmi, tni;
+        grouped_tile(xcd_remap(pid, nwg), tiles_m, tiles_n, 4, &tmi, &tni);
+        if (tmi < 0 || tmi >= tiles_m || tni < 0 || tni >= tiles_n) { er.tile_dup++; continue; }
+        if (seen[tmi * tiles_n + tni]++) er.tile_dup++;
+        const int m0 = tmi * S::BM, n0 = tni * S::BN;
+        std::vector<float> acc((size_t)S::WAVES * S::TN * S::TM * 64 * 4, 0.0f);
+        // fragments of k-step s of the stage in `lds` and the MFMAs on them
+        auto kstep = [&](int s) {
+            for (int w = 0; w < S::WAVES; ++w) {
+                const int wm0 = (w / S::WN) * S::WTM, wn0 = (w % S::WN) * S::WTN;
+                std::vector<float> bf((size_t)S::TN * 64 * 8), af((size_t)S::TM * 64 * 8);
+                for (int tn = 0; tn < S::TN; ++tn)
+                    for (int h = 0; h < 2; ++h) {
+                        int addr[64];
+                        for (int l = 0; l < 64; ++l) {
+                            addr[l] = frag_b16_lane<S>(wn0, tn, l) + (32 * s + 4 * h) * S::RB;
+                            if (addr[l] != frag_b16_offset<S>(wn0, tn, s, h, l)) er.lds_oob++;
+                            if (addr[l] < 0 || addr[l] + 8 > S::B_BYTES || addr[l] % 8) er.lds_oob++;
+                        }
+                        for (int half = 0; half < 2; ++half) {  // 32 lanes x 8 bytes on 64 banks
+                            int used[64] = {0};
+                            for (int l = 32 * half; l < 32 * half + 32; ++l)
+                                for (int d = 0; d < 2; ++d)
+                                    if (used[((addr[l] + 4 * d) / 4) % 64]++) er.bank_conflict++;
+                        }
+                        for (int l = 0; l < 64; ++l) {  // the transposing read's lane semantics
+                            int g = l / 16, i = l % 16;
+                            for (int j = 0; j < 4; ++j) {
+                                int a = addr[16 * g + i / 4 + 4 * j];
+                                uint16_t v = 0;
+                                if (a >= 0 && a + 8 <= S::B_BYTES) memcpy(&v, &lds[S::A_BYTES + a + 2 * (i % 4)], 2);
+                                bf[((size_t)tn * 64 + l) * 8 + 4 * h + j] = h2f(v);
+                            }
+                        }
+                    }
+                for (int tm = 0; tm < S::TM; ++tm) {
+                    int addr[64];
+                    for (int l = 0; l < 64; ++l) {
+                        addr[l] = frag_a16_lane<S>(wm0, s & 1, l) + tm * 16 * S::RA;
+                        if (addr[l] != frag_a16_offset<S>(wm0, tm, s, l)) er.lds_oob++;
+                        if (addr[l] < 0 || addr[l] + 16 > S::A_BYTES || addr[l] % 16) er.lds_oob++;
+                    }
+                    for (int q = 0; q < 4; ++q) {  // 16 lanes x 16 bytes per LDS cycle
+                        int used[16] = {0};
+                        for (int l = 16 * q; l < 16 * q + 16; ++l)
+                            if (used[slot16(addr[l])]++) er.bank_conflict++;
+                    }
+                    for (int l = 0; l < 64; ++l)
+                        for (int e = 0; e < 8; ++e) {
+                            uint16_t v = 0;
+                            if (addr[l] >= 0 && addr[l] + 16 <= S::A_BYTES) memcpy(&v, &lds[addr[l] + 2 * e], 2);
+                            af[((size_t)tm * 64 + l) * 8 + e] = h2f(v);
+                        }
+                }
+                // D = X * Y, X (16 x 32) the B fragment: lane l row l%16, k 8*(l/16)+e;
+                // Y (32 x 16) the A fragment: lane l column l%16, k 8*(l/16)+e;
+                // result register r of lane l: D[4*(l/16) + r][l%16]
+                for (int tn = 0; tn < S::TN; ++tn)
+                    for (int tm = 0; tm < S::TM; ++tm)
+                        for (int l = 0; l < 64; ++l)
+                            for (int r = 0; r < 4; ++r) {
+                                int i = 4 * (l / 16) + r, j = l % 16;
+                                float sum = 0.0f;
+                                for (int kk = 0; kk < 32; ++kk) {
+                                    int lx = i + 16 * (kk / 8), ly = j + 16 * (kk / 8), e = kk % 8;
+                                    sum += bf[((size_t)tn * 64 + lx) * 8 + e] * af[((size_t)tm * 64 + ly) * 8 + e];
+                                }
+                                float &d = acc[((((size_t)w * S::TN + tn) * S::TM + tm) * 64 + l) * 4 + r];
+                                d = d + sum;
+                            }
+            }
+        };
+        auto clear = [&]() {
+            std::fill(lds.begin(), lds.end(), 0xAB);
+            std::fill(lds_w.begin(), lds_w.end(), 0);
+        };
+        // the loop's whole stages: offsets computed once per lane, the stage
+        // moving only the descriptor base; A's range ends after row M - 1
+        for (int kt = 0; kt < nk; ++kt) {
+            const int k0 = kt * S::BK;
+            clear();
+            for (int w = 0; w < S::WAVES; ++w)
+                for (int lane = 0; lane < 64; ++lane) {
+                    for (int i = 0; i < S::DMA_A; ++i) {
+                        const int slab = w * S::DMA_A + i;
+                        const long base = (long)(m0 + slab * 8) * p.lda + k0;  // the descriptor's base
+                        const long rows = (long)p.M - m0 - slab * 8;
+                        const long nrec = rows <= 0 ? 0 : rows * p.lda * 2;
+                        const long off = (long)p16_a_lane_bytes<S>(lane, slab % 2, p.lda);
+                        const int dst = slab * 1024 + lane * 16;
+                        mark(dst, 16, S::A_BYTES);
+                        const bool in = off + 16 <= nrec;
+                        if (!in && off < nrec) er.oob_global++;  // a load only partly in range
+                        const ChunkRef c = dma_a_chunk<S>(w, i, lane);  // what the layout expects here
+                        if (in != (m0 + c.row < p.M)) er.oob_global++;
+                        for (int e = 0; e < 8; ++e) {
+                            uint16_t v = in ? read_a(m0 + c.row, k0 + 8 * c.chunk + e, base + off / 2 + e, kmain) : 0;
+                            if (dst + 2 * e + 2 <= S::A_BYTES) memcpy(&lds[dst + 2 * e], &v, 2);
+                        }
+                    }
+                    for (int i = 0; i < S::DMA_B; ++i) {
+                        const int slab = w * S::DMA_B + i;
+                        const long base = (long)k0 * p.ldb + n0;
+                        const long soff = (long)p16_b_slab_bytes(slab, p.ldb);
+                        const long off = (long)p16_b_lane_bytes<S>(lane, p16_b_pattern(slab), n0, p.N, p.ldb);
+                        const int dst = S::A_BYTES + slab * 1024 + lane * 16;
+                        mark(dst, 16, STAGE);
+                        const ChunkRef c = dma_b16_chunk<S>(w, i, lane);
+                        if ((off >= 0) != (n0 + 8 * c.chunk < p.N)) er.oob_global++;
+                        for (int e = 0; e < 8; ++e) {
+                            uint16_t v = off >= 0 ? read_b(k0 + c.row, n0 + 8 * c.chunk + e, base + (soff + off) / 2 + e,
+                                                           kmain)
+                                                  : 0;
+                            if (dst + 2 * e + 2 <= STAGE) memcpy(&lds[dst + 2 * e], &v, 2);
+                        }
+                    }
+                }
+            for (int b = 0; b < STAGE; ++b)
+                if (lds_w[b] != 1) er.lds_multi++;
+            for (int s = 0; s < S::KSTEPS; ++s) kstep(s);
+        }
+        // rows [64*nk, kmain): one stage with every lane's chunk checked
+        const int kfull = nk * S::BK;
+        if (kfull < kmain) {
+            clear();
+            for (int w = 0; w < S::WAVES; ++w)
+                for (int lane = 0; lane < 64; ++lane) {
+                    for (int i = 0; i < S::DMA_A; ++i) {
+                        const ChunkRef c = dma_a_chunk<S>(w, i, lane);
+                        const int dst = (w * S::DMA_A + i) * 1024 + lane * 16;
+                        mark(dst, 16, S::A_BYTES);
+                        const bool in = m0 + c.row < p.M && kfull + 8 * c.chunk < kmain;
+                        for (int e = 0; e < 8; ++e) {
+                            const long row = m0 + c.row, col = kfull + 8 * c.chunk + e;
+                            uint16_t v = in ? read_a(row, col, row * p.lda + col, kmain) : 0;
+                            memcpy(&lds[dst + 2 * e], &v, 2);
+                        }
+                    }
+                    for (int i = 0; i < S::DMA_B; ++i) {
+                        const ChunkRef c = dma_b16_chunk<S>(w, i, lane);
+                        const int dst = S::A_BYTES + (w * S::DMA_B + i) * 1024 + lane * 16;
+                        mark(dst, 16, STAGE);
+                        const bool in = kfull + c.row < kmain && n0 + 8 * c.chunk < p.N;
+                        for (int e = 0; e < 8; ++e) {
+                            const long row = kfull + c.row, col = n0 + 8 * c.chunk + e;
+                            uint16_t v = in ? read_b(row, col, row * p.ldb + col, kmain) : 0;
+                            memcpy(&lds[dst + 2 * e], &v, 2);
+                        }
+                    }
+                }
+            for (int b = 0; b < STAGE; ++b)
+                if (lds_w[b] != 1) er.lds_multi++;
+            for (int s = 0; s < S::KSTEPS; ++s) kstep(s);
+        }
+        // rows [kmain, K): a zero-padded 32-deep block, element by element
+        if (kmain < p.K) {
+            std::fill(lds.begin(), lds.end(), 0xAB);
+            for (int row = 0; row < S::BM; ++row)
+                for (int chunk = 0; chunk < 4; ++chunk)
+                    for (int e = 0; e < 8; ++e) {
+                        long m = m0 + row, k = kmain + 8 * chunk + e;
+                        uint16_t v = (m < p.M && k < p.K) ? p.A[m * p.lda + k] : 0;
+                        memcpy(&lds[lds_a_offset<S>(row, chunk) + 2 * e], &v, 2);
+                    }
+            for (int row = 0; row < 32; ++row)
+                for (int chunk = 0; chunk < S::CB; ++chunk)
+                    for (int e = 0; e < 8; ++e) {
+                        long k = kmain + row, n = n0 + 8 * chunk + e;
+                        uint16_t v = (k < p.K && n < p.N) ? p.B[k * p.ldb + n] : 0;
+                        memcpy(&lds[S::A_BYTES + lds_b16_offset<S>(row, chunk) + 2 * e], &v, 2);
+                    }
+            kstep(0);
+        }
+        // epilogue: each wave's block through LDS, then whole row pieces
+        constexpr int PIECES = S::WTN / 8;
+        const int EPI = S::WAVES * S::WTM * S::WTN * 2;
+        std::vector<uint8_t> elds(EPI, 0);
+        std::vector<int> ew(EPI, 0);
+        for (int w = 0; w < S::WAVES; ++w) {
+            const int q = w * S::WTM * S::WTN * 2;
+            const int wm0 = (w / S::WN) * S::WTM, wn0 = (w % S::WN) * S::WTN;
+            for (int tn = 0; tn < S::TN; ++tn)
+                for (int tm = 0; tm < S::TM; ++tm) {
+                    int addr[64];
+                    for (int l = 0; l < 64; ++l) {
+                        const int row = 16 * tm + l % 16, col = 16 * tn + 4 * (l / 16);
+                        addr[l] = q + epi16_offset<S>(row, col / 8) + 2 * (col % 8);
+                        if (addr[l] < q || addr[l] + 8 > q + S::WTM * S::WTN * 2) { er.lds_oob++; continue; }
+                        for (int r = 0; r < 4; ++r) {
+                            float v = acc[((((size_t)w * S::TN + tn) * S::TM + tm) * 64 + l) * 4 + r];
+                            uint16_t h = f2h(v > 0.0f ? v : 0.0f);
+                            memcpy(&elds[addr[l] + 2 * r], &h, 2);
+                        }
+                        for (int b = 0; b < 8; ++b)
+                            if (ew[addr[l] + b]++) er.lds_multi++;
+                    }
+                    for (int half = 0; half < 2; ++half) {  // 32 lanes x 8 bytes on 64 banks
+                        int used[64] = {0};
+                        for (int l = 32 * half; l < 32 * half + 32; ++l)
+                            for (int d = 0; d < 2; ++d)
+                                if (used[((addr[l] + 4 * d) / 4) % 64]++) er.bank_conflict++;
+                    }
+                }
+            for (int k = 0; k < S::WTM / (64 / PIECES); ++k) {
+                int addr[64];
+                for (int l = 0; l < 64; ++l) addr[l] = q + epi16_offset<S>(k * (64 / PIECES) + l / PIECES, l % PIECES);
+                for (int g = 0; g < 4; ++g) {
+                    int used[16] = {0};
+                    for (int l = 16 * g; l < 16 * g + 16; ++l)
+                        if (used[slot16(addr[l])]++) er.bank_conflict++;
+                }
+                for (int l = 0; l < 64; ++l) {
+                    const int row = k * (64 / PIECES) + l / PIECES, piece = l % PIECES;
+                    const int m = m0 + wm0 + row;
+                    if (m >= p.M) continue;  // dropped by the range check
+                    for (int e = 0; e < 8; ++e) {
+                        const int n = n0 + wn0 + 8 * piece + e;
+                        if (n >= p.N) {
+                            if (n0 + wn0 + 8 * piece + 8 <= p.N) er.c_outside++;
+                            continue;  // stored element by element up to N
+                        }
+                        uint16_t v;
+                        memcpy(&v, &elds[addr[l] + 2 * e], 2);
+                        p.C[(size_t)m * p.ldc + n] = v;
+                        cover[(size_t)m * p.N + n]++;
+                    }
+                }
+            }
+        }
+        for (int b = 0; b < EPI; ++b)
+            if (ew[b] != 1) er.lds_multi++;
+    }
+    for (int t = 0; t < nwg; ++t)
+        if (seen[t] != 1) er.tile_dup++;
+}
+
+template <class S>
+int emulate_pipe16(const Problem &p, long *errs) {
+    Errs er;
+    std::vector<int> cover((size_t)p.M * p.N, 0);
+    run_pipe16<S>(p, er, cover);
+    for (int c : cover) {
+        if (c == 0) er.c_missing++;
+        if (c > 1) er.c_multi++;
+    }
+    errs[0] = er.oob_global;
+    errs[1] = er.lds_multi;
+    errs[2] = er.lds_oob;
+    errs[3] = er.bank_conflict;
+    errs[4] = er.c_multi;
+    errs[5] = er.c_missing;
+    errs[6] = er.c_outside;
+    errs[7] = er.tile_dup;
+    return 0;
+}
+
 template <class S>
 int emulate(const Problem &p, bool split, long *errs) {
     Errs er;
@@ -360,6 +660,11 @@ using E256w8x32 = TileShape<256, 256, 32, 2, 4, 4>;
 using EP256x128 = TileShape<256, 128, 64, 2, 2, 3>;  // pipelined half tiles
 using EP128x256 = TileShape<128, 256, 64, 1, 4, 3>;
 using EStrip64 = TileShape<64, 64, 64, 1, 1, 3>;  // one wave per 64 x 64 strip ring
+// the 16 x 16 x 32 pipelined kernel: four waves of 128 x 128, the 128 x 256
+// half tiles, eight waves of 128 x 64
+using E16w4 = TileShape16<256, 256, 64, 2, 2, 2>;
+using E16h = TileShape16<128, 256, 64, 1, 4, 3>;
+using E16w8 = TileShape16<256, 256, 64, 2, 4, 2>;
 
 extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A, long lda, const uint16_t *B,
                              long ldb, uint16_t *C, long ldc, int splits, int k_split, float *W, long *errs) {
@@ -376,6 +681,9 @@ extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A,
         case 8: return emulate<EStrip64>(p, false, errs);
         case 10: return emulate<ES128>(p, true, errs);
         case 11: return emulate<ES256>(p, true, errs);
+        case 20: return emulate_pipe16<E16w4>(p, errs);
+        case 21: return emulate_pipe16<E16h>(p, errs);
+        case 22: return emulate_pipe16<E16w8>(p, errs);
         default: return -1;
     }
 }

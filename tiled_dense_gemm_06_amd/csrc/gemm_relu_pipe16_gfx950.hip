@@ -275,21 +275,18 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
     // Loads. A: load i of this wave covers LDS slab (wave*DMA_A + i), rows
     // 8*slab .. +7 of the tile; its descriptor starts at the slab's first row
     // and ends after row M - 1 (rows past M read zeros), and the lane's offset
-    // inside the slab depends only on the slab's parity (the swizzle of rows 16
-    // apart repeats). B: load i covers slab (wave*DMA_B + i), rows 2*slab and
-    // 2*slab + 1 of the stage; the slab's start is the instruction's scalar
-    // offset, and the lane's offset (kOOB for a column chunk past N) takes one
-    // of four forms, by the slab's swizzle pattern.
-    static_assert(S::ROWS_A_SLAB == 8 && S::ROWS_B_SLAB == 2 && S::CA == 8, "64-deep A rows, 256-column B rows");
+    // inside the slab depends only on the slab's parity (p16_a_lane_bytes). B:
+    // load i covers slab (wave*DMA_B + i), rows 2*slab and 2*slab + 1 of the
+    // stage; the slab's start is the instruction's scalar offset, and the
+    // lane's offset (kOOB for a column chunk past N) takes one of four forms,
+    // by the slab's swizzle pattern (p16_b_lane_bytes).
     uint32_t voff_a[2], voff_b[4];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-        voff_a[q] = (uint32_t)((lane / 8) * a.lda * 2 + 16 * ((lane % 8) ^ ((4 * q + lane / 16) % 8)));
+    for (int q = 0; q < 2; ++q) voff_a[q] = (uint32_t)p16_a_lane_bytes<S>(lane, q, a.lda);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int k = 2 * (q % 2) + 8 * (q / 2) + lane / 32;  // a row with the pattern's swizzle
-        const int chunk = (lane % 32) ^ swz_b16(k);
-        voff_b[q] = n0 + 8 * chunk < a.N ? (uint32_t)((lane / 32) * a.ldb * 2 + 16 * chunk) : kOOB;
+        const int64_t o = p16_b_lane_bytes<S>(lane, q, n0, a.N, a.ldb);
+        voff_b[q] = o < 0 ? kOOB : (uint32_t)o;
     }
     uint32_t nrec_a[S::DMA_A];  // bytes of the slab's rows inside M
 #pragma unroll
@@ -320,7 +317,7 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
             int4_t r = make_srd(b_tile + (int64_t)k0 * a.ldb);
             if (kt >= nk) r[2] = 0;
             dma16_soff(r, (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES + slab * 1024),
-                       voff_b[(slab % 2) + 2 * ((slab / 4) % 2)], (uint32_t)(slab * 2 * a.ldb * 2));
+                       voff_b[p16_b_pattern(slab)], (uint32_t)p16_b_slab_bytes(slab, a.ldb));
         }
     };
 
@@ -425,6 +422,8 @@ using Pipe16w4B3 = TileShape16<256, 256, 64, 2, 2, 3>;  // three B buffers
 // 128 x 256 tiles, four waves of 128 x 64: twice the tiles of 256 x 256 for
 // problems that would leave CUs idle at that size
 using Pipe16h = TileShape16<128, 256, 64, 1, 4, 3>;
+// eight waves of 128 x 64 (two per SIMD, 128 accumulators each)
+using Pipe16w8 = TileShape16<256, 256, 64, 2, 4, 2>;
 
 template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
 static hipError_t launch_pipe16_t(const Problem &p, hipStream_t stream) {
@@ -470,6 +469,10 @@ hipError_t launch_tiled_pipe16(int config, const Problem &p, hipStream_t stream)
         // 12 loads per wave and stage over the 64-slot step
         case PIPE16_128x256x64_A3: return launch_pipe16_t<Pipe16h, 4, 1, 3, false>(p, stream);
         case PIPE16_128x256x64_A4: return launch_pipe16_t<Pipe16h, 4, 1, 4, false>(p, stream);
+        // eight waves: 8 loads per wave and stage over the 64-slot step
+        case PIPE16_256x256x64_W8_A3_SP8: return launch_pipe16_t<Pipe16w8, 8, 1, 3, false>(p, stream);
+        case PIPE16_256x256x64_W8_A3_SP4: return launch_pipe16_t<Pipe16w8, 4, 1, 3, false>(p, stream);
+        case PIPE16_256x256x64_W8_A3_EARLY_SP6: return launch_pipe16_t<Pipe16w8, 6, 1, 3, true>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

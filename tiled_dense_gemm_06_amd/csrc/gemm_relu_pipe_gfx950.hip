@@ -381,6 +381,9 @@ const TileConfig kPipeConfigs[PIPE_CONFIGS] = {
     {256, 256, 64, 256, 2, "pipe16_256x256x64_w2x2_s2_a3_early_sp6"},
     {128, 256, 64, 256, 3, "pipe16_128x256x64_w1x4_s3_a3"},
     {128, 256, 64, 256, 3, "pipe16_128x256x64_w1x4_s3_a4"},
+    {256, 256, 64, 512, 2, "pipe16_256x256x64_w2x4_s2_a3_sp8"},
+    {256, 256, 64, 512, 2, "pipe16_256x256x64_w2x4_s2_a3_sp4"},
+    {256, 256, 64, 512, 2, "pipe16_256x256x64_w2x4_s2_a3_early_sp6"},
 };
 
 template <class S, bool BT>

@@ -84,7 +84,11 @@ enum PipeConfig {
     PIPE16_256x256x64_A3_EARLY_SP6 = 20,
     PIPE16_128x256x64_A3 = 21,  // four waves of 128 x 64
     PIPE16_128x256x64_A4 = 22,
-    PIPE_CONFIGS = 23
+    // eight waves of 128 x 64, two per SIMD
+    PIPE16_256x256x64_W8_A3_SP8 = 23,
+    PIPE16_256x256x64_W8_A3_SP4 = 24,
+    PIPE16_256x256x64_W8_A3_EARLY_SP6 = 25,
+    PIPE_CONFIGS = 26
 };
 
 // wave-role (ping-pong) schedule: two groups of waves alternate between

@@ -213,6 +213,30 @@ TLG_HD ChunkRef dma_b16_chunk(int wave, int i, int lane) {
     int pos = lane % S::CB;
     return ChunkRef{row, pos ^ swz_b16(row)};
 }
+// The 16 x 16 x 32 pipelined kernel computes its load offsets once per lane
+// (a stage changes only the buffer descriptor's base). A slab (8 rows of 64
+// k, the rows of load dma_a_chunk(wave, i, lane)): the lane's byte offset from
+// the slab's first row depends on the slab's parity q alone, since the
+// swizzle of rows 16 apart repeats. B slab (2 rows of 256 n,
+// dma_b16_chunk): the slab's start is the instruction's scalar offset
+// (p16_b_slab_bytes), and the lane's offset inside the slab takes one of
+// four forms, by the swizzle pattern of the slab's rows (p16_b_pattern); a
+// chunk that starts at or past column N gets -1 (the kernel's out-of-range
+// offset).
+template <class S>
+TLG_HD int64_t p16_a_lane_bytes(int lane, int q, int64_t lda) {
+    static_assert(S::CA == 8 && S::ROWS_A_SLAB == 8, "64-deep A rows");
+    return (int64_t)(lane / 8) * lda * 2 + 16 * ((lane % 8) ^ ((4 * q + lane / 16) % 8));
+}
+TLG_HD constexpr int p16_b_pattern(int slab) { return (slab % 2) + 2 * ((slab / 4) % 2); }
+template <class S>
+TLG_HD int64_t p16_b_lane_bytes(int lane, int pattern, int n0, int N, int64_t ldb) {
+    static_assert(S::CB == 32 && S::ROWS_B_SLAB == 2, "256-column B rows");
+    const int k = 2 * (pattern % 2) + 8 * (pattern / 2) + lane / 32;  // a row with the pattern's swizzle
+    const int chunk = (lane % 32) ^ swz_b16(k);
+    return n0 + 8 * chunk < N ? (int64_t)(lane / 32) * ldb * 2 + 16 * chunk : -1;
+}
+TLG_HD int64_t p16_b_slab_bytes(int slab, int64_t ldb) { return (int64_t)slab * 2 * ldb * 2; }
 // Second operand (A tile), MFMA tile tm, 32-deep k-step s: lane l reads 16
 // bytes = A[wm0 + 16*tm + l%16][32*s + 8*(l/16) .. +7].
 template <class S>
