@@ -665,6 +665,7 @@ using EStrip64 = TileShape<64, 64, 64, 1, 1, 3>;  // one wave per 64 x 64 strip 
 using E16w4 = TileShape16<256, 256, 64, 2, 2, 2>;
 using E16h = TileShape16<128, 256, 64, 1, 4, 3>;
 using E16w8 = TileShape16<256, 256, 64, 2, 4, 2>;
+using E16t = TileShape16<192, 256, 64, 2, 2, 2>;
 
 extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A, long lda, const uint16_t *B,
                              long ldb, uint16_t *C, long ldc, int splits, int k_split, float *W, long *errs) {
@@ -684,6 +685,7 @@ extern "C" int emu_gemm_relu(int config, int M, int N, int K, const uint16_t *A,
         case 20: return emulate_pipe16<E16w4>(p, errs);
         case 21: return emulate_pipe16<E16h>(p, errs);
         case 22: return emulate_pipe16<E16w8>(p, errs);
+        case 23: return emulate_pipe16<E16t>(p, errs);
         default: return -1;
     }
 }

@@ -105,7 +105,17 @@ def test_plan_shapes_of_the_workloads():
     assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 32 * 4
     p = tlg.plan(1, 4096, 4096)
     assert p["config_name"] == "splitk_waves_32x64x64_w2_s3" and p["splits"] == 4 and p["grid"] == 64 * 4
-    assert tlg.plan(3072, 3072, 3072)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"  # 144 tiles of 256 x 256
+    # fewer than 256 tiles of 256 x 256: 129-256 tiles of 128 x 256, else
+    # 192 x 256 tiles while they fit one wave, else 256 x 256
+    p = tlg.plan(3072, 3072, 3072)  # 144 tiles of 256 x 256, 288 of 128 x 256, 192 of 192 x 256
+    assert p["config_name"] == "pipe16_192x256x64_w2x2_s2_a3_sp6" and p["grid"] == 192
+    p = tlg.plan(2560, 2560, 2560)  # 200 tiles of 128 x 256
+    assert p["config_name"] == "pipe16_128x256x64_w1x4_s3_a3" and p["grid"] == 200
+    p = tlg.plan(2560, 2560, 2568)  # a K tail: the 32 x 32 x 16 half tiles
+    assert p["config_name"] == "pipe_128x256x64_w1x4_s3" and p["grid"] == 200
+    assert tlg.plan(8192, 1024, 4096)["config_name"] == "pipe16_128x256x64_w1x4_s3_a3"  # 256 tiles of 128 x 256
+    assert tlg.plan(4096, 3072, 4096)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"  # 264 of 192 x 256
+    assert tlg.plan(2048, 2048, 2048)["variant_name"] == "tiled_dma"  # 128 tiles of 128 x 256
     # forced 16 x 16 x 32 tiles take any K and N (whole stages, then a masked
     # stage and a zero-padded block); they refuse a transposed B
     assert tlg.plan(300, 264, 200, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10)["config_name"] == \

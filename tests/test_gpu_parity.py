@@ -577,7 +577,7 @@ def test_invalid_arguments_enqueue_nothing(dev):
     assert torch.all(C == 7.0)
 
 
-@pytest.mark.parametrize("config", list(range(10, 26)))
+@pytest.mark.parametrize("config", list(range(10, 28)))
 @pytest.mark.parametrize("shape", [(300, 264, 192), (513, 520, 64), (1024, 1032, 1024), (256, 256, 64), (257, 8, 4096),
                                    (200, 264, 128), (129, 1000, 320), (512, 768, 2048),
                                    (300, 264, 200), (513, 520, 72), (301, 259, 203), (256, 256, 8), (257, 9, 4104),

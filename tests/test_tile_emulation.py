@@ -220,8 +220,8 @@ def test_mx_tiles_match_oracle_integer(emu, fmt, config, shape):
 
 
 # the 16 x 16 x 32 pipelined kernel: four waves of 128 x 128 (20), the 128 x 256
-# half tiles (21), eight waves of 128 x 64 (22)
-PIPE16_CONFIGS = [20, 21, 22]
+# half tiles (21), eight waves of 128 x 64 (22), 192 x 256 tiles (23)
+PIPE16_CONFIGS = [20, 21, 22, 23]
 PIPE16_SHAPES = [(256, 256, 64), (300, 264, 192), (200, 264, 200), (130, 300, 203), (64, 256, 40), (257, 9, 520),
                  (1, 8, 8), (513, 40, 136)]
 

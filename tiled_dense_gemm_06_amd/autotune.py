@@ -57,7 +57,7 @@ def candidates(tlg, M, N, K):
     """(variant, config, splits) triples the library accepts for this shape."""
     out = []
     trials = [(tlg.TLG_VARIANT_AUTO, -1, 0)]
-    trials += [(tlg.TLG_VARIANT_TILED_PIPE, c, 0) for c in range(26)]
+    trials += [(tlg.TLG_VARIANT_TILED_PIPE, c, 0) for c in range(28)]
     trials += [(tlg.TLG_VARIANT_TILED_DMA, c, 0) for c in range(5)]
     if M <= 64:
         # two-kernel split-K (0, 1), stream-K tiles (2), strips with 1..8

@@ -309,10 +309,32 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
         // and so does one wave of tiles with a nearly empty second one (272
         // tiles: 4096x4104x4096 174.9 vs 183.9, 4096x4352x4096 173.2 vs
         // 178.0).
+        //
+        // With fewer than 256 tiles of 256 x 256 the CUs go part idle, and
+        // smaller tiles that fill them win (interleaved medians, us): 128 x 256
+        // tiles when they number 129 to 256 (2560^3 41.3 vs 48.0 on the
+        // 128 x 128 direct-to-LDS tiles, 2816^3 47.7 vs 60.8, 1536x4096x4096
+        // 60.3 vs 73.3, 2048x4096x4096 67.9 vs 90.9 on 256 x 256,
+        // 1024x8192x4096 66.9 vs 94.7; the 16 x 16 x 32 form where it
+        // serves, within 5 % of the 32 x 32 x 16 one and up to 13 % ahead of
+        // it), else 192 x 256 tiles while they fit one wave (3072^3 66.9 vs
+        // 73.4, 2560x4096x4096 85.7 vs 93.3; 192 x 256 from 257 tiles up
+        // loses, 4096x3072x4096 143.9 vs 96.6).
         const int64_t tiles256 = ceil_div(p.M, 256) * ceil_div(p.N, 256);
+        const int64_t tiles_half = ceil_div(p.M, 128) * ceil_div(p.N, 256);
+        const int64_t tiles192 = ceil_div(p.M, 192) * ceil_div(p.N, 256);
+        const bool k64 = p.K % 64 == 0 && p.N % 8 == 0 && !p.trans_b;
         const bool use16 = p.N % 8 == 0 && !p.trans_b && (p.K % 64 == 0 || tiles256 >= 256) &&
                            !(tiles256 > 256 && tiles256 < 320);
-        const int cfg = config >= 0 ? config : use16 ? tlg::PIPE16_256x256x64_A3_SP8 : tlg::PIPE_256x256x64_W8_A3_EARLY;
+        int cfg = config;
+        if (cfg < 0) {
+            if (tiles256 < 256 && tiles_half > 128 && tiles_half <= 256)
+                cfg = k64 ? tlg::PIPE16_128x256x64_A3 : tlg::PIPE_128x256x64;
+            else if (k64 && tiles256 >= 128 && tiles256 < 256 && tiles192 <= 256)
+                cfg = tlg::PIPE16_192x256x64_A3_SP6;
+            else
+                cfg = use16 ? tlg::PIPE16_256x256x64_A3_SP8 : tlg::PIPE_256x256x64_W8_A3_EARLY;
+        }
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
         const bool shape_ok = cfg < tlg::PIPE16_FIRST || !p.trans_b;

@@ -424,6 +424,9 @@ using Pipe16w4B3 = TileShape16<256, 256, 64, 2, 2, 3>;  // three B buffers
 using Pipe16h = TileShape16<128, 256, 64, 1, 4, 3>;
 // eight waves of 128 x 64 (two per SIMD, 128 accumulators each)
 using Pipe16w8 = TileShape16<256, 256, 64, 2, 4, 2>;
+// 192 x 256 tiles, four waves of 96 x 128 (14 loads per wave and stage over
+// a 96-slot step)
+using Pipe16t = TileShape16<192, 256, 64, 2, 2, 2>;
 
 template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
 static hipError_t launch_pipe16_t(const Problem &p, hipStream_t stream) {
@@ -473,6 +476,8 @@ hipError_t launch_tiled_pipe16(int config, const Problem &p, hipStream_t stream)
         case PIPE16_256x256x64_W8_A3_SP8: return launch_pipe16_t<Pipe16w8, 8, 1, 3, false>(p, stream);
         case PIPE16_256x256x64_W8_A3_SP4: return launch_pipe16_t<Pipe16w8, 4, 1, 3, false>(p, stream);
         case PIPE16_256x256x64_W8_A3_EARLY_SP6: return launch_pipe16_t<Pipe16w8, 6, 1, 3, true>(p, stream);
+        case PIPE16_192x256x64_A3_SP6: return launch_pipe16_t<Pipe16t, 6, 1, 3, false>(p, stream);
+        case PIPE16_192x256x64_A3_SP7: return launch_pipe16_t<Pipe16t, 7, 1, 3, false>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -384,6 +384,8 @@ const TileConfig kPipeConfigs[PIPE_CONFIGS] = {
     {256, 256, 64, 512, 2, "pipe16_256x256x64_w2x4_s2_a3_sp8"},
     {256, 256, 64, 512, 2, "pipe16_256x256x64_w2x4_s2_a3_sp4"},
     {256, 256, 64, 512, 2, "pipe16_256x256x64_w2x4_s2_a3_early_sp6"},
+    {192, 256, 64, 256, 2, "pipe16_192x256x64_w2x2_s2_a3_sp6"},
+    {192, 256, 64, 256, 2, "pipe16_192x256x64_w2x2_s2_a3_sp7"},
 };
 
 template <class S, bool BT>

@@ -88,7 +88,11 @@ enum PipeConfig {
     PIPE16_256x256x64_W8_A3_SP8 = 23,
     PIPE16_256x256x64_W8_A3_SP4 = 24,
     PIPE16_256x256x64_W8_A3_EARLY_SP6 = 25,
-    PIPE_CONFIGS = 26
+    // 192 x 256 tiles, four waves of 96 x 128: a third more tiles than
+    // 256 x 256 where those leave CUs idle
+    PIPE16_192x256x64_A3_SP6 = 26,
+    PIPE16_192x256x64_A3_SP7 = 27,
+    PIPE_CONFIGS = 28
 };
 
 // wave-role (ping-pong) schedule: two groups of waves alternate between
