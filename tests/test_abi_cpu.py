@@ -73,9 +73,14 @@ def test_plan_shapes_of_the_workloads():
     assert tlg.plan(4096, 4096, 4104)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
     assert tlg.plan(8192, 8192, 8200)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
     # otherwise the eight-wave 32 x 32 x 16 tiles: a K tail below 256 tiles,
-    # one wave with a nearly empty second (272 tiles), N not a multiple of 8
+    # N not a multiple of 8
     assert tlg.plan(3072, 3072, 3080)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
-    assert tlg.plan(4096, 4104, 4096)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
+    # tile height by rounds x relative tile time: 272 tiles of 256 x 256 take
+    # two rounds, 374 of 192 x 256 two cheaper ones; 576 and 768 take three
+    # each; 400 of 256 x 256 two rounds against three of 192 x 256
+    assert tlg.plan(4096, 4104, 4096)["config_name"] == "pipe16_192x256x64_w2x2_s2_a3_sp6"
+    assert tlg.plan(6144, 6144, 6144)["config_name"] == "pipe16_192x256x64_w2x2_s2_a3_sp6"
+    assert tlg.plan(5120, 5120, 5120)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
     assert tlg.plan(4096, 4100, 4096, aligned=True, ldb=4104, ldc=4104)["config_name"] == \
         "pipe_256x256x64_w2x4_s2_a3_early"
     assert tlg.plan(8192, 8192, 8192, trans_b=True)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"

@@ -31,9 +31,10 @@ import time
 SHAPES = [
     # squares
     (512, 512, 512), (1024, 1024, 1024), (2048, 2048, 2048), (3072, 3072, 3072), (4096, 4096, 4096),
-    (6144, 6144, 6144), (8192, 8192, 8192),
+    (6144, 6144, 6144), (8192, 8192, 8192), (2560, 2560, 2560), (2816, 2816, 2816),
     # rectangles
     (4096, 14336, 4096), (14336, 4096, 4096), (2048, 8192, 1024), (8192, 2048, 8192), (1024, 4096, 16384),
+    (1024, 8192, 4096), (2560, 4096, 4096),
     # skinny M
     (1, 4096, 4096), (16, 14336, 4096), (32, 14336, 4096), (64, 14336, 4096), (16, 4096, 14336),
     (48, 4096, 14336), (16, 2048, 4096), (8, 8192, 8192), (64, 4096, 8192), (48, 1024, 1024), (48, 1024, 1536),

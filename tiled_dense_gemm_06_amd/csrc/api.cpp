@@ -306,34 +306,56 @@ tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int
         // 806.9 vs 888.8, 4096x4096x4104 114.7 vs 119.6, 6144x6144x6152
         // 420.4 vs 442.9); below 256 tiles a K tail favours the 32 x 32 x 16
         // tiles (3072x3072x3080 77.0 vs 79.7, 5000x3000x2000 65.0 vs 70.2),
-        // and so does one wave of tiles with a nearly empty second one (272
-        // tiles: 4096x4104x4096 174.9 vs 183.9, 4096x4352x4096 173.2 vs
-        // 178.0).
+        // and so does one round of 256 x 256 tiles with a nearly empty second
+        // one (272 tiles: 4096x4104x4096 174.9 vs 183.9, 4096x4352x4096
+        // 173.2 vs 178.0; with K in whole stages such shapes take 192 x 256
+        // tiles, below: 155.3).
         //
-        // With fewer than 256 tiles of 256 x 256 the CUs go part idle, and
-        // smaller tiles that fill them win (interleaved medians, us): 128 x 256
-        // tiles when they number 129 to 256 (2560^3 41.3 vs 48.0 on the
-        // 128 x 128 direct-to-LDS tiles, 2816^3 47.7 vs 60.8, 1536x4096x4096
-        // 60.3 vs 73.3, 2048x4096x4096 67.9 vs 90.9 on 256 x 256,
-        // 1024x8192x4096 66.9 vs 94.7; the 16 x 16 x 32 form where it
-        // serves, within 5 % of the 32 x 32 x 16 one and up to 13 % ahead of
-        // it), else 192 x 256 tiles while they fit one wave (3072^3 66.9 vs
-        // 73.4, 2560x4096x4096 85.7 vs 93.3; 192 x 256 from 257 tiles up
-        // loses, 4096x3072x4096 143.9 vs 96.6).
+        // Tile height by waves of work-groups: a launch takes ceil(tiles /
+        // CUs) rounds of one work-group per CU, each as long as one tile, so
+        // the choice among 256 x 256, 192 x 256 and 128 x 256 tiles minimises
+        // rounds x the tile's relative time. Relative times measured per
+        // tile against 256 x 256 (area over efficiency): 192 x 256 0.9375
+        // (3072^3 66.9 vs 73.4 us in one round each; 6144^3, three rounds
+        // each, 380.9 vs 402.2), 128 x 256 0.75 (2048x4096x4096 67.9 vs
+        // 90.9). So 128 x 256 where it fills one round that 256 x 256 leaves
+        // part idle (2560^3 41.3 vs 48.0 on the 128 x 128 direct-to-LDS
+        // tiles, 2816^3 47.7 vs 60.8, 1024x8192x4096 66.9 vs 94.7), 192 x
+        // 256 where its rounds stay as few (2560x4096x4096 85.7 vs 93.3),
+        // 256 x 256 otherwise (4096x3072x4096: 96.6, against 143.9 on two
+        // rounds of 192 x 256). The 128 x 256 tiles are the 16 x 16 x 32
+        // ones where those serve (within 5 % of the 32 x 32 x 16 ones, up to
+        // 13 % ahead); the 192 x 256 tiles exist in that form only. A form
+        // with fewer than 128 tiles of its own is not taken (the
+        // direct-to-LDS tiles then serve), nor a smaller form at 128 tiles
+        // (2048^3: 32.1 us against 29.9 on the 128 x 128 direct-to-LDS tiles).
         const int64_t tiles256 = ceil_div(p.M, 256) * ceil_div(p.N, 256);
-        const int64_t tiles_half = ceil_div(p.M, 128) * ceil_div(p.N, 256);
-        const int64_t tiles192 = ceil_div(p.M, 192) * ceil_div(p.N, 256);
         const bool k64 = p.K % 64 == 0 && p.N % 8 == 0 && !p.trans_b;
         const bool use16 = p.N % 8 == 0 && !p.trans_b && (p.K % 64 == 0 || tiles256 >= 256) &&
                            !(tiles256 > 256 && tiles256 < 320);
         int cfg = config;
         if (cfg < 0) {
-            if (tiles256 < 256 && tiles_half > 128 && tiles_half <= 256)
-                cfg = k64 ? tlg::PIPE16_128x256x64_A3 : tlg::PIPE_128x256x64;
-            else if (k64 && tiles256 >= 128 && tiles256 < 256 && tiles192 <= 256)
-                cfg = tlg::PIPE16_192x256x64_A3_SP6;
-            else
-                cfg = use16 ? tlg::PIPE16_256x256x64_A3_SP8 : tlg::PIPE_256x256x64_W8_A3_EARLY;
+            struct Cand {
+                int cfg;
+                int bm;
+                double rel;
+            };
+            const Cand cands[3] = {
+                {use16 ? tlg::PIPE16_256x256x64_A3_SP8 : tlg::PIPE_256x256x64_W8_A3_EARLY, 256, 1.0},
+                {k64 ? tlg::PIPE16_192x256x64_A3_SP6 : -1, 192, 0.9375},
+                {k64 ? tlg::PIPE16_128x256x64_A3 : tlg::PIPE_128x256x64, 128, 0.75}};
+            double best = 0.0;
+            cfg = cands[0].cfg;
+            for (const Cand &c : cands) {
+                if (c.cfg < 0) continue;
+                const int64_t t = ceil_div(p.M, c.bm) * ceil_div(p.N, 256);
+                if (t <= 128 && c.bm != 256) continue;
+                const double score = (double)ceil_div(t, cus > 0 ? cus : 256) * c.rel;
+                if (best == 0.0 || score < best) {
+                    best = score;
+                    cfg = c.cfg;
+                }
+            }
         }
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         const int64_t tiles = ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn);
