@@ -93,8 +93,11 @@ tlg_status tlg_destroy(tlg_handle h);
  * nothing would be read or written through them. Returns
  * TLG_ERROR_INVALID_VALUE (nothing enqueued) for a NULL handle, negative
  * sizes, a leading dimension below the row width, a needed NULL pointer or a
- * pointer that is not 2-byte aligned; TLG_ERROR_HIP if a launch fails.
- * Device faults surface when the caller synchronises. */
+ * pointer that is not 2-byte aligned; TLG_ERROR_NOT_SUPPORTED (nothing
+ * enqueued) when M, N or K exceeds 2^31 - 1024 or the launch would need more
+ * than 2^31 - 1 work-groups (an output of more than 2^45 elements);
+ * TLG_ERROR_HIP if a launch fails. Device faults surface when the caller
+ * synchronises. */
 tlg_status tlg_gemm_relu(tlg_handle h, int64_t M, int64_t N, int64_t K,
                          const void *A, int64_t lda,
                          const void *B, int64_t ldb,

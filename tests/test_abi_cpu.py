@@ -400,3 +400,22 @@ def test_noalloc_entry_point_checks_arguments_without_a_gpu():
            (4, 4, 4, A16 + 1, 4, A16, 4, A16, 4), (4, 4, 4, A16, 4, A16, 4, A16, 3)]
     for args in bad:
         assert nat.tlg_gemm_relu_noalloc(*args, 0) == nat.TLG_ERROR_INVALID_VALUE, args
+
+
+def test_grids_beyond_int32_are_refused():
+    """Every kernel computes its tile indices in 32-bit integers, so a plan
+    that would need more than INT32_MAX work-groups is refused (only an
+    output of more than 2^45 elements asks for one), while the largest
+    dimensions the ABI accepts still plan: 2^31 - 1024 rows in 256 x 256
+    tiles, 2^31 - 1024 columns in 128 x 128 general tiles."""
+    big = (1 << 31) - 1024
+    for bt in (False, True):
+        for shape in [(1 << 24, 1 << 24, 1), (big, big, 1)]:
+            with pytest.raises(tlg.TlgError) as e:
+                tlg.plan(*shape, trans_b=bt)
+            assert e.value.status == nat.TLG_ERROR_NOT_SUPPORTED
+    assert tlg.plan(1 << 22, 1 << 22, 64)["grid"] == 1 << 30
+    p = tlg.plan(big, 8, 8)
+    assert p["variant_name"] == "tiled_pipe" and p["grid"] == (big + 255) // 256
+    p = tlg.plan(1, big, 1)
+    assert p["variant_name"] == "tiled_general" and p["grid"] == (big + 127) // 128

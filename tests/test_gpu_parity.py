@@ -519,6 +519,63 @@ def test_degenerate_sizes(dev):
             assert np.array_equal(bits(run(A, B, dev, variant=v)), oracle.gemm_relu(A, B)), (M, N, K, v)
 
 
+MAX_DIM = (1 << 31) - 1024  # the largest M, N or K the ABI accepts
+
+
+def _int_pattern(idx, j, dev):
+    """Integer values in {-2..2}: ((i mod 5) + 2 j) mod 5 - 2 for row (or
+    column) indices idx and the other index j, on the device."""
+    return (((idx % 5)[:, None] + 2 * j[None, :]) % 5 - 2).to(torch.float16)
+
+
+@pytest.mark.parametrize("case", ["max_M", "max_N"])
+def test_maximum_dimensions(dev, case):
+    """M or N at the largest value the ABI accepts (2^31 - 1024), integer
+    inputs, the default plan: 2^31 - 1024 rows in 256 x 256 tiles (8.4 M
+    work-groups, tile row offsets up to 2^31) or 2^31 - 1024 columns in
+    general tiles (16.8 M work-groups, B rows too long for 32-bit in-tile
+    offsets, so every chunk is gathered through 64-bit addresses). Sampled
+    rows (or columns), among them the first and the last tiles, bit-exact
+    against the oracle; the inputs are built on the device in pieces."""
+    print(f"maximum dimensions {case}", flush=True)
+    CH = 1 << 25
+    if case == "max_M":
+        M, N, K = MAX_DIM, 8, 8
+        kk = torch.arange(K, device=dev, dtype=torch.int64)
+        A = torch.empty((M, K), dtype=torch.float16, device=dev)
+        for r0 in range(0, M, CH):
+            r1 = min(M, r0 + CH)
+            A[r0:r1] = _int_pattern(torch.arange(r0, r1, device=dev, dtype=torch.int64), kk, dev)
+        Bh = wl.make_random(K, N, K, seed=5, kind="integer")[1]
+        C = tlg.gemm_relu(A, to_dev(Bh, dev))
+        torch.cuda.synchronize()
+        rows = np.array(sorted({0, 1, 255, 256, 257, M // 2, M - 1025, M - 1024, M - 257, M - 256, M - 2, M - 1} |
+                               set(np.random.default_rng(1).integers(0, M, 40).tolist())))
+        ri = torch.from_numpy(rows).to(dev)
+        got = C.index_select(0, ri).cpu().numpy().view(np.uint16)
+        Ah = A.index_select(0, ri).cpu().numpy()
+        want = oracle.gemm_relu(Ah, Bh)
+    else:
+        M, N, K = 1, MAX_DIM, 1
+        B = torch.empty((K, N), dtype=torch.float16, device=dev)
+        one = torch.zeros(1, device=dev, dtype=torch.int64)
+        for c0 in range(0, N, CH):
+            c1 = min(N, c0 + CH)
+            B[0, c0:c1] = _int_pattern(torch.arange(c0, c1, device=dev, dtype=torch.int64), one, dev)[:, 0]
+        Ah = np.full((1, 1), 2.0, dtype=np.float16)
+        C = tlg.gemm_relu(to_dev(Ah, dev), B)
+        torch.cuda.synchronize()
+        cols = np.array(sorted({0, 1, 127, 128, N // 2, N - 129, N - 128, N - 2, N - 1} |
+                               set(np.random.default_rng(2).integers(0, N, 40).tolist())))
+        ci = torch.from_numpy(cols).to(dev)
+        got = C.index_select(1, ci).cpu().numpy().view(np.uint16)
+        want = oracle.gemm_relu(Ah, B.index_select(1, ci).cpu().numpy())
+    print(f"  plan {tlg.plan(M, N, K)['config_name']}", flush=True)
+    assert np.array_equal(got, want), case
+    del C
+    torch.cuda.empty_cache()
+
+
 def test_worked_examples_on_gpu(dev):
     """The hand-worked fixtures (overflow to inf, subnormal outputs, ties) through the naive and tiled paths."""
     from test_oracle_pins import _parse_worked

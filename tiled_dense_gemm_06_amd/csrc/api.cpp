@@ -147,8 +147,22 @@ bool choose_splits(const tlg::Problem &p, const tlg::TileConfig &tc, int32_t for
 // A forced tile configuration index must exist for its variant.
 bool config_ok(int32_t config, int count) { return config < 0 || config < count; }
 
+// Every kernel takes one work-group per grid entry and computes its tile
+// indices in 32-bit integers, so a plan whose grid exceeds INT32_MAX (only
+// an output of more than 2^45 elements can ask for one) is refused.
+tlg_status grid_fits(tlg_status st, const tlg_plan_info *o) {
+    return st == TLG_SUCCESS && o->grid > 0x7fffffff ? TLG_ERROR_NOT_SUPPORTED : st;
+}
+
+tlg_status plan_select(const tlg::Problem &p, int32_t variant, int32_t config, int32_t splits, int64_t cap, int cus,
+                       tlg_plan_info *o, int64_t *k_split_out);
 tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int32_t splits, int64_t cap, int cus,
                      tlg_plan_info *o, int64_t *k_split_out) {
+    return grid_fits(plan_select(p, variant, config, splits, cap, cus, o, k_split_out), o);
+}
+
+tlg_status plan_select(const tlg::Problem &p, int32_t variant, int32_t config, int32_t splits, int64_t cap, int cus,
+                       tlg_plan_info *o, int64_t *k_split_out) {
     cap -= kCounterBytes;
     *k_split_out = 0;
     if (variant < TLG_VARIANT_AUTO || variant > TLG_VARIANT_PINGPONG) return TLG_ERROR_INVALID_VALUE;
@@ -521,7 +535,11 @@ constexpr int kSquareDmaConfigs = 3;
 // eight-wave pipelined 256 x 256 kernel
 constexpr int kGroupedPipe = kSquareDmaConfigs;
 
+tlg_status plan_bt_select(const tlg::Problem &p, int32_t variant, int32_t config, tlg_plan_info *o);
 tlg_status plan_bt(const tlg::Problem &p, int32_t variant, int32_t config, tlg_plan_info *o) {
+    return grid_fits(plan_bt_select(p, variant, config, o), o);
+}
+tlg_status plan_bt_select(const tlg::Problem &p, int32_t variant, int32_t config, tlg_plan_info *o) {
     if (variant != TLG_VARIANT_AUTO && variant != TLG_VARIANT_TILED_DMA && variant != TLG_VARIANT_TILED_PIPE &&
         variant != TLG_VARIANT_PINGPONG)
         return TLG_ERROR_INVALID_VALUE;
@@ -663,7 +681,11 @@ tlg_status check_args_mx(int32_t format, int64_t M, int64_t N, int64_t K, const 
     return TLG_SUCCESS;
 }
 
+tlg_status plan_mx_select(const tlg::MxProblem &p, int32_t config, tlg_plan_info *o);
 tlg_status plan_mx(const tlg::MxProblem &p, int32_t config, tlg_plan_info *o) {
+    return grid_fits(plan_mx_select(p, config, o), o);
+}
+tlg_status plan_mx_select(const tlg::MxProblem &p, int32_t config, tlg_plan_info *o) {
     if (config < -1 || config >= tlg::MX_CONFIGS) return TLG_ERROR_INVALID_VALUE;
     if (p.M == 0 || p.N == 0) {
         fill_info(o, TLG_VARIANT_NOOP, 0, nullptr, 1, 0, 0, 0);
