@@ -103,7 +103,23 @@ def test_plan_shapes_of_the_workloads():
     assert tlg.plan(48, 4096, 4096)["config_name"] == "splitk_waves_64x64x64_w2_s3"
     assert tlg.plan(64, 1024, 2048)["config_name"] == "splitk_waves_64x64x64_w2_s3"
     assert tlg.plan(48, 4096, 1024)["variant_name"] == "tiled_dma"
-    assert tlg.plan(65, 4096, 4096)["variant_name"] != "splitk"
+    # M > 64: no strips; with K >= 4096 and fewer 64 x 64 tiles than CUs, K
+    # split over 32 x 128 tiles and a second kernel's ordered sum
+    p = tlg.plan(65, 4096, 4096)
+    assert p["config_name"] == "splitk_32x128x64_w1x4_s4" and p["kernels"] == 2 and p["splits"] == 6
+    assert tlg.plan(65, 4096, 2048)["variant_name"] == "tiled_dma"
+    for shape, splits in [((512, 512, 4096), 8), ((1024, 512, 4096), 4), ((1024, 1024, 8192), 2),
+                          ((256, 256, 16384), 16)]:
+        p = tlg.plan(*shape)
+        assert p["config_name"] == "splitk_32x128x64_w1x4_s4" and p["splits"] == splits, shape
+        assert p["workspace_bytes"] == (64 << 10) + splits * shape[0] * shape[1] * 4 <= tlg.tlg_workspace_bytes()
+    assert tlg.plan(1024, 1024, 4096)["variant_name"] == "tiled_dma"  # a full round of 64 x 64 tiles
+    assert tlg.plan(512, 512, 4096, lda=4100)["variant_name"] == "tiled_dma"  # unaligned rows: no split
+    # fewer than 128 tiles of 256 x 256: the 32 x 32 x 16 128 x 256 tiles from 96 of them up
+    for shape, grid in [((2048, 2048, 2048), 128), ((1536, 2048, 4096), 96), ((2048, 2048, 8192), 128)]:
+        p = tlg.plan(*shape)
+        assert p["config_name"] == "pipe_128x256x64_w1x4_s3" and p["grid"] == grid, shape
+    assert tlg.plan(1280, 2048, 2048)["variant_name"] == "tiled_dma"  # 80 of them
     # unaligned (the split-K kernels load 16-byte pieces): tiles
     assert tlg.plan(48, 4100, 4096)["variant_name"] == "tiled_dma"
     p = tlg.plan(16, 2048, 4096)  # few strips: K split among work-groups too, up to the CUs
@@ -120,7 +136,8 @@ def test_plan_shapes_of_the_workloads():
     assert p["config_name"] == "pipe_128x256x64_w1x4_s3" and p["grid"] == 200
     assert tlg.plan(8192, 1024, 4096)["config_name"] == "pipe16_128x256x64_w1x4_s3_a3"  # 256 tiles of 128 x 256
     assert tlg.plan(4096, 3072, 4096)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"  # 264 of 192 x 256
-    assert tlg.plan(2048, 2048, 2048)["variant_name"] == "tiled_dma"  # 128 tiles of 128 x 256
+    # 128 tiles of 128 x 256: the 32 x 32 x 16 form
+    assert tlg.plan(2048, 2048, 2048)["config_name"] == "pipe_128x256x64_w1x4_s3"
     # forced 16 x 16 x 32 tiles take any K and N (whole stages, then a masked
     # stage and a zero-padded block); they refuse a transposed B
     assert tlg.plan(300, 264, 200, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10)["config_name"] == \

@@ -190,13 +190,18 @@ def test_strip64_shapes(dev, shape, parts):
 
 
 @pytest.mark.parametrize("shape", [(48, 4096, 14336), (64, 4096, 8192), (48, 4096, 4096), (64, 14336, 4096),
-                                   (1, 4096, 4096), (16, 2048, 4096), (3072, 3072, 3072)])
+                                   (1, 4096, 4096), (16, 2048, 4096), (3072, 3072, 3072),
+                                   (512, 512, 4096), (65, 4096, 4096), (896, 896, 8192), (256, 256, 16384),
+                                   (2048, 2048, 2048), (1536, 2048, 4096)])
 def test_planned_kernel_choice(dev, shape):
     """The default path on shapes whose kernel comes from the tuned table
     (48x4096x14336, 64x4096x8192) or from the heuristic's measured
     boundaries (stream-K, 64 x 64 tiles, strips split among work-groups, 256 x
-    256 tiles from 128 tiles up): full output against the oracle on integer
-    inputs (exact) and sampled rows on uniform inputs."""
+    256 tiles from 128 tiles up, K split over 32 x 128 tiles for long K and
+    few tiles, 128 x 256 tiles of the 32 x 32 x 16 form below 128 tiles of
+    256 x 256): full output against the oracle on integer inputs (exact;
+    sampled rows beyond 2^31 multiply-adds) and sampled rows on normal
+    inputs."""
     M, N, K = shape
     print(f"planned {shape}: {tlg.plan(M, N, K)['config_name']}", flush=True)
     rows = _sample_rows(M)

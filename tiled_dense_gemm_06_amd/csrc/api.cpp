@@ -218,7 +218,18 @@ tlg_status plan_select(const tlg::Problem &p, int32_t variant, int32_t config, i
     const bool strip64_fits = !strip_fits && p.M <= t64.bm && dma_ok_aligned(p, t64.bm, t64.bn, t64.bk) &&
                               ceil_div(p.N, t64.bn) <= 0x7fffffff;
     const bool few_tiles = p.M <= 64 && ceil_div(p.N, 64) * 2 < cus;
-    const bool auto_split = strip_fits || (strip64_fits ? p.K >= 2048 : few_tiles);
+    // M > 64 with long K and fewer 64 x 64 tiles than CUs: K split over
+    // 32 x 128 tiles, partials summed by a second kernel in ascending split
+    // order (interleaved, us: 512x512x4096 15.6 vs 23.2 on 64 x 64 tiles,
+    // 1024x512x4096 16.0 vs 22.8, 896x896x8192 36.1 vs 42.7, 1024x1024x8192
+    // 40.5 vs 44.2, 256x256x16384 15.8 vs 81.6; the vendor BLAS 19.4, 20.2,
+    // 40.4, 46.3, 31.2); not at K = 2048 (512x512x2048 15.5 vs 12.9) nor
+    // with a full round of tiles at K = 4096 (1024x1024x4096 24.7 vs 23.9)
+    const int64_t tiles64 = ceil_div(p.M, 64) * ceil_div(p.N, 64);
+    const tlg::TileConfig &ts0 = tlg::kSplitConfigs[tlg::SPLIT_32x128x64];
+    const bool long_k_split = p.M > 64 && p.K >= 4096 && (tiles64 < cus || (p.K >= 8192 && tiles64 <= cus)) &&
+                              dma_ok_aligned(p, ts0.bm, ts0.bn, ts0.bk);
+    const bool auto_split = strip_fits || (strip64_fits ? p.K >= 2048 : few_tiles) || long_k_split;
     if (variant == TLG_VARIANT_SPLITK || (variant == TLG_VARIANT_AUTO && auto_split && p.K >= 512)) {
         if (!config_ok(config, tlg::SPLIT_CONFIGS)) return TLG_ERROR_INVALID_VALUE;
         // K split among the waves of a work-group per column strip, when M
@@ -228,7 +239,10 @@ tlg_status plan_select(const tlg::Problem &p, int32_t variant, int32_t config, i
             const tlg::TileConfig &t0 = tlg::kStripConfig;
             const bool ok0 = p.M <= t0.bm && dma_ok_aligned(p, t0.bm, t0.bn, t0.bk) &&
                              ceil_div(p.N, t0.bn) <= 0x7fffffff;
-            cfg = ok0 ? tlg::SPLIT_WAVES_32x64x64 : strip64_fits ? tlg::SPLIT_WAVES_64x64x64 : tlg::SPLIT_STREAMK_32x128x64;
+            cfg = ok0            ? tlg::SPLIT_WAVES_32x64x64
+                  : strip64_fits ? tlg::SPLIT_WAVES_64x64x64
+                  : long_k_split ? tlg::SPLIT_32x128x64
+                                 : tlg::SPLIT_STREAMK_32x128x64;
         }
         if (tlg::is_strip_config(cfg)) {
             const tlg::TileConfig &ts = tlg::kStripConfigs[cfg - tlg::SPLIT_WAVES_32x64x64];
@@ -378,6 +392,19 @@ tlg_status plan_select(const tlg::Problem &p, int32_t variant, int32_t config, i
         // 128 x 128 tiles already (3072^3: 72 vs 101 us)
         if (shape_ok && dma_ok(p, tc.bm, tc.bn, tc.bk) && (variant == TLG_VARIANT_TILED_PIPE || tiles >= 128)) {
             fill_info(o, TLG_VARIANT_TILED_PIPE, cfg, &tc, 1, 1, tiles, 0);
+            return TLG_SUCCESS;
+        }
+        // Fewer: the 32 x 32 x 16 MFMA 128 x 256 tiles from 96 of them up
+        // (interleaved, us: 2048^3 24.7 vs 28.4 on 128 x 128 direct-to-LDS
+        // tiles and 27.4 on the 16 x 16 x 32 form, 2048x2048x8192 78.0 vs
+        // 97.2 and 87.1, 1536x2048x4096 41.4 vs 46.4 on 64 x 64 tiles,
+        // 1792x2048x2048 24.2 vs 27.9; the vendor BLAS 25.5, 77.7, 40.2,
+        // 24.5); at 60 tiles the 64 x 64 ones stay ahead (1280x1536x4096
+        // 32.0 vs 40.1)
+        const tlg::TileConfig &th = tlg::kPipeConfigs[tlg::PIPE_128x256x64];
+        const int64_t t_half = ceil_div(p.M, th.bm) * ceil_div(p.N, th.bn);
+        if (variant == TLG_VARIANT_AUTO && tiles < 128 && t_half >= 96 && dma_ok(p, th.bm, th.bn, th.bk)) {
+            fill_info(o, TLG_VARIANT_TILED_PIPE, tlg::PIPE_128x256x64, &th, 1, 1, t_half, 0);
             return TLG_SUCCESS;
         }
         if (variant == TLG_VARIANT_TILED_PIPE) return TLG_ERROR_NOT_SUPPORTED;
