@@ -108,7 +108,7 @@ def test_plan_shapes_of_the_workloads():
     p = tlg.plan(65, 4096, 4096)
     assert p["config_name"] == "splitk_32x128x64_w1x4_s4" and p["kernels"] == 2 and p["splits"] == 6
     assert tlg.plan(65, 4096, 2048)["variant_name"] == "tiled_dma"
-    for shape, splits in [((512, 512, 4096), 8), ((1024, 512, 4096), 4), ((1024, 1024, 8192), 2),
+    for shape, splits in [((512, 512, 4096), 4), ((1024, 512, 4096), 4), ((1024, 1024, 8192), 2),
                           ((256, 256, 16384), 16)]:
         p = tlg.plan(*shape)
         assert p["config_name"] == "splitk_32x128x64_w1x4_s4" and p["splits"] == splits, shape

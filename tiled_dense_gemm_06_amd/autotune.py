@@ -40,6 +40,8 @@ SHAPES = [
     (48, 4096, 14336), (16, 2048, 4096), (8, 8192, 8192), (64, 4096, 8192), (48, 1024, 1024), (48, 1024, 1536),
     (64, 1024, 2048),
     (128, 4096, 4096), (256, 8192, 4096),
+    # few tiles, long K
+    (512, 512, 4096), (256, 256, 16384), (1024, 1024, 8192), (1536, 2048, 4096), (2048, 2048, 8192),
     # ragged
     (3001, 2049, 1537), (1000, 1000, 1000), (777, 555, 333), (5000, 3000, 2000),
 ]
@@ -66,6 +68,9 @@ def candidates(tlg, M, N, K):
         # stream-K strips (10, 11)
         trials += [(tlg.TLG_VARIANT_SPLITK, 3, s) for s in (1, 2, 4, 8)]
         trials += [(tlg.TLG_VARIANT_SPLITK, c, 0) for c in (0, 1, 2) + tuple(range(4, 12))]
+    elif K >= 2048:
+        # the two-kernel split over 32 x 128 tiles with 2..16 parts
+        trials += [(tlg.TLG_VARIANT_SPLITK, 0, s) for s in (0, 2, 4, 8, 16)]
     for v, c, s in trials:
         try:
             p = tlg.plan(M, N, K, variant=v, config=c, splits=s)
