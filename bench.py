@@ -459,13 +459,17 @@ def main() -> int:
     if args.grouped:
         # the grouped call picks its tile by the total tile count of the blocks
         rows = [(w.M * g // args.grouped, w.M * (g + 1) // args.grouped) for g in range(args.grouped)]
-        # (the library's rule: the pipelined 256 x 256 kernel, grouped
-        # configuration 3, from 128 such tiles in total, else direct-to-LDS
-        # tiles 0..2 by tile count)
+        # (the library's rule: from 128 tiles of 256 x 256 in total the
+        # pipelined 256 x 256 kernel, grouped configuration 4 (16 x 16 x 32
+        # MFMA) for B not transposed, N % 8 == 0 and K % 64 == 0, else 3
+        # (32 x 32 x 16); below, direct-to-LDS tiles 0..2 by tile count)
         t256 = sum(-(-(r1 - r0) // 256) * -(-w.N // 256) for r0, r1 in rows)
         t128 = sum(-(-(r1 - r0) // 128) * -(-w.N // 128) for r0, r1 in rows)
-        gcfg = args.config if args.config >= 0 else (3 if t256 >= 128 else 1 if t128 >= 192 else 2)
-        name = (tlg.tlg_plan_config_name(tlg.TLG_VARIANT_TILED_PIPE, 7) if gcfg == 3
+        pipe16_ok = not args.trans_b and w.N % 8 == 0 and w.K % 64 == 0
+        gcfg = args.config if args.config >= 0 else ((4 if pipe16_ok else 3) if t256 >= 128 else
+                                                     1 if t128 >= 192 else 2)
+        name = (tlg.tlg_plan_config_name(tlg.TLG_VARIANT_TILED_PIPE, 17) if gcfg == 4
+                else tlg.tlg_plan_config_name(tlg.TLG_VARIANT_TILED_PIPE, 7) if gcfg == 3
                 else tlg.tlg_plan_config_name(tlg.TLG_VARIANT_TILED_DMA, gcfg))
         plan = {"config_name": name, "variant_name": "grouped", "splits": 1}
     else:

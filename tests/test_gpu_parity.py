@@ -417,6 +417,35 @@ def test_grouped_large(dev, trans_b):
         assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
 
 
+@pytest.mark.parametrize("config", [-1, 4])
+def test_grouped_pipe16(dev, config):
+    """Problems with B not transposed and N a multiple of 8 in one launch of
+    the 16 x 16 x 32 pipelined kernel: the library's choice from 128 tiles of
+    256 x 256 when every K is whole 64-deep stages, and forced (4) with K
+    tails too; ragged M, an empty problem; bit-exact per problem, guard bands
+    intact."""
+    shapes = [(2048, 2048, 256), (1000, 2048, 512), (1031, 1800, 128), (0, 64, 64), (257, 264, 64)]
+    if config == 4:
+        shapes += [(300, 264, 200), (129, 256, 1000), (64, 8, 8)]
+    probs, As, Bs, bigs, outs = [], [], [], [], []
+    for i, (M, N, K) in enumerate(shapes):
+        A, B = wl.make_random(M, N, K, seed=300 + i, kind="integer_pos")
+        probs.append((A, B))
+        As.append(to_dev(A, dev))
+        Bs.append(to_dev(B, dev))
+        big = torch.full((M + 2, N + 8), float("nan"), dtype=torch.float16, device=dev)
+        bigs.append(big)
+        outs.append(big[:M, :N])
+    assert sum(-(-M // 256) * -(-N // 256) for M, N, _ in shapes) >= 128
+    tlg.gemm_relu_grouped(As, Bs, outs, config=config)
+    torch.cuda.synchronize()
+    refs = oracle.gemm_relu_grouped(probs)
+    for (M, N, K), big, ref in zip(shapes, bigs, refs):
+        allb = bits(big)
+        assert np.array_equal(allb[:M, :N], ref), (M, N, K)
+        assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+
+
 def test_grouped_rejects_bad_calls(dev):
     """Too many problems, an ld below the row width, a mixed device: errors, nothing enqueued."""
     A = torch.ones((8, 8), dtype=torch.float16, device=dev)

@@ -561,6 +561,8 @@ constexpr int kSquareDmaConfigs = 3;
 // grouped calls: configurations 0..2 are those direct-to-LDS ones, 3 the
 // eight-wave pipelined 256 x 256 kernel
 constexpr int kGroupedPipe = kSquareDmaConfigs;
+// 4: the 16 x 16 x 32 pipelined 256 x 256 kernel (B not transposed)
+constexpr int kGroupedPipe16 = kGroupedPipe + 1;
 
 tlg_status plan_bt_select(const tlg::Problem &p, int32_t variant, int32_t config, tlg_plan_info *o);
 tlg_status plan_bt(const tlg::Problem &p, int32_t variant, int32_t config, tlg_plan_info *o) {
@@ -647,7 +649,7 @@ tlg_status run_grouped(tlg_handle h, int32_t config, int32_t count, const tlg_ge
     tlg_status st = device_ok(h);
     if (st != TLG_SUCCESS) return st;
     if (count < 0 || count > TLG_GROUP_MAX || (trans_b != 0 && trans_b != 1)) return TLG_ERROR_INVALID_VALUE;
-    if (config < -1 || config > kGroupedPipe) return TLG_ERROR_INVALID_VALUE;
+    if (config < -1 || config > kGroupedPipe16) return TLG_ERROR_INVALID_VALUE;
     if (count == 0) return TLG_SUCCESS;
     if (!descs) return TLG_ERROR_INVALID_VALUE;
     tlg::Problem ps[TLG_GROUP_MAX];
@@ -666,10 +668,22 @@ tlg_status run_grouped(tlg_handle h, int32_t config, int32_t count, const tlg_ge
         t128 += ceil_div(d.M, 128) * ceil_div(d.N, 128);
     }
     if (n == 0) return TLG_SUCCESS;
-    // the pipelined 256 x 256 kernel from the same total tile count as a
-    // single call (128 tiles of 256 x 256), when every problem can take it
-    bool pipe = config == kGroupedPipe || (config == -1 && t256 >= 128);
-    if (pipe) {
+    // the pipelined 256 x 256 kernels from the same total tile count as a
+    // single call (128 tiles of 256 x 256), when every problem can take them:
+    // the 16 x 16 x 32 form for B not transposed, N a multiple of 8 and K in
+    // whole 64-deep stages (8192^3 as 8 row blocks: 855.0-858.7 us against
+    // 882.4-887.1 on the 32 x 32 x 16 form), else the 32 x 32 x 16 form
+    const bool auto_pipe = config == -1 && t256 >= 128;
+    if (config == kGroupedPipe16 || auto_pipe) {
+        const tlg::TileConfig &tp = tlg::kPipeConfigs[tlg::PIPE16_256x256x64_A3_SP8];
+        bool ok = t256 <= 0x7fffffff && !trans_b;
+        for (int i = 0; i < n && ok; ++i)
+            ok = ps[i].N % 8 == 0 && (ps[i].K % tp.bk == 0 || config == kGroupedPipe16) &&
+                 dma_ok(ps[i], tp.bm, tp.bn, tp.bk);
+        if (ok) return tlg::launch_tiled_pipe16_grouped(ps, n, stream) == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
+        if (config == kGroupedPipe16) return TLG_ERROR_NOT_SUPPORTED;
+    }
+    if (config == kGroupedPipe || auto_pipe) {
         const tlg::TileConfig &tp = tlg::kPipeConfigs[tlg::PIPE_256x256x64_W8_A3_EARLY];
         bool ok = t256 <= 0x7fffffff;
         for (int i = 0; i < n && ok; ++i)

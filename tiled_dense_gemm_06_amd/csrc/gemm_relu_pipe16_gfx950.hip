@@ -417,6 +417,21 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe16(const KArgs a) {
     pipe16_tile<S, SPACING, DOFF, ASTAGES, EARLY>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
 }
 
+// Several problems in one launch: work-group ids are dealt to the XCDs as in
+// the single-problem kernel, then split by problem in order (tile_start holds
+// the running tile counts), each problem's tiles in its own grouped order.
+template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
+__global__ __launch_bounds__(S::NT) void k_tiled_pipe16_grouped(const GroupArgs g) {
+    __shared__ __attribute__((aligned(1024))) char smem[pipe16_lds_bytes<S, ASTAGES>()];
+    const int v = xcd_remap(blockIdx.x, g.tile_start[g.count]);
+    int p = 0;
+    while (p + 1 < g.count && v >= g.tile_start[p + 1]) ++p;
+    const KArgs &a = g.p[p];
+    int tm_idx, tn_idx;
+    grouped_tile(v - g.tile_start[p], a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
+    pipe16_tile<S, SPACING, DOFF, ASTAGES, EARLY>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
+}
+
 using Pipe16w4 = TileShape16<256, 256, 64, 2, 2, 2>;    // four waves of 128 x 128, two B buffers
 using Pipe16w4B3 = TileShape16<256, 256, 64, 2, 2, 3>;  // three B buffers
 // 128 x 256 tiles, four waves of 128 x 64: twice the tiles of 256 x 256 for
@@ -428,9 +443,8 @@ using Pipe16w8 = TileShape16<256, 256, 64, 2, 4, 2>;
 // a 96-slot step)
 using Pipe16t = TileShape16<192, 256, 64, 2, 2, 2>;
 
-template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
-static hipError_t launch_pipe16_t(const Problem &p, hipStream_t stream) {
-    if (p.trans_b) return hipErrorInvalidValue;
+template <class S>
+static KArgs pipe16_args(const Problem &p) {
     KArgs a;
     a.A = (const _Float16 *)p.A;
     a.B = (const _Float16 *)p.B;
@@ -448,8 +462,35 @@ static hipError_t launch_pipe16_t(const Problem &p, hipStream_t stream) {
     a.kmain = p.K % 8 == 0 && p.N % 8 == 0 ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
     a.tiles_m = (a.M + S::BM - 1) / S::BM;
     a.tiles_n = (a.N + S::BN - 1) / S::BN;
+    return a;
+}
+
+template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
+static hipError_t launch_pipe16_t(const Problem &p, hipStream_t stream) {
+    if (p.trans_b) return hipErrorInvalidValue;
+    const KArgs a = pipe16_args<S>(p);
     hipLaunchKernelGGL((k_tiled_pipe16<S, SPACING, DOFF, ASTAGES, EARLY>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
                        dim3(S::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+// The default configuration (four waves, loads every eight MFMA slots) over
+// up to kGroupMax problems, none with a transposed B.
+hipError_t launch_tiled_pipe16_grouped(const Problem *ps, int count, hipStream_t stream) {
+    using S = Pipe16w4;
+    static_assert(sizeof(GroupArgs) <= 4096, "kernel arguments");
+    if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
+    GroupArgs g;
+    g.count = count;
+    g.tile_start[0] = 0;
+    for (int i = 0; i < count; ++i) {
+        if (ps[i].trans_b) return hipErrorInvalidValue;
+        g.p[i] = pipe16_args<S>(ps[i]);
+        g.tile_start[i + 1] = g.tile_start[i] + g.p[i].tiles_m * g.p[i].tiles_n;
+    }
+    if (g.tile_start[count] == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_tiled_pipe16_grouped<S, 8, 1, 3, false>), dim3((unsigned)g.tile_start[count]), dim3(S::NT), 0,
+                       stream, g);
     return hipGetLastError();
 }
 

@@ -118,6 +118,9 @@ hipError_t launch_tiled_pipe16(int config, const Problem &p, hipStream_t stream)
 // count (1 .. kGroupMax) problems, all with the same trans_b, in one launch
 // of the eight-wave early-barrier pipelined kernel (each must pass its checks)
 hipError_t launch_tiled_pipe_grouped(const Problem *ps, int count, hipStream_t stream);
+// count (1 .. kGroupMax) problems, none with a transposed B, in one launch of
+// the default 16 x 16 x 32 pipelined configuration
+hipError_t launch_tiled_pipe16_grouped(const Problem *ps, int count, hipStream_t stream);
 hipError_t launch_pingpong(int config, const Problem &p, hipStream_t stream);
 // Stage 1 writes fp32 partials W[s][m][n] (M x N packed per split) for
 // splits s covering k in [s*k_split, (s+1)*k_split); stage 2 sums them in
