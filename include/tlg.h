@@ -199,10 +199,12 @@ int64_t tlg_noalloc_scratch_bytes(void);
 
 /* C = ReLU(A . Bt^T): Bt is the N x K fp16 row-major matrix (B transposed),
  * ldbt >= max(1, K); everything else as tlg_gemm_relu. B's tiles are loaded
- * and read like A's: by the pipelined kernel when the problem has at least
- * 128 output tiles of 256 x 256, else by the direct-to-LDS tiled kernel (tile
- * by tile count). TLG_ERROR_NOT_SUPPORTED when a tile's byte offsets exceed
- * 2 GB (e.g. ldbt * 256 * 2 >= 2^31); nothing is enqueued then. */
+ * and read like A's: by the pipelined kernel on 256 x 256 tiles when the
+ * problem has at least 128 of them, else on 128 x 256 tiles (16 x 16 x 32
+ * MFMA) when it has at least 192 of those, else by the direct-to-LDS tiled
+ * kernel (tile by tile count). Any K and N. TLG_ERROR_NOT_SUPPORTED when a
+ * tile's byte offsets exceed 2 GB (e.g. ldbt * 256 * 2 >= 2^31); nothing is
+ * enqueued then. */
 tlg_status tlg_gemm_relu_bt(tlg_handle h, int64_t M, int64_t N, int64_t K,
                             const void *A, int64_t lda,
                             const void *Bt, int64_t ldbt,
@@ -212,8 +214,9 @@ tlg_status tlg_gemm_relu_bt(tlg_handle h, int64_t M, int64_t N, int64_t K,
 /* tlg_gemm_relu_bt with a forced kernel family and tile configuration, for
  * tests and measurements: variant TLG_VARIANT_AUTO (then config must be -1),
  * TLG_VARIANT_TILED_DMA (configs 0..2) or TLG_VARIANT_TILED_PIPE (configs 2,
- * 4 and 7, the 256 x 256 ones with a third A buffer); config -1 lets the
- * library choose inside the family. */
+ * 4 and 7, the 256 x 256 ones with a third A buffer, and the 16 x 16 x 32
+ * MFMA tiles 17 (256 x 256), 21 (128 x 256) and 26 (192 x 256)); config -1
+ * lets the library choose inside the family. */
 tlg_status tlg_gemm_relu_bt_variant(tlg_handle h, int32_t variant, int32_t config, int64_t M, int64_t N, int64_t K,
                                     const void *A, int64_t lda,
                                     const void *Bt, int64_t ldbt,

@@ -325,15 +325,18 @@ void run_dma(const Problem &p, bool split, Errs &er, std::vector<int> &cover) {
 // frag_b16_lane), v_mfma_f32_16x16x32_f16 with its measured layouts, the K
 // tail (a masked stage, then a zero-padded 32-deep block) and the LDS-staged
 // epilogue (epi16_offset).
+// p.bt: B given transposed (N x K), its tile held like the A tile
+// (dma_bt16_chunk, p16_a_lane_bytes, frag_a16_lane over the rows n).
 template <class S>
 void run_pipe16(const Problem &p, Errs &er, std::vector<int> &cover) {
+    const bool bt = p.bt;
     const int tiles_m = (p.M + S::BM - 1) / S::BM, tiles_n = (p.N + S::BN - 1) / S::BN;
     const int nwg = tiles_m * tiles_n;
     std::vector<int> seen(nwg, 0);
     const int STAGE = S::A_BYTES + S::B_BYTES;
     std::vector<uint8_t> lds(STAGE);
     std::vector<int> lds_w(STAGE);
-    const int kmain = (p.K % 8 == 0 && p.N % 8 == 0) ? p.K : 8 * ((p.K - 1) / 8);
+    const int kmain = (p.K % 8 == 0 && (bt || p.N % 8 == 0)) ? p.K : 8 * ((p.K - 1) / 8);
     const int nk = kmain / S::BK;
     const long b_end = (long)(p.K - 1) * p.ldb + p.N;  // elements of B the caller owns
     // a global element read by a direct-to-LDS load, given by its logical
@@ -346,6 +349,14 @@ void run_pipe16(const Problem &p, Errs &er, std::vector<int> &cover) {
             return 0;
         }
         return p.A[idx];
+    };
+    // a transposed B: position (n, k), inside N and K's rows [0, kend)
+    auto read_bt = [&](long row, long col, long idx, int kend) -> uint16_t {
+        if (idx != row * p.ldb + col || row < 0 || row >= p.N || col < 0 || col >= kend) {
+            er.oob_global++;
+            return 0;
+        }
+        return p.B[idx];
     };
     auto read_b = [&](long row, long col, long idx, int kend) -> uint16_t {
         // past column N only when N is not a multiple of 8, then into the
@@ -374,7 +385,26 @@ void run_pipe16(const Problem &p, Errs &er, std::vector<int> &cover) {
             for (int w = 0; w < S::WAVES; ++w) {
                 const int wm0 = (w / S::WN) * S::WTM, wn0 = (w % S::WN) * S::WTN;
                 std::vector<float> bf((size_t)S::TN * 64 * 8), af((size_t)S::TM * 64 * 8);
-                for (int tn = 0; tn < S::TN; ++tn)
+                for (int tn = 0; bt && tn < S::TN; ++tn) {  // one 16-byte read per lane, as for A
+                    int addr[64];
+                    for (int l = 0; l < 64; ++l) {
+                        addr[l] = frag_a16_lane<S>(wn0, s & 1, l) + tn * 16 * S::RA;
+                        if (addr[l] != frag_a16_offset<S>(wn0, tn, s, l)) er.lds_oob++;
+                        if (addr[l] < 0 || addr[l] + 16 > S::B_BYTES || addr[l] % 16) er.lds_oob++;
+                    }
+                    for (int q = 0; q < 4; ++q) {  // 16 lanes x 16 bytes per LDS cycle
+                        int used[16] = {0};
+                        for (int l = 16 * q; l < 16 * q + 16; ++l)
+                            if (used[slot16(addr[l])]++) er.bank_conflict++;
+                    }
+                    for (int l = 0; l < 64; ++l)
+                        for (int e = 0; e < 8; ++e) {
+                            uint16_t v = 0;
+                            if (addr[l] >= 0 && addr[l] + 16 <= S::B_BYTES) memcpy(&v, &lds[S::A_BYTES + addr[l] + 2 * e], 2);
+                            bf[((size_t)tn * 64 + l) * 8 + e] = h2f(v);
+                        }
+                }
+                for (int tn = 0; !bt && tn < S::TN; ++tn)
                     for (int h = 0; h < 2; ++h) {
                         int addr[64];
                         for (int l = 0; l < 64; ++l) {
@@ -463,7 +493,24 @@ void run_pipe16(const Problem &p, Errs &er, std::vector<int> &cover) {
                             if (dst + 2 * e + 2 <= S::A_BYTES) memcpy(&lds[dst + 2 * e], &v, 2);
                         }
                     }
-                    for (int i = 0; i < S::DMA_B; ++i) {
+                    for (int i = 0; bt && i < S::DMA_B; ++i) {
+                        const int slab = w * S::DMA_B + i;
+                        const long base = (long)(n0 + slab * 8) * p.ldb + k0;  // the descriptor's base
+                        const long rows = (long)p.N - n0 - slab * 8;
+                        const long nrec = rows <= 0 ? 0 : rows * p.ldb * 2;
+                        const long off = (long)p16_a_lane_bytes<S>(lane, slab % 2, p.ldb);
+                        const int dst = S::A_BYTES + slab * 1024 + lane * 16;
+                        mark(dst, 16, STAGE);
+                        const bool in = off + 16 <= nrec;
+                        if (!in && off < nrec) er.oob_global++;
+                        const ChunkRef c = dma_bt16_chunk<S>(w, i, lane);
+                        if (in != (n0 + c.row < p.N)) er.oob_global++;
+                        for (int e = 0; e < 8; ++e) {
+                            uint16_t v = in ? read_bt(n0 + c.row, k0 + 8 * c.chunk + e, base + off / 2 + e, kmain) : 0;
+                            if (dst + 2 * e + 2 <= STAGE) memcpy(&lds[dst + 2 * e], &v, 2);
+                        }
+                    }
+                    for (int i = 0; !bt && i < S::DMA_B; ++i) {
                         const int slab = w * S::DMA_B + i;
                         const long base = (long)k0 * p.ldb + n0;
                         const long soff = (long)p16_b_slab_bytes(slab, p.ldb);
@@ -501,7 +548,18 @@ void run_pipe16(const Problem &p, Errs &er, std::vector<int> &cover) {
                             memcpy(&lds[dst + 2 * e], &v, 2);
                         }
                     }
-                    for (int i = 0; i < S::DMA_B; ++i) {
+                    for (int i = 0; bt && i < S::DMA_B; ++i) {
+                        const ChunkRef c = dma_bt16_chunk<S>(w, i, lane);
+                        const int dst = S::A_BYTES + (w * S::DMA_B + i) * 1024 + lane * 16;
+                        mark(dst, 16, STAGE);
+                        const bool in = n0 + c.row < p.N && kfull + 8 * c.chunk < kmain;
+                        for (int e = 0; e < 8; ++e) {
+                            const long row = n0 + c.row, col = kfull + 8 * c.chunk + e;
+                            uint16_t v = in ? read_bt(row, col, row * p.ldb + col, kmain) : 0;
+                            memcpy(&lds[dst + 2 * e], &v, 2);
+                        }
+                    }
+                    for (int i = 0; !bt && i < S::DMA_B; ++i) {
                         const ChunkRef c = dma_b16_chunk<S>(w, i, lane);
                         const int dst = S::A_BYTES + (w * S::DMA_B + i) * 1024 + lane * 16;
                         mark(dst, 16, STAGE);
@@ -527,7 +585,14 @@ void run_pipe16(const Problem &p, Errs &er, std::vector<int> &cover) {
                         uint16_t v = (m < p.M && k < p.K) ? p.A[m * p.lda + k] : 0;
                         memcpy(&lds[lds_a_offset<S>(row, chunk) + 2 * e], &v, 2);
                     }
-            for (int row = 0; row < 32; ++row)
+            for (int row = 0; bt && row < S::BN; ++row)
+                for (int chunk = 0; chunk < 4; ++chunk)
+                    for (int e = 0; e < 8; ++e) {
+                        long n = n0 + row, k = kmain + 8 * chunk + e;
+                        uint16_t v = (n < p.N && k < p.K) ? p.B[n * p.ldb + k] : 0;
+                        memcpy(&lds[S::A_BYTES + lds_a_offset<S>(row, chunk) + 2 * e], &v, 2);
+                    }
+            for (int row = 0; !bt && row < 32; ++row)
                 for (int chunk = 0; chunk < S::CB; ++chunk)
                     for (int e = 0; e < 8; ++e) {
                         long k = kmain + row, n = n0 + 8 * chunk + e;
@@ -702,6 +767,9 @@ extern "C" int emu_gemm_relu_bt(int config, int M, int N, int K, const uint16_t 
         case 2: return emulate<E64>(p, false, errs);
         case 3: return emulate<EP64>(p, false, errs);    // pipelined, four waves
         case 4: return emulate<E256w8>(p, false, errs);  // pipelined, eight waves
+        case 20: return emulate_pipe16<E16w4>(p, errs);  // 16 x 16 x 32 pipelined tiles
+        case 21: return emulate_pipe16<E16h>(p, errs);
+        case 23: return emulate_pipe16<E16t>(p, errs);
         default: return -1;
     }
 }

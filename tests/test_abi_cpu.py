@@ -84,6 +84,11 @@ def test_plan_shapes_of_the_workloads():
     assert tlg.plan(4096, 4100, 4096, aligned=True, ldb=4104, ldc=4104)["config_name"] == \
         "pipe_256x256x64_w2x4_s2_a3_early"
     assert tlg.plan(8192, 8192, 8192, trans_b=True)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
+    # B transposed below 128 tiles of 256 x 256: 128 x 256 pipelined tiles
+    # from 192 of them, else the direct-to-LDS tiles by count
+    assert tlg.plan(3001, 2049, 1537, trans_b=True)["config_name"] == "pipe16_128x256x64_w1x4_s3_a3"
+    assert tlg.plan(2560, 2560, 2560, trans_b=True)["config_name"] == "pipe16_128x256x64_w1x4_s3_a3"
+    assert tlg.plan(2048, 2048, 2048, trans_b=True)["config_name"] == "dma_128x128x32_w2x2_s4"
     # odd sizes and leading dimensions: direct-to-LDS loads, staged K tail; the
     # tuned table gives this class the pipelined 128 x 256 tiles (216 of them)
     p = tlg.plan(3001, 2049, 1537)
@@ -139,12 +144,16 @@ def test_plan_shapes_of_the_workloads():
     # 128 tiles of 128 x 256: the 32 x 32 x 16 form
     assert tlg.plan(2048, 2048, 2048)["config_name"] == "pipe_128x256x64_w1x4_s3"
     # forced 16 x 16 x 32 tiles take any K and N (whole stages, then a masked
-    # stage and a zero-padded block); they refuse a transposed B
+    # stage and a zero-padded block); with B transposed only the three
+    # pipelined ones (17, 21, 26) are built
     assert tlg.plan(300, 264, 200, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10)["config_name"] == \
         "pipe16_256x256x64_w2x2_s2_a3"
     assert tlg.plan(300, 260, 256, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10, ldb=264, ldc=264)["grid"] == 4
     with pytest.raises(tlg.TlgError):
         tlg.plan(512, 512, 512, variant=tlg.TLG_VARIANT_TILED_PIPE, config=10, trans_b=True)
+    for cfg, bm in ((17, 256), (21, 128), (26, 192)):
+        info = tlg.plan(1000, 1000, 200, variant=tlg.TLG_VARIANT_TILED_PIPE, config=cfg, trans_b=True)
+        assert info["grid"] == -(-1000 // bm) * 4, (cfg, info)
     assert tlg.plan(256, 256, 256)["variant_name"] == "tiled_dma"
     assert tlg.plan(5, 7, 0)["variant_name"] == "fill_zero"
     assert tlg.plan(0, 7, 9)["variant_name"] == "noop"

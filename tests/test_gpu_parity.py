@@ -329,9 +329,11 @@ def test_dma_configs(dev, config, shape):
 # ---------------------------------------------------------------- transposed B, grouped calls
 
 @pytest.mark.parametrize("variant,config", [(V_AUTO, -1), (V_DMA, 0), (V_DMA, 1), (V_DMA, 2), (V_PIPE, 2),
-                                            (V_PIPE, 4), (V_PIPE, 7)])
+                                            (V_PIPE, 4), (V_PIPE, 7), (V_PIPE, 17), (V_PIPE, 21),
+                                            (V_PIPE, 26)])
 @pytest.mark.parametrize("shape", [(300, 264, 200), (513, 520, 72), (1024, 1032, 1000), (301, 259, 203),
-                                   (16, 2048, 512), (257, 8, 4104), (65, 70, 9), (130, 129, 1)])
+                                   (16, 2048, 512), (257, 8, 4104), (65, 70, 9), (130, 129, 1),
+                                   (256, 256, 64), (512, 768, 2048), (257, 9, 4104)])
 def test_transposed_b(dev, variant, config, shape):
     """B given as its N x K transpose: bit-exact against the oracle on integer
     inputs, ragged K and N included; the guard bands stay untouched."""
@@ -345,6 +347,47 @@ def test_transposed_b(dev, variant, config, shape):
     allb = bits(big)
     assert np.array_equal(allb[:M, :N], ref)
     assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+
+
+@pytest.mark.parametrize("config", [-1, 17])
+def test_transposed_b_square4096_full(dev, config):
+    """B transposed on the 4096^3 workload, the whole output against the
+    oracle: integer inputs exact, own inputs within the tolerance (the
+    planned kernel and the 16 x 16 x 32 256 x 256 tiles)."""
+    w = wl.WORKLOADS["square4096"]
+    variant = V_AUTO if config < 0 else V_PIPE
+    for integer in (True, False):
+        A, B = wl.make_inputs(w, integer=integer)
+        Bt = np.ascontiguousarray(B.T)
+        print(f"transposed 4096 config={config} integer={integer}", flush=True)
+        got = bits(tlg.gemm_relu(to_dev(A, dev), to_dev(Bt, dev), trans_b=True, variant=variant, config=config))
+        ref = oracle.gemm_relu_bt(A, Bt)
+        if integer:
+            assert np.array_equal(got, ref), config
+        else:
+            assert_close(got, ref, f"transposed 4096 config {config}")
+
+
+@pytest.mark.parametrize("shape", [(3001, 2049, 1537), (2560, 2560, 264), (2000, 3000, 100)])
+def test_transposed_b_planned_half_tiles(dev, shape):
+    """B transposed below 128 tiles of 256 x 256 with at least 192 of 128 x 256:
+    the planned 128 x 256 pipelined tiles (ragged M, N and K included), integer
+    inputs exact in a NaN-filled padded output, uniform within the tolerance."""
+    M, N, K = shape
+    assert tlg.plan(M, N, K, trans_b=True)["config_name"] == "pipe16_128x256x64_w1x4_s3_a3"
+    print(f"transposed planned {shape}", flush=True)
+    A, B = wl.make_random(M, N, K, seed=M + N + K, kind="integer_pos")
+    Bt = np.ascontiguousarray(B.T)
+    big = torch.full((M + 2, N + 8), float("nan"), dtype=torch.float16, device=dev)
+    tlg.gemm_relu(to_dev(A, dev), to_dev(Bt, dev), out=big[:M, :N], trans_b=True)
+    torch.cuda.synchronize()
+    allb = bits(big)
+    assert np.array_equal(allb[:M, :N], oracle.gemm_relu_bt(A, Bt))
+    assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+    A, B = wl.make_random(M, N, K, seed=M * 3 + N + K, kind="uniform")
+    Bt = np.ascontiguousarray(B.T)
+    got = bits(tlg.gemm_relu(to_dev(A, dev), to_dev(Bt, dev), trans_b=True))
+    assert_close(got, oracle.gemm_relu_bt(A, Bt), f"transposed planned {shape}")
 
 
 def test_transposed_b_uniform_and_strided(dev):

@@ -95,11 +95,14 @@ def test_lds_epilogue_index_math(emu, config):
 SHAPES = [(64, 64, 64), (200, 136, 88), (257, 264, 520), (70, 512, 40), (1, 8, 8), (300, 40, 16)]
 
 
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
-@pytest.mark.parametrize("shape", SHAPES + [(301, 259, 203), (65, 70, 9), (130, 129, 1)])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 20, 21, 23])
+@pytest.mark.parametrize("shape", SHAPES + [(301, 259, 203), (65, 70, 9), (130, 129, 1), (300, 264, 200),
+                                            (257, 9, 4104), (513, 520, 72)])
 def test_transposed_b_tiles_match_oracle_integer(emu, config, shape):
     """B given transposed (N x K): its tile is loaded and read like A's; the
-    ragged K tail is staged the same way. Any K and N work."""
+    ragged K tail is staged the same way. Any K and N work (configurations
+    20, 21, 23: the 16 x 16 x 32 pipelined tiles, 256 x 256, 128 x 256 and
+    192 x 256)."""
     M, N, K = shape
     A, B = wl.make_random(M, N, K, seed=M + 3 * N + K, kind="integer_pos" if K > 100 else "integer")
     Bt = np.ascontiguousarray(B.T)

@@ -576,7 +576,9 @@ tlg_status plan_bt_select(const tlg::Problem &p, int32_t variant, int32_t config
     if (variant == TLG_VARIANT_TILED_DMA && (config < -1 || config >= kSquareDmaConfigs))
         return TLG_ERROR_INVALID_VALUE;
     if (variant == TLG_VARIANT_TILED_PIPE && config != -1 && config != tlg::PIPE_256x256x64_A3 &&
-        config != tlg::PIPE_256x256x64_W8_A3 && config != tlg::PIPE_256x256x64_W8_A3_EARLY)
+        config != tlg::PIPE_256x256x64_W8_A3 && config != tlg::PIPE_256x256x64_W8_A3_EARLY &&
+        config != tlg::PIPE16_256x256x64_A3_SP8 && config != tlg::PIPE16_128x256x64_A3 &&
+        config != tlg::PIPE16_192x256x64_A3_SP6)
         return TLG_ERROR_INVALID_VALUE;
     if (p.M == 0 || p.N == 0) {
         fill_info(o, TLG_VARIANT_NOOP, 0, nullptr, 1, 0, 0, 0);
@@ -602,10 +604,22 @@ tlg_status plan_bt_select(const tlg::Problem &p, int32_t variant, int32_t config
         const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64_W8_A3_EARLY;
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         if (offsets_ok_bt(p, tc.bm, tc.bn)) {
-            fill_info(o, TLG_VARIANT_TILED_PIPE, cfg, &tc, 1, 1, t256, 0);
+            fill_info(o, TLG_VARIANT_TILED_PIPE, cfg, &tc, 1, 1, ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn), 0);
             return TLG_SUCCESS;
         }
         if (variant == TLG_VARIANT_TILED_PIPE) return TLG_ERROR_NOT_SUPPORTED;
+    }
+    // below that, 128 x 256 pipelined tiles (16 x 16 x 32 MFMA) once there
+    // are at least 192 of them: 3001 x 2049 x 1537 measured 34.4 vs 46.4 us
+    // and 2560^3 41.0 vs 51.3 us on 128 x 128 direct-to-LDS tiles, while at
+    // 128 of them (2048^3) 31.3 vs 28.6 us the smaller tiles still win
+    if (variant == TLG_VARIANT_AUTO) {
+        const tlg::TileConfig &th = tlg::kPipeConfigs[tlg::PIPE16_128x256x64_A3];
+        const int64_t t_half = ceil_div(p.M, th.bm) * ceil_div(p.N, th.bn);
+        if (t_half >= 192 && offsets_ok_bt(p, th.bm, th.bn)) {
+            fill_info(o, TLG_VARIANT_TILED_PIPE, tlg::PIPE16_128x256x64_A3, &th, 1, 1, t_half, 0);
+            return TLG_SUCCESS;
+        }
     }
     const int cfg = config >= 0 && variant == TLG_VARIANT_TILED_DMA
                         ? config

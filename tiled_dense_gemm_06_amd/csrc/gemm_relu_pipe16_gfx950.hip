@@ -45,22 +45,35 @@ struct Frags16 {
 
 // The fragment reads of one k-step, in the order the MFMAs use them (tile i
 // uses b[i / TM] and a[i % TM]): b[0] (two reads), a[0..TM-1], then
-// b[1..TN-1] (two reads each).
-template <class S>
-constexpr int kFragReads16 = S::TM + 2 * S::TN;
+// b[1..TN-1] (two reads each). BT (B given transposed, N x K): the B tile is
+// held like the A tile and each B fragment is one 16-byte read.
+template <class S, bool BT = false>
+constexpr int kFragReads16 = S::TM + (BT ? 1 : 2) * S::TN;
 
 // Per-lane parts of the fragment addresses (frag_a16_lane, frag_b16_lane):
-// A for each k-step parity, B for each fragment column; the rest of each
-// address is a constant in the read's offset field.
+// A for each k-step parity, B for each fragment column (BT: b[0], b[1] for
+// each k-step parity, as for A); the rest of each address is a constant in
+// the read's offset field.
 template <class S>
 struct FragLanes16 {
     uint32_t a[2];
     uint32_t b[S::TN];
 };
 
-template <class S>
+template <class S, bool BT = false>
 __device__ __forceinline__ void frag_read16(Frags16<S> &f, LDS_PTR(const char) sA, LDS_PTR(const char) sB,
                                             const FragLanes16<S> &o, int s, int r) {
+    if constexpr (BT) {
+        if (r == 0 || r > S::TM) {
+            const int tn = r == 0 ? 0 : r - S::TM;
+            const short8_t v = *(LDS_PTR(const short8_t))(sB + o.b[s & 1] + tn * 16 * S::RA);
+            f.blo[tn] = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+            f.bhi[tn] = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+        } else {
+            f.a[r - 1] = *(LDS_PTR(const half8_t))(sA + o.a[s & 1] + (r - 1) * 16 * S::RA);
+        }
+        return;
+    }
     if (r < 2) {
         LDS_PTR(short4_t) p = (LDS_PTR(short4_t))(sB + o.b[0] + (32 * s + 4 * r) * S::RB);
         if (r == 0)
@@ -153,12 +166,12 @@ __device__ __forceinline__ void store_c_tile16_lds(const KArgs &a, int m0, int n
 }
 
 // The tile product of a 32-deep k-step s of the stage held in (sA, sB).
-template <class S>
+template <class S, bool BT = false>
 __device__ __forceinline__ void mma16_kstep(LDS_PTR(const char) sA, LDS_PTR(const char) sB, const FragLanes16<S> &fo,
                                             int s, float4_t (&acc)[S::TN][S::TM]) {
     Frags16<S> f;
 #pragma unroll
-    for (int r = 0; r < kFragReads16<S>; ++r) frag_read16<S>(f, sA, sB, fo, s, r);
+    for (int r = 0; r < kFragReads16<S, BT>; ++r) frag_read16<S, BT>(f, sA, sB, fo, s, r);
 #pragma unroll
     for (int i = 0; i < S::TM * S::TN; ++i) mfma16_tile<S>(f, i, acc);
 }
@@ -168,8 +181,9 @@ __device__ __forceinline__ void mma16_kstep(LDS_PTR(const char) sA, LDS_PTR(cons
 // stage of direct-to-LDS loads into buffer 0 with every lane's chunk checked
 // against kmain and against M or N, then both k-steps. (2) Rows [kmain, K) (1
 // to 8 of them, when K or N is not a multiple of 8): one zero-padded 32-deep
-// block staged element by element with bounds checks, then one k-step.
-template <class S, int ASTAGES>
+// block staged element by element with bounds checks, then one k-step. BT:
+// B's rows are those of the transposed B (n, K-contiguous), held like A's.
+template <class S, int ASTAGES, bool BT = false>
 __device__ __forceinline__ void pipe16_k_tail(const KArgs &a, int m0, int n0, int wave, int lane, int wm0, int wn0,
                                            const FragLanes16<S> &fo, float4_t (&acc)[S::TN][S::TM],
                                            LDS_PTR(char) lds) {
@@ -179,7 +193,7 @@ __device__ __forceinline__ void pipe16_k_tail(const KArgs &a, int m0, int n0, in
     if (kfull < a.kmain) {
         barrier_lds();  // no wave reads buffer 0 any more
         const int4_t ra = make_srd(a.A + (int64_t)m0 * a.lda + kfull);
-        const int4_t rb = make_srd(a.B + (int64_t)kfull * a.ldb + n0);
+        const int4_t rb = make_srd(BT ? a.B + (int64_t)n0 * a.ldb + kfull : a.B + (int64_t)kfull * a.ldb + n0);
 #pragma unroll
         for (int i = 0; i < S::DMA_A; ++i) {
             const ChunkRef c = dma_a_chunk<S>(wave, i, lane);
@@ -189,15 +203,16 @@ __device__ __forceinline__ void pipe16_k_tail(const KArgs &a, int m0, int n0, in
         }
 #pragma unroll
         for (int i = 0; i < S::DMA_B; ++i) {
-            const ChunkRef c = dma_b16_chunk<S>(wave, i, lane);
-            const bool in = kfull + c.row < a.kmain && n0 + 8 * c.chunk < a.N;
+            const ChunkRef c = BT ? dma_bt16_chunk<S>(wave, i, lane) : dma_b16_chunk<S>(wave, i, lane);
+            const bool in = BT ? n0 + c.row < a.N && kfull + 8 * c.chunk < a.kmain
+                               : kfull + c.row < a.kmain && n0 + 8 * c.chunk < a.N;
             dma16(rb, (uint32_t)(uintptr_t)(lds + B_REGION + (wave * S::DMA_B + i) * 1024),
                   in ? (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16) : kOOB);
         }
         wait_vmcnt<0>();
         barrier_lds();
 #pragma unroll
-        for (int s = 0; s < S::KSTEPS; ++s) mma16_kstep<S>(lds, lds + B_REGION, fo, s, acc);
+        for (int s = 0; s < S::KSTEPS; ++s) mma16_kstep<S, BT>(lds, lds + B_REGION, fo, s, acc);
     }
     if (a.kmain < a.K) {
         barrier_lds();
@@ -211,18 +226,31 @@ __device__ __forceinline__ void pipe16_k_tail(const KArgs &a, int m0, int n0, in
                 v[e] = (m < a.M && k + e < a.K) ? a.A[(int64_t)m * a.lda + k + e] : (_Float16)0.0f;
             *(LDS_PTR(half8_t))(lds + lds_a_offset<S>(row, chunk)) = v;
         }
-        // B: rows k = kmain .. kmain+31 of the block, all BN columns
-        for (int q = tid; q < 32 * S::CB; q += S::NT) {
-            const int row = q / S::CB, chunk = q % S::CB;
-            const int k = a.kmain + row, n = n0 + 8 * chunk;
-            half8_t v;
+        if constexpr (BT) {
+            // B: rows n of the tile, logical chunks 0..3 (k = kmain + 8c .. +7)
+            for (int q = tid; q < S::BN * 4; q += S::NT) {
+                const int row = q / 4, chunk = q % 4;
+                const int n = n0 + row, k = a.kmain + 8 * chunk;
+                half8_t v;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                v[e] = (k < a.K && n + e < a.N) ? a.B[(int64_t)k * a.ldb + n + e] : (_Float16)0.0f;
-            *(LDS_PTR(half8_t))(lds + B_REGION + lds_b16_offset<S>(row, chunk)) = v;
+                for (int e = 0; e < 8; ++e)
+                    v[e] = (n < a.N && k + e < a.K) ? a.B[(int64_t)n * a.ldb + k + e] : (_Float16)0.0f;
+                *(LDS_PTR(half8_t))(lds + B_REGION + lds_a_offset<S>(row, chunk)) = v;
+            }
+        } else {
+            // B: rows k = kmain .. kmain+31 of the block, all BN columns
+            for (int q = tid; q < 32 * S::CB; q += S::NT) {
+                const int row = q / S::CB, chunk = q % S::CB;
+                const int k = a.kmain + row, n = n0 + 8 * chunk;
+                half8_t v;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] = (k < a.K && n + e < a.N) ? a.B[(int64_t)k * a.ldb + n + e] : (_Float16)0.0f;
+                *(LDS_PTR(half8_t))(lds + B_REGION + lds_b16_offset<S>(row, chunk)) = v;
+            }
         }
         barrier_lds();
-        mma16_kstep<S>(lds, lds + B_REGION, fo, 0, acc);
+        mma16_kstep<S, BT>(lds, lds + B_REGION, fo, 0, acc);
     }
 }
 
@@ -239,12 +267,13 @@ __device__ __forceinline__ void pipe16_k_tail(const KArgs &a, int m0, int n0, in
 // for and the barrier publishes it (and retires stage kt). EARLY: the wait and
 // the barrier come before the last H slots (which read no LDS of stage kt),
 // and the reads of stage kt+1's k-step-0 fragments move into those slots.
-template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
+template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY, bool BT = false>
 __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_idx, LDS_PTR(char) lds) {
     constexpr int T = S::TM * S::TN;
     constexpr int H = T / 2;
     static_assert(T % 2 == 0 && S::KSTEPS % 2 == 0, "the last k-step of a stage must use f[1]");
-    constexpr int READS = kFragReads16<S>;
+    static_assert(!BT || S::BN * S::RA == S::B_BYTES, "a transposed B tile fills the B buffer like an A tile");
+    constexpr int READS = kFragReads16<S, BT>;
     static_assert(READS <= H, "fragment reads must fit under half the MFMAs of a k-step");
     constexpr int LOADS = S::DMA_A + S::DMA_B;
     constexpr int AHEAD = S::STAGES - 1;
@@ -279,13 +308,14 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
     // load i covers slab (wave*DMA_B + i), rows 2*slab and 2*slab + 1 of the
     // stage; the slab's start is the instruction's scalar offset, and the
     // lane's offset (kOOB for a column chunk past N) takes one of four forms,
-    // by the slab's swizzle pattern (p16_b_lane_bytes).
-    uint32_t voff_a[2], voff_b[4];
+    // by the slab's swizzle pattern (p16_b_lane_bytes). BT: B's loads are
+    // A's, over the rows n of the transposed B.
+    uint32_t voff_a[2], voff_b[BT ? 2 : 4];
 #pragma unroll
     for (int q = 0; q < 2; ++q) voff_a[q] = (uint32_t)p16_a_lane_bytes<S>(lane, q, a.lda);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int64_t o = p16_b_lane_bytes<S>(lane, q, n0, a.N, a.ldb);
+    for (int q = 0; q < (BT ? 2 : 4); ++q) {
+        const int64_t o = BT ? p16_a_lane_bytes<S>(lane, q, a.ldb) : p16_b_lane_bytes<S>(lane, q, n0, a.N, a.ldb);
         voff_b[q] = o < 0 ? kOOB : (uint32_t)o;
     }
     uint32_t nrec_a[S::DMA_A];  // bytes of the slab's rows inside M
@@ -295,13 +325,25 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
         const int64_t bytes = rows <= 0 ? 0 : rows * a.lda * 2;
         nrec_a[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(bytes > (int64_t)kRange ? (int64_t)kRange : bytes));
     }
+    uint32_t nrec_b[BT ? S::DMA_B : 1];  // BT: bytes of the slab's rows inside N
+#pragma unroll
+    for (int i = 0; i < (BT ? S::DMA_B : 0); ++i) {
+        const int64_t rows = (int64_t)a.N - n0 - (int64_t)(wave * S::DMA_B + i) * 8;
+        const int64_t bytes = rows <= 0 ? 0 : rows * a.ldb * 2;
+        nrec_b[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(bytes > (int64_t)kRange ? (int64_t)kRange : bytes));
+    }
     const _Float16 *a_tile = a.A + (int64_t)m0 * a.lda;
-    const _Float16 *b_tile = a.B + n0;
+    const _Float16 *b_tile = BT ? a.B + (int64_t)n0 * a.ldb : a.B + n0;
     FragLanes16<S> fo;
     fo.a[0] = (uint32_t)frag_a16_lane<S>(wm0, 0, lane);
     fo.a[1] = (uint32_t)frag_a16_lane<S>(wm0, 1, lane);
+    if constexpr (BT) {
+        fo.b[0] = (uint32_t)frag_a16_lane<S>(wn0, 0, lane);
+        fo.b[1] = (uint32_t)frag_a16_lane<S>(wn0, 1, lane);
+    } else {
 #pragma unroll
-    for (int tn = 0; tn < S::TN; ++tn) fo.b[tn] = (uint32_t)frag_b16_lane<S>(wn0, tn, lane);
+        for (int tn = 0; tn < S::TN; ++tn) fo.b[tn] = (uint32_t)frag_b16_lane<S>(wn0, tn, lane);
+    }
 
     // Load j of stage kt into buffer buf of its operand; past the end of K
     // the descriptor's range is 0 bytes, so every lane writes zeros.
@@ -312,6 +354,11 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
             int4_t r = make_srd(a_tile + (int64_t)slab * 8 * a.lda + k0);
             r[2] = kt < nk ? (int)nrec_a[j] : 0;
             dma16(r, (uint32_t)(uintptr_t)(lds + buf * S::A_BYTES + slab * 1024), voff_a[slab % 2]);
+        } else if constexpr (BT) {
+            const int slab = wave * S::DMA_B + (j - S::DMA_A);
+            int4_t r = make_srd(b_tile + (int64_t)slab * 8 * a.ldb + k0);
+            r[2] = kt < nk ? (int)nrec_b[j - S::DMA_A] : 0;
+            dma16(r, (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES + slab * 1024), voff_b[slab % 2]);
         } else {
             const int slab = wave * S::DMA_B + (j - S::DMA_A);
             int4_t r = make_srd(b_tile + (int64_t)k0 * a.ldb);
@@ -353,7 +400,7 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
     barrier_lds();
     if (EARLY) {
 #pragma unroll
-        for (int r = 0; r < READS; ++r) frag_read16<S>(f[0], lds, lds + B_REGION, fo, 0, r);
+        for (int r = 0; r < READS; ++r) frag_read16<S, BT>(f[0], lds, lds + B_REGION, fo, 0, r);
     }
 
     int bbuf = 0, abuf = 0;
@@ -369,11 +416,11 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
         for (int q = 0; q < SLOTS; ++q) {
             if (q < H) {
                 mfma16_tile<S>(f[1], H + q, acc);
-                if (!EARLY && q < READS) frag_read16<S>(f[0], sA, sB, fo, 0, q);
+                if (!EARLY && q < READS) frag_read16<S, BT>(f[0], sA, sB, fo, 0, q);
             } else if (q < H + (S::KSTEPS - 1) * T) {
                 const int ks = (q - H) / T, i = (q - H) % T;
                 mfma16_tile<S>(f[ks & 1], i, acc);
-                if (i < READS) frag_read16<S>(f[(ks + 1) & 1], sA, sB, fo, ks + 1, i);
+                if (i < READS) frag_read16<S, BT>(f[(ks + 1) & 1], sA, sB, fo, ks + 1, i);
             } else {
                 const int u = q - H - (S::KSTEPS - 1) * T;
                 if (EARLY && u == 0) {
@@ -381,7 +428,7 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
                     barrier_lds();       // ... and every wave's; no wave reads stage kt any more
                 }
                 mfma16_tile<S>(f[1], u, acc);
-                if (EARLY && u < READS) frag_read16<S>(f[0], sA1, sB1, fo, 0, u);
+                if (EARLY && u < READS) frag_read16<S, BT>(f[0], sA1, sB1, fo, 0, u);
             }
             if (q >= DOFF && (q - DOFF) % SPACING == 0 && (q - DOFF) / SPACING < LOADS) {
                 const int n = (q - DOFF) / SPACING;
@@ -403,18 +450,18 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
 #pragma unroll
     for (int i = H; i < T; ++i) mfma16_tile<S>(f[1], i, acc);
     wait_vmcnt<0>();  // no load may still be writing LDS
-    if (nk * S::BK < a.K) pipe16_k_tail<S, ASTAGES>(a, m0, n0, wave, lane, wm0, wn0, fo, acc, lds);
+    if (nk * S::BK < a.K) pipe16_k_tail<S, ASTAGES, BT>(a, m0, n0, wave, lane, wm0, wn0, fo, acc, lds);
     mfma16_results_ready();
     barrier_lds();  // every wave is done with the stages
     store_c_tile16_lds<S>(a, m0, n0, wave, lane, acc, lds);
 }
 
-template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
+template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY, bool BT = false>
 __global__ __launch_bounds__(S::NT) void k_tiled_pipe16(const KArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[pipe16_lds_bytes<S, ASTAGES>()];
     int tm_idx, tn_idx;
     grouped_tile(xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
-    pipe16_tile<S, SPACING, DOFF, ASTAGES, EARLY>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
+    pipe16_tile<S, SPACING, DOFF, ASTAGES, EARLY, BT>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
 }
 
 // Several problems in one launch: work-group ids are dealt to the XCDs as in
@@ -443,7 +490,7 @@ using Pipe16w8 = TileShape16<256, 256, 64, 2, 4, 2>;
 // a 96-slot step)
 using Pipe16t = TileShape16<192, 256, 64, 2, 2, 2>;
 
-template <class S>
+template <class S, bool BT = false>
 static KArgs pipe16_args(const Problem &p) {
     KArgs a;
     a.A = (const _Float16 *)p.A;
@@ -459,17 +506,19 @@ static KArgs pipe16_args(const Problem &p) {
     a.ldc = p.ldc;
     a.group_m = 4;
     a.k_split = (int)p.K;
-    a.kmain = p.K % 8 == 0 && p.N % 8 == 0 ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
+    // BT: a chunk must not cross the end of a row of the transposed B (K
+    // only); otherwise the end of an A row (K) or column N of B
+    a.kmain = p.K % 8 == 0 && (BT || p.N % 8 == 0) ? (int)p.K : (int)(8 * ((p.K - 1) / 8));
     a.tiles_m = (a.M + S::BM - 1) / S::BM;
     a.tiles_n = (a.N + S::BN - 1) / S::BN;
     return a;
 }
 
-template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
+template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY, bool BT = false>
 static hipError_t launch_pipe16_t(const Problem &p, hipStream_t stream) {
-    if (p.trans_b) return hipErrorInvalidValue;
-    const KArgs a = pipe16_args<S>(p);
-    hipLaunchKernelGGL((k_tiled_pipe16<S, SPACING, DOFF, ASTAGES, EARLY>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
+    if (p.trans_b != BT) return hipErrorInvalidValue;
+    const KArgs a = pipe16_args<S, BT>(p);
+    hipLaunchKernelGGL((k_tiled_pipe16<S, SPACING, DOFF, ASTAGES, EARLY, BT>), dim3((unsigned)(a.tiles_m * a.tiles_n)),
                        dim3(S::NT), 0, stream, a);
     return hipGetLastError();
 }
@@ -495,6 +544,14 @@ hipError_t launch_tiled_pipe16_grouped(const Problem *ps, int count, hipStream_t
 }
 
 hipError_t launch_tiled_pipe16(int config, const Problem &p, hipStream_t stream) {
+    if (p.trans_b) {
+        switch (config) {
+            case PIPE16_256x256x64_A3_SP8: return launch_pipe16_t<Pipe16w4, 8, 1, 3, false, true>(p, stream);
+            case PIPE16_128x256x64_A3: return launch_pipe16_t<Pipe16h, 4, 1, 3, false, true>(p, stream);
+            case PIPE16_192x256x64_A3_SP6: return launch_pipe16_t<Pipe16t, 6, 1, 3, false, true>(p, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (config) {
         // 16 loads per wave and stage, every four slots from slot 1 (the
         // 128-slot step leaves its last 64 slots free of loads)

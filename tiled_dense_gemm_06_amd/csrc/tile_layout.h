@@ -206,6 +206,16 @@ struct TileShape16 : TileShape<BM_, BN_, BK_, WM_, WN_, STAGES_> {
 TLG_HD constexpr int swz_b16(int k) { return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)); }
 template <class S>
 TLG_HD int lds_b16_offset(int k, int c) { return k * S::RB + 16 * (c ^ swz_b16(k)); }
+// A transposed B (N x K, rows of n with 64 k per stage) is held like the A
+// tile: load i of wave w covers slab (w*DMA_B + i), rows 8*slab .. +7 (the
+// same number of 1 KiB loads as a 256-column B tile).
+template <class S>
+TLG_HD ChunkRef dma_bt16_chunk(int wave, int i, int lane) {
+    int slab = wave * S::DMA_B + i;
+    int row = slab * S::ROWS_A_SLAB + lane / S::CA;
+    int pos = lane % S::CA;
+    return ChunkRef{row, pos ^ swz_a(row, S::CA)};
+}
 template <class S>
 TLG_HD ChunkRef dma_b16_chunk(int wave, int i, int lane) {
     int slab = wave * S::DMA_B + i;
