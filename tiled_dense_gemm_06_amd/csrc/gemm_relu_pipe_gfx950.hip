@@ -116,12 +116,13 @@ constexpr int pipe_lds_bytes() {
 }
 
 // One output tile (tm_idx, tn_idx) of problem a, with the work-group's LDS.
-// FULLK (kmain a multiple of BK): every stage is either wholly inside K or
-// wholly past it, so whether a load reads memory is decided per stage, on
-// the scalar unit, by the buffer descriptor's range (0 bytes past the end of
-// K); each lane's offset is fixed for the whole loop. This keeps the chain of
-// vector compares and selects out of the slot program, where with one wave
-// per SIMD it would hold up the next MFMA's issue.
+// Whether a load reads memory is decided per stage, on the scalar unit, by
+// the buffer descriptor's range (0 bytes past the end of K); each lane's
+// offset is fixed for the whole loop. This keeps a chain of vector compares
+// and selects out of the slot program, where with one wave per SIMD it would
+// hold up the next MFMA's issue. FULLK: kmain is a multiple of BK, every
+// stage wholly inside K or wholly past it; else the last stage inside K takes
+// a second set of offsets, fixed too, that also drop what lies past kmain.
 template <class S, int SPACING, int DOFF, int ASTAGES, bool BT, bool EARLY, bool FULLK>
 __device__ __forceinline__ void pipe_tile(const KArgs &a, int tm_idx, int tn_idx, LDS_PTR(char) lds) {
     constexpr int T = S::TM * S::TN;  // MFMA tiles of a wave (MFMAs per k-step)
@@ -176,36 +177,35 @@ __device__ __forceinline__ void pipe_tile(const KArgs &a, int tm_idx, int tn_idx
 
     const _Float16 *a_tile = a.A + (int64_t)m0 * a.lda;
     const _Float16 *b_tile = BT ? a.B + (int64_t)n0 * a.ldb : a.B + n0;
-    uint32_t voff[LOADS];  // (FULLK) the offset, or kOOB for a row or column outside M or N
+    uint32_t voff[LOADS];  // the offset, or kOOB for a row or column outside M or N
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) voff[i] = ok[i] ? off[i] : kOOB;
+    // (!FULLK) the last stage, nk - 1, ends inside K: its offsets also drop
+    // the chunks at or past kmain. Every earlier stage lies wholly inside K,
+    // so one select per load, on a scalar condition, is all the slot program
+    // carries for a ragged K (against a compare chain per load in every
+    // stage: 3008 x 2049 x 1536 29.5 vs 31.3 us, 4096 x 4100 x 4096 187.4 vs
+    // 192.3 us).
+    uint32_t vlast[FULLK ? 1 : LOADS];
+    if (!FULLK) {
+        const int klast = (nk - 1) * S::BK;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) vlast[i] = ok[i] && klast + kin[i] < a.kmain ? off[i] : kOOB;
+    }
 
     // Load j of stage kt into LDS buffer buf of its operand (stages past K
     // load zeros); j < DMA_A loads A, the others B.
     auto dma = [&](int j, int kt, int buf) {
         const int k0 = kt * S::BK;
-        if (FULLK) {
-            int4_t r = j < S::DMA_A ? make_srd(a_tile + k0)
-                                    : make_srd(BT ? b_tile + k0 : b_tile + (int64_t)k0 * a.ldb);
-            if (kt >= nk) r[2] = 0;  // past the end of K: every lane out of range, zeros
-            const uint32_t l =
-                j < S::DMA_A ? (uint32_t)(uintptr_t)(lds + buf * S::A_BYTES + (wave * S::DMA_A + j) * 1024)
-                             : (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES +
-                                                     (wave * S::DMA_B + (j - S::DMA_A)) * 1024);
+        int4_t r = j < S::DMA_A ? make_srd(a_tile + k0) : make_srd(BT ? b_tile + k0 : b_tile + (int64_t)k0 * a.ldb);
+        if (kt >= nk) r[2] = 0;  // past the end of K: every lane out of range, zeros
+        const uint32_t l = j < S::DMA_A ? (uint32_t)(uintptr_t)(lds + buf * S::A_BYTES + (wave * S::DMA_A + j) * 1024)
+                                        : (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES +
+                                                                (wave * S::DMA_B + (j - S::DMA_A)) * 1024);
+        if (FULLK)
             dma16(r, l, voff[j]);
-            return;
-        }
-        const bool in = ok[j] && k0 + kin[j] < a.kmain;
-        if (j < S::DMA_A) {
-            const int4_t r = make_srd(a_tile + k0);
-            const uint32_t l = (uint32_t)(uintptr_t)(lds + buf * S::A_BYTES + (wave * S::DMA_A + j) * 1024);
-            dma16(r, l, in ? off[j] : kOOB);
-        } else {
-            const int4_t r = make_srd(BT ? b_tile + k0 : b_tile + (int64_t)k0 * a.ldb);
-            const uint32_t l = (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES +
-                                                     (wave * S::DMA_B + (j - S::DMA_A)) * 1024);
-            dma16(r, l, in ? off[j] : kOOB);
-        }
+        else
+            dma16(r, l, kt == nk - 1 ? vlast[FULLK ? 0 : j] : voff[j]);
     };
 
     float16_t acc[S::TN][S::TM];
