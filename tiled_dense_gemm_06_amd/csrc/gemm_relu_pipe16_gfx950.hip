@@ -102,11 +102,7 @@ __device__ __forceinline__ void frag_read16(Frags16<S> &f, LDS_PTR(const char) s
 // accumulator used again, only 64 MFMA slots after its last use, and the
 // epilogue waits explicitly before it reads the accumulators
 // (mfma16_results_ready). The compiler still makes every MFMA wait for the
-// LDS reads of its operands. What the schedule cannot exclude is a copy or a
-// spill of an accumulator that the register allocator places right behind
-// the MFMA writing it (it reads the old value): tests/test_mfma_hazards.py
-// compiles this file and rejects any instruction that touches an MFMA's
-// result within its 18 wait states.
+// LDS reads of its operands.
 template <class S>
 __device__ __forceinline__ void mfma16_tile(const Frags16<S> &f, int i, float4_t (&acc)[S::TN][S::TM]) {
     const int tn = i / S::TM, tm = i % S::TM;
