@@ -82,3 +82,18 @@ def test_counters_derives_clock_occupancy_and_conflicts(tmp_path):
     assert "matrix cores busy: 60.0 %" in text and "37.5 % of the 2.4 GHz dense peak" in text
     assert "bank-conflict cycles per LDS instruction: 0.250" in text
     assert text.rstrip().endswith("a note")
+
+
+def test_committed_traffic_matches_the_current_kernels():
+    """Every workload's HBM traffic record in profiles/traffic.json was taken
+    on the tile configuration the planner picks today and on the kernel
+    sources as they stand (a source change voids the record, and the
+    benchmark line then reports no traffic)."""
+    import tiled_dense_gemm_06_amd as tlg
+    from tiled_dense_gemm_06_amd import workloads as wl
+    from tiled_dense_gemm_06_amd.profiling import measured_traffic
+    for name in ("square256", "square4096", "ragged3001x2049x1537", "skinny16x14336x4096", "square8192"):
+        w = wl.WORKLOADS[name]
+        cfg = tlg.plan(w.M, w.N, w.K)["config_name"]
+        t = measured_traffic(name, cfg)
+        assert t is not None and t > 0, (name, cfg)
