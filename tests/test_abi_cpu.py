@@ -83,7 +83,12 @@ def test_plan_shapes_of_the_workloads():
     assert tlg.plan(5120, 5120, 5120)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
     assert tlg.plan(4096, 4100, 4096, aligned=True, ldb=4104, ldc=4104)["config_name"] == \
         "pipe_256x256x64_w2x4_s2_a3_early"
-    assert tlg.plan(8192, 8192, 8192, trans_b=True)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
+    # B transposed from 128 tiles of 256 x 256: the 16 x 16 x 32 tiles under
+    # the plain call's conditions, else the 32 x 32 x 16 early ones
+    assert tlg.plan(8192, 8192, 8192, trans_b=True)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
+    assert tlg.plan(4096, 4096, 4104, trans_b=True)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
+    assert tlg.plan(3072, 3072, 3080, trans_b=True)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
+    assert tlg.plan(4096, 4352, 4096, trans_b=True)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
     # B transposed below 128 tiles of 256 x 256: 128 x 256 pipelined tiles
     # from 192 of them, else the direct-to-LDS tiles by count
     assert tlg.plan(3001, 2049, 1537, trans_b=True)["config_name"] == "pipe16_128x256x64_w1x4_s3_a3"

@@ -599,9 +599,14 @@ tlg_status plan_bt_select(const tlg::Problem &p, int32_t variant, int32_t config
         return TLG_SUCCESS;
     }
     // the same boundary as the plain call: 256 x 256 pipelined tiles from 128
-    // tiles up (half the CUs; 3072^3 measured 72 vs 101 us on 128 x 128 tiles)
+    // tiles up (half the CUs; 3072^3 measured 72 vs 101 us on 128 x 128
+    // tiles), on the 16 x 16 x 32 form under the plain call's conditions
+    // (K whole 64-deep stages, or at least 256 tiles, not 257..319 of them;
+    // B's rows need no condition on N here: 8192^3 823.0 vs 871.5 us, 4096^3
+    // 139.6-145.6 vs 143.1-147.9 on the 32 x 32 x 16 early form)
     if (variant == TLG_VARIANT_TILED_PIPE || (variant == TLG_VARIANT_AUTO && t256 >= 128)) {
-        const int cfg = config >= 0 ? config : tlg::PIPE_256x256x64_W8_A3_EARLY;
+        const bool use16 = (p.K % 64 == 0 || t256 >= 256) && !(t256 > 256 && t256 < 320);
+        const int cfg = config >= 0 ? config : use16 ? tlg::PIPE16_256x256x64_A3_SP8 : tlg::PIPE_256x256x64_W8_A3_EARLY;
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         if (offsets_ok_bt(p, tc.bm, tc.bn)) {
             fill_info(o, TLG_VARIANT_TILED_PIPE, cfg, &tc, 1, 1, ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn), 0);

@@ -165,15 +165,57 @@ __device__ __forceinline__ void store_c_tile16_lds(const KArgs &a, int m0, int n
     }
 }
 
-// The tile product of a 32-deep k-step s of the stage held in (sA, sB).
+// The MFMAs of one B column (acc[tn][0..TM-1]) as one block that ends with 20
+// wait states, so that whatever the compiler places after it (a copy or a
+// spill of an accumulator, which it may schedule right behind an MFMA it
+// does not see the latency of) reads finished results. Used by the K tail,
+// which runs once per tile.
+template <class S>
+__device__ __forceinline__ void mfma16_column_fenced(const Frags16<S> &f, int tn, float4_t (&acc)[S::TN][S::TM]) {
+    static_assert(S::TM == 8 || S::TM == 6, "a column of six or eight 16 x 16 tiles");
+    const half8_t b =
+        __builtin_bit_cast(half8_t, __builtin_shufflevector(f.blo[tn], f.bhi[tn], 0, 1, 2, 3, 4, 5, 6, 7));
+    if constexpr (S::TM == 8) {
+        asm volatile(
+            "v_mfma_f32_16x16x32_f16 %0, %8, %9, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %8, %10, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %8, %11, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %8, %12, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %8, %13, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %8, %14, %5\n\t"
+            "v_mfma_f32_16x16x32_f16 %6, %8, %15, %6\n\t"
+            "v_mfma_f32_16x16x32_f16 %7, %8, %16, %7\n\t"
+            "s_nop 7\n\ts_nop 7\n\ts_nop 3"
+            : "+a"(acc[tn][0]), "+a"(acc[tn][1]), "+a"(acc[tn][2]), "+a"(acc[tn][3]), "+a"(acc[tn][4]),
+              "+a"(acc[tn][5]), "+a"(acc[tn][6]), "+a"(acc[tn][7])
+            : "v"(b), "v"(f.a[0]), "v"(f.a[1]), "v"(f.a[2]), "v"(f.a[3]), "v"(f.a[4]), "v"(f.a[5]), "v"(f.a[6]),
+              "v"(f.a[7]));
+    } else {
+        asm volatile(
+            "v_mfma_f32_16x16x32_f16 %0, %6, %7, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %6, %8, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %6, %9, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %6, %10, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %6, %11, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %6, %12, %5\n\t"
+            "s_nop 7\n\ts_nop 7\n\ts_nop 3"
+            : "+a"(acc[tn][0]), "+a"(acc[tn][1]), "+a"(acc[tn][2]), "+a"(acc[tn][3]), "+a"(acc[tn][4]),
+              "+a"(acc[tn][5])
+            : "v"(b), "v"(f.a[0]), "v"(f.a[1]), "v"(f.a[2]), "v"(f.a[3]), "v"(f.a[4]), "v"(f.a[5]));
+    }
+}
+
+// The tile product of a 32-deep k-step s of the stage held in (sA, sB), for
+// the K tail: the fragments, then the columns as fenced blocks.
 template <class S, bool BT = false>
-__device__ __forceinline__ void mma16_kstep(LDS_PTR(const char) sA, LDS_PTR(const char) sB, const FragLanes16<S> &fo,
-                                            int s, float4_t (&acc)[S::TN][S::TM]) {
+__device__ __forceinline__ void mma16_kstep_fenced(LDS_PTR(const char) sA, LDS_PTR(const char) sB,
+                                                   const FragLanes16<S> &fo, int s,
+                                                   float4_t (&acc)[S::TN][S::TM]) {
     Frags16<S> f;
 #pragma unroll
     for (int r = 0; r < kFragReads16<S, BT>; ++r) frag_read16<S, BT>(f, sA, sB, fo, s, r);
 #pragma unroll
-    for (int i = 0; i < S::TM * S::TN; ++i) mfma16_tile<S>(f, i, acc);
+    for (int tn = 0; tn < S::TN; ++tn) mfma16_column_fenced<S>(f, tn, acc);
 }
 
 // Rows of K past the loop's whole stages, after every wave is done with the
@@ -212,7 +254,7 @@ __device__ __forceinline__ void pipe16_k_tail(const KArgs &a, int m0, int n0, in
         wait_vmcnt<0>();
         barrier_lds();
 #pragma unroll
-        for (int s = 0; s < S::KSTEPS; ++s) mma16_kstep<S, BT>(lds, lds + B_REGION, fo, s, acc);
+        for (int s = 0; s < S::KSTEPS; ++s) mma16_kstep_fenced<S, BT>(lds, lds + B_REGION, fo, s, acc);
     }
     if (a.kmain < a.K) {
         barrier_lds();
@@ -250,7 +292,7 @@ __device__ __forceinline__ void pipe16_k_tail(const KArgs &a, int m0, int n0, in
             }
         }
         barrier_lds();
-        mma16_kstep<S, BT>(lds, lds + B_REGION, fo, 0, acc);
+        mma16_kstep_fenced<S, BT>(lds, lds + B_REGION, fo, 0, acc);
     }
 }
 
@@ -267,7 +309,7 @@ __device__ __forceinline__ void pipe16_k_tail(const KArgs &a, int m0, int n0, in
 // for and the barrier publishes it (and retires stage kt). EARLY: the wait and
 // the barrier come before the last H slots (which read no LDS of stage kt),
 // and the reads of stage kt+1's k-step-0 fragments move into those slots.
-template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY, bool BT = false>
+template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY, bool BT = false, bool BROWS = false>
 __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_idx, LDS_PTR(char) lds) {
     constexpr int T = S::TM * S::TN;
     constexpr int H = T / 2;
@@ -308,8 +350,13 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
     // load i covers slab (wave*DMA_B + i), rows 2*slab and 2*slab + 1 of the
     // stage; the slab's start is the instruction's scalar offset, and the
     // lane's offset (kOOB for a column chunk past N) takes one of four forms,
-    // by the slab's swizzle pattern (p16_b_lane_bytes). BT: B's loads are
-    // A's, over the rows n of the transposed B.
+    // by the slab's swizzle pattern (p16_b_lane_bytes). BT: B's slabs are
+    // laid out and read like A's, over the rows n of the transposed B; in a
+    // tile whose rows all lie inside N one descriptor per stage serves them,
+    // each slab's start the scalar offset, and only the tile that holds row
+    // N (BROWS) gives each slab A's kind of descriptor, ending after row
+    // N - 1 (a descriptor per slab everywhere spilled 61 scalar registers
+    // instead of 20 at 256 x 256: 8192^3 907 vs 823 us).
     uint32_t voff_a[2], voff_b[BT ? 2 : 4];
 #pragma unroll
     for (int q = 0; q < 2; ++q) voff_a[q] = (uint32_t)p16_a_lane_bytes<S>(lane, q, a.lda);
@@ -325,9 +372,9 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
         const int64_t bytes = rows <= 0 ? 0 : rows * a.lda * 2;
         nrec_a[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(bytes > (int64_t)kRange ? (int64_t)kRange : bytes));
     }
-    uint32_t nrec_b[BT ? S::DMA_B : 1];  // BT: bytes of the slab's rows inside N
+    uint32_t nrec_b[BROWS ? S::DMA_B : 1];  // BROWS: bytes of the slab's rows inside N
 #pragma unroll
-    for (int i = 0; i < (BT ? S::DMA_B : 0); ++i) {
+    for (int i = 0; i < (BROWS ? S::DMA_B : 0); ++i) {
         const int64_t rows = (int64_t)a.N - n0 - (int64_t)(wave * S::DMA_B + i) * 8;
         const int64_t bytes = rows <= 0 ? 0 : rows * a.ldb * 2;
         nrec_b[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(bytes > (int64_t)kRange ? (int64_t)kRange : bytes));
@@ -354,11 +401,17 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
             int4_t r = make_srd(a_tile + (int64_t)slab * 8 * a.lda + k0);
             r[2] = kt < nk ? (int)nrec_a[j] : 0;
             dma16(r, (uint32_t)(uintptr_t)(lds + buf * S::A_BYTES + slab * 1024), voff_a[slab % 2]);
-        } else if constexpr (BT) {
+        } else if constexpr (BROWS) {
             const int slab = wave * S::DMA_B + (j - S::DMA_A);
             int4_t r = make_srd(b_tile + (int64_t)slab * 8 * a.ldb + k0);
-            r[2] = kt < nk ? (int)nrec_b[j - S::DMA_A] : 0;
+            r[2] = kt < nk ? (int)nrec_b[BROWS ? j - S::DMA_A : 0] : 0;
             dma16(r, (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES + slab * 1024), voff_b[slab % 2]);
+        } else if constexpr (BT) {
+            const int slab = wave * S::DMA_B + (j - S::DMA_A);
+            int4_t r = make_srd(b_tile + k0);
+            if (kt >= nk) r[2] = 0;
+            dma16_soff(r, (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES + slab * 1024), voff_b[slab % 2],
+                       (uint32_t)(slab * 8 * a.ldb * 2));
         } else {
             const int slab = wave * S::DMA_B + (j - S::DMA_A);
             int4_t r = make_srd(b_tile + (int64_t)k0 * a.ldb);
@@ -461,7 +514,10 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe16(const KArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[pipe16_lds_bytes<S, ASTAGES>()];
     int tm_idx, tn_idx;
     grouped_tile(xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n), a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
-    pipe16_tile<S, SPACING, DOFF, ASTAGES, EARLY, BT>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
+    if (BT && (tn_idx + 1) * S::BN > a.N)
+        pipe16_tile<S, SPACING, DOFF, ASTAGES, EARLY, BT, BT>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
+    else
+        pipe16_tile<S, SPACING, DOFF, ASTAGES, EARLY, BT>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
 }
 
 // Several problems in one launch: work-group ids are dealt to the XCDs as in
