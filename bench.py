@@ -465,11 +465,11 @@ def main() -> int:
         rows = [(w.M * g // args.grouped, w.M * (g + 1) // args.grouped) for g in range(args.grouped)]
         # (the library's rule: from 128 tiles of 256 x 256 in total the
         # pipelined 256 x 256 kernel, grouped configuration 4 (16 x 16 x 32
-        # MFMA) for B not transposed, N % 8 == 0 and K % 64 == 0, else 3
+        # MFMA) for K % 64 == 0 and, B not transposed, N % 8 == 0, else 3
         # (32 x 32 x 16); below, direct-to-LDS tiles 0..2 by tile count)
         t256 = sum(-(-(r1 - r0) // 256) * -(-w.N // 256) for r0, r1 in rows)
         t128 = sum(-(-(r1 - r0) // 128) * -(-w.N // 128) for r0, r1 in rows)
-        pipe16_ok = not args.trans_b and w.N % 8 == 0 and w.K % 64 == 0
+        pipe16_ok = w.K % 64 == 0 and (args.trans_b or w.N % 8 == 0)
         gcfg = args.config if args.config >= 0 else ((4 if pipe16_ok else 3) if t256 >= 128 else
                                                      1 if t128 >= 192 else 2)
         name = (tlg.tlg_plan_config_name(tlg.TLG_VARIANT_TILED_PIPE, 17) if gcfg == 4

@@ -259,13 +259,13 @@ tlg_status tlg_gemm_relu_grouped(tlg_handle h, int32_t count, const tlg_gemm_des
 
 /* tlg_gemm_relu_grouped with a forced tile configuration: -1 the library's
  * choice (from 128 tiles of 256 x 256 in total the pipelined kernel, in its
- * 16 x 16 x 32 form when no B is transposed, every N is a multiple of 8 and
- * every K a multiple of 64, else in its 32 x 32 x 16 form; below, the
+ * 16 x 16 x 32 form when every K is a multiple of 64 and, B not transposed,
+ * every N a multiple of 8, else in its 32 x 32 x 16 form; below, the
  * direct-to-LDS tiles by tile count); 0, 1, 2 the direct-to-LDS
  * 256 x 256 x 32, 128 x 128 x 32 and 64 x 64 x 64 tiles; 3 the eight-wave
  * 32 x 32 x 16 pipelined 256 x 256 x 64 kernel; 4 the four-wave
- * 16 x 16 x 32 pipelined 256 x 256 x 64 kernel (B not transposed, every N a
- * multiple of 8, any K; TLG_ERROR_NOT_SUPPORTED otherwise). */
+ * 16 x 16 x 32 pipelined 256 x 256 x 64 kernel (any K; B not transposed:
+ * every N a multiple of 8, TLG_ERROR_NOT_SUPPORTED otherwise). */
 tlg_status tlg_gemm_relu_grouped_variant(tlg_handle h, int32_t config, int32_t count, const tlg_gemm_desc *descs,
                                          int32_t trans_b, hipStream_t stream);
 

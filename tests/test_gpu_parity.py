@@ -461,29 +461,36 @@ def test_grouped_large(dev, trans_b):
         assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
 
 
+@pytest.mark.parametrize("trans_b", [False, True])
 @pytest.mark.parametrize("config", [-1, 4])
-def test_grouped_pipe16(dev, config):
-    """Problems with B not transposed and N a multiple of 8 in one launch of
-    the 16 x 16 x 32 pipelined kernel: the library's choice from 128 tiles of
-    256 x 256 when every K is whole 64-deep stages, and forced (4) with K
-    tails too; ragged M, an empty problem; bit-exact per problem, guard bands
-    intact."""
+def test_grouped_pipe16(dev, config, trans_b):
+    """Problems in one launch of the 16 x 16 x 32 pipelined kernel (B not
+    transposed: N a multiple of 8; transposed: any N): the library's choice
+    from 128 tiles of 256 x 256 when every K is whole 64-deep stages, and
+    forced (4) with K tails too; ragged M, an empty problem; bit-exact per
+    problem, guard bands intact."""
     shapes = [(2048, 2048, 256), (1000, 2048, 512), (1031, 1800, 128), (0, 64, 64), (257, 264, 64)]
+    if trans_b:
+        shapes.append((300, 259, 128))
     if config == 4:
         shapes += [(300, 264, 200), (129, 256, 1000), (64, 8, 8)]
+        if trans_b:
+            shapes += [(301, 259, 203), (130, 513, 1001)]
     probs, As, Bs, bigs, outs = [], [], [], [], []
     for i, (M, N, K) in enumerate(shapes):
         A, B = wl.make_random(M, N, K, seed=300 + i, kind="integer_pos")
-        probs.append((A, B))
+        Bx = np.ascontiguousarray(B.T) if trans_b else B
+        probs.append((A, Bx))
         As.append(to_dev(A, dev))
-        Bs.append(to_dev(B, dev))
+        Bs.append(to_dev(Bx, dev))
         big = torch.full((M + 2, N + 8), float("nan"), dtype=torch.float16, device=dev)
         bigs.append(big)
         outs.append(big[:M, :N])
     assert sum(-(-M // 256) * -(-N // 256) for M, N, _ in shapes) >= 128
-    tlg.gemm_relu_grouped(As, Bs, outs, config=config)
+    print(f"grouped pipe16 config={config} trans_b={trans_b}", flush=True)
+    tlg.gemm_relu_grouped(As, Bs, outs, trans_b=trans_b, config=config)
     torch.cuda.synchronize()
-    refs = oracle.gemm_relu_grouped(probs)
+    refs = oracle.gemm_relu_grouped(probs, trans_b=trans_b)
     for (M, N, K), big, ref in zip(shapes, bigs, refs):
         allb = bits(big)
         assert np.array_equal(allb[:M, :N], ref), (M, N, K)

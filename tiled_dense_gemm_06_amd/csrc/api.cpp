@@ -689,16 +689,16 @@ tlg_status run_grouped(tlg_handle h, int32_t config, int32_t count, const tlg_ge
     if (n == 0) return TLG_SUCCESS;
     // the pipelined 256 x 256 kernels from the same total tile count as a
     // single call (128 tiles of 256 x 256), when every problem can take them:
-    // the 16 x 16 x 32 form for B not transposed, N a multiple of 8 and K in
-    // whole 64-deep stages (8192^3 as 8 row blocks: 855.0-858.7 us against
-    // 882.4-887.1 on the 32 x 32 x 16 form), else the 32 x 32 x 16 form
+    // the 16 x 16 x 32 form for K in whole 64-deep stages and, with B not
+    // transposed, N a multiple of 8 (8192^3 as 8 row blocks: 855.0-858.7 us
+    // against 882.4-887.1 on the 32 x 32 x 16 form), else the 32 x 32 x 16 form
     const bool auto_pipe = config == -1 && t256 >= 128;
     if (config == kGroupedPipe16 || auto_pipe) {
         const tlg::TileConfig &tp = tlg::kPipeConfigs[tlg::PIPE16_256x256x64_A3_SP8];
-        bool ok = t256 <= 0x7fffffff && !trans_b;
+        bool ok = t256 <= 0x7fffffff;
         for (int i = 0; i < n && ok; ++i)
-            ok = ps[i].N % 8 == 0 && (ps[i].K % tp.bk == 0 || config == kGroupedPipe16) &&
-                 dma_ok(ps[i], tp.bm, tp.bn, tp.bk);
+            ok = (ps[i].K % tp.bk == 0 || config == kGroupedPipe16) &&
+                 (trans_b ? offsets_ok_bt(ps[i], tp.bm, tp.bn) : ps[i].N % 8 == 0 && dma_ok(ps[i], tp.bm, tp.bn, tp.bk));
         if (ok) return tlg::launch_tiled_pipe16_grouped(ps, n, stream) == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;
         if (config == kGroupedPipe16) return TLG_ERROR_NOT_SUPPORTED;
     }

@@ -523,7 +523,7 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe16(const KArgs a) {
 // Several problems in one launch: work-group ids are dealt to the XCDs as in
 // the single-problem kernel, then split by problem in order (tile_start holds
 // the running tile counts), each problem's tiles in its own grouped order.
-template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY>
+template <class S, int SPACING, int DOFF, int ASTAGES, bool EARLY, bool BT = false>
 __global__ __launch_bounds__(S::NT) void k_tiled_pipe16_grouped(const GroupArgs g) {
     __shared__ __attribute__((aligned(1024))) char smem[pipe16_lds_bytes<S, ASTAGES>()];
     const int v = xcd_remap(blockIdx.x, g.tile_start[g.count]);
@@ -532,7 +532,10 @@ __global__ __launch_bounds__(S::NT) void k_tiled_pipe16_grouped(const GroupArgs 
     const KArgs &a = g.p[p];
     int tm_idx, tn_idx;
     grouped_tile(v - g.tile_start[p], a.tiles_m, a.tiles_n, a.group_m, &tm_idx, &tn_idx);
-    pipe16_tile<S, SPACING, DOFF, ASTAGES, EARLY>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
+    if (BT && (tn_idx + 1) * S::BN > a.N)
+        pipe16_tile<S, SPACING, DOFF, ASTAGES, EARLY, BT, BT>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
+    else
+        pipe16_tile<S, SPACING, DOFF, ASTAGES, EARLY, BT>(a, tm_idx, tn_idx, (LDS_PTR(char))smem);
 }
 
 using Pipe16w4 = TileShape16<256, 256, 64, 2, 2, 2>;    // four waves of 128 x 128, two B buffers
@@ -580,23 +583,30 @@ static hipError_t launch_pipe16_t(const Problem &p, hipStream_t stream) {
 }
 
 // The default configuration (four waves, loads every eight MFMA slots) over
-// up to kGroupMax problems, none with a transposed B.
-hipError_t launch_tiled_pipe16_grouped(const Problem *ps, int count, hipStream_t stream) {
+// up to kGroupMax problems, all with the same trans_b.
+template <bool BT>
+static hipError_t launch_pipe16_grouped_t(const Problem *ps, int count, hipStream_t stream) {
     using S = Pipe16w4;
     static_assert(sizeof(GroupArgs) <= 4096, "kernel arguments");
-    if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
     GroupArgs g;
     g.count = count;
     g.tile_start[0] = 0;
     for (int i = 0; i < count; ++i) {
-        if (ps[i].trans_b) return hipErrorInvalidValue;
-        g.p[i] = pipe16_args<S>(ps[i]);
+        g.p[i] = pipe16_args<S, BT>(ps[i]);
         g.tile_start[i + 1] = g.tile_start[i] + g.p[i].tiles_m * g.p[i].tiles_n;
     }
     if (g.tile_start[count] == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_tiled_pipe16_grouped<S, 8, 1, 3, false>), dim3((unsigned)g.tile_start[count]), dim3(S::NT), 0,
-                       stream, g);
+    hipLaunchKernelGGL((k_tiled_pipe16_grouped<S, 8, 1, 3, false, BT>), dim3((unsigned)g.tile_start[count]),
+                       dim3(S::NT), 0, stream, g);
     return hipGetLastError();
+}
+
+hipError_t launch_tiled_pipe16_grouped(const Problem *ps, int count, hipStream_t stream) {
+    if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
+    const bool bt = ps[0].trans_b;
+    for (int i = 1; i < count; ++i)
+        if (ps[i].trans_b != bt) return hipErrorInvalidValue;
+    return bt ? launch_pipe16_grouped_t<true>(ps, count, stream) : launch_pipe16_grouped_t<false>(ps, count, stream);
 }
 
 hipError_t launch_tiled_pipe16(int config, const Problem &p, hipStream_t stream) {
