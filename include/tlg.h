@@ -202,8 +202,10 @@ int64_t tlg_noalloc_scratch_bytes(void);
  * and read like A's: by the pipelined kernel on 256 x 256 tiles when the
  * problem has at least 128 of them (16 x 16 x 32 MFMA when K is whole 64-deep
  * stages or there are at least 256 tiles, but not 257 to 319; else 32 x 32 x
- * 16), else on 128 x 256 tiles (16 x 16 x 32 MFMA) when it has at least 192
- * of those, else by the direct-to-LDS tiled
+ * 16; with K whole stages 192 x 256 or 128 x 256 tiles where they take fewer
+ * rounds of work-groups, as tlg_gemm_relu does), else on 128 x 256 tiles
+ * (16 x 16 x 32 MFMA) when it has at least 192 of those, else by the
+ * direct-to-LDS tiled
  * kernel (tile by tile count). Any K and N. TLG_ERROR_NOT_SUPPORTED when a
  * tile's byte offsets exceed 2 GB (e.g. ldbt * 256 * 2 >= 2^31); nothing is
  * enqueued then. */

@@ -606,7 +606,28 @@ tlg_status plan_bt_select(const tlg::Problem &p, int32_t variant, int32_t config
     // 139.6-145.6 vs 143.1-147.9 on the 32 x 32 x 16 early form)
     if (variant == TLG_VARIANT_TILED_PIPE || (variant == TLG_VARIANT_AUTO && t256 >= 128)) {
         const bool use16 = (p.K % 64 == 0 || t256 >= 256) && !(t256 > 256 && t256 < 320);
-        const int cfg = config >= 0 ? config : use16 ? tlg::PIPE16_256x256x64_A3_SP8 : tlg::PIPE_256x256x64_W8_A3_EARLY;
+        int cfg = config >= 0 ? config : use16 ? tlg::PIPE16_256x256x64_A3_SP8 : tlg::PIPE_256x256x64_W8_A3_EARLY;
+        if (config < 0 && p.K % 64 == 0) {
+            // tile height by rounds x relative tile time, as for the plain
+            // call (the 192 x 256 and 128 x 256 tiles in their 16 x 16 x 32
+            // form, K whole stages; against the 256 x 256 ones, us: 3072^3
+            // 64.7 vs 70.1, 6144^3 411.4 vs 419.5, 2560x4096x4096 82.2 vs
+            // 89.5, 2048x4096x4096 62.8 vs 88.5)
+            const int cus = kPlanCUs;
+            const int cand_cfg[3] = {cfg, tlg::PIPE16_192x256x64_A3_SP6, tlg::PIPE16_128x256x64_A3};
+            const int cand_bm[3] = {256, 192, 128};
+            const double cand_rel[3] = {1.0, 0.9375, 0.75};
+            double best = 0.0;
+            for (int c = 0; c < 3; ++c) {
+                const int64_t t = ceil_div(p.M, cand_bm[c]) * ceil_div(p.N, 256);
+                if (t <= 128 && cand_bm[c] != 256) continue;
+                const double score = (double)ceil_div(t, cus > 0 ? cus : 256) * cand_rel[c];
+                if (best == 0.0 || score < best) {
+                    best = score;
+                    cfg = cand_cfg[c];
+                }
+            }
+        }
         const tlg::TileConfig &tc = tlg::kPipeConfigs[cfg];
         if (offsets_ok_bt(p, tc.bm, tc.bn)) {
             fill_info(o, TLG_VARIANT_TILED_PIPE, cfg, &tc, 1, 1, ceil_div(p.M, tc.bm) * ceil_div(p.N, tc.bn), 0);
