@@ -88,11 +88,12 @@ def test_plan_shapes_of_the_workloads():
     assert tlg.plan(8192, 8192, 8192, trans_b=True)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
     assert tlg.plan(4096, 4096, 4104, trans_b=True)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
     assert tlg.plan(3072, 3072, 3080, trans_b=True)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
-    assert tlg.plan(4096, 4352, 4096, trans_b=True)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
+    assert tlg.plan(4096, 4352, 4104, trans_b=True)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
     # ... and the plain call's tile height by rounds (K whole stages)
     assert tlg.plan(3072, 3072, 3072, trans_b=True)["config_name"] == "pipe16_192x256x64_w2x2_s2_a3_sp6"
     assert tlg.plan(2048, 4096, 4096, trans_b=True)["config_name"] == "pipe16_128x256x64_w1x4_s3_a3"
-    for shape in ((3072, 3072, 3072), (6144, 6144, 6144), (2560, 4096, 4096), (2048, 4096, 4096), (8192, 8192, 8192)):
+    for shape in ((3072, 3072, 3072), (6144, 6144, 6144), (2560, 4096, 4096), (2048, 4096, 4096), (8192, 8192, 8192),
+                  (4096, 4352, 4096)):
         assert tlg.plan(*shape, trans_b=True)["config_name"] == tlg.plan(*shape)["config_name"], shape
     # B transposed below 128 tiles of 256 x 256: 128 x 256 pipelined tiles
     # from 192 of them, else the direct-to-LDS tiles by count
