@@ -391,6 +391,27 @@ def test_transposed_b_planned_half_tiles(dev, shape):
     assert_close(got, oracle.gemm_relu_bt(A, Bt), f"transposed planned {shape}")
 
 
+@pytest.mark.parametrize("shape,config_name", [((3072, 3072, 1024), "pipe16_192x256x64_w2x2_s2_a3_sp6"),
+                                               ((2048, 4096, 512), "pipe16_128x256x64_w1x4_s3_a3"),
+                                               ((3001, 3072, 640), "pipe16_192x256x64_w2x2_s2_a3_sp6")])
+def test_transposed_b_planned_tile_height(dev, shape, config_name):
+    """B transposed from 128 tiles of 256 x 256 with K whole stages: the
+    planned 192 x 256 or 128 x 256 tiles, integer inputs exact, uniform
+    within the tolerance."""
+    M, N, K = shape
+    assert tlg.plan(M, N, K, trans_b=True)["config_name"] == config_name
+    print(f"transposed planned {shape} {config_name}", flush=True)
+    for kind in ("integer_pos", "uniform"):
+        A, B = wl.make_random(M, N, K, seed=M + 7 * N + K, kind=kind)
+        Bt = np.ascontiguousarray(B.T)
+        got = bits(tlg.gemm_relu(to_dev(A, dev), to_dev(Bt, dev), trans_b=True))
+        ref = oracle.gemm_relu_bt(A, Bt)
+        if kind == "integer_pos":
+            assert np.array_equal(got, ref)
+        else:
+            assert_close(got, ref, f"transposed planned {shape}")
+
+
 def test_transposed_b_uniform_and_strided(dev):
     """Uniform inputs within the tolerance; padded leading dimensions of A, Bt, C."""
     M, N, K = 777, 555, 333
