@@ -204,8 +204,9 @@ int64_t tlg_noalloc_scratch_bytes(void);
  * stages or there are at least 256 tiles, but not 257 to 319; else 32 x 32 x
  * 16; with K whole stages 192 x 256 or 128 x 256 tiles where they take fewer
  * rounds of work-groups, as tlg_gemm_relu does), else on 128 x 256 tiles
- * (16 x 16 x 32 MFMA) when it has at least 192 of those, else by the
- * direct-to-LDS tiled
+ * (16 x 16 x 32 MFMA) when it has at least 192 of those; with M at most 32
+ * (K >= 512) or 64 (K >= 2048) and aligned data, by the column-strip split-K
+ * kernel as tlg_gemm_relu; else by the direct-to-LDS tiled
  * kernel (tile by tile count). Any K and N. TLG_ERROR_NOT_SUPPORTED when a
  * tile's byte offsets exceed 2 GB (e.g. ldbt * 256 * 2 >= 2^31); nothing is
  * enqueued then. */
@@ -217,10 +218,14 @@ tlg_status tlg_gemm_relu_bt(tlg_handle h, int64_t M, int64_t N, int64_t K,
 
 /* tlg_gemm_relu_bt with a forced kernel family and tile configuration, for
  * tests and measurements: variant TLG_VARIANT_AUTO (then config must be -1),
- * TLG_VARIANT_TILED_DMA (configs 0..2) or TLG_VARIANT_TILED_PIPE (configs 2,
+ * TLG_VARIANT_TILED_DMA (configs 0..2), TLG_VARIANT_TILED_PIPE (configs 2,
  * 4 and 7, the 256 x 256 ones with a third A buffer, and the 16 x 16 x 32
- * MFMA tiles 17 (256 x 256), 21 (128 x 256) and 26 (192 x 256)); config -1
- * lets the library choose inside the family. */
+ * MFMA tiles 17 (256 x 256), 21 (128 x 256) and 26 (192 x 256)) or
+ * TLG_VARIANT_SPLITK (the column-strip configurations 3..9 with the library's
+ * parts per strip; M within the strip, 16-byte aligned pointers, leading
+ * dimensions, K and N multiples of 8, else TLG_ERROR_NOT_SUPPORTED; split
+ * strips use the handle's workspace); config -1 lets the library choose
+ * inside the family. */
 tlg_status tlg_gemm_relu_bt_variant(tlg_handle h, int32_t variant, int32_t config, int64_t M, int64_t N, int64_t K,
                                     const void *A, int64_t lda,
                                     const void *Bt, int64_t ldbt,

@@ -89,6 +89,19 @@ def test_plan_shapes_of_the_workloads():
     assert tlg.plan(4096, 4096, 4104, trans_b=True)["config_name"] == "pipe16_256x256x64_w2x2_s2_a3_sp8"
     assert tlg.plan(3072, 3072, 3080, trans_b=True)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
     assert tlg.plan(4096, 4352, 4104, trans_b=True)["config_name"] == "pipe_256x256x64_w2x4_s2_a3_early"
+    # skinny M with B transposed: the strip kernel under the plain call's rule
+    for shape, name, parts in (((16, 14336, 4096), "splitk_waves_32x64x64_w2_s3", 1),
+                               ((1, 4096, 4096), "splitk_waves_32x64x64_w2_s3", 4),
+                               ((48, 4096, 14336), "splitk_waves_64x64x64_w2_s3", 4)):
+        info = tlg.plan(*shape, trans_b=True)
+        assert (info["config_name"], info["splits"]) == (name, parts), shape
+        assert info["config_name"] == tlg.plan(*shape)["config_name"], shape
+    assert tlg.plan(16, 14336, 256, trans_b=True)["variant_name"] == "tiled_dma"  # K below 512
+    assert tlg.plan(16, 14336, 4096, trans_b=True, ldb=4100)["variant_name"] == "tiled_dma"  # ldb % 8
+    with pytest.raises(tlg.TlgError):
+        tlg.plan(100, 4096, 4096, variant=tlg.TLG_VARIANT_SPLITK, config=3, trans_b=True)  # M above the strip
+    with pytest.raises(tlg.TlgError):
+        tlg.plan(16, 4096, 4096, variant=tlg.TLG_VARIANT_SPLITK, config=0, trans_b=True)  # not a strip
     # ... and the plain call's tile height by rounds (K whole stages)
     assert tlg.plan(3072, 3072, 3072, trans_b=True)["config_name"] == "pipe16_192x256x64_w2x2_s2_a3_sp6"
     assert tlg.plan(2048, 4096, 4096, trans_b=True)["config_name"] == "pipe16_128x256x64_w1x4_s3_a3"

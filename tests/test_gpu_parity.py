@@ -412,6 +412,43 @@ def test_transposed_b_planned_tile_height(dev, shape, config_name):
             assert_close(got, ref, f"transposed planned {shape}")
 
 
+@pytest.mark.parametrize("shape,config_name,parts", [((16, 14336, 4096), "splitk_waves_32x64x64_w2_s3", 1),
+                                                     ((1, 4096, 4096), "splitk_waves_32x64x64_w2_s3", 4),
+                                                     ((48, 4096, 14336), "splitk_waves_64x64x64_w2_s3", 4),
+                                                     ((7, 1000, 2048), "splitk_waves_32x64x64_w2_s3", 4),
+                                                     ((32, 64, 512), "splitk_waves_32x64x64_w2_s3", 4),
+                                                     ((64, 8192, 8192), "splitk_waves_64x64x64_w2_s3", 2)])
+def test_transposed_b_strips(dev, shape, config_name, parts):
+    """B transposed with skinny M: the planned strip kernel (B's blocks read
+    like A's rows), one part per strip or several summed in order, a ragged
+    last strip; integer inputs exact in a NaN-filled padded output, uniform
+    within the tolerance, and twice in a row (the split strips' counters are
+    left at zero)."""
+    M, N, K = shape
+    info = tlg.plan(M, N, K, trans_b=True)
+    assert (info["config_name"], info["splits"]) == (config_name, parts)
+    print(f"transposed strips {shape} {config_name} parts={parts}", flush=True)
+    A, B = wl.make_random(M, N, K, seed=M + 5 * N + K, kind="integer_pos")
+    Bt = np.ascontiguousarray(B.T)
+    ref = oracle.gemm_relu_bt(A, Bt)
+    Ad, Btd = to_dev(A, dev), to_dev(Bt, dev)
+    for _ in range(2):
+        big = torch.full((M + 2, N + 8), float("nan"), dtype=torch.float16, device=dev)
+        tlg.gemm_relu(Ad, Btd, out=big[:M, :N], trans_b=True)
+        torch.cuda.synchronize()
+        allb = bits(big)
+        assert np.array_equal(allb[:M, :N], ref)
+        assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+    A, B = wl.make_random(M, N, K, seed=M + 5 * N + K + 1, kind="uniform")
+    Bt = np.ascontiguousarray(B.T)
+    got = bits(tlg.gemm_relu(to_dev(A, dev), to_dev(Bt, dev), trans_b=True))
+    assert_close(got, oracle.gemm_relu_bt(A, Bt), f"transposed strips {shape}")
+    # the strip forced through the split-K family gives the same bits
+    got2 = bits(tlg.gemm_relu(to_dev(A, dev), to_dev(Bt, dev), trans_b=True, variant=tlg.TLG_VARIANT_SPLITK,
+                              config=tlg.plan(M, N, K, trans_b=True)["config"]))
+    assert np.array_equal(got, got2)
+
+
 def test_transposed_b_uniform_and_strided(dev):
     """Uniform inputs within the tolerance; padded leading dimensions of A, Bt, C."""
     M, N, K = 777, 555, 333

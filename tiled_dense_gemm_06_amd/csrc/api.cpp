@@ -154,6 +154,25 @@ tlg_status grid_fits(tlg_status st, const tlg_plan_info *o) {
     return st == TLG_SUCCESS && o->grid > 0x7fffffff ? TLG_ERROR_NOT_SUPPORTED : st;
 }
 
+// Strip configuration cfg (checked by the caller): parts per strip, forced,
+// else as many as fit the CUs whole (1x4096x4096: 4 parts 12 us vs 1 part
+// 23 us; 16x14336x4096: 1 part 25 us vs 2 parts 29 us), at most 4
+// (16x2048x4096: 4 parts 10.3 us vs 8 parts 10.9 us), within the workspace.
+void plan_strip_parts(const tlg::Problem &p, int cfg, int32_t splits, int64_t cap, int cus, tlg_plan_info *o) {
+    const tlg::TileConfig &ts = tlg::kStripConfigs[cfg - tlg::SPLIT_WAVES_32x64x64];
+    const int64_t strips = ceil_div(p.N, ts.bn);
+    int64_t parts = splits > 0 ? splits : (strips >= cus ? 1 : cus / strips);
+    if (splits <= 0 && parts > 4) parts = 4;
+    const int64_t nkb = ceil_div(p.K, ts.bk);
+    if (parts > nkb) parts = nkb > 0 ? nkb : 1;
+    const int64_t slot_bytes = (int64_t)ts.bm * ts.bn * 4;
+    if (parts > 1 && strips * parts * slot_bytes > cap) parts = cap / (strips * slot_bytes);
+    if (parts < 1) parts = 1;
+    if (parts > 1 && strips * 4 > kCounterBytes) parts = 1;
+    const int64_t ws = parts > 1 ? kCounterBytes + strips * parts * slot_bytes : 0;
+    fill_info(o, TLG_VARIANT_SPLITK, cfg, &ts, (int)parts, 1, strips * parts, ws);
+}
+
 tlg_status plan_select(const tlg::Problem &p, int32_t variant, int32_t config, int32_t splits, int64_t cap, int cus,
                        tlg_plan_info *o, int64_t *k_split_out);
 tlg_status plan_impl(const tlg::Problem &p, int32_t variant, int32_t config, int32_t splits, int64_t cap, int cus,
@@ -246,23 +265,10 @@ tlg_status plan_select(const tlg::Problem &p, int32_t variant, int32_t config, i
         }
         if (tlg::is_strip_config(cfg)) {
             const tlg::TileConfig &ts = tlg::kStripConfigs[cfg - tlg::SPLIT_WAVES_32x64x64];
-            const int64_t strips = ceil_div(p.N, ts.bn);
-            const bool strip_ok = p.M <= ts.bm && dma_ok_aligned(p, ts.bm, ts.bn, ts.bk) && strips <= 0x7fffffff;
+            const bool strip_ok = p.M <= ts.bm && dma_ok_aligned(p, ts.bm, ts.bn, ts.bk) &&
+                                  ceil_div(p.N, ts.bn) <= 0x7fffffff;
             if (!strip_ok) return TLG_ERROR_NOT_SUPPORTED;
-            // parts per strip: forced, else as many as fit the CUs whole
-            // (1x4096x4096: 4 parts 12 us vs 1 part 23 us; 16x14336x4096:
-            // 1 part 25 us vs 2 parts 29 us), at most 4 (16x2048x4096: 4
-            // parts 10.3 us vs 8 parts 10.9 us)
-            int64_t parts = splits > 0 ? splits : (strips >= cus ? 1 : cus / strips);
-            if (splits <= 0 && parts > 4) parts = 4;
-            const int64_t nkb = ceil_div(p.K, ts.bk);
-            if (parts > nkb) parts = nkb > 0 ? nkb : 1;
-            const int64_t slot_bytes = (int64_t)ts.bm * ts.bn * 4;
-            if (parts > 1 && strips * parts * slot_bytes > cap) parts = cap / (strips * slot_bytes);
-            if (parts < 1) parts = 1;
-            if (parts > 1 && strips * 4 > kCounterBytes) parts = 1;
-            const int64_t ws = parts > 1 ? kCounterBytes + strips * parts * slot_bytes : 0;
-            fill_info(o, TLG_VARIANT_SPLITK, cfg, &ts, (int)parts, 1, strips * parts, ws);
+            plan_strip_parts(p, cfg, splits, cap, cus, o);
             return TLG_SUCCESS;
         }
         if (tlg::is_strip_sk_config(cfg)) {
@@ -570,8 +576,9 @@ tlg_status plan_bt(const tlg::Problem &p, int32_t variant, int32_t config, tlg_p
 }
 tlg_status plan_bt_select(const tlg::Problem &p, int32_t variant, int32_t config, tlg_plan_info *o) {
     if (variant != TLG_VARIANT_AUTO && variant != TLG_VARIANT_TILED_DMA && variant != TLG_VARIANT_TILED_PIPE &&
-        variant != TLG_VARIANT_PINGPONG)
+        variant != TLG_VARIANT_PINGPONG && variant != TLG_VARIANT_SPLITK)
         return TLG_ERROR_INVALID_VALUE;
+    if (variant == TLG_VARIANT_SPLITK && config != -1 && !tlg::is_strip_config(config)) return TLG_ERROR_INVALID_VALUE;
     if (variant == TLG_VARIANT_AUTO && config != -1) return TLG_ERROR_INVALID_VALUE;
     if (variant == TLG_VARIANT_TILED_DMA && (config < -1 || config >= kSquareDmaConfigs))
         return TLG_ERROR_INVALID_VALUE;
@@ -590,6 +597,31 @@ tlg_status plan_bt_select(const tlg::Problem &p, int32_t variant, int32_t config
         return TLG_SUCCESS;
     }
     const int64_t t256 = ceil_div(p.M, 256) * ceil_div(p.N, 256);
+    // Skinny M: the strip kernel, B's blocks loaded and read like A's rows,
+    // under the plain call's rule (one 32-row strip from K = 512, the 64-row
+    // strip for 32 < M <= 64 from K = 2048; aligned data), parts as there
+    // (16x14336x4096: 21.6 vs 30.7 us on the 64 x 64 direct-to-LDS tiles;
+    // 48x4096x14336: 27.8)
+    {
+        auto strip_ok = [&](int cfg) {
+            const tlg::TileConfig &ts = tlg::kStripConfigs[cfg - tlg::SPLIT_WAVES_32x64x64];
+            return p.M <= ts.bm && aligned(p.A, 16) && aligned(p.B, 16) && aligned(p.C, 16) && p.lda % 8 == 0 &&
+                   p.ldb % 8 == 0 && p.ldc % 8 == 0 && p.K % 8 == 0 && p.N % 8 == 0 && offsets_ok_bt(p, ts.bm, ts.bn) &&
+                   ceil_div(p.N, ts.bn) <= 0x7fffffff;
+        };
+        int cfg = -1;
+        if (variant == TLG_VARIANT_SPLITK)
+            cfg = config >= 0 ? config : tlg::SPLIT_WAVES_32x64x64;
+        else if (variant == TLG_VARIANT_AUTO && p.K >= 512 && strip_ok(tlg::SPLIT_WAVES_32x64x64))
+            cfg = tlg::SPLIT_WAVES_32x64x64;
+        else if (variant == TLG_VARIANT_AUTO && p.K >= 2048 && strip_ok(tlg::SPLIT_WAVES_64x64x64))
+            cfg = tlg::SPLIT_WAVES_64x64x64;
+        if (cfg >= 0) {
+            if (!strip_ok(cfg)) return TLG_ERROR_NOT_SUPPORTED;
+            plan_strip_parts(p, cfg, 0, kWorkspaceBytes - kCounterBytes, kPlanCUs, o);
+            return TLG_SUCCESS;
+        }
+    }
     if (variant == TLG_VARIANT_PINGPONG) {
         if (config < -1 || config >= tlg::PINGPONG_CONFIGS) return TLG_ERROR_INVALID_VALUE;
         const int cfg = config >= 0 ? config : tlg::PINGPONG_256x256x32;
@@ -679,6 +711,14 @@ tlg_status run_bt(tlg_handle h, int32_t variant, int32_t config, tlg::Problem p,
         case TLG_VARIANT_TILED_DMA: e = tlg::launch_tiled_dma(info.config, p, stream); break;
         case TLG_VARIANT_TILED_PIPE: e = tlg::launch_tiled_pipe(info.config, p, stream); break;
         case TLG_VARIANT_PINGPONG: e = tlg::launch_pingpong(info.config, p, stream); break;
+        case TLG_VARIANT_SPLITK: {
+            if (!tlg::is_strip_config(info.config) || info.workspace_bytes > h->workspace_bytes)
+                return TLG_ERROR_NOT_SUPPORTED;
+            float *const ws = h->workspace;
+            e = tlg::launch_skinny_strip(info.config - tlg::SPLIT_WAVES_32x64x64, p, info.splits,
+                                         ws + kCounterBytes / sizeof(float), (int *)ws, stream);
+            break;
+        }
         default: return TLG_ERROR_NOT_SUPPORTED;
     }
     return e == hipSuccess ? TLG_SUCCESS : TLG_ERROR_HIP;

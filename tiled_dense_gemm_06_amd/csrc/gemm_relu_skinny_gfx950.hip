@@ -61,7 +61,9 @@ constexpr int kPartialScope = 16;
 
 // Grid: strips x parts (a.k_split parts per strip, adjacent work-groups share
 // a strip). Part p takes the strip's K blocks [p*nkb/parts, (p+1)*nkb/parts).
-template <class S, int W>
+// BT (B given transposed, N x K): a block of B is BN rows n of 64 k, loaded
+// and read the way A's rows are.
+template <class S, int W, bool BT = false>
 __global__ __launch_bounds__(W * 64) void k_skinny_strip(const KArgs a) {
     static_assert(S::WAVES == 1, "one wave per ring");
     constexpr int LOADS = S::DMA_A + S::DMA_B;  // loads per block per wave
@@ -84,10 +86,11 @@ __global__ __launch_bounds__(W * 64) void k_skinny_strip(const KArgs a) {
     LDS_PTR(char) ring = (LDS_PTR(char))smem + wave * RING;
 
     // Block j of this wave (block kb0 + wave + W j of the strip) into stage buffer buf.
+    static_assert(!BT || S::BN * S::BK * 2 == S::DMA_B * 1024, "a transposed B block is whole loads of A's kind");
     auto issue = [&](int j, int buf) {
         const int k0 = (kb0 + wave + W * j) * S::BK;
         const int4_t ra = make_srd(a.A + k0);
-        const int4_t rb = make_srd(a.B + (int64_t)k0 * a.ldb + n0);
+        const int4_t rb = make_srd(BT ? a.B + (int64_t)n0 * a.ldb + k0 : a.B + (int64_t)k0 * a.ldb + n0);
         LDS_PTR(char) st = ring + buf * S::STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < S::DMA_A; ++i) {
@@ -97,8 +100,9 @@ __global__ __launch_bounds__(W * 64) void k_skinny_strip(const KArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < S::DMA_B; ++i) {
-            const ChunkRef c = dma_b_chunk<S>(0, i, lane);
-            const bool in = n0 + 8 * c.chunk < a.N && k0 + c.row < a.K;
+            const ChunkRef c = BT ? dma_a_chunk<S>(0, i, lane) : dma_b_chunk<S>(0, i, lane);
+            const bool in = BT ? n0 + c.row < a.N && k0 + 8 * c.chunk < a.K
+                               : n0 + 8 * c.chunk < a.N && k0 + c.row < a.K;
             dma16_nt(rb, (uint32_t)(uintptr_t)(st + S::A_BYTES + i * 1024),
                      in ? (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16) : kOOB);
         }
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(W * 64) void k_skinny_strip(const KArgs a) {
         // this wave's blocks still in flight behind block j may keep loading
         wait_blocks<LOADS, S::STAGES>(imin(S::STAGES - 1, mine - 1 - j));
         LDS_PTR(const char) st = ring + buf * S::STAGE_BYTES;
-        mma_stage<S>(st, st + S::A_BYTES, 0, 0, lane, acc);
+        mma_stage<S, BT>(st, st + S::A_BYTES, 0, 0, lane, acc);
         // every read of this buffer is complete before the block STAGES ahead
         // is loaded into it (compiler-visible lgkmcnt(0))
         __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -493,6 +497,7 @@ const TileConfig &kStripConfig = kStripConfigs[0];
 
 template <class S, int W>
 static hipError_t launch_strip_t(const Problem &p, int parts, float *partials, int *counters, hipStream_t stream) {
+    static_assert(S::BN * S::BK * 2 == S::DMA_B * 1024, "strip blocks are whole loads");
     static_assert(W * S::STAGES * S::STAGE_BYTES <= 160 * 1024, "rings fit the LDS");
     KArgs a;
     a.A = (const _Float16 *)p.A;
@@ -511,7 +516,11 @@ static hipError_t launch_strip_t(const Problem &p, int parts, float *partials, i
     a.group_m = 1;
     a.k_split = parts;
     a.kmain = (int)p.K;
-    hipLaunchKernelGGL((k_skinny_strip<S, W>), dim3((unsigned)(a.tiles_n * parts)), dim3(W * 64), 0, stream, a);
+    if (p.trans_b)
+        hipLaunchKernelGGL((k_skinny_strip<S, W, true>), dim3((unsigned)(a.tiles_n * parts)), dim3(W * 64), 0, stream,
+                           a);
+    else
+        hipLaunchKernelGGL((k_skinny_strip<S, W>), dim3((unsigned)(a.tiles_n * parts)), dim3(W * 64), 0, stream, a);
     return hipGetLastError();
 }
 
