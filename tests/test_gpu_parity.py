@@ -642,6 +642,46 @@ def test_random_ragged_sweep(dev):
             assert np.array_equal(got, ref), (case, M, N, K, v)
 
 
+def test_random_transposed_sweep(dev):
+    """Seeded random shapes with B transposed, drawn so that every planned
+    path occurs: the 16 x 16 x 32 256 x 256 tiles with interior and edge
+    column tiles and K tails, their 192 x 256 and 128 x 256 forms, the
+    32 x 32 x 16 form, the column strips (one part and several) and the
+    direct-to-LDS tiles; each result bit-exact against the oracle on integer
+    inputs (the planned kernel and, where it differs, the forced 16 x 16 x 32
+    256 x 256 tiles)."""
+    rng = np.random.default_rng(77)
+    seen = set()
+    for case in range(24):
+        kind = case % 4
+        if kind == 0:    # 128 tiles of 256 x 256 or more, ragged N and K
+            M, N = int(rng.integers(2049, 3400)), int(rng.integers(3800, 4500))
+            K = int(rng.integers(1, 9)) * 64 + (int(rng.integers(0, 64)) if case % 8 == 0 else 0)
+        elif kind == 1 and case % 8 == 1:  # below 128 tiles of 256 x 256, at least 192 of 128 x 256
+            M, N, K = int(rng.integers(2600, 3000)), int(rng.integers(2100, 2560)), int(rng.integers(100, 700))
+        elif kind == 1:  # fewer: the 128 x 128 direct-to-LDS tiles
+            M, N, K = int(rng.integers(1700, 1900)), int(rng.integers(1900, 2040)), int(rng.integers(100, 700))
+        elif kind == 2:  # skinny M, aligned
+            M, N, K = int(rng.integers(1, 65)), 8 * int(rng.integers(8, 900)), 8 * int(rng.integers(64, 700))
+        else:            # anything small
+            M, N, K = (int(x) for x in rng.integers(1, 400, size=3))
+        A, B = wl.make_random(M, N, K, seed=500 + case, kind="integer_pos")
+        Bt = np.ascontiguousarray(B.T)
+        ref = oracle.gemm_relu_bt(A, Bt)
+        name = tlg.plan(M, N, K, trans_b=True)["config_name"]
+        seen.add(name)
+        print(f"random transposed case {case}: {(M, N, K)} {name}", flush=True)
+        Ad, Btd = to_dev(A, dev), to_dev(Bt, dev)
+        got = bits(tlg.gemm_relu(Ad, Btd, trans_b=True))
+        assert np.array_equal(got, ref), (case, M, N, K, name)
+        if M * N >= 256 * 256:
+            got = bits(tlg.gemm_relu(Ad, Btd, trans_b=True, variant=V_PIPE, config=17))
+            assert np.array_equal(got, ref), (case, M, N, K, "forced 17")
+    families = ("pipe16_256x256x64", "pipe16_192x256x64", "pipe16_128x256x64", "pipe_256x256x64", "splitk_waves",
+                "dma_128x128x32", "dma_64x64x64")
+    assert all(any(n.startswith(f) for n in seen) for f in families), seen
+
+
 def test_degenerate_sizes(dev):
     # K == 0: C = +0 in the window
     C = torch.full((5, 7), float("nan"), dtype=torch.float16, device=dev)
