@@ -642,6 +642,41 @@ def test_random_ragged_sweep(dev):
             assert np.array_equal(got, ref), (case, M, N, K, v)
 
 
+def test_random_planned_sweep(dev):
+    """Seeded random shapes for the plain call, drawn so that the planner's
+    main families occur (the 16 x 16 x 32 tiles in their three heights with
+    K tails, the 32 x 32 x 16 pipelined tiles for N not a multiple of 8, the
+    column strips, the two-kernel split-K for long K, the direct-to-LDS
+    tiles); each result bit-exact against the oracle on integer inputs."""
+    rng = np.random.default_rng(78)
+    seen = set()
+    for case in range(24):
+        kind = case % 6
+        if kind == 0:    # 256 x 256 tiles (K tails from 256 tiles)
+            M, N = int(rng.integers(3900, 4300)), 8 * int(rng.integers(500, 540))
+            K = int(rng.integers(1, 6)) * 64 + (int(rng.integers(1, 64)) if case % 12 == 0 else 0)
+        elif kind == 1:  # tile height by rounds, K whole stages
+            M, N, K = int(rng.integers(2300, 3100)), 8 * int(rng.integers(380, 400)), 64 * int(rng.integers(2, 8))
+        elif kind == 2:  # N not a multiple of 8
+            M, N, K = int(rng.integers(2100, 3000)), int(rng.integers(3800, 4400)) | 1, int(rng.integers(100, 500))
+        elif kind == 3:  # skinny M
+            M, N, K = int(rng.integers(1, 65)), 8 * int(rng.integers(8, 900)), 8 * int(rng.integers(300, 700))
+        elif kind == 4:  # M > 64, long K, few tiles
+            M, N, K = 64 * int(rng.integers(2, 9)), 64 * int(rng.integers(4, 9)), 64 * int(rng.integers(64, 129))
+        else:            # anything mid-sized
+            M, N, K = (int(x) for x in rng.integers(50, 1500, size=3))
+        A, B = wl.make_random(M, N, K, seed=600 + case, kind="integer_pos")
+        ref = oracle.gemm_relu(A, B)
+        name = tlg.plan(M, N, K)["config_name"]
+        seen.add(name)
+        print(f"random planned case {case}: {(M, N, K)} {name}", flush=True)
+        got = bits(run(A, B, dev))
+        assert np.array_equal(got, ref), (case, M, N, K, name)
+    families = ("pipe16_256x256x64", "pipe16_192x256x64", "pipe16_128x256x64", "pipe_256x256x64", "splitk_waves",
+                "splitk_32x128x64")
+    assert all(any(n.startswith(f) for n in seen) for f in families), seen
+
+
 def test_random_transposed_sweep(dev):
     """Seeded random shapes with B transposed, drawn so that every planned
     path occurs: the 16 x 16 x 32 256 x 256 tiles with interior and edge
