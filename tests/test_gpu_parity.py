@@ -555,6 +555,46 @@ def test_grouped_pipe16(dev, config, trans_b):
         assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
 
 
+@pytest.mark.parametrize("trans_b", [False, True])
+def test_random_grouped_sweep(dev, trans_b):
+    """Seeded random groups (2 to 16 problems of mixed sizes, some empty,
+    some with K tails or N not a multiple of 8), each group once with the
+    library's choice: every problem bit-exact against its oracle result,
+    guard bands intact. Some groups total 128 tiles of 256 x 256 or more (the
+    pipelined kernels), the others fewer (the direct-to-LDS tiles)."""
+    rng = np.random.default_rng(90 + int(trans_b))
+    for g in range(6):
+        count = int(rng.integers(2, 17))
+        big_group = g % 2 == 0
+        shapes = []
+        for i in range(count):
+            if big_group:
+                M, N = int(rng.integers(600, 2200)), int(rng.integers(600, 2200))
+                K = 64 * int(rng.integers(1, 6)) if (g // 2) % 2 == 0 else int(rng.integers(30, 400))
+            else:
+                M, N, K = (int(x) for x in rng.integers(0, 300, size=3))
+            shapes.append((M, N, K))
+        probs, As, Bs, bigs, outs = [], [], [], [], []
+        for i, (M, N, K) in enumerate(shapes):
+            A, B = wl.make_random(M, N, K, seed=1000 * g + i, kind="integer_pos")
+            Bx = np.ascontiguousarray(B.T) if trans_b else B
+            probs.append((A, Bx))
+            As.append(to_dev(A, dev))
+            Bs.append(to_dev(Bx, dev))
+            big = torch.full((M + 2, N + 8), float("nan"), dtype=torch.float16, device=dev)
+            bigs.append(big)
+            outs.append(big[:M, :N])
+        t256 = sum(-(-M // 256) * -(-N // 256) for M, N, _ in shapes)
+        print(f"random grouped {g} trans_b={trans_b}: {count} problems, {t256} tiles of 256^2", flush=True)
+        tlg.gemm_relu_grouped(As, Bs, outs, trans_b=trans_b)
+        torch.cuda.synchronize()
+        refs = oracle.gemm_relu_grouped(probs, trans_b=trans_b)
+        for (M, N, K), big, ref in zip(shapes, bigs, refs):
+            allb = bits(big)
+            assert np.array_equal(allb[:M, :N], ref), (g, M, N, K)
+            assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+
+
 def test_grouped_rejects_bad_calls(dev):
     """Too many problems, an ld below the row width, a mixed device: errors, nothing enqueued."""
     A = torch.ones((8, 8), dtype=torch.float16, device=dev)
