@@ -68,8 +68,9 @@ enum PipeConfig {
     PIPE_256x256x64_W8_A3_EARLY = 7,  // stage barrier before the last half k-step (the default)
     PIPE_256x256x64_W8_B3_EARLY = 8,  // two A buffers, three B buffers
     PIPE_256x256x64_B3 = 9,           // four waves, two A buffers, three B buffers
-    // v_mfma_f32_16x16x32_f16 tiles (any K and N, B not transposed): four
-    // waves of 128 x 128 (128 x 256 tiles: four waves of 128 x 64)
+    // v_mfma_f32_16x16x32_f16 tiles (any K and N; with B transposed
+    // configurations 17, 21 and 26): four waves of 128 x 128 (128 x 256
+    // tiles: four waves of 128 x 64)
     PIPE16_FIRST = 10,
     PIPE16_256x256x64_A3 = 10,
     PIPE16_256x256x64_A3_EARLY = 11,
@@ -112,13 +113,13 @@ hipError_t launch_tiled_dma(int config, const Problem &p, hipStream_t stream);
 hipError_t launch_tiled_dma_grouped(int config, const Problem *ps, int count, hipStream_t stream);
 hipError_t launch_tiled_general(int config, const Problem &p, hipStream_t stream);
 hipError_t launch_tiled_pipe(int config, const Problem &p, hipStream_t stream);
-// the 16 x 16 x 32 MFMA configurations (PIPE16_FIRST and up); B not
-// transposed (hipErrorInvalidValue otherwise)
+// the 16 x 16 x 32 MFMA configurations (PIPE16_FIRST and up); with B
+// transposed only 17, 21 and 26 (hipErrorInvalidValue otherwise)
 hipError_t launch_tiled_pipe16(int config, const Problem &p, hipStream_t stream);
 // count (1 .. kGroupMax) problems, all with the same trans_b, in one launch
 // of the eight-wave early-barrier pipelined kernel (each must pass its checks)
 hipError_t launch_tiled_pipe_grouped(const Problem *ps, int count, hipStream_t stream);
-// count (1 .. kGroupMax) problems, none with a transposed B, in one launch of
+// count (1 .. kGroupMax) problems, all with the same trans_b, in one launch of
 // the default 16 x 16 x 32 pipelined configuration
 hipError_t launch_tiled_pipe16_grouped(const Problem *ps, int count, hipStream_t stream);
 hipError_t launch_pingpong(int config, const Problem &p, hipStream_t stream);
