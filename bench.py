@@ -454,9 +454,9 @@ def main() -> int:
     if args.grouped and (variant != tlg.TLG_VARIANT_AUTO or args.splits):
         print("bench.py: --grouped takes only --config", file=sys.stderr)
         return 2
-    if args.trans_b and (variant not in (tlg.TLG_VARIANT_AUTO, tlg.TLG_VARIANT_TILED_PIPE, tlg.TLG_VARIANT_TILED_DMA)
-                         or args.splits):
-        print("bench.py: --trans-b takes --variant auto, tiled_pipe or tiled_dma and --config", file=sys.stderr)
+    if args.trans_b and (variant not in (tlg.TLG_VARIANT_AUTO, tlg.TLG_VARIANT_TILED_PIPE, tlg.TLG_VARIANT_TILED_DMA,
+                                         tlg.TLG_VARIANT_SPLITK) or args.splits):
+        print("bench.py: --trans-b takes --variant auto, tiled_pipe, tiled_dma or splitk and --config", file=sys.stderr)
         return 2
     if args.trans_b:
         B = np.ascontiguousarray(B.T)
