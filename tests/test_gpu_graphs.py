@@ -88,3 +88,62 @@ def test_graph_replays_match_oracle(dev, shape, variant, config, splits):
         torch.cuda.synchronize()
         assert np.array_equal(bits(Co), ref_o), f"eager call after replay {rep}"
     del g
+
+
+# B transposed (the strips in parts keep counters in the handle's workspace)
+# and grouped calls: (M, N, K), trans_b, variant, config, grouped config
+BT_CASES = [
+    ((16, 2048, 4096), True, V_AUTO, -1, None),    # strips in 4 parts, B transposed
+    ((512, 520, 264), True, V_PIPE, 17, None),     # 16 x 16 x 32 256 x 256: interior and edge tiles, K tail
+    ((301, 259, 203), True, V_PIPE, 21, None),     # 16 x 16 x 32 128 x 256, ragged
+    ((520, 264, 200), False, None, None, 4),       # grouped 16 x 16 x 32, K tails
+    ((520, 259, 192), True, None, None, 4),        # grouped 16 x 16 x 32, B transposed
+    ((300, 264, 72), True, None, None, 1),         # grouped direct-to-LDS, B transposed
+]
+
+
+@pytest.mark.parametrize("shape,trans_b,variant,config,gconfig", BT_CASES)
+def test_graph_replays_transposed_and_grouped(dev, shape, trans_b, variant, config, gconfig):
+    """As above for calls with B transposed and for grouped calls (three
+    problems of the shape, the second and third one row shorter each)."""
+    M, N, K = shape
+    print(f"graph {shape} trans_b={trans_b} variant={variant} config={config} grouped={gconfig}", flush=True)
+    shapes = [(M - i, N, K) for i in range(3)]
+    ins = [wl.make_random(m, n, k, seed=m + 7 * n + 13 * k + s, kind="integer") for s, (m, n, k) in enumerate(shapes)]
+    ins = [(A, np.ascontiguousarray(B.T) if trans_b else B) for A, B in ins]
+    refs = oracle.gemm_relu_grouped(ins, trans_b=trans_b)
+    As = [torch.from_numpy(A).to(dev) for A, _ in ins]
+    Bs = [torch.from_numpy(B).to(dev) for _, B in ins]
+    Cs = [torch.full((m, n), float("nan"), dtype=torch.float16, device=dev) for m, n, _ in shapes]
+    h = tlg.handle_for(dev)
+
+    def calls():
+        if gconfig is not None:
+            tlg.gemm_relu_grouped(As, Bs, Cs, trans_b=trans_b, config=gconfig, handle=h)
+        else:
+            for A, B, C in zip(As, Bs, Cs):
+                tlg.gemm_relu(A, B, out=C, handle=h, trans_b=trans_b, variant=variant, config=config)
+
+    calls()
+    torch.cuda.synchronize()
+    for C, ref in zip(Cs, refs):
+        assert np.array_equal(bits(C), ref), "eager"
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    Ao, Bo = wl.make_random(16, 1024, 2048, seed=98, kind="integer")
+    Bot = np.ascontiguousarray(Bo.T)
+    Aod, Botd = torch.from_numpy(Ao).to(dev), torch.from_numpy(Bot).to(dev)
+    ref_o = oracle.gemm_relu_bt(Ao, Bot)
+    for rep in range(4):
+        for C in Cs:
+            C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (C, ref) in enumerate(zip(Cs, refs)):
+            assert np.array_equal(bits(C), ref), f"replay {rep}, problem {i}"
+        Co = tlg.gemm_relu(Aod, Botd, handle=h, trans_b=True)  # split strips of the same handle between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(Co), ref_o), f"eager call after replay {rep}"
+    del g
