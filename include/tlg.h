@@ -232,7 +232,9 @@ tlg_status tlg_gemm_relu_bt_variant(tlg_handle h, int32_t variant, int32_t confi
                                     void *C, int64_t ldc,
                                     hipStream_t stream);
 
-/* What tlg_gemm_relu_bt(_variant) would launch (host only, no GPU). */
+/* What tlg_gemm_relu_bt(_variant) would launch (host only, no GPU), planned
+ * for a handle's workspace of tlg_workspace_bytes() (only split strips use it;
+ * out->workspace_bytes says how much). */
 tlg_status tlg_plan_bt(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                        const void *Bt, int64_t ldbt, const void *C, int64_t ldc,
                        int32_t variant, int32_t config, tlg_plan_info *out);

@@ -75,7 +75,8 @@ int main() {
         tlg_plan_info ob;
         const tlg_status sb = tlg_plan_bt(M, N, K, A, (K > 1 ? K : 1) + (lda - (K > 1 ? K : 1)), B,
                                           (K > 1 ? K : 1) + (ldb - (N > 1 ? N : 1)), C, ldc, v, c, &ob);
-        if (sb == TLG_SUCCESS) check_info(ob, 0, M, N, K, v, c);
+        // the transposed-B call's split strips use the handle's workspace
+        if (sb == TLG_SUCCESS) check_info(ob, tlg_workspace_bytes(), M, N, K, v, c);
         const int fmt = (int)(rnd() % 5);
         const int64_t Kx = K >= 0 && rnd() % 2 ? K - K % 32 : K;
         tlg_plan_info om;
