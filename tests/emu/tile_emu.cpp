@@ -767,6 +767,7 @@ extern "C" int emu_gemm_relu_bt(int config, int M, int N, int K, const uint16_t 
         case 2: return emulate<E64>(p, false, errs);
         case 3: return emulate<EP64>(p, false, errs);    // pipelined, four waves
         case 4: return emulate<E256w8>(p, false, errs);  // pipelined, eight waves
+        case 8: return emulate<EStrip64>(p, false, errs);  // the 64-row strip, B's blocks like A's rows
         case 20: return emulate_pipe16<E16w4>(p, errs);  // 16 x 16 x 32 pipelined tiles
         case 21: return emulate_pipe16<E16h>(p, errs);
         case 23: return emulate_pipe16<E16t>(p, errs);

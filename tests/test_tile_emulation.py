@@ -140,6 +140,26 @@ def test_one_wave_strip_tile_matches_oracle_integer(emu, shape):
     assert np.array_equal(C, oracle.gemm_relu(A, B))
 
 
+@pytest.mark.parametrize("shape", [(48, 64, 128), (64, 136, 520), (33, 392, 64), (1, 8, 8), (63, 200, 1000)])
+def test_one_wave_strip_tile_transposed_b(emu, shape):
+    """The same strip ring with B given transposed (N x K): each block of B is
+    64 rows n of 64 k, loaded with A's chunk order and swizzle and read with
+    A's fragment reads; loads in bounds, each LDS byte written once, no bank
+    conflicts, exact result."""
+    M, N, K = shape
+    A, B = wl.make_random(M, N, K, seed=M + 3 * N + K, kind="integer_pos" if K > 100 else "integer")
+    Bt = np.ascontiguousarray(B.T)
+    C = np.full((M, N), 0xFFFF, np.uint16)
+    errs = np.zeros(8, np.int64)
+    A16, Bt16 = np.ascontiguousarray(A.view(np.uint16)), Bt.view(np.uint16)
+    rc = emu.emu_gemm_relu_bt(8, M, N, K, A16.ctypes.data, K, Bt16.ctypes.data, K, C.ctypes.data, N,
+                              errs.ctypes.data)
+    assert rc == 0
+    errs = dict(zip(ERR_NAMES, errs.tolist()))
+    assert all(v == 0 for v in errs.values()), errs
+    assert np.array_equal(C, oracle.gemm_relu(A, B))
+
+
 RAGGED = [(301, 259, 203), (65, 9, 17), (130, 264, 97), (33, 41, 8), (257, 131, 1), (64, 64, 65), (3, 263, 72)]
 
 
