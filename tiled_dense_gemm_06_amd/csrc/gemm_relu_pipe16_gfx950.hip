@@ -165,6 +165,46 @@ __device__ __forceinline__ void store_c_tile16_lds(const KArgs &a, int m0, int n
     }
 }
 
+// Direct-to-LDS loads that leave five wait states between any earlier
+// instruction and the load. With B transposed the kernel runs with more
+// scalar registers spilled, and the compiler may reload a descriptor word
+// (v_readlane, a vector-ALU write of a scalar register) right before the
+// inline-assembly load, which reads the descriptor, and must not read it
+// within five wait states of that write. The K tail of those instantiations
+// and the loop of their tile that holds row N (BROWS) take these; the loop
+// of the tiles inside N keeps the plain loads (the test of the generated
+// assembly finds no such reload there, and the wait would cost 2 %).
+__device__ __forceinline__ void dma16_settled(int4_t srd, uint32_t lds_base, uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_base),
+        "v"(voff), "s"(srd)
+        : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_soff_settled(int4_t srd, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_base),
+        "v"(voff), "s"(srd), "s"(soff)
+        : "memory", "m0");
+}
+template <bool SETTLED>
+__device__ __forceinline__ void p16_dma(int4_t srd, uint32_t lds_base, uint32_t voff) {
+    if constexpr (SETTLED)
+        dma16_settled(srd, lds_base, voff);
+    else
+        dma16(srd, lds_base, voff);
+}
+template <bool SETTLED>
+__device__ __forceinline__ void p16_dma_soff(int4_t srd, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+    if constexpr (SETTLED)
+        dma16_soff_settled(srd, lds_base, voff, soff);
+    else
+        dma16_soff(srd, lds_base, voff, soff);
+}
+
 // The MFMAs of one B column (acc[tn][0..TM-1]) as one block that ends with 20
 // wait states, so that whatever the compiler places after it (a copy or a
 // spill of an accumulator, which it may schedule right behind an MFMA it
@@ -240,7 +280,7 @@ __device__ __forceinline__ void pipe16_k_tail(const KArgs &a, int m0, int n0, in
         for (int i = 0; i < S::DMA_A; ++i) {
             const ChunkRef c = dma_a_chunk<S>(wave, i, lane);
             const bool in = m0 + c.row < a.M && kfull + 8 * c.chunk < a.kmain;
-            dma16(ra, (uint32_t)(uintptr_t)(lds + (wave * S::DMA_A + i) * 1024),
+            p16_dma<BT>(ra, (uint32_t)(uintptr_t)(lds + (wave * S::DMA_A + i) * 1024),
                   in ? (uint32_t)(c.row * a.lda * 2 + c.chunk * 16) : kOOB);
         }
 #pragma unroll
@@ -248,7 +288,7 @@ __device__ __forceinline__ void pipe16_k_tail(const KArgs &a, int m0, int n0, in
             const ChunkRef c = BT ? dma_bt16_chunk<S>(wave, i, lane) : dma_b16_chunk<S>(wave, i, lane);
             const bool in = BT ? n0 + c.row < a.N && kfull + 8 * c.chunk < a.kmain
                                : kfull + c.row < a.kmain && n0 + 8 * c.chunk < a.N;
-            dma16(rb, (uint32_t)(uintptr_t)(lds + B_REGION + (wave * S::DMA_B + i) * 1024),
+            p16_dma<BT>(rb, (uint32_t)(uintptr_t)(lds + B_REGION + (wave * S::DMA_B + i) * 1024),
                   in ? (uint32_t)(c.row * a.ldb * 2 + c.chunk * 16) : kOOB);
         }
         wait_vmcnt<0>();
@@ -400,18 +440,18 @@ __device__ __forceinline__ void pipe16_tile(const KArgs &a, int tm_idx, int tn_i
             const int slab = wave * S::DMA_A + j;
             int4_t r = make_srd(a_tile + (int64_t)slab * 8 * a.lda + k0);
             r[2] = kt < nk ? (int)nrec_a[j] : 0;
-            dma16(r, (uint32_t)(uintptr_t)(lds + buf * S::A_BYTES + slab * 1024), voff_a[slab % 2]);
+            p16_dma<BROWS>(r, (uint32_t)(uintptr_t)(lds + buf * S::A_BYTES + slab * 1024), voff_a[slab % 2]);
         } else if constexpr (BROWS) {
             const int slab = wave * S::DMA_B + (j - S::DMA_A);
             int4_t r = make_srd(b_tile + (int64_t)slab * 8 * a.ldb + k0);
             r[2] = kt < nk ? (int)nrec_b[BROWS ? j - S::DMA_A : 0] : 0;
-            dma16(r, (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES + slab * 1024), voff_b[slab % 2]);
+            p16_dma<BROWS>(r, (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES + slab * 1024), voff_b[slab % 2]);
         } else if constexpr (BT) {
             const int slab = wave * S::DMA_B + (j - S::DMA_A);
             int4_t r = make_srd(b_tile + k0);
             if (kt >= nk) r[2] = 0;
-            dma16_soff(r, (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES + slab * 1024), voff_b[slab % 2],
-                       (uint32_t)(slab * 8 * a.ldb * 2));
+            p16_dma_soff<BROWS>(r, (uint32_t)(uintptr_t)(lds + B_REGION + buf * S::B_BYTES + slab * 1024),
+                                voff_b[slab % 2], (uint32_t)(slab * 8 * a.ldb * 2));
         } else {
             const int slab = wave * S::DMA_B + (j - S::DMA_A);
             int4_t r = make_srd(b_tile + (int64_t)k0 * a.ldb);
