@@ -449,6 +449,25 @@ def test_transposed_b_strips(dev, shape, config_name, parts):
     assert np.array_equal(got, got2)
 
 
+@pytest.mark.parametrize("config", [3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("shape", [(16, 2048, 4096), (7, 1000, 2048), (32, 1032, 520), (1, 264, 8192), (8, 16384, 512)])
+def test_transposed_b_strip_configs(dev, config, shape):
+    """Every column-strip configuration forced with B transposed (four waves,
+    four stages, 128- and 256-column strips, the 64-row strip), with the
+    library's parts per strip: integer inputs exact, guard bands intact."""
+    M, N, K = shape
+    print(f"transposed strip config={config} {shape}", flush=True)
+    A, B = wl.make_random(M, N, K, seed=M + 11 * N + K + config, kind="integer_pos")
+    Bt = np.ascontiguousarray(B.T)
+    big = torch.full((M + 2, N + 8), float("nan"), dtype=torch.float16, device=dev)
+    tlg.gemm_relu(to_dev(A, dev), to_dev(Bt, dev), out=big[:M, :N], trans_b=True, variant=tlg.TLG_VARIANT_SPLITK,
+                  config=config)
+    torch.cuda.synchronize()
+    allb = bits(big)
+    assert np.array_equal(allb[:M, :N], oracle.gemm_relu_bt(A, Bt))
+    assert np.all(np.isnan(allb[:M, N:].view(np.float16))) and np.all(np.isnan(allb[M:].view(np.float16)))
+
+
 def test_transposed_b_uniform_and_strided(dev):
     """Uniform inputs within the tolerance; padded leading dimensions of A, Bt, C."""
     M, N, K = 777, 555, 333
